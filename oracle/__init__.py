@@ -1,0 +1,173 @@
+"""CPU oracle for C = A·B — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (``dense_gemm_17_amd``) never imports
+it and shares no code with it; the two meet only through the seeded input
+generators in ``workloads.py``, which hold none of the product's arithmetic.
+
+``oracle.c`` is the plain definition of the matrix product ("Bare Metal Bard",
+page 1, first paragraph: the ladder of matmul kernels; vidyal.ai Part 5,
+"Writing a Fast Matmul in CUDA, Step by Step"), accumulated in fp64 together
+with the magnitude sum D = sum_k |a_ik * b_kj| that the correctness gate
+divides by.  Every entry point here is pinned by ``tests/test_oracle.py``
+(identity, permutation, ones, exact small-integer, brute force against exact
+rational arithmetic, numpy fp64 BLAS, thread-count invariance and planted
+mutants); no function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# -O2 without fast-math and with contraction off: the sums are evaluated in
+# source order, one rounding per addition, no fused multiply-add.
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
+          "-pthread", "-shared", "-fPIC", "-Wall", "-Wextra"]
+
+MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP")
+
+
+def build(out: str = _LIB_PATH, mutant: Optional[str] = None) -> str:
+    """Compile oracle.c with gcc into ``out``.  ``mutant`` names one planted
+    mistake (see MUTANTS) for the oracle's own sensitivity tests."""
+    cmd = ["gcc", *CFLAGS, _SRC, "-o", out, "-lm"]
+    if mutant is not None:
+        if mutant not in MUTANTS:
+            raise ValueError(f"unknown oracle mutant {mutant!r}")
+        cmd.insert(1, f"-DORACLE_MUTANT_{mutant}")
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    full = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, ctypes.c_int]
+    rows = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, ctypes.c_int]
+    for name, argt in (("oracle_gemm_f32", full), ("oracle_gemm_bf16", full),
+                       ("oracle_gemm_f32_rows", rows), ("oracle_gemm_bf16_rows", rows)):
+        fn = getattr(lib, name)
+        fn.argtypes = argt
+        fn.restype = ctypes.c_int
+    lib.oracle_decode_bf16.argtypes = [_vp, _vp, _i64]
+    lib.oracle_decode_bf16.restype = None
+    return lib
+
+
+_lib: Optional["Oracle"] = None
+
+
+class Oracle:
+    """Thin ctypes wrapper around one build of oracle.c."""
+
+    def __init__(self, path: str):
+        self.path = path
+        self.lib = _bind(ctypes.CDLL(path))
+
+    @staticmethod
+    def _operand(x: np.ndarray, dtype) -> Tuple[np.ndarray, int]:
+        if x.ndim != 2:
+            raise ValueError("operands must be 2-D")
+        if x.dtype != dtype:
+            raise TypeError(f"expected {np.dtype(dtype)}, got {x.dtype}")
+        if x.shape[0] and x.shape[1] and x.strides[1] != x.itemsize:
+            x = np.ascontiguousarray(x)
+        ld = x.strides[0] // x.itemsize if x.shape[0] > 1 else max(1, x.shape[1])
+        return x, max(ld, x.shape[1], 1)
+
+    def _call(self, fn_name, dtype, A, B, rows, threads):
+        A, lda = self._operand(A, dtype)
+        B, ldb = self._operand(B, dtype)
+        M, K = A.shape
+        K2, N = B.shape
+        if K != K2:
+            raise ValueError(f"inner dimensions differ: {A.shape} x {B.shape}")
+        if rows is None:
+            nr = M
+        else:
+            rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+            nr = rows.shape[0]
+        C = np.zeros((nr, N), dtype=np.float64)
+        D = np.zeros((nr, N), dtype=np.float64)
+        ptr = lambda a: a.ctypes.data if a.size else None  # noqa: E731
+        if rows is None:
+            rc = getattr(self.lib, fn_name)(M, N, K, ptr(A), lda, ptr(B), ldb,
+                                            ptr(C), ptr(D), max(N, 1), threads)
+        else:
+            rc = getattr(self.lib, fn_name + "_rows")(M, N, K, ptr(A), lda, ptr(B), ldb,
+                                                      ptr(rows), nr, ptr(C), ptr(D),
+                                                      max(N, 1), threads)
+        if rc != 0:
+            raise RuntimeError(f"{fn_name} failed with code {rc}")
+        return C, D
+
+    def gemm_f32(self, A: np.ndarray, B: np.ndarray, rows: Optional[Sequence[int]] = None,
+                 threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """(C, D) in fp64 for fp32 operands; ``rows`` restricts to those rows of C."""
+        return self._call("oracle_gemm_f32", np.float32, A, B, rows, threads)
+
+    def gemm_bf16(self, A_bits: np.ndarray, B_bits: np.ndarray,
+                  rows: Optional[Sequence[int]] = None,
+                  threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """(C, D) in fp64 for bf16 operands given as raw uint16 patterns."""
+        return self._call("oracle_gemm_bf16", np.uint16, A_bits, B_bits, rows, threads)
+
+    def decode_bf16(self, bits: np.ndarray) -> np.ndarray:
+        bits = np.ascontiguousarray(bits, dtype=np.uint16).reshape(-1)
+        out = np.empty(bits.shape, dtype=np.float64)
+        if bits.size:
+            self.lib.oracle_decode_bf16(bits.ctypes.data, out.ctypes.data, bits.size)
+        return out
+
+
+def load(path: str = _LIB_PATH) -> Oracle:
+    """The default oracle build, compiled on first use if it is missing."""
+    global _lib
+    if _lib is None or _lib.path != path:
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build(path)
+        _lib = Oracle(path)
+    return _lib
+
+
+def gemm_f32(A, B, rows=None, threads=0):
+    return load().gemm_f32(A, B, rows, threads)
+
+
+def gemm_bf16(A_bits, B_bits, rows=None, threads=0):
+    return load().gemm_bf16(A_bits, B_bits, rows, threads)
+
+
+def normalized_error(c: np.ndarray, c_ref: np.ndarray, d: np.ndarray):
+    """The correctness gate's statistic: max_ij |c_ij - C_ij| / D_ij.
+
+    Returns (e, (i, j) of the worst entry, count of entries above 1e-5).
+    A non-finite c gives e = inf.  Where D_ij = 0 every product is zero, so the
+    only correct value is exactly C_ij (= 0): any other value gives e = inf.
+    """
+    c = np.asarray(c, dtype=np.float64)
+    if c.shape != c_ref.shape or c.shape != d.shape:
+        raise ValueError(f"shape mismatch {c.shape} {c_ref.shape} {d.shape}")
+    if c.size == 0:
+        return 0.0, (0, 0), 0
+    diff = np.abs(c - c_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(d > 0, diff / np.where(d > 0, d, 1.0),
+                         np.where(diff == 0, 0.0, np.inf))
+    ratio = np.where(np.isfinite(c), ratio, np.inf)
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    return float(ratio[idx]), (int(idx[0]), int(idx[1])), int(np.count_nonzero(ratio > 1e-5))
+
+
+# Gate on the normalized error for both the fp32 and the bf16 path.
+GATE = 5e-4

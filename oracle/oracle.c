@@ -1,0 +1,204 @@
+/*
+ * CPU oracle for the dense matrix product C = A·B (row-major operands).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library or
+ * its Python binding) may link, load or call this file; only the test suite,
+ * the smoke check and the CPU-baseline leg of the benchmark use it.  It shares
+ * no code, header or constant with the HIP kernels.
+ *
+ * What it computes (the plain definition of the product, written out):
+ *   The subject of the pages is the matrix multiply itself: the ladder of
+ *   kernels on "Bare Metal Bard" (page 1, first paragraph) and "Writing a
+ *   Fast Matmul in CUDA, Step by Step" (vidyal.ai, Part 5) all compute
+ *       C[i][j] = sum_{k<K} A[i][k] * B[k][j]
+ *   and the correctness gate of this library additionally needs the
+ *   magnitude sum
+ *       D[i][j] = sum_{k<K} |A[i][k] * B[k][j]|
+ *   so that a result c is judged by max_ij |c_ij - C_ij| / D_ij.
+ *
+ * Precision: every product of two fp32 (or two bf16) values is exact in
+ * fp64 (24 + 24 significand bits <= 53), so the only rounding is the fp64
+ * running sum, whose error is at most K * 2^-53 * D[i][j].  bf16 operands
+ * are given as raw 16-bit patterns and decoded here (the pattern is the top
+ * half of an IEEE binary32 value).
+ *
+ * Loop order is i-k-j (a row of B is contiguous), rows are split into
+ * contiguous static blocks over POSIX threads.  Each output row is computed
+ * by exactly one thread in a fixed order, so the result does not depend on
+ * the thread count.  Build with -O2 -ffp-contract=off and no fast-math so the
+ * compiler neither fuses the multiply into the add nor reorders the sums.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* Compile-time planted mistakes, used only by the oracle's own sensitivity
+ * tests (the pins must reject each of them).  The default build defines none.
+ *   ORACLE_MUTANT_DROP_LAST_K  - the last k term is left out of both sums
+ *   ORACLE_MUTANT_TRANSPOSE_B  - B is read as B[j][k] instead of B[k][j]
+ *   ORACLE_MUTANT_SIGNED_D     - D sums signed products instead of |products|
+ *   ORACLE_MUTANT_BF16_SWAP    - bf16 decode takes the pattern byte-swapped
+ */
+
+static double decode_bf16(uint16_t bits)
+{
+#ifdef ORACLE_MUTANT_BF16_SWAP
+    bits = (uint16_t)((bits >> 8) | (bits << 8));
+#endif
+    uint32_t w = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+enum { KIND_F32 = 0, KIND_BF16 = 1 };
+
+typedef struct {
+    int kind;
+    int64_t M, N, K;
+    const void *A; int64_t lda;
+    const void *B; int64_t ldb;
+    double *C; double *D; int64_t ldo;
+    const int64_t *rows;   /* NULL: output row r is input row r */
+    int64_t nrows;
+    int64_t r0, r1;        /* this worker's block of output rows */
+} job_t;
+
+static double load_a(const job_t *j, int64_t i, int64_t k)
+{
+    if (j->kind == KIND_F32)
+        return (double)((const float *)j->A)[i * j->lda + k];
+    return decode_bf16(((const uint16_t *)j->A)[i * j->lda + k]);
+}
+
+static double load_b(const job_t *j, int64_t k, int64_t n)
+{
+#ifdef ORACLE_MUTANT_TRANSPOSE_B
+    int64_t t = k; k = n % j->K; n = t % j->N;
+#endif
+    if (j->kind == KIND_F32)
+        return (double)((const float *)j->B)[k * j->ldb + n];
+    return decode_bf16(((const uint16_t *)j->B)[k * j->ldb + n]);
+}
+
+/* One output row: acc and den start at zero, then for each k the row of B is
+ * scaled by A[i][k] and added (signed into C, absolute into D). */
+static void one_row(const job_t *j, int64_t i, double *crow, double *drow)
+{
+    for (int64_t n = 0; n < j->N; ++n) { crow[n] = 0.0; drow[n] = 0.0; }
+    int64_t kend = j->K;
+#ifdef ORACLE_MUTANT_DROP_LAST_K
+    if (kend > 0) kend -= 1;
+#endif
+    for (int64_t k = 0; k < kend; ++k) {
+        double a = load_a(j, i, k);
+        for (int64_t n = 0; n < j->N; ++n) {
+            double p = a * load_b(j, k, n);
+            crow[n] += p;
+#ifdef ORACLE_MUTANT_SIGNED_D
+            drow[n] += p;
+#else
+            drow[n] += fabs(p);
+#endif
+        }
+    }
+}
+
+static void *worker(void *arg)
+{
+    const job_t *j = (const job_t *)arg;
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        int64_t i = j->rows ? j->rows[r] : r;
+        one_row(j, i, j->C + r * j->ldo, j->D + r * j->ldo);
+    }
+    return NULL;
+}
+
+static int default_threads(void)
+{
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}
+
+static int run(job_t base, int nthreads)
+{
+    if (base.M < 0 || base.N < 0 || base.K < 0 || base.nrows < 0) return 1;
+    if (base.nrows == 0 || base.N == 0) return 0;
+    if (base.ldo < base.N) return 1;
+    if (base.K > 0 && (base.lda < base.K || base.ldb < base.N)) return 1;
+    if (base.rows)
+        for (int64_t r = 0; r < base.nrows; ++r)
+            if (base.rows[r] < 0 || base.rows[r] >= base.M) return 1;
+    if (nthreads <= 0) nthreads = default_threads();
+    if (nthreads > base.nrows) nthreads = (int)base.nrows;
+    if (nthreads > 1024) nthreads = 1024;
+
+    job_t *jobs = (job_t *)malloc(sizeof(job_t) * (size_t)nthreads);
+    pthread_t *tids = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!jobs || !tids) { free(jobs); free(tids); return 2; }
+    int64_t per = base.nrows / nthreads, extra = base.nrows % nthreads, r = 0;
+    int started = 0, rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = base;
+        jobs[t].r0 = r;
+        r += per + (t < extra ? 1 : 0);
+        jobs[t].r1 = r;
+    }
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, worker, &jobs[t]) != 0) { rc = 2; break; }
+        started = t;
+    }
+    if (rc == 0) worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
+    free(jobs);
+    free(tids);
+    return rc;
+}
+
+/* Full product.  C and D are M x N row-major fp64 with leading dimension ldo.
+ * Returns 0 on success, 1 on invalid arguments, 2 on a thread/alloc failure.
+ * nthreads <= 0 uses every online core. */
+int oracle_gemm_f32(int64_t M, int64_t N, int64_t K,
+                    const float *A, int64_t lda, const float *B, int64_t ldb,
+                    double *C, double *D, int64_t ldo, int nthreads)
+{
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0};
+    return run(j, nthreads);
+}
+
+int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
+                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                     double *C, double *D, int64_t ldo, int nthreads)
+{
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0};
+    return run(j, nthreads);
+}
+
+/* Selected rows only: output row r (of nrows) is the product's row rows[r].
+ * Used where the full product is too slow on a CPU (8192-cubed workloads). */
+int oracle_gemm_f32_rows(int64_t M, int64_t N, int64_t K,
+                         const float *A, int64_t lda, const float *B, int64_t ldb,
+                         const int64_t *rows, int64_t nrows,
+                         double *C, double *D, int64_t ldo, int nthreads)
+{
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0};
+    return run(j, nthreads);
+}
+
+int oracle_gemm_bf16_rows(int64_t M, int64_t N, int64_t K,
+                          const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                          const int64_t *rows, int64_t nrows,
+                          double *C, double *D, int64_t ldo, int nthreads)
+{
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0};
+    return run(j, nthreads);
+}
+
+/* bf16 pattern -> fp64, exposed so tests can pin the decoder on its own. */
+void oracle_decode_bf16(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_bf16(in[i]);
+}

@@ -1,0 +1,285 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+The oracle computes the plain definition of the matrix product (the subject of
+"Bare Metal Bard", page 1, first paragraph) in fp64 with the magnitude sum D.
+Each pin below is chosen so that a plausible mistake (a dropped term, a wrong
+index or transposed operand, a signed magnitude sum, a mis-decoded bf16
+pattern) fails at least one of them; the planted-mutant test at the end builds
+those mistakes into the oracle and checks exactly that.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ULP53 = 2.0 ** -53
+
+
+def read_golden(name):
+    mats, cur, rows = {}, None, []
+    with open(os.path.join(HERE, "golden", name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            if parts[0].isalpha() or parts[0][0].isalpha():
+                if cur:
+                    mats[cur] = np.array(rows, dtype=np.float64)
+                cur, rows = parts[0], []
+            else:
+                rows.append([float(x) for x in parts])
+    mats[cur] = np.array(rows, dtype=np.float64)
+    return mats
+
+
+def rng(seed=99):
+    return np.random.default_rng(seed)
+
+
+def rand_f32(shape, seed):
+    return (rng(seed).random(shape, dtype=np.float32) * 2 - 1).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# pins, written as functions of an Oracle instance so the mutant test can
+# re-run them against planted mistakes.
+# --------------------------------------------------------------------------
+
+def pin_golden(o):
+    g = read_golden("textbook_2x3x2.txt")
+    C, D = o.gemm_f32(g["A"].astype(np.float32), g["B"].astype(np.float32))
+    assert np.array_equal(C, g["C"]) and np.array_equal(D, g["C"])
+    C2, D2 = o.gemm_f32(g["A2"].astype(np.float32), g["B"].astype(np.float32))
+    assert np.array_equal(C2, g["C2"]) and np.array_equal(D2, g["D2"])
+
+
+def pin_identity(o):
+    B = rand_f32((37, 53), 1)
+    C, D = o.gemm_f32(np.eye(37, dtype=np.float32), B)
+    assert np.array_equal(C, B.astype(np.float64))
+    assert np.array_equal(D, np.abs(B).astype(np.float64))
+    A = rand_f32((41, 29), 2)
+    C, _ = o.gemm_f32(A, np.eye(29, dtype=np.float32))
+    assert np.array_equal(C, A.astype(np.float64))
+
+
+def pin_permutation(o):
+    r = rng(3)
+    B = rand_f32((31, 45), 4)
+    perm = r.permutation(31)
+    P = np.zeros((31, 31), dtype=np.float32)
+    P[np.arange(31), perm] = 1.0            # (P B)[i] = B[perm[i]]
+    C, _ = o.gemm_f32(P, B)
+    assert np.array_equal(C, B[perm].astype(np.float64))
+    A = rand_f32((23, 45), 5)
+    perm2 = r.permutation(45)
+    Q = np.zeros((45, 45), dtype=np.float32)
+    Q[perm2, np.arange(45)] = 1.0           # (A Q)[:, j] = A[:, perm2[j]]
+    C, _ = o.gemm_f32(A, Q)
+    assert np.array_equal(C, A[:, perm2].astype(np.float64))
+
+
+def pin_ones(o):
+    M, N, K = 5, 19, 301
+    B = rand_f32((K, N), 6)
+    C, D = o.gemm_f32(np.ones((M, K), dtype=np.float32), B)
+    # every row of C is the column sums of B; math.fsum is correctly rounded
+    colsum = np.array([math.fsum(float(x) for x in B[:, j]) for j in range(N)])
+    colabs = np.array([math.fsum(abs(float(x)) for x in B[:, j]) for j in range(N)])
+    for i in range(M):
+        assert np.all(np.abs(C[i] - colsum) <= K * ULP53 * colabs)
+        assert np.all(np.abs(D[i] - colabs) <= K * ULP53 * colabs)
+    C1, D1 = o.gemm_f32(np.ones((3, 777), np.float32), np.ones((777, 4), np.float32))
+    assert np.all(C1 == 777.0) and np.all(D1 == 777.0)
+
+
+def pin_small_int_f32(o):
+    g = workloads.generator(11)
+    for (M, N, K) in [(33, 65, 129), (7, 300, 1000), (64, 64, 64)]:
+        A = workloads.small_int((M, K), -4, 4, g).numpy()
+        B = workloads.small_int((K, N), -4, 4, g).numpy()
+        C, D = o.gemm_f32(A, B)
+        Ai, Bi = A.astype(np.int64), B.astype(np.int64)
+        assert np.array_equal(C, (Ai @ Bi).astype(np.float64))
+        assert np.array_equal(D, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+
+
+def pin_small_int_bf16(o):
+    g = workloads.generator(12)
+    for (M, N, K) in [(17, 40, 96), (5, 128, 333)]:
+        At = workloads.small_int((M, K), -8, 8, g, torch.bfloat16)
+        Bt = workloads.small_int((K, N), -8, 8, g, torch.bfloat16)
+        C, D = o.gemm_bf16(workloads.bf16_bits(At), workloads.bf16_bits(Bt))
+        Ai = At.to(torch.int64).numpy()
+        Bi = Bt.to(torch.int64).numpy()
+        assert np.array_equal(C, (Ai @ Bi).astype(np.float64))
+        assert np.array_equal(D, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+
+
+def pin_bf16_matches_decoded_f32(o):
+    # torch's bf16 -> fp32 conversion is exact, so the bf16 product must equal
+    # the fp32 product of the converted operands bit for bit.
+    At, Bt = workloads.make_inputs(workloads.Workload("t", 19, 27, 70, "bf16",
+                                                      ("normal", 1.0), ("normal", 1.0)))
+    C, D = o.gemm_bf16(workloads.bf16_bits(At), workloads.bf16_bits(Bt))
+    C2, D2 = o.gemm_f32(At.float().numpy(), Bt.float().numpy())
+    assert np.array_equal(C, C2) and np.array_equal(D, D2)
+
+
+def pin_numpy_blas(o):
+    for (M, N, K), seed in [((256, 256, 256), 7), ((13, 71, 250), 8), ((65, 3, 1000), 9)]:
+        A, B = rand_f32((M, K), seed), rand_f32((K, N), seed + 100)
+        C, D = o.gemm_f32(A, B)
+        ref = A.astype(np.float64) @ B.astype(np.float64)
+        dref = np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64))
+        assert np.all(np.abs(C - ref) <= 1e-12 * dref)
+        assert np.all(np.abs(D - dref) <= 1e-12 * dref)
+
+
+def pin_brute_force(o, shapes):
+    for (M, N, K) in shapes:
+        seed = 1000 * M + 100 * N + K
+        A, B = rand_f32((M, K), seed), rand_f32((K, N), seed + 7)
+        C, D = o.gemm_f32(A, B)
+        Af = [[Fraction(float(x)) for x in row] for row in A]
+        Bf = [[Fraction(float(x)) for x in row] for row in B]
+        for i in range(M):
+            for j in range(N):
+                exact = sum((Af[i][k] * Bf[k][j] for k in range(K)), Fraction(0))
+                mag = sum((abs(Af[i][k] * Bf[k][j]) for k in range(K)), Fraction(0))
+                bound = K * ULP53 * float(mag)
+                assert abs(Fraction(C[i, j]) - exact) <= Fraction(bound) + Fraction(1, 2**1074)
+                assert abs(Fraction(D[i, j]) - mag) <= Fraction(bound) + Fraction(1, 2**1074)
+
+
+PINS = [pin_golden, pin_identity, pin_permutation, pin_ones, pin_small_int_f32,
+        pin_small_int_bf16, pin_bf16_matches_decoded_f32, pin_numpy_blas,
+        lambda o: pin_brute_force(o, [(2, 3, 4), (3, 1, 5), (4, 4, 2)])]
+
+
+# --------------------------------------------------------------------------
+# the tests proper
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.load()
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: getattr(p, "__name__", "brute_small"))
+def test_pin(orc, pin):
+    pin(orc)
+
+
+def test_brute_force_all_tiny_shapes(orc):
+    shapes = [(m, n, k) for m in range(1, 9) for n in range(1, 9) for k in range(1, 9)]
+    pin_brute_force(orc, shapes)
+
+
+def test_brute_force_edge_shapes(orc):
+    pin_brute_force(orc, [(13, 17, 31), (33, 5, 65), (1, 65, 33), (17, 13, 1)])
+
+
+def test_thread_count_invariance(orc):
+    A, B = rand_f32((97, 130), 20), rand_f32((130, 77), 21)
+    C1, D1 = orc.gemm_f32(A, B, threads=1)
+    for t in (2, 3, 8, 200):
+        Ct, Dt = orc.gemm_f32(A, B, threads=t)
+        assert np.array_equal(C1, Ct) and np.array_equal(D1, Dt)
+
+
+def test_rows_subset_matches_full(orc):
+    A, B = rand_f32((50, 40), 22), rand_f32((40, 33), 23)
+    C, D = orc.gemm_f32(A, B)
+    rows = [49, 0, 17, 17, 3]
+    Cr, Dr = orc.gemm_f32(A, B, rows=rows, threads=3)
+    assert np.array_equal(Cr, C[rows]) and np.array_equal(Dr, D[rows])
+    g = workloads.generator(5)
+    Ab = workloads.bf16_bits(workloads.small_int((20, 30), -8, 8, g, torch.bfloat16))
+    Bb = workloads.bf16_bits(workloads.small_int((30, 10), -8, 8, g, torch.bfloat16))
+    Cb, Db = orc.gemm_bf16(Ab, Bb)
+    Cbr, Dbr = orc.gemm_bf16(Ab, Bb, rows=[19, 2])
+    assert np.array_equal(Cbr, Cb[[19, 2]]) and np.array_equal(Dbr, Db[[19, 2]])
+    with pytest.raises(RuntimeError):
+        orc.gemm_f32(A, B, rows=[50])
+
+
+def test_leading_dimensions(orc):
+    # operands that are views into wider buffers (lda > K, ldb > N)
+    Abuf, Bbuf = rand_f32((30, 64), 24), rand_f32((50, 40), 25)
+    A, B = Abuf[:, :50], Bbuf[:, :21]
+    C, D = orc.gemm_f32(A, B)
+    C2, D2 = orc.gemm_f32(np.ascontiguousarray(A), np.ascontiguousarray(B))
+    assert np.array_equal(C, C2) and np.array_equal(D, D2)
+
+
+def test_degenerate_sizes(orc):
+    C, D = orc.gemm_f32(np.zeros((4, 0), np.float32), np.zeros((0, 6), np.float32))
+    assert C.shape == (4, 6) and np.all(C == 0) and np.all(D == 0)
+    C, D = orc.gemm_f32(np.zeros((0, 5), np.float32), np.zeros((5, 6), np.float32))
+    assert C.shape == (0, 6)
+    C, D = orc.gemm_f32(np.ones((3, 5), np.float32), np.zeros((5, 0), np.float32))
+    assert C.shape == (3, 0)
+
+
+def test_bf16_decoder_all_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = orc.decode_bf16(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+    # a few patterns worked by hand from the binary32 layout
+    assert list(orc.decode_bf16(np.array([0x3F80, 0xC000, 0x3F81, 0x0001, 0x8000], np.uint16))) == \
+        [1.0, -2.0, 1.0078125, 2.0 ** -133, -0.0]
+
+
+def test_normalized_error_statistic():
+    cref = np.array([[1.0, 2.0], [0.0, -3.0]])
+    d = np.array([[2.0, 4.0], [0.0, 3.0]])
+    c = cref.copy()
+    assert oracle.normalized_error(c, cref, d)[0] == 0.0
+    c[0, 1] += 1.0                          # error 1 over magnitude 4
+    e, at, n = oracle.normalized_error(c, cref, d)
+    assert e == 0.25 and at == (0, 1) and n == 1
+    c2 = cref.copy(); c2[1, 0] = 1e-30      # D = 0 demands exactly 0
+    assert oracle.normalized_error(c2, cref, d)[0] == math.inf
+    c3 = cref.copy(); c3[1, 1] = np.nan
+    assert oracle.normalized_error(c3, cref, d)[0] == math.inf
+
+
+def test_workload_generator_is_seeded():
+    w = workloads.WORKLOADS["f32_256"]
+    A1, B1 = workloads.make_inputs(w)
+    A2, B2 = workloads.make_inputs(w)
+    assert torch.equal(A1, A2) and torch.equal(B1, B2)
+    assert float(A1.min()) >= -1.0 and float(A1.max()) < 1.0
+    wb = workloads.Workload("b", 64, 64, 64, "bf16", ("normal", 1.0), ("normal", 1.0))
+    Ab, _ = workloads.make_inputs(wb)
+    assert Ab.dtype == torch.bfloat16
+    # bf16 inputs are the fp32 draw rounded to nearest even
+    g = workloads.generator()
+    assert torch.equal(Ab, torch.randn((64, 64), generator=g).to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("mutant", oracle.MUTANTS)
+def test_planted_mutant_fails_a_pin(tmp_path, mutant):
+    """Each planted mistake in the oracle must be caught by at least one pin."""
+    path = oracle.build(str(tmp_path / f"liboracle_{mutant}.so"), mutant=mutant)
+    bad = oracle.Oracle(path)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(bad)
+        except AssertionError:
+            caught.append(getattr(pin, "__name__", "brute_small"))
+    assert caught, f"mutant {mutant} passed every pin"

@@ -1,0 +1,124 @@
+"""Seeded synthetic inputs for the GEMM workloads.
+
+This module is shared by the tests, the smoke check and the benchmark, on both
+sides of the parity check (HIP library and CPU oracle).  It draws operands and
+holds none of the product's arithmetic.
+
+Recipe (every workload): one CPU ``torch.Generator`` seeded with 1234 — the
+seed the hackathon write-up on devpost ("Tools") gives for its synthetic
+tensors — draws A first, then B, in fp32:
+  * ``uniform``   rand * 2 - 1            (i.i.d. on [-1, 1))
+  * ``normal``    randn * sigma
+  * bf16 inputs   the fp32 draw rounded to bf16 (round to nearest even)
+The same bytes are copied to the GPU and handed to the oracle.
+
+Workload sizes come from the pages' subject: square 4096 and 8192 products
+(the kernel ladder of "Bare Metal Bard", page 1, first paragraph), the
+projection shapes of the 10.8M-parameter, 6-layer, d_model 384 character GPT
+of the same page (second paragraph) at 16384 tokens, and skinny or ragged
+shapes that exercise the launch- and bandwidth-bound regimes that the devpost
+write-up ("What we built") routes through a dispatch table.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Tuple
+
+import torch
+
+SEED = 1234
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str                    # "f32" or "bf16" (inputs); output is always fp32
+    dist_a: Tuple[str, float] = ("uniform", 1.0)
+    dist_b: Tuple[str, float] = ("uniform", 1.0)
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Each operand read once and C written once."""
+        s = self.in_bytes
+        return s * (self.M * self.K + self.K * self.N) + 4 * self.M * self.N
+
+
+_ACT = ("normal", 1.0)      # GPT activations
+_WGT = ("normal", 0.02)     # GPT weights
+
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
+    Workload("f32_256", 256, 256, 256, "f32", note="small square; oracle in well under a second"),
+    Workload("f32_4096", 4096, 4096, 4096, "f32", note="square fp32"),
+    Workload("f32_8192", 8192, 8192, 8192, "f32", note="square fp32 at the headline size"),
+    Workload("gpt_qkv", 16384, 1152, 384, "f32", _ACT, _WGT, note="GPT QKV projection"),
+    Workload("gpt_mlp_up", 16384, 1536, 384, "f32", _ACT, _WGT, note="GPT MLP up"),
+    Workload("gpt_mlp_down", 16384, 384, 1536, "f32", _ACT, _WGT, note="GPT MLP down"),
+    Workload("bf16_8192", 8192, 8192, 8192, "bf16", ("normal", 1.0), ("normal", 1.0),
+             note="bf16 in / fp32 accumulate at the headline size"),
+    Workload("skinny_1x8960x1536", 1, 8960, 1536, "f32", note="one-row product (decode-like)"),
+    Workload("skinny_7x4096x4096", 7, 4096, 4096, "f32", note="seven-row product"),
+    Workload("ragged_1000x3000x777", 1000, 3000, 777, "f32", note="ragged, K not a multiple of 4"),
+    Workload("ragged_4097x4095x1023", 4097, 4095, 1023, "f32", note="ragged in every dimension"),
+]}
+
+# Groups of the workload list as the parity tests and the benchmark use them.
+PARITY_WORKLOADS: List[str] = [
+    "f32_256", "f32_4096", "gpt_qkv", "gpt_mlp_up", "gpt_mlp_down", "bf16_8192",
+    "skinny_1x8960x1536", "skinny_7x4096x4096", "ragged_1000x3000x777",
+    "ragged_4097x4095x1023", "f32_8192",
+]
+
+
+def generator(seed: int = SEED) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return g
+
+
+def draw(shape, dist: Tuple[str, float], g: torch.Generator) -> torch.Tensor:
+    kind, scale = dist
+    if kind == "uniform":
+        return torch.rand(shape, generator=g, dtype=torch.float32) * 2.0 - 1.0
+    if kind == "normal":
+        return torch.randn(shape, generator=g, dtype=torch.float32) * scale
+    raise ValueError(f"unknown distribution {kind!r}")
+
+
+def make_inputs(w: Workload, seed: int = SEED) -> Tuple[torch.Tensor, torch.Tensor]:
+    """CPU tensors (A, B): fp32, or bf16 rounded from the fp32 draw."""
+    g = generator(seed)
+    A = draw((w.M, w.K), w.dist_a, g)
+    B = draw((w.K, w.N), w.dist_b, g)
+    if w.dtype == "bf16":
+        A, B = A.to(torch.bfloat16), B.to(torch.bfloat16)
+    return A, B
+
+
+def small_int(shape, lo: int, hi: int, g: torch.Generator, dtype=torch.float32) -> torch.Tensor:
+    """Integer-valued entries in [lo, hi], exactly representable in fp32/bf16."""
+    return torch.randint(lo, hi + 1, shape, generator=g).to(dtype)
+
+
+def bf16_bits(t: torch.Tensor):
+    """Raw bf16 patterns of a CPU bf16 tensor as a numpy uint16 array."""
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def as_numpy_operand(t: torch.Tensor):
+    """numpy view of a CPU operand in the form the oracle takes."""
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.contiguous().numpy()
