@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Throughput of libmi355gemm on one MI355X: GFLOP/s (2MNK/t) at 8192^3.
+
+One step = one fp32 GEMM and one bf16-in / fp32-accumulate GEMM, both
+8192 x 8192 x 8192 row-major, through the C-ABI on torch's current stream,
+with operands resident in HBM before timing starts.  `value` is the step's
+total flops over its time.  Each GEMM is also bracketed by HIP events, which
+give the per-kernel average durations used for the roofline fractions.
+
+Prints exactly one JSON line.  Extra legs:
+  --cpu-baseline (default on): the CPU oracle on a bounded sample of the same
+      workload (a few rows of each product) on this host's cores.
+  --copy-calibration: also runs a plain device copy of known size, so that
+      hardware byte counters (FETCH_SIZE / WRITE_SIZE) read under a profiler
+      can be scaled against it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}     # MI355X dense, per dtype
+HBM_PEAK_GBS = 8000.0
+METRIC = "GFLOP/s (2MNK/t) fp32 & bf16 GEMM at 8192³; % of MI355X dtype peak"
+STEP_WORKLOADS = ("f32_8192", "bf16_8192")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workloads", default=",".join(STEP_WORKLOADS),
+                   help="comma-separated workload names making up one step")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target length of the CPU-baseline sample")
+    p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--check-rows", type=int, default=8,
+                   help="rows per product checked against the oracle after timing")
+    return p.parse_args()
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit():
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import dense_gemm_17_amd as g   # fails loudly if the HIP library is missing
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names = [n for n in args.workloads.split(",") if n]
+    ws = [workloads.WORKLOADS[n] for n in names]
+
+    host = {}
+    ops = []
+    for w in ws:
+        A, B = workloads.make_inputs(w)
+        host[w.name] = (A, B)
+        Ad, Bd = A.to(dev), B.to(dev)
+        Cd = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+        ops.append((w, Ad, Bd, Cd))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        for i, (w, Ad, Bd, Cd) in enumerate(ops):
+            if evs is not None:
+                evs[i][0].record(stream)
+            g.gemm(Ad, Bd, out=Cd)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kernel_of = {w.name: g.gemm_kernel_name(g.gemm_plan(
+        g.F32 if w.dtype == "f32" else g.BF16, w.M, w.N, w.K,
+        Ad.data_ptr(), Ad.stride(0), Bd.data_ptr(), Bd.stride(0), Cd.data_ptr(), Cd.stride(0)))
+        for (w, Ad, Bd, Cd) in ops}
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {}
+    for i, (w, *_rest) in enumerate(ops):
+        ms = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        avg = float(np.mean(ms))
+        tflops = w.flops / (avg * 1e-3) / 1e12
+        per[w.name] = {
+            "kernel": kernel_of[w.name], "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype,
+            "avg_ms": round(avg, 4), "min_ms": round(float(np.min(ms)), 4),
+            "max_ms": round(float(np.max(ms)), 4),
+            "tflops": round(tflops, 2), "frac_peak": round(tflops / PEAK_TFLOPS[w.dtype], 4),
+        }
+
+    total_flops = sum(w.flops for w in ws)
+    ms_per_step = wall * 1e3 / args.steps
+    value = total_flops / (wall / args.steps) / 1e9
+
+    # correctness of what was timed: a few rows against the oracle
+    check = {}
+    cpu = None
+    import oracle
+    rng = np.random.default_rng(0)
+    for (w, Ad, Bd, Cd) in ops:
+        A, B = host[w.name]
+        rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, args.check_rows),
+                                                     replace=False).tolist()))
+        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        Cref, D = fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B), rows=rows,
+                     threads=cpu_threads())
+        e, _, _ = oracle.normalized_error(Cd[rows].cpu().numpy(), Cref, D)
+        check[w.name] = float(f"{e:.3e}")
+
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(ws, host, args.cpu_seconds)
+
+    copy = None
+    if args.copy_calibration:
+        copy = copy_calibration(dev)
+
+    dom = max(per.values(), key=lambda r: r["avg_ms"])
+    dom_w = next(w for w in ws if per[w.name] is dom)
+    roofline = {
+        "bound": "mfma", "kernel": dom["kernel"], "workload": dom_w.name,
+        "achieved": dom["tflops"], "peak": PEAK_TFLOPS[dom_w.dtype], "unit": "TFLOP/s",
+        "frac": dom["frac_peak"], "traffic": None,
+    }
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "+".join(sorted({"f32" if w.dtype == "f32" else "bf16" for w in ws})),
+        "data": "synthetic (seed 1234; fp32 uniform[-1,1], bf16 from N(0,1))",
+        "config": {"workload": "+".join(names),
+                   "shapes": {w.name: [w.M, w.N, w.K] for w in ws}},
+        "per_kernel": per, "max_norm_err_sampled": check,
+        "roofline": roofline,
+        "roofline_by_kernel": {n: {"bound": "mfma", "achieved": r["tflops"],
+                                   "peak": PEAK_TFLOPS[r["dtype"]], "unit": "TFLOP/s",
+                                   "frac": r["frac_peak"]} for n, r in per.items()},
+        "cpu_baseline": cpu,
+    }
+    if copy is not None:
+        line["copy_calibration"] = copy
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(ws, host, seconds):
+    """The oracle, as it stands, on a bounded sample: the first R rows of each
+    product of the step, R sized from a short calibration run."""
+    import oracle
+    th = cpu_threads()
+    probe_rows = max(1, th)
+    t0 = time.perf_counter()
+    for w in ws:
+        A, B = host[w.name]
+        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B),
+           rows=list(range(min(probe_rows, w.M))), threads=th)
+    t_probe = time.perf_counter() - t0
+    rows = max(probe_rows, int(probe_rows * seconds / max(t_probe, 1e-3)) // th * th)
+    flops = 0
+    t0 = time.perf_counter()
+    for w in ws:
+        A, B = host[w.name]
+        r = min(rows, w.M)
+        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B),
+           rows=list(range(r)), threads=th)
+        flops += 2 * r * w.N * w.K
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": th,
+            "kind": "oracle",
+            "sample": f"first {rows} rows of each product of the step "
+                      f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 accumulation)"}
+
+
+def copy_calibration(dev):
+    """A plain device-to-device copy of 256 MiB, timed, for counter scaling."""
+    n = 64 * 1024 * 1024
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 3}
+
+
+if __name__ == "__main__":
+    main()

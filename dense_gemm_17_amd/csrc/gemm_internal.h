@@ -1,0 +1,50 @@
+// Internal declarations shared by the kernel files and the C-ABI layer.
+// Not installed; the public interface is include/mi355gemm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355gemm {
+
+enum Dtype : int { kF32 = 0, kBF16 = 1 };
+
+// Arguments of one product after validation.  Pointers are device pointers;
+// A and B are `const void*` so one signature serves both element types.
+struct Problem {
+    int64_t M, N, K;
+    const void *A; int64_t lda;
+    const void *B; int64_t ldb;
+    float *C; int64_t ldc;
+    int dtype;
+};
+
+// A launcher enqueues its kernel(s) for `p` on `stream` and returns the
+// launch status.  It may assume p passed validation and its `supports` test.
+using LaunchFn = hipError_t (*)(const Problem &p, hipStream_t stream);
+using SupportsFn = bool (*)(const Problem &p);
+
+struct KernelInfo {
+    const char *name;
+    int dtype;
+    LaunchFn launch;
+    SupportsFn supports;   // shapes / alignments this kernel can take
+};
+
+// ---- per-family launchers (defined in the kernel files) -------------------
+hipError_t launch_naive_f32(const Problem &p, hipStream_t s);
+hipError_t launch_naive_bf16(const Problem &p, hipStream_t s);
+hipError_t launch_fill_zero(const Problem &p, hipStream_t s);
+hipError_t launch_valu_f32(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f32(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_bf16(const Problem &p, hipStream_t s);
+hipError_t launch_skinny_f32(const Problem &p, hipStream_t s);
+hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s);
+
+// Largest M the skinny (bandwidth) family takes.
+constexpr int64_t kSkinnyMaxM = 16;
+
+// 1-D grids only: gridDim.x is the sole dimension with a 2^31 - 1 limit.
+constexpr int64_t kMaxBlocks = 2147483647LL;
+
+}  // namespace mi355gemm

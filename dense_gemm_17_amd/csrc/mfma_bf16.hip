@@ -1,0 +1,244 @@
+// bf16-in / fp32-accumulate matrix-core family: v_mfma_f32_32x32x16_bf16.
+//
+// The matrix-instruction rung of the kernel ladder ("Bare Metal Bard", page
+// 1, first paragraph) with bf16 operands (vidyal.ai Part 6, "Tensor Cores":
+// what one instruction computes, feeding it from shared memory without bank
+// conflicts, and what BF16 costs in accuracy).  A bf16 x bf16 product is
+// exact in fp32, so the only rounding is the fp32 accumulation.
+//
+//   * block tile 256 x 256, K step 64; 4 wave64s in a 2 x 2 grid, each
+//     owning 128 x 128 of C as 4 x 4 MFMA blocks of 32 x 32 (256 fp32
+//     accumulators per lane);
+//   * global -> registers with 128-bit loads (8 bf16), registers -> LDS
+//     after the current tile's math, two LDS stages, one barrier per step;
+//   * A operand: lane (h, c) needs row c of a 32-row block and k = 8h..8h+7
+//     of a 16-wide K slice, which is one 16-byte chunk of a row-major A tile
+//     (ds_read_b128).  The eight chunks of each LDS row are XOR-permuted by a
+//     row hash so that the rows of one read land in distinct banks;
+//   * B operand: lane (h, c) needs column c and the same eight k.  B is
+//     row-major (columns contiguous), so it stays that way in LDS and is read
+//     with gfx950's transposing LDS load (ds_read_b64_tr_b16): in each group
+//     of 16 lanes, lane s points at 4 consecutive columns of row s/4 and the
+//     hardware hands lane i the column i of those four rows.  Two such reads
+//     give the eight k.  The 16-byte chunks of each B row are XOR-permuted by
+//     (row mod 4) so the four rows of one read fall in distinct banks;
+//   * ragged edges: rows past M, columns past N and k past K load as zeros;
+//     C is stored with row and column masks.
+#include "gemm_internal.h"
+#include "tile_map.h"
+
+namespace mi355gemm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 256;
+constexpr int kAChunks = BM * BK / 8 / kThreads;   // 8
+constexpr int kBChunks = BK * BN / 8 / kThreads;   // 8
+constexpr int kGroup = 4;
+
+// A rows hold 8 chunks; see the fp32 family for the property of this hash.
+__device__ __forceinline__ int a_swz(int row) { return (row + (row >> 3)) & 7; }
+
+// B rows hold 32 chunks.  A transposing read by 16 lanes touches two
+// adjacent chunks of four consecutive rows; a half-wave touches four
+// adjacent chunks of the same rows.  XOR masks {0, 4, 10, 14} for row mod 4
+// put both sets in distinct bank slots (8 slots of 16 bytes and 16 slots of
+// 16 bytes respectively).
+__device__ __forceinline__ int b_swz(int row)
+{
+    const int r = row & 3;
+    return ((r >> 1) << 1) | ((r & 1) << 2) | ((r >> 1) << 3);
+}
+
+struct Frag {
+    u16x8 a[kAChunks];
+    u16x8 b[kBChunks];
+};
+
+template <bool kVec>
+__device__ __forceinline__ u16x8 load8(const uint16_t *__restrict__ base, int64_t ld, int64_t row,
+                                       int64_t col, int64_t rows, int64_t cols, bool full)
+{
+    if (kVec && full) return *reinterpret_cast<const u16x8 *>(base + row * ld + col);
+    u16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (row < rows) {
+        const uint16_t *p = base + row * ld;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col + e < cols) v[e] = p[col + e];
+    }
+    return v;
+}
+
+template <bool kVec>
+__device__ __forceinline__ void load_tile(Frag &f, const uint16_t *__restrict__ A, int64_t lda,
+                                          const uint16_t *__restrict__ B, int64_t ldb, int64_t M,
+                                          int64_t N, int64_t K, int64_t m0, int64_t n0, int64_t k0,
+                                          bool a_full, bool b_full)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+        const int p = tid + kThreads * i;
+        const int row = p >> 3, c = p & 7;
+        f.a[i] = load8<kVec>(A, lda, m0 + row, k0 + 8 * c, M, K, a_full);
+    }
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i) {
+        const int p = tid + kThreads * i;
+        const int row = p >> 5, c = p & 31;
+        f.b[i] = load8<kVec>(B, ldb, k0 + row, n0 + 8 * c, K, N, b_full);
+    }
+}
+
+__device__ __forceinline__ void store_tile(const Frag &f, uint16_t *As, uint16_t *Bs)
+{
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < kAChunks; ++i) {
+        const int p = tid + kThreads * i;
+        const int row = p >> 3, c = p & 7;
+        *reinterpret_cast<u16x8 *>(As + row * BK + ((c ^ a_swz(row)) << 3)) = f.a[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i) {
+        const int p = tid + kThreads * i;
+        const int row = p >> 5, c = p & 31;
+        *reinterpret_cast<u16x8 *>(Bs + row * BN + ((c ^ b_swz(row)) << 3)) = f.b[i];
+    }
+}
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 read_tr(const uint16_t *lds_elem)
+{
+    auto p = (lds_bf16x4 *)((__attribute__((address_space(3))) uint16_t *)(lds_elem));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
+}
+
+__device__ __forceinline__ void compute_tile(f32x16 (&acc)[4][4], const uint16_t *As,
+                                             const uint16_t *Bs, int wm, int wn, int lane)
+{
+    const int h = lane >> 5, c = lane & 31;
+    const int i = lane & 15, nhalf = (lane >> 4) & 1;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+        bf16x8 a[4], b[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            const int row = wm * 128 + mb * 32 + c;
+            const u16x8 v =
+                *reinterpret_cast<const u16x8 *>(As + row * BK + (((2 * s + h) ^ a_swz(row)) << 3));
+            a[mb] = __builtin_bit_cast(bf16x8, v);
+        }
+        const int k_lo = 16 * s + 8 * h + (i >> 2);   // row of the first read; +4 for the second
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int n = wn * 128 + nb * 32 + nhalf * 16 + 4 * (i & 3);
+            const int chunk = n >> 3, within = n & 7;
+            const int sw = b_swz(k_lo);                  // same for k_lo + 4
+            const uint16_t *p0 = Bs + k_lo * BN + ((chunk ^ sw) << 3) + within;
+            const uint16_t *p1 = p0 + 4 * BN;
+            const bf16x4 lo = read_tr(p0), hi = read_tr(p1);
+            b[nb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb],
+                                                                       0, 0, 0);
+    }
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A, int64_t lda,
+                      const uint16_t *__restrict__ B, int64_t ldb, float *__restrict__ C,
+                      int64_t ldc, int64_t tiles_m, int64_t tiles_n)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BK * BN];
+
+    const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const bool a_rows_full = m0 + BM <= M;
+    const bool b_cols_full = n0 + BN <= N;
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int64_t ktiles = (K + BK - 1) / BK;
+    Frag f;
+    load_tile<kVec>(f, A, lda, B, ldb, M, N, K, m0, n0, 0, a_rows_full && BK <= K,
+                    b_cols_full && BK <= K);
+    store_tile(f, As[0], Bs[0]);
+    __syncthreads();
+
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < ktiles;
+        if (more) {
+            const int64_t k0 = (kt + 1) * BK;
+            const bool kfull = k0 + BK <= K;
+            load_tile<kVec>(f, A, lda, B, ldb, M, N, K, m0, n0, k0, a_rows_full && kfull,
+                            b_cols_full && kfull);
+        }
+        compute_tile(acc, As[cur], Bs[cur], wm, wn, lane);
+        if (more) store_tile(f, As[cur ^ 1], Bs[cur ^ 1]);
+        __syncthreads();
+    }
+
+    // Epilogue: register r of block (mb, nb) in lane (h, c) is C row
+    // 8*(r/4) + 4*h + r%4, column c of that 32 x 32 block.
+    const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int64_t col = n0 + wn * 128 + nb * 32 + c;
+            if (col >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < M) C[row * ldc + col] = acc[mb][nb][r];
+            }
+        }
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+hipError_t launch_mfma_bf16(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
+    if (tm * tn > kMaxBlocks) return hipErrorInvalidValue;
+    const bool vec = aligned16(p.A) && aligned16(p.B) && p.lda % 8 == 0 && p.ldb % 8 == 0;
+    const auto *A = static_cast<const uint16_t *>(p.A);
+    const auto *B = static_cast<const uint16_t *>(p.B);
+    if (vec)
+        hipLaunchKernelGGL(mfma_bf16_kernel<true>, dim3(static_cast<uint32_t>(tm * tn)),
+                           dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm,
+                           tn);
+    else
+        hipLaunchKernelGGL(mfma_bf16_kernel<false>, dim3(static_cast<uint32_t>(tm * tn)),
+                           dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm,
+                           tn);
+    return hipGetLastError();
+}
+
+}  // namespace mi355gemm

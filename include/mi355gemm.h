@@ -1,0 +1,118 @@
+/*
+ * mi355gemm — dense matrix multiply C = A·B for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the plain matrix product that the pages build a ladder of
+ * kernels for ("Bare Metal Bard", page 1, first paragraph: naive, coalesced,
+ * shared-memory tiled, register tiled, vector loads, warp blocked, double
+ * buffered, matrix-instruction kernels; vidyal.ai Part 5 "Writing a Fast
+ * Matmul in CUDA, Step by Step"):
+ *
+ *     C[i][j] = sum_{k < K} A[i][k] * B[k][j]      0 <= i < M, 0 <= j < N
+ *
+ * The call model is the one vidyal.ai Part 1 ("From torch.matmul to Silicon")
+ * follows: the host call validates, picks a kernel and enqueues it on a
+ * stream, then returns without waiting.
+ *
+ * Layout: all three matrices are row-major with a leading dimension (the
+ * distance, in elements, between the starts of consecutive rows):
+ *     A is M x K, element (i,k) at A[i*lda + k], lda >= K
+ *     B is K x N, element (k,j) at B[k*ldb + j], ldb >= N
+ *     C is M x N, element (i,j) at C[i*ldc + j], ldc >= N
+ * C is overwritten (there is no alpha/beta and no transpose option).  Entries
+ * of C's rows beyond column N-1 (the padding up to ldc) are never written.
+ *
+ * Precision: gemm_f32 multiplies fp32 operands and accumulates in fp32;
+ * gemm_bf16_f32acc takes bf16 operands (raw 16-bit patterns, the upper half
+ * of an IEEE binary32) and accumulates in fp32.  Output is fp32 for both.
+ * The summation order is the kernel's; every result satisfies
+ *     max_ij |c_ij - C_ij| / sum_k |A_ik B_kj| <= 5e-4
+ * against the exact product, and each kernel is deterministic (same inputs,
+ * same launch -> same bits; no atomics).
+ *
+ * Ownership: A, B and C are device memory owned by the caller (for example
+ * PyTorch tensors on the current device).  The library never allocates,
+ * frees, copies to or from the host, or synchronises.  A and B must stay
+ * valid, and C must not be read, until `stream` has passed the kernel.
+ *
+ * Errors (the return value is a hipError_t value cast to int):
+ *   0 (hipSuccess)          enqueued (or nothing to do)
+ *   hipErrorInvalidValue    negative or too large dimension, a leading
+ *                           dimension below the row width, a null pointer
+ *                           for a non-empty operand, or C overlapping A or B;
+ *                           nothing is launched
+ *   anything else           the launch error reported by the HIP runtime
+ * M == 0 or N == 0 is a no-op.  K == 0 writes C = 0 (the empty sum).
+ * Dimensions are limited to 2^31 - 1.  The functions never print or abort.
+ *
+ * Thread safety: calls from several host threads are safe; kernel selection
+ * is a pure function of the arguments unless gemm_force_kernel is in effect.
+ */
+#ifndef MI355GEMM_H
+#define MI355GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* C = A·B with fp32 operands, fp32 accumulation, fp32 output. */
+int gemm_f32(int64_t M, int64_t N, int64_t K,
+             const float *A, int64_t lda,
+             const float *B, int64_t ldb,
+             float *C, int64_t ldc,
+             hipStream_t stream);
+
+/* C = A·B with bf16 operands (raw patterns), fp32 accumulation and output. */
+int gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K,
+                     const uint16_t *A, int64_t lda,
+                     const uint16_t *B, int64_t ldb,
+                     float *C, int64_t ldc,
+                     hipStream_t stream);
+
+/* ---- introspection and test hooks (not needed by ordinary callers) -------
+ *
+ * Kernel selection follows the regime classification of the devpost write-up
+ * ("What we built": classify each shape as launch-, bandwidth- or
+ * compute-bound, then route it through a small fixed dispatch table).
+ */
+
+/* Element type codes for gemm_plan. */
+#define MI355GEMM_F32  0
+#define MI355GEMM_BF16 1
+
+/* Number of kernels in the library; ids are 0 .. count-1. */
+int gemm_kernel_count(void);
+
+/* Static name of kernel `id` ("?" for an unknown id); never freed. */
+const char *gemm_kernel_name(int id);
+
+/* Element type (MI355GEMM_F32 / MI355GEMM_BF16) kernel `id` computes, or -1. */
+int gemm_kernel_dtype(int id);
+
+/* The kernel id the dispatch table picks for these arguments, without
+ * launching anything and without any HIP call (pure host function).  Pointer
+ * values matter only through their alignment.  Returns -1 for arguments the
+ * entry points would reject, and -2 when there is nothing to launch
+ * (M == 0 or N == 0) and -3 when only C = 0 is written (K == 0). */
+int gemm_plan(int dtype, int64_t M, int64_t N, int64_t K,
+              uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
+              uintptr_t C, int64_t ldc);
+
+/* Process-wide override for tests: every later call uses kernel `id` when it
+ * computes that call's element type (other calls keep the table's choice);
+ * -1 restores the table.  Returns hipErrorInvalidValue for an unknown id.
+ * A forced kernel that cannot take a given shape makes that call return
+ * hipErrorInvalidValue without launching. */
+int gemm_force_kernel(int id);
+
+/* Kernel id used by the most recent successful launch in this process
+ * (-1 before any). */
+int gemm_last_kernel(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355GEMM_H */

@@ -1,0 +1,124 @@
+"""Host-side checks of the C-ABI library; no GPU and no kernel launch.
+
+The library must load on a machine without a GPU, export every symbol the
+public header declares, reject invalid arguments before touching the HIP
+runtime, and pick kernels through a dispatch table that is a pure function of
+shape, element type and alignment (the devpost write-up, "What we built":
+regimes classified up front, then routed by a fixed table).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_gemm_17_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
+INVALID = g.HIP_ERROR_INVALID_VALUE
+
+# distinct, well-aligned fake device addresses (only their values matter)
+PA, PB, PC = 1 << 40, 2 << 40, 3 << 40
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_exactly_the_exports():
+    assert header_functions() == set(g.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(g.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_kernel_registry():
+    n = g.gemm_kernel_count()
+    assert n >= 2
+    names = g.kernel_names()
+    assert len(set(names)) == n
+    for i in range(n):
+        assert g.gemm_kernel_dtype(i) in (g.F32, g.BF16)
+    assert g.gemm_kernel_name(-1) == "?" and g.gemm_kernel_name(n) == "?"
+    assert g.gemm_kernel_dtype(n) == -1
+    assert {g.gemm_kernel_dtype(i) for i in range(n)} == {g.F32, g.BF16}
+
+
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+def test_plan_rejects_invalid_arguments(dtype):
+    ok = dict(A=PA, B=PB, C=PC)
+    assert g.gemm_plan(dtype, 64, 64, 64, **ok) >= 0
+    assert g.gemm_plan(dtype, -1, 64, 64, **ok) == -1
+    assert g.gemm_plan(dtype, 64, -1, 64, **ok) == -1
+    assert g.gemm_plan(dtype, 64, 64, -1, **ok) == -1
+    assert g.gemm_plan(dtype, 2 ** 31, 64, 64, **ok) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, lda=63, **ok) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, ldb=63, **ok) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, ldc=63, **ok) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, A=0, B=PB, C=PC) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, A=PA, B=0, C=PC) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, A=PA, B=PB, C=0) == -1
+    # C overlapping A or B
+    assert g.gemm_plan(dtype, 64, 64, 64, A=PA, B=PB, C=PA + 64) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, A=PA, B=PB, C=PB - 4) == -1
+    # C ending exactly where A starts does not overlap
+    assert g.gemm_plan(dtype, 64, 64, 64, A=PA, B=PB, C=PA - 64 * 64 * 4) >= 0
+    # misaligned element pointers
+    assert g.gemm_plan(dtype, 64, 64, 64, A=PA + 1, B=PB, C=PC) == -1
+    assert g.gemm_plan(dtype, 64, 64, 64, A=PA, B=PB, C=PC + 2) == -1
+    # unknown element type
+    assert g.gemm_plan(7, 64, 64, 64, **ok) == -1
+
+
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+def test_plan_degenerate_sizes(dtype):
+    assert g.gemm_plan(dtype, 0, 64, 64, A=0, B=0, C=0) == -2
+    assert g.gemm_plan(dtype, 64, 0, 64, A=0, B=0, C=0) == -2
+    assert g.gemm_plan(dtype, 64, 64, 0, A=0, B=0, C=PC) == -3
+    assert g.gemm_plan(dtype, 64, 64, 0, A=0, B=0, C=0) == -1
+
+
+def test_entry_points_validate_before_any_hip_call():
+    # Invalid calls return hipErrorInvalidValue and M == 0 returns success;
+    # neither reaches the HIP runtime, so this runs without a GPU.
+    for fn in (g.gemm_f32, g.gemm_bf16_f32acc):
+        assert fn(-1, 4, 4, PA, 4, PB, 4, PC, 4, None) == INVALID
+        assert fn(4, 4, 4, 0, 4, PB, 4, PC, 4, None) == INVALID
+        assert fn(4, 4, 4, PA, 3, PB, 4, PC, 4, None) == INVALID
+        assert fn(4, 4, 4, PA, 4, PB, 4, PA, 4, None) == INVALID
+        assert fn(0, 4, 4, 0, 4, 0, 4, 0, 4, None) == 0
+        assert fn(4, 0, 4, 0, 4, 0, 4, 0, 4, None) == 0
+
+
+def test_force_kernel_bounds():
+    n = g.gemm_kernel_count()
+    assert g.gemm_force_kernel(-2) == INVALID
+    assert g.gemm_force_kernel(n) == INVALID
+    assert g.gemm_force_kernel(-1) == 0
+
+
+def test_force_kernel_applies_only_to_its_dtype():
+    f32_naive, bf16_naive = g.kernel_id("naive_f32"), g.kernel_id("naive_bf16")
+    try:
+        assert g.gemm_force_kernel(f32_naive) == 0
+        assert g.gemm_plan(g.F32, 4096, 4096, 4096, A=PA, B=PB, C=PC) == f32_naive
+        table_bf16 = g.gemm_plan(g.BF16, 4096, 4096, 4096, A=PA, B=PB, C=PC)
+        assert g.gemm_kernel_dtype(table_bf16) == g.BF16
+        assert g.gemm_force_kernel(bf16_naive) == 0
+        assert g.gemm_plan(g.BF16, 4096, 4096, 4096, A=PA, B=PB, C=PC) == bf16_naive
+    finally:
+        g.gemm_force_kernel(-1)
+
+
+def test_plan_is_pure():
+    a = [g.gemm_plan(g.F32, m, n, k, A=PA, B=PB, C=PC)
+         for (m, n, k) in [(1, 8960, 1536), (4096, 4096, 4096), (1000, 3000, 777)]]
+    b = [g.gemm_plan(g.F32, m, n, k, A=PA, B=PB, C=PC)
+         for (m, n, k) in [(1, 8960, 1536), (4096, 4096, 4096), (1000, 3000, 777)]]
+    assert a == b

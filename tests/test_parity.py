@@ -1,0 +1,250 @@
+"""GPU parity: every kernel of the library against the CPU oracle.
+
+The gate is the normalized error max_ij |c - C| / sum_k |a_ik b_kj| <= 5e-4
+for both element types.  Because that gate is loose (at K = 8192 it sits
+just above the worst-case bound of any fp32 summation order), the kernels are
+also held to exact results where exactness is available: small-integer
+operands (every partial sum is an integer below 2^24, so any order is exact),
+identity and permutation operands.  Each kernel is forced through the
+library's test hook, so every family is checked on every shape it can take,
+and the table's own choice is checked in the launch configuration the
+benchmark times.  Calls go through the C-ABI (the Python binding only passes
+pointers).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_17_amd as g
+import oracle
+import workloads
+from workloads import WORKLOADS, Workload
+
+pytestmark = pytest.mark.gpu
+GATE = oracle.GATE
+DEV = "cuda:0"
+
+# Full oracle below this many multiply-adds; sampled rows above it.
+FULL_ORACLE_LIMIT = 2.0e10
+SAMPLE_ROWS = 48
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def kernels_for(dtype):
+    code = g.F32 if dtype == "f32" else g.BF16
+    return [n for n in g.kernel_names() if g.gemm_kernel_dtype(g.kernel_id(n)) == code]
+
+
+def supports(name, M, N, K):
+    if name.startswith("skinny"):
+        return M <= 16
+    return True
+
+
+class Forced:
+    def __init__(self, name):
+        self.kid = g.kernel_id(name) if name else -1
+
+    def __enter__(self):
+        assert g.gemm_force_kernel(self.kid) == 0
+
+    def __exit__(self, *exc):
+        g.gemm_force_kernel(-1)
+
+
+def run(A, B, kernel=None, out=None):
+    with Forced(kernel):
+        C = g.gemm(A, B, out=out)
+    torch.cuda.synchronize()
+    if kernel:
+        assert g.gemm_last_kernel() == g.kernel_id(kernel)
+    return C
+
+
+# ---------------------------------------------------------------- oracle cache
+_cache = {}
+
+
+def sample_rows(M, seed=0):
+    r = np.random.default_rng(seed)
+    fixed = [0, 1, M - 1, M // 2]
+    for t in (31, 32, 63, 64, 127, 128, 255, 256):
+        fixed += [t, M - 1 - t]
+    rnd = r.choice(M, size=min(M, SAMPLE_ROWS), replace=False).tolist()
+    return sorted({x for x in fixed + rnd if 0 <= x < M})
+
+
+def reference(w: Workload):
+    """(A, B) on the CPU, rows checked and (C_ref, D) for those rows."""
+    if w.name not in _cache:
+        A, B = workloads.make_inputs(w)
+        An, Bn = workloads.as_numpy_operand(A), workloads.as_numpy_operand(B)
+        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        if w.M * w.N * w.K <= FULL_ORACLE_LIMIT:
+            rows = None
+            C, D = fn(An, Bn)
+        else:
+            rows = sample_rows(w.M)
+            C, D = fn(An, Bn, rows=rows)
+        _cache[w.name] = (A, B, rows, C, D)
+    return _cache[w.name]
+
+
+def check(w: Workload, kernel):
+    A, B, rows, Cref, D = reference(w)
+    say(f"[parity] {w.name} kernel={kernel or 'table'} rows={'all' if rows is None else len(rows)}")
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    C = run(Ad, Bd, kernel)
+    C2 = run(Ad, Bd, kernel)
+    assert torch.equal(C, C2), "kernel is not deterministic"
+    Ch = C.cpu().numpy()
+    if rows is not None:
+        Ch = Ch[rows]
+    e, at, n = oracle.normalized_error(Ch, Cref, D)
+    say(f"[parity] {w.name} kernel={kernel or g.gemm_kernel_name(g.gemm_last_kernel())} "
+        f"e={e:.3e} at={at} n>1e-5={n}")
+    assert e <= GATE, f"normalized error {e} at {at}"
+    return e
+
+
+# -------------------------------------------------------------------- tests
+
+SMALL_WORKLOADS = ["f32_256", "gpt_qkv", "gpt_mlp_up", "gpt_mlp_down", "skinny_1x8960x1536",
+                   "skinny_7x4096x4096", "ragged_1000x3000x777", "ragged_4097x4095x1023"]
+LARGE_WORKLOADS = ["f32_4096", "f32_8192", "bf16_8192"]
+
+
+def kernel_workload_cases():
+    cases = []
+    for wn in SMALL_WORKLOADS + LARGE_WORKLOADS:
+        w = WORKLOADS[wn]
+        for k in kernels_for(w.dtype):
+            if not supports(k, w.M, w.N, w.K):
+                continue
+            if k.startswith("naive") and wn in LARGE_WORKLOADS:
+                continue   # the debug kernel is only run on the smaller shapes
+            cases.append((wn, k))
+    return cases
+
+
+@pytest.mark.parametrize("wn", SMALL_WORKLOADS + LARGE_WORKLOADS)
+def test_table_choice_matches_oracle(wn):
+    check(WORKLOADS[wn], None)
+
+
+@pytest.mark.parametrize("wn,kernel", kernel_workload_cases())
+def test_kernel_matches_oracle(wn, kernel):
+    check(WORKLOADS[wn], kernel)
+
+
+EXACT_SHAPES = [(1, 1, 1), (3, 5, 7), (64, 64, 64), (65, 63, 67), (256, 256, 512),
+                (257, 383, 129), (300, 520, 200), (1, 8960, 96), (7, 1000, 300),
+                (513, 17, 1025), (17, 513, 33), (128, 256, 4100)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_small_integer_exact(dtype):
+    """Integer operands: every kernel must be exact (bitwise equal to int64)."""
+    gen = workloads.generator(77)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
+    for (M, N, K) in EXACT_SHAPES:
+        A = workloads.small_int((M, K), lo, hi, gen, tdt)
+        B = workloads.small_int((K, N), lo, hi, gen, tdt)
+        exact = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float64).numpy()
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        for k in kernels_for(dtype):
+            if not supports(k, M, N, K):
+                continue
+            say(f"[exact] {dtype} {M}x{N}x{K} kernel={k}")
+            C = run(Ad, Bd, k).cpu().numpy().astype(np.float64)
+            bad = np.argwhere(C != exact)
+            assert bad.size == 0, f"{k} {M}x{N}x{K}: {len(bad)} wrong, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_identity_and_permutation_exact(dtype):
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    gen = workloads.generator(78)
+    K, N = 300, 260
+    B = workloads.draw((K, N), ("uniform", 1.0), gen).to(tdt)
+    perm = torch.randperm(K, generator=gen)
+    P = torch.zeros((K, K), dtype=tdt)
+    P[torch.arange(K), perm] = 1
+    Bd = B.to(DEV)
+    for k in kernels_for(dtype):
+        if not supports(k, K, N, K):
+            continue
+        say(f"[identity] {dtype} kernel={k}")
+        C = run(torch.eye(K, dtype=tdt, device=DEV), Bd, k)
+        assert torch.equal(C.cpu(), B.float())
+        C = run(P.to(DEV), Bd, k)
+        assert torch.equal(C.cpu(), B.float()[perm])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_guard_bands_and_poisoned_padding(dtype):
+    """Padding of A/B rows holds NaN and must not leak; C padding and the rows
+    past M must keep their sentinel."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    gen = workloads.generator(79)
+    for (M, N, K) in [(130, 200, 150), (5, 300, 64), (300, 257, 1000)]:
+        A = workloads.small_int((M, K), -4, 4, gen, tdt)
+        B = workloads.small_int((K, N), -4, 4, gen, tdt)
+        exact = (A.to(torch.int64) @ B.to(torch.int64)).float()
+        Abuf = torch.full((M, K + 13), float("nan"), dtype=tdt)
+        Abuf[:, :K] = A
+        Bbuf = torch.full((K, N + 9), float("nan"), dtype=tdt)
+        Bbuf[:, :N] = B
+        Ad, Bd = Abuf.to(DEV)[:, :K], Bbuf.to(DEV)[:, :N]
+        for k in kernels_for(dtype):
+            if not supports(k, M, N, K):
+                continue
+            say(f"[guard] {dtype} {M}x{N}x{K} kernel={k}")
+            Cbuf = torch.full((M + 3, N + 7), -777.0, device=DEV)
+            run(Ad, Bd, k, out=Cbuf[:M, :N])
+            Ch = Cbuf.cpu()
+            assert torch.equal(Ch[:M, :N], exact)
+            assert torch.all(Ch[:M, N:] == -777.0) and torch.all(Ch[M:, :] == -777.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_degenerate_shapes(dtype):
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    C = torch.full((5, 7), 3.0, device=DEV)
+    g.gemm(torch.empty((5, 0), dtype=tdt, device=DEV), torch.empty((0, 7), dtype=tdt, device=DEV),
+           out=C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 0)
+    C = g.gemm(torch.empty((0, 4), dtype=tdt, device=DEV), torch.ones((4, 6), dtype=tdt, device=DEV))
+    assert C.shape == (0, 6)
+    C = g.gemm(torch.ones((3, 4), dtype=tdt, device=DEV), torch.empty((4, 0), dtype=tdt, device=DEV))
+    assert C.shape == (3, 0)
+
+
+def test_invalid_call_raises():
+    a = torch.ones((4, 4), device=DEV)
+    with pytest.raises(g.GemmError) as ei:
+        g.gemm(a, a, out=a)          # C aliases A
+    assert ei.value.code == g.HIP_ERROR_INVALID_VALUE
+
+
+def test_non_default_stream():
+    w = WORKLOADS["ragged_1000x3000x777"]
+    A, B, rows, Cref, D = reference(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        C = g.gemm(Ad, Bd)
+    s.synchronize()
+    Ch = C.cpu().numpy()
+    if rows is not None:
+        Ch = Ch[rows]
+    assert oracle.normalized_error(Ch, Cref, D)[0] <= GATE
