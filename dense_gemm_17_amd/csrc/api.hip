@@ -27,6 +27,7 @@ const KernelInfo kKernels[] = {
     {"naive_bf16", kBF16, launch_naive_bf16, supports_any},
     {"mfma_f32", kF32, launch_mfma_f32, supports_any},
     {"mfma_bf16", kBF16, launch_mfma_bf16, supports_any},
+    {"mfma_bf16_direct", kBF16, launch_mfma_bf16_direct, supports_mfma_bf16_direct},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -92,6 +93,7 @@ Verdict validate(const Problem &p)
 int select_kernel(const Problem &p)
 {
     if (p.dtype == kF32) return kernel_id("mfma_f32");
+    if (supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16_direct");
     return kernel_id("mfma_bf16");
 }
 

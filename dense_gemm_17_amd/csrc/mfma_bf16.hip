@@ -42,8 +42,17 @@ constexpr int kAChunks = BM * BK / 8 / kThreads;   // 8
 constexpr int kBChunks = BK * BN / 8 / kThreads;   // 8
 constexpr int kGroup = 4;
 
-// A rows hold 8 chunks; see the fp32 family for the property of this hash.
-__device__ __forceinline__ int a_swz(int row) { return (row + (row >> 3)) & 7; }
+// Chunk permutation of an A row in LDS.  With 8 chunks per row (K step 64)
+// any 16 consecutive rows read at one logical chunk occupy distinct 16-byte
+// slots modulo 256 bytes, and any 8 consecutive rows distinct slots modulo
+// 128 bytes; with 4 chunks per row (K step 32) the same holds for the
+// 64-byte rows.
+template <int kChunks>
+__device__ __forceinline__ int a_swz(int row)
+{
+    if constexpr (kChunks == 8) return (row + (row >> 3)) & 7;
+    else return ((row >> 1) ^ (row >> 3)) & 3;
+}
 
 // B rows hold 32 chunks.  A transposing read by 16 lanes touches two
 // adjacent chunks of four consecutive rows; a half-wave touches four
@@ -104,7 +113,7 @@ __device__ __forceinline__ void store_tile(const Frag &f, uint16_t *As, uint16_t
     for (int i = 0; i < kAChunks; ++i) {
         const int p = tid + kThreads * i;
         const int row = p >> 3, c = p & 7;
-        *reinterpret_cast<u16x8 *>(As + row * BK + ((c ^ a_swz(row)) << 3)) = f.a[i];
+        *reinterpret_cast<u16x8 *>(As + row * BK + ((c ^ a_swz<8>(row)) << 3)) = f.a[i];
     }
 #pragma unroll
     for (int i = 0; i < kBChunks; ++i) {
@@ -122,19 +131,20 @@ __device__ __forceinline__ bf16x4 read_tr(const uint16_t *lds_elem)
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p);
 }
 
+template <int kBK>
 __device__ __forceinline__ void compute_tile(f32x16 (&acc)[4][4], const uint16_t *As,
                                              const uint16_t *Bs, int wm, int wn, int lane)
 {
     const int h = lane >> 5, c = lane & 31;
     const int i = lane & 15, nhalf = (lane >> 4) & 1;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
+    for (int s = 0; s < kBK / 16; ++s) {
         bf16x8 a[4], b[4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const int row = wm * 128 + mb * 32 + c;
-            const u16x8 v =
-                *reinterpret_cast<const u16x8 *>(As + row * BK + (((2 * s + h) ^ a_swz(row)) << 3));
+            const u16x8 v = *reinterpret_cast<const u16x8 *>(
+                As + row * kBK + (((2 * s + h) ^ a_swz<kBK / 8>(row)) << 3));
             a[mb] = __builtin_bit_cast(bf16x8, v);
         }
         const int k_lo = 16 * s + 8 * h + (i >> 2);   // row of the first read; +4 for the second
@@ -155,6 +165,27 @@ __device__ __forceinline__ void compute_tile(f32x16 (&acc)[4][4], const uint16_t
                 acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb],
                                                                        0, 0, 0);
     }
+}
+
+// Epilogue: register r of block (mb, nb) in lane (h, c) is C row
+// 8*(r/4) + 4*h + r%4, column c of that 32 x 32 block.
+__device__ __forceinline__ void store_c(const f32x16 (&acc)[4][4], float *__restrict__ C,
+                                        int64_t ldc, int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                        int wm, int wn, int lane)
+{
+    const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int64_t col = n0 + wn * 128 + nb * 32 + c;
+            if (col >= N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < M) C[row * ldc + col] = acc[mb][nb][r];
+            }
+        }
 }
 
 template <bool kVec>
@@ -197,26 +228,169 @@ void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restric
             load_tile<kVec>(f, A, lda, B, ldb, M, N, K, m0, n0, k0, a_rows_full && kfull,
                             b_cols_full && kfull);
         }
-        compute_tile(acc, As[cur], Bs[cur], wm, wn, lane);
+        compute_tile<BK>(acc, As[cur], Bs[cur], wm, wn, lane);
         if (more) store_tile(f, As[cur ^ 1], Bs[cur ^ 1]);
         __syncthreads();
     }
 
-    // Epilogue: register r of block (mb, nb) in lane (h, c) is C row
-    // 8*(r/4) + 4*h + r%4, column c of that 32 x 32 block.
-    const int h = lane >> 5, c = lane & 31;
+    store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
+}
+
+
+// ---------------------------------------------------------------------------
+// Direct variant: global -> LDS with gfx950's LDS-direct 128-bit loads
+// (global_load_lds_dwordx4), no register staging and no LDS write
+// instructions, into a ring of kStages LDS stages so that the loads for tile
+// t + kStages - 1 are in flight while tile t is multiplied.  One such load
+// per wave writes 1 KiB of LDS at consecutive 16-byte slots in lane order;
+// choosing which global chunk each lane fetches realises the same swizzled
+// layouts as above.  Shapes: K a multiple of the K step, N a multiple of 8,
+// 16-byte aligned A and B with lda and ldb multiples of 8 (the dispatch table
+// checks this).  Rows of A past M and columns of B past N are fetched from
+// the last valid row / chunk instead (their products land only in rows and
+// columns of C that are not stored).
+
+template <int kBK>
+struct DirectShape {
+    static constexpr int kAInst = BM * kBK * 2 / 1024 / 4;   // LDS-direct loads per wave for A
+    static constexpr int kBInst = kBK * BN * 2 / 1024 / 4;   // ... for B
+    static constexpr int kPerTile = kAInst + kBInst;
+    static constexpr int kStageElems = BM * kBK + kBK * BN;  // bf16 elements per stage
+};
+
+template <int kCnt>
+__device__ __forceinline__ void wait_vm_then_barrier()
+{
+    // s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15 = no wait),
+    // then the work-group barrier.  The asm statements keep the compiler from
+    // moving LDS accesses across the barrier.
+    constexpr int imm = (kCnt & 15) | ((kCnt >> 4) << 14) | (7 << 4) | (15 << 8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(imm);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One LDS-direct 128-bit load: M0 holds the wave's LDS destination, each lane
+// fetches 16 bytes from `src` and the hardware writes them to M0 + 16 * lane.
+// Written as inline assembly on purpose: the compiler's wait-count pass does
+// not see these loads, so it does not drain them before every LDS read; the
+// kernel waits for them itself (wait_vm_then_barrier) with exact counts.
+// M0 is declared clobbered.  The s_nop covers the M0-write hazard.
+__device__ __forceinline__ void lds_direct_load16(const void *src, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) void *)(p)));
+}
+
+template <int kBK>
+__device__ __forceinline__ void issue_tile(uint16_t *stage, const uint16_t *const (&asrc)[DirectShape<kBK>::kAInst],
+                                           const uint16_t *const (&bsrc)[DirectShape<kBK>::kBInst],
+                                           int64_t k0, int64_t ldb, int wave)
+{
+    using S = DirectShape<kBK>;
+    const uint32_t a_dst = lds_offset(stage) + wave * S::kAInst * 1024;
+    const uint32_t b_dst = lds_offset(stage + BM * kBK) + wave * S::kBInst * 1024;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int i = 0; i < S::kAInst; ++i)
+        lds_direct_load16(asrc[i] + k0, __builtin_amdgcn_readfirstlane(a_dst + i * 1024));
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int64_t col = n0 + wn * 128 + nb * 32 + c;
-            if (col >= N) continue;
+    for (int i = 0; i < S::kBInst; ++i)
+        lds_direct_load16(bsrc[i] + k0 * ldb, __builtin_amdgcn_readfirstlane(b_dst + i * 1024));
+}
+
+template <int kBK, int kStages>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
+                             int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
+                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n)
+{
+    using S = DirectShape<kBK>;
+    static_assert(kStages >= 2 && kStages <= 4, "two to four LDS stages");
+    // One LDS object per stage: the compiler's wait-count pass can then tell
+    // that the reads of stage s do not depend on loads in flight to another
+    // stage, and it does not drain every outstanding load before each tile.
+    __shared__ __attribute__((aligned(1024))) uint16_t st0[S::kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t st1[S::kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t st2[kStages > 2 ? S::kStageElems : 8];
+    __shared__ __attribute__((aligned(1024))) uint16_t st3[kStages > 3 ? S::kStageElems : 8];
+
+    const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // Per-lane source of every LDS-direct load of this wave, at k = 0.
+    constexpr int kAChunksPerRow = kBK / 8;
+    const uint16_t *asrc[S::kAInst];
+    const uint16_t *bsrc[S::kBInst];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M) C[row * ldc + col] = acc[mb][nb][r];
+    for (int i = 0; i < S::kAInst; ++i) {
+        const int p = (wave * S::kAInst + i) * 64 + lane;    // LDS chunk this lane fills
+        const int row = p / kAChunksPerRow, slot = p % kAChunksPerRow;
+        const int c = slot ^ a_swz<kAChunksPerRow>(row);
+        const int64_t r = (m0 + row < M) ? m0 + row : M - 1;
+        asrc[i] = A + r * lda + 8 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < S::kBInst; ++i) {
+        const int p = (wave * S::kBInst + i) * 64 + lane;
+        const int row = p >> 5, slot = p & 31;
+        const int c = slot ^ b_swz(row);
+        const int64_t col = (n0 + 8 * c < N) ? n0 + 8 * c : N - 8;
+        bsrc[i] = B + row * ldb + col;
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Stage u of the ring; u is a constant after unrolling, so each access
+    // has one known LDS object.
+    auto stage = [&](int u) -> uint16_t * {
+        return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : st3;
+    };
+
+    const int64_t ktiles = K / kBK;
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < ktiles) issue_tile<kBK>(stage(s), asrc, bsrc, s * kBK, ldb, wave);
+
+    for (int64_t k0t = 0; k0t < ktiles; k0t += kStages) {
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) {
+            const int64_t kt = k0t + u;
+            if (kt < ktiles) {
+                // Tile kt has landed once at most (tiles issued after it) x
+                // (loads per tile) LDS-direct loads of this wave are still
+                // outstanding; the barrier then covers every wave's loads and
+                // every wave's reads of the stage about to be refilled.
+                if (kt + kStages - 2 < ktiles) wait_vm_then_barrier<(kStages - 2) * S::kPerTile>();
+                else wait_vm_then_barrier<0>();
+                const int64_t nxt = kt + kStages - 1;
+                if (nxt < ktiles)
+                    issue_tile<kBK>(stage((u + kStages - 1) % kStages), asrc, bsrc, nxt * kBK, ldb,
+                                    wave);
+                uint16_t *cur = stage(u);
+                compute_tile<kBK>(acc, cur, cur + BM * kBK, wm, wn, lane);
             }
         }
+    }
+
+    store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -238,6 +412,27 @@ hipError_t launch_mfma_bf16(const Problem &p, hipStream_t s)
         hipLaunchKernelGGL(mfma_bf16_kernel<false>, dim3(static_cast<uint32_t>(tm * tn)),
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm,
                            tn);
+    return hipGetLastError();
+}
+
+}  // namespace mi355gemm
+
+namespace mi355gemm {
+
+// Shapes the LDS-direct variant takes (see its description above).
+bool supports_mfma_bf16_direct(const Problem &p)
+{
+    const auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    return p.K % 32 == 0 && p.N % 8 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 && al(p.A) && al(p.B);
+}
+
+hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
+    if (tm * tn > kMaxBlocks || !supports_mfma_bf16_direct(p)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((mfma_bf16_direct_kernel<32, 4>), dim3(static_cast<uint32_t>(tm * tn)),
+                       dim3(kThreads), 0, s, p.M, p.N, p.K, static_cast<const uint16_t *>(p.A),
+                       p.lda, static_cast<const uint16_t *>(p.B), p.ldb, p.C, p.ldc, tm, tn);
     return hipGetLastError();
 }
 

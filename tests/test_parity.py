@@ -42,10 +42,24 @@ def kernels_for(dtype):
     return [n for n in g.kernel_names() if g.gemm_kernel_dtype(g.kernel_id(n)) == code]
 
 
-def supports(name, M, N, K):
-    if name.startswith("skinny"):
-        return M <= 16
-    return True
+FAKE_C = 3 << 40   # stand-in output address for plan queries (256-byte aligned)
+
+
+def _ld(t):
+    return t.stride(0) if t.shape[0] > 1 and t.shape[1] > 0 else max(t.shape[1], 1)
+
+
+def takes(name, A, B):
+    """Does the library accept kernel `name` for these operands (device or
+    host tensors of the call's shape, strides and alignment)?"""
+    M, K = A.shape
+    N = B.shape[1]
+    dt = g.F32 if A.dtype == torch.float32 else g.BF16
+    kid = g.kernel_id(name)
+    with Forced(name):
+        got = g.gemm_plan(dt, M, N, K, A.data_ptr() or (1 << 40), _ld(A),
+                          B.data_ptr() or (2 << 40), _ld(B), FAKE_C, N)
+    return got == kid
 
 
 class Forced:
@@ -99,8 +113,10 @@ def reference(w: Workload):
 
 def check(w: Workload, kernel):
     A, B, rows, Cref, D = reference(w)
-    say(f"[parity] {w.name} kernel={kernel or 'table'} rows={'all' if rows is None else len(rows)}")
     Ad, Bd = A.to(DEV), B.to(DEV)
+    if kernel and not takes(kernel, Ad, Bd):
+        pytest.skip(f"{kernel} does not take {w.name}")
+    say(f"[parity] {w.name} kernel={kernel or 'table'} rows={'all' if rows is None else len(rows)}")
     C = run(Ad, Bd, kernel)
     C2 = run(Ad, Bd, kernel)
     assert torch.equal(C, C2), "kernel is not deterministic"
@@ -126,8 +142,6 @@ def kernel_workload_cases():
     for wn in SMALL_WORKLOADS + LARGE_WORKLOADS:
         w = WORKLOADS[wn]
         for k in kernels_for(w.dtype):
-            if not supports(k, w.M, w.N, w.K):
-                continue
             if k.startswith("naive") and wn in LARGE_WORKLOADS:
                 continue   # the debug kernel is only run on the smaller shapes
             cases.append((wn, k))
@@ -146,7 +160,8 @@ def test_kernel_matches_oracle(wn, kernel):
 
 EXACT_SHAPES = [(1, 1, 1), (3, 5, 7), (64, 64, 64), (65, 63, 67), (256, 256, 512),
                 (257, 383, 129), (300, 520, 200), (1, 8960, 96), (7, 1000, 300),
-                (513, 17, 1025), (17, 513, 33), (128, 256, 4100)]
+                (513, 17, 1025), (17, 513, 33), (128, 256, 4100), (1, 8, 32), (255, 264, 96),
+                (520, 776, 2048), (16, 4096, 1024)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -161,7 +176,7 @@ def test_small_integer_exact(dtype):
         exact = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float64).numpy()
         Ad, Bd = A.to(DEV), B.to(DEV)
         for k in kernels_for(dtype):
-            if not supports(k, M, N, K):
+            if not takes(k, Ad, Bd):
                 continue
             say(f"[exact] {dtype} {M}x{N}x{K} kernel={k}")
             C = run(Ad, Bd, k).cpu().numpy().astype(np.float64)
@@ -173,20 +188,26 @@ def test_small_integer_exact(dtype):
 def test_identity_and_permutation_exact(dtype):
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     gen = workloads.generator(78)
-    K, N = 300, 260
-    B = workloads.draw((K, N), ("uniform", 1.0), gen).to(tdt)
-    perm = torch.randperm(K, generator=gen)
-    P = torch.zeros((K, K), dtype=tdt)
-    P[torch.arange(K), perm] = 1
-    Bd = B.to(DEV)
-    for k in kernels_for(dtype):
-        if not supports(k, K, N, K):
-            continue
-        say(f"[identity] {dtype} kernel={k}")
-        C = run(torch.eye(K, dtype=tdt, device=DEV), Bd, k)
-        assert torch.equal(C.cpu(), B.float())
-        C = run(P.to(DEV), Bd, k)
-        assert torch.equal(C.cpu(), B.float()[perm])
+    for (K, N) in [(300, 260), (320, 264)]:
+        B = workloads.draw((K, N), ("uniform", 1.0), gen).to(tdt)
+        perm = torch.randperm(K, generator=gen)
+        P = torch.zeros((K, K), dtype=tdt)
+        P[torch.arange(K), perm] = 1
+        Bd, Id, Pd = B.to(DEV), torch.eye(K, dtype=tdt, device=DEV), P.to(DEV)
+        for k in kernels_for(dtype):
+            if not takes(k, Id, Bd):
+                continue
+            say(f"[identity] {dtype} K={K} N={N} kernel={k}")
+            C = run(Id, Bd, k)
+            assert torch.equal(C.cpu(), B.float())
+            C = run(Pd, Bd, k)
+            assert torch.equal(C.cpu(), B.float()[perm])
+
+
+GUARD_CASES = [  # (M, N, K, extra A columns, extra B columns)
+    (130, 200, 150, 13, 9), (5, 300, 64, 13, 9), (300, 257, 1000, 13, 9),
+    (300, 264, 512, 16, 8), (257, 520, 96, 8, 24),
+]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -195,17 +216,17 @@ def test_guard_bands_and_poisoned_padding(dtype):
     past M must keep their sentinel."""
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     gen = workloads.generator(79)
-    for (M, N, K) in [(130, 200, 150), (5, 300, 64), (300, 257, 1000)]:
+    for (M, N, K, pa, pb) in GUARD_CASES:
         A = workloads.small_int((M, K), -4, 4, gen, tdt)
         B = workloads.small_int((K, N), -4, 4, gen, tdt)
         exact = (A.to(torch.int64) @ B.to(torch.int64)).float()
-        Abuf = torch.full((M, K + 13), float("nan"), dtype=tdt)
+        Abuf = torch.full((M, K + pa), float("nan"), dtype=tdt)
         Abuf[:, :K] = A
-        Bbuf = torch.full((K, N + 9), float("nan"), dtype=tdt)
+        Bbuf = torch.full((K, N + pb), float("nan"), dtype=tdt)
         Bbuf[:, :N] = B
         Ad, Bd = Abuf.to(DEV)[:, :K], Bbuf.to(DEV)[:, :N]
         for k in kernels_for(dtype):
-            if not supports(k, M, N, K):
+            if not takes(k, Ad, Bd):
                 continue
             say(f"[guard] {dtype} {M}x{N}x{K} kernel={k}")
             Cbuf = torch.full((M + 3, N + 7), -777.0, device=DEV)
