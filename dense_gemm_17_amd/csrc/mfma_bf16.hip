@@ -258,24 +258,12 @@ struct DirectShape {
     static constexpr int kStageElems = BM * kBK + kBK * BN;  // bf16 elements per stage
 };
 
-template <int kCnt>
-__device__ __forceinline__ void wait_vm_then_barrier()
-{
-    // s_waitcnt with only vmcnt constrained (expcnt 7, lgkmcnt 15 = no wait),
-    // then the work-group barrier.  The asm statements keep the compiler from
-    // moving LDS accesses across the barrier.
-    constexpr int imm = (kCnt & 15) | ((kCnt >> 4) << 14) | (7 << 4) | (15 << 8);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(imm);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // One LDS-direct 128-bit load: M0 holds the wave's LDS destination, each lane
 // fetches 16 bytes from `src` and the hardware writes them to M0 + 16 * lane.
 // Written as inline assembly on purpose: the compiler's wait-count pass does
 // not see these loads, so it does not drain them before every LDS read; the
-// kernel waits for them itself (wait_vm_then_barrier) with exact counts.
+// kernel waits for them itself (wait_all_lds_and_vm_then_barrier) with exact
+// counts.
 // M0 is declared clobbered.  The s_nop covers the M0-write hazard.
 __device__ __forceinline__ void lds_direct_load16(const void *src, uint32_t lds_addr)
 {
@@ -307,6 +295,95 @@ __device__ __forceinline__ void issue_tile(uint16_t *stage, const uint16_t *cons
         lds_direct_load16(bsrc[i] + k0 * ldb, __builtin_amdgcn_readfirstlane(b_dst + i * 1024));
 }
 
+// Operand fragments of one 16-wide K slice for a wave's 4 x 4 MFMA blocks:
+// A as one 8-element register quad per 32-row block, B as two 4-element
+// halves (k 0-3 and 4-7 of the lane's eight) per 32-column block.
+struct Frag16 {
+    bf16x8 a[4];
+    bf16x4 blo[4], bhi[4];
+};
+
+// Slice reads are issued one at a time (12 per slice: 4 A reads, 8 B
+// transposing reads) so they can be slotted between MFMAs.
+template <int kBK>
+struct SliceReader {
+    const uint16_t *As, *Bs;
+    int s, wm, wn, lane;
+
+    __device__ __forceinline__ void read(Frag16 &f, int j) const
+    {
+        const int h = lane >> 5, c = lane & 31;
+        const int i = lane & 15, nhalf = (lane >> 4) & 1;
+        if (j < 4) {
+            const int row = wm * 128 + j * 32 + c;
+            const u16x8 v = *reinterpret_cast<const u16x8 *>(
+                As + row * kBK + (((2 * s + h) ^ a_swz<kBK / 8>(row)) << 3));
+            f.a[j] = __builtin_bit_cast(bf16x8, v);
+        } else {
+            const int nb = (j - 4) >> 1, upper = (j - 4) & 1;
+            const int k_lo = 16 * s + 8 * h + (i >> 2);
+            const int n = wn * 128 + nb * 32 + nhalf * 16 + 4 * (i & 3);
+            const uint16_t *p0 = Bs + k_lo * BN + (((n >> 3) ^ b_swz(k_lo)) << 3) + (n & 7);
+            if (upper) f.bhi[nb] = read_tr(p0 + 4 * BN);
+            else f.blo[nb] = read_tr(p0);
+        }
+    }
+};
+
+__device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frag16 &f, int q)
+{
+    const int mb = q >> 2, nb = q & 3;
+    const bf16x8 b = __builtin_shufflevector(f.blo[nb], f.bhi[nb], 0, 1, 2, 3, 4, 5, 6, 7);
+    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], b, acc[mb][nb], 0, 0, 0);
+}
+
+// The 16 MFMAs of slice `cur`, with the 12 reads of slice `nxt` slotted
+// after MFMAs 0..11 and (if do_loads) this wave's LDS-direct loads of a later
+// tile after every other MFMA.  sched_barrier(0) pins that order so that the
+// matrix unit keeps running while reads and loads are in flight; the first
+// MFMA waits only for `cur`, whose reads went out a whole slice earlier.
+template <int kBK>
+__device__ __forceinline__ void mfma_phase(
+    f32x16 (&acc)[4][4], const Frag16 &cur, Frag16 &nxt, const SliceReader<kBK> &rd,
+    uint16_t *stage, const uint16_t *const (&asrc)[DirectShape<kBK>::kAInst],
+    const uint16_t *const (&bsrc)[DirectShape<kBK>::kBInst], int64_t k0, int64_t ldb, int wave,
+    bool do_loads)
+{
+    using S = DirectShape<kBK>;
+    constexpr int kLoads = S::kAInst + S::kBInst;
+    static_assert(16 % kLoads == 0, "loads must divide the MFMA count");
+    constexpr int kEvery = 16 / kLoads;
+    const uint32_t a_dst = lds_offset(stage) + wave * S::kAInst * 1024;
+    const uint32_t b_dst = lds_offset(stage + BM * kBK) + wave * S::kBInst * 1024;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        mfma_one(acc, cur, q);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q < 12) rd.read(nxt, q);
+        if (q % kEvery == kEvery - 1 && do_loads) {
+            const int l = q / kEvery;
+            if (l < S::kAInst)
+                lds_direct_load16(asrc[l] + k0, __builtin_amdgcn_readfirstlane(a_dst + l * 1024));
+            else
+                lds_direct_load16(bsrc[l - S::kAInst] + k0 * ldb,
+                                  __builtin_amdgcn_readfirstlane(b_dst + (l - S::kAInst) * 1024));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int kCntVm>
+__device__ __forceinline__ void wait_all_lds_and_vm_then_barrier()
+{
+    // This wave's LDS reads complete (lgkmcnt 0) and its LDS-direct loads
+    // down to kCntVm in flight, then the work-group barrier.  Inline assembly
+    // so that the compiler's wait-count pass cannot weaken the LDS part: it
+    // is what guarantees that no wave still reads a stage another wave
+    // refills after the barrier.
+    static_assert(kCntVm >= 0 && kCntVm <= 63, "vmcnt is six bits");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(kCntVm) : "memory");
+}
+
 template <int kBK, int kStages>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
@@ -314,14 +391,9 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
                              float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n)
 {
     using S = DirectShape<kBK>;
-    static_assert(kStages >= 2 && kStages <= 4, "two to four LDS stages");
-    // One LDS object per stage: the compiler's wait-count pass can then tell
-    // that the reads of stage s do not depend on loads in flight to another
-    // stage, and it does not drain every outstanding load before each tile.
-    __shared__ __attribute__((aligned(1024))) uint16_t st0[S::kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t st1[S::kStageElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t st2[kStages > 2 ? S::kStageElems : 8];
-    __shared__ __attribute__((aligned(1024))) uint16_t st3[kStages > 3 ? S::kStageElems : 8];
+    static_assert(kBK == 32, "two 16-wide K slices per tile");
+    static_assert(kStages >= 3, "the ring needs a stage being filled, one in flight, one read");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * S::kStageElems];
 
     const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
     const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
@@ -358,36 +430,42 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Stage u of the ring; u is a constant after unrolling, so each access
-    // has one known LDS object.
-    auto stage = [&](int u) -> uint16_t * {
-        return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : st3;
-    };
-
     const int64_t ktiles = K / kBK;
+    auto stage = [&](int64_t kt) { return lds + (kt % kStages) * S::kStageElems; };
+
+    // Prologue: tiles 0 .. kStages-2 in flight, wait for tile 0, read its
+    // first slice.
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
         if (s < ktiles) issue_tile<kBK>(stage(s), asrc, bsrc, s * kBK, ldb, wave);
+    if (ktiles >= kStages - 1) wait_all_lds_and_vm_then_barrier<(kStages - 2) * S::kPerTile>();
+    else wait_all_lds_and_vm_then_barrier<0>();
 
-    for (int64_t k0t = 0; k0t < ktiles; k0t += kStages) {
+    Frag16 f0, f1;
+    {
+        const SliceReader<kBK> rd{stage(0), stage(0) + BM * kBK, 0, wm, wn, lane};
 #pragma unroll
-        for (int u = 0; u < kStages; ++u) {
-            const int64_t kt = k0t + u;
-            if (kt < ktiles) {
-                // Tile kt has landed once at most (tiles issued after it) x
-                // (loads per tile) LDS-direct loads of this wave are still
-                // outstanding; the barrier then covers every wave's loads and
-                // every wave's reads of the stage about to be refilled.
-                if (kt + kStages - 2 < ktiles) wait_vm_then_barrier<(kStages - 2) * S::kPerTile>();
-                else wait_vm_then_barrier<0>();
-                const int64_t nxt = kt + kStages - 1;
-                if (nxt < ktiles)
-                    issue_tile<kBK>(stage((u + kStages - 1) % kStages), asrc, bsrc, nxt * kBK, ldb,
-                                    wave);
-                uint16_t *cur = stage(u);
-                compute_tile<kBK>(acc, cur, cur + BM * kBK, wm, wn, lane);
-            }
-        }
+        for (int j = 0; j < 12; ++j) rd.read(f0, j);
+    }
+
+    // Tile kt:  MFMAs on slice 0 with the reads of slice 1 and the loads of
+    // tile kt + kStages - 1 slotted in (that stage was last read in tile
+    // kt - 1, which every wave finished before the previous barrier) | wait
+    // until tile kt + 1 has landed everywhere and this wave's reads are done,
+    // barrier | MFMAs on slice 1 with the reads of slice 0 of tile kt + 1 (in
+    // the last tile, a harmless re-read of the current stage).
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        uint16_t *cur = stage(kt);
+        const int64_t nxt = kt + kStages - 1;
+        const SliceReader<kBK> rd1{cur, cur + BM * kBK, 1, wm, wn, lane};
+        mfma_phase<kBK>(acc, f0, f1, rd1, stage(nxt), asrc, bsrc, nxt * kBK, ldb, wave,
+                        nxt < ktiles);
+        // In flight after this: tiles kt + 2 .. min(nxt, ktiles - 1).
+        if (nxt < ktiles) wait_all_lds_and_vm_then_barrier<(kStages - 2) * S::kPerTile>();
+        else wait_all_lds_and_vm_then_barrier<0>();
+        uint16_t *n1 = stage(kt + 1 < ktiles ? kt + 1 : kt);
+        const SliceReader<kBK> rd0{n1, n1 + BM * kBK, 0, wm, wn, lane};
+        mfma_phase<kBK>(acc, f1, f0, rd0, n1, asrc, bsrc, 0, ldb, wave, false);
     }
 
     store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
