@@ -144,11 +144,17 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
     elif (out.dtype != torch.float32 or out.shape != (M, N) or out.device != a.device
           or (N > 1 and out.stride(1) != 1)):
         raise ValueError("out must be a float32 (M, N) tensor with unit column stride on a's GPU")
-    with torch.cuda.device(a.device):
-        s = stream if stream is not None else torch.cuda.current_stream(a.device)
-        fn = lib.gemm_f32 if a.dtype == torch.float32 else lib.gemm_bf16_f32acc
+    fn = lib.gemm_f32 if a.dtype == torch.float32 else lib.gemm_bf16_f32acc
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    # The library launches on the calling thread's current HIP device.
+    if a.device.index != torch.cuda.current_device():
+        with torch.cuda.device(a.device):
+            rc = fn(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b),
+                    out.data_ptr(), _ld(out), stream.cuda_stream)
+    else:
         rc = fn(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b),
-                out.data_ptr(), _ld(out), s.cuda_stream)
+                out.data_ptr(), _ld(out), stream.cuda_stream)
     if rc != HIP_SUCCESS:
         raise GemmError(rc, "gemm_f32" if a.dtype == torch.float32 else "gemm_bf16_f32acc")
     return out

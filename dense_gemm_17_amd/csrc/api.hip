@@ -26,8 +26,12 @@ const KernelInfo kKernels[] = {
     {"naive_f32", kF32, launch_naive_f32, supports_any},
     {"naive_bf16", kBF16, launch_naive_bf16, supports_any},
     {"mfma_f32", kF32, launch_mfma_f32, supports_any},
+    {"mfma_f32_128", kF32, launch_mfma_f32_128, supports_any},
     {"mfma_bf16", kBF16, launch_mfma_bf16, supports_any},
     {"mfma_bf16_direct", kBF16, launch_mfma_bf16_direct, supports_mfma_bf16_direct},
+    {"skinny_f32", kF32, launch_skinny_f32, supports_skinny},
+    {"skinny_bf16", kBF16, launch_skinny_bf16, supports_skinny},
+    {"valu_f32", kF32, launch_valu_f32, supports_any},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -89,12 +93,41 @@ Verdict validate(const Problem &p)
     return kCompute;
 }
 
-// The dispatch table: a pure function of shape, element type and alignment.
+// ---- the dispatch table ------------------------------------------------------
+// A pure function of shape, element type and alignment.  Regimes:
+//   * bandwidth-bound: M <= 16 rows.  Arithmetic intensity is about M/2 flop
+//     per byte of B for fp32 (M flop per byte for bf16), far below the ridge
+//     point (~20 flop/B fp32, ~315 flop/B bf16 on MI355X), so the time is
+//     the time to stream B once: the skinny family;
+//   * compute-bound: everything else, on the matrix cores.  The fp32 tile is
+//     picked by an estimate of the time in work-group waves: a 256 x 256 tile
+//     runs one work-group per CU, a 128 x 128 tile two (each at half the
+//     CU's rate), over 256 CUs; the smaller tile wins when the larger one
+//     leaves CUs idle in its last wave (gpt-sized and ragged shapes).  bf16
+//     uses the LDS-direct kernel when its layout conditions hold.
+constexpr int64_t kCUs = 256;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Relative time of a tiled launch: waves x per-work-group time, in units of
+// one CU doing a 128 x 128 tile alone.
+int64_t tiled_cost(const Problem &p, int64_t tile, int64_t per_cu)
+{
+    const int64_t tiles = ceil_div(p.M, tile) * ceil_div(p.N, tile);
+    const int64_t waves = ceil_div(tiles, kCUs * per_cu);
+    return waves * (tile / 128) * (tile / 128) * per_cu;
+}
+
 int select_kernel(const Problem &p)
 {
-    if (p.dtype == kF32) return kernel_id("mfma_f32");
-    if (supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16_direct");
-    return kernel_id("mfma_bf16");
+    if (p.M <= kSkinnyMaxM)
+        return kernel_id(p.dtype == kF32 ? "skinny_f32" : "skinny_bf16");
+    if (p.dtype == kBF16) {
+        if (supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16_direct");
+        return kernel_id("mfma_bf16");
+    }
+    if (tiled_cost(p, 256, 1) <= tiled_cost(p, 128, 2)) return kernel_id("mfma_f32");
+    return kernel_id("mfma_f32_128");
 }
 
 // Table choice, overridden by gemm_force_kernel for calls of the forced

@@ -122,3 +122,49 @@ def test_plan_is_pure():
     b = [g.gemm_plan(g.F32, m, n, k, A=PA, B=PB, C=PC)
          for (m, n, k) in [(1, 8960, 1536), (4096, 4096, 4096), (1000, 3000, 777)]]
     assert a == b
+
+
+# The dispatch table's choice for every workload of the benchmark set, and
+# for the layout cases that change it.  Measured alternatives for each row
+# are recorded by dense_gemm_17_amd/sweep.py.
+DISPATCH_GOLDEN = {
+    "f32_256": "mfma_f32_128",
+    "f32_4096": "mfma_f32",
+    "f32_8192": "mfma_f32",
+    "gpt_qkv": "mfma_f32_128",
+    "gpt_mlp_up": "mfma_f32_128",
+    "gpt_mlp_down": "mfma_f32_128",
+    "bf16_8192": "mfma_bf16_direct",
+    "skinny_1x8960x1536": "skinny_f32",
+    "skinny_7x4096x4096": "skinny_f32",
+    "ragged_1000x3000x777": "mfma_f32_128",
+    "ragged_4097x4095x1023": "mfma_f32_128",
+}
+
+
+@pytest.mark.parametrize("name", sorted(DISPATCH_GOLDEN))
+def test_dispatch_golden(name):
+    import workloads
+    w = workloads.WORKLOADS[name]
+    dt = g.F32 if w.dtype == "f32" else g.BF16
+    assert g.gemm_kernel_name(g.gemm_plan(dt, w.M, w.N, w.K, A=PA, B=PB, C=PC)) == DISPATCH_GOLDEN[name]
+
+
+def test_dispatch_layout_cases():
+    name = lambda *a, **k: g.gemm_kernel_name(g.gemm_plan(*a, **k))  # noqa: E731
+    # bf16: the LDS-direct kernel needs K % 32, N % 8, 16-byte aligned rows
+    assert name(g.BF16, 8192, 8192, 8192, A=PA, B=PB, C=PC) == "mfma_bf16_direct"
+    assert name(g.BF16, 8192, 8192, 8200, A=PA, B=PB, C=PC) == "mfma_bf16"
+    assert name(g.BF16, 8192, 8196, 8192, A=PA, B=PB, C=PC) == "mfma_bf16"
+    assert name(g.BF16, 8192, 8192, 8192, A=PA + 2, B=PB, C=PC) == "mfma_bf16"
+    assert name(g.BF16, 8192, 8192, 8192, A=PA, lda=8196, B=PB, C=PC) == "mfma_bf16"
+    # few rows -> bandwidth family, both element types, up to 16 rows
+    assert name(g.BF16, 1, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_bf16"
+    assert name(g.F32, 16, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_f32"
+    assert name(g.F32, 17, 4096, 4096, A=PA, B=PB, C=PC) != "skinny_f32"
+    # the skinny family refuses more than 16 rows when forced
+    try:
+        g.gemm_force_kernel(g.kernel_id("skinny_f32"))
+        assert g.gemm_plan(g.F32, 17, 64, 64, A=PA, B=PB, C=PC) == -1
+    finally:
+        g.gemm_force_kernel(-1)
