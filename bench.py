@@ -13,10 +13,19 @@ Prints exactly one JSON line.  Extra legs:
   --copy-calibration: also runs a plain device copy of known size, so that
       hardware byte counters (FETCH_SIZE / WRITE_SIZE) read under a profiler
       can be scaled against it.
+  --ingest-counters FETCH_DIR WRITE_DIR: turn two rocprofv3 --pmc runs of
+      this script (FETCH_SIZE, then WRITE_SIZE, with --copy-calibration) into
+      profiles/hbm_traffic_8192.txt: HBM bytes per launch of each kernel,
+      scaled by what the counters read for the copy, tagged with a digest of
+      the kernel's sources.  The benchmark line reports that traffic for the
+      dominant kernel only while the digest still matches (else null).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +43,17 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}     # MI355X dense, per dtype
 HBM_PEAK_GBS = 8000.0
 METRIC = "GFLOP/s (2MNK/t) fp32 & bf16 GEMM at 8192³; % of MI355X dtype peak"
 STEP_WORKLOADS = ("f32_8192", "bf16_8192")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_8192.txt")
+CSRC = os.path.join(ROOT, "dense_gemm_17_amd", "csrc")
+# library kernel name -> (symbol substring in profiler output, source files)
+KERNEL_SOURCES = {
+    "mfma_f32": ("mfma_f32_kernel<256, 256, true>", ["mfma_f32.hip"]),
+    "mfma_f32_128": ("mfma_f32_kernel<128, 128, true>", ["mfma_f32.hip"]),
+    "mfma_bf16_direct": ("mfma_bf16_direct_kernel<32, 4>", ["mfma_bf16.hip"]),
+    "mfma_bf16": ("mfma_bf16_kernel<true>", ["mfma_bf16.hip"]),
+}
+COMMON_SOURCES = ["gemm_internal.h", "tile_map.h"]
+COPY_BYTES = 256 * 1024 * 1024
 
 
 def parse():
@@ -49,7 +69,76 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--check-rows", type=int, default=8,
                    help="rows per product checked against the oracle after timing")
+    p.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     return p.parse_args()
+
+
+def source_digest(kernel: str):
+    if kernel not in KERNEL_SOURCES:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel][1] + COMMON_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter(run_dir: str, counter: str):
+    """{kernel symbol: [KiB per dispatch, ...]} from a rocprofv3 --pmc run."""
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "*counter_collection.csv")):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return out
+
+
+def ingest_counters(fetch_dir: str, write_dir: str):
+    fetch = read_counter(fetch_dir, "FETCH_SIZE")
+    write = read_counter(write_dir, "WRITE_SIZE")
+
+    def copy_kib(table):
+        vals = [v for name, rows in table.items() if "copyBuffer" in name
+                for (grid, v) in rows]
+        return max(vals)   # the 256 MiB device copy is the largest copy dispatch
+
+    fetch_scale = COPY_BYTES / (copy_kib(fetch) * 1024)
+    write_scale = COPY_BYTES / (copy_kib(write) * 1024)
+    rec = {"copy_bytes": COPY_BYTES, "fetch_scale": round(fetch_scale, 4),
+           "write_scale": round(write_scale, 4), "kernels": {}}
+    for kernel, (sym, _) in KERNEL_SOURCES.items():
+        f = [v for name, rows in fetch.items() if sym in name for (_, v) in rows]
+        w = [v for name, rows in write.items() if sym in name for (_, v) in rows]
+        if not f or not w:
+            continue
+        fb = sum(f) / len(f) * 1024 * fetch_scale
+        wb = sum(w) / len(w) * 1024 * write_scale
+        rec["kernels"][kernel] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                                  "bytes_per_launch": round(fb + wb), "dispatches": len(f),
+                                  "source_digest": source_digest(kernel)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("# HBM bytes per launch at 8192^3, from rocprofv3 FETCH_SIZE / WRITE_SIZE\n")
+        fh.write("# runs of: python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
+                 "--copy-calibration\n")
+        fh.write("# (one run per counter), scaled by the counters' reading of a 256 MiB "
+                 "device copy.\n")
+        fh.write(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec))
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch for `kernel`, or None if not measured for the
+    current sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    rec = json.loads(text[text.index("{"):])
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or k.get("source_digest") != source_digest(kernel):
+        return None
+    return k["bytes_per_launch"]
 
 
 def cpu_threads() -> int:
@@ -65,6 +154,9 @@ def cpu_threads() -> int:
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
@@ -159,7 +251,7 @@ def main():
     roofline = {
         "bound": "mfma", "kernel": dom["kernel"], "workload": dom_w.name,
         "achieved": dom["tflops"], "peak": PEAK_TFLOPS[dom_w.dtype], "unit": "TFLOP/s",
-        "frac": dom["frac_peak"], "traffic": None,
+        "frac": dom["frac_peak"], "traffic": traffic_for(dom["kernel"]),
     }
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1,
