@@ -32,6 +32,7 @@ const KernelInfo kKernels[] = {
     {"skinny_f32", kF32, launch_skinny_f32, supports_skinny},
     {"skinny_bf16", kBF16, launch_skinny_bf16, supports_skinny},
     {"valu_f32", kF32, launch_valu_f32, supports_any},
+    {"mfma_f32_direct", kF32, launch_mfma_f32_direct, supports_mfma_f32_direct},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -102,20 +103,23 @@ Verdict validate(const Problem &p)
 //   * compute-bound: everything else, on the matrix cores.  The fp32 tile is
 //     picked by an estimate of the time in work-group waves: a 256 x 256 tile
 //     runs one work-group per CU, a 128 x 128 tile two (each at half the
-//     CU's rate), over 256 CUs; the smaller tile wins when the larger one
-//     leaves CUs idle in its last wave (gpt-sized and ragged shapes).  bf16
-//     uses the LDS-direct kernel when its layout conditions hold.
+//     CU's rate), over 256 CUs, each divided by the kernel's measured
+//     fraction of the matrix-core peak (LDS-direct 256: 0.91, register-staged
+//     256: 0.70, register-staged 128 with two per CU: 0.67).  The smaller tile
+//     wins when the larger one leaves CUs idle in its last wave (gpt-sized
+//     and ragged shapes).  The LDS-direct kernels are used wherever their
+//     layout conditions hold (bf16 and fp32 alike).
 constexpr int64_t kCUs = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Relative time of a tiled launch: waves x per-work-group time, in units of
-// one CU doing a 128 x 128 tile alone.
-int64_t tiled_cost(const Problem &p, int64_t tile, int64_t per_cu)
+// Relative time of a tiled launch: waves x per-work-group work / efficiency,
+// in units of one CU doing a 128 x 128 tile alone at full rate.
+int64_t tiled_cost(const Problem &p, int64_t tile, int64_t per_cu, int64_t eff_pct)
 {
     const int64_t tiles = ceil_div(p.M, tile) * ceil_div(p.N, tile);
     const int64_t waves = ceil_div(tiles, kCUs * per_cu);
-    return waves * (tile / 128) * (tile / 128) * per_cu;
+    return waves * (tile / 128) * (tile / 128) * per_cu * 10000 / eff_pct;
 }
 
 int select_kernel(const Problem &p)
@@ -126,7 +130,10 @@ int select_kernel(const Problem &p)
         if (supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16_direct");
         return kernel_id("mfma_bf16");
     }
-    if (tiled_cost(p, 256, 1) <= tiled_cost(p, 128, 2)) return kernel_id("mfma_f32");
+    const bool direct = supports_mfma_f32_direct(p);
+    const int64_t big = tiled_cost(p, 256, 1, direct ? 91 : 70);
+    if (big <= tiled_cost(p, 128, 2, 67))
+        return kernel_id(direct ? "mfma_f32_direct" : "mfma_f32");
     return kernel_id("mfma_f32_128");
 }
 

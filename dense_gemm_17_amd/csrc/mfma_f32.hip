@@ -265,9 +265,240 @@ hipError_t launch_tiles(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Direct variant (256 x 256 tile, K step 16, four LDS stages): global -> LDS
+// with LDS-direct 128-bit loads (no register staging, no LDS write
+// instructions) so the loads for tile t + 3 are in flight while tile t is
+// multiplied; operand fragments are read one 8-wide K group ahead, across
+// the tile boundary, each read and each load slotted between MFMAs; one
+// barrier per tile.  Same layouts and epilogue as the staged kernel (A rows
+// of 16 floats = 4 chunks, chunk-swizzled; B rows of 256 floats).  Shapes: K
+// a multiple of 16, N a multiple of 4, 16-byte aligned A and B with lda and
+// ldb multiples of 4; rows of A past M and columns of B past N are fetched
+// from the last valid row / chunk (their products land only in rows and
+// columns of C that are not stored).
+
+constexpr int DBK = 16;           // K step of the direct variant
+constexpr int DSTAGES = 4;
+constexpr int kDAInst = 256 * DBK * 4 / 1024 / 4;   // LDS-direct loads per wave per tile (A): 4
+constexpr int kDBInst = DBK * 256 * 4 / 1024 / 4;   // ... (B): 4
+constexpr int kDPerTile = kDAInst + kDBInst;
+constexpr int kDStageFloats = 256 * DBK + DBK * 256;
+
+// A rows of 4 chunks: for 16 consecutive rows at one logical chunk the
+// 16-byte slots modulo 256 bytes are distinct, and for 8 consecutive rows
+// modulo 128 bytes.
+__device__ __forceinline__ int a_swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// One LDS-direct 128-bit load as inline assembly: M0 = LDS destination of
+// the wave, lane i's 16 bytes land at M0 + 16 i.  The compiler's wait-count
+// pass does not see these loads (it would otherwise drain them before every
+// LDS read); the kernel counts them itself.  M0 is declared clobbered; the
+// s_nop covers the M0-write hazard.
+__device__ __forceinline__ void lds_direct_load16(const void *src, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_addr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) void *)(p)));
+}
+
+// This wave's LDS reads complete, its LDS-direct loads down to kCntVm in
+// flight, then the barrier; inline assembly so the LDS part is not weakened
+// by the compiler (it guarantees no wave still reads a stage being refilled).
+template <int kCntVm>
+__device__ __forceinline__ void wait_lds_vm_barrier()
+{
+    static_assert(kCntVm >= 0 && kCntVm <= 63, "vmcnt is six bits");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(kCntVm) : "memory");
+}
+
+struct DSrc {
+    const float *a[kDAInst];
+    const float *b[kDBInst];
+};
+
+__device__ __forceinline__ void issue_tile_direct(float *stage, const DSrc &src, int64_t k0,
+                                                  int64_t ldb, int wave, int first, int count)
+{
+    const uint32_t a_dst = lds_offset(stage) + wave * kDAInst * 1024;
+    const uint32_t b_dst = lds_offset(stage + 256 * DBK) + wave * kDBInst * 1024;
+#pragma unroll
+    for (int l = 0; l < kDPerTile; ++l) {
+        if (l < first || l >= first + count) continue;
+        if (l < kDAInst)
+            lds_direct_load16(src.a[l] + k0, __builtin_amdgcn_readfirstlane(a_dst + l * 1024));
+        else
+            lds_direct_load16(src.b[l - kDAInst] + k0 * ldb,
+                              __builtin_amdgcn_readfirstlane(b_dst + (l - kDAInst) * 1024));
+    }
+}
+
+// Fragments of one 8-wide K group for a wave's 4 x 4 blocks: a[mb] holds
+// k = 4h .. 4h+3 of row c of block mb; b[j] holds, for k-step j, the four
+// columns 4c .. 4c+3 (one per block nb).
+struct FragG {
+    f32x4 a[4];
+    f32x4 b[4];
+};
+
+__device__ __forceinline__ void read_one(FragG &f, const float *As, const float *Bs, int g,
+                                         int idx, int wm, int wn, int lane)
+{
+    const int h = lane >> 5, c = lane & 31;
+    if (idx < 4) {
+        const int row = wm * 128 + idx * 32 + c;
+        f.a[idx] = *reinterpret_cast<const f32x4 *>(As + row * DBK +
+                                                    (((2 * g + h) ^ a_swz4(row)) << 2));
+    } else {
+        const int j = idx - 4;
+        f.b[j] = *reinterpret_cast<const f32x4 *>(Bs + (8 * g + 4 * h + j) * 256 + wn * 128 + 4 * c);
+    }
+}
+
+// The 64 MFMAs of group `cur`; after every 8th the next read of `nxt`, and
+// (if do_loads) after every 8th + 4 one LDS-direct load of a later tile.
+__device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[4][4], const FragG &cur, FragG &nxt,
+                                               const float *As, const float *Bs, int g_next,
+                                               int wm, int wn, int lane, float *load_stage,
+                                               const DSrc &src, int64_t k0, int64_t ldb,
+                                               int wave, bool do_loads)
+{
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {
+        const int j = q >> 4, mb = (q >> 2) & 3, nb = q & 3;
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[mb][j], cur.b[j][nb], acc[mb][nb],
+                                                            0, 0, 0);
+        if ((q & 7) == 0 || (q & 7) == 4) {
+            __builtin_amdgcn_sched_barrier(0);
+            if ((q & 7) == 0) read_one(nxt, As, Bs, g_next, q >> 3, wm, wn, lane);
+            else if (do_loads) issue_tile_direct(load_stage, src, k0, ldb, wave, q >> 3, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A,
+                            int64_t lda, const float *__restrict__ B, int64_t ldb,
+                            float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
+                            int cvec)
+{
+    __shared__ __attribute__((aligned(1024))) float lds[DSTAGES * kDStageFloats];
+
+    const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+    const int64_t m0 = t.tm * 256, n0 = t.tn * 256;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    DSrc src;
+#pragma unroll
+    for (int i = 0; i < kDAInst; ++i) {
+        const int p = (wave * kDAInst + i) * 64 + lane;     // LDS chunk this lane fills
+        const int row = p >> 2, slot = p & 3;
+        const int c = slot ^ a_swz4(row);
+        const int64_t r = (m0 + row < M) ? m0 + row : M - 1;
+        src.a[i] = A + r * lda + 4 * c;
+    }
+#pragma unroll
+    for (int i = 0; i < kDBInst; ++i) {
+        const int p = (wave * kDBInst + i) * 64 + lane;
+        const int row = p >> 6, slot = p & 63;
+        const int64_t col = (n0 + 4 * slot < N) ? n0 + 4 * slot : N - 4;
+        src.b[i] = B + row * ldb + col;
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int64_t ktiles = K / DBK;
+    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * kDStageFloats; };
+
+#pragma unroll
+    for (int s = 0; s < DSTAGES - 1; ++s)
+        if (s < ktiles) issue_tile_direct(stage(s), src, s * DBK, ldb, wave, 0, kDPerTile);
+    if (ktiles >= DSTAGES - 1) wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+    else wait_lds_vm_barrier<0>();
+
+    FragG f0, f1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) read_one(f0, stage(0), stage(0) + 256 * DBK, 0, i, wm, wn, lane);
+
+    // Tile kt: MFMAs on group 0 with group 1's reads and the loads of tile
+    // kt + 3 slotted in (its stage was last read in tile kt - 1, finished by
+    // every wave before the previous barrier) | wait for tile kt + 1 and for
+    // this wave's reads, barrier | MFMAs on group 1 with the reads of group 0
+    // of tile kt + 1 (in the last tile a harmless re-read of this stage).
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        float *cur = stage(kt);
+        const int64_t nxt = kt + DSTAGES - 1;
+        mfma_phase_f32(acc, f0, f1, cur, cur + 256 * DBK, 1, wm, wn, lane, stage(nxt), src,
+                       nxt * DBK, ldb, wave, nxt < ktiles);
+        if (nxt < ktiles) wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+        else wait_lds_vm_barrier<0>();
+        float *n1 = stage(kt + 1 < ktiles ? kt + 1 : kt);
+        mfma_phase_f32(acc, f1, f0, n1, n1 + 256 * DBK, 0, wm, wn, lane, n1, src, 0, ldb, wave,
+                       false);
+    }
+
+    const int h = lane >> 5, c = lane & 31;
+    const int64_t col = n0 + wn * 128 + 4 * c;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row >= M) continue;
+            float *p = C + row * ldc + col;
+            const f32x4 v = {acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
+            if (cvec && col + 3 < N) {
+                *reinterpret_cast<f32x4 *>(p) = v;
+            } else {
+                if (col + 0 < N) p[0] = v.x;
+                if (col + 1 < N) p[1] = v.y;
+                if (col + 2 < N) p[2] = v.z;
+                if (col + 3 < N) p[3] = v.w;
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_mfma_f32(const Problem &p, hipStream_t s) { return launch_tiles<256, 256>(p, s); }
 hipError_t launch_mfma_f32_128(const Problem &p, hipStream_t s) { return launch_tiles<128, 128>(p, s); }
+
+}  // namespace mi355gemm
+
+namespace mi355gemm {
+
+bool supports_mfma_f32_direct(const Problem &p)
+{
+    const auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    return p.K % 16 == 0 && p.N % 4 == 0 && p.lda % 4 == 0 && p.ldb % 4 == 0 && al(p.A) &&
+           al(p.B);
+}
+
+hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+    if (tm * tn > kMaxBlocks || !supports_mfma_f32_direct(p)) return hipErrorInvalidValue;
+    const int cvec = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0;
+    hipLaunchKernelGGL(mfma_f32_direct_kernel, dim3(static_cast<uint32_t>(tm * tn)), dim3(256), 0,
+                       s, p.M, p.N, p.K, static_cast<const float *>(p.A), p.lda,
+                       static_cast<const float *>(p.B), p.ldb, p.C, p.ldc, tm, tn, cvec);
+    return hipGetLastError();
+}
 
 }  // namespace mi355gemm

@@ -129,10 +129,10 @@ def test_plan_is_pure():
 # are recorded by dense_gemm_17_amd/sweep.py.
 DISPATCH_GOLDEN = {
     "f32_256": "mfma_f32_128",
-    "f32_4096": "mfma_f32",
-    "f32_8192": "mfma_f32",
-    "gpt_qkv": "mfma_f32_128",
-    "gpt_mlp_up": "mfma_f32_128",
+    "f32_4096": "mfma_f32_direct",
+    "f32_8192": "mfma_f32_direct",
+    "gpt_qkv": "mfma_f32_direct",
+    "gpt_mlp_up": "mfma_f32_direct",
     "gpt_mlp_down": "mfma_f32_128",
     "bf16_8192": "mfma_bf16_direct",
     "skinny_1x8960x1536": "skinny_f32",
@@ -158,6 +158,11 @@ def test_dispatch_layout_cases():
     assert name(g.BF16, 8192, 8196, 8192, A=PA, B=PB, C=PC) == "mfma_bf16"
     assert name(g.BF16, 8192, 8192, 8192, A=PA + 2, B=PB, C=PC) == "mfma_bf16"
     assert name(g.BF16, 8192, 8192, 8192, A=PA, lda=8196, B=PB, C=PC) == "mfma_bf16"
+    # fp32: the LDS-direct kernel needs K % 16, N % 4, 16-byte aligned rows
+    assert name(g.F32, 8192, 8192, 8192, A=PA, B=PB, C=PC) == "mfma_f32_direct"
+    assert name(g.F32, 8192, 8192, 8200, A=PA, B=PB, C=PC) == "mfma_f32"
+    assert name(g.F32, 8192, 8192, 8192, A=PA, B=PB, ldb=8194, C=PC) == "mfma_f32"
+    assert name(g.F32, 8192, 8192, 8192, A=PA + 4, B=PB, C=PC) == "mfma_f32"
     # few rows -> bandwidth family, both element types, up to 16 rows
     assert name(g.BF16, 1, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_bf16"
     assert name(g.F32, 16, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_f32"
