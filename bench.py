@@ -61,7 +61,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workloads", default=",".join(STEP_WORKLOADS),
                    help="comma-separated workload names making up one step")
     p.add_argument("--no-cpu-baseline", action="store_true")
