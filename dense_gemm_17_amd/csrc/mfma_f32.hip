@@ -272,11 +272,22 @@ hipError_t launch_tiles(const Problem &p, hipStream_t s)
 // multiplied; operand fragments are read one 8-wide K group ahead, across
 // the tile boundary, each read and each load slotted between MFMAs; one
 // barrier per tile.  Same layouts and epilogue as the staged kernel (A rows
-// of 16 floats = 4 chunks, chunk-swizzled; B rows of 256 floats).  Shapes: K
-// a multiple of 16, N a multiple of 4, 16-byte aligned A and B with lda and
-// ldb multiples of 4; rows of A past M and columns of B past N are fetched
-// from the last valid row / chunk (their products land only in rows and
-// columns of C that are not stored).
+// of 16 floats = 4 chunks, chunk-swizzled; B rows of 256 floats).
+//
+// Instruction economy matters here: with one wave per SIMD every non-MFMA
+// instruction sits between two MFMAs.  So the loads use the scalar-base
+// form (a wave-uniform 64-bit base advanced once per tile plus a fixed
+// 32-bit lane offset: no vector address arithmetic), the reads use one
+// lane base per stage plus immediate offsets (the A-row swizzle of the rows
+// a lane reads depends only on the lane), and the loads past the last tile
+// re-fetch the last tile into a stage nobody reads again instead of being
+// branched around.
+//
+// Shapes: K a multiple of 16, N a multiple of 4, 16-byte aligned A and B
+// with lda and ldb multiples of 4, and lane offsets within 32 bits
+// (256 * lda and 16 * ldb below 2^30 elements).  Rows of A past M and
+// columns of B past N are fetched from the last valid row / chunk (their
+// products land only in rows and columns of C that are not stored).
 
 constexpr int DBK = 16;           // K step of the direct variant
 constexpr int DSTAGES = 4;
@@ -290,16 +301,17 @@ constexpr int kDStageFloats = 256 * DBK + DBK * 256;
 // modulo 128 bytes.
 __device__ __forceinline__ int a_swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// One LDS-direct 128-bit load as inline assembly: M0 = LDS destination of
-// the wave, lane i's 16 bytes land at M0 + 16 i.  The compiler's wait-count
-// pass does not see these loads (it would otherwise drain them before every
-// LDS read); the kernel counts them itself.  M0 is declared clobbered; the
-// s_nop covers the M0-write hazard.
-__device__ __forceinline__ void lds_direct_load16(const void *src, uint32_t lds_addr)
+// One LDS-direct 128-bit load as inline assembly, scalar-base form: lane i
+// reads 16 bytes at sbase + voff and they land at LDS byte M0 + 16 i.  The
+// compiler's wait-count pass does not see these loads (it would otherwise
+// drain them before every LDS read); the kernel counts them itself.  M0 is
+// declared clobbered (nothing else in these kernels keeps a value in it);
+// the s_nop covers the M0-write hazard.
+__device__ __forceinline__ void lds_direct_load16(uint32_t voff, const void *sbase, uint32_t m0v)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(src), "s"(lds_addr)
+                 : "v"(voff), "s"(sbase), "s"(m0v)
                  : "memory", "m0");
 }
 
@@ -319,25 +331,24 @@ __device__ __forceinline__ void wait_lds_vm_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(kCntVm) : "memory");
 }
 
-struct DSrc {
-    const float *a[kDAInst];
-    const float *b[kDBInst];
+// Everything a wave needs to address its loads and reads.
+struct DCtx {
+    uint32_t a_voff[kDAInst], b_voff[kDBInst];   // lane offsets (bytes) of each load
+    const char *abase, *bbase;                   // tile (k = 0) bases, wave-uniform
+    int64_t a_kstride, b_kstride;                // bytes per K step
+    uint32_t lds0;                               // LDS byte address of stage 0
+    int wave;
+    uint32_t rdA0, rdA1, rdB;                    // lane parts of the read offsets in a stage
 };
 
-__device__ __forceinline__ void issue_tile_direct(float *stage, const DSrc &src, int64_t k0,
-                                                  int64_t ldb, int wave, int first, int count)
+__device__ __forceinline__ void load_one(const DCtx &x, uint32_t stage_lds, int64_t kt, int l)
 {
-    const uint32_t a_dst = lds_offset(stage) + wave * kDAInst * 1024;
-    const uint32_t b_dst = lds_offset(stage + 256 * DBK) + wave * kDBInst * 1024;
-#pragma unroll
-    for (int l = 0; l < kDPerTile; ++l) {
-        if (l < first || l >= first + count) continue;
-        if (l < kDAInst)
-            lds_direct_load16(src.a[l] + k0, __builtin_amdgcn_readfirstlane(a_dst + l * 1024));
-        else
-            lds_direct_load16(src.b[l - kDAInst] + k0 * ldb,
-                              __builtin_amdgcn_readfirstlane(b_dst + (l - kDAInst) * 1024));
-    }
+    if (l < kDAInst)
+        lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride,
+                          stage_lds + (x.wave * kDAInst + l) * 1024);
+    else
+        lds_direct_load16(x.b_voff[l - kDAInst], x.bbase + kt * x.b_kstride,
+                          stage_lds + 256 * DBK * 4 + (x.wave * kDBInst + l - kDAInst) * 1024);
 }
 
 // Fragments of one 8-wide K group for a wave's 4 x 4 blocks: a[mb] holds
@@ -348,37 +359,35 @@ struct FragG {
     f32x4 b[4];
 };
 
-__device__ __forceinline__ void read_one(FragG &f, const float *As, const float *Bs, int g,
-                                         int idx, int wm, int wn, int lane)
+__device__ __forceinline__ void read_one(FragG &f, const float *stage, const DCtx &x, int g,
+                                         int idx)
 {
-    const int h = lane >> 5, c = lane & 31;
-    if (idx < 4) {
-        const int row = wm * 128 + idx * 32 + c;
-        f.a[idx] = *reinterpret_cast<const f32x4 *>(As + row * DBK +
-                                                    (((2 * g + h) ^ a_swz4(row)) << 2));
-    } else {
-        const int j = idx - 4;
-        f.b[j] = *reinterpret_cast<const f32x4 *>(Bs + (8 * g + 4 * h + j) * 256 + wn * 128 + 4 * c);
-    }
+    const char *st = reinterpret_cast<const char *>(stage);
+    if (idx < 4)
+        f.a[idx] = *reinterpret_cast<const f32x4 *>(st + (g ? x.rdA1 : x.rdA0) + idx * 2048);
+    else
+        f.b[idx - 4] = *reinterpret_cast<const f32x4 *>(st + x.rdB + (8 * g + (idx - 4)) * 1024);
 }
 
-// The 64 MFMAs of group `cur`; after every 8th the next read of `nxt`, and
-// (if do_loads) after every 8th + 4 one LDS-direct load of a later tile.
+// The 64 MFMAs of group `cur`: the 8 reads of `nxt` go out after MFMAs
+// 0, 2, .., 14 (well ahead of their use), and (if loads) the 8 LDS-direct
+// loads of a later tile after MFMAs 20, 24, .., 48.  sched_barrier(0) pins
+// that order.
 __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[4][4], const FragG &cur, FragG &nxt,
-                                               const float *As, const float *Bs, int g_next,
-                                               int wm, int wn, int lane, float *load_stage,
-                                               const DSrc &src, int64_t k0, int64_t ldb,
-                                               int wave, bool do_loads)
+                                               const float *rstage, const DCtx &x, int g_next,
+                                               uint32_t lstage, int64_t kload, bool loads)
 {
 #pragma unroll
     for (int q = 0; q < 64; ++q) {
         const int j = q >> 4, mb = (q >> 2) & 3, nb = q & 3;
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[mb][j], cur.b[j][nb], acc[mb][nb],
                                                             0, 0, 0);
-        if ((q & 7) == 0 || (q & 7) == 4) {
+        const bool rd = q < 16 && (q & 1) == 0;
+        const bool ld = loads && q >= 20 && q < 52 && (q & 3) == 0;
+        if (rd || ld) {
             __builtin_amdgcn_sched_barrier(0);
-            if ((q & 7) == 0) read_one(nxt, As, Bs, g_next, q >> 3, wm, wn, lane);
-            else if (do_loads) issue_tile_direct(load_stage, src, k0, ldb, wave, q >> 3, 1);
+            if (rd) read_one(nxt, rstage, x, g_next, q >> 1);
+            if (ld) load_one(x, lstage, kload, (q - 20) >> 2);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -397,23 +406,35 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, c = lane & 31;
 
-    DSrc src;
+    DCtx x;
+    x.wave = wave;
+    x.lds0 = lds_offset(lds);
+    x.abase = reinterpret_cast<const char *>(A + m0 * lda);
+    x.bbase = reinterpret_cast<const char *>(B + n0);
+    x.a_kstride = DBK * 4;
+    x.b_kstride = DBK * ldb * 4;
 #pragma unroll
     for (int i = 0; i < kDAInst; ++i) {
         const int p = (wave * kDAInst + i) * 64 + lane;     // LDS chunk this lane fills
         const int row = p >> 2, slot = p & 3;
-        const int c = slot ^ a_swz4(row);
-        const int64_t r = (m0 + row < M) ? m0 + row : M - 1;
-        src.a[i] = A + r * lda + 4 * c;
+        const int cc = slot ^ a_swz4(row);
+        const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
+        x.a_voff[i] = static_cast<uint32_t>((r * lda + 4 * cc) * 4);
     }
 #pragma unroll
     for (int i = 0; i < kDBInst; ++i) {
         const int p = (wave * kDBInst + i) * 64 + lane;
         const int row = p >> 6, slot = p & 63;
-        const int64_t col = (n0 + 4 * slot < N) ? n0 + 4 * slot : N - 4;
-        src.b[i] = B + row * ldb + col;
+        const int64_t col = (n0 + 4 * slot < N) ? 4 * slot : N - 4 - n0;
+        x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 4);
     }
+    // Rows this lane reads are wm*128 + 32*idx + c: their swizzle is a_swz4(c).
+    const int swz = a_swz4(c);
+    x.rdA0 = (wm * 128 + c) * DBK * 4 + (((0 + h) ^ swz) << 4);
+    x.rdA1 = (wm * 128 + c) * DBK * 4 + (((2 + h) ^ swz) << 4);
+    x.rdB = 256 * DBK * 4 + 4 * h * 1024 + (wn * 128 + 4 * c) * 4;
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -425,35 +446,37 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
 
     const int64_t ktiles = K / DBK;
     auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * kDStageFloats; };
+    auto lstage = [&](int64_t kt) {
+        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * kDStageFloats * 4;
+    };
+    auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
 
+    // Prologue: tiles 0..2 in flight (re-fetching the last tile past the
+    // end), wait for tile 0, read its first group.
 #pragma unroll
     for (int s = 0; s < DSTAGES - 1; ++s)
-        if (s < ktiles) issue_tile_direct(stage(s), src, s * DBK, ldb, wave, 0, kDPerTile);
-    if (ktiles >= DSTAGES - 1) wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
-    else wait_lds_vm_barrier<0>();
+#pragma unroll
+        for (int l = 0; l < kDPerTile; ++l) load_one(x, lstage(s), kclamp(s), l);
+    wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
 
     FragG f0, f1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) read_one(f0, stage(0), stage(0) + 256 * DBK, 0, i, wm, wn, lane);
+    for (int i = 0; i < 8; ++i) read_one(f0, stage(0), x, 0, i);
 
     // Tile kt: MFMAs on group 0 with group 1's reads and the loads of tile
     // kt + 3 slotted in (its stage was last read in tile kt - 1, finished by
     // every wave before the previous barrier) | wait for tile kt + 1 and for
     // this wave's reads, barrier | MFMAs on group 1 with the reads of group 0
-    // of tile kt + 1 (in the last tile a harmless re-read of this stage).
+    // of tile kt + 1 (in the last tile: reads of a landed stage, unused).
     for (int64_t kt = 0; kt < ktiles; ++kt) {
-        float *cur = stage(kt);
         const int64_t nxt = kt + DSTAGES - 1;
-        mfma_phase_f32(acc, f0, f1, cur, cur + 256 * DBK, 1, wm, wn, lane, stage(nxt), src,
-                       nxt * DBK, ldb, wave, nxt < ktiles);
-        if (nxt < ktiles) wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
-        else wait_lds_vm_barrier<0>();
-        float *n1 = stage(kt + 1 < ktiles ? kt + 1 : kt);
-        mfma_phase_f32(acc, f1, f0, n1, n1 + 256 * DBK, 0, wm, wn, lane, n1, src, 0, ldb, wave,
-                       false);
+        mfma_phase_f32(acc, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
+        wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+        mfma_phase_f32(acc, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
     }
+    // No LDS-direct load may still be writing LDS when the work-group ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    const int h = lane >> 5, c = lane & 31;
     const int64_t col = n0 + wn * 128 + 4 * c;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -486,8 +509,10 @@ namespace mi355gemm {
 bool supports_mfma_f32_direct(const Problem &p)
 {
     const auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    // Lane offsets of the scalar-base loads are 32-bit byte offsets within a
+    // 256-row panel of A and a 16-row panel of B.
     return p.K % 16 == 0 && p.N % 4 == 0 && p.lda % 4 == 0 && p.ldb % 4 == 0 && al(p.A) &&
-           al(p.B);
+           al(p.B) && p.lda < (int64_t(1) << 22) && p.ldb < (int64_t(1) << 26);
 }
 
 hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s)
