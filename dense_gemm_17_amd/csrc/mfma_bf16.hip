@@ -240,36 +240,45 @@ void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restric
 // ---------------------------------------------------------------------------
 // Direct variant: global -> LDS with gfx950's LDS-direct 128-bit loads
 // (global_load_lds_dwordx4), no register staging and no LDS write
-// instructions, into a ring of kStages LDS stages so that the loads for tile
-// t + kStages - 1 are in flight while tile t is multiplied.  One such load
-// per wave writes 1 KiB of LDS at consecutive 16-byte slots in lane order;
+// instructions, into a ring of four 32-wide K stages so that the loads for
+// tile t + 3 are in flight while tile t is multiplied.  One such load per
+// wave writes 1 KiB of LDS at consecutive 16-byte slots in lane order;
 // choosing which global chunk each lane fetches realises the same swizzled
-// layouts as above.  Shapes: K a multiple of the K step, N a multiple of 8,
-// 16-byte aligned A and B with lda and ldb multiples of 8 (the dispatch table
-// checks this).  Rows of A past M and columns of B past N are fetched from
-// the last valid row / chunk instead (their products land only in rows and
-// columns of C that are not stored).
+// layouts as above.  Operand fragments are read one 16-wide K slice ahead
+// (across the tile boundary), each read and each load slotted between
+// MFMAs; one barrier per tile.
+//
+// Instruction economy: the loads use the scalar-base form (wave-uniform base
+// advanced once per tile + a fixed 32-bit lane offset), the reads use a few
+// lane bases plus immediate offsets (the swizzles of the rows a lane reads
+// depend only on the lane), and the loads past the last tile re-fetch the
+// last tile into a stage nobody reads again instead of being branched
+// around.
+//
+// Shapes: K a multiple of 32, N a multiple of 8, 16-byte aligned A and B
+// with lda and ldb multiples of 8, lane offsets within 32 bits (256 * lda
+// and 32 * ldb below 2^31 elements).  Rows of A past M and columns of B past
+// N are fetched from the last valid row / chunk (their products land only
+// in rows and columns of C that are not stored).
 
-template <int kBK>
-struct DirectShape {
-    static constexpr int kAInst = BM * kBK * 2 / 1024 / 4;   // LDS-direct loads per wave for A
-    static constexpr int kBInst = kBK * BN * 2 / 1024 / 4;   // ... for B
-    static constexpr int kPerTile = kAInst + kBInst;
-    static constexpr int kStageElems = BM * kBK + kBK * BN;  // bf16 elements per stage
-};
+constexpr int DBK = 32;
+constexpr int DSTAGES = 4;
+constexpr int kDAInst = BM * DBK * 2 / 1024 / 4;   // LDS-direct loads per wave per tile (A): 4
+constexpr int kDBInst = DBK * BN * 2 / 1024 / 4;   // ... (B): 4
+constexpr int kDPerTile = kDAInst + kDBInst;
+constexpr int kDStageElems = BM * DBK + DBK * BN;  // bf16 elements per stage
 
-// One LDS-direct 128-bit load: M0 holds the wave's LDS destination, each lane
-// fetches 16 bytes from `src` and the hardware writes them to M0 + 16 * lane.
-// Written as inline assembly on purpose: the compiler's wait-count pass does
-// not see these loads, so it does not drain them before every LDS read; the
-// kernel waits for them itself (wait_all_lds_and_vm_then_barrier) with exact
-// counts.
-// M0 is declared clobbered.  The s_nop covers the M0-write hazard.
-__device__ __forceinline__ void lds_direct_load16(const void *src, uint32_t lds_addr)
+// One LDS-direct 128-bit load as inline assembly, scalar-base form: lane i
+// reads 16 bytes at sbase + voff and they land at LDS byte M0 + 16 i.  The
+// compiler's wait-count pass does not see these loads (it would drain them
+// before every LDS read); the kernel waits for them itself with exact
+// counts.  M0 is declared clobbered (nothing else in these kernels keeps a
+// value in it); the s_nop covers the M0-write hazard.
+__device__ __forceinline__ void lds_direct_load16(uint32_t voff, const void *sbase, uint32_t m0v)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(src), "s"(lds_addr)
+                 : "v"(voff), "s"(sbase), "s"(m0v)
                  : "memory", "m0");
 }
 
@@ -279,20 +288,25 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
         (const __attribute__((address_space(3))) void *)(p)));
 }
 
-template <int kBK>
-__device__ __forceinline__ void issue_tile(uint16_t *stage, const uint16_t *const (&asrc)[DirectShape<kBK>::kAInst],
-                                           const uint16_t *const (&bsrc)[DirectShape<kBK>::kBInst],
-                                           int64_t k0, int64_t ldb, int wave)
+// Everything a wave needs to address its loads and reads.
+struct DCtx {
+    uint32_t a_voff[kDAInst], b_voff[kDBInst];   // lane offsets (bytes) of each load
+    const char *abase, *bbase;                   // tile (k = 0) bases, wave-uniform
+    int64_t a_kstride, b_kstride;                // bytes per K step
+    uint32_t lds0;                               // LDS byte address of stage 0
+    int wave;
+    uint32_t rdA[2];                             // lane read offsets: A, per K slice
+    uint32_t rdB[4];                             // lane read offsets: B, per 32-column block
+};
+
+__device__ __forceinline__ void load_one(const DCtx &x, uint32_t stage_lds, int64_t kt, int l)
 {
-    using S = DirectShape<kBK>;
-    const uint32_t a_dst = lds_offset(stage) + wave * S::kAInst * 1024;
-    const uint32_t b_dst = lds_offset(stage + BM * kBK) + wave * S::kBInst * 1024;
-#pragma unroll
-    for (int i = 0; i < S::kAInst; ++i)
-        lds_direct_load16(asrc[i] + k0, __builtin_amdgcn_readfirstlane(a_dst + i * 1024));
-#pragma unroll
-    for (int i = 0; i < S::kBInst; ++i)
-        lds_direct_load16(bsrc[i] + k0 * ldb, __builtin_amdgcn_readfirstlane(b_dst + i * 1024));
+    if (l < kDAInst)
+        lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride,
+                          stage_lds + (x.wave * kDAInst + l) * 1024);
+    else
+        lds_direct_load16(x.b_voff[l - kDAInst], x.bbase + kt * x.b_kstride,
+                          stage_lds + BM * DBK * 2 + (x.wave * kDBInst + l - kDAInst) * 1024);
 }
 
 // Operand fragments of one 16-wide K slice for a wave's 4 x 4 MFMA blocks:
@@ -303,32 +317,26 @@ struct Frag16 {
     bf16x4 blo[4], bhi[4];
 };
 
-// Slice reads are issued one at a time (12 per slice: 4 A reads, 8 B
-// transposing reads) so they can be slotted between MFMAs.
-template <int kBK>
-struct SliceReader {
-    const uint16_t *As, *Bs;
-    int s, wm, wn, lane;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-    __device__ __forceinline__ void read(Frag16 &f, int j) const
-    {
-        const int h = lane >> 5, c = lane & 31;
-        const int i = lane & 15, nhalf = (lane >> 4) & 1;
-        if (j < 4) {
-            const int row = wm * 128 + j * 32 + c;
-            const u16x8 v = *reinterpret_cast<const u16x8 *>(
-                As + row * kBK + (((2 * s + h) ^ a_swz<kBK / 8>(row)) << 3));
-            f.a[j] = __builtin_bit_cast(bf16x8, v);
-        } else {
-            const int nb = (j - 4) >> 1, upper = (j - 4) & 1;
-            const int k_lo = 16 * s + 8 * h + (i >> 2);
-            const int n = wn * 128 + nb * 32 + nhalf * 16 + 4 * (i & 3);
-            const uint16_t *p0 = Bs + k_lo * BN + (((n >> 3) ^ b_swz(k_lo)) << 3) + (n & 7);
-            if (upper) f.bhi[nb] = read_tr(p0 + 4 * BN);
-            else f.blo[nb] = read_tr(p0);
-        }
+// Read j (0..11) of slice s from the stage at `stage`: j < 4 is A block j,
+// then B block (j - 4) / 2, lower / upper four k.
+__device__ __forceinline__ void read_one(Frag16 &f, const uint16_t *stage, const DCtx &x, int s,
+                                         int j)
+{
+    const char *st = reinterpret_cast<const char *>(stage);
+    if (j < 4) {
+        const u16x8 v = *reinterpret_cast<const u16x8 *>(st + x.rdA[s] + j * 2048);
+        f.a[j] = __builtin_bit_cast(bf16x8, v);
+    } else {
+        const int nb = (j - 4) >> 1, upper = (j - 4) & 1;
+        const char *p = st + x.rdB[nb] + s * (16 * BN * 2) + upper * (4 * BN * 2);
+        const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4_t *)((__attribute__((address_space(3))) char *)(p)));
+        if (upper) f.bhi[nb] = v;
+        else f.blo[nb] = v;
     }
-};
+}
 
 __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frag16 &f, int q)
 {
@@ -337,89 +345,86 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frag16 &f, i
     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], b, acc[mb][nb], 0, 0, 0);
 }
 
-// The 16 MFMAs of slice `cur`, with the 12 reads of slice `nxt` slotted
-// after MFMAs 0..11 and (if do_loads) this wave's LDS-direct loads of a later
-// tile after every other MFMA.  sched_barrier(0) pins that order so that the
-// matrix unit keeps running while reads and loads are in flight; the first
-// MFMA waits only for `cur`, whose reads went out a whole slice earlier.
-template <int kBK>
-__device__ __forceinline__ void mfma_phase(
-    f32x16 (&acc)[4][4], const Frag16 &cur, Frag16 &nxt, const SliceReader<kBK> &rd,
-    uint16_t *stage, const uint16_t *const (&asrc)[DirectShape<kBK>::kAInst],
-    const uint16_t *const (&bsrc)[DirectShape<kBK>::kBInst], int64_t k0, int64_t ldb, int wave,
-    bool do_loads)
+// The 16 MFMAs of one slice: the 12 reads of the next slice go out after
+// MFMAs 0..11 and (if loads) this wave's 8 LDS-direct loads of a later tile
+// after every other MFMA.  sched_barrier(0) pins that order so the matrix
+// unit keeps running while reads and loads are in flight.
+__device__ __forceinline__ void mfma_phase(f32x16 (&acc)[4][4], const Frag16 &cur, Frag16 &nxt,
+                                           const uint16_t *rstage, const DCtx &x, int s_next,
+                                           uint32_t lstage, int64_t kload, bool loads)
 {
-    using S = DirectShape<kBK>;
-    constexpr int kLoads = S::kAInst + S::kBInst;
-    static_assert(16 % kLoads == 0, "loads must divide the MFMA count");
-    constexpr int kEvery = 16 / kLoads;
-    const uint32_t a_dst = lds_offset(stage) + wave * S::kAInst * 1024;
-    const uint32_t b_dst = lds_offset(stage + BM * kBK) + wave * S::kBInst * 1024;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         mfma_one(acc, cur, q);
         __builtin_amdgcn_sched_barrier(0);
-        if (q < 12) rd.read(nxt, q);
-        if (q % kEvery == kEvery - 1 && do_loads) {
-            const int l = q / kEvery;
-            if (l < S::kAInst)
-                lds_direct_load16(asrc[l] + k0, __builtin_amdgcn_readfirstlane(a_dst + l * 1024));
-            else
-                lds_direct_load16(bsrc[l - S::kAInst] + k0 * ldb,
-                                  __builtin_amdgcn_readfirstlane(b_dst + (l - S::kAInst) * 1024));
-        }
+        if (q < 12) read_one(nxt, rstage, x, s_next, q);
+        if (loads && (q & 1)) load_one(x, lstage, kload, q >> 1);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
+// This wave's LDS reads complete (lgkmcnt 0) and its LDS-direct loads down
+// to kCntVm in flight, then the work-group barrier.  Inline assembly so that
+// the compiler's wait-count pass cannot weaken the LDS part: it is what
+// guarantees that no wave still reads a stage another wave refills after
+// the barrier.
 template <int kCntVm>
-__device__ __forceinline__ void wait_all_lds_and_vm_then_barrier()
+__device__ __forceinline__ void wait_lds_vm_barrier()
 {
-    // This wave's LDS reads complete (lgkmcnt 0) and its LDS-direct loads
-    // down to kCntVm in flight, then the work-group barrier.  Inline assembly
-    // so that the compiler's wait-count pass cannot weaken the LDS part: it
-    // is what guarantees that no wave still reads a stage another wave
-    // refills after the barrier.
     static_assert(kCntVm >= 0 && kCntVm <= 63, "vmcnt is six bits");
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(kCntVm) : "memory");
 }
 
-template <int kBK, int kStages>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
                              int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
                              float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n)
 {
-    using S = DirectShape<kBK>;
-    static_assert(kBK == 32, "two 16-wide K slices per tile");
-    static_assert(kStages >= 3, "the ring needs a stage being filled, one in flight, one read");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[kStages * S::kStageElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * kDStageElems];
 
     const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
     const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, c = lane & 31;
+    const int i16 = lane & 15, nhalf = (lane >> 4) & 1;
 
-    // Per-lane source of every LDS-direct load of this wave, at k = 0.
-    constexpr int kAChunksPerRow = kBK / 8;
-    const uint16_t *asrc[S::kAInst];
-    const uint16_t *bsrc[S::kBInst];
+    DCtx x;
+    x.wave = wave;
+    x.lds0 = lds_offset(lds);
+    x.abase = reinterpret_cast<const char *>(A + m0 * lda);
+    x.bbase = reinterpret_cast<const char *>(B + n0);
+    x.a_kstride = DBK * 2;
+    x.b_kstride = DBK * ldb * 2;
 #pragma unroll
-    for (int i = 0; i < S::kAInst; ++i) {
-        const int p = (wave * S::kAInst + i) * 64 + lane;    // LDS chunk this lane fills
-        const int row = p / kAChunksPerRow, slot = p % kAChunksPerRow;
-        const int c = slot ^ a_swz<kAChunksPerRow>(row);
-        const int64_t r = (m0 + row < M) ? m0 + row : M - 1;
-        asrc[i] = A + r * lda + 8 * c;
+    for (int i = 0; i < kDAInst; ++i) {
+        const int p = (wave * kDAInst + i) * 64 + lane;    // LDS chunk this lane fills
+        const int row = p >> 2, slot = p & 3;
+        const int cc = slot ^ a_swz<4>(row);
+        const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
+        x.a_voff[i] = static_cast<uint32_t>((r * lda + 8 * cc) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < S::kBInst; ++i) {
-        const int p = (wave * S::kBInst + i) * 64 + lane;
+    for (int i = 0; i < kDBInst; ++i) {
+        const int p = (wave * kDBInst + i) * 64 + lane;
         const int row = p >> 5, slot = p & 31;
-        const int c = slot ^ b_swz(row);
-        const int64_t col = (n0 + 8 * c < N) ? n0 + 8 * c : N - 8;
-        bsrc[i] = B + row * ldb + col;
+        const int cc = slot ^ b_swz(row);
+        const int64_t col = (n0 + 8 * cc < N) ? 8 * cc : N - 8 - n0;
+        x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 2);
+    }
+    // A rows this lane reads are wm*128 + 32*j + c: their swizzle is a_swz<4>(c).
+    const int aswz = a_swz<4>(c);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        x.rdA[s] = (wm * 128 + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+    // B rows this lane points at are 16s + 8h + i16/4 (+4): swizzle b_swz(i16/4).
+    const int bswz = b_swz(i16 >> 2);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const int n = wn * 128 + nb * 32 + nhalf * 16 + 4 * (i16 & 3);
+        x.rdB[nb] = BM * DBK * 2 + (8 * h + (i16 >> 2)) * BN * 2 + (((n >> 3) ^ bswz) << 4) +
+                    (n & 7) * 2;
     }
 
     f32x16 acc[4][4];
@@ -430,43 +435,39 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int64_t ktiles = K / kBK;
-    auto stage = [&](int64_t kt) { return lds + (kt % kStages) * S::kStageElems; };
+    const int64_t ktiles = K / DBK;
+    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * kDStageElems; };
+    auto lstage = [&](int64_t kt) {
+        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * kDStageElems * 2;
+    };
+    auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
 
-    // Prologue: tiles 0 .. kStages-2 in flight, wait for tile 0, read its
-    // first slice.
+    // Prologue: tiles 0..2 in flight (re-fetching the last tile past the
+    // end), wait for tile 0, read its first slice.
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-        if (s < ktiles) issue_tile<kBK>(stage(s), asrc, bsrc, s * kBK, ldb, wave);
-    if (ktiles >= kStages - 1) wait_all_lds_and_vm_then_barrier<(kStages - 2) * S::kPerTile>();
-    else wait_all_lds_and_vm_then_barrier<0>();
+    for (int st = 0; st < DSTAGES - 1; ++st)
+#pragma unroll
+        for (int l = 0; l < kDPerTile; ++l) load_one(x, lstage(st), kclamp(st), l);
+    wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
 
     Frag16 f0, f1;
-    {
-        const SliceReader<kBK> rd{stage(0), stage(0) + BM * kBK, 0, wm, wn, lane};
 #pragma unroll
-        for (int j = 0; j < 12; ++j) rd.read(f0, j);
-    }
+    for (int j = 0; j < 12; ++j) read_one(f0, stage(0), x, 0, j);
 
     // Tile kt:  MFMAs on slice 0 with the reads of slice 1 and the loads of
-    // tile kt + kStages - 1 slotted in (that stage was last read in tile
-    // kt - 1, which every wave finished before the previous barrier) | wait
-    // until tile kt + 1 has landed everywhere and this wave's reads are done,
-    // barrier | MFMAs on slice 1 with the reads of slice 0 of tile kt + 1 (in
-    // the last tile, a harmless re-read of the current stage).
+    // tile kt + 3 slotted in (that stage was last read in tile kt - 1, which
+    // every wave finished before the previous barrier) | wait until tile
+    // kt + 1 has landed everywhere and this wave's reads are done, barrier |
+    // MFMAs on slice 1 with the reads of slice 0 of tile kt + 1 (in the last
+    // tile: reads of a landed stage, unused).
     for (int64_t kt = 0; kt < ktiles; ++kt) {
-        uint16_t *cur = stage(kt);
-        const int64_t nxt = kt + kStages - 1;
-        const SliceReader<kBK> rd1{cur, cur + BM * kBK, 1, wm, wn, lane};
-        mfma_phase<kBK>(acc, f0, f1, rd1, stage(nxt), asrc, bsrc, nxt * kBK, ldb, wave,
-                        nxt < ktiles);
-        // In flight after this: tiles kt + 2 .. min(nxt, ktiles - 1).
-        if (nxt < ktiles) wait_all_lds_and_vm_then_barrier<(kStages - 2) * S::kPerTile>();
-        else wait_all_lds_and_vm_then_barrier<0>();
-        uint16_t *n1 = stage(kt + 1 < ktiles ? kt + 1 : kt);
-        const SliceReader<kBK> rd0{n1, n1 + BM * kBK, 0, wm, wn, lane};
-        mfma_phase<kBK>(acc, f1, f0, rd0, n1, asrc, bsrc, 0, ldb, wave, false);
+        const int64_t nxt = kt + DSTAGES - 1;
+        mfma_phase(acc, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
+        wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+        mfma_phase(acc, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
     }
+    // No LDS-direct load may still be writing LDS when the work-group ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
 }
@@ -501,14 +502,17 @@ namespace mi355gemm {
 bool supports_mfma_bf16_direct(const Problem &p)
 {
     const auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
-    return p.K % 32 == 0 && p.N % 8 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 && al(p.A) && al(p.B);
+    // Lane offsets of the scalar-base loads are 32-bit byte offsets within a
+    // 256-row panel of A and a 32-row panel of B.
+    return p.K % 32 == 0 && p.N % 8 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 && al(p.A) &&
+           al(p.B) && p.lda < (int64_t(1) << 23) && p.ldb < (int64_t(1) << 26);
 }
 
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
     if (tm * tn > kMaxBlocks || !supports_mfma_bf16_direct(p)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((mfma_bf16_direct_kernel<32, 4>), dim3(static_cast<uint32_t>(tm * tn)),
+    hipLaunchKernelGGL(mfma_bf16_direct_kernel, dim3(static_cast<uint32_t>(tm * tn)),
                        dim3(kThreads), 0, s, p.M, p.N, p.K, static_cast<const uint16_t *>(p.A),
                        p.lda, static_cast<const uint16_t *>(p.B), p.ldb, p.C, p.ldc, tm, tn);
     return hipGetLastError();
