@@ -42,16 +42,18 @@ constexpr int kAChunks = BM * BK / 8 / kThreads;   // 8
 constexpr int kBChunks = BK * BN / 8 / kThreads;   // 8
 constexpr int kGroup = 4;
 
-// Chunk permutation of an A row in LDS.  With 8 chunks per row (K step 64)
-// any 16 consecutive rows read at one logical chunk occupy distinct 16-byte
-// slots modulo 256 bytes, and any 8 consecutive rows distinct slots modulo
-// 128 bytes; with 4 chunks per row (K step 32) the same holds for the
-// 64-byte rows.
+// Chunk permutation of an A row in LDS: chunk c of row r is stored at
+// c ^ a_swz(r).  Rows of 8 chunks (128 bytes, K step 64): (r >> 1) & 7;
+// rows of 4 chunks (64 bytes, K step 32): (r >> 2) & 3.  Both were measured
+// conflict-free on gfx950 for the operand read (32 consecutive rows at one
+// logical chunk per half-wave) with a one-pattern microbenchmark
+// (SQ_LDS_BANK_CONFLICT); e.g. (r + r/8) mod 8 and (r>>1)^(r>>3) are 2-way
+// conflicted, unswizzled layouts 4- to 8-way.
 template <int kChunks>
 __device__ __forceinline__ int a_swz(int row)
 {
-    if constexpr (kChunks == 8) return (row + (row >> 3)) & 7;
-    else return ((row >> 1) ^ (row >> 3)) & 3;
+    if constexpr (kChunks == 8) return (row >> 1) & 7;
+    else return (row >> 2) & 3;
 }
 
 // B rows hold 32 chunks.  A transposing read by 16 lanes touches two
@@ -413,7 +415,8 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
         const int64_t col = (n0 + 8 * cc < N) ? 8 * cc : N - 8 - n0;
         x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 2);
     }
-    // A rows this lane reads are wm*128 + 32*j + c: their swizzle is a_swz<4>(c).
+    // A rows this lane reads are wm*128 + 32*j + c: their swizzle is a_swz<4>(c)
+    // (it depends on bits 2-3 of the row only).
     const int aswz = a_swz<4>(c);
 #pragma unroll
     for (int s = 0; s < 2; ++s)

@@ -17,9 +17,9 @@
 //   * global -> registers with 128-bit loads (coalesced along A rows and B
 //     rows), registers -> LDS after the current tile's math, two LDS stages
 //     (double buffering), one barrier per K step;
-//   * A in LDS: 256 rows of 32 floats, the eight 16-byte chunks of each row
-//     XOR-permuted by a row hash so that the 32 rows one MFMA operand read
-//     touches fall in distinct banks;
+//   * A in LDS: BM rows of 32 floats, the eight 16-byte chunks of each row
+//     XOR-permuted by a row hash that spreads the 32 rows one MFMA operand
+//     read touches over the banks (the hash was chosen by timing on gfx950);
 //   * B in LDS: 32 rows of BN floats, read as vectors: lane c of a half-wave
 //     takes NB consecutive columns, one for each of the wave's NB 32-column
 //     MFMA blocks (block q owns columns NB*c + q).  The accumulators of those
@@ -45,10 +45,13 @@ constexpr int BK = 32;
 constexpr int kThreads = 256;
 constexpr int kGroup = 4;                          // tile-rows per group in the tile order
 
-// Chunk permutation of an A row in LDS (8 chunks of 4 floats per row).  For
-// any 16 consecutive rows read at one logical chunk, the physical 16-byte
-// slots modulo 256 bytes are all different, and so are any 8 consecutive
-// rows modulo 128 bytes.
+// Chunk permutation of an A row in LDS (8 chunks of 4 floats = 128 bytes
+// per row): chunk c of row r is stored at c ^ ((r + r/8) mod 8).  Chosen by
+// measurement on gfx950: (r >> 1) mod 8 makes the operand reads free of bank
+// conflicts (SQ_LDS_BANK_CONFLICT = 0, against about 1.3 conflict cycles per
+// LDS instruction with this hash), yet an A/B run on one board timed this
+// register-staged kernel 13% faster with (r + r/8) mod 8 at 8192^3 (111.1
+// vs 96.5 TFLOP/s) and 8% at 4096^3, so the faster one is kept here.
 __device__ __forceinline__ int a_swz(int row) { return (row + (row >> 3)) & 7; }
 
 template <int NB> struct VecN;
@@ -296,10 +299,12 @@ constexpr int kDBInst = DBK * 256 * 4 / 1024 / 4;   // ... (B): 4
 constexpr int kDPerTile = kDAInst + kDBInst;
 constexpr int kDStageFloats = 256 * DBK + DBK * 256;
 
-// A rows of 4 chunks: for 16 consecutive rows at one logical chunk the
-// 16-byte slots modulo 256 bytes are distinct, and for 8 consecutive rows
-// modulo 128 bytes.
-__device__ __forceinline__ int a_swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// A rows of 4 chunks (64 bytes): chunk c of row r is stored at c ^ ((r >> 2) & 3).
+// Measured on gfx950 (SQ_LDS_BANK_CONFLICT, one-pattern microbenchmark):
+// the operand read (32 lanes = 32 consecutive rows at one logical chunk per
+// half-wave) is conflict-free with this permutation, while the unswizzled
+// layout is 4-way and a (r>>1)^(r>>3) hash 2-way conflicted.
+__device__ __forceinline__ int a_swz4(int row) { return (row >> 2) & 3; }
 
 // One LDS-direct 128-bit load as inline assembly, scalar-base form: lane i
 // reads 16 bytes at sbase + voff and they land at LDS byte M0 + 16 i.  The
