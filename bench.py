@@ -119,11 +119,13 @@ def ingest_counters(fetch_dir: str, write_dir: str):
                                   "bytes_per_launch": round(fb + wb), "dispatches": len(f),
                                   "source_digest": source_digest(kernel)}
     with open(TRAFFIC_FILE, "w") as fh:
-        fh.write("# HBM bytes per launch at 8192^3, from rocprofv3 FETCH_SIZE / WRITE_SIZE\n")
-        fh.write("# runs of: python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline "
-                 "--copy-calibration\n")
-        fh.write("# (one run per counter), scaled by the counters' reading of a 256 MiB "
-                 "device copy.\n")
+        run = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration"
+        fh.write("# HBM bytes per launch at 8192^3, one rocprofv3 run per counter:\n")
+        for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            fh.write(f"#   timeout -s KILL 90 rocprofv3 --pmc {ctr} -d {d} -o pmc "
+                     f"--output-format csv -- {run}\n")
+        fh.write("# then: python bench.py --ingest-counters <fetch dir> <write dir>.\n")
+        fh.write("# Each counter is scaled by its reading of a 256 MiB device copy.\n")
         fh.write(json.dumps(rec, indent=1) + "\n")
     print(json.dumps(rec))
 

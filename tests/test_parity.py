@@ -269,3 +269,31 @@ def test_non_default_stream():
     if rows is not None:
         Ch = Ch[rows]
     assert oracle.normalized_error(Ch, Cref, D)[0] <= GATE
+
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [("f32", 32768, 256, 32768), ("bf16", 40960, 512, 32768)])
+def test_large_operands_64bit_offsets(dtype, M, N, K):
+    """A spans more than 2^31 bytes (4 GiB fp32, 2.5 GiB bf16), so row
+    offsets need 64-bit arithmetic.  Every kernel that takes the shape, and
+    the table's choice, is checked on sampled rows (first, last, tile
+    boundaries, random) against the oracle."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    gen = workloads.generator(80)
+    A = workloads.draw((M, K), ("uniform", 1.0), gen).to(tdt)
+    B = workloads.draw((K, N), ("uniform", 1.0), gen).to(tdt)
+    rows = sample_rows(M, seed=3)
+    fn = oracle.gemm_f32 if dtype == "f32" else oracle.gemm_bf16
+    Cref, D = fn(workloads.as_numpy_operand(A[rows]), workloads.as_numpy_operand(B))
+    Ad, Bd = A.to(DEV), B.to(DEV)
+    del A
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    for kernel in [None] + [k for k in kernels_for(dtype) if takes(k, Ad, Bd)]:
+        C.fill_(float("nan"))
+        say(f"[large] {dtype} {M}x{N}x{K} kernel={kernel or 'table'}")
+        run(Ad, Bd, kernel, out=C)
+        e, at, _ = oracle.normalized_error(C[rows].cpu().numpy(), Cref, D)
+        say(f"[large] e={e:.3e} at={at}")
+        assert e <= GATE, (kernel, e, at)
+    del Ad, Bd, C
+    torch.cuda.empty_cache()
