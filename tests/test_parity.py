@@ -204,6 +204,37 @@ def test_identity_and_permutation_exact(dtype):
             assert torch.equal(C.cpu(), B.float()[perm])
 
 
+# Skinny family: every compiled row count (1, 2, 4, 8, 16 after rounding up),
+# every strip width (the table picks 64/128/256-byte strips from N) and
+# work-group tier, K not a multiple of the 4-row blocks, for both element
+# types, plus one unaligned layout per case (element-load path).
+SKINNY_M = [1, 2, 3, 5, 8, 9, 16]
+SKINNY_NK = [(1000, 37), (4100, 260), (8200, 61), (16400, 36)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_skinny_configurations_exact(dtype):
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
+    gen = workloads.generator(81)
+    for (N, K) in SKINNY_NK:
+        B = workloads.small_int((K, N + 3), lo, hi, gen, tdt)
+        Bd_al = B[:, :N].contiguous().to(DEV)
+        Bd_un = B.to(DEV)[:, 1:N + 1]            # row stride N + 3, offset one element
+        for M in SKINNY_M:
+            A = workloads.small_int((M, K), lo, hi, gen, tdt)
+            exact = (A.to(torch.int64) @ B[:, :N].to(torch.int64)).to(torch.float64).numpy()
+            exact_un = (A.to(torch.int64) @ B[:, 1:N + 1].to(torch.int64)).to(torch.float64).numpy()
+            Ad = A.to(DEV)
+            for Bd, ref, tag in ((Bd_al, exact, "aligned"), (Bd_un, exact_un, "unaligned")):
+                k = "skinny_f32" if dtype == "f32" else "skinny_bf16"
+                assert takes(k, Ad, Bd)
+                say(f"[skinny] {dtype} {M}x{N}x{K} {tag}")
+                C = run(Ad, Bd, k).cpu().numpy().astype(np.float64)
+                bad = np.argwhere(C != ref)
+                assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
+
+
 GUARD_CASES = [  # (M, N, K, extra A columns, extra B columns)
     (130, 200, 150, 13, 9), (5, 300, 64, 13, 9), (300, 257, 1000, 13, 9),
     (300, 264, 512, 16, 8), (257, 520, 96, 8, 24),
