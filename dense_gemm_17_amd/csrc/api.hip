@@ -33,6 +33,7 @@ const KernelInfo kKernels[] = {
     {"skinny_bf16", kBF16, launch_skinny_bf16, supports_skinny},
     {"valu_f32", kF32, launch_valu_f32, supports_any},
     {"mfma_f32_direct", kF32, launch_mfma_f32_direct, supports_mfma_f32_direct},
+    {"mfma_f32_direct128", kF32, launch_mfma_f32_direct128, supports_mfma_f32_direct},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -104,22 +105,24 @@ Verdict validate(const Problem &p)
 //     picked by an estimate of the time in work-group waves: a 256 x 256 tile
 //     runs one work-group per CU, a 128 x 128 tile two (each at half the
 //     CU's rate), over 256 CUs, each divided by the kernel's measured
-//     fraction of the matrix-core peak (LDS-direct 256: 0.91, register-staged
-//     256: 0.70, register-staged 128 with two per CU: 0.67).  The smaller tile
-//     wins when the larger one leaves CUs idle in its last wave (gpt-sized
-//     and ragged shapes).  The LDS-direct kernels are used wherever their
-//     layout conditions hold (bf16 and fp32 alike).
+//     fraction of the matrix-core peak at 8192^3 (LDS-direct 256: 0.96,
+//     LDS-direct 128: 0.946; register-staged 256: 0.70, register-staged 128:
+//     0.67).  The smaller tile wins when the larger one leaves CUs idle in
+//     its last wave (gpt-sized, small and ragged shapes).  The LDS-direct
+//     kernels are used wherever their layout conditions hold (bf16 and fp32
+//     alike).
 constexpr int64_t kCUs = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Relative time of a tiled launch: waves x per-work-group work / efficiency,
 // in units of one CU doing a 128 x 128 tile alone at full rate.
-int64_t tiled_cost(const Problem &p, int64_t tile, int64_t per_cu, int64_t eff_pct)
+// eff_permille: the kernel's fraction of peak, in thousandths.
+int64_t tiled_cost(const Problem &p, int64_t tile, int64_t per_cu, int64_t eff_permille)
 {
     const int64_t tiles = ceil_div(p.M, tile) * ceil_div(p.N, tile);
     const int64_t waves = ceil_div(tiles, kCUs * per_cu);
-    return waves * (tile / 128) * (tile / 128) * per_cu * 10000 / eff_pct;
+    return waves * (tile / 128) * (tile / 128) * per_cu * 1000000 / eff_permille;
 }
 
 int select_kernel(const Problem &p)
@@ -130,10 +133,12 @@ int select_kernel(const Problem &p)
         if (supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16_direct");
         return kernel_id("mfma_bf16");
     }
-    const bool direct = supports_mfma_f32_direct(p);
-    const int64_t big = tiled_cost(p, 256, 1, direct ? 91 : 70);
-    if (big <= tiled_cost(p, 128, 2, 67))
-        return kernel_id(direct ? "mfma_f32_direct" : "mfma_f32");
+    if (supports_mfma_f32_direct(p)) {
+        if (tiled_cost(p, 256, 1, 960) <= tiled_cost(p, 128, 2, 946))
+            return kernel_id("mfma_f32_direct");
+        return kernel_id("mfma_f32_direct128");
+    }
+    if (tiled_cost(p, 256, 1, 700) <= tiled_cost(p, 128, 2, 670)) return kernel_id("mfma_f32");
     return kernel_id("mfma_f32_128");
 }
 

@@ -39,6 +39,7 @@ hipError_t launch_valu_f32(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f32_direct128(const Problem &p, hipStream_t s);
 bool supports_mfma_f32_direct(const Problem &p);
 hipError_t launch_mfma_bf16(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s);

@@ -269,13 +269,19 @@ hipError_t launch_tiles(const Problem &p, hipStream_t s)
 }
 
 // ---------------------------------------------------------------------------
-// Direct variant (256 x 256 tile, K step 16, four LDS stages): global -> LDS
-// with LDS-direct 128-bit loads (no register staging, no LDS write
-// instructions) so the loads for tile t + 3 are in flight while tile t is
-// multiplied; operand fragments are read one 8-wide K group ahead, across
-// the tile boundary, each read and each load slotted between MFMAs; one
-// barrier per tile.  Same layouts and epilogue as the staged kernel (A rows
-// of 16 floats = 4 chunks, chunk-swizzled; B rows of 256 floats).
+// Direct variants (BM x BN tile of 256 x 256 or 128 x 128, K step 16, four
+// LDS stages): global -> LDS with LDS-direct 128-bit loads (no register
+// staging, no LDS write instructions) so the loads for tile t + 3 are in
+// flight while tile t is multiplied; operand fragments are read one 8-wide K
+// group ahead, across the tile boundary, each read and each load slotted
+// between MFMAs; one barrier per tile.  Four waves in a 2 x 2 grid, each
+// owning (BM/2) x (BN/2) of C as MB x NB blocks of 32 x 32.  Same layouts as
+// the staged kernel (A rows of 16 floats = 4 chunks, chunk-swizzled; B rows
+// of BN floats; B read NB columns at a time, interleaved over the blocks).
+// The 256 tile runs one work-group per CU (256 accumulators per lane); the
+// 128 tile (64 accumulators, 64 KB of LDS) runs two, so that one
+// work-group's MFMAs cover the other's barrier, and it leaves fewer CUs idle
+// on shapes whose 256-tile count is a poor multiple of 256.
 //
 // Instruction economy matters here: with one wave per SIMD every non-MFMA
 // instruction sits between two MFMAs.  So the loads use the scalar-base
@@ -292,12 +298,26 @@ hipError_t launch_tiles(const Problem &p, hipStream_t s)
 // columns of B past N are fetched from the last valid row / chunk (their
 // products land only in rows and columns of C that are not stored).
 
-constexpr int DBK = 16;           // K step of the direct variant
+constexpr int DBK = 16;           // K step of the direct variants
 constexpr int DSTAGES = 4;
-constexpr int kDAInst = 256 * DBK * 4 / 1024 / 4;   // LDS-direct loads per wave per tile (A): 4
-constexpr int kDBInst = DBK * 256 * 4 / 1024 / 4;   // ... (B): 4
-constexpr int kDPerTile = kDAInst + kDBInst;
-constexpr int kDStageFloats = 256 * DBK + DBK * 256;
+
+template <int BM, int BN>
+struct DTile {
+    static constexpr int kMB = BM / 64, kNB = BN / 64;          // blocks per wave
+    static constexpr int kAInst = BM * DBK * 4 / 1024 / 4;     // LDS-direct loads per wave per tile (A)
+    static constexpr int kBInst = DBK * BN * 4 / 1024 / 4;     // ... (B)
+    static constexpr int kPerTile = kAInst + kBInst;
+    static constexpr int kStageFloats = BM * DBK + DBK * BN;
+    static constexpr int kBChunksPerRow = BN / 4;
+    static constexpr int kQ = 4 * kMB * kNB;                    // MFMAs per 8-wide K group
+    static constexpr int kReads = kMB + 4;                      // fragment reads per group
+    // The reads of the next group go out after MFMAs 0, 2, 4, ..; the loads
+    // of a later tile after MFMAs kLoadQ0, kLoadQ0 + kLoadStep, ...
+    static constexpr int kLoadQ0 = BM == 256 ? 20 : 1;
+    static constexpr int kLoadStep = 4;
+    static_assert(2 * kReads <= kQ && kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ, "slots");
+    static_assert(kNB == 2 || kNB == 4, "B read width");
+};
 
 // A rows of 4 chunks (64 bytes): chunk c of row r is stored at c ^ ((r >> 2) & 3).
 // Measured on gfx950 (SQ_LDS_BANK_CONFLICT, one-pattern microbenchmark):
@@ -337,83 +357,103 @@ __device__ __forceinline__ void wait_lds_vm_barrier()
 }
 
 // Everything a wave needs to address its loads and reads.
+template <int BM, int BN>
 struct DCtx {
-    uint32_t a_voff[kDAInst], b_voff[kDBInst];   // lane offsets (bytes) of each load
-    const char *abase, *bbase;                   // tile (k = 0) bases, wave-uniform
-    int64_t a_kstride, b_kstride;                // bytes per K step
-    uint32_t lds0;                               // LDS byte address of stage 0
+    using T = DTile<BM, BN>;
+    uint32_t a_voff[T::kAInst], b_voff[T::kBInst];   // lane offsets (bytes) of each load
+    const char *abase, *bbase;                       // tile (k = 0) bases, wave-uniform
+    int64_t a_kstride, b_kstride;                    // bytes per K step
+    uint32_t lds0;                                   // LDS byte address of stage 0
     int wave;
-    uint32_t rdA0, rdA1, rdB;                    // lane parts of the read offsets in a stage
+    uint32_t rdA0, rdA1, rdB;                        // lane parts of the read offsets in a stage
 };
 
-__device__ __forceinline__ void load_one(const DCtx &x, uint32_t stage_lds, int64_t kt, int l)
+template <int BM, int BN>
+__device__ __forceinline__ void load_one(const DCtx<BM, BN> &x, uint32_t stage_lds, int64_t kt, int l)
 {
-    if (l < kDAInst)
+    using T = DTile<BM, BN>;
+    if (l < T::kAInst)
         lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride,
-                          stage_lds + (x.wave * kDAInst + l) * 1024);
+                          stage_lds + (x.wave * T::kAInst + l) * 1024);
     else
-        lds_direct_load16(x.b_voff[l - kDAInst], x.bbase + kt * x.b_kstride,
-                          stage_lds + 256 * DBK * 4 + (x.wave * kDBInst + l - kDAInst) * 1024);
+        lds_direct_load16(x.b_voff[l - T::kAInst], x.bbase + kt * x.b_kstride,
+                          stage_lds + BM * DBK * 4 + (x.wave * T::kBInst + l - T::kAInst) * 1024);
 }
 
-// Fragments of one 8-wide K group for a wave's 4 x 4 blocks: a[mb] holds
-// k = 4h .. 4h+3 of row c of block mb; b[j] holds, for k-step j, the four
-// columns 4c .. 4c+3 (one per block nb).
+// Fragments of one 8-wide K group for a wave's MB x NB blocks: a[mb] holds
+// k = 4h .. 4h+3 of row c of block mb; b[j] holds, for k-step j, the NB
+// columns NB c .. NB c + NB - 1 (one per block nb).
+template <int BM, int BN>
 struct FragG {
-    f32x4 a[4];
-    f32x4 b[4];
+    using T = DTile<BM, BN>;
+    using BV = typename VecN<T::kNB>::T;
+    f32x4 a[T::kMB];
+    BV b[4];
 };
 
-__device__ __forceinline__ void read_one(FragG &f, const float *stage, const DCtx &x, int g,
-                                         int idx)
+template <int BM, int BN>
+__device__ __forceinline__ void read_one(FragG<BM, BN> &f, const float *stage,
+                                         const DCtx<BM, BN> &x, int g, int idx)
 {
+    using T = DTile<BM, BN>;
+    using BV = typename VecN<T::kNB>::T;
     const char *st = reinterpret_cast<const char *>(stage);
-    if (idx < 4)
+    if (idx < T::kMB)
         f.a[idx] = *reinterpret_cast<const f32x4 *>(st + (g ? x.rdA1 : x.rdA0) + idx * 2048);
     else
-        f.b[idx - 4] = *reinterpret_cast<const f32x4 *>(st + x.rdB + (8 * g + (idx - 4)) * 1024);
+        f.b[idx - T::kMB] =
+            *reinterpret_cast<const BV *>(st + x.rdB + (8 * g + (idx - T::kMB)) * (BN * 4));
 }
 
-// The 64 MFMAs of group `cur`: the 8 reads of `nxt` go out after MFMAs
-// 0, 2, .., 14 (well ahead of their use), and (if loads) the 8 LDS-direct
-// loads of a later tile after MFMAs 20, 24, .., 48.  sched_barrier(0) pins
-// that order.
-__device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[4][4], const FragG &cur, FragG &nxt,
-                                               const float *rstage, const DCtx &x, int g_next,
-                                               uint32_t lstage, int64_t kload, bool loads)
+// The MFMAs of group `cur`: the reads of `nxt` go out after MFMAs 0, 2, ..
+// (well ahead of their use), and (if loads) this wave's LDS-direct loads
+// of a later tile after the load slots.  sched_barrier(0) pins that order.
+template <int BM, int BN>
+__device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
+                                               const FragG<BM, BN> &cur, FragG<BM, BN> &nxt,
+                                               const float *rstage, const DCtx<BM, BN> &x,
+                                               int g_next, uint32_t lstage, int64_t kload,
+                                               bool loads)
 {
+    using T = DTile<BM, BN>;
 #pragma unroll
-    for (int q = 0; q < 64; ++q) {
-        const int j = q >> 4, mb = (q >> 2) & 3, nb = q & 3;
+    for (int q = 0; q < T::kQ; ++q) {
+        const int j = q / (T::kMB * T::kNB), mb = (q / T::kNB) % T::kMB, nb = q % T::kNB;
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[mb][j], cur.b[j][nb], acc[mb][nb],
                                                             0, 0, 0);
-        const bool rd = q < 16 && (q & 1) == 0;
-        const bool ld = loads && q >= 20 && q < 52 && (q & 3) == 0;
+        const bool rd = q < 2 * T::kReads && (q & 1) == 0;
+        const bool ld = loads && q >= T::kLoadQ0 &&
+                        q < T::kLoadQ0 + T::kLoadStep * T::kPerTile &&
+                        (q - T::kLoadQ0) % T::kLoadStep == 0;
         if (rd || ld) {
             __builtin_amdgcn_sched_barrier(0);
             if (rd) read_one(nxt, rstage, x, g_next, q >> 1);
-            if (ld) load_one(x, lstage, kload, (q - 20) >> 2);
+            if (ld) load_one(x, lstage, kload, (q - T::kLoadQ0) / T::kLoadStep);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2, BM == 256 ? 1 : 2)))
 void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A,
                             int64_t lda, const float *__restrict__ B, int64_t ldb,
                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
                             int cvec)
 {
-    __shared__ __attribute__((aligned(1024))) float lds[DSTAGES * kDStageFloats];
+    using T = DTile<BM, BN>;
+    constexpr int MB = T::kMB, NB = T::kNB, WM = BM / 2, WN = BN / 2;
+    __shared__ __attribute__((aligned(1024))) float lds[DSTAGES * T::kStageFloats];
 
     const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
-    const int64_t m0 = t.tm * 256, n0 = t.tn * 256;
+    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, c = lane & 31;
 
-    DCtx x;
+    DCtx<BM, BN> x;
     x.wave = wave;
     x.lds0 = lds_offset(lds);
     x.abase = reinterpret_cast<const char *>(A + m0 * lda);
@@ -421,38 +461,38 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     x.a_kstride = DBK * 4;
     x.b_kstride = DBK * ldb * 4;
 #pragma unroll
-    for (int i = 0; i < kDAInst; ++i) {
-        const int p = (wave * kDAInst + i) * 64 + lane;     // LDS chunk this lane fills
+    for (int i = 0; i < T::kAInst; ++i) {
+        const int p = (wave * T::kAInst + i) * 64 + lane;     // LDS chunk this lane fills
         const int row = p >> 2, slot = p & 3;
         const int cc = slot ^ a_swz4(row);
         const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
         x.a_voff[i] = static_cast<uint32_t>((r * lda + 4 * cc) * 4);
     }
 #pragma unroll
-    for (int i = 0; i < kDBInst; ++i) {
-        const int p = (wave * kDBInst + i) * 64 + lane;
-        const int row = p >> 6, slot = p & 63;
+    for (int i = 0; i < T::kBInst; ++i) {
+        const int p = (wave * T::kBInst + i) * 64 + lane;
+        const int row = p / T::kBChunksPerRow, slot = p % T::kBChunksPerRow;
         const int64_t col = (n0 + 4 * slot < N) ? 4 * slot : N - 4 - n0;
         x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 4);
     }
-    // Rows this lane reads are wm*128 + 32*idx + c: their swizzle is a_swz4(c).
+    // Rows this lane reads are wm*WM + 32*idx + c: their swizzle is a_swz4(c).
     const int swz = a_swz4(c);
-    x.rdA0 = (wm * 128 + c) * DBK * 4 + (((0 + h) ^ swz) << 4);
-    x.rdA1 = (wm * 128 + c) * DBK * 4 + (((2 + h) ^ swz) << 4);
-    x.rdB = 256 * DBK * 4 + 4 * h * 1024 + (wn * 128 + 4 * c) * 4;
+    x.rdA0 = (wm * WM + c) * DBK * 4 + (((0 + h) ^ swz) << 4);
+    x.rdA1 = (wm * WM + c) * DBK * 4 + (((2 + h) ^ swz) << 4);
+    x.rdB = BM * DBK * 4 + 4 * h * (BN * 4) + (wn * WN + NB * c) * 4;
 
-    f32x16 acc[4][4];
+    f32x16 acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int64_t ktiles = K / DBK;
-    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * kDStageFloats; };
+    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * T::kStageFloats; };
     auto lstage = [&](int64_t kt) {
-        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * kDStageFloats * 4;
+        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * T::kStageFloats * 4;
     };
     auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
 
@@ -461,12 +501,12 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
 #pragma unroll
     for (int s = 0; s < DSTAGES - 1; ++s)
 #pragma unroll
-        for (int l = 0; l < kDPerTile; ++l) load_one(x, lstage(s), kclamp(s), l);
-    wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+        for (int l = 0; l < T::kPerTile; ++l) load_one(x, lstage(s), kclamp(s), l);
+    wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
 
-    FragG f0, f1;
+    FragG<BM, BN> f0, f1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) read_one(f0, stage(0), x, 0, i);
+    for (int i = 0; i < T::kReads; ++i) read_one(f0, stage(0), x, 0, i);
 
     // Tile kt: MFMAs on group 0 with group 1's reads and the loads of tile
     // kt + 3 slotted in (its stage was last read in tile kt - 1, finished by
@@ -476,28 +516,31 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     for (int64_t kt = 0; kt < ktiles; ++kt) {
         const int64_t nxt = kt + DSTAGES - 1;
         mfma_phase_f32(acc, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
-        wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+        wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
         mfma_phase_f32(acc, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
     }
     // No LDS-direct load may still be writing LDS when the work-group ends.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    const int64_t col = n0 + wn * 128 + 4 * c;
+    // Epilogue: register r of block (mb, nb) in lane (h, c) is C row
+    // 8*(r/4) + 4*h + r%4 of block mb and column NB*c + nb of the wave's piece.
+    const int64_t col = n0 + wn * WN + NB * c;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int64_t row = m0 + wm * WM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             if (row >= M) continue;
             float *p = C + row * ldc + col;
-            const f32x4 v = {acc[mb][0][r], acc[mb][1][r], acc[mb][2][r], acc[mb][3][r]};
-            if (cvec && col + 3 < N) {
-                *reinterpret_cast<f32x4 *>(p) = v;
+            typename VecN<NB>::T v;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
+            if (cvec && col + NB <= N) {
+                *reinterpret_cast<typename VecN<NB>::T *>(p) = v;
             } else {
-                if (col + 0 < N) p[0] = v.x;
-                if (col + 1 < N) p[1] = v.y;
-                if (col + 2 < N) p[2] = v.z;
-                if (col + 3 < N) p[3] = v.w;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    if (col + nb < N) p[nb] = v[nb];
             }
         }
 }
@@ -520,15 +563,23 @@ bool supports_mfma_f32_direct(const Problem &p)
            al(p.B) && p.lda < (int64_t(1) << 22) && p.ldb < (int64_t(1) << 26);
 }
 
-hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s)
+namespace {
+
+template <int BM, int BN>
+hipError_t launch_direct(const Problem &p, hipStream_t s)
 {
-    const int64_t tm = (p.M + 255) / 256, tn = (p.N + 255) / 256;
+    const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
     if (tm * tn > kMaxBlocks || !supports_mfma_f32_direct(p)) return hipErrorInvalidValue;
     const int cvec = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0;
-    hipLaunchKernelGGL(mfma_f32_direct_kernel, dim3(static_cast<uint32_t>(tm * tn)), dim3(256), 0,
-                       s, p.M, p.N, p.K, static_cast<const float *>(p.A), p.lda,
-                       static_cast<const float *>(p.B), p.ldb, p.C, p.ldc, tm, tn, cvec);
+    hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN>), dim3(static_cast<uint32_t>(tm * tn)),
+                       dim3(kThreads), 0, s, p.M, p.N, p.K, static_cast<const float *>(p.A),
+                       p.lda, static_cast<const float *>(p.B), p.ldb, p.C, p.ldc, tm, tn, cvec);
     return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256>(p, s); }
+hipError_t launch_mfma_f32_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128>(p, s); }
 
 }  // namespace mi355gemm

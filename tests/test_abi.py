@@ -128,12 +128,12 @@ def test_plan_is_pure():
 # for the layout cases that change it.  Measured alternatives for each row
 # are recorded by dense_gemm_17_amd/sweep.py.
 DISPATCH_GOLDEN = {
-    "f32_256": "mfma_f32_128",
+    "f32_256": "mfma_f32_direct128",
     "f32_4096": "mfma_f32_direct",
     "f32_8192": "mfma_f32_direct",
-    "gpt_qkv": "mfma_f32_direct",
-    "gpt_mlp_up": "mfma_f32_direct",
-    "gpt_mlp_down": "mfma_f32_128",
+    "gpt_qkv": "mfma_f32_direct128",
+    "gpt_mlp_up": "mfma_f32_direct128",
+    "gpt_mlp_down": "mfma_f32_direct128",
     "bf16_8192": "mfma_bf16_direct",
     "skinny_1x8960x1536": "skinny_f32",
     "skinny_7x4096x4096": "skinny_f32",

@@ -24,6 +24,8 @@ OCCUPANCY_BUDGET = {
     "mfma_f32_kernelILi128ELi128E": 2,
     "mfma_bf16_kernel": 1,
     "mfma_bf16_direct_kernel": 1,
+    "mfma_f32_direct_kernelILi256ELi256E": 1,
+    "mfma_f32_direct_kernelILi128ELi128E": 2,
     "valu_f32_kernel": 3,
     "skinny_kernel": 1,
     "naive_kernel": 8,
