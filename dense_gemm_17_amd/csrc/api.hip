@@ -34,6 +34,7 @@ const KernelInfo kKernels[] = {
     {"valu_f32", kF32, launch_valu_f32, supports_any},
     {"mfma_f32_direct", kF32, launch_mfma_f32_direct, supports_mfma_f32_direct},
     {"mfma_f32_direct128", kF32, launch_mfma_f32_direct128, supports_mfma_f32_direct},
+    {"mfma_f32_narrow128", kF32, launch_mfma_f32_narrow128, supports_mfma_f32_narrow},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -108,9 +109,11 @@ Verdict validate(const Problem &p)
 //     fraction of the matrix-core peak at 8192^3 (LDS-direct 256: 0.96,
 //     LDS-direct 128: 0.946; register-staged 256: 0.70, register-staged 128:
 //     0.67).  The smaller tile wins when the larger one leaves CUs idle in
-//     its last wave (gpt-sized, small and ragged shapes).  The LDS-direct
-//     kernels are used wherever their layout conditions hold (bf16 and fp32
-//     alike).
+//     its last wave (gpt-sized and small shapes).  The LDS-direct kernels
+//     are used wherever their layout conditions hold (bf16 and fp32 alike);
+//     other fp32 layouts (ragged K, unaligned rows) go to the narrow-load
+//     LDS-direct kernel, and the register-staged kernels only take leading
+//     dimensions too large for its 32-bit lane offsets.
 constexpr int64_t kCUs = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -138,6 +141,9 @@ int select_kernel(const Problem &p)
             return kernel_id("mfma_f32_direct");
         return kernel_id("mfma_f32_direct128");
     }
+    // Ragged K, unaligned rows: the narrow-load kernel (0.938 at 8192^3)
+    // beats both register-staged tiles on every shape.
+    if (supports_mfma_f32_narrow(p)) return kernel_id("mfma_f32_narrow128");
     if (tiled_cost(p, 256, 1, 700) <= tiled_cost(p, 128, 2, 670)) return kernel_id("mfma_f32");
     return kernel_id("mfma_f32_128");
 }

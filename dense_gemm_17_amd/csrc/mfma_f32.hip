@@ -301,11 +301,13 @@ hipError_t launch_tiles(const Problem &p, hipStream_t s)
 constexpr int DBK = 16;           // K step of the direct variants
 constexpr int DSTAGES = 4;
 
-template <int BM, int BN>
+// kW: bytes per lane of one LDS-direct load (16 for the aligned kernels, 4
+// for the narrow one); one wave's load fills 64 kW bytes of LDS.
+template <int BM, int BN, int kW>
 struct DTile {
     static constexpr int kMB = BM / 64, kNB = BN / 64;          // blocks per wave
-    static constexpr int kAInst = BM * DBK * 4 / 1024 / 4;     // LDS-direct loads per wave per tile (A)
-    static constexpr int kBInst = DBK * BN * 4 / 1024 / 4;     // ... (B)
+    static constexpr int kAInst = BM * DBK * 4 / (64 * kW) / 4; // LDS-direct loads per wave per tile (A)
+    static constexpr int kBInst = DBK * BN * 4 / (64 * kW) / 4; // ... (B)
     static constexpr int kPerTile = kAInst + kBInst;
     static constexpr int kStageFloats = BM * DBK + DBK * BN;
     static constexpr int kBChunksPerRow = BN / 4;
@@ -313,9 +315,10 @@ struct DTile {
     static constexpr int kReads = kMB + 4;                      // fragment reads per group
     // The reads of the next group go out after MFMAs 0, 2, 4, ..; the loads
     // of a later tile after MFMAs kLoadQ0, kLoadQ0 + kLoadStep, ...
-    static constexpr int kLoadQ0 = BM == 256 ? 20 : 1;
-    static constexpr int kLoadStep = 4;
+    static constexpr int kLoadQ0 = BM == 256 ? 20 : (kW == 16 ? 1 : 0);
+    static constexpr int kLoadStep = kW == 16 ? 4 : 1;
     static_assert(2 * kReads <= kQ && kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ, "slots");
+    static_assert((DSTAGES - 2) * kPerTile <= 63, "vmcnt is six bits");
     static_assert(kNB == 2 || kNB == 4, "B read width");
 };
 
@@ -340,6 +343,16 @@ __device__ __forceinline__ void lds_direct_load16(uint32_t voff, const void *sba
                  : "memory", "m0");
 }
 
+// The same with 4 bytes per lane (lane i's dword lands at M0 + 4 i); any
+// fp32 element address qualifies.
+__device__ __forceinline__ void lds_direct_load4(uint32_t voff, const void *sbase, uint32_t m0v)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_offset(const void *p)
 {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -357,9 +370,9 @@ __device__ __forceinline__ void wait_lds_vm_barrier()
 }
 
 // Everything a wave needs to address its loads and reads.
-template <int BM, int BN>
+template <int BM, int BN, int kW>
 struct DCtx {
-    using T = DTile<BM, BN>;
+    using T = DTile<BM, BN, kW>;
     uint32_t a_voff[T::kAInst], b_voff[T::kBInst];   // lane offsets (bytes) of each load
     const char *abase, *bbase;                       // tile (k = 0) bases, wave-uniform
     int64_t a_kstride, b_kstride;                    // bytes per K step
@@ -368,16 +381,24 @@ struct DCtx {
     uint32_t rdA0, rdA1, rdB;                        // lane parts of the read offsets in a stage
 };
 
-template <int BM, int BN>
-__device__ __forceinline__ void load_one(const DCtx<BM, BN> &x, uint32_t stage_lds, int64_t kt, int l)
+template <int kW>
+__device__ __forceinline__ void lds_direct_load(uint32_t voff, const void *sbase, uint32_t m0v)
 {
-    using T = DTile<BM, BN>;
+    if constexpr (kW == 16) lds_direct_load16(voff, sbase, m0v);
+    else lds_direct_load4(voff, sbase, m0v);
+}
+
+template <int BM, int BN, int kW>
+__device__ __forceinline__ void load_one(const DCtx<BM, BN, kW> &x, uint32_t stage_lds, int64_t kt,
+                                         int l)
+{
+    using T = DTile<BM, BN, kW>;
     if (l < T::kAInst)
-        lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride,
-                          stage_lds + (x.wave * T::kAInst + l) * 1024);
+        lds_direct_load<kW>(x.a_voff[l], x.abase + kt * x.a_kstride,
+                            stage_lds + (x.wave * T::kAInst + l) * 64 * kW);
     else
-        lds_direct_load16(x.b_voff[l - T::kAInst], x.bbase + kt * x.b_kstride,
-                          stage_lds + BM * DBK * 4 + (x.wave * T::kBInst + l - T::kAInst) * 1024);
+        lds_direct_load<kW>(x.b_voff[l - T::kAInst], x.bbase + kt * x.b_kstride,
+                            stage_lds + BM * DBK * 4 + (x.wave * T::kBInst + l - T::kAInst) * 64 * kW);
 }
 
 // Fragments of one 8-wide K group for a wave's MB x NB blocks: a[mb] holds
@@ -385,17 +406,17 @@ __device__ __forceinline__ void load_one(const DCtx<BM, BN> &x, uint32_t stage_l
 // columns NB c .. NB c + NB - 1 (one per block nb).
 template <int BM, int BN>
 struct FragG {
-    using T = DTile<BM, BN>;
+    using T = DTile<BM, BN, 16>;
     using BV = typename VecN<T::kNB>::T;
     f32x4 a[T::kMB];
     BV b[4];
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int kW>
 __device__ __forceinline__ void read_one(FragG<BM, BN> &f, const float *stage,
-                                         const DCtx<BM, BN> &x, int g, int idx)
+                                         const DCtx<BM, BN, kW> &x, int g, int idx)
 {
-    using T = DTile<BM, BN>;
+    using T = DTile<BM, BN, kW>;
     using BV = typename VecN<T::kNB>::T;
     const char *st = reinterpret_cast<const char *>(stage);
     if (idx < T::kMB)
@@ -408,14 +429,14 @@ __device__ __forceinline__ void read_one(FragG<BM, BN> &f, const float *stage,
 // The MFMAs of group `cur`: the reads of `nxt` go out after MFMAs 0, 2, ..
 // (well ahead of their use), and (if loads) this wave's LDS-direct loads
 // of a later tile after the load slots.  sched_barrier(0) pins that order.
-template <int BM, int BN>
+template <int BM, int BN, int kW>
 __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
                                                const FragG<BM, BN> &cur, FragG<BM, BN> &nxt,
-                                               const float *rstage, const DCtx<BM, BN> &x,
+                                               const float *rstage, const DCtx<BM, BN, kW> &x,
                                                int g_next, uint32_t lstage, int64_t kload,
                                                bool loads)
 {
-    using T = DTile<BM, BN>;
+    using T = DTile<BM, BN, kW>;
 #pragma unroll
     for (int q = 0; q < T::kQ; ++q) {
         const int j = q / (T::kMB * T::kNB), mb = (q / T::kNB) % T::kMB, nb = q % T::kNB;
@@ -434,7 +455,7 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
     }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int kW>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2, BM == 256 ? 1 : 2)))
 void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A,
@@ -442,7 +463,7 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
                             int cvec)
 {
-    using T = DTile<BM, BN>;
+    using T = DTile<BM, BN, kW>;
     constexpr int MB = T::kMB, NB = T::kNB, WM = BM / 2, WN = BN / 2;
     __shared__ __attribute__((aligned(1024))) float lds[DSTAGES * T::kStageFloats];
 
@@ -453,26 +474,42 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, c = lane & 31;
 
-    DCtx<BM, BN> x;
+    DCtx<BM, BN, kW> x;
     x.wave = wave;
     x.lds0 = lds_offset(lds);
     x.abase = reinterpret_cast<const char *>(A + m0 * lda);
     x.bbase = reinterpret_cast<const char *>(B + n0);
     x.a_kstride = DBK * 4;
     x.b_kstride = DBK * ldb * 4;
+    // p: the kW-byte unit of the stage's A (or B) region this lane fills;
+    // the element(s) it holds follow from the layout.
 #pragma unroll
     for (int i = 0; i < T::kAInst; ++i) {
-        const int p = (wave * T::kAInst + i) * 64 + lane;     // LDS chunk this lane fills
-        const int row = p >> 2, slot = p & 3;
-        const int cc = slot ^ a_swz4(row);
+        const int p = (wave * T::kAInst + i) * 64 + lane;
+        int row, kk;
+        if constexpr (kW == 16) {
+            row = p >> 2;
+            kk = 4 * ((p & 3) ^ a_swz4(row));
+        } else {
+            row = p >> 4;
+            kk = 4 * (((p >> 2) & 3) ^ a_swz4(row)) + (p & 3);
+        }
         const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
-        x.a_voff[i] = static_cast<uint32_t>((r * lda + 4 * cc) * 4);
+        x.a_voff[i] = static_cast<uint32_t>((r * lda + kk) * 4);
     }
 #pragma unroll
     for (int i = 0; i < T::kBInst; ++i) {
         const int p = (wave * T::kBInst + i) * 64 + lane;
-        const int row = p / T::kBChunksPerRow, slot = p % T::kBChunksPerRow;
-        const int64_t col = (n0 + 4 * slot < N) ? 4 * slot : N - 4 - n0;
+        int64_t row, col;
+        if constexpr (kW == 16) {
+            row = p / T::kBChunksPerRow;
+            const int slot = p % T::kBChunksPerRow;
+            col = (n0 + 4 * slot < N) ? 4 * slot : N - 4 - n0;
+        } else {
+            row = p / BN;
+            const int cl = p % BN;
+            col = (n0 + cl < N) ? cl : N - 1 - n0;
+        }
         x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 4);
     }
     // Rows this lane reads are wm*WM + 32*idx + c: their swizzle is a_swz4(c).
@@ -496,31 +533,63 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     };
     auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
 
-    // Prologue: tiles 0..2 in flight (re-fetching the last tile past the
-    // end), wait for tile 0, read its first group.
-#pragma unroll
-    for (int s = 0; s < DSTAGES - 1; ++s)
-#pragma unroll
-        for (int l = 0; l < T::kPerTile; ++l) load_one(x, lstage(s), kclamp(s), l);
-    wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
-
     FragG<BM, BN> f0, f1;
+    // The aligned kernels take K % 16 == 0 and K > 0 only; the narrow one
+    // may have no full tile (K < 16), then only the tail below runs.
+    if (kW == 16 || ktiles > 0) {
+        // Prologue: tiles 0..2 in flight (re-fetching the last tile past
+        // the end), wait for tile 0, read its first group.
 #pragma unroll
-    for (int i = 0; i < T::kReads; ++i) read_one(f0, stage(0), x, 0, i);
-
-    // Tile kt: MFMAs on group 0 with group 1's reads and the loads of tile
-    // kt + 3 slotted in (its stage was last read in tile kt - 1, finished by
-    // every wave before the previous barrier) | wait for tile kt + 1 and for
-    // this wave's reads, barrier | MFMAs on group 1 with the reads of group 0
-    // of tile kt + 1 (in the last tile: reads of a landed stage, unused).
-    for (int64_t kt = 0; kt < ktiles; ++kt) {
-        const int64_t nxt = kt + DSTAGES - 1;
-        mfma_phase_f32(acc, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
+        for (int s = 0; s < DSTAGES - 1; ++s)
+#pragma unroll
+            for (int l = 0; l < T::kPerTile; ++l) load_one(x, lstage(s), kclamp(s), l);
         wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
-        mfma_phase_f32(acc, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
+
+#pragma unroll
+        for (int i = 0; i < T::kReads; ++i) read_one(f0, stage(0), x, 0, i);
+
+        // Tile kt: MFMAs on group 0 with group 1's reads and the loads of
+        // tile kt + 3 slotted in (its stage was last read in tile kt - 1,
+        // finished by every wave before the previous barrier) | wait for tile
+        // kt + 1 and for this wave's reads, barrier | MFMAs on group 1 with
+        // the reads of group 0 of tile kt + 1 (in the last tile: reads of a
+        // landed stage, unused).
+        for (int64_t kt = 0; kt < ktiles; ++kt) {
+            const int64_t nxt = kt + DSTAGES - 1;
+            mfma_phase_f32(acc, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
+            wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
+            mfma_phase_f32(acc, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
+        }
+        // No LDS-direct load may still be writing LDS when the work-group
+        // ends or stage 0 is refilled below.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
-    // No LDS-direct load may still be writing LDS when the work-group ends.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (kW == 4) {
+        // K tail (K % 16 columns of A, rows of B): written into stage 0 by
+        // ordinary loads and LDS stores, zero past K, in the same layout;
+        // rows of A past M and columns of B past N repeat the last valid
+        // one as in the loads above.
+        const int64_t k0 = ktiles * DBK;
+        if (k0 < K) {
+            wait_lds_vm_barrier<0>();        // every wave done with every stage
+            for (int p = threadIdx.x; p < BM * DBK; p += kThreads) {
+                const int row = p >> 4;
+                const int64_t k = k0 + 4 * (((p >> 2) & 3) ^ a_swz4(row)) + (p & 3);
+                const int64_t r = (m0 + row < M) ? m0 + row : M - 1;
+                lds[p] = (k < K) ? A[r * lda + k] : 0.f;
+            }
+            for (int p = threadIdx.x; p < DBK * BN; p += kThreads) {
+                const int64_t k = k0 + p / BN;
+                const int64_t cl = n0 + p % BN;
+                lds[BM * DBK + p] = (k < K) ? B[k * ldb + (cl < N ? cl : N - 1)] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < T::kReads; ++i) read_one(f0, stage(0), x, 0, i);
+            mfma_phase_f32(acc, f0, f1, stage(0), x, 1, 0, 0, false);
+            mfma_phase_f32(acc, f1, f0, stage(0), x, 0, 0, 0, false);
+        }
+    }
 
     // Epilogue: register r of block (mb, nb) in lane (h, c) is C row
     // 8*(r/4) + 4*h + r%4 of block mb and column NB*c + nb of the wave's piece.
@@ -563,15 +632,24 @@ bool supports_mfma_f32_direct(const Problem &p)
            al(p.B) && p.lda < (int64_t(1) << 22) && p.ldb < (int64_t(1) << 26);
 }
 
+// The narrow variant takes any fp32 layout: 4-byte loads need only element
+// alignment, and the K tail is zero-filled.  Lane offsets are 32-bit byte
+// offsets within a 128-row panel of A and a 16-row panel of B.
+bool supports_mfma_f32_narrow(const Problem &p)
+{
+    return p.lda < (int64_t(1) << 23) && p.ldb < (int64_t(1) << 26);
+}
+
 namespace {
 
-template <int BM, int BN>
+template <int BM, int BN, int kW>
 hipError_t launch_direct(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
-    if (tm * tn > kMaxBlocks || !supports_mfma_f32_direct(p)) return hipErrorInvalidValue;
+    const bool ok = kW == 16 ? supports_mfma_f32_direct(p) : supports_mfma_f32_narrow(p);
+    if (tm * tn > kMaxBlocks || !ok) return hipErrorInvalidValue;
     const int cvec = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0;
-    hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN>), dim3(static_cast<uint32_t>(tm * tn)),
+    hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN, kW>), dim3(static_cast<uint32_t>(tm * tn)),
                        dim3(kThreads), 0, s, p.M, p.N, p.K, static_cast<const float *>(p.A),
                        p.lda, static_cast<const float *>(p.B), p.ldb, p.C, p.ldc, tm, tn, cvec);
     return hipGetLastError();
@@ -579,7 +657,8 @@ hipError_t launch_direct(const Problem &p, hipStream_t s)
 
 }  // namespace
 
-hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256>(p, s); }
-hipError_t launch_mfma_f32_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128>(p, s); }
+hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256, 16>(p, s); }
+hipError_t launch_mfma_f32_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, 16>(p, s); }
+hipError_t launch_mfma_f32_narrow128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, 4>(p, s); }
 
 }  // namespace mi355gemm

@@ -137,8 +137,8 @@ DISPATCH_GOLDEN = {
     "bf16_8192": "mfma_bf16_direct",
     "skinny_1x8960x1536": "skinny_f32",
     "skinny_7x4096x4096": "skinny_f32",
-    "ragged_1000x3000x777": "mfma_f32_128",
-    "ragged_4097x4095x1023": "mfma_f32_128",
+    "ragged_1000x3000x777": "mfma_f32_narrow128",
+    "ragged_4097x4095x1023": "mfma_f32_narrow128",
 }
 
 
@@ -158,11 +158,15 @@ def test_dispatch_layout_cases():
     assert name(g.BF16, 8192, 8196, 8192, A=PA, B=PB, C=PC) == "mfma_bf16"
     assert name(g.BF16, 8192, 8192, 8192, A=PA + 2, B=PB, C=PC) == "mfma_bf16"
     assert name(g.BF16, 8192, 8192, 8192, A=PA, lda=8196, B=PB, C=PC) == "mfma_bf16"
-    # fp32: the LDS-direct kernel needs K % 16, N % 4, 16-byte aligned rows
+    # fp32: the LDS-direct kernels need K % 16, N % 4, 16-byte aligned rows;
+    # every other layout takes the narrow-load kernel
     assert name(g.F32, 8192, 8192, 8192, A=PA, B=PB, C=PC) == "mfma_f32_direct"
-    assert name(g.F32, 8192, 8192, 8200, A=PA, B=PB, C=PC) == "mfma_f32"
-    assert name(g.F32, 8192, 8192, 8192, A=PA, B=PB, ldb=8194, C=PC) == "mfma_f32"
-    assert name(g.F32, 8192, 8192, 8192, A=PA + 4, B=PB, C=PC) == "mfma_f32"
+    assert name(g.F32, 8192, 8192, 8200, A=PA, B=PB, C=PC) == "mfma_f32_narrow128"
+    assert name(g.F32, 8192, 8192, 8192, A=PA, B=PB, ldb=8194, C=PC) == "mfma_f32_narrow128"
+    assert name(g.F32, 8192, 8192, 8192, A=PA + 4, B=PB, C=PC) == "mfma_f32_narrow128"
+    assert name(g.F32, 4096, 1152, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct128"
+    # ... except leading dimensions beyond its 32-bit lane offsets
+    assert name(g.F32, 64, 64, 64, A=PA, lda=1 << 23, B=PB, C=PC) == "mfma_f32_128"
     # few rows -> bandwidth family, both element types, up to 16 rows
     assert name(g.BF16, 1, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_bf16"
     assert name(g.F32, 16, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_f32"
