@@ -168,6 +168,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     import dense_gemm_17_amd as g   # fails loudly if the HIP library is missing
+    from dense_gemm_17_amd.measure import ClockSampler, toolchain
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -205,11 +206,12 @@ def main():
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
            for _ in ops] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(ev[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     per = {}
     for i, (w, *_rest) in enumerate(ops):
@@ -270,6 +272,9 @@ def main():
                                    "peak": PEAK_TFLOPS[r["dtype"]], "unit": "TFLOP/s",
                                    "frac": r["frac_peak"]} for n, r in per.items()},
         "cpu_baseline": cpu,
+        # GPU core clock and board power sampled over the timed steps, and
+        # the toolchain that built the kernels
+        "env": dict(clocks.summary(), toolchain=toolchain()),
     }
     if copy is not None:
         line["copy_calibration"] = copy
