@@ -235,6 +235,51 @@ def test_skinny_configurations_exact(dtype):
                 assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ones_exact(dtype):
+    """A = B = ones gives K everywhere; A = ones with integer B gives every
+    row equal to B's column sums (exact: integer partial sums below 2^24)."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    gen = workloads.generator(82)
+    for (M, N, K) in [(300, 260, 200), (33, 17, 4100), (1, 8960, 96), (257, 264, 1024)]:
+        ones_a = torch.ones((M, K), dtype=tdt)
+        Bint = workloads.small_int((K, N), -4, 4, gen, tdt)
+        colsum = Bint.to(torch.int64).sum(0).to(torch.float64).numpy()
+        Ad, Od, Bd = ones_a.to(DEV), torch.ones((K, N), dtype=tdt, device=DEV), Bint.to(DEV)
+        for k in kernels_for(dtype):
+            if not takes(k, Ad, Bd):
+                continue
+            say(f"[ones] {dtype} {M}x{N}x{K} kernel={k}")
+            C = run(Ad, Od, k).cpu().numpy()
+            assert np.all(C == K), (k, M, N, K)
+            C = run(Ad, Bd, k).cpu().numpy().astype(np.float64)
+            assert np.all(C == colsum[None, :]), (k, M, N, K)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_brute_force_tiny_shapes(dtype):
+    """Every (M, N, K) in {1..8}^3, every kernel that takes it, integer
+    operands: bitwise equal to the int64 product."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
+    gen = workloads.generator(83)
+    A8 = workloads.small_int((8, 8), lo, hi, gen, tdt)
+    B8 = workloads.small_int((8, 8), lo, hi, gen, tdt)
+    names = kernels_for(dtype)
+    say(f"[tiny] {dtype} 512 shapes x {len(names)} kernels")
+    for M in range(1, 9):
+        for N in range(1, 9):
+            for K in range(1, 9):
+                A, B = A8[:M, :K].contiguous(), B8[:K, :N].contiguous()
+                exact = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float64).numpy()
+                Ad, Bd = A.to(DEV), B.to(DEV)
+                for k in names:
+                    if not takes(k, Ad, Bd):
+                        continue
+                    C = run(Ad, Bd, k).cpu().numpy().astype(np.float64)
+                    assert np.array_equal(C, exact), (k, M, N, K)
+
+
 GUARD_CASES = [  # (M, N, K, extra A columns, extra B columns)
     (130, 200, 150, 13, 9), (5, 300, 64, 13, 9), (300, 257, 1000, 13, 9),
     (300, 264, 512, 16, 8), (257, 520, 96, 8, 24),
