@@ -35,6 +35,7 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_direct", kF32, launch_mfma_f32_direct, supports_mfma_f32_direct},
     {"mfma_f32_direct128", kF32, launch_mfma_f32_direct128, supports_mfma_f32_direct},
     {"mfma_f32_narrow128", kF32, launch_mfma_f32_narrow128, supports_mfma_f32_narrow},
+    {"mfma_f32_direct128x64", kF32, launch_mfma_f32_direct128x64, supports_mfma_f32_direct},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -107,9 +108,10 @@ Verdict validate(const Problem &p)
 //     runs one work-group per CU, a 128 x 128 tile two (each at half the
 //     CU's rate), over 256 CUs, each divided by the kernel's measured
 //     fraction of the matrix-core peak at 8192^3 (LDS-direct 256: 0.96,
-//     LDS-direct 128: 0.946; register-staged 256: 0.70, register-staged 128:
-//     0.67).  The smaller tile wins when the larger one leaves CUs idle in
-//     its last wave (gpt-sized and small shapes).  The LDS-direct kernels
+//     LDS-direct 128: 0.946, LDS-direct 128 x 64 with three per CU: 0.917;
+//     register-staged 256: 0.70, register-staged 128: 0.67).  A smaller tile
+//     wins when the larger one leaves CUs idle in its last wave (gpt-sized
+//     and small shapes).  The LDS-direct kernels
 //     are used wherever their layout conditions hold (bf16 and fp32 alike);
 //     other fp32 layouts (ragged K, unaligned rows) go to the narrow-load
 //     LDS-direct kernel, and the register-staged kernels only take leading
@@ -120,12 +122,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Relative time of a tiled launch: waves x per-work-group work / efficiency,
 // in units of one CU doing a 128 x 128 tile alone at full rate.
-// eff_permille: the kernel's fraction of peak, in thousandths.
-int64_t tiled_cost(const Problem &p, int64_t tile, int64_t per_cu, int64_t eff_permille)
+// bm x bn tiles, per_cu work-groups resident per CU, eff_permille: the
+// kernel's fraction of peak in thousandths.  Unit: one CU computing a
+// 128 x 128 tile alone at full rate.
+int64_t tiled_cost(const Problem &p, int64_t bm, int64_t bn, int64_t per_cu, int64_t eff_permille)
 {
-    const int64_t tiles = ceil_div(p.M, tile) * ceil_div(p.N, tile);
+    const int64_t tiles = ceil_div(p.M, bm) * ceil_div(p.N, bn);
     const int64_t waves = ceil_div(tiles, kCUs * per_cu);
-    return waves * (tile / 128) * (tile / 128) * per_cu * 1000000 / eff_permille;
+    return waves * bm * bn * per_cu * 1000000 / (128 * 128) / eff_permille;
 }
 
 int select_kernel(const Problem &p)
@@ -137,14 +141,18 @@ int select_kernel(const Problem &p)
         return kernel_id("mfma_bf16");
     }
     if (supports_mfma_f32_direct(p)) {
-        if (tiled_cost(p, 256, 1, 960) <= tiled_cost(p, 128, 2, 946))
-            return kernel_id("mfma_f32_direct");
-        return kernel_id("mfma_f32_direct128");
+        const int64_t c256 = tiled_cost(p, 256, 256, 1, 960);
+        const int64_t c128 = tiled_cost(p, 128, 128, 2, 946);
+        const int64_t c64 = tiled_cost(p, 128, 64, 3, 917);
+        if (c256 <= c128 && c256 <= c64) return kernel_id("mfma_f32_direct");
+        if (c128 <= c64) return kernel_id("mfma_f32_direct128");
+        return kernel_id("mfma_f32_direct128x64");
     }
     // Ragged K, unaligned rows: the narrow-load kernel (0.938 at 8192^3)
     // beats both register-staged tiles on every shape.
     if (supports_mfma_f32_narrow(p)) return kernel_id("mfma_f32_narrow128");
-    if (tiled_cost(p, 256, 1, 700) <= tiled_cost(p, 128, 2, 670)) return kernel_id("mfma_f32");
+    if (tiled_cost(p, 256, 256, 1, 700) <= tiled_cost(p, 128, 128, 2, 670))
+        return kernel_id("mfma_f32");
     return kernel_id("mfma_f32_128");
 }
 

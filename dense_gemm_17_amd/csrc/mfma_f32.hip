@@ -301,6 +301,12 @@ hipError_t launch_tiles(const Problem &p, hipStream_t s)
 constexpr int DBK = 16;           // K step of the direct variants
 constexpr int DSTAGES = 4;
 
+typedef float f32x1 __attribute__((ext_vector_type(1)));
+template <int NB> struct DVec;
+template <> struct DVec<1> { typedef f32x1 T; };
+template <> struct DVec<2> { typedef f32x2 T; };
+template <> struct DVec<4> { typedef f32x4 T; };
+
 // kW: bytes per lane of one LDS-direct load (16 for the aligned kernels, 4
 // for the narrow one); one wave's load fills 64 kW bytes of LDS.
 template <int BM, int BN, int kW>
@@ -313,14 +319,25 @@ struct DTile {
     static constexpr int kBChunksPerRow = BN / 4;
     static constexpr int kQ = 4 * kMB * kNB;                    // MFMAs per 8-wide K group
     static constexpr int kReads = kMB + 4;                      // fragment reads per group
-    // The reads of the next group go out after MFMAs 0, 2, 4, ..; the loads
-    // of a later tile after MFMAs kLoadQ0, kLoadQ0 + kLoadStep, ...
-    static constexpr int kLoadQ0 = BM == 256 ? 20 : (kW == 16 ? 1 : 0);
-    static constexpr int kLoadStep = kW == 16 ? 4 : 1;
-    static_assert(2 * kReads <= kQ && kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ, "slots");
+    // The reads of the next group go out after MFMAs 0, 2, 4, .. (after
+    // every MFMA when there are fewer than two per read); the loads of a
+    // later tile after MFMAs kLoadQ0, kLoadQ0 + kLoadStep, ...
+    static constexpr bool kReadEveryOther = 2 * kReads <= kQ;
+    static constexpr int kLoadQ0 = BM == 256 ? 20 : kNB == 1 ? kQ - kPerTile : (kW == 16 ? 1 : 0);
+    static constexpr int kLoadStep = kW == 16 && kNB > 1 ? 4 : 1;
+    // Work-groups per CU the LDS ring allows (and the occupancy asked of the
+    // compiler): 1 for 256 x 256, 2 for 128 x 128, 3 for 128 x 64.
+    static constexpr int kPerCU = 160 * 1024 / (DSTAGES * kStageFloats * 4);
+    // With one 32-column block per wave, B is read 4 bytes per lane and the
+    // two half-waves read rows 4 apart: 16-byte chunks of B rows are
+    // XOR-permuted by 8 * bit 2 of the row so those rows use different banks.
+    static constexpr bool kBSwz = kNB == 1;
+    static_assert(kReads <= kQ && kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ, "slots");
     static_assert((DSTAGES - 2) * kPerTile <= 63, "vmcnt is six bits");
-    static_assert(kNB == 2 || kNB == 4, "B read width");
+    static_assert(kNB == 1 || kNB == 2 || kNB == 4, "B read width");
 };
+
+__device__ __forceinline__ int b_swz8(int row) { return ((row >> 2) & 1) << 3; }
 
 // A rows of 4 chunks (64 bytes): chunk c of row r is stored at c ^ ((r >> 2) & 3).
 // Measured on gfx950 (SQ_LDS_BANK_CONFLICT, one-pattern microbenchmark):
@@ -407,7 +424,7 @@ __device__ __forceinline__ void load_one(const DCtx<BM, BN, kW> &x, uint32_t sta
 template <int BM, int BN>
 struct FragG {
     using T = DTile<BM, BN, 16>;
-    using BV = typename VecN<T::kNB>::T;
+    using BV = typename DVec<T::kNB>::T;
     f32x4 a[T::kMB];
     BV b[4];
 };
@@ -417,7 +434,7 @@ __device__ __forceinline__ void read_one(FragG<BM, BN> &f, const float *stage,
                                          const DCtx<BM, BN, kW> &x, int g, int idx)
 {
     using T = DTile<BM, BN, kW>;
-    using BV = typename VecN<T::kNB>::T;
+    using BV = typename DVec<T::kNB>::T;
     const char *st = reinterpret_cast<const char *>(stage);
     if (idx < T::kMB)
         f.a[idx] = *reinterpret_cast<const f32x4 *>(st + (g ? x.rdA1 : x.rdA0) + idx * 2048);
@@ -442,13 +459,13 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
         const int j = q / (T::kMB * T::kNB), mb = (q / T::kNB) % T::kMB, nb = q % T::kNB;
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[mb][j], cur.b[j][nb], acc[mb][nb],
                                                             0, 0, 0);
-        const bool rd = q < 2 * T::kReads && (q & 1) == 0;
+        const bool rd = T::kReadEveryOther ? (q < 2 * T::kReads && (q & 1) == 0) : q < T::kReads;
         const bool ld = loads && q >= T::kLoadQ0 &&
                         q < T::kLoadQ0 + T::kLoadStep * T::kPerTile &&
                         (q - T::kLoadQ0) % T::kLoadStep == 0;
         if (rd || ld) {
             __builtin_amdgcn_sched_barrier(0);
-            if (rd) read_one(nxt, rstage, x, g_next, q >> 1);
+            if (rd) read_one(nxt, rstage, x, g_next, T::kReadEveryOther ? q >> 1 : q);
             if (ld) load_one(x, lstage, kload, (q - T::kLoadQ0) / T::kLoadStep);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -457,7 +474,7 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
 
 template <int BM, int BN, int kW>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(BM == 256 ? 1 : 2, BM == 256 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(DTile<BM, BN, kW>::kPerCU, DTile<BM, BN, kW>::kPerCU)))
 void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A,
                             int64_t lda, const float *__restrict__ B, int64_t ldb,
                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
@@ -504,7 +521,8 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
         if constexpr (kW == 16) {
             row = p / T::kBChunksPerRow;
             const int slot = p % T::kBChunksPerRow;
-            col = (n0 + 4 * slot < N) ? 4 * slot : N - 4 - n0;
+            const int lc = T::kBSwz ? slot ^ b_swz8(static_cast<int>(row)) : slot;
+            col = (n0 + 4 * lc < N) ? 4 * lc : N - 4 - n0;
         } else {
             row = p / BN;
             const int cl = p % BN;
@@ -516,7 +534,13 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     const int swz = a_swz4(c);
     x.rdA0 = (wm * WM + c) * DBK * 4 + (((0 + h) ^ swz) << 4);
     x.rdA1 = (wm * WM + c) * DBK * 4 + (((2 + h) ^ swz) << 4);
-    x.rdB = BM * DBK * 4 + 4 * h * (BN * 4) + (wn * WN + NB * c) * 4;
+    if constexpr (T::kBSwz) {
+        // rows this lane reads are 4h + 8g + j: bit 2 is h
+        const int n = wn * WN + c;
+        x.rdB = BM * DBK * 4 + 4 * h * (BN * 4) + ((((n >> 2) ^ (h << 3)) << 2) + (n & 3)) * 4;
+    } else {
+        x.rdB = BM * DBK * 4 + 4 * h * (BN * 4) + (wn * WN + NB * c) * 4;
+    }
 
     f32x16 acc[MB][NB];
 #pragma unroll
@@ -601,11 +625,11 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
             const int64_t row = m0 + wm * WM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             if (row >= M) continue;
             float *p = C + row * ldc + col;
-            typename VecN<NB>::T v;
+            typename DVec<NB>::T v;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
             if (cvec && col + NB <= N) {
-                *reinterpret_cast<typename VecN<NB>::T *>(p) = v;
+                *reinterpret_cast<typename DVec<NB>::T *>(p) = v;
             } else {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
@@ -660,5 +684,6 @@ hipError_t launch_direct(const Problem &p, hipStream_t s)
 hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256, 16>(p, s); }
 hipError_t launch_mfma_f32_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, 16>(p, s); }
 hipError_t launch_mfma_f32_narrow128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, 4>(p, s); }
+hipError_t launch_mfma_f32_direct128x64(const Problem &p, hipStream_t s) { return launch_direct<128, 64, 16>(p, s); }
 
 }  // namespace mi355gemm

@@ -128,12 +128,12 @@ def test_plan_is_pure():
 # for the layout cases that change it.  Measured alternatives for each row
 # are recorded by dense_gemm_17_amd/sweep.py.
 DISPATCH_GOLDEN = {
-    "f32_256": "mfma_f32_direct128",
+    "f32_256": "mfma_f32_direct128x64",
     "f32_4096": "mfma_f32_direct",
     "f32_8192": "mfma_f32_direct",
-    "gpt_qkv": "mfma_f32_direct128",
+    "gpt_qkv": "mfma_f32_direct128x64",
     "gpt_mlp_up": "mfma_f32_direct128",
-    "gpt_mlp_down": "mfma_f32_direct128",
+    "gpt_mlp_down": "mfma_f32_direct128x64",
     "bf16_8192": "mfma_bf16_direct",
     "skinny_1x8960x1536": "skinny_f32",
     "skinny_7x4096x4096": "skinny_f32",
@@ -164,7 +164,8 @@ def test_dispatch_layout_cases():
     assert name(g.F32, 8192, 8192, 8200, A=PA, B=PB, C=PC) == "mfma_f32_narrow128"
     assert name(g.F32, 8192, 8192, 8192, A=PA, B=PB, ldb=8194, C=PC) == "mfma_f32_narrow128"
     assert name(g.F32, 8192, 8192, 8192, A=PA + 4, B=PB, C=PC) == "mfma_f32_narrow128"
-    assert name(g.F32, 4096, 1152, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct128"
+    assert name(g.F32, 4096, 1152, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct128x64"
+    assert name(g.F32, 16384, 1536, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct128"
     # ... except leading dimensions beyond its 32-bit lane offsets
     assert name(g.F32, 64, 64, 64, A=PA, lda=1 << 23, B=PB, C=PC) == "mfma_f32_128"
     # few rows -> bandwidth family, both element types, up to 16 rows

@@ -26,6 +26,7 @@ OCCUPANCY_BUDGET = {
     "mfma_bf16_direct_kernel": 1,
     "mfma_f32_direct_kernelILi256ELi256E": 1,
     "mfma_f32_direct_kernelILi128ELi128E": 2,
+    "mfma_f32_direct_kernelILi128ELi64E": 3,
     "valu_f32_kernel": 3,
     "skinny_kernel": 1,
     "naive_kernel": 8,
