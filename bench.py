@@ -19,6 +19,14 @@ Prints exactly one JSON line.  Extra legs:
       scaled by what the counters read for the copy, tagged with a digest of
       the kernel's sources.  The benchmark line reports that traffic for the
       dominant kernel only while the digest still matches (else null).
+  mfma ceiling (default on, --no-ceiling skips it; --ceiling-only runs just
+      it, with zero operands for contrast): a loop of nothing but MFMAs on
+      random operands of each timed dtype, from libmi355probe.so, after the
+      clock has settled.  Reported beside the roofline as context: on this
+      board the bf16 matrix cores run at the power limit, where the clock
+      (and so the reachable throughput) depends on the operand data.
+  Every line also records the GPU clock and board power sampled over the
+  timed steps and the toolchain.
 """
 from __future__ import annotations
 
@@ -71,7 +79,61 @@ def parse():
     p.add_argument("--check-rows", type=int, default=8,
                    help="rows per product checked against the oracle after timing")
     p.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the matrix-core ceiling probe (profiler runs)")
+    p.add_argument("--ceiling-only", action="store_true",
+                   help="run only the ceiling probe, random and zero operands")
     return p.parse_args()
+
+
+PROBE_LIB = os.path.join(ROOT, "dense_gemm_17_amd", "libmi355probe.so")
+# flops per MFMA of the probe's instructions: 32x32x16 bf16, 32x32x2 fp32
+PROBE_FLOPS = {"bf16": 2 * 32 * 32 * 16, "f32": 2 * 32 * 32 * 2}
+
+
+def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
+    """Steady-state throughput of a loop of nothing but MFMAs (operands in
+    registers, no memory traffic) on 1024 work-groups of one wave per SIMD,
+    as the GEMM kernels run: the most a kernel built on the same instruction
+    can reach on this board with such operand data.  Each case first runs
+    for `settle_s` seconds so the clock has settled at the power limit."""
+    import ctypes
+    from dense_gemm_17_amd.measure import ClockSampler
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    blocks = 1024
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for dt in dtypes:
+        iters = 8000 if dt == "bf16" else 2000          # ~5-10 ms per launch
+        for zero in ([0, 1] if zero_too else [0]):
+            def launch():
+                rc = lib.probe_mfma_loop(1 if dt == "bf16" else 0, blocks, iters, zero,
+                                         out.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"probe_mfma_loop failed: {rc}")
+            t_end = time.perf_counter() + settle_s
+            while time.perf_counter() < t_end:
+                for _ in range(20):
+                    launch()
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 40
+            with ClockSampler() as clocks:
+                e0.record(stream)
+                for _ in range(reps):
+                    launch()
+                e1.record(stream)
+                torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            flops = blocks * 4 * iters * 16 * PROBE_FLOPS[dt]
+            tf = flops / (ms * 1e-3) / 1e12
+            res[f"{dt}_{'zero' if zero else 'random'}"] = {
+                "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_TFLOPS[dt], 4),
+                **clocks.summary()}
+    return res
 
 
 def source_digest(kernel: str):
@@ -172,6 +234,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.ceiling_only:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, zero_too=True),
+                          "toolchain": toolchain()}), flush=True)
+        return
     names = [n for n in args.workloads.split(",") if n]
     ws = [workloads.WORKLOADS[n] for n in names]
 
@@ -251,6 +317,10 @@ def main():
     if args.copy_calibration:
         copy = copy_calibration(dev)
 
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = mfma_ceiling(dev, dtypes=sorted({w.dtype for w in ws}))
+
     dom = max(per.values(), key=lambda r: r["avg_ms"])
     dom_w = next(w for w in ws if per[w.name] is dom)
     roofline = {
@@ -270,7 +340,13 @@ def main():
         "roofline": roofline,
         "roofline_by_kernel": {n: {"bound": "mfma", "achieved": r["tflops"],
                                    "peak": PEAK_TFLOPS[r["dtype"]], "unit": "TFLOP/s",
-                                   "frac": r["frac_peak"]} for n, r in per.items()},
+                                   "frac": r["frac_peak"],
+                                   "frac_of_measured_ceiling":
+                                       round(r["tflops"] / ceiling[f"{r['dtype']}_random"]["tflops"], 4)
+                                       if ceiling else None} for n, r in per.items()},
+        # context, not the roofline: an MFMA-only loop on random operands of
+        # the same type, timed on this board in this run
+        "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels

@@ -3,7 +3,9 @@
 Every HIP source under csrc/ is compiled to an object (in parallel), then the
 objects are linked into ``dense_gemm_17_amd/libmi355gemm.so``.  The compiler's
 per-kernel resource remarks (VGPR/AGPR/SGPR counts, scratch, LDS, occupancy)
-are kept in ``_build/resources.txt`` for the resource-budget test.
+are kept in ``_build/resources.txt`` for the resource-budget test.  Sources
+named ``probe_*.hip`` are measurement probes, not GEMM kernels: they go into
+a separate ``libmi355probe.so`` that only the benchmark loads.
 
 Usage:  python dense_gemm_17_amd/build.py   (run by path: importing the package
         needs the library this script builds)
@@ -19,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmi355gemm.so")
+PROBE_LIB = os.path.join(HERE, "libmi355probe.so")
 ROOT = os.path.dirname(HERE)
 
 ARCH = "gfx950"
@@ -35,8 +38,18 @@ HIP_FLAGS = [
 REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(probes: bool = False):
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") and f.startswith("probe_") == probes)
+
+
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
 
 
 def _compile(src: str) -> tuple:
@@ -49,24 +62,22 @@ def _compile(src: str) -> tuple:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared library; returns its path."""
+    """Compile every HIP source and link the shared libraries; returns the
+    GEMM library's path."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
+    srcs, probes = sources(), sources(probes=True)
+    jobs = max(1, min(len(srcs) + len(probes), int(os.environ.get("MAX_JOBS", "8"))))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, srcs))
-    objs = [o for o, _ in results]
+        results = list(ex.map(_compile, srcs + probes))
+    gemm, probe = results[:len(srcs)], results[len(srcs):]
     with open(os.path.join(BUILD, "resources.txt"), "w") as f:
-        for _, remarks in results:
+        for _, remarks in gemm:
             f.write(remarks)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    _link([o for o, _ in gemm], LIB)
+    if probe:
+        _link([o for o, _ in probe], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB} from {len(probes)}")
     return LIB
 
 
