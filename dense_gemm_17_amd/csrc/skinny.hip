@@ -21,6 +21,10 @@
 //     flight that hide HBM latency); the work-group size and that depth
 //     follow from the accumulator count (output rows x columns per lane);
 //   * A is tiny (M x K) and read by every work-group from the caches;
+//   * when strips are fewer than CUs and there are more than 4 rows, each
+//     strip is split by rows between two work-groups whose ids land on the
+//     same XCD back to back, so all CUs stream B and the second read of each
+//     B line hits that XCD's L2 (1.26x at 7 x 4096 x 4096);
 //   * the partial sums of the K-groups are added in a fixed order (lane
 //     shuffles inside a wave, then LDS across waves), so the result is
 //     deterministic; no atomics, no workspace;
@@ -88,8 +92,10 @@ __device__ __forceinline__ f32x4 load_a4(const T *__restrict__ A, int64_t lda, i
     return v;
 }
 
-// kL lanes per K-group, kU rows (kU / 4 blocks) in flight per thread.
-template <typename T, int kM, int kL, int kThreads, int kU, bool kVec>
+// kL lanes per K-group, kU rows (kU / 4 blocks) in flight per thread;
+// kSplit = 2: rows split between two work-groups (ids 16 q + 8 h + x hold
+// strip 8 q + x, rows kM h .. kM h + kM - 1; ids differing by 8 share an XCD).
+template <typename T, int kM, int kL, int kThreads, int kU, bool kVec, int kSplit>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, int64_t K,
                                                           const T *__restrict__ A, int64_t lda,
                                                           const T *__restrict__ B, int64_t ldb,
@@ -105,7 +111,17 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
 
     const int tid = threadIdx.x;
     const int lane = tid % kL, grp = tid / kL;
-    const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kCols;
+    int64_t strip = blockIdx.x;
+    if constexpr (kSplit == 2) {
+        const int64_t id = blockIdx.x;
+        const int64_t half = (id >> 3) & 1;
+        strip = (id >> 4) * 8 + (id & 7);
+        A += half * kM * lda;
+        C += half * kM * ldc;
+        M -= half * kM;
+        if (M <= 0 || strip * kCols >= N) return;   // whole work-group
+    }
+    const int64_t n0 = strip * kCols;
     const int64_t n = n0 + lane * P;
 
     float acc[kM][P];
@@ -171,20 +187,21 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
     }
 }
 
-template <typename T, int kM, int kL, int kThreads, int kU>
+template <typename T, int kM, int kL, int kThreads, int kU, int kSplit>
 hipError_t launch_cfg(const Problem &p, hipStream_t s, bool vec)
 {
     constexpr int kCols = kL * Elem<T>::kPerLoad;
-    const int64_t blocks = (p.N + kCols - 1) / kCols;
+    const int64_t strips = (p.N + kCols - 1) / kCols;
+    const int64_t blocks = kSplit == 2 ? 16 * ((strips + 7) / 8) : strips;
     if (blocks > kMaxBlocks) return hipErrorInvalidValue;
     const T *A = static_cast<const T *>(p.A);
     const T *B = static_cast<const T *>(p.B);
     if (vec)
-        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, true>),
+        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, true, kSplit>),
                            dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p.M, p.N,
                            p.K, A, p.lda, B, p.ldb, p.C, p.ldc);
     else
-        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, false>),
+        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, false, kSplit>),
                            dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p.M, p.N,
                            p.K, A, p.lda, B, p.ldb, p.C, p.ldc);
     return hipGetLastError();
@@ -194,29 +211,44 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s, bool vec)
 // (measured: 512 x 8 rows for M = 1, 1024 x 4 rows for M = 7 fp32).  Larger
 // sets take smaller work-groups so that each thread has the registers
 // without spilling (1024 threads allow 128 VGPRs, 512 allow 256).
-template <typename T, int kM, int kL>
+// (kM is the rows per work-group; measured for split work-groups of 4
+// fp32 rows: 1024 x 4 beats 512 x 8.)
+template <typename T, int kM, int kL, int kSplit>
 hipError_t launch_lanes(const Problem &p, hipStream_t s, bool vec)
 {
     constexpr int kAcc = kM * Elem<T>::kPerLoad;
-    if constexpr (kAcc <= 16) return launch_cfg<T, kM, kL, 512, 8>(p, s, vec);
-    else if constexpr (kAcc <= 32) return launch_cfg<T, kM, kL, 1024, 4>(p, s, vec);
-    else if constexpr (kAcc <= 64) return launch_cfg<T, kM, kL, 512, 4>(p, s, vec);
-    else return launch_cfg<T, kM, kL, 256, 4>(p, s, vec);
+    if constexpr (kAcc <= 16 && kSplit == 1) return launch_cfg<T, kM, kL, 512, 8, kSplit>(p, s, vec);
+    else if constexpr (kAcc <= 32) return launch_cfg<T, kM, kL, 1024, 4, kSplit>(p, s, vec);
+    else if constexpr (kAcc <= 64) return launch_cfg<T, kM, kL, 512, 4, kSplit>(p, s, vec);
+    else return launch_cfg<T, kM, kL, 256, 4, kSplit>(p, s, vec);
 }
 
 // Strip width: the widest of 16, 8, 4 lanes (256, 128, 64 bytes of a B
 // row) that leaves at least 128 strips; wider strips read longer runs of
 // each row but leave CUs idle when strips are few.
-template <typename T, int kM>
+template <typename T, int kM, int kSplit>
 hipError_t launch_m(const Problem &p, hipStream_t s, bool vec)
 {
     constexpr int P = Elem<T>::kPerLoad;
-    if ((p.N + 16 * P - 1) / (16 * P) >= 128) return launch_lanes<T, kM, 16>(p, s, vec);
-    if ((p.N + 8 * P - 1) / (8 * P) >= 128) return launch_lanes<T, kM, 8>(p, s, vec);
-    return launch_lanes<T, kM, 4>(p, s, vec);
+    if ((p.N + 16 * P - 1) / (16 * P) >= 128) return launch_lanes<T, kM, 16, kSplit>(p, s, vec);
+    if ((p.N + 8 * P - 1) / (8 * P) >= 128) return launch_lanes<T, kM, 8, kSplit>(p, s, vec);
+    return launch_lanes<T, kM, 4, kSplit>(p, s, vec);
 }
 
-// Row counts are rounded up to one of a few compiled sizes.
+// Strips of the width launch_m picks (one per work-group without a split).
+template <typename T>
+int64_t strips_of(const Problem &p)
+{
+    constexpr int P = Elem<T>::kPerLoad;
+    for (int lanes : {16, 8}) {
+        const int64_t n = (p.N + lanes * P - 1) / (lanes * P);
+        if (n >= 128) return n;
+    }
+    return (p.N + 4 * P - 1) / (4 * P);
+}
+
+// Row counts are rounded up to one of a few compiled sizes; more than 4
+// rows with fewer strips than CUs are split between two work-groups.
 template <typename T>
 hipError_t launch_skinny(const Problem &p, hipStream_t s)
 {
@@ -224,11 +256,12 @@ hipError_t launch_skinny(const Problem &p, hipStream_t s)
     const bool vec = (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 &&
                      p.ldb % Elem<T>::kPerLoad == 0 &&
                      (reinterpret_cast<uintptr_t>(p.A) & (4 * sizeof(T) - 1)) == 0 && p.lda % 4 == 0;
-    if (p.M <= 1) return launch_m<T, 1>(p, s, vec);
-    if (p.M <= 2) return launch_m<T, 2>(p, s, vec);
-    if (p.M <= 4) return launch_m<T, 4>(p, s, vec);
-    if (p.M <= 8) return launch_m<T, 8>(p, s, vec);
-    return launch_m<T, 16>(p, s, vec);
+    if (p.M <= 1) return launch_m<T, 1, 1>(p, s, vec);
+    if (p.M <= 2) return launch_m<T, 2, 1>(p, s, vec);
+    if (p.M <= 4) return launch_m<T, 4, 1>(p, s, vec);
+    const bool split = strips_of<T>(p) < 256;
+    if (p.M <= 8) return split ? launch_m<T, 4, 2>(p, s, vec) : launch_m<T, 8, 1>(p, s, vec);
+    return split ? launch_m<T, 8, 2>(p, s, vec) : launch_m<T, 16, 1>(p, s, vec);
 }
 
 }  // namespace
