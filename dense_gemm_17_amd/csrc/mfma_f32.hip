@@ -31,6 +31,14 @@
 //     B row;
 //   * ragged edges: rows of A past M, columns of B past N and k past K are
 //     loaded as zeros; rows and columns of C past M, N are not stored.
+//
+// Those are the register-staged kernels (mfma_f32, mfma_f32_128).  The
+// LDS-direct kernels further down (mfma_f32_direct with 256 x 256 tiles,
+// mfma_f32_direct128 with 128 x 128, mfma_f32_direct128x64 with 128 x 64,
+// and mfma_f32_narrow128, the 128 x 128 one with 4-byte loads for any
+// layout) are one template: global -> LDS without registers, a four-stage
+// LDS ring, fragments read one K group ahead, one barrier per tile; they
+// are what the dispatch table runs wherever they apply.
 #include "gemm_internal.h"
 #include "tile_map.h"
 

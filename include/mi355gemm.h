@@ -46,6 +46,8 @@
  *
  * Thread safety: calls from several host threads are safe; kernel selection
  * is a pure function of the arguments unless gemm_force_kernel is in effect.
+ * Graph capture: a call only enqueues kernels (no memset, allocation or
+ * synchronisation), so it can be captured into a HIP graph and replayed.
  */
 #ifndef MI355GEMM_H
 #define MI355GEMM_H

@@ -373,3 +373,79 @@ def test_large_operands_64bit_offsets(dtype, M, N, K):
         assert e <= GATE, (kernel, e, at)
     del Ad, Bd, C
     torch.cuda.empty_cache()
+
+
+def test_concurrent_host_threads_and_streams():
+    """The header promises thread safety: four host threads, each on its own
+    stream, each running several kernel families; every result must equal
+    the single-threaded result bitwise (the kernels are deterministic)."""
+    import threading
+    gen = workloads.generator(84)
+    cases = []
+    for (M, N, K, dt) in [(2048, 2048, 512, torch.float32), (16384, 384, 1536, torch.float32),
+                          (7, 4096, 1024, torch.float32), (1024, 1024, 1024, torch.bfloat16),
+                          (1000, 3000, 777, torch.float32)]:
+        A = workloads.draw((M, K), ("uniform", 1.0), gen).to(dt).to(DEV)
+        B = workloads.draw((K, N), ("uniform", 1.0), gen).to(dt).to(DEV)
+        cases.append((A, B, run(A, B).clone()))
+    errors = []
+
+    def worker(tid):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = []
+                for rep in range(4):
+                    for (A, B, _) in cases:
+                        outs.append(g.gemm(A, B))
+            s.synchronize()
+            for i, C in enumerate(outs):
+                if not torch.equal(C, cases[i % len(cases)][2]):
+                    errors.append((tid, i))
+        except Exception as e:   # noqa: BLE001 - reported below
+            errors.append((tid, repr(e)))
+
+    say("[threads] 4 host threads x 4 reps x 5 cases")
+    ts = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert not errors, errors[:5]
+
+
+def test_graph_capture_replays_match_eager():
+    """Calls captured into a HIP graph (no memset nodes: K = 0 is a fill
+    kernel) replay with the eager result, replay after replay, with eager
+    work and synchronisation between replays."""
+    gen = workloads.generator(85)
+    specs = [(1024, 1024, 512, torch.float32), (512, 768, 256, torch.bfloat16),
+             (3, 4096, 1024, torch.float32), (300, 260, 0, torch.float32),
+             (1000, 3000, 777, torch.float32)]
+    ins, eager, outs = [], [], []
+    for (M, N, K, dt) in specs:
+        A = workloads.draw((M, K), ("uniform", 1.0), gen).to(dt).to(DEV)
+        B = workloads.draw((K, N), ("uniform", 1.0), gen).to(dt).to(DEV)
+        ins.append((A, B))
+        eager.append(run(A, B).clone())
+        outs.append(torch.full((M, N), 7.0, device=DEV))
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for (A, B), C in zip(ins, outs):       # warm-up on the capture stream
+            g.gemm(A, B, out=C)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        for (A, B), C in zip(ins, outs):
+            g.gemm(A, B, out=C)
+    say("[graph] 3 replays")
+    for rep in range(3):
+        for C in outs:
+            C.fill_(-3.0)                       # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, C in enumerate(outs):
+            assert torch.equal(C, eager[i]), (rep, specs[i])
