@@ -10,6 +10,10 @@ averaged per dispatch and turned into:
   * MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES summed over the 1024 SIMDs, over
     GRBM_GUI_ACTIVE summed over the 8 XCDs (both per dispatch), i.e. the
     fraction of the dispatch's cycles each SIMD's matrix core was busy;
+  * VALU issue rate: SQ_INSTS_VALU per SIMD over the dispatch's cycles per
+    XCD.  Without packed math a wave64 fp32 FMA holds a SIMD for 4 cycles
+    (16 lanes per cycle: 1024 SIMDs x 2.4 GHz x 16 x 2 flops = the 78.6
+    TFLOP/s non-packed vector peak), so a kernel of FMAs saturates at 0.25;
   * LDS bank-conflict cycles per LDS instruction;
   * HBM bytes fetched per dispatch: FETCH_SIZE (KiB) x 1024 x the copy
     calibration factor of profiles/hbm_traffic_8192.txt (a plain 256 MiB
@@ -109,20 +113,22 @@ def main(dirs):
             rows[(workload, k)].update({c: v for c, v in cs.items() if c != "_dispatches"})
             rows[(workload, k)]["_dispatches"] = max(cs["_dispatches"],
                                                      rows[(workload, k)].get("_dispatches", 0))
-    print("| Workload | Kernel | Dispatches | MFMA busy | LDS conflict cycles / LDS instr "
+    print("| Workload | Kernel | Dispatches | MFMA busy | VALU instr / SIMD / cycle | LDS conflict cycles / LDS instr "
           "| HBM fetch per dispatch (MB) | VGPR | AGPR | waves/SIMD |")
-    print("|---|---|---|---|---|---|---|---|---|")
+    print("|---|---|---|---|---|---|---|---|---|---|")
     for (w, k), cs in sorted(rows.items()):
         grbm = cs.get("GRBM_GUI_ACTIVE")
         mfma = cs.get("SQ_VALU_MFMA_BUSY_CYCLES")
         busy = f"{100 * (mfma / SIMDS) / (grbm / XCDS):.1f}%" if mfma is not None and grbm else ""
+        valu = cs.get("SQ_INSTS_VALU")
+        vbusy = f"{(valu / SIMDS) / (grbm / XCDS):.3f}" if valu is not None and grbm else ""
         lds = cs.get("SQ_INSTS_LDS")
         conf = cs.get("SQ_LDS_BANK_CONFLICT")
         ldsr = f"{conf / lds:.3f}" if lds and conf is not None else ""
         fetch = cs.get("FETCH_SIZE")
         fmb = f"{fetch * 1024 * scale / 1e6:.1f}" if fetch is not None else ""
         r = res.get(k, {})
-        print(f"| {w} | `{k}` | {cs['_dispatches']} | {busy} | {ldsr} | {fmb} | "
+        print(f"| {w} | `{k}` | {cs['_dispatches']} | {busy} | {vbusy} | {ldsr} | {fmb} | "
               f"{r.get('VGPRs', '')} | {r.get('AGPRs', '')} | {r.get('Occupancy [waves/SIMD]', '')} |")
 
 

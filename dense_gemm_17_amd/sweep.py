@@ -116,6 +116,8 @@ def main():
                     help="time only the dispatch table's choice for each workload")
     ap.add_argument("--max-reps", type=int, default=2000,
                     help="calls per timing window at most (keep small under a counter profiler)")
+    ap.add_argument("--kernel", default=None,
+                    help="time only this kernel (forced) on each workload that it takes")
     ap.add_argument("--no-null", action="store_true",
                     help="skip the identity null (counter runs: every library dispatch is then "
                          "the workload's)")
@@ -151,6 +153,8 @@ def main():
             if g.gemm_kernel_name(kid).startswith("naive") and w.flops > 4e11:
                 continue
             if args.table_only and kid != table:
+                continue
+            if args.kernel and g.gemm_kernel_name(kid) != args.kernel:
                 continue
             g.gemm_force_kernel(kid)
             try:
