@@ -36,6 +36,7 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_direct128", kF32, launch_mfma_f32_direct128, supports_mfma_f32_direct},
     {"mfma_f32_narrow128", kF32, launch_mfma_f32_narrow128, supports_mfma_f32_narrow},
     {"mfma_f32_direct128x64", kF32, launch_mfma_f32_direct128x64, supports_mfma_f32_direct},
+    {"mfma_bf16_direct128", kBF16, launch_mfma_bf16_direct128, supports_mfma_bf16_direct},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -137,8 +138,13 @@ int select_kernel(const Problem &p)
     if (p.M <= kSkinnyMaxM)
         return kernel_id(p.dtype == kF32 ? "skinny_f32" : "skinny_bf16");
     if (p.dtype == kBF16) {
-        if (supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16_direct");
-        return kernel_id("mfma_bf16");
+        if (!supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16");
+        // 128 x 128 runs at 0.8 of the 256 x 256 tile's per-tile efficiency
+        // (fitted over twelve shapes, 0.66-1.03; 0.512 of peak at 8192^3 for
+        // the large tile), so it wins only where 256 tiles fill the CUs badly.
+        if (tiled_cost(p, 256, 256, 1, 512) <= tiled_cost(p, 128, 128, 2, 410))
+            return kernel_id("mfma_bf16_direct");
+        return kernel_id("mfma_bf16_direct128");
     }
     if (supports_mfma_f32_direct(p)) {
         const int64_t c256 = tiled_cost(p, 256, 256, 1, 960);

@@ -46,6 +46,7 @@ bool supports_mfma_f32_narrow(const Problem &p);
 bool supports_mfma_f32_direct(const Problem &p);
 hipError_t launch_mfma_bf16(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_bf16_direct128(const Problem &p, hipStream_t s);
 bool supports_mfma_bf16_direct(const Problem &p);
 hipError_t launch_skinny_f32(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s);

@@ -169,22 +169,24 @@ __device__ __forceinline__ void compute_tile(f32x16 (&acc)[4][4], const uint16_t
     }
 }
 
-// Epilogue: register r of block (mb, nb) in lane (h, c) is C row
-// 8*(r/4) + 4*h + r%4, column c of that 32 x 32 block.
-__device__ __forceinline__ void store_c(const f32x16 (&acc)[4][4], float *__restrict__ C,
+// Epilogue for a wave owning MB x NB blocks (a 32 MB x 32 NB piece of the
+// tile at wave position (wm, wn)): register r of block (mb, nb) in lane
+// (h, c) is C row 8*(r/4) + 4*h + r%4, column c of that 32 x 32 block.
+template <int MB, int NB>
+__device__ __forceinline__ void store_c(const f32x16 (&acc)[MB][NB], float *__restrict__ C,
                                         int64_t ldc, int64_t M, int64_t N, int64_t m0, int64_t n0,
                                         int wm, int wn, int lane)
 {
     const int h = lane >> 5, c = lane & 31;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int64_t col = n0 + wn * 128 + nb * 32 + c;
+        for (int nb = 0; nb < NB; ++nb) {
+            const int64_t col = n0 + wn * 32 * NB + nb * 32 + c;
             if (col >= N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int64_t row = m0 + wm * 32 * MB + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (row < M) C[row * ldc + col] = acc[mb][nb][r];
             }
         }
@@ -240,15 +242,18 @@ void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restric
 
 
 // ---------------------------------------------------------------------------
-// Direct variant: global -> LDS with gfx950's LDS-direct 128-bit loads
-// (global_load_lds_dwordx4), no register staging and no LDS write
-// instructions, into a ring of four 32-wide K stages so that the loads for
-// tile t + 3 are in flight while tile t is multiplied.  One such load per
-// wave writes 1 KiB of LDS at consecutive 16-byte slots in lane order;
-// choosing which global chunk each lane fetches realises the same swizzled
-// layouts as above.  Operand fragments are read one 16-wide K slice ahead
-// (across the tile boundary), each read and each load slotted between
-// MFMAs; one barrier per tile.
+// Direct variants (256 x 256 tile, one work-group per CU; 128 x 128 tile,
+// two per CU, for shapes whose 256-tile count leaves CUs idle): global -> LDS
+// with gfx950's LDS-direct 128-bit loads (global_load_lds_dwordx4), no
+// register staging and no LDS write instructions, into a ring of four
+// 32-wide K stages so that the loads for tile t + 3 are in flight while tile
+// t is multiplied.  One such load per wave writes 1 KiB of LDS at
+// consecutive 16-byte slots in lane order; choosing which global chunk each
+// lane fetches realises the same swizzled layouts as above.  Operand
+// fragments are read one 16-wide K slice ahead (across the tile boundary),
+// each read and each load slotted between MFMAs; one barrier per tile.  Four
+// waves in a 2 x 2 grid, each owning (TM/2) x (TN/2) of C as MB x NB blocks
+// of 32 x 32.
 //
 // Instruction economy: the loads use the scalar-base form (wave-uniform base
 // advanced once per tile + a fixed 32-bit lane offset), the reads use a few
@@ -265,10 +270,21 @@ void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restric
 
 constexpr int DBK = 32;
 constexpr int DSTAGES = 4;
-constexpr int kDAInst = BM * DBK * 2 / 1024 / 4;   // LDS-direct loads per wave per tile (A): 4
-constexpr int kDBInst = DBK * BN * 2 / 1024 / 4;   // ... (B): 4
-constexpr int kDPerTile = kDAInst + kDBInst;
-constexpr int kDStageElems = BM * DBK + DBK * BN;  // bf16 elements per stage
+
+template <int TM, int TN>
+struct DTile {
+    static constexpr int kMB = TM / 64, kNB = TN / 64;         // blocks per wave
+    static constexpr int kAInst = TM * DBK * 2 / 1024 / 4;     // LDS-direct loads per wave per tile (A)
+    static constexpr int kBInst = DBK * TN * 2 / 1024 / 4;     // ... (B)
+    static constexpr int kPerTile = kAInst + kBInst;
+    static constexpr int kStageElems = TM * DBK + DBK * TN;    // bf16 elements per stage
+    static constexpr int kBChunks = TN / 8;                    // 16-byte chunks per B row
+    static constexpr int kQ = kMB * kNB;                       // MFMAs per 16-wide K slice
+    static constexpr int kReads = kMB + 2 * kNB;               // fragment reads per slice
+    // Work-groups per CU the LDS ring allows: 1 (256 x 256), 2 (128 x 128).
+    static constexpr int kPerCU = 160 * 1024 / (DSTAGES * kStageElems * 2);
+    static_assert((DSTAGES - 2) * kPerTile <= 63, "vmcnt is six bits");
+};
 
 // One LDS-direct 128-bit load as inline assembly, scalar-base form: lane i
 // reads 16 bytes at sbase + voff and they land at LDS byte M0 + 16 i.  The
@@ -291,48 +307,56 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
 }
 
 // Everything a wave needs to address its loads and reads.
+template <int TM, int TN>
 struct DCtx {
-    uint32_t a_voff[kDAInst], b_voff[kDBInst];   // lane offsets (bytes) of each load
-    const char *abase, *bbase;                   // tile (k = 0) bases, wave-uniform
-    int64_t a_kstride, b_kstride;                // bytes per K step
-    uint32_t lds0;                               // LDS byte address of stage 0
+    using T = DTile<TM, TN>;
+    uint32_t a_voff[T::kAInst], b_voff[T::kBInst];   // lane offsets (bytes) of each load
+    const char *abase, *bbase;                       // tile (k = 0) bases, wave-uniform
+    int64_t a_kstride, b_kstride;                    // bytes per K step
+    uint32_t lds0;                                   // LDS byte address of stage 0
     int wave;
-    uint32_t rdA[2];                             // lane read offsets: A, per K slice
-    uint32_t rdB[4];                             // lane read offsets: B, per 32-column block
+    uint32_t rdA[2];                                 // lane read offsets: A, per K slice
+    uint32_t rdB[T::kNB];                            // lane read offsets: B, per 32-column block
 };
 
-__device__ __forceinline__ void load_one(const DCtx &x, uint32_t stage_lds, int64_t kt, int l)
+template <int TM, int TN>
+__device__ __forceinline__ void load_one(const DCtx<TM, TN> &x, uint32_t stage_lds, int64_t kt,
+                                         int l)
 {
-    if (l < kDAInst)
+    using T = DTile<TM, TN>;
+    if (l < T::kAInst)
         lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride,
-                          stage_lds + (x.wave * kDAInst + l) * 1024);
+                          stage_lds + (x.wave * T::kAInst + l) * 1024);
     else
-        lds_direct_load16(x.b_voff[l - kDAInst], x.bbase + kt * x.b_kstride,
-                          stage_lds + BM * DBK * 2 + (x.wave * kDBInst + l - kDAInst) * 1024);
+        lds_direct_load16(x.b_voff[l - T::kAInst], x.bbase + kt * x.b_kstride,
+                          stage_lds + TM * DBK * 2 + (x.wave * T::kBInst + l - T::kAInst) * 1024);
 }
 
-// Operand fragments of one 16-wide K slice for a wave's 4 x 4 MFMA blocks:
+// Operand fragments of one 16-wide K slice for a wave's MB x NB MFMA blocks:
 // A as one 8-element register quad per 32-row block, B as two 4-element
 // halves (k 0-3 and 4-7 of the lane's eight) per 32-column block.
+template <int TM, int TN>
 struct Frag16 {
-    bf16x8 a[4];
-    bf16x4 blo[4], bhi[4];
+    bf16x8 a[DTile<TM, TN>::kMB];
+    bf16x4 blo[DTile<TM, TN>::kNB], bhi[DTile<TM, TN>::kNB];
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-// Read j (0..11) of slice s from the stage at `stage`: j < 4 is A block j,
-// then B block (j - 4) / 2, lower / upper four k.
-__device__ __forceinline__ void read_one(Frag16 &f, const uint16_t *stage, const DCtx &x, int s,
-                                         int j)
+// Read j of slice s from the stage at `stage`: j < MB is A block j, then B
+// block (j - MB) / 2, lower / upper four k.
+template <int TM, int TN>
+__device__ __forceinline__ void read_one(Frag16<TM, TN> &f, const uint16_t *stage,
+                                         const DCtx<TM, TN> &x, int s, int j)
 {
+    using T = DTile<TM, TN>;
     const char *st = reinterpret_cast<const char *>(stage);
-    if (j < 4) {
+    if (j < T::kMB) {
         const u16x8 v = *reinterpret_cast<const u16x8 *>(st + x.rdA[s] + j * 2048);
         f.a[j] = __builtin_bit_cast(bf16x8, v);
     } else {
-        const int nb = (j - 4) >> 1, upper = (j - 4) & 1;
-        const char *p = st + x.rdB[nb] + s * (16 * BN * 2) + upper * (4 * BN * 2);
+        const int nb = (j - T::kMB) >> 1, upper = (j - T::kMB) & 1;
+        const char *p = st + x.rdB[nb] + s * (16 * TN * 2) + upper * (4 * TN * 2);
         const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (lds_bf16x4_t *)((__attribute__((address_space(3))) char *)(p)));
         if (upper) f.bhi[nb] = v;
@@ -340,27 +364,49 @@ __device__ __forceinline__ void read_one(Frag16 &f, const uint16_t *stage, const
     }
 }
 
-__device__ __forceinline__ void mfma_one(f32x16 (&acc)[4][4], const Frag16 &f, int q)
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_one(f32x16 (&acc)[TM / 64][TN / 64], const Frag16<TM, TN> &f,
+                                         int q)
 {
-    const int mb = q >> 2, nb = q & 3;
+    constexpr int NB = DTile<TM, TN>::kNB;
+    const int mb = q / NB, nb = q % NB;
     const bf16x8 b = __builtin_shufflevector(f.blo[nb], f.bhi[nb], 0, 1, 2, 3, 4, 5, 6, 7);
     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], b, acc[mb][nb], 0, 0, 0);
 }
 
-// The 16 MFMAs of one slice: the 12 reads of the next slice go out after
-// MFMAs 0..11 and (if loads) this wave's 8 LDS-direct loads of a later tile
-// after every other MFMA.  sched_barrier(0) pins that order so the matrix
-// unit keeps running while reads and loads are in flight.
-__device__ __forceinline__ void mfma_phase(f32x16 (&acc)[4][4], const Frag16 &cur, Frag16 &nxt,
-                                           const uint16_t *rstage, const DCtx &x, int s_next,
-                                           uint32_t lstage, int64_t kload, bool loads)
+// The MFMAs of one slice with the reads of the next slice and (if loads)
+// this wave's LDS-direct loads of a later tile slotted in: one read after
+// each of the first MFMAs and a load after every other MFMA when there are
+// enough MFMAs (256 x 256), spread evenly otherwise (128 x 128: 4 MFMAs, 6
+// reads, 4 loads).  sched_barrier(0) pins that order so the matrix unit
+// keeps running while reads and loads are in flight.
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_phase(f32x16 (&acc)[TM / 64][TN / 64],
+                                           const Frag16<TM, TN> &cur, Frag16<TM, TN> &nxt,
+                                           const uint16_t *rstage, const DCtx<TM, TN> &x,
+                                           int s_next, uint32_t lstage, int64_t kload, bool loads)
 {
+    using T = DTile<TM, TN>;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < T::kQ; ++q) {
         mfma_one(acc, cur, q);
         __builtin_amdgcn_sched_barrier(0);
-        if (q < 12) read_one(nxt, rstage, x, s_next, q);
-        if (loads && (q & 1)) load_one(x, lstage, kload, q >> 1);
+        if constexpr (T::kReads <= T::kQ) {
+            if (q < T::kReads) read_one(nxt, rstage, x, s_next, q);
+        } else {
+#pragma unroll
+            for (int r = 0; r < T::kReads; ++r)
+                if (r * T::kQ / T::kReads == q) read_one(nxt, rstage, x, s_next, r);
+        }
+        if (loads) {
+            if constexpr (2 * T::kPerTile <= T::kQ) {
+                if (q & 1) load_one(x, lstage, kload, q >> 1);
+            } else {
+#pragma unroll
+                for (int l = 0; l < T::kPerTile; ++l)
+                    if (l * T::kQ / T::kPerTile == q) load_one(x, lstage, kload, l);
+            }
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -377,22 +423,26 @@ __device__ __forceinline__ void wait_lds_vm_barrier()
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(kCntVm) : "memory");
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int TM, int TN>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DTile<TM, TN>::kPerCU, DTile<TM, TN>::kPerCU)))
 void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
                              int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
                              float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * kDStageElems];
+    using T = DTile<TM, TN>;
+    constexpr int MB = T::kMB, NB = T::kNB, WM = TM / 2, WN = TN / 2;
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * T::kStageElems];
 
     const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
-    const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
+    const int64_t m0 = t.tm * TM, n0 = t.tn * TN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, c = lane & 31;
     const int i16 = lane & 15, nhalf = (lane >> 4) & 1;
 
-    DCtx x;
+    DCtx<TM, TN> x;
     x.wave = wave;
     x.lds0 = lds_offset(lds);
     x.abase = reinterpret_cast<const char *>(A + m0 * lda);
@@ -400,48 +450,48 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
     x.a_kstride = DBK * 2;
     x.b_kstride = DBK * ldb * 2;
 #pragma unroll
-    for (int i = 0; i < kDAInst; ++i) {
-        const int p = (wave * kDAInst + i) * 64 + lane;    // LDS chunk this lane fills
+    for (int i = 0; i < T::kAInst; ++i) {
+        const int p = (wave * T::kAInst + i) * 64 + lane;   // LDS chunk this lane fills
         const int row = p >> 2, slot = p & 3;
         const int cc = slot ^ a_swz<4>(row);
         const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
         x.a_voff[i] = static_cast<uint32_t>((r * lda + 8 * cc) * 2);
     }
 #pragma unroll
-    for (int i = 0; i < kDBInst; ++i) {
-        const int p = (wave * kDBInst + i) * 64 + lane;
-        const int row = p >> 5, slot = p & 31;
+    for (int i = 0; i < T::kBInst; ++i) {
+        const int p = (wave * T::kBInst + i) * 64 + lane;
+        const int row = p / T::kBChunks, slot = p % T::kBChunks;
         const int cc = slot ^ b_swz(row);
         const int64_t col = (n0 + 8 * cc < N) ? 8 * cc : N - 8 - n0;
         x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 2);
     }
-    // A rows this lane reads are wm*128 + 32*j + c: their swizzle is a_swz<4>(c)
+    // A rows this lane reads are wm*WM + 32*j + c: their swizzle is a_swz<4>(c)
     // (it depends on bits 2-3 of the row only).
     const int aswz = a_swz<4>(c);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        x.rdA[s] = (wm * 128 + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+        x.rdA[s] = (wm * WM + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
     // B rows this lane points at are 16s + 8h + i16/4 (+4): swizzle b_swz(i16/4).
     const int bswz = b_swz(i16 >> 2);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int n = wn * 128 + nb * 32 + nhalf * 16 + 4 * (i16 & 3);
-        x.rdB[nb] = BM * DBK * 2 + (8 * h + (i16 >> 2)) * BN * 2 + (((n >> 3) ^ bswz) << 4) +
+    for (int nb = 0; nb < NB; ++nb) {
+        const int n = wn * WN + nb * 32 + nhalf * 16 + 4 * (i16 & 3);
+        x.rdB[nb] = TM * DBK * 2 + (8 * h + (i16 >> 2)) * TN * 2 + (((n >> 3) ^ bswz) << 4) +
                     (n & 7) * 2;
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int64_t ktiles = K / DBK;
-    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * kDStageElems; };
+    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * T::kStageElems; };
     auto lstage = [&](int64_t kt) {
-        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * kDStageElems * 2;
+        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * T::kStageElems * 2;
     };
     auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
 
@@ -450,12 +500,12 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 #pragma unroll
     for (int st = 0; st < DSTAGES - 1; ++st)
 #pragma unroll
-        for (int l = 0; l < kDPerTile; ++l) load_one(x, lstage(st), kclamp(st), l);
-    wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+        for (int l = 0; l < T::kPerTile; ++l) load_one(x, lstage(st), kclamp(st), l);
+    wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
 
-    Frag16 f0, f1;
+    Frag16<TM, TN> f0, f1;
 #pragma unroll
-    for (int j = 0; j < 12; ++j) read_one(f0, stage(0), x, 0, j);
+    for (int j = 0; j < T::kReads; ++j) read_one(f0, stage(0), x, 0, j);
 
     // Tile kt:  MFMAs on slice 0 with the reads of slice 1 and the loads of
     // tile kt + 3 slotted in (that stage was last read in tile kt - 1, which
@@ -466,7 +516,7 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
     for (int64_t kt = 0; kt < ktiles; ++kt) {
         const int64_t nxt = kt + DSTAGES - 1;
         mfma_phase(acc, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
-        wait_lds_vm_barrier<(DSTAGES - 2) * kDPerTile>();
+        wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
         mfma_phase(acc, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
     }
     // No LDS-direct load may still be writing LDS when the work-group ends.
@@ -511,14 +561,22 @@ bool supports_mfma_bf16_direct(const Problem &p)
            al(p.B) && p.lda < (int64_t(1) << 23) && p.ldb < (int64_t(1) << 26);
 }
 
-hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s)
+namespace {
+
+template <int TM, int TN>
+hipError_t launch_direct(const Problem &p, hipStream_t s)
 {
-    const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
+    const int64_t tm = (p.M + TM - 1) / TM, tn = (p.N + TN - 1) / TN;
     if (tm * tn > kMaxBlocks || !supports_mfma_bf16_direct(p)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mfma_bf16_direct_kernel, dim3(static_cast<uint32_t>(tm * tn)),
+    hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN>), dim3(static_cast<uint32_t>(tm * tn)),
                        dim3(kThreads), 0, s, p.M, p.N, p.K, static_cast<const uint16_t *>(p.A),
                        p.lda, static_cast<const uint16_t *>(p.B), p.ldb, p.C, p.ldc, tm, tn);
     return hipGetLastError();
 }
+
+}  // namespace
+
+hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256>(p, s); }
+hipError_t launch_mfma_bf16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128>(p, s); }
 
 }  // namespace mi355gemm

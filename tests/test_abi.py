@@ -139,6 +139,8 @@ DISPATCH_GOLDEN = {
     "skinny_7x4096x4096": "skinny_f32",
     "ragged_1000x3000x777": "mfma_f32_narrow128",
     "ragged_4097x4095x1023": "mfma_f32_narrow128",
+    "bf16_gpt_qkv": "mfma_bf16_direct128",
+    "bf16_gpt_mlp_down": "mfma_bf16_direct128",
 }
 
 
@@ -152,8 +154,12 @@ def test_dispatch_golden(name):
 
 def test_dispatch_layout_cases():
     name = lambda *a, **k: g.gemm_kernel_name(g.gemm_plan(*a, **k))  # noqa: E731
-    # bf16: the LDS-direct kernel needs K % 32, N % 8, 16-byte aligned rows
+    # bf16: the LDS-direct kernels need K % 32, N % 8, 16-byte aligned rows;
+    # the 128 tile only where 256 tiles fill the CUs badly
     assert name(g.BF16, 8192, 8192, 8192, A=PA, B=PB, C=PC) == "mfma_bf16_direct"
+    assert name(g.BF16, 4096, 4096, 4096, A=PA, B=PB, C=PC) == "mfma_bf16_direct"
+    assert name(g.BF16, 2048, 2048, 8192, A=PA, B=PB, C=PC) == "mfma_bf16_direct128"
+    assert name(g.BF16, 5120, 5120, 2048, A=PA, B=PB, C=PC) == "mfma_bf16_direct"
     assert name(g.BF16, 8192, 8192, 8200, A=PA, B=PB, C=PC) == "mfma_bf16"
     assert name(g.BF16, 8192, 8196, 8192, A=PA, B=PB, C=PC) == "mfma_bf16"
     assert name(g.BF16, 8192, 8192, 8192, A=PA + 2, B=PB, C=PC) == "mfma_bf16"

@@ -133,7 +133,8 @@ def check(w: Workload, kernel):
 # -------------------------------------------------------------------- tests
 
 SMALL_WORKLOADS = ["f32_256", "gpt_qkv", "gpt_mlp_up", "gpt_mlp_down", "skinny_1x8960x1536",
-                   "skinny_7x4096x4096", "ragged_1000x3000x777", "ragged_4097x4095x1023"]
+                   "skinny_7x4096x4096", "ragged_1000x3000x777", "ragged_4097x4095x1023",
+                   "bf16_gpt_qkv", "bf16_gpt_mlp_down"]
 LARGE_WORKLOADS = ["f32_4096", "f32_8192", "bf16_8192"]
 
 

@@ -23,7 +23,8 @@ OCCUPANCY_BUDGET = {
     "mfma_f32_kernelILi256ELi256E": 1,
     "mfma_f32_kernelILi128ELi128E": 2,
     "mfma_bf16_kernel": 1,
-    "mfma_bf16_direct_kernel": 1,
+    "mfma_bf16_direct_kernelILi256ELi256E": 1,
+    "mfma_bf16_direct_kernelILi128ELi128E": 2,
     "mfma_f32_direct_kernelILi256ELi256E": 1,
     "mfma_f32_direct_kernelILi128ELi128E": 2,
     "mfma_f32_direct_kernelILi128ELi64E": 3,
@@ -78,9 +79,14 @@ def test_occupancy_budget(kernels):
 
 def test_matrix_core_accumulators_live_in_agprs(kernels):
     # the 256 x 256 tiles keep all 256 accumulators per lane in AGPRs
+    big = ("mfma_f32_kernelILi256ELi256E", "mfma_f32_direct_kernelILi256ELi256E",
+           "mfma_bf16_kernel", "mfma_bf16_direct_kernelILi256ELi256E")
+    seen = 0
     for name, r in kernels.items():
-        if "mfma_f32_kernelILi256ELi256E" in name or "mfma_bf16" in name:
+        if any(f in name for f in big):
+            seen += 1
             assert int(r["AGPRs"]) == 256, (name, r)
+    assert seen >= 4
 
 
 def test_lds_within_gfx950_limit(kernels):

@@ -71,6 +71,12 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("skinny_7x4096x4096", 7, 4096, 4096, "f32", note="seven-row product"),
     Workload("ragged_1000x3000x777", 1000, 3000, 777, "f32", note="ragged, K not a multiple of 4"),
     Workload("ragged_4097x4095x1023", 4097, 4095, 1023, "f32", note="ragged in every dimension"),
+    # beyond the listed configurations: the GPT projections in bf16 (the same
+    # draws rounded), where 256 x 256 tiles leave CUs idle
+    Workload("bf16_gpt_qkv", 16384, 1152, 384, "bf16", _ACT, _WGT,
+             note="GPT QKV projection, bf16 operands"),
+    Workload("bf16_gpt_mlp_down", 16384, 384, 1536, "bf16", _ACT, _WGT,
+             note="GPT MLP down, bf16 operands"),
 ]}
 
 # Groups of the workload list as the parity tests and the benchmark use them.
