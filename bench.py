@@ -36,6 +36,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -57,11 +58,14 @@ CSRC = os.path.join(ROOT, "dense_gemm_17_amd", "csrc")
 KERNEL_SOURCES = {
     "mfma_f32": ("mfma_f32_kernel<256, 256, true>", ["mfma_f32.hip"]),
     "mfma_f32_128": ("mfma_f32_kernel<128, 128, true>", ["mfma_f32.hip"]),
-    "mfma_f32_direct": ("mfma_f32_direct_kernel", ["mfma_f32.hip"]),
-    "mfma_bf16_direct": ("mfma_bf16_direct_kernel", ["mfma_bf16.hip"]),
+    "mfma_f32_direct": ("mfma_f32_direct_kernel<256, 256, 16>", ["mfma_f32.hip"]),
+    "mfma_bf16_direct": ("mfma_bf16_direct_kernel<256, 256>", ["mfma_bf16.hip"]),
     "mfma_bf16": ("mfma_bf16_kernel<true>", ["mfma_bf16.hip"]),
 }
-COMMON_SOURCES = ["gemm_internal.h", "tile_map.h"]
+# The traffic a kernel causes is set by its own source and the tile order;
+# gemm_internal.h only declares the launchers and the host-side argument
+# struct, so it is not part of the digest.
+COMMON_SOURCES = ["tile_map.h"]
 COPY_BYTES = 256 * 1024 * 1024
 
 
@@ -136,13 +140,21 @@ def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
     return res
 
 
+def code_text(path: str) -> str:
+    """Source text without comments and with whitespace runs collapsed: what
+    the compiler sees of it (a comment edit does not change the kernel)."""
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel: str):
     if kernel not in KERNEL_SOURCES:
         return None
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel][1] + COMMON_SOURCES:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        h.update(code_text(os.path.join(CSRC, f)).encode())
     return h.hexdigest()[:16]
 
 
