@@ -37,6 +37,7 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_narrow128", kF32, launch_mfma_f32_narrow128, supports_mfma_f32_narrow},
     {"mfma_f32_direct128x64", kF32, launch_mfma_f32_direct128x64, supports_mfma_f32_direct},
     {"mfma_bf16_direct128", kBF16, launch_mfma_bf16_direct128, supports_mfma_bf16_direct},
+    {"mfma_f32_narrow128x64", kF32, launch_mfma_f32_narrow128x64, supports_mfma_f32_narrow},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -154,9 +155,14 @@ int select_kernel(const Problem &p)
         if (c128 <= c64) return kernel_id("mfma_f32_direct128");
         return kernel_id("mfma_f32_direct128x64");
     }
-    // Ragged K, unaligned rows: the narrow-load kernel (0.938 at 8192^3)
-    // beats both register-staged tiles on every shape.
-    if (supports_mfma_f32_narrow(p)) return kernel_id("mfma_f32_narrow128");
+    // Ragged K, unaligned rows: the narrow-load kernels (128 x 128: 0.938,
+    // 128 x 64 with three per CU: 0.874 at 8192^3) beat both register-staged
+    // tiles on every shape.
+    if (supports_mfma_f32_narrow(p)) {
+        if (tiled_cost(p, 128, 128, 2, 938) <= tiled_cost(p, 128, 64, 3, 874))
+            return kernel_id("mfma_f32_narrow128");
+        return kernel_id("mfma_f32_narrow128x64");
+    }
     if (tiled_cost(p, 256, 256, 1, 700) <= tiled_cost(p, 128, 128, 2, 670))
         return kernel_id("mfma_f32");
     return kernel_id("mfma_f32_128");

@@ -35,8 +35,8 @@
 // Those are the register-staged kernels (mfma_f32, mfma_f32_128).  The
 // LDS-direct kernels further down (mfma_f32_direct with 256 x 256 tiles,
 // mfma_f32_direct128 with 128 x 128, mfma_f32_direct128x64 with 128 x 64,
-// and mfma_f32_narrow128, the 128 x 128 one with 4-byte loads for any
-// layout) are one template: global -> LDS without registers, a four-stage
+// and mfma_f32_narrow128 / mfma_f32_narrow128x64, the 128-row ones with
+// 4-byte loads for any layout) are one template: global -> LDS without registers, a four-stage
 // LDS ring, fragments read one K group ahead, one barrier per tile; they
 // are what the dispatch table runs wherever they apply.
 #include "gemm_internal.h"
@@ -331,7 +331,11 @@ struct DTile {
     // every MFMA when there are fewer than two per read); the loads of a
     // later tile after MFMAs kLoadQ0, kLoadQ0 + kLoadStep, ...
     static constexpr bool kReadEveryOther = 2 * kReads <= kQ;
-    static constexpr int kLoadQ0 = BM == 256 ? 20 : kNB == 1 ? kQ - kPerTile : (kW == 16 ? 1 : 0);
+    // When the loads outnumber the MFMAs of a group (the narrow 128 x 64
+    // tile: 12 loads, 8 MFMAs), load l goes after MFMA l * kQ / kPerTile.
+    static constexpr bool kSpreadLoads = kPerTile > kQ;
+    static constexpr int kLoadQ0 =
+        BM == 256 ? 20 : kSpreadLoads ? 0 : kNB == 1 ? kQ - kPerTile : (kW == 16 ? 1 : 0);
     static constexpr int kLoadStep = kW == 16 && kNB > 1 ? 4 : 1;
     // Work-groups per CU the LDS ring allows (and the occupancy asked of the
     // compiler): 1 for 256 x 256, 2 for 128 x 128, 3 for 128 x 64.
@@ -340,7 +344,8 @@ struct DTile {
     // two half-waves read rows 4 apart: 16-byte chunks of B rows are
     // XOR-permuted by 8 * bit 2 of the row so those rows use different banks.
     static constexpr bool kBSwz = kNB == 1;
-    static_assert(kReads <= kQ && kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ, "slots");
+    static_assert(kReads <= kQ && (kSpreadLoads || kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ),
+                  "slots");
     static_assert((DSTAGES - 2) * kPerTile <= 63, "vmcnt is six bits");
     static_assert(kNB == 1 || kNB == 2 || kNB == 4, "B read width");
 };
@@ -468,14 +473,25 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[mb][j], cur.b[j][nb], acc[mb][nb],
                                                             0, 0, 0);
         const bool rd = T::kReadEveryOther ? (q < 2 * T::kReads && (q & 1) == 0) : q < T::kReads;
-        const bool ld = loads && q >= T::kLoadQ0 &&
-                        q < T::kLoadQ0 + T::kLoadStep * T::kPerTile &&
-                        (q - T::kLoadQ0) % T::kLoadStep == 0;
-        if (rd || ld) {
+        if constexpr (T::kSpreadLoads) {
             __builtin_amdgcn_sched_barrier(0);
-            if (rd) read_one(nxt, rstage, x, g_next, T::kReadEveryOther ? q >> 1 : q);
-            if (ld) load_one(x, lstage, kload, (q - T::kLoadQ0) / T::kLoadStep);
+            if (rd) read_one(nxt, rstage, x, g_next, q);
+            if (loads) {
+#pragma unroll
+                for (int l = 0; l < T::kPerTile; ++l)
+                    if (l * T::kQ / T::kPerTile == q) load_one(x, lstage, kload, l);
+            }
             __builtin_amdgcn_sched_barrier(0);
+        } else {
+            const bool ld = loads && q >= T::kLoadQ0 &&
+                            q < T::kLoadQ0 + T::kLoadStep * T::kPerTile &&
+                            (q - T::kLoadQ0) % T::kLoadStep == 0;
+            if (rd || ld) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (rd) read_one(nxt, rstage, x, g_next, T::kReadEveryOther ? q >> 1 : q);
+                if (ld) load_one(x, lstage, kload, (q - T::kLoadQ0) / T::kLoadStep);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 }
@@ -533,7 +549,8 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
             col = (n0 + 4 * lc < N) ? 4 * lc : N - 4 - n0;
         } else {
             row = p / BN;
-            const int cl = p % BN;
+            int cl = p % BN;
+            if constexpr (T::kBSwz) cl = 4 * ((cl >> 2) ^ b_swz8(static_cast<int>(row))) + (cl & 3);
             col = (n0 + cl < N) ? cl : N - 1 - n0;
         }
         x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 4);
@@ -611,8 +628,11 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
                 lds[p] = (k < K) ? A[r * lda + k] : 0.f;
             }
             for (int p = threadIdx.x; p < DBK * BN; p += kThreads) {
-                const int64_t k = k0 + p / BN;
-                const int64_t cl = n0 + p % BN;
+                const int row = p / BN;
+                int c4 = p % BN;
+                if constexpr (T::kBSwz) c4 = 4 * ((c4 >> 2) ^ b_swz8(row)) + (c4 & 3);
+                const int64_t k = k0 + row;
+                const int64_t cl = n0 + c4;
                 lds[BM * DBK + p] = (k < K) ? B[k * ldb + (cl < N ? cl : N - 1)] : 0.f;
             }
             __syncthreads();
@@ -693,5 +713,6 @@ hipError_t launch_mfma_f32_direct(const Problem &p, hipStream_t s) { return laun
 hipError_t launch_mfma_f32_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, 16>(p, s); }
 hipError_t launch_mfma_f32_narrow128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, 4>(p, s); }
 hipError_t launch_mfma_f32_direct128x64(const Problem &p, hipStream_t s) { return launch_direct<128, 64, 16>(p, s); }
+hipError_t launch_mfma_f32_narrow128x64(const Problem &p, hipStream_t s) { return launch_direct<128, 64, 4>(p, s); }
 
 }  // namespace mi355gemm

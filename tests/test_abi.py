@@ -137,8 +137,8 @@ DISPATCH_GOLDEN = {
     "bf16_8192": "mfma_bf16_direct",
     "skinny_1x8960x1536": "skinny_f32",
     "skinny_7x4096x4096": "skinny_f32",
-    "ragged_1000x3000x777": "mfma_f32_narrow128",
-    "ragged_4097x4095x1023": "mfma_f32_narrow128",
+    "ragged_1000x3000x777": "mfma_f32_narrow128x64",
+    "ragged_4097x4095x1023": "mfma_f32_narrow128x64",
     "bf16_gpt_qkv": "mfma_bf16_direct128",
     "bf16_gpt_mlp_down": "mfma_bf16_direct128",
 }
