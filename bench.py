@@ -143,7 +143,10 @@ def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
 def code_text(path: str) -> str:
     """Source text without comments and with whitespace runs collapsed: what
     the compiler sees of it (a comment edit does not change the kernel)."""
-    text = open(path, encoding="utf-8").read()
+    return code_text_from(open(path, encoding="utf-8").read())
+
+
+def code_text_from(text: str) -> str:
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     return " ".join(text.split())
