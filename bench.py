@@ -106,15 +106,17 @@ def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
     lib = ctypes.CDLL(PROBE_LIB)
     lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_void_p, ctypes.c_void_p]
-    blocks = 1024
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    out = torch.empty(4096 * 256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     res = {}
     for dt in dtypes:
-        iters = 8000 if dt == "bf16" else 2000          # ~5-10 ms per launch
+        # ~5-10 ms per launch.  The vector-ALU loop runs four waves per SIMD
+        # (4096 work-groups) to cover the FMA latency.
+        code, blocks, iters = {"f32": (0, 1024, 2000), "bf16": (1, 1024, 8000),
+                               "f32_valu": (2, 4096, 20000)}[dt]
         for zero in ([0, 1] if zero_too else [0]):
             def launch():
-                rc = lib.probe_mfma_loop(1 if dt == "bf16" else 0, blocks, iters, zero,
+                rc = lib.probe_mfma_loop(code, blocks, iters, zero,
                                          out.data_ptr(), stream.cuda_stream)
                 if rc != 0:
                     raise RuntimeError(f"probe_mfma_loop failed: {rc}")
@@ -132,10 +134,11 @@ def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
                 e1.record(stream)
                 torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            flops = blocks * 4 * iters * 16 * PROBE_FLOPS[dt]
+            flops = blocks * 4 * iters * 16 * PROBE_FLOPS[dt] if dt != "f32_valu" else \
+                blocks * 256 * iters * 16 * 2
             tf = flops / (ms * 1e-3) / 1e12
             res[f"{dt}_{'zero' if zero else 'random'}"] = {
-                "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_TFLOPS[dt], 4),
+                "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_TFLOPS["bf16" if dt == "bf16" else "f32"], 4),
                 **clocks.summary()}
     return res
 
@@ -250,8 +253,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.ceiling_only:
-        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, zero_too=True),
-                          "toolchain": toolchain()}), flush=True)
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, dtypes=("bf16", "f32", "f32_valu"),
+                                                        zero_too=True),
+                          "toolchain": toolchain(g.gemm_build_info())}), flush=True)
         return
     names = [n for n in args.workloads.split(",") if n]
     ws = [workloads.WORKLOADS[n] for n in names]
@@ -365,7 +369,7 @@ def main():
         "cpu_baseline": cpu,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels
-        "env": dict(clocks.summary(), toolchain=toolchain()),
+        "env": dict(clocks.summary(), toolchain=toolchain(g.gemm_build_info())),
     }
     if copy is not None:
         line["copy_calibration"] = copy

@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm_force_kernel.restype = ci
     lib.gemm_last_kernel.argtypes = []
     lib.gemm_last_kernel.restype = ci
+    lib.gemm_build_info.argtypes = []
+    lib.gemm_build_info.restype = ctypes.c_char_p
     return lib
 
 
@@ -57,7 +59,8 @@ lib = _load()
 
 # Every symbol include/mi355gemm.h declares.
 EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_kernel_count", "gemm_kernel_name",
-           "gemm_kernel_dtype", "gemm_plan", "gemm_force_kernel", "gemm_last_kernel")
+           "gemm_kernel_dtype", "gemm_plan", "gemm_force_kernel", "gemm_last_kernel",
+           "gemm_build_info")
 
 
 # ---- raw entry points (pointers and sizes, same names as the C-ABI) --------
@@ -97,6 +100,10 @@ def gemm_force_kernel(kid: int) -> int:
 
 def gemm_last_kernel() -> int:
     return lib.gemm_last_kernel()
+
+
+def gemm_build_info() -> str:
+    return lib.gemm_build_info().decode()
 
 
 def kernel_id(name: str) -> int:

@@ -11,9 +11,9 @@ averaged per dispatch and turned into:
     GRBM_GUI_ACTIVE summed over the 8 XCDs (both per dispatch), i.e. the
     fraction of the dispatch's cycles each SIMD's matrix core was busy;
   * VALU issue rate: SQ_INSTS_VALU per SIMD over the dispatch's cycles per
-    XCD.  Without packed math a wave64 fp32 FMA holds a SIMD for 4 cycles
-    (16 lanes per cycle: 1024 SIMDs x 2.4 GHz x 16 x 2 flops = the 78.6
-    TFLOP/s non-packed vector peak), so a kernel of FMAs saturates at 0.25;
+    XCD.  A loop of nothing but scalar fp32 FMAs reaches 90% of the 157.3
+    TFLOP/s vector peak on gfx950 (profiles/mfma_ceiling.md), i.e. a wave64
+    FMA issues in about two cycles, so such a loop sits near 0.45-0.5;
   * LDS bank-conflict cycles per LDS instruction;
   * HBM bytes fetched per dispatch: FETCH_SIZE (KiB) x 1024 x the copy
     calibration factor of profiles/hbm_traffic_8192.txt (a plain 256 MiB

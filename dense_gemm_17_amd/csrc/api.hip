@@ -252,4 +252,12 @@ int gemm_force_kernel(int id)
 
 int gemm_last_kernel(void) { return g_last.load(std::memory_order_relaxed); }
 
+#define MI355_STR2(x) #x
+#define MI355_STR(x) MI355_STR2(x)
+const char *gemm_build_info(void)
+{
+    return "clang " __clang_version__ "; HIP " MI355_STR(HIP_VERSION_MAJOR) "." MI355_STR(
+        HIP_VERSION_MINOR) "." MI355_STR(HIP_VERSION_PATCH) "; gfx950";
+}
+
 }  // extern "C"

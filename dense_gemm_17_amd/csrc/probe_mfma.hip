@@ -130,9 +130,35 @@ void f32_loop(float *out, int iters)
     out[t] = sum;
 }
 
+// Vector-ALU counterpart: 16 independent fp32 FMA chains per lane
+// (acc = acc * a + b, |a| < 1 so the values stay bounded), no memory
+// traffic, several waves per SIMD to cover the FMA latency.  The ceiling of
+// the scalar (non-packed) fp32 FMA issue rate, which the vector-ALU GEMM
+// kernel is built on.
+template <bool kZero>
+__global__ __launch_bounds__(256) void valu_loop(float *out, int iters)
+{
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    float acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = kZero ? 0.f : f32_operand(t * 16u + j);
+    // a in [0.5, 0.99): 0.49 * (a float in [1, 2) with a hashed mantissa) + 0.01
+    const float a = kZero ? 0.f : 0.49f * __uint_as_float(0x3f800000u | (mix(t ^ 0x9e3779b9u) >> 9)) + 0.01f;
+    const float b = kZero ? 0.f : f32_operand(t * 16u + 15u) * 0.01f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = __builtin_fmaf(acc[j], a, b);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += acc[j];
+    out[t] = sum;
+}
+
 }  // namespace
 
-// dtype 0 = fp32 (v_mfma_f32_32x32x2_f32), 1 = bf16 (v_mfma_f32_32x32x16_bf16).
+// dtype 0 = fp32 (v_mfma_f32_32x32x2_f32), 1 = bf16 (v_mfma_f32_32x32x16_bf16),
+// 2 = fp32 vector FMA (valu_loop: blocks * 256 * iters * 16 FMAs of 2 flops).
 // One launch: `blocks` work-groups of 256 threads, each wave doing `iters`
 // (even) rounds of 16 MFMAs, i.e. blocks * 4 * iters * 16 MFMAs of
 // 2*32*32*2 (fp32) or 2*32*32*16 (bf16) flops.  `out` holds blocks * 256
@@ -140,12 +166,14 @@ void f32_loop(float *out, int iters)
 extern "C" int probe_mfma_loop(int dtype, int blocks, int iters, int zero, float *out,
                                hipStream_t stream)
 {
-    if (blocks <= 0 || iters <= 0 || (iters & 1) || !out || (dtype != 0 && dtype != 1))
+    if (blocks <= 0 || iters <= 0 || (iters & 1) || !out || dtype < 0 || dtype > 2)
         return hipErrorInvalidValue;
     const dim3 g(blocks), b(256);
     if (dtype == 1 && zero) hipLaunchKernelGGL(bf16_loop<true>, g, b, 0, stream, out, iters);
     if (dtype == 1 && !zero) hipLaunchKernelGGL(bf16_loop<false>, g, b, 0, stream, out, iters);
     if (dtype == 0 && zero) hipLaunchKernelGGL(f32_loop<true>, g, b, 0, stream, out, iters);
     if (dtype == 0 && !zero) hipLaunchKernelGGL(f32_loop<false>, g, b, 0, stream, out, iters);
+    if (dtype == 2 && zero) hipLaunchKernelGGL(valu_loop<true>, g, b, 0, stream, out, iters);
+    if (dtype == 2 && !zero) hipLaunchKernelGGL(valu_loop<false>, g, b, 0, stream, out, iters);
     return hipGetLastError();
 }

@@ -8,14 +8,14 @@ across runs.  The toolchain matters because a compiler change can move a
 kernel across an occupancy cliff without failing any test; "Bare Metal
 Bard" (page 1, fourth paragraph) found such a regression only through the
 version recorded with its measurements.  Clock and power come from the
-amdgpu driver's sysfs files (no GPU call), sampled by a background thread.
+amdgpu driver's sysfs files (no GPU call), sampled by a background thread;
+the compiler version comes from the library (no process is started).
 """
 from __future__ import annotations
 
 import glob
 import re
 import statistics
-import subprocess
 import threading
 from typing import Dict, List, Optional
 
@@ -98,21 +98,10 @@ class ClockSampler:
         return {"sclk_mhz": _stats(self.sclk), "power_w": _stats(self.power)}
 
 
-_TOOLCHAIN: Optional[Dict[str, Optional[str]]] = None
-
-
-def toolchain() -> Dict[str, Optional[str]]:
-    """ROCm release and the HIP compiler that builds the kernels."""
-    global _TOOLCHAIN
-    if _TOOLCHAIN is None:
-        rocm = _read("/opt/rocm/.info/version")
-        compiler = None
-        try:
-            out = subprocess.run(["hipcc", "--version"], capture_output=True, text=True,
-                                 timeout=60).stdout
-            compiler = next((l.strip() for l in out.splitlines() if "clang version" in l), None)
-        except (OSError, subprocess.SubprocessError):
-            pass
-        _TOOLCHAIN = {"rocm": rocm.strip() if rocm else None, "compiler": compiler}
-    return _TOOLCHAIN
-
+def toolchain(build_info: Optional[str] = None) -> Dict[str, Optional[str]]:
+    """ROCm release (read from the installation's version file) and the
+    toolchain that compiled the kernels, as the library itself reports it
+    (gemm_build_info).  Starts no process: the caller may already hold the
+    GPU."""
+    rocm = _read("/opt/rocm/.info/version")
+    return {"rocm": rocm.strip() if rocm else None, "compiler": build_info}

@@ -132,7 +132,7 @@ def main():
         a1 = torch.ones((1, 1), device=dev)
         null_ms = time_calls(lambda: g.gemm(a1, a1), args.windows, max_reps=args.max_reps)
         print(json.dumps({"workload": "identity_null_1x1x1", "ms": round(null_ms, 5),
-                          "toolchain": toolchain()}), flush=True)
+                          "toolchain": toolchain(g.gemm_build_info())}), flush=True)
 
     for name in args.workloads.split(","):
         w = workloads.WORKLOADS[name]

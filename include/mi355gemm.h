@@ -113,6 +113,11 @@ int gemm_force_kernel(int id);
  * (-1 before any). */
 int gemm_last_kernel(void);
 
+/* Static description of the toolchain that compiled this library (compiler
+ * version, HIP version, target), for recording beside measurements; never
+ * freed.  Reading it needs no GPU and starts no process. */
+const char *gemm_build_info(void);
+
 #ifdef __cplusplus
 }
 #endif
