@@ -38,6 +38,8 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_direct128x64", kF32, launch_mfma_f32_direct128x64, supports_mfma_f32_direct},
     {"mfma_bf16_direct128", kBF16, launch_mfma_bf16_direct128, supports_mfma_bf16_direct},
     {"mfma_f32_narrow128x64", kF32, launch_mfma_f32_narrow128x64, supports_mfma_f32_narrow},
+    {"mfma_f32_direct64", kF32, launch_mfma_f32_direct64, supports_mfma_f32_direct},
+    {"mfma_f32_narrow64", kF32, launch_mfma_f32_narrow64, supports_mfma_f32_narrow},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -147,21 +149,29 @@ int select_kernel(const Problem &p)
             return kernel_id("mfma_bf16_direct");
         return kernel_id("mfma_bf16_direct128");
     }
+    // Efficiencies (per mille of peak with every CU busy) measured at 4096^3
+    // and 8192^3; 64 x 64 tiles (five per CU) only pay where the larger
+    // tiles would leave CUs idle (a few hundred tiles or fewer).
     if (supports_mfma_f32_direct(p)) {
         const int64_t c256 = tiled_cost(p, 256, 256, 1, 960);
         const int64_t c128 = tiled_cost(p, 128, 128, 2, 946);
         const int64_t c64 = tiled_cost(p, 128, 64, 3, 917);
-        if (c256 <= c128 && c256 <= c64) return kernel_id("mfma_f32_direct");
-        if (c128 <= c64) return kernel_id("mfma_f32_direct128");
-        return kernel_id("mfma_f32_direct128x64");
+        const int64_t c6464 = tiled_cost(p, 64, 64, 5, 880);
+        if (c256 <= c128 && c256 <= c64 && c256 <= c6464) return kernel_id("mfma_f32_direct");
+        if (c128 <= c64 && c128 <= c6464) return kernel_id("mfma_f32_direct128");
+        if (c64 <= c6464) return kernel_id("mfma_f32_direct128x64");
+        return kernel_id("mfma_f32_direct64");
     }
     // Ragged K, unaligned rows: the narrow-load kernels (128 x 128: 0.938,
-    // 128 x 64 with three per CU: 0.874 at 8192^3) beat both register-staged
-    // tiles on every shape.
+    // 128 x 64 with three per CU: 0.874, 64 x 64 with five: 0.873) beat both
+    // register-staged tiles on every shape.
     if (supports_mfma_f32_narrow(p)) {
-        if (tiled_cost(p, 128, 128, 2, 938) <= tiled_cost(p, 128, 64, 3, 874))
-            return kernel_id("mfma_f32_narrow128");
-        return kernel_id("mfma_f32_narrow128x64");
+        const int64_t c128 = tiled_cost(p, 128, 128, 2, 938);
+        const int64_t c64 = tiled_cost(p, 128, 64, 3, 874);
+        const int64_t c6464 = tiled_cost(p, 64, 64, 5, 873);
+        if (c128 <= c64 && c128 <= c6464) return kernel_id("mfma_f32_narrow128");
+        if (c64 <= c6464) return kernel_id("mfma_f32_narrow128x64");
+        return kernel_id("mfma_f32_narrow64");
     }
     if (tiled_cost(p, 256, 256, 1, 700) <= tiled_cost(p, 128, 128, 2, 670))
         return kernel_id("mfma_f32");

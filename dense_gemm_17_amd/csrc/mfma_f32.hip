@@ -333,7 +333,10 @@ struct DTile {
     static constexpr bool kReadEveryOther = 2 * kReads <= kQ;
     // When the loads outnumber the MFMAs of a group (the narrow 128 x 64
     // tile: 12 loads, 8 MFMAs), load l goes after MFMA l * kQ / kPerTile.
-    static constexpr bool kSpreadLoads = kPerTile > kQ;
+    // With one block per wave (64 x 64) the reads outnumber the MFMAs too
+    // (5 reads, 4 MFMAs): reads and loads are then both spread that way.
+    static constexpr bool kSpreadReads = kReads > kQ;
+    static constexpr bool kSpreadLoads = kPerTile > kQ || kSpreadReads;
     static constexpr int kLoadQ0 =
         BM == 256 ? 20 : kSpreadLoads ? 0 : kNB == 1 ? kQ - kPerTile : (kW == 16 ? 1 : 0);
     static constexpr int kLoadStep = kW == 16 && kNB > 1 ? 4 : 1;
@@ -344,7 +347,8 @@ struct DTile {
     // two half-waves read rows 4 apart: 16-byte chunks of B rows are
     // XOR-permuted by 8 * bit 2 of the row so those rows use different banks.
     static constexpr bool kBSwz = kNB == 1;
-    static_assert(kReads <= kQ && (kSpreadLoads || kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ),
+    static_assert((kReads <= kQ || kSpreadLoads) &&
+                      (kSpreadLoads || kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ),
                   "slots");
     static_assert((DSTAGES - 2) * kPerTile <= 63, "vmcnt is six bits");
     static_assert(kNB == 1 || kNB == 2 || kNB == 4, "B read width");
@@ -475,7 +479,13 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
         const bool rd = T::kReadEveryOther ? (q < 2 * T::kReads && (q & 1) == 0) : q < T::kReads;
         if constexpr (T::kSpreadLoads) {
             __builtin_amdgcn_sched_barrier(0);
-            if (rd) read_one(nxt, rstage, x, g_next, q);
+            if constexpr (T::kSpreadReads) {
+#pragma unroll
+                for (int r = 0; r < T::kReads; ++r)
+                    if (r * T::kQ / T::kReads == q) read_one(nxt, rstage, x, g_next, r);
+            } else {
+                if (rd) read_one(nxt, rstage, x, g_next, q);
+            }
             if (loads) {
 #pragma unroll
                 for (int l = 0; l < T::kPerTile; ++l)
@@ -714,5 +724,7 @@ hipError_t launch_mfma_f32_direct128(const Problem &p, hipStream_t s) { return l
 hipError_t launch_mfma_f32_narrow128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, 4>(p, s); }
 hipError_t launch_mfma_f32_direct128x64(const Problem &p, hipStream_t s) { return launch_direct<128, 64, 16>(p, s); }
 hipError_t launch_mfma_f32_narrow128x64(const Problem &p, hipStream_t s) { return launch_direct<128, 64, 4>(p, s); }
+hipError_t launch_mfma_f32_direct64(const Problem &p, hipStream_t s) { return launch_direct<64, 64, 16>(p, s); }
+hipError_t launch_mfma_f32_narrow64(const Problem &p, hipStream_t s) { return launch_direct<64, 64, 4>(p, s); }
 
 }  // namespace mi355gemm

@@ -128,7 +128,7 @@ def test_plan_is_pure():
 # for the layout cases that change it.  Measured alternatives for each row
 # are recorded by dense_gemm_17_amd/sweep.py.
 DISPATCH_GOLDEN = {
-    "f32_256": "mfma_f32_direct128x64",
+    "f32_256": "mfma_f32_direct64",
     "f32_4096": "mfma_f32_direct",
     "f32_8192": "mfma_f32_direct",
     "gpt_qkv": "mfma_f32_direct128x64",
@@ -137,7 +137,7 @@ DISPATCH_GOLDEN = {
     "bf16_8192": "mfma_bf16_direct",
     "skinny_1x8960x1536": "skinny_f32",
     "skinny_7x4096x4096": "skinny_f32",
-    "ragged_1000x3000x777": "mfma_f32_narrow128x64",
+    "ragged_1000x3000x777": "mfma_f32_narrow64",
     "ragged_4097x4095x1023": "mfma_f32_narrow128x64",
     "bf16_gpt_qkv": "mfma_bf16_direct128",
     "bf16_gpt_mlp_down": "mfma_bf16_direct128",
@@ -170,8 +170,12 @@ def test_dispatch_layout_cases():
     assert name(g.F32, 8192, 8192, 8200, A=PA, B=PB, C=PC) == "mfma_f32_narrow128"
     assert name(g.F32, 8192, 8192, 8192, A=PA, B=PB, ldb=8194, C=PC) == "mfma_f32_narrow128"
     assert name(g.F32, 8192, 8192, 8192, A=PA + 4, B=PB, C=PC) == "mfma_f32_narrow128"
-    assert name(g.F32, 4096, 1152, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct128x64"
+    assert name(g.F32, 4096, 1152, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
     assert name(g.F32, 16384, 1536, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct128"
+    # a few hundred tiles or fewer: the 64 x 64 tiles, five per CU
+    assert name(g.F32, 512, 512, 4096, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
+    assert name(g.F32, 1000, 3000, 784, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
+    assert name(g.F32, 1000, 3000, 777, A=PA, B=PB, C=PC) == "mfma_f32_narrow64"
     # ... except leading dimensions beyond its 32-bit lane offsets
     assert name(g.F32, 64, 64, 64, A=PA, lda=1 << 23, B=PB, C=PC) == "mfma_f32_128"
     # few rows -> bandwidth family, both element types, up to 16 rows
