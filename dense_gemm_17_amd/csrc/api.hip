@@ -120,7 +120,6 @@ Verdict validate(const Problem &p)
 //     other fp32 layouts (ragged K, unaligned rows) go to the narrow-load
 //     LDS-direct kernel, and the register-staged kernels only take leading
 //     dimensions too large for its 32-bit lane offsets.
-constexpr int64_t kCUs = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

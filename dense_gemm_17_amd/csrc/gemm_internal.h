@@ -57,6 +57,10 @@ hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s);
 // Largest M the skinny (bandwidth) family takes.
 constexpr int64_t kSkinnyMaxM = 16;
 
+// Compute units of an MI355X (8 XCDs of 32); the dispatch table and the
+// skinny family size their grids against it.
+constexpr int64_t kCUs = 256;
+
 // 1-D grids only: gridDim.x is the sole dimension with a 2^31 - 1 limit.
 constexpr int64_t kMaxBlocks = 2147483647LL;
 

@@ -10,8 +10,9 @@
 //
 //   * a work-group owns a strip of C's columns; its threads form K-groups of
 //     kL lanes, each lane loading 16 bytes of a B row, so a K-group reads kL
-//     x 16 contiguous bytes of every row it visits (256, 128 or 64 bytes:
-//     the widest strip that still gives the chip at least 128 strips);
+//     x 16 contiguous bytes of every row it visits (256 or 128 bytes,
+//     whichever puts fewer bytes of a row through the busiest CU; 64 bytes
+//     only for very narrow B);
 //   * K is dealt to the K-groups in blocks of four rows, round robin (group g
 //     takes blocks g, g + G, g + 2G, ...): at any moment the groups of all
 //     work-groups read one contiguous band of B rows, which measured 1.3-1.4x
@@ -223,15 +224,29 @@ hipError_t launch_lanes(const Problem &p, hipStream_t s, bool vec)
     else return launch_cfg<T, kM, kL, 256, 4, kSplit>(p, s, vec);
 }
 
-// Strip width: the widest of 16, 8, 4 lanes (256, 128, 64 bytes of a B
-// row) that leaves at least 128 strips; wider strips read longer runs of
-// each row but leave CUs idle when strips are few.
+// Strip width in lanes: 16 (256 bytes of a B row) when those strips occupy
+// more than half the CUs, else 8 (128 bytes), else 4 (64 bytes) when even
+// 8-lane strips number fewer than 128.  Wider strips read longer runs of
+// each row; narrower ones put more CUs to work.  Measured: 1 x 8960 x 1536
+// 15.2 us with 140 strips of 256 bytes (17.8 with 280 of 128); 4 x 8192 x
+// 2048 18.1 us with 256 strips of 128 bytes (22.1 with 128 of 256);
+// 1 x 19200 x 1536 28.7 us with 300 of 256 (29.5 with 600 of 128); 1 x 4096
+// x 4096 22.4 us with 128 of 128 (25.3 with 256 of 64).
+template <typename T>
+int lanes_of(const Problem &p)
+{
+    constexpr int P = Elem<T>::kPerLoad;
+    if ((p.N + 16 * P - 1) / (16 * P) > kCUs / 2) return 16;
+    if ((p.N + 8 * P - 1) / (8 * P) >= 128) return 8;
+    return 4;
+}
+
 template <typename T, int kM, int kSplit>
 hipError_t launch_m(const Problem &p, hipStream_t s, bool vec)
 {
-    constexpr int P = Elem<T>::kPerLoad;
-    if ((p.N + 16 * P - 1) / (16 * P) >= 128) return launch_lanes<T, kM, 16, kSplit>(p, s, vec);
-    if ((p.N + 8 * P - 1) / (8 * P) >= 128) return launch_lanes<T, kM, 8, kSplit>(p, s, vec);
+    const int lanes = lanes_of<T>(p);
+    if (lanes == 16) return launch_lanes<T, kM, 16, kSplit>(p, s, vec);
+    if (lanes == 8) return launch_lanes<T, kM, 8, kSplit>(p, s, vec);
     return launch_lanes<T, kM, 4, kSplit>(p, s, vec);
 }
 
@@ -239,12 +254,8 @@ hipError_t launch_m(const Problem &p, hipStream_t s, bool vec)
 template <typename T>
 int64_t strips_of(const Problem &p)
 {
-    constexpr int P = Elem<T>::kPerLoad;
-    for (int lanes : {16, 8}) {
-        const int64_t n = (p.N + lanes * P - 1) / (lanes * P);
-        if (n >= 128) return n;
-    }
-    return (p.N + 4 * P - 1) / (4 * P);
+    const int64_t cols = static_cast<int64_t>(lanes_of<T>(p)) * Elem<T>::kPerLoad;
+    return (p.N + cols - 1) / cols;
 }
 
 // Row counts are rounded up to one of a few compiled sizes; more than 4

@@ -210,7 +210,7 @@ def test_identity_and_permutation_exact(dtype):
 # work-group tier, K not a multiple of the 4-row blocks, for both element
 # types, plus one unaligned layout per case (element-load path).
 SKINNY_M = [1, 2, 3, 5, 8, 9, 16]
-SKINNY_NK = [(1000, 37), (4100, 260), (8200, 61), (16400, 36)]
+SKINNY_NK = [(1000, 37), (4100, 260), (8192, 44), (8200, 61), (16400, 36)]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
