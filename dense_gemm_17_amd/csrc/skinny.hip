@@ -31,6 +31,7 @@
 //     deterministic; no atomics, no workspace;
 //   * ragged N and unaligned B or A fall back to element loads with masks.
 #include "gemm_internal.h"
+#include "tile_map.h"
 
 namespace mi355gemm {
 namespace {
@@ -93,10 +94,32 @@ __device__ __forceinline__ f32x4 load_a4(const T *__restrict__ A, int64_t lda, i
     return v;
 }
 
-// kL lanes per K-group, kU rows (kU / 4 blocks) in flight per thread;
-// kSplit = 2: rows split between two work-groups (ids 16 q + 8 h + x hold
-// strip 8 q + x, rows kM h .. kM h + kM - 1; ids differing by 8 share an XCD).
-template <typename T, int kM, int kL, int kThreads, int kU, bool kVec, int kSplit>
+// Work-group -> columns and rows of C:
+//   kStrips:   work-group s owns columns s kCols .. s kCols + kCols - 1;
+//   kRowSplit: rows split between two work-groups (ids 16 q + 8 h + x hold
+//              strip 8 q + x, rows kM h .. kM h + kM - 1; ids differing by
+//              8 share an XCD);
+//   kBalanced: exactly one work-group per CU, the columns dealt out evenly
+//              in kPerLoad-column units (at most kL of them each), so every
+//              CU streams about the same share of B; consecutive shares go
+//              to one XCD, so a cache line split between two shares is read
+//              from HBM once and hit in that XCD's L2 the second time.
+constexpr int kStrips = 1, kRowSplit = 2, kBalanced = 3;
+
+// First (next = 0) or one-past-last (next = 1) column of this work-group's
+// share under kBalanced: shares are consecutive on one XCD (work-group ids
+// x, x + 8, x + 16, .. run on XCD x).
+template <int P>
+__device__ __forceinline__ int64_t balanced_edge(int64_t N, int next)
+{
+    const int64_t W = gridDim.x, units = (N + P - 1) / P;
+    const int64_t share = (blockIdx.x % kNumXcd) * (W / kNumXcd) + blockIdx.x / kNumXcd + next;
+    const int64_t edge = P * (share * units / W);
+    return edge < N ? edge : N;
+}
+
+// kL lanes per K-group, kU rows (kU / 4 blocks) in flight per thread.
+template <typename T, int kM, int kL, int kThreads, int kU, bool kVec, int kMode>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, int64_t K,
                                                           const T *__restrict__ A, int64_t lda,
                                                           const T *__restrict__ B, int64_t ldb,
@@ -113,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
     const int tid = threadIdx.x;
     const int lane = tid % kL, grp = tid / kL;
     int64_t strip = blockIdx.x;
-    if constexpr (kSplit == 2) {
+    if constexpr (kMode == kRowSplit) {
         const int64_t id = blockIdx.x;
         const int64_t half = (id >> 3) & 1;
         strip = (id >> 4) * 8 + (id & 7);
@@ -122,7 +145,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
         M -= half * kM;
         if (M <= 0 || strip * kCols >= N) return;   // whole work-group
     }
-    const int64_t n0 = strip * kCols;
+    // This work-group's columns [n0, n1).
+    const int64_t n0 = kMode == kBalanced ? balanced_edge<P>(N, 0) : strip * kCols;
+    const int64_t n1 = kMode == kBalanced ? balanced_edge<P>(N, 1) : N;
     const int64_t n = n0 + lane * P;
 
     float acc[kM][P];
@@ -131,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
 #pragma unroll
         for (int e = 0; e < P; ++e) acc[m][e] = 0.f;
 
-    if (n < N) {
+    if (n < n1) {
         const int64_t nblk = (K + 3) / 4;
         for (int64_t b0 = grp; b0 < nblk; b0 += int64_t(kGroups) * kBlocks) {
             typename Elem<T>::Raw b[kU];
@@ -140,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int64_t k = 4 * (b0 + int64_t(kGroups) * v) + r;
-                    b[4 * v + r] = load_b<T, kVec>(B, ldb, k, n, N, k < K);
+                    b[4 * v + r] = load_b<T, kVec>(B, ldb, k, n, n1, k < K);
                 }
 #pragma unroll
             for (int v = 0; v < kBlocks; ++v) {
@@ -184,25 +209,26 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) sum += red[(w * kM + m) * kCols + col];
-        if (m < M && n0 + col < N) C[m * ldc + n0 + col] = sum;
+        if (m < M && n0 + col < n1) C[m * ldc + n0 + col] = sum;
     }
 }
 
-template <typename T, int kM, int kL, int kThreads, int kU, int kSplit>
+template <typename T, int kM, int kL, int kThreads, int kU, int kMode>
 hipError_t launch_cfg(const Problem &p, hipStream_t s, bool vec)
 {
     constexpr int kCols = kL * Elem<T>::kPerLoad;
     const int64_t strips = (p.N + kCols - 1) / kCols;
-    const int64_t blocks = kSplit == 2 ? 16 * ((strips + 7) / 8) : strips;
+    const int64_t blocks = kMode == kRowSplit ? 16 * ((strips + 7) / 8)
+                           : kMode == kBalanced ? kCUs : strips;
     if (blocks > kMaxBlocks) return hipErrorInvalidValue;
     const T *A = static_cast<const T *>(p.A);
     const T *B = static_cast<const T *>(p.B);
     if (vec)
-        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, true, kSplit>),
+        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, true, kMode>),
                            dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p.M, p.N,
                            p.K, A, p.lda, B, p.ldb, p.C, p.ldc);
     else
-        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, false, kSplit>),
+        hipLaunchKernelGGL((skinny_kernel<T, kM, kL, kThreads, kU, false, kMode>),
                            dim3(static_cast<uint32_t>(blocks)), dim3(kThreads), 0, s, p.M, p.N,
                            p.K, A, p.lda, B, p.ldb, p.C, p.ldc);
     return hipGetLastError();
@@ -214,14 +240,14 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s, bool vec)
 // without spilling (1024 threads allow 128 VGPRs, 512 allow 256).
 // (kM is the rows per work-group; measured for split work-groups of 4
 // fp32 rows: 1024 x 4 beats 512 x 8.)
-template <typename T, int kM, int kL, int kSplit>
+template <typename T, int kM, int kL, int kMode>
 hipError_t launch_lanes(const Problem &p, hipStream_t s, bool vec)
 {
     constexpr int kAcc = kM * Elem<T>::kPerLoad;
-    if constexpr (kAcc <= 16 && kSplit == 1) return launch_cfg<T, kM, kL, 512, 8, kSplit>(p, s, vec);
-    else if constexpr (kAcc <= 32) return launch_cfg<T, kM, kL, 1024, 4, kSplit>(p, s, vec);
-    else if constexpr (kAcc <= 64) return launch_cfg<T, kM, kL, 512, 4, kSplit>(p, s, vec);
-    else return launch_cfg<T, kM, kL, 256, 4, kSplit>(p, s, vec);
+    if constexpr (kAcc <= 16 && kMode == kStrips) return launch_cfg<T, kM, kL, 512, 8, kMode>(p, s, vec);
+    else if constexpr (kAcc <= 32) return launch_cfg<T, kM, kL, 1024, 4, kMode>(p, s, vec);
+    else if constexpr (kAcc <= 64) return launch_cfg<T, kM, kL, 512, 4, kMode>(p, s, vec);
+    else return launch_cfg<T, kM, kL, 256, 4, kMode>(p, s, vec);
 }
 
 // Strip width in lanes: 16 (256 bytes of a B row) when those strips occupy
@@ -241,13 +267,13 @@ int lanes_of(const Problem &p)
     return 4;
 }
 
-template <typename T, int kM, int kSplit>
+template <typename T, int kM, int kMode>
 hipError_t launch_m(const Problem &p, hipStream_t s, bool vec)
 {
     const int lanes = lanes_of<T>(p);
-    if (lanes == 16) return launch_lanes<T, kM, 16, kSplit>(p, s, vec);
-    if (lanes == 8) return launch_lanes<T, kM, 8, kSplit>(p, s, vec);
-    return launch_lanes<T, kM, 4, kSplit>(p, s, vec);
+    if (lanes == 16) return launch_lanes<T, kM, 16, kMode>(p, s, vec);
+    if (lanes == 8) return launch_lanes<T, kM, 8, kMode>(p, s, vec);
+    return launch_lanes<T, kM, 4, kMode>(p, s, vec);
 }
 
 // Strips of the width launch_m picks (one per work-group without a split).
@@ -258,21 +284,39 @@ int64_t strips_of(const Problem &p)
     return (p.N + cols - 1) / cols;
 }
 
-// Row counts are rounded up to one of a few compiled sizes; more than 4
-// rows with fewer strips than CUs are split between two work-groups.
+// Row counts are rounded up to one of a few compiled sizes.  With fewer
+// strips than CUs, up to 4 rows take the balanced split (one work-group per
+// CU, 1024 threads with 4 rows in flight each: 1 x 8960 x 1536 in 13.8
+// instead of 15.1 us, 1 x 4096 x 4096 in 20.4 instead of 22.4, 3 x 12288 x
+// 1024 in 13.0 instead of 14.4, with 140, 128 and 192 strips), and more
+// rows are split between two work-groups (for 7 and 8 rows that beats the
+// balanced split, 22.5 vs 36.9 us at 7 x 4096 x 4096: it reads each B line
+// twice, once per half, but keeps half the accumulators per thread).  The
+// balanced split is used for fp32 with at most 3/4 as many strips as CUs
+// (with 224 strips of 2 x 14336 x 4096 the strips already stream at 5.1
+// TB/s and the balanced split is slower, 51.0 vs 46.5 us) and where 8-lane
+// strips number at least 128 (where it was measured).  For bf16 a share
+// holds half as many bytes per lane and it measured slower on every shape
+// but one (1 x 8960 x 1536: 10.9 vs 10.3 us; 4 x 8192 x 2048: 24.1 vs 19.0).
 template <typename T>
 hipError_t launch_skinny(const Problem &p, hipStream_t s)
 {
+    constexpr int P = Elem<T>::kPerLoad;
     if (p.M < 1 || p.M > kMaxM) return hipErrorInvalidValue;
-    const bool vec = (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 &&
-                     p.ldb % Elem<T>::kPerLoad == 0 &&
+    const bool vec = (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && p.ldb % P == 0 &&
                      (reinterpret_cast<uintptr_t>(p.A) & (4 * sizeof(T) - 1)) == 0 && p.lda % 4 == 0;
-    if (p.M <= 1) return launch_m<T, 1, 1>(p, s, vec);
-    if (p.M <= 2) return launch_m<T, 2, 1>(p, s, vec);
-    if (p.M <= 4) return launch_m<T, 4, 1>(p, s, vec);
-    const bool split = strips_of<T>(p) < 256;
-    if (p.M <= 8) return split ? launch_m<T, 4, 2>(p, s, vec) : launch_m<T, 8, 1>(p, s, vec);
-    return split ? launch_m<T, 8, 2>(p, s, vec) : launch_m<T, 16, 1>(p, s, vec);
+    const int64_t strips = strips_of<T>(p);
+    const bool few = strips < kCUs;
+    if (P == 4 && p.M <= 4 && 4 * strips <= 3 * kCUs && (p.N + 8 * P - 1) / (8 * P) >= 128) {
+        if (p.M <= 1) return launch_cfg<T, 1, 16, 1024, 4, kBalanced>(p, s, vec);
+        if (p.M <= 2) return launch_cfg<T, 2, 16, 1024, 4, kBalanced>(p, s, vec);
+        return launch_cfg<T, 4, 16, 1024, 4, kBalanced>(p, s, vec);
+    }
+    if (p.M <= 1) return launch_m<T, 1, kStrips>(p, s, vec);
+    if (p.M <= 2) return launch_m<T, 2, kStrips>(p, s, vec);
+    if (p.M <= 4) return launch_m<T, 4, kStrips>(p, s, vec);
+    if (p.M <= 8) return few ? launch_m<T, 4, kRowSplit>(p, s, vec) : launch_m<T, 8, kStrips>(p, s, vec);
+    return few ? launch_m<T, 8, kRowSplit>(p, s, vec) : launch_m<T, 16, kStrips>(p, s, vec);
 }
 
 }  // namespace
