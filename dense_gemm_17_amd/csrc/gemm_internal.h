@@ -61,6 +61,17 @@ constexpr int64_t kSkinnyMaxM = 16;
 // skinny family size their grids against it.
 constexpr int64_t kCUs = 256;
 
+// Every kernel writes each element of C once and never reads it back, so C
+// goes out with the nontemporal (streaming) hint: the output stream then
+// does not displace operand lines from the L2 and the last-level cache.
+// Measured on bf16 products whose fp32 output dominates: 16384 x 1152 x 384
+// from 38.8 to 29.0 us, 8192 x 8192 x 1024 from 182 to 158 us.
+template <typename V>
+__device__ __forceinline__ void store_c_stream(V *p, V v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
 // 1-D grids only: gridDim.x is the sole dimension with a 2^31 - 1 limit.
 constexpr int64_t kMaxBlocks = 2147483647LL;
 

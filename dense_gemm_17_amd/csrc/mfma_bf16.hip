@@ -187,7 +187,7 @@ __device__ __forceinline__ void store_c(const f32x16 (&acc)[MB][NB], float *__re
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm * 32 * MB + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < M) C[row * ldc + col] = acc[mb][nb][r];
+                if (row < M) store_c_stream(C + row * ldc + col, acc[mb][nb][r]);
             }
         }
 }

@@ -245,11 +245,11 @@ void mfma_f32_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ 
 #pragma unroll
                     for (int nb = 0; nb < T::kNB; ++nb) v[nb] = acc[mb][nb][r];
                 }
-                *reinterpret_cast<BV *>(p) = v;
+                store_c_stream(reinterpret_cast<BV *>(p), v);
             } else {
 #pragma unroll
                 for (int nb = 0; nb < T::kNB; ++nb)
-                    if (col + nb < N) p[nb] = acc[mb][nb][r];
+                    if (col + nb < N) store_c_stream(p + nb, acc[mb][nb][r]);
             }
         }
 }
@@ -667,11 +667,11 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
             if (cvec && col + NB <= N) {
-                *reinterpret_cast<typename DVec<NB>::T *>(p) = v;
+                store_c_stream(reinterpret_cast<typename DVec<NB>::T *>(p), v);
             } else {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    if (col + nb < N) p[nb] = v[nb];
+                    if (col + nb < N) store_c_stream(p + nb, static_cast<float>(v[nb]));
             }
         }
 }

@@ -154,12 +154,11 @@ void valu_f32_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ 
             const f32x4 v = {acc[i][4 * half + 0], acc[i][4 * half + 1], acc[i][4 * half + 2],
                              acc[i][4 * half + 3]};
             if (cvec && col + 3 < N) {
-                *reinterpret_cast<f32x4 *>(p) = v;
+                store_c_stream(reinterpret_cast<f32x4 *>(p), v);
             } else {
-                if (col + 0 < N) p[0] = v.x;
-                if (col + 1 < N) p[1] = v.y;
-                if (col + 2 < N) p[2] = v.z;
-                if (col + 3 < N) p[3] = v.w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (col + e < N) store_c_stream(p + e, static_cast<float>(v[e]));
             }
         }
     }
