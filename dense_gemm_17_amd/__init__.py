@@ -119,6 +119,13 @@ def kernel_names():
 
 # ---- tensor-level call -----------------------------------------------------
 
+def _current_raw_stream(dev: int) -> int:
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if get is not None:
+        return get(dev)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
 def _ld(t: torch.Tensor) -> int:
     rows, cols = t.shape
     if rows > 1 and cols > 0:
@@ -152,16 +159,19 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
           or (N > 1 and out.stride(1) != 1)):
         raise ValueError("out must be a float32 (M, N) tensor with unit column stride on a's GPU")
     fn = lib.gemm_f32 if a.dtype == torch.float32 else lib.gemm_bf16_f32acc
-    if stream is None:
-        stream = torch.cuda.current_stream(a.device)
+    dev = a.get_device()
+    # The raw handle of the current stream, without building a Stream object
+    # (a few microseconds per call, which is the whole kernel time of the
+    # smallest products).
+    raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
     # The library launches on the calling thread's current HIP device.
-    if a.device.index != torch.cuda.current_device():
-        with torch.cuda.device(a.device):
+    if dev != torch.cuda.current_device():
+        with torch.cuda.device(dev):
             rc = fn(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b),
-                    out.data_ptr(), _ld(out), stream.cuda_stream)
+                    out.data_ptr(), _ld(out), raw)
     else:
         rc = fn(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b),
-                out.data_ptr(), _ld(out), stream.cuda_stream)
+                out.data_ptr(), _ld(out), raw)
     if rc != HIP_SUCCESS:
         raise GemmError(rc, "gemm_f32" if a.dtype == torch.float32 else "gemm_bf16_f32acc")
     return out
