@@ -40,6 +40,7 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_narrow128x64", kF32, launch_mfma_f32_narrow128x64, supports_mfma_f32_narrow},
     {"mfma_f32_direct64", kF32, launch_mfma_f32_direct64, supports_mfma_f32_direct},
     {"mfma_f32_narrow64", kF32, launch_mfma_f32_narrow64, supports_mfma_f32_narrow},
+    {"mfma_f32_splitk", kF32, launch_mfma_f32_splitk, supports_any},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -148,6 +149,12 @@ int select_kernel(const Problem &p)
             return kernel_id("mfma_bf16_direct");
         return kernel_id("mfma_bf16_direct128");
     }
+    // At most kCUs / 4 tiles of 64 x 64 (a 512 x 512 output or smaller): the
+    // split-K kernel, whose 32 x 32 tiles share their K range between four
+    // waves, so each wave runs a quarter of the dependent MFMA chain (256^3:
+    // 5.4 vs 7.8 us; 512 x 512 x 4096: 47.7 vs 73.7; 640 x 640 x 2048, 100
+    // tiles: 42.2 vs 39.0, so the larger tiles win from there on).
+    if ((p.M + 63) / 64 * ((p.N + 63) / 64) <= kCUs / 4) return kernel_id("mfma_f32_splitk");
     // Efficiencies (per mille of peak with every CU busy) measured at 4096^3
     // and 8192^3; 64 x 64 tiles (five per CU) only pay where the larger
     // tiles would leave CUs idle (a few hundred tiles or fewer).

@@ -44,6 +44,7 @@ hipError_t launch_mfma_f32_narrow128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_narrow128x64(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_direct64(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_narrow64(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f32_splitk(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_direct128x64(const Problem &p, hipStream_t s);
 bool supports_mfma_f32_narrow(const Problem &p);
 bool supports_mfma_f32_direct(const Problem &p);

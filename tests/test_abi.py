@@ -128,7 +128,7 @@ def test_plan_is_pure():
 # for the layout cases that change it.  Measured alternatives for each row
 # are recorded by dense_gemm_17_amd/sweep.py.
 DISPATCH_GOLDEN = {
-    "f32_256": "mfma_f32_direct64",
+    "f32_256": "mfma_f32_splitk",
     "f32_4096": "mfma_f32_direct",
     "f32_8192": "mfma_f32_direct",
     "gpt_qkv": "mfma_f32_direct128x64",
@@ -172,12 +172,17 @@ def test_dispatch_layout_cases():
     assert name(g.F32, 8192, 8192, 8192, A=PA + 4, B=PB, C=PC) == "mfma_f32_narrow128"
     assert name(g.F32, 4096, 1152, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
     assert name(g.F32, 16384, 1536, 384, A=PA, B=PB, C=PC) == "mfma_f32_direct128"
+    # at most 64 tiles of 64 x 64: the split-K kernel (any layout)
+    assert name(g.F32, 512, 512, 4096, A=PA, B=PB, C=PC) == "mfma_f32_splitk"
+    assert name(g.F32, 100, 300, 777, A=PA, B=PB, C=PC) == "mfma_f32_splitk"
+    assert name(g.F32, 640, 640, 2048, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
     # a few hundred tiles or fewer: the 64 x 64 tiles, five per CU
-    assert name(g.F32, 512, 512, 4096, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
     assert name(g.F32, 1000, 3000, 784, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
     assert name(g.F32, 1000, 3000, 777, A=PA, B=PB, C=PC) == "mfma_f32_narrow64"
     # ... except leading dimensions beyond its 32-bit lane offsets
-    assert name(g.F32, 64, 64, 64, A=PA, lda=1 << 23, B=PB, C=PC) == "mfma_f32_128"
+    assert name(g.F32, 2048, 2048, 64, A=PA, lda=1 << 23, B=PB, C=PC) in ("mfma_f32", "mfma_f32_128")
+    # (the split-K kernel uses 64-bit row offsets and takes any layout)
+    assert name(g.F32, 64, 64, 64, A=PA, lda=1 << 23, B=PB, C=PC) == "mfma_f32_splitk"
     # few rows -> bandwidth family, both element types, up to 16 rows
     assert name(g.BF16, 1, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_bf16"
     assert name(g.F32, 16, 4096, 4096, A=PA, B=PB, C=PC) == "skinny_f32"

@@ -29,6 +29,7 @@ OCCUPANCY_BUDGET = {
     "mfma_f32_direct_kernelILi128ELi128E": 2,
     "mfma_f32_direct_kernelILi128ELi64E": 3,
     "mfma_f32_direct_kernelILi64ELi64E": 5,
+    "mfma_f32_splitk_kernel": 2,
     "valu_f32_kernel": 3,
     "skinny_kernel": 1,
     "naive_kernel": 8,
