@@ -162,3 +162,13 @@ def test_committed_traffic_file_parses():
     for k, v in rec["kernels"].items():
         assert k in bench.KERNEL_SOURCES
         assert v["bytes_per_launch"] == pytest.approx(v["fetch_bytes"] + v["write_bytes"], abs=1)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
