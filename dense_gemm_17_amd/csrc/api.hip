@@ -108,19 +108,23 @@ Verdict validate(const Problem &p)
 //     per byte of B for fp32 (M flop per byte for bf16), far below the ridge
 //     point (~20 flop/B fp32, ~315 flop/B bf16 on MI355X), so the time is
 //     the time to stream B once: the skinny family;
-//   * compute-bound: everything else, on the matrix cores.  The fp32 tile is
+//   * latency-bound (fp32): at most kCUs / 4 tiles of 64 x 64, where each
+//     wave's dependent MFMA chain over K, not the chip's throughput, sets
+//     the time: the split-K family (32 x 32 tiles, K shared by four waves);
+//   * compute-bound: everything else, on the matrix cores.  The tile is
 //     picked by an estimate of the time in work-group waves: a 256 x 256 tile
-//     runs one work-group per CU, a 128 x 128 tile two (each at half the
-//     CU's rate), over 256 CUs, each divided by the kernel's measured
-//     fraction of the matrix-core peak at 8192^3 (LDS-direct 256: 0.96,
-//     LDS-direct 128: 0.946, LDS-direct 128 x 64 with three per CU: 0.917;
-//     register-staged 256: 0.70, register-staged 128: 0.67).  A smaller tile
-//     wins when the larger one leaves CUs idle in its last wave (gpt-sized
-//     and small shapes).  The LDS-direct kernels
-//     are used wherever their layout conditions hold (bf16 and fp32 alike);
-//     other fp32 layouts (ragged K, unaligned rows) go to the narrow-load
-//     LDS-direct kernel, and the register-staged kernels only take leading
-//     dimensions too large for its 32-bit lane offsets.
+//     runs one work-group per CU, a 128 x 128 tile two, 128 x 64 three and
+//     64 x 64 five (each at its share of the CU's rate), over 256 CUs, each
+//     divided by the kernel's measured fraction of the matrix-core peak with
+//     every CU busy (fp32 LDS-direct 256: 0.96, 128: 0.946, 128 x 64: 0.917,
+//     64 x 64: 0.88; narrow-load 128: 0.938, 128 x 64: 0.874, 64 x 64:
+//     0.873; register-staged 256: 0.70, 128: 0.67; bf16 256: 0.512, 128:
+//     0.41).  A smaller tile wins when the larger one leaves CUs idle in its
+//     last wave (GPT-sized and small shapes).  The LDS-direct kernels are
+//     used wherever their layout conditions hold (bf16 and fp32 alike); other
+//     fp32 layouts (ragged K, unaligned rows) go to the narrow-load
+//     LDS-direct kernels, and the register-staged kernels only take leading
+//     dimensions too large for their 32-bit lane offsets.
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

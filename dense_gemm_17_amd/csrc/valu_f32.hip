@@ -17,8 +17,12 @@
 //   * global -> registers (128-bit where aligned), registers -> LDS after the
 //     current step's math, two LDS stages, one barrier per step;
 //   * ragged edges load zeros and are masked at the store.
-// This family is used where the matrix-core tiles would leave most CUs idle
-// or for the smallest products; the MFMA families are faster for large ones.
+// The dispatch table does not pick this family (the matrix-core families are
+// faster on every measured shape); it is kept as the vector-ALU rung of the
+// ladder and as an independent cross-check in the parity tests.  A 128 x 256
+// tile with 8 x 16 per lane (fewer LDS reads per FMA) measured 89.5 instead
+// of 78.8 TFLOP/s at 4096^3 but 85.4 instead of 87.4 at 8192^3 and slower on
+// shapes with fewer tiles, so the 8 x 8 lane tile stays.
 #include "gemm_internal.h"
 #include "tile_map.h"
 
