@@ -25,6 +25,12 @@ Prints exactly one JSON line.  Extra legs:
       clock has settled.  Reported beside the roofline as context: on this
       board the bf16 matrix cores run at the power limit, where the clock
       (and so the reachable throughput) depends on the operand data.
+  other configurations (default on, --no-configs skips it): the table's
+      kernel on every other workload of the set (the small, GPT-shaped,
+      skinny and ragged products), time per call of back-to-back calls (and
+      of a replayed HIP graph for calls under 20 us), the roofline it sits under (HBM below the ridge point, the
+      matrix cores above) and a sampled check against the oracle.  Context
+      beside the step, not part of `value`.
   Every line also records the GPU clock and board power sampled over the
   timed steps and the toolchain.
 """
@@ -83,6 +89,8 @@ def parse():
     p.add_argument("--check-rows", type=int, default=8,
                    help="rows per product checked against the oracle after timing")
     p.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other configurations' section (profiler runs of the step)")
     p.add_argument("--no-ceiling", action="store_true",
                    help="skip the matrix-core ceiling probe (profiler runs)")
     p.add_argument("--ceiling-only", action="store_true",
@@ -199,7 +207,7 @@ def ingest_counters(fetch_dir: str, write_dir: str):
                                   "bytes_per_launch": round(fb + wb), "dispatches": len(f),
                                   "source_digest": source_digest(kernel)}
     with open(TRAFFIC_FILE, "w") as fh:
-        run = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calibration"
+        run = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-ceiling --no-configs --copy-calibration"
         fh.write("# HBM bytes per launch at 8192^3, one rocprofv3 run per counter:\n")
         for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             fh.write(f"#   timeout -s KILL 90 rocprofv3 --pmc {ctr} -d {d} -o pmc "
@@ -336,6 +344,10 @@ def main():
     if args.copy_calibration:
         copy = copy_calibration(dev)
 
+    others = None
+    if not args.no_configs:
+        others = other_configs(dev, set(names), args.check_rows)
+
     ceiling = None
     if not args.no_ceiling:
         ceiling = mfma_ceiling(dev, dtypes=sorted({w.dtype for w in ws}))
@@ -367,6 +379,10 @@ def main():
         # the same type, timed on this board in this run
         "mfma_ceiling": ceiling,
         "cpu_baseline": cpu,
+        # every other configuration of the set, the table's kernel, time per
+        # call (short calls also from a replayed HIP graph), its roofline and
+        # a sampled check against the oracle; context, not `value`
+        "other_configs": others,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels
         "env": dict(clocks.summary(), toolchain=toolchain(g.gemm_build_info())),
@@ -374,6 +390,101 @@ def main():
     if copy is not None:
         line["copy_calibration"] = copy
     print(json.dumps(line), flush=True)
+
+
+LLC_BYTES = 256 * 1024 * 1024   # MI355X last-level (Infinity) cache
+
+
+def other_configs(dev, skip, check_rows):
+    """The table's kernel on every configuration not in the step, timed as
+    back-to-back calls through the binding (median of 5 windows).  Operands
+    too small to outgrow the last-level cache rotate through enough copies
+    that each call reads from HBM.  Calls under 20 us, whose pace the host
+    sets, are also replayed from a HIP graph for the GPU's own time."""
+    import dense_gemm_17_amd as g
+    import oracle
+    from dense_gemm_17_amd.measure import ClockSampler
+    out = {}
+    rng = np.random.default_rng(1)
+    for name, w in workloads.WORKLOADS.items():
+        if name in skip:
+            continue
+        A, B = workloads.make_inputs(w)
+        per_copy = w.algorithmic_bytes
+        copies = 1 if per_copy * 2 > LLC_BYTES else max(2, -(-2 * LLC_BYTES // per_copy))
+        ops = [(A.to(dev), B.to(dev), torch.empty((w.M, w.N), dtype=torch.float32, device=dev))
+               for _ in range(copies)]
+        code = g.F32 if w.dtype == "f32" else g.BF16
+        a0, b0, c0 = ops[0]
+        kernel = g.gemm_kernel_name(g.gemm_plan(code, w.M, w.N, w.K, a0.data_ptr(), a0.stride(0),
+                                                b0.data_ptr(), b0.stride(0), c0.data_ptr(),
+                                                c0.stride(0)))
+        st = torch.cuda.Stream(dev)
+        st.wait_stream(torch.cuda.current_stream(dev))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        state = {"i": 0}
+
+        def call():
+            a, b, c = ops[state["i"] % copies]
+            state["i"] += 1
+            g.gemm(a, b, out=c)
+
+        def windows(run, reps):
+            times = []
+            for _ in range(5):
+                e0.record(st)
+                run()
+                e1.record(st)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1) / reps)
+            return float(np.median(times))
+
+        graph_ms = None
+        with torch.cuda.stream(st):
+            for _ in range(copies):
+                call()
+            e0.record(st)
+            call()
+            e1.record(st)
+            torch.cuda.synchronize()
+            one = max(e0.elapsed_time(e1), 1e-3)
+            reps = copies * max(1, min(2000 // copies, int(20.0 / one / copies) + 1))
+            # back-to-back calls from Python, as an application makes them
+            with ClockSampler() as clocks:
+                ms = windows(lambda: [call() for _ in range(reps)], reps)
+            if ms < 0.02:
+                # short calls: the host call sets their pace, so the same
+                # calls replayed from a HIP graph give the GPU's own time
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=st):
+                    for _ in range(reps):
+                        call()
+                graph.replay()
+                torch.cuda.synchronize()
+                graph_ms = windows(graph.replay, reps)
+                del graph
+        rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, check_rows),
+                                                     replace=False).tolist()))
+        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        Cref, D = fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B), rows=rows,
+                     threads=cpu_threads())
+        err, _, _ = oracle.normalized_error(c0[rows].cpu().numpy(), Cref, D)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        gbs = per_copy / (ms * 1e-3) / 1e9
+        ridge = PEAK_TFLOPS[w.dtype] * 1e3 / HBM_PEAK_GBS     # flop per byte
+        hbm = w.flops / per_copy < ridge
+        out[name] = {
+            "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "kernel": kernel,
+            "us_per_call": round(ms * 1e3, 2), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+            "bound": "hbm" if hbm else "mfma",
+            "frac": round(gbs / HBM_PEAK_GBS if hbm else tflops / PEAK_TFLOPS[w.dtype], 4),
+            "us_per_call_graph": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+            "operand_copies": copies, "max_norm_err_sampled": float(f"{err:.3e}"),
+            "sclk_mhz": (clocks.summary()["sclk_mhz"] or {}).get("median"),
+        }
+        del ops
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(ws, host, seconds):
