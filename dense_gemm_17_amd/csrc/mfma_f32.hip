@@ -415,9 +415,23 @@ struct DCtx {
     uint32_t rdA0, rdA1, rdB;                        // lane parts of the read offsets in a stage
 };
 
+// The scalar-base loads need their base in scalar registers; where the
+// compiler cannot prove a base wave-uniform (after the row epilogue below
+// was added it stopped proving it for these kernels) the two readfirstlanes
+// put it there.  They cost nothing where the base already is scalar (the
+// kernels' code is unchanged by them).
+__device__ __forceinline__ const void *uniform_ptr(const void *p)
+{
+    const uint64_t v = reinterpret_cast<uintptr_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const void *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int kW>
 __device__ __forceinline__ void lds_direct_load(uint32_t voff, const void *sbase, uint32_t m0v)
 {
+    sbase = uniform_ptr(sbase);
     if constexpr (kW == 16) lds_direct_load16(voff, sbase, m0v);
     else lds_direct_load4(voff, sbase, m0v);
 }
@@ -506,7 +520,56 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
     }
 }
 
+// Row epilogue of the 128-row tiles: the accumulators go into the idle LDS
+// ring as rows (16-byte chunks XOR-permuted by bit 2 of the row so the two
+// half-waves' rows 4 apart use different banks), then the work-group writes
+// C as 16-byte streaming stores of whole rows, one pass (the ring holds the
+// tile).  In the library, on the table's choices: GPT QKV (128 x 64) 112.8
+// -> 111.4 us, MLP-up (128 x 128) 145.8 -> 144.2, MLP-down unchanged; the
+// 128 x 128 tile on QKV 125.6 -> 118.6.  The 256 x 256 tile, whose lanes
+// already hold four consecutive columns, keeps its direct 16-byte stores
+// (the staging cost it 1.3%).  Needs C 16-byte aligned with ldc and N
+// multiples of 4.
 template <int BM, int BN, int kW>
+__device__ __forceinline__ void store_c_rows_f32(const f32x16 (&acc)[BM / 64][BN / 64],
+                                                 float *lf, float *__restrict__ C, int64_t ldc,
+                                                 int64_t M, int64_t N, int64_t m0, int64_t n0,
+                                                 int wm, int wn, int lane)
+{
+    using T = DTile<BM, BN, kW>;
+    constexpr int MB = T::kMB, NB = T::kNB, WN = BN / 2;
+    constexpr int kHalf = MB * 32;           // rows per wave
+    constexpr int kChunks = BN / 4;          // 16-byte chunks per row
+    static_assert(BM * BN <= DSTAGES * T::kStageFloats, "the ring holds the tile");
+    static_assert(BM * kChunks % kThreads == 0, "whole chunks per thread");
+    const int h = lane >> 5, c = lane & 31;
+    // every wave's loads landed and reads done: the ring is free
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int col = wn * WN + NB * c + nb;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int lrow = wm * kHalf + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int swz = kChunks >= 16 ? (((lrow >> 2) & 1) << 3) : 0;
+                lf[lrow * BN + (((col >> 2) ^ swz) << 2) + (col & 3)] = acc[mb][nb][r];
+            }
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < BM * kChunks / kThreads; ++i) {
+        const int q = threadIdx.x + kThreads * i;
+        const int lrow = q / kChunks, chunk = q % kChunks;
+        const int swz = kChunks >= 16 ? (((lrow >> 2) & 1) << 3) : 0;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(lf + lrow * BN + ((chunk ^ swz) << 2));
+        const int64_t row = m0 + lrow, col = n0 + 4 * chunk;
+        if (row < M && col < N) store_c_stream(reinterpret_cast<f32x4 *>(C + row * ldc + col), v);
+    }
+}
+
+template <int BM, int BN, int kW, bool kRowsC = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DTile<BM, BN, kW>::kPerCU, DTile<BM, BN, kW>::kPerCU)))
 void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A,
@@ -653,6 +716,10 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
         }
     }
 
+    if constexpr (kRowsC) {
+        store_c_rows_f32<BM, BN, kW>(acc, lds, C, ldc, M, N, m0, n0, wm, wn, lane);
+        return;
+    }
     // Epilogue: register r of block (mb, nb) in lane (h, c) is C row
     // 8*(r/4) + 4*h + r%4 of block mb and column NB*c + nb of the wave's piece.
     const int64_t col = n0 + wn * WN + NB * c;
@@ -711,9 +778,19 @@ hipError_t launch_direct(const Problem &p, hipStream_t s)
     const bool ok = kW == 16 ? supports_mfma_f32_direct(p) : supports_mfma_f32_narrow(p);
     if (tm * tn > kMaxBlocks || !ok) return hipErrorInvalidValue;
     const int cvec = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0;
+    const auto *A = static_cast<const float *>(p.A);
+    const auto *B = static_cast<const float *>(p.B);
+    if constexpr (BM == 128) {
+        if (cvec && p.N % 4 == 0) {
+            hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN, kW, true>),
+                               dim3(static_cast<uint32_t>(tm * tn)), dim3(kThreads), 0, s, p.M,
+                               p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm, tn, cvec);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN, kW>), dim3(static_cast<uint32_t>(tm * tn)),
-                       dim3(kThreads), 0, s, p.M, p.N, p.K, static_cast<const float *>(p.A),
-                       p.lda, static_cast<const float *>(p.B), p.ldb, p.C, p.ldc, tm, tn, cvec);
+                       dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm,
+                       tn, cvec);
     return hipGetLastError();
 }
 
