@@ -32,7 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
           "-pthread", "-shared", "-fPIC", "-Wall", "-Wextra"]
 
-MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP")
+MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP", "IGNORE_TA", "BATCH_B0")
 
 
 def build(out: str = _LIB_PATH, mutant: Optional[str] = None) -> str:
@@ -59,6 +59,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = argt
         fn.restype = ctypes.c_int
+    ci = ctypes.c_int
+    lib.oracle_gemm_batched.argtypes = [ci, ci, ci, _i64, _i64, _i64, _vp, _i64, _i64,
+                                        _vp, _i64, _i64, _i64, _vp, _vp, _i64, ci]
+    lib.oracle_gemm_batched.restype = ci
     lib.oracle_decode_bf16.argtypes = [_vp, _vp, _i64]
     lib.oracle_decode_bf16.restype = None
     return lib
@@ -122,6 +126,63 @@ class Oracle:
         """(C, D) in fp64 for bf16 operands given as raw uint16 patterns."""
         return self._call("oracle_gemm_bf16", np.uint16, A_bits, B_bits, rows, threads)
 
+    @staticmethod
+    def _stored(x: np.ndarray, dtype) -> Tuple[np.ndarray, int, int, int]:
+        """(array, batch, batch stride, row stride) of a 2-D or 3-D operand as
+        stored; a 2-D operand is one matrix reused by every product."""
+        if x.dtype != dtype:
+            raise TypeError(f"expected {np.dtype(dtype)}, got {x.dtype}")
+        if x.ndim == 2:
+            x = x[None]
+            bstride_zero = True
+        elif x.ndim == 3:
+            bstride_zero = False
+        else:
+            raise ValueError("operands must be 2-D or 3-D")
+        if x.size and x.shape[2] > 1 and x.strides[2] != x.itemsize:
+            x = np.ascontiguousarray(x)
+        if x.size and x.shape[1] > 1 and (x.strides[1] < 0 or x.strides[1] % x.itemsize):
+            x = np.ascontiguousarray(x)
+        if x.size and x.shape[0] > 1 and (x.strides[0] < 0 or x.strides[0] % x.itemsize):
+            x = np.ascontiguousarray(x)
+        ld = x.strides[1] // x.itemsize if x.shape[1] > 1 else max(1, x.shape[2])
+        ld = max(ld, x.shape[2], 1)
+        sb = 0 if (bstride_zero or x.shape[0] <= 1) else x.strides[0] // x.itemsize
+        return x, x.shape[0], sb, ld
+
+    def gemm_batched(self, A: np.ndarray, B: np.ndarray, transa: bool = False,
+                     transb: bool = False, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """(C, D) in fp64 for C_b = op(A_b) op(B_b), b over the batch.
+
+        A and B are given as stored: A is M x K (K x M when ``transa``), B is
+        K x N (N x K when ``transb``); float32 or uint16 bf16 patterns.  A
+        3-D operand is a batch (any batch stride, 0 included, e.g. from
+        numpy.broadcast_to); a 2-D one is reused by every product.  The result
+        is (batch, M, N), or (M, N) when both operands are 2-D."""
+        dtype = A.dtype
+        if dtype not in (np.float32, np.uint16) or B.dtype != dtype:
+            raise TypeError(f"operands must both be float32 or both uint16, got {A.dtype}, {B.dtype}")
+        kind = 0 if dtype == np.float32 else 1
+        two_d = A.ndim == 2 and B.ndim == 2
+        A3, ba, sa, lda = self._stored(A, dtype)
+        B3, bb, sb, ldb = self._stored(B, dtype)
+        if A.ndim == 3 and B.ndim == 3 and ba != bb:
+            raise ValueError(f"batch sizes differ: {ba} and {bb}")
+        batch = ba if A.ndim == 3 else bb
+        M, K = (A3.shape[2], A3.shape[1]) if transa else (A3.shape[1], A3.shape[2])
+        K2, N = (B3.shape[2], B3.shape[1]) if transb else (B3.shape[1], B3.shape[2])
+        if K != K2:
+            raise ValueError(f"inner dimensions differ: {K} and {K2}")
+        C = np.zeros((batch, M, N), dtype=np.float64)
+        D = np.zeros((batch, M, N), dtype=np.float64)
+        ptr = lambda a: a.ctypes.data if a.size else None  # noqa: E731
+        rc = self.lib.oracle_gemm_batched(kind, int(transa), int(transb), M, N, K,
+                                          ptr(A3), lda, sa, ptr(B3), ldb, sb, batch,
+                                          ptr(C), ptr(D), max(N, 1), threads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_batched failed with code {rc}")
+        return (C[0], D[0]) if two_d else (C, D)
+
     def decode_bf16(self, bits: np.ndarray) -> np.ndarray:
         bits = np.ascontiguousarray(bits, dtype=np.uint16).reshape(-1)
         out = np.empty(bits.shape, dtype=np.float64)
@@ -146,6 +207,10 @@ def gemm_f32(A, B, rows=None, threads=0):
 
 def gemm_bf16(A_bits, B_bits, rows=None, threads=0):
     return load().gemm_bf16(A_bits, B_bits, rows, threads)
+
+
+def gemm_batched(A, B, transa=False, transb=False, threads=0):
+    return load().gemm_batched(A, B, transa, transb, threads)
 
 
 def normalized_error(c: np.ndarray, c_ref: np.ndarray, d: np.ndarray):

@@ -41,6 +41,8 @@
  *   ORACLE_MUTANT_TRANSPOSE_B  - B is read as B[j][k] instead of B[k][j]
  *   ORACLE_MUTANT_SIGNED_D     - D sums signed products instead of |products|
  *   ORACLE_MUTANT_BF16_SWAP    - bf16 decode takes the pattern byte-swapped
+ *   ORACLE_MUTANT_IGNORE_TA    - a transposed A is read as if it were not
+ *   ORACLE_MUTANT_BATCH_B0     - every product of a batch reads the first B
  */
 
 static double decode_bf16(uint16_t bits)
@@ -65,13 +67,21 @@ typedef struct {
     const int64_t *rows;   /* NULL: output row r is input row r */
     int64_t nrows;
     int64_t r0, r1;        /* this worker's block of output rows */
+    int ta, tb;            /* operand stored transposed: A as K x M, B as N x K */
 } job_t;
 
+/* Element (i, k) of the M x K left factor.  Stored as written (row i at
+ * A + i*lda) or transposed (stored K x M: element (i, k) at A[k*lda + i]). */
 static double load_a(const job_t *j, int64_t i, int64_t k)
 {
+    int64_t at = j->ta ? k * j->lda + i : i * j->lda + k;
+#ifdef ORACLE_MUTANT_IGNORE_TA
+    /* row-major indexing of transposed storage, wrapped to stay inside it */
+    if (j->ta) at = (i * j->lda + k) % ((j->K - 1) * j->lda + j->M);
+#endif
     if (j->kind == KIND_F32)
-        return (double)((const float *)j->A)[i * j->lda + k];
-    return decode_bf16(((const uint16_t *)j->A)[i * j->lda + k]);
+        return (double)((const float *)j->A)[at];
+    return decode_bf16(((const uint16_t *)j->A)[at]);
 }
 
 static double load_b(const job_t *j, int64_t k, int64_t n)
@@ -79,9 +89,12 @@ static double load_b(const job_t *j, int64_t k, int64_t n)
 #ifdef ORACLE_MUTANT_TRANSPOSE_B
     int64_t t = k; k = n % j->K; n = t % j->N;
 #endif
+    /* Element (k, n) of the K x N right factor; stored as written (row k at
+     * B + k*ldb) or transposed (stored N x K: element (k, n) at B[n*ldb + k]). */
+    int64_t at = j->tb ? n * j->ldb + k : k * j->ldb + n;
     if (j->kind == KIND_F32)
-        return (double)((const float *)j->B)[k * j->ldb + n];
-    return decode_bf16(((const uint16_t *)j->B)[k * j->ldb + n]);
+        return (double)((const float *)j->B)[at];
+    return decode_bf16(((const uint16_t *)j->B)[at]);
 }
 
 /* One output row: acc and den start at zero, then for each k the row of B is
@@ -128,7 +141,8 @@ static int run(job_t base, int nthreads)
     if (base.M < 0 || base.N < 0 || base.K < 0 || base.nrows < 0) return 1;
     if (base.nrows == 0 || base.N == 0) return 0;
     if (base.ldo < base.N) return 1;
-    if (base.K > 0 && (base.lda < base.K || base.ldb < base.N)) return 1;
+    if (base.K > 0 && (base.lda < (base.ta ? base.M : base.K) ||
+                       base.ldb < (base.tb ? base.K : base.N))) return 1;
     if (base.rows)
         for (int64_t r = 0; r < base.nrows; ++r)
             if (base.rows[r] < 0 || base.rows[r] >= base.M) return 1;
@@ -165,7 +179,7 @@ int oracle_gemm_f32(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda, const float *B, int64_t ldb,
                     double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -173,7 +187,7 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                      double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -184,7 +198,7 @@ int oracle_gemm_f32_rows(int64_t M, int64_t N, int64_t K,
                          const int64_t *rows, int64_t nrows,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -193,8 +207,43 @@ int oracle_gemm_bf16_rows(int64_t M, int64_t N, int64_t K,
                           const int64_t *rows, int64_t nrows,
                           double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0};
     return run(j, nthreads);
+}
+
+/* A strided batch of products with either factor optionally stored
+ * transposed: for b < batch,
+ *     C_b[i][j] = sum_k op(A)_b[i][k] * op(B)_b[k][j]
+ * where op(A)_b is the M x K matrix at A + b*sa (stored M x K with row
+ * stride lda, or K x M when ta != 0) and op(B)_b the K x N matrix at
+ * B + b*sb (stored K x N, or N x K when tb != 0).  These are the layouts a
+ * training step's backward pass multiplies ("Bare Metal Bard", page 1,
+ * second paragraph: the GPT trained on the same kernels, whose gradients
+ * are products with one factor transposed).  A stride of 0 reuses one
+ * matrix for every product.  C and D are batch consecutive M x ldo fp64
+ * matrices.  kind is 0 for fp32 operands, 1 for bf16 patterns.  Same
+ * return codes as above. */
+int oracle_gemm_batched(int kind, int ta, int tb, int64_t M, int64_t N, int64_t K,
+                        const void *A, int64_t lda, int64_t sa,
+                        const void *B, int64_t ldb, int64_t sb, int64_t batch,
+                        double *C, double *D, int64_t ldo, int nthreads)
+{
+    if (kind != KIND_F32 && kind != KIND_BF16) return 1;
+    if (batch < 0 || sa < 0 || sb < 0 || M < 0 || N < 0) return 1;
+    const int64_t es = kind == KIND_F32 ? 4 : 2;
+    for (int64_t b = 0; b < batch; ++b) {
+        int64_t bb = b;
+#ifdef ORACLE_MUTANT_BATCH_B0
+        bb = 0;
+#endif
+        job_t j = {kind, M, N, K,
+                   (const char *)A + b * sa * es, lda,
+                   (const char *)B + bb * sb * es, ldb,
+                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0};
+        int rc = run(j, nthreads);
+        if (rc != 0) return rc;
+    }
+    return 0;
 }
 
 /* bf16 pattern -> fp64, exposed so tests can pin the decoder on its own. */

@@ -160,8 +160,82 @@ def pin_brute_force(o, shapes):
                 assert abs(Fraction(D[i, j]) - mag) <= Fraction(bound) + Fraction(1, 2**1074)
 
 
+TRANS = [(False, False), (True, False), (False, True), (True, True)]
+
+
+def stored(x, trans):
+    """The storage of a logical matrix x: itself, or its transpose written out."""
+    return np.ascontiguousarray(x.T) if trans else np.ascontiguousarray(x)
+
+
+def pin_transposed_small_int(o):
+    # Transposed storage of either factor: the product of the logical
+    # matrices, exactly (integer entries, every partial sum below 2^24),
+    # against numpy's int64 product.
+    g = workloads.generator(13)
+    for ta, tb in TRANS:
+        for (M, N, K) in [(33, 65, 129), (7, 30, 100), (40, 9, 17)]:
+            A = workloads.small_int((M, K), -4, 4, g).numpy()
+            B = workloads.small_int((K, N), -4, 4, g).numpy()
+            C, D = o.gemm_batched(stored(A, ta), stored(B, tb), ta, tb)
+            Ai, Bi = A.astype(np.int64), B.astype(np.int64)
+            assert np.array_equal(C, (Ai @ Bi).astype(np.float64))
+            assert np.array_equal(D, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+        At = workloads.small_int((19, 48), -8, 8, g, torch.bfloat16)
+        Bt = workloads.small_int((48, 23), -8, 8, g, torch.bfloat16)
+        Ab, Bb = workloads.bf16_bits(At), workloads.bf16_bits(Bt)
+        C, D = o.gemm_batched(stored(Ab, ta), stored(Bb, tb), ta, tb)
+        Ai, Bi = At.to(torch.int64).numpy(), Bt.to(torch.int64).numpy()
+        assert np.array_equal(C, (Ai @ Bi).astype(np.float64))
+        assert np.array_equal(D, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+
+
+def pin_transposed_permutation(o):
+    # A transposed permutation factor permutes rows (or columns) of the other
+    # factor exactly; reading the storage the wrong way round applies the
+    # inverse permutation instead.
+    r = rng(14)
+    perm = r.permutation(29)
+    P = np.zeros((29, 29), dtype=np.float32)
+    P[np.arange(29), perm] = 1.0            # (P B)[i] = B[perm[i]]
+    B = rand_f32((29, 41), 15)
+    C, _ = o.gemm_batched(stored(P, True), B, True, False)
+    assert np.array_equal(C, B[perm].astype(np.float64))
+    A = rand_f32((17, 29), 16)
+    Q = np.zeros((29, 29), dtype=np.float32)
+    Q[perm, np.arange(29)] = 1.0            # (A Q)[:, j] = A[:, perm[j]]
+    C, _ = o.gemm_batched(A, stored(Q, True), False, True)
+    assert np.array_equal(C, A[:, perm].astype(np.float64))
+
+
+def pin_batched(o):
+    # Each product of a strided batch is the product of its own pair, exactly;
+    # a 2-D or stride-0 operand is reused by every product; the batch stride
+    # may skip matrices of a larger array.
+    g = workloads.generator(17)
+    nb, M, N, K = 4, 11, 13, 37
+    A = workloads.small_int((2 * nb, M, K), -4, 4, g).numpy()[::2]   # batch stride 2*M*K
+    B = workloads.small_int((nb, K, N), -4, 4, g).numpy()
+    for ta, tb in TRANS:
+        As = np.stack([stored(a, ta) for a in A])[:, :, :]
+        Bs = np.stack([stored(b, tb) for b in B])
+        C, D = o.gemm_batched(As, Bs, ta, tb)
+        assert C.shape == (nb, M, N)
+        for b in range(nb):
+            Ai, Bi = A[b].astype(np.int64), B[b].astype(np.int64)
+            assert np.array_equal(C[b], (Ai @ Bi).astype(np.float64))
+            assert np.array_equal(D[b], (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+    C, _ = o.gemm_batched(A, B[1])                                   # shared B
+    Cz, _ = o.gemm_batched(np.broadcast_to(A[2], (3, M, K)), B[:3])  # batch stride 0
+    for b in range(nb):
+        assert np.array_equal(C[b], (A[b].astype(np.int64) @ B[1].astype(np.int64)).astype(np.float64))
+    for b in range(3):
+        assert np.array_equal(Cz[b], (A[2].astype(np.int64) @ B[b].astype(np.int64)).astype(np.float64))
+
+
 PINS = [pin_golden, pin_identity, pin_permutation, pin_ones, pin_small_int_f32,
         pin_small_int_bf16, pin_bf16_matches_decoded_f32, pin_numpy_blas,
+        pin_transposed_small_int, pin_transposed_permutation, pin_batched,
         lambda o: pin_brute_force(o, [(2, 3, 4), (3, 1, 5), (4, 4, 2)])]
 
 
@@ -186,6 +260,33 @@ def test_brute_force_all_tiny_shapes(orc):
 
 def test_brute_force_edge_shapes(orc):
     pin_brute_force(orc, [(13, 17, 31), (33, 5, 65), (1, 65, 33), (17, 13, 1)])
+
+
+@pytest.mark.parametrize("ta,tb", TRANS)
+def test_brute_force_transposed(orc, ta, tb):
+    # exact rational arithmetic on the logical matrices, every tiny shape up to 5
+    for (M, N, K) in [(m, n, k) for m in range(1, 6) for n in range(1, 6) for k in range(1, 6)]:
+        seed = 7000 + 100 * M + 10 * N + K
+        A, B = rand_f32((M, K), seed), rand_f32((K, N), seed + 1)
+        C, D = orc.gemm_batched(stored(A, ta), stored(B, tb), ta, tb)
+        for i in range(M):
+            for j in range(N):
+                terms = [Fraction(float(A[i, k])) * Fraction(float(B[k, j])) for k in range(K)]
+                exact, mag = sum(terms, Fraction(0)), sum((abs(t) for t in terms), Fraction(0))
+                bound = Fraction(K * ULP53 * float(mag)) + Fraction(1, 2**1074)
+                assert abs(Fraction(C[i, j]) - exact) <= bound
+                assert abs(Fraction(D[i, j]) - mag) <= bound
+
+
+def test_batched_degenerate_and_invalid(orc):
+    C, D = orc.gemm_batched(np.zeros((0, 3, 4), np.float32), np.zeros((0, 4, 5), np.float32))
+    assert C.shape == (0, 3, 5)
+    C, D = orc.gemm_batched(np.zeros((2, 3, 0), np.float32), np.zeros((2, 0, 5), np.float32))
+    assert C.shape == (2, 3, 5) and np.all(C == 0) and np.all(D == 0)
+    with pytest.raises(ValueError):
+        orc.gemm_batched(np.zeros((2, 3, 4), np.float32), np.zeros((3, 4, 5), np.float32))
+    with pytest.raises(ValueError):
+        orc.gemm_batched(np.zeros((3, 4), np.float32), np.zeros((3, 5), np.float32), True, True)
 
 
 def test_thread_count_invariance(orc):
