@@ -37,6 +37,14 @@ def _load() -> ctypes.CDLL:
     for name in ("gemm_f32", "gemm_bf16_f32acc"):
         getattr(lib, name).argtypes = sig
         getattr(lib, name).restype = ci
+    bsig = [ci, ci, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, vp]
+    for name in ("gemm_f32_batched", "gemm_bf16_f32acc_batched"):
+        getattr(lib, name).argtypes = bsig
+        getattr(lib, name).restype = ci
+    sz = ctypes.c_size_t
+    lib.gemm_plan_batched.argtypes = [ci, ci, ci, i64, i64, i64, sz, i64, i64, sz, i64, i64,
+                                      sz, i64, i64, i64]
+    lib.gemm_plan_batched.restype = ci
     lib.gemm_kernel_count.argtypes = []
     lib.gemm_kernel_count.restype = ci
     lib.gemm_kernel_name.argtypes = [ci]
@@ -58,9 +66,9 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 # Every symbol include/mi355gemm.h declares.
-EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_kernel_count", "gemm_kernel_name",
-           "gemm_kernel_dtype", "gemm_plan", "gemm_force_kernel", "gemm_last_kernel",
-           "gemm_build_info")
+EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_batched", "gemm_bf16_f32acc_batched",
+           "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
+           "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info")
 
 
 # ---- raw entry points (pointers and sizes, same names as the C-ABI) --------
@@ -71,6 +79,18 @@ def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 
 def gemm_bf16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
     return lib.gemm_bf16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc,
+                     stride_c, batch, stream) -> int:
+    return lib.gemm_f32_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, stride_b,
+                                C, ldc, stride_c, batch, stream)
+
+
+def gemm_bf16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, stride_b, C,
+                             ldc, stride_c, batch, stream) -> int:
+    return lib.gemm_bf16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb,
+                                        stride_b, C, ldc, stride_c, batch, stream)
 
 
 def gemm_kernel_count() -> int:
@@ -92,6 +112,21 @@ def gemm_plan(dtype, M, N, K, A=1 << 40, lda=None, B=2 << 40, ldb=None, C=3 << 4
     ldb = N if ldb is None else ldb
     ldc = N if ldc is None else ldc
     return lib.gemm_plan(dtype, M, N, K, A, lda, B, ldb, C, ldc)
+
+
+def gemm_plan_batched(dtype, transa, transb, M, N, K, batch, A=1 << 40, lda=None, stride_a=None,
+                      B=2 << 40, ldb=None, stride_b=None, C=3 << 40, ldc=None,
+                      stride_c=None) -> int:
+    """gemm_plan for a batch of products with optionally transposed factors;
+    unset leading dimensions and strides are those of packed storage."""
+    lda = (M if transa else K) if lda is None else lda
+    ldb = (K if transb else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    stride_a = M * K if stride_a is None else stride_a
+    stride_b = K * N if stride_b is None else stride_b
+    stride_c = M * N if stride_c is None else stride_c
+    return lib.gemm_plan_batched(dtype, int(transa), int(transb), M, N, K, A, lda, stride_a,
+                                 B, ldb, stride_b, C, ldc, stride_c, batch)
 
 
 def gemm_force_kernel(kid: int) -> int:
@@ -133,45 +168,84 @@ def _ld(t: torch.Tensor) -> int:
     return max(cols, 1)
 
 
+def _layout(t: torch.Tensor, name: str):
+    """(transposed, leading dimension) of the last two dims of an operand: a
+    unit stride along the columns is the stored layout, a unit stride along
+    the rows is a transposed view (e.g. ``x.t()``)."""
+    rows, cols = t.shape[-2], t.shape[-1]
+    rs, cs = t.stride(-2), t.stride(-1)
+    if rows == 0 or cols == 0:
+        return False, max(cols, 1)
+    if cols <= 1 or cs == 1:
+        ld = rs if rows > 1 else max(cols, 1)
+        if ld >= max(cols, 1):
+            return False, ld
+    if rows <= 1 or rs == 1:
+        ld = cs if cols > 1 else max(rows, 1)
+        if ld >= max(rows, 1):
+            return True, ld
+    raise ValueError(f"{name} needs a unit stride along its rows or its columns "
+                     f"(got strides {tuple(t.stride())} for shape {tuple(t.shape)})")
+
+
+def _batch_stride(t: torch.Tensor) -> int:
+    return t.stride(0) if t.dim() == 3 and t.shape[0] > 1 else 0
+
+
 def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """out = a @ b for 2-D device tensors (fp32·fp32 or bf16·bf16 -> fp32).
+    """out = a @ b on the GPU (fp32·fp32 or bf16·bf16 -> fp32).
 
-    Rows may be padded (any row stride), columns must be unit-stride.  The
-    call is asynchronous on `stream` (default: the current stream of a's
-    device)."""
-    if a.dim() != 2 or b.dim() != 2:
-        raise ValueError("gemm takes 2-D tensors")
+    a is (M, K) or (batch, M, K), b is (K, N) or (batch, K, N); a 2-D operand
+    is shared by every product of a batch, and a 3-D one may have any batch
+    stride (0 included, as from ``expand``).  Each matrix needs a unit stride
+    along its rows or its columns: rows may be padded, and a transposed view
+    such as ``w.t()`` is read in place as a transposed factor.  The result is
+    (M, N) for two 2-D operands, else (batch, M, N).  The call is asynchronous
+    on `stream` (default: the current stream of a's device)."""
+    if a.dim() not in (2, 3) or b.dim() not in (2, 3):
+        raise ValueError("gemm takes 2-D or 3-D tensors")
     if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError(f"operands must both be float32 or both bfloat16, got {a.dtype}, {b.dtype}")
     if a.device.type != "cuda" or b.device != a.device:
         raise ValueError("operands must be on the same GPU")
-    M, K = a.shape
-    K2, N = b.shape
+    M, K = a.shape[-2], a.shape[-1]
+    K2, N = b.shape[-2], b.shape[-1]
     if K != K2:
         raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
-    for name, t in (("a", a), ("b", b)):
-        if t.shape[1] > 1 and t.stride(1) != 1:
-            raise ValueError(f"{name} must have unit column stride")
+    if a.dim() == 3 and b.dim() == 3 and a.shape[0] != b.shape[0]:
+        raise ValueError(f"batch sizes differ: {a.shape[0]} and {b.shape[0]}")
+    batched = a.dim() == 3 or b.dim() == 3
+    batch = a.shape[0] if a.dim() == 3 else (b.shape[0] if b.dim() == 3 else 1)
+    ta, lda = _layout(a, "a")
+    tb, ldb = _layout(b, "b")
+    shape = (batch, M, N) if batched else (M, N)
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
-    elif (out.dtype != torch.float32 or out.shape != (M, N) or out.device != a.device
-          or (N > 1 and out.stride(1) != 1)):
-        raise ValueError("out must be a float32 (M, N) tensor with unit column stride on a's GPU")
-    fn = lib.gemm_f32 if a.dtype == torch.float32 else lib.gemm_bf16_f32acc
+        out = torch.empty(shape, dtype=torch.float32, device=a.device)
+    elif (out.dtype != torch.float32 or tuple(out.shape) != shape or out.device != a.device
+          or (N > 1 and out.stride(-1) != 1)):
+        raise ValueError(f"out must be a float32 {shape} tensor with unit column stride on a's GPU")
+    ldc = out.stride(-2) if M > 1 else max(N, 1)
+    f32 = a.dtype == torch.float32
     dev = a.get_device()
     # The raw handle of the current stream, without building a Stream object
     # (a few microseconds per call, which is the whole kernel time of the
     # smallest products).
     raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
+    if not batched and not ta and not tb:
+        fn, what = (lib.gemm_f32, "gemm_f32") if f32 else (lib.gemm_bf16_f32acc, "gemm_bf16_f32acc")
+        args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, raw)
+    else:
+        fn, what = ((lib.gemm_f32_batched, "gemm_f32_batched") if f32 else
+                    (lib.gemm_bf16_f32acc_batched, "gemm_bf16_f32acc_batched"))
+        args = (int(ta), int(tb), M, N, K, a.data_ptr(), lda, _batch_stride(a), b.data_ptr(),
+                ldb, _batch_stride(b), out.data_ptr(), ldc, _batch_stride(out), batch, raw)
     # The library launches on the calling thread's current HIP device.
     if dev != torch.cuda.current_device():
         with torch.cuda.device(dev):
-            rc = fn(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b),
-                    out.data_ptr(), _ld(out), raw)
+            rc = fn(*args)
     else:
-        rc = fn(M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b),
-                out.data_ptr(), _ld(out), raw)
+        rc = fn(*args)
     if rc != HIP_SUCCESS:
-        raise GemmError(rc, "gemm_f32" if a.dtype == torch.float32 else "gemm_bf16_f32acc")
+        raise GemmError(rc, what)
     return out

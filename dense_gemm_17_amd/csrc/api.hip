@@ -41,6 +41,10 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_direct64", kF32, launch_mfma_f32_direct64, supports_mfma_f32_direct},
     {"mfma_f32_narrow64", kF32, launch_mfma_f32_narrow64, supports_mfma_f32_narrow},
     {"mfma_f32_splitk", kF32, launch_mfma_f32_splitk, supports_any},
+    {"mfma_f32_batched", kF32, launch_mfma_f32_batched, supports_any, true},
+    {"mfma_f32_batched128", kF32, launch_mfma_f32_batched128, supports_any, true},
+    {"mfma_bf16_batched", kBF16, launch_mfma_bf16_batched, supports_any, true},
+    {"mfma_bf16_batched128", kBF16, launch_mfma_bf16_batched128, supports_any, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -79,24 +83,52 @@ bool overlaps(uintptr_t a, int64_t na, uintptr_t b, int64_t nb)
 
 enum Verdict { kInvalid = -1, kNothing = -2, kZeroFill = -3, kCompute = 0 };
 
+// Byte extent of `batch` matrices `stride` elements apart, each of `one`
+// bytes, or -1 if it does not fit in an int64.
+int64_t batch_extent(int64_t one, int64_t batch, int64_t stride, int64_t elem)
+{
+    if (one <= 0) return one;
+    const __int128 bytes = static_cast<__int128>(batch - 1) * stride * elem + one;
+    if (bytes > static_cast<__int128>(INT64_MAX)) return -1;
+    return static_cast<int64_t>(bytes);
+}
+
+// The products of a batch write disjoint parts of C: either each product's
+// rows come after the previous product's (stride_c >= (M-1)*ldc + N), or the
+// products sit side by side within each row (stride_c >= N and the last
+// product ends within the row: (batch-1)*stride_c + N <= ldc).
+bool outputs_disjoint(const Problem &p)
+{
+    if (p.batch <= 1) return true;
+    const __int128 sc = p.sc, ldc = p.ldc;
+    if (sc >= static_cast<__int128>(p.M - 1) * ldc + p.N) return true;
+    return sc >= p.N && static_cast<__int128>(p.batch - 1) * sc + p.N <= ldc;
+}
+
 Verdict validate(const Problem &p)
 {
-    if (p.M < 0 || p.N < 0 || p.K < 0) return kInvalid;
-    if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim) return kInvalid;
-    if (p.M == 0 || p.N == 0) return kNothing;
+    if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0) return kInvalid;
+    if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim || p.batch > kMaxDim) return kInvalid;
+    if ((p.ta != 0 && p.ta != 1) || (p.tb != 0 && p.tb != 1)) return kInvalid;
+    if (p.sa < 0 || p.sb < 0 || p.sc < 0) return kInvalid;
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return kNothing;
     const int64_t es = p.dtype == kF32 ? 4 : 2;
     const uintptr_t c = reinterpret_cast<uintptr_t>(p.C);
     if (!p.C || p.ldc < p.N || (c % 4) != 0) return kInvalid;
-    const int64_t cbytes = extent_bytes(p.M, p.N, p.ldc, 4);
+    if (!outputs_disjoint(p)) return kInvalid;
+    const int64_t cbytes = batch_extent(extent_bytes(p.M, p.N, p.ldc, 4), p.batch, p.sc, 4);
     if (cbytes < 0) return kInvalid;
     if (p.K == 0) return kZeroFill;
     const uintptr_t a = reinterpret_cast<uintptr_t>(p.A);
     const uintptr_t b = reinterpret_cast<uintptr_t>(p.B);
     if (!p.A || !p.B) return kInvalid;
-    if (p.lda < p.K || p.ldb < p.N) return kInvalid;
+    // Stored shapes: A is M x K (K x M when ta), B is K x N (N x K when tb).
+    const int64_t a_rows = p.ta ? p.K : p.M, a_cols = p.ta ? p.M : p.K;
+    const int64_t b_rows = p.tb ? p.N : p.K, b_cols = p.tb ? p.K : p.N;
+    if (p.lda < a_cols || p.ldb < b_cols) return kInvalid;
     if ((a % es) != 0 || (b % es) != 0) return kInvalid;
-    const int64_t abytes = extent_bytes(p.M, p.K, p.lda, es);
-    const int64_t bbytes = extent_bytes(p.K, p.N, p.ldb, es);
+    const int64_t abytes = batch_extent(extent_bytes(a_rows, a_cols, p.lda, es), p.batch, p.sa, es);
+    const int64_t bbytes = batch_extent(extent_bytes(b_rows, b_cols, p.ldb, es), p.batch, p.sb, es);
     if (abytes < 0 || bbytes < 0) return kInvalid;
     if (overlaps(c, cbytes, a, abytes) || overlaps(c, cbytes, b, bbytes)) return kInvalid;
     return kCompute;
@@ -128,6 +160,11 @@ Verdict validate(const Problem &p)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Fractions of peak (per mille, every CU busy) of the general family at
+// large sizes, used by select_general.
+constexpr int64_t F32_GENERAL_256 = 700, F32_GENERAL_128 = 670;
+constexpr int64_t BF16_GENERAL_256 = 340, BF16_GENERAL_128 = 300;
+
 // Relative time of a tiled launch: waves x per-work-group work / efficiency,
 // in units of one CU doing a 128 x 128 tile alone at full rate.
 // bm x bn tiles, per_cu work-groups resident per CU, eff_permille: the
@@ -135,13 +172,28 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // 128 x 128 tile alone at full rate.
 int64_t tiled_cost(const Problem &p, int64_t bm, int64_t bn, int64_t per_cu, int64_t eff_permille)
 {
-    const int64_t tiles = ceil_div(p.M, bm) * ceil_div(p.N, bn);
+    const int64_t tiles = ceil_div(p.M, bm) * ceil_div(p.N, bn) * p.batch;
     const int64_t waves = ceil_div(tiles, kCUs * per_cu);
     return waves * bm * bn * per_cu * 1000000 / (128 * 128) / eff_permille;
 }
 
+// Transposed factors and batches of products: the general (register-staged,
+// any layout) family, 256 x 256 or 128 x 128 tiles by the same wave-count
+// estimate as above, over the tiles of every product.
+int select_general(const Problem &p)
+{
+    if (p.dtype == kBF16)
+        return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
+                   ? kernel_id("mfma_bf16_batched")
+                   : kernel_id("mfma_bf16_batched128");
+    return tiled_cost(p, 256, 256, 1, F32_GENERAL_256) <= tiled_cost(p, 128, 128, 2, F32_GENERAL_128)
+               ? kernel_id("mfma_f32_batched")
+               : kernel_id("mfma_f32_batched128");
+}
+
 int select_kernel(const Problem &p)
 {
+    if (is_general(p)) return select_general(p);
     if (p.M <= kSkinnyMaxM)
         return kernel_id(p.dtype == kF32 ? "skinny_f32" : "skinny_bf16");
     if (p.dtype == kBF16) {
@@ -197,16 +249,24 @@ int choose(const Problem &p)
     return select_kernel(p);
 }
 
+bool can_take(int id, const Problem &p)
+{
+    return id >= 0 && kKernels[id].supports(p) && (kKernels[id].general || !is_general(p));
+}
+
 int run(const Problem &p, hipStream_t stream)
 {
     switch (validate(p)) {
     case kInvalid: return hipErrorInvalidValue;
     case kNothing: return hipSuccess;
-    case kZeroFill: return launch_fill_zero(p, stream);
+    case kZeroFill:
+        // The general kernels write C_b = 0 themselves when K = 0.
+        if (!is_general(p)) return launch_fill_zero(p, stream);
+        break;
     case kCompute: break;
     }
     const int id = choose(p);
-    if (id < 0 || !kKernels[id].supports(p)) return hipErrorInvalidValue;
+    if (!can_take(id, p)) return hipErrorInvalidValue;
     const hipError_t err = kKernels[id].launch(p, stream);
     if (err == hipSuccess) g_last.store(id, std::memory_order_relaxed);
     return err;
@@ -233,6 +293,25 @@ int gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t
     return run(p, stream);
 }
 
+int gemm_f32_batched(int transa, int transb, int64_t M, int64_t N, int64_t K, const float *A,
+                     int64_t lda, int64_t stride_a, const float *B, int64_t ldb, int64_t stride_b,
+                     float *C, int64_t ldc, int64_t stride_c, int64_t batch, hipStream_t stream)
+{
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kF32, transa, transb, batch,
+                    stride_a, stride_b, stride_c};
+    return run(p, stream);
+}
+
+int gemm_bf16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                             const uint16_t *A, int64_t lda, int64_t stride_a, const uint16_t *B,
+                             int64_t ldb, int64_t stride_b, float *C, int64_t ldc,
+                             int64_t stride_c, int64_t batch, hipStream_t stream)
+{
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kBF16, transa, transb, batch,
+                    stride_a, stride_b, stride_c};
+    return run(p, stream);
+}
+
 int gemm_kernel_count(void) { return kNumKernels; }
 
 const char *gemm_kernel_name(int id)
@@ -245,22 +324,41 @@ int gemm_kernel_dtype(int id)
     return (id >= 0 && id < kNumKernels) ? kKernels[id].dtype : -1;
 }
 
-int gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
-              int64_t ldb, uintptr_t C, int64_t ldc)
+namespace {
+int plan(const Problem &p)
 {
-    if (dtype != kF32 && dtype != kBF16) return -1;
-    const Problem p{M, N, K, reinterpret_cast<const void *>(A), lda,
-                    reinterpret_cast<const void *>(B), ldb, reinterpret_cast<float *>(C), ldc,
-                    dtype};
+    if (p.dtype != kF32 && p.dtype != kBF16) return -1;
     switch (validate(p)) {
     case kInvalid: return -1;
     case kNothing: return -2;
-    case kZeroFill: return -3;
+    case kZeroFill:
+        if (!is_general(p)) return -3;
+        break;
     case kCompute: break;
     }
     const int id = choose(p);
-    if (id < 0 || !kKernels[id].supports(p)) return -1;
+    if (!can_take(id, p)) return -1;
     return id;
+}
+}  // namespace
+
+int gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t B,
+              int64_t ldb, uintptr_t C, int64_t ldc)
+{
+    const Problem p{M, N, K, reinterpret_cast<const void *>(A), lda,
+                    reinterpret_cast<const void *>(B), ldb, reinterpret_cast<float *>(C), ldc,
+                    dtype};
+    return plan(p);
+}
+
+int gemm_plan_batched(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                      uintptr_t A, int64_t lda, int64_t stride_a, uintptr_t B, int64_t ldb,
+                      int64_t stride_b, uintptr_t C, int64_t ldc, int64_t stride_c, int64_t batch)
+{
+    const Problem p{M, N, K, reinterpret_cast<const void *>(A), lda,
+                    reinterpret_cast<const void *>(B), ldb, reinterpret_cast<float *>(C), ldc,
+                    dtype, transa, transb, batch, stride_a, stride_b, stride_c};
+    return plan(p);
 }
 
 int gemm_force_kernel(int id)

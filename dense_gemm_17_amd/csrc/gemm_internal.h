@@ -11,13 +11,23 @@ enum Dtype : int { kF32 = 0, kBF16 = 1 };
 
 // Arguments of one product after validation.  Pointers are device pointers;
 // A and B are `const void*` so one signature serves both element types.
+// The last fields describe the general form C_b = op(A_b) op(B_b), b < batch:
+// ta / tb mark a factor stored transposed (A as K x M, B as N x K) and
+// sa, sb, sc are the element distances between consecutive products.  A
+// plain product has ta = tb = 0 and batch = 1; only the kernels registered
+// as general read these fields.
 struct Problem {
     int64_t M, N, K;
     const void *A; int64_t lda;
     const void *B; int64_t ldb;
     float *C; int64_t ldc;
     int dtype;
+    int ta = 0, tb = 0;
+    int64_t batch = 1, sa = 0, sb = 0, sc = 0;
 };
+
+// True when only a general (transposed / batched) kernel can take p.
+inline bool is_general(const Problem &p) { return p.ta || p.tb || p.batch != 1; }
 
 // A launcher enqueues its kernel(s) for `p` on `stream` and returns the
 // launch status.  It may assume p passed validation and its `supports` test.
@@ -29,6 +39,7 @@ struct KernelInfo {
     int dtype;
     LaunchFn launch;
     SupportsFn supports;   // shapes / alignments this kernel can take
+    bool general = false;  // also takes transposed factors and batches
 };
 
 // ---- per-family launchers (defined in the kernel files) -------------------
@@ -52,6 +63,10 @@ hipError_t launch_mfma_bf16(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_direct128(const Problem &p, hipStream_t s);
 bool supports_mfma_bf16_direct(const Problem &p);
+hipError_t launch_mfma_f32_batched(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f32_batched128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_bf16_batched(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_bf16_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_f32(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s);
 

@@ -18,7 +18,8 @@
  *     A is M x K, element (i,k) at A[i*lda + k], lda >= K
  *     B is K x N, element (k,j) at B[k*ldb + j], ldb >= N
  *     C is M x N, element (i,j) at C[i*ldc + j], ldc >= N
- * C is overwritten (there is no alpha/beta and no transpose option).  Entries
+ * C is overwritten (there is no alpha/beta; transposed factors and batches
+ * are the *_batched entry points below).  Entries
  * of C's rows beyond column N-1 (the padding up to ldc) are never written.
  *
  * Precision: gemm_f32 multiplies fp32 operands and accumulates in fp32;
@@ -73,6 +74,50 @@ int gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K,
                      float *C, int64_t ldc,
                      hipStream_t stream);
 
+/* ---- transposed factors and strided batches --------------------------------
+ *
+ * For b = 0 .. batch-1:   C_b = op(A_b) · op(B_b)
+ *
+ * These are the products of a training step's backward pass and of per-head
+ * attention ("Bare Metal Bard", page 1, second and third paragraphs: the GPT
+ * trained on the same kernels, whose gradient of a layer's input multiplies
+ * by the weight transposed and whose weight gradient multiplies by the
+ * activations transposed).
+ *
+ * Layout (element offsets; every matrix row-major in memory):
+ *   op(A_b) is M x K.  transa == 0: A_b is stored M x K, element (i,k) at
+ *     A[b*stride_a + i*lda + k], lda >= K.  transa == 1: A_b is stored
+ *     K x M, element (i,k) at A[b*stride_a + k*lda + i], lda >= M.
+ *   op(B_b) is K x N.  transb == 0: stored K x N, element (k,j) at
+ *     B[b*stride_b + k*ldb + j], ldb >= N.  transb == 1: stored N x K,
+ *     element (k,j) at B[b*stride_b + j*ldb + k], ldb >= K.
+ *   C_b is M x N at C[b*stride_c + i*ldc + j], ldc >= N; overwritten.
+ * A stride of 0 reuses one A (or B) for every product.  The products must
+ * write disjoint parts of C: stride_c >= (M-1)*ldc + N (one after another),
+ * or stride_c >= N and (batch-1)*stride_c + N <= ldc (side by side in each
+ * row); anything else is rejected.  The address range C covers, over the
+ * whole batch, must not intersect A's or B's.
+ *
+ * Precision, ownership, determinism, threading and graph capture are as for
+ * gemm_f32 / gemm_bf16_f32acc above, and so are the return codes, with also
+ * hipErrorInvalidValue for transa or transb other than 0 or 1, a negative
+ * batch or stride, or outputs of the batch that overlap.  batch == 0, M == 0
+ * or N == 0 is a no-op; K == 0 writes every C_b = 0.  batch is limited to
+ * 2^31 - 1, and so is the number of 128 x 128 tiles over all products.
+ * With transa == transb == 0 and batch == 1 the call is exactly gemm_f32
+ * (or gemm_bf16_f32acc) and takes the same kernels. */
+int gemm_f32_batched(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                     const float *A, int64_t lda, int64_t stride_a,
+                     const float *B, int64_t ldb, int64_t stride_b,
+                     float *C, int64_t ldc, int64_t stride_c,
+                     int64_t batch, hipStream_t stream);
+
+int gemm_bf16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                             const uint16_t *A, int64_t lda, int64_t stride_a,
+                             const uint16_t *B, int64_t ldb, int64_t stride_b,
+                             float *C, int64_t ldc, int64_t stride_c,
+                             int64_t batch, hipStream_t stream);
+
 /* ---- introspection and test hooks (not needed by ordinary callers) -------
  *
  * Kernel selection follows the regime classification of the devpost write-up
@@ -101,6 +146,14 @@ int gemm_kernel_dtype(int id);
 int gemm_plan(int dtype, int64_t M, int64_t N, int64_t K,
               uintptr_t A, int64_t lda, uintptr_t B, int64_t ldb,
               uintptr_t C, int64_t ldc);
+
+/* gemm_plan for the arguments of gemm_f32_batched / gemm_bf16_f32acc_batched
+ * (same return values; K == 0 with a transposed factor or batch > 1 returns
+ * the kernel that writes the zeros). */
+int gemm_plan_batched(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                      uintptr_t A, int64_t lda, int64_t stride_a,
+                      uintptr_t B, int64_t ldb, int64_t stride_b,
+                      uintptr_t C, int64_t ldc, int64_t stride_c, int64_t batch);
 
 /* Process-wide override for tests: every later call uses kernel `id` when it
  * computes that call's element type (other calls keep the table's choice);

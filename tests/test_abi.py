@@ -193,3 +193,85 @@ def test_dispatch_layout_cases():
         assert g.gemm_plan(g.F32, 17, 64, 64, A=PA, B=PB, C=PC) == -1
     finally:
         g.gemm_force_kernel(-1)
+
+
+# ---- transposed factors and strided batches (pure host planning) ------------
+
+GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128"),
+                 g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128")}
+
+
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+@pytest.mark.parametrize("ta,tb,batch", [(1, 0, 1), (0, 1, 1), (1, 1, 1), (0, 0, 4), (1, 1, 7)])
+def test_plan_batched_takes_general_family(dtype, ta, tb, batch):
+    kid = g.gemm_plan_batched(dtype, ta, tb, 1000, 900, 300, batch)
+    assert g.gemm_kernel_name(kid) in GENERAL_NAMES[dtype]
+    # K = 0 is computed (zeros) by the general kernel, not by the plain fill
+    kid0 = g.gemm_plan_batched(dtype, ta, tb, 1000, 900, 0, batch)
+    assert g.gemm_kernel_name(kid0) in GENERAL_NAMES[dtype]
+
+
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+def test_plan_batched_plain_problem_is_the_plain_plan(dtype):
+    for (M, N, K) in [(8192, 8192, 8192), (1, 8960, 1536), (300, 200, 100), (64, 64, 0)]:
+        assert g.gemm_plan_batched(dtype, 0, 0, M, N, K, 1) == g.gemm_plan(dtype, M, N, K)
+
+
+def test_plan_batched_tile_choice():
+    # many products of 128 x 128 tiles: the small tile fills the CUs; a few
+    # large products: the 256 x 256 tile
+    small = g.gemm_plan_batched(g.F32, 0, 1, 256, 256, 64, 384)
+    large = g.gemm_plan_batched(g.F32, 1, 0, 8192, 8192, 8192, 1)
+    assert g.gemm_kernel_name(large) == "mfma_f32_batched"
+    assert g.gemm_kernel_name(small) in GENERAL_NAMES[g.F32]
+
+
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+def test_plan_batched_rejects_invalid_arguments(dtype):
+    P = dict(A=PA, B=PB, C=PC)
+    assert g.gemm_plan_batched(dtype, 1, 1, 64, 48, 32, 3, **P) >= 0
+    assert g.gemm_plan_batched(dtype, 2, 0, 64, 48, 32, 3, **P) == -1       # transa not 0/1
+    assert g.gemm_plan_batched(dtype, 0, -1, 64, 48, 32, 3, **P) == -1      # transb not 0/1
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, -1, **P) == -1      # negative batch
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 2 ** 31, **P) == -1
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, stride_a=-1, **P) == -1
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, stride_c=-5, **P) == -1
+    # stored leading dimensions: A^T is K x M (lda >= M), B^T is N x K (ldb >= K)
+    assert g.gemm_plan_batched(dtype, 1, 0, 64, 48, 32, 3, lda=63, **P) == -1
+    assert g.gemm_plan_batched(dtype, 1, 0, 64, 48, 32, 3, lda=64, **P) >= 0
+    assert g.gemm_plan_batched(dtype, 0, 1, 64, 48, 32, 3, ldb=31, **P) == -1
+    assert g.gemm_plan_batched(dtype, 0, 1, 64, 48, 32, 3, ldb=32, **P) >= 0
+    # overlapping outputs: neither one after another nor side by side in a row
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, stride_c=47, **P) == -1
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, stride_c=48, ldc=144, **P) >= 0
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, stride_c=48, ldc=143, **P) == -1
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, stride_c=63 * 48 + 48, **P) >= 0
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, stride_c=63 * 48 + 47, **P) == -1
+    # C's range over the batch reaching into A's (A after the first product of C)
+    es = 4 if dtype == g.F32 else 2
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, A=PC + 64 * 48 * 4 * 2, C=PC,
+                               B=PB) == -1
+    assert g.gemm_plan_batched(dtype, 0, 0, 64, 48, 32, 3, A=PC + 64 * 48 * 4 * 3, C=PC,
+                               B=PB) >= 0
+    # misaligned element pointer
+    assert g.gemm_plan_batched(dtype, 1, 0, 64, 48, 32, 3, A=PA + es - 1, B=PB, C=PC) == -1
+    # nothing to do
+    assert g.gemm_plan_batched(dtype, 1, 1, 64, 48, 32, 0, **P) == -2
+    assert g.gemm_plan_batched(dtype, 1, 1, 0, 48, 32, 3, **P) == -2
+    assert g.gemm_plan_batched(dtype, 1, 1, 64, 0, 32, 3, **P) == -2
+    # stride 0 (one operand reused) is fine for A and B
+    assert g.gemm_plan_batched(dtype, 1, 1, 64, 48, 32, 3, stride_a=0, stride_b=0, **P) >= 0
+
+
+def test_forced_plain_kernel_cannot_take_general_problem():
+    plain = g.kernel_id("mfma_f32_direct")
+    general = g.kernel_id("mfma_f32_batched128")
+    try:
+        assert g.gemm_force_kernel(plain) == 0
+        assert g.gemm_plan_batched(g.F32, 1, 0, 512, 512, 512, 1) == -1
+        assert g.gemm_plan_batched(g.F32, 0, 0, 512, 512, 512, 2) == -1
+        assert g.gemm_force_kernel(general) == 0
+        assert g.gemm_plan_batched(g.F32, 1, 0, 512, 512, 512, 1) == general
+        assert g.gemm_plan(g.F32, 512, 512, 512, PA, 512, PB, 512, PC, 512) == general
+    finally:
+        g.gemm_force_kernel(-1)

@@ -1,0 +1,294 @@
+"""GPU parity of transposed-factor and strided-batched products.
+
+C_b = op(A_b) op(B_b) through gemm_f32_batched / gemm_bf16_f32acc_batched
+(the Python binding passes a transposed view such as ``w.t()`` as a
+transposed factor and a 3-D tensor as a strided batch), against the oracle's
+batched entry point on the same seeded operands.  Exact on small-integer
+operands (every partial sum is an integer below 2^24, so any summation order
+gives the same bits), the 5e-4 normalized-error gate on random operands, and
+the layout edge cases: ragged tails over several tiles, unaligned and padded
+rows, shared and stride-0 operands, products side by side in one output
+row, K = 0, empty batches, guard bands that must stay untouched.  The GPT
+backward-pass and attention shapes are checked in the launch configuration
+the benchmark times, on sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_17_amd as g
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GATE = oracle.GATE
+TRANS = [(False, False), (True, False), (False, True), (True, True)]
+GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128"],
+           "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128"]}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class Forced:
+    def __init__(self, name):
+        self.kid = g.kernel_id(name) if name else -1
+
+    def __enter__(self):
+        assert g.gemm_force_kernel(self.kid) == 0
+
+    def __exit__(self, *exc):
+        g.gemm_force_kernel(-1)
+
+
+def stored(x, trans):
+    """Storage of the logical matrices x (..., R, C): x itself, or its
+    transpose written out ((..., C, R), contiguous)."""
+    return x.transpose(-1, -2).contiguous() if trans else x.contiguous()
+
+
+def view(xs, trans):
+    """The logical matrix as a view of its storage (a transposed view when
+    the storage is transposed) - what a caller hands to gemm()."""
+    return xs.transpose(-1, -2) if trans else xs
+
+
+def as_oracle(x):
+    return workloads.as_numpy_operand(x)
+
+
+def run(a, b, kernel=None, out=None):
+    with Forced(kernel):
+        c = g.gemm(a, b, out=out)
+    torch.cuda.synchronize()
+    if kernel:
+        assert g.gemm_last_kernel() == g.kernel_id(kernel)
+    return c
+
+
+def small_int(shape, dtype, gen):
+    lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    return workloads.small_int(shape, lo, hi, gen, tdt)
+
+
+def exact_case(dtype, kernel, ta, tb, M, N, K, batch, seed):
+    gen = workloads.generator(seed)
+    A = small_int((batch, M, K), dtype, gen)
+    B = small_int((batch, K, N), dtype, gen)
+    As, Bs = stored(A, ta), stored(B, tb)
+    say(f"[batched] exact {dtype} {kernel} ta={ta} tb={tb} M={M} N={N} K={K} batch={batch}")
+    C = run(view(As.to(DEV), ta), view(Bs.to(DEV), tb), kernel)
+    Cref, _ = oracle.gemm_batched(as_oracle(As), as_oracle(Bs), ta, tb)
+    assert C.shape == (batch, M, N)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), Cref)
+    C2 = run(view(As.to(DEV), ta), view(Bs.to(DEV), tb), kernel)
+    assert torch.equal(C, C2), "not deterministic"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kernel_idx", [0, 1])
+@pytest.mark.parametrize("ta,tb", TRANS)
+def test_small_integer_exact(dtype, kernel_idx, ta, tb):
+    kernel = GENERAL[dtype][kernel_idx]
+    # several tiles in each direction with ragged tails in M, N and K
+    exact_case(dtype, kernel, ta, tb, 300, 270, 100, 3, 41)
+    exact_case(dtype, kernel, ta, tb, 513, 129, 200, 2, 42)
+    exact_case(dtype, kernel, ta, tb, 7, 9, 3, 5, 43)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ta,tb", TRANS)
+def test_brute_force_tiny_shapes(dtype, ta, tb):
+    # every (M, N, K) in {1..6}^3, two products each, every general kernel;
+    # one batch holds all shapes' operands so each kernel launches per shape
+    gen = workloads.generator(44)
+    for kernel in GENERAL[dtype]:
+        for M in range(1, 7):
+            for N in range(1, 7):
+                for K in range(1, 7):
+                    A = small_int((2, M, K), dtype, gen)
+                    B = small_int((2, K, N), dtype, gen)
+                    As, Bs = stored(A, ta), stored(B, tb)
+                    with Forced(kernel):
+                        C = g.gemm(view(As.to(DEV), ta), view(Bs.to(DEV), tb))
+                    ref = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float32)
+                    assert torch.equal(C.cpu(), ref), (kernel, M, N, K)
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ta,tb", TRANS)
+def test_random_operands_gate(dtype, ta, tb):
+    w = workloads.Workload("batched_rand", 333, 287, 515, dtype)
+    gen = workloads.generator()
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    A = workloads.draw((4, w.M, w.K), ("uniform", 1.0), gen).to(tdt)
+    B = workloads.draw((4, w.K, w.N), ("uniform", 1.0), gen).to(tdt)
+    As, Bs = stored(A, ta), stored(B, tb)
+    Cref, D = oracle.gemm_batched(as_oracle(As), as_oracle(Bs), ta, tb)
+    for kernel in GENERAL[dtype] + [None]:
+        say(f"[batched] gate {dtype} {kernel or 'table'} ta={ta} tb={tb}")
+        C = run(view(As.to(DEV), ta), view(Bs.to(DEV), tb), kernel).cpu().numpy()
+        e, at, n = oracle.normalized_error(C.reshape(-1, w.N), Cref.reshape(-1, w.N),
+                                           D.reshape(-1, w.N))
+        say(f"[batched]   e={e:.3e} at={at} n>1e-5={n}")
+        assert e <= GATE, (kernel, e, at)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_padded_and_offset_layouts(dtype):
+    # odd leading dimensions and batch strides, operands starting one element
+    # into their buffers: the element-load path of every general kernel
+    gen = workloads.generator(45)
+    M, N, K, batch = 130, 67, 77, 3
+    for ta, tb in TRANS:
+        A = small_int((batch, M, K), dtype, gen)
+        B = small_int((batch, K, N), dtype, gen)
+        ref = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float32)
+        ar, ac = (K, M) if ta else (M, K)
+        br, bc = (N, K) if tb else (K, N)
+        abuf = torch.zeros(batch * (ar * (ac + 3) + 5) + 1, dtype=A.dtype)
+        bbuf = torch.zeros(batch * (br * (bc + 1) + 3) + 1, dtype=A.dtype)
+        As = abuf[1:1 + batch * (ar * (ac + 3) + 5)].view(batch, -1)[:, :ar * (ac + 3)]
+        As = As.reshape(batch, ar, ac + 3)[:, :, :ac]
+        Bs = bbuf[1:1 + batch * (br * (bc + 1) + 3)].view(batch, -1)[:, :br * (bc + 1)]
+        Bs = Bs.reshape(batch, br, bc + 1)[:, :, :bc]
+        As.copy_(stored(A, ta))
+        Bs.copy_(stored(B, tb))
+        abuf_d, bbuf_d = abuf.to(DEV), bbuf.to(DEV)
+        Ad = abuf_d[1:1 + batch * (ar * (ac + 3) + 5)].view(batch, -1)[:, :ar * (ac + 3)]
+        Ad = Ad.reshape(batch, ar, ac + 3)[:, :, :ac]
+        Bd = bbuf_d[1:1 + batch * (br * (bc + 1) + 3)].view(batch, -1)[:, :br * (bc + 1)]
+        Bd = Bd.reshape(batch, br, bc + 1)[:, :, :bc]
+        for kernel in GENERAL[dtype]:
+            say(f"[batched] unaligned {dtype} {kernel} ta={ta} tb={tb}")
+            C = run(view(Ad, ta), view(Bd, tb), kernel)
+            assert torch.equal(C.cpu(), ref), (kernel, ta, tb)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shared_and_stride_zero_operands(dtype):
+    gen = workloads.generator(46)
+    M, N, K, batch = 200, 150, 90, 4
+    A = small_int((batch, M, K), dtype, gen)
+    W = small_int((N, K), dtype, gen)               # a weight stored N x K, used as W^T
+    Ad, Wd = A.to(DEV), W.to(DEV)
+    ref = (A.to(torch.int64) @ W.to(torch.int64).t()).to(torch.float32)
+    for kernel in GENERAL[dtype] + [None]:
+        C = run(Ad, Wd.t(), kernel)                 # 2-D factor shared by the batch
+        assert torch.equal(C.cpu(), ref)
+        C = run(Ad, Wd.t().unsqueeze(0).expand(batch, K, N), kernel)   # batch stride 0
+        assert torch.equal(C.cpu(), ref)
+    X = small_int((M, K), dtype, gen)
+    Bs = small_int((batch, K, N), dtype, gen)
+    ref2 = (X.to(torch.int64) @ Bs.to(torch.int64)).to(torch.float32)
+    C = run(X.to(DEV), Bs.to(DEV))
+    assert torch.equal(C.cpu(), ref2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_outputs_side_by_side_and_guard_bands(dtype):
+    # C viewed as (M, batch, N) inside rows padded by 5: products sit side by
+    # side in each row; padding and everything outside stays NaN
+    gen = workloads.generator(47)
+    M, N, K, batch = 70, 33, 41, 3
+    A = small_int((batch, M, K), dtype, gen)
+    B = small_int((batch, K, N), dtype, gen)
+    ref = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float32)
+    ldc = batch * N + 5
+    for kernel in GENERAL[dtype]:
+        buf = torch.full((M * ldc + 64,), float("nan"), device=DEV)
+        out = buf[32:32 + M * ldc].view(M, ldc)[:, :batch * N].view(M, batch, N).transpose(0, 1)
+        run(A.to(DEV), B.to(DEV), kernel, out=out)
+        got = out.cpu()
+        assert torch.equal(got, ref)
+        rest = buf.cpu().clone()
+        rest[32:32 + M * ldc].view(M, ldc)[:, :batch * N] = 0.0
+        assert torch.isnan(rest[:32]).all() and torch.isnan(rest[32 + M * ldc:]).all()
+        assert torch.isnan(rest[32:32 + M * ldc].view(M, ldc)[:, batch * N:]).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_degenerate_batches(dtype):
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    # K = 0: every product is the empty sum
+    for kernel in GENERAL[dtype] + [None]:
+        out = torch.full((3, 40, 30), float("nan"), device=DEV)
+        a = torch.zeros((3, 0, 40), dtype=tdt, device=DEV).transpose(1, 2)
+        b = torch.zeros((3, 0, 30), dtype=tdt, device=DEV)
+        run(a, b, kernel, out=out)
+        assert torch.equal(out.cpu(), torch.zeros(3, 40, 30))
+    # empty batch, M = 0, N = 0: nothing is written
+    out = torch.full((0, 5, 6), 7.0, device=DEV)
+    run(torch.zeros((0, 5, 4), dtype=tdt, device=DEV), torch.zeros((0, 4, 6), dtype=tdt, device=DEV),
+        out=out)
+    out = torch.full((2, 5, 0), 7.0, device=DEV)
+    run(torch.zeros((2, 5, 4), dtype=tdt, device=DEV).transpose(1, 2).transpose(1, 2),
+        torch.zeros((4, 0), dtype=tdt, device=DEV), out=out)
+
+
+def test_invalid_batched_calls_raise():
+    a = torch.zeros((2, 8, 4), device=DEV)
+    b = torch.zeros((2, 4, 8), device=DEV)
+    out = torch.zeros((2, 8, 8), device=DEV)
+    with pytest.raises(ValueError):
+        g.gemm(a, torch.zeros((3, 4, 8), device=DEV))
+    # overlapping products in C (stride_c = 1) are refused by the library
+    rc = g.gemm_f32_batched(0, 0, 8, 8, 4, a.data_ptr(), 4, 32, b.data_ptr(), 8, 32,
+                            out.data_ptr(), 8, 1, 2, 0)
+    assert rc == g.HIP_ERROR_INVALID_VALUE
+    rc = g.gemm_f32_batched(2, 0, 8, 8, 4, a.data_ptr(), 4, 32, b.data_ptr(), 8, 32,
+                            out.data_ptr(), 8, 64, 2, 0)
+    assert rc == g.HIP_ERROR_INVALID_VALUE
+    # C overlapping A across the batch
+    rc = g.gemm_f32_batched(0, 0, 8, 8, 4, a.data_ptr(), 4, 32, b.data_ptr(), 8, 32,
+                            a.data_ptr(), 8, 64, 2, 0)
+    assert rc == g.HIP_ERROR_INVALID_VALUE
+    torch.cuda.synchronize()
+
+
+def test_plain_problem_keeps_plain_kernels():
+    # transa = transb = 0 and batch = 1 through the batched entry point is the
+    # plain product and runs the plain table's kernel
+    a = torch.rand((512, 512), device=DEV)
+    b = torch.rand((512, 512), device=DEV)
+    out = torch.empty((512, 512), device=DEV)
+    g.gemm(a, b, out=out)
+    torch.cuda.synchronize()
+    plain = g.gemm_last_kernel()
+    rc = g.gemm_f32_batched(0, 0, 512, 512, 512, a.data_ptr(), 512, 0, b.data_ptr(), 512, 0,
+                            out.data_ptr(), 512, 0, 1, 0)
+    torch.cuda.synchronize()
+    assert rc == 0 and g.gemm_last_kernel() == plain
+    assert not g.gemm_kernel_name(plain).endswith(("batched", "batched128"))
+
+
+@pytest.mark.parametrize("name", sorted(workloads.GENERAL_WORKLOADS))
+def test_benchmark_shapes_sampled(name):
+    """The backward-pass and attention shapes, table choice, sampled rows of
+    products spread over the batch."""
+    w = workloads.GENERAL_WORKLOADS[name]
+    As, Bs = workloads.make_general_inputs(w)
+    a, b = workloads.general_views(w, As.to(DEV), Bs.to(DEV))
+    say(f"[batched] {name} {w.batch}x({w.M},{w.N},{w.K}) ta={w.ta} tb={w.tb}")
+    C = run(a, b)
+    C2 = run(a, b)
+    assert torch.equal(C, C2)
+    Ch = C.cpu().numpy().reshape(w.batch, w.M, w.N)
+    rng = np.random.default_rng(5)
+    for bi in sorted({0, w.batch - 1, int(rng.integers(w.batch))}):
+        rows = sorted({0, w.M - 1, *rng.choice(w.M, size=min(w.M, 12), replace=False).tolist()})
+        A_b = As[bi] if As.dim() == 3 else As
+        B_b = Bs[bi] if Bs.dim() == 3 else Bs
+        # the rows of op(A) that matter, as a small stored operand of their own
+        A_rows = (A_b.t()[rows] if w.ta else A_b[rows]).contiguous()
+        Cref, D = oracle.gemm_batched(as_oracle(A_rows), as_oracle(B_b), False, w.tb)
+        e, at, n = oracle.normalized_error(Ch[bi][rows], Cref, D)
+        say(f"[batched]   product {bi}: e={e:.3e} at={at}")
+        assert e <= GATE

@@ -128,3 +128,75 @@ def as_numpy_operand(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return bf16_bits(t)
     return t.contiguous().numpy()
+
+
+# ---- transposed factors and strided batches --------------------------------
+# The backward pass of the same GPT (gradients are products with one factor
+# stored transposed: the input gradient dX = dY W^T reads the weight as
+# stored, the weight gradient dW = X^T dY the activations as stored) and its
+# attention (6 heads of width 64 over a context of 256, 64 sequences: 384
+# per-head products).  Each product's operands are drawn in their stored
+# layout, A first, then B, from the same seeded generator.
+
+
+@dataclass(frozen=True)
+class GeneralWorkload:
+    name: str
+    batch: int
+    M: int
+    N: int
+    K: int
+    ta: bool                      # A stored K x M
+    tb: bool                      # B stored N x K
+    dtype: str
+    dist_a: Tuple[str, float] = ("normal", 1.0)
+    dist_b: Tuple[str, float] = ("normal", 1.0)
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+    @property
+    def in_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        s = self.in_bytes
+        return self.batch * (s * (self.M * self.K + self.K * self.N) + 4 * self.M * self.N)
+
+
+GENERAL_WORKLOADS: Dict[str, GeneralWorkload] = {w.name: w for w in [
+    GeneralWorkload("gpt_qkv_dx", 1, 16384, 384, 1152, False, True, "f32", _ACT, _WGT,
+                    note="QKV input gradient dY W^T"),
+    GeneralWorkload("gpt_qkv_dw", 1, 384, 1152, 16384, True, False, "f32", _ACT, _ACT,
+                    note="QKV weight gradient X^T dY"),
+    GeneralWorkload("gpt_mlp_down_dx", 1, 16384, 1536, 384, False, True, "f32", _ACT, _WGT,
+                    note="MLP-down input gradient dY W^T"),
+    GeneralWorkload("attn_scores", 384, 256, 256, 64, False, True, "f32",
+                    note="per-head scores Q K^T"),
+    GeneralWorkload("attn_pv", 384, 256, 64, 256, False, False, "f32",
+                    note="per-head probabilities times values"),
+    GeneralWorkload("bf16_gpt_qkv_dw", 1, 384, 1152, 16384, True, False, "bf16", _ACT, _ACT,
+                    note="QKV weight gradient, bf16 operands"),
+    GeneralWorkload("bf16_attn_scores", 384, 256, 256, 64, False, True, "bf16",
+                    note="per-head scores, bf16 operands"),
+]}
+
+
+def make_general_inputs(w: GeneralWorkload, seed: int = SEED) -> Tuple[torch.Tensor, torch.Tensor]:
+    """CPU tensors (A, B) in their stored layouts: A is (batch,) M x K or
+    K x M when transposed, B is (batch,) K x N or N x K; 2-D when batch is 1."""
+    g = generator(seed)
+    lead = (w.batch,) if w.batch > 1 else ()
+    A = draw(lead + ((w.K, w.M) if w.ta else (w.M, w.K)), w.dist_a, g)
+    B = draw(lead + ((w.N, w.K) if w.tb else (w.K, w.N)), w.dist_b, g)
+    if w.dtype == "bf16":
+        A, B = A.to(torch.bfloat16), B.to(torch.bfloat16)
+    return A, B
+
+
+def general_views(w: GeneralWorkload, A: torch.Tensor, B: torch.Tensor):
+    """The logical factors op(A), op(B) as views of the stored tensors."""
+    return (A.transpose(-1, -2) if w.ta else A), (B.transpose(-1, -2) if w.tb else B)
