@@ -344,9 +344,10 @@ def main():
     if args.copy_calibration:
         copy = copy_calibration(dev)
 
-    others = None
+    others = general = None
     if not args.no_configs:
         others = other_configs(dev, set(names), args.check_rows)
+        general = general_configs(dev, args.check_rows)
 
     ceiling = None
     if not args.no_ceiling:
@@ -383,6 +384,9 @@ def main():
         # call (short calls also from a replayed HIP graph), its roofline and
         # a sampled check against the oracle; context, not `value`
         "other_configs": others,
+        # the same for products with a transposed factor or a batch (the GPT
+        # backward pass and attention shapes)
+        "general_configs": general,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels
         "env": dict(clocks.summary(), toolchain=toolchain(g.gemm_build_info())),
@@ -403,7 +407,6 @@ def other_configs(dev, skip, check_rows):
     sets, are also replayed from a HIP graph for the GPU's own time."""
     import dense_gemm_17_amd as g
     import oracle
-    from dense_gemm_17_amd.measure import ClockSampler
     out = {}
     rng = np.random.default_rng(1)
     for name, w in workloads.WORKLOADS.items():
@@ -419,9 +422,6 @@ def other_configs(dev, skip, check_rows):
         kernel = g.gemm_kernel_name(g.gemm_plan(code, w.M, w.N, w.K, a0.data_ptr(), a0.stride(0),
                                                 b0.data_ptr(), b0.stride(0), c0.data_ptr(),
                                                 c0.stride(0)))
-        st = torch.cuda.Stream(dev)
-        st.wait_stream(torch.cuda.current_stream(dev))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         state = {"i": 0}
 
         def call():
@@ -429,40 +429,7 @@ def other_configs(dev, skip, check_rows):
             state["i"] += 1
             g.gemm(a, b, out=c)
 
-        def windows(run, reps):
-            times = []
-            for _ in range(5):
-                e0.record(st)
-                run()
-                e1.record(st)
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1) / reps)
-            return float(np.median(times))
-
-        graph_ms = None
-        with torch.cuda.stream(st):
-            for _ in range(copies):
-                call()
-            e0.record(st)
-            call()
-            e1.record(st)
-            torch.cuda.synchronize()
-            one = max(e0.elapsed_time(e1), 1e-3)
-            reps = copies * max(1, min(2000 // copies, int(20.0 / one / copies) + 1))
-            # back-to-back calls from Python, as an application makes them
-            with ClockSampler() as clocks:
-                ms = windows(lambda: [call() for _ in range(reps)], reps)
-            if ms < 0.02:
-                # short calls: the host call sets their pace, so the same
-                # calls replayed from a HIP graph give the GPU's own time
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph, stream=st):
-                    for _ in range(reps):
-                        call()
-                graph.replay()
-                torch.cuda.synchronize()
-                graph_ms = windows(graph.replay, reps)
-                del graph
+        ms, graph_ms, clocks = time_calls(dev, call, copies)
         rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, check_rows),
                                                      replace=False).tolist()))
         fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
@@ -475,6 +442,111 @@ def other_configs(dev, skip, check_rows):
         hbm = w.flops / per_copy < ridge
         out[name] = {
             "M": w.M, "N": w.N, "K": w.K, "dtype": w.dtype, "kernel": kernel,
+            "us_per_call": round(ms * 1e3, 2), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+            "bound": "hbm" if hbm else "mfma",
+            "frac": round(gbs / HBM_PEAK_GBS if hbm else tflops / PEAK_TFLOPS[w.dtype], 4),
+            "us_per_call_graph": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+            "operand_copies": copies, "max_norm_err_sampled": float(f"{err:.3e}"),
+            "sclk_mhz": (clocks.summary()["sclk_mhz"] or {}).get("median"),
+        }
+        del ops
+        torch.cuda.empty_cache()
+    return out
+
+
+def time_calls(dev, call, copies):
+    """Median time per call (ms) of back-to-back calls on a side stream over 5
+    windows of at least ~20 ms; for calls under 20 us also the time of the
+    same calls replayed from a HIP graph; and the clock sampler."""
+    from dense_gemm_17_amd.measure import ClockSampler
+    st = torch.cuda.Stream(dev)
+    st.wait_stream(torch.cuda.current_stream(dev))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def windows(run, reps):
+        times = []
+        for _ in range(5):
+            e0.record(st)
+            run()
+            e1.record(st)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / reps)
+        return float(np.median(times))
+
+    graph_ms = None
+    with torch.cuda.stream(st):
+        for _ in range(copies):
+            call()
+        e0.record(st)
+        call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        one = max(e0.elapsed_time(e1), 1e-3)
+        reps = copies * max(1, min(2000 // copies, int(20.0 / one / copies) + 1))
+        # back-to-back calls from Python, as an application makes them
+        with ClockSampler() as clocks:
+            ms = windows(lambda: [call() for _ in range(reps)], reps)
+        if ms < 0.02:
+            # short calls: the host call sets their pace, so the same
+            # calls replayed from a HIP graph give the GPU's own time
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=st):
+                for _ in range(reps):
+                    call()
+            graph.replay()
+            torch.cuda.synchronize()
+            graph_ms = windows(graph.replay, reps)
+            del graph
+    return ms, graph_ms, clocks
+
+
+def general_configs(dev, check_rows):
+    """Transposed-factor and batched products (the GPT backward pass and
+    attention shapes): the table's kernel timed like the configurations
+    above, with sampled rows of the first and last product checked against
+    the oracle."""
+    import dense_gemm_17_amd as g
+    import oracle
+    out = {}
+    rng = np.random.default_rng(2)
+    for name, w in workloads.GENERAL_WORKLOADS.items():
+        As, Bs = workloads.make_general_inputs(w)
+        per_copy = w.algorithmic_bytes
+        copies = 1 if per_copy * 2 > LLC_BYTES else max(2, -(-2 * LLC_BYTES // per_copy))
+        shape = (w.batch, w.M, w.N) if w.batch > 1 else (w.M, w.N)
+        ops = []
+        for _ in range(copies):
+            a, b = workloads.general_views(w, As.to(dev), Bs.to(dev))
+            ops.append((a, b, torch.empty(shape, dtype=torch.float32, device=dev)))
+        state = {"i": 0}
+
+        def call():
+            a, b, c = ops[state["i"] % copies]
+            state["i"] += 1
+            g.gemm(a, b, out=c)
+
+        ms, graph_ms, clocks = time_calls(dev, call, copies)
+        kernel = g.gemm_kernel_name(g.gemm_last_kernel())
+        c0 = ops[0][2].reshape(w.batch, w.M, w.N)
+        err = 0.0
+        for bi in sorted({0, w.batch - 1}):
+            rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, check_rows),
+                                                         replace=False).tolist()))
+            A_b = As[bi] if As.dim() == 3 else As
+            B_b = Bs[bi] if Bs.dim() == 3 else Bs
+            A_rows = (A_b.t()[rows] if w.ta else A_b[rows]).contiguous()
+            Cref, D = oracle.gemm_batched(workloads.as_numpy_operand(A_rows),
+                                          workloads.as_numpy_operand(B_b), False, w.tb,
+                                          threads=cpu_threads())
+            e, _, _ = oracle.normalized_error(c0[bi][rows].cpu().numpy(), Cref, D)
+            err = max(err, e)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        gbs = per_copy / (ms * 1e-3) / 1e9
+        ridge = PEAK_TFLOPS[w.dtype] * 1e3 / HBM_PEAK_GBS
+        hbm = w.flops / per_copy < ridge
+        out[name] = {
+            "batch": w.batch, "M": w.M, "N": w.N, "K": w.K, "transa": w.ta, "transb": w.tb,
+            "dtype": w.dtype, "kernel": kernel,
             "us_per_call": round(ms * 1e3, 2), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
             "bound": "hbm" if hbm else "mfma",
             "frac": round(gbs / HBM_PEAK_GBS if hbm else tflops / PEAK_TFLOPS[w.dtype], 4),

@@ -45,6 +45,8 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_batched128", kF32, launch_mfma_f32_batched128, supports_any, true},
     {"mfma_bf16_batched", kBF16, launch_mfma_bf16_batched, supports_any, true},
     {"mfma_bf16_batched128", kBF16, launch_mfma_bf16_batched128, supports_any, true},
+    {"mfma_f32_batched_splitk", kF32, launch_mfma_f32_batched_splitk, supports_any, true},
+    {"mfma_bf16_batched_splitk", kBF16, launch_mfma_bf16_batched_splitk, supports_any, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -177,11 +179,21 @@ int64_t tiled_cost(const Problem &p, int64_t bm, int64_t bn, int64_t per_cu, int
     return waves * bm * bn * per_cu * 1000000 / (128 * 128) / eff_permille;
 }
 
-// Transposed factors and batches of products: the general (register-staged,
-// any layout) family, 256 x 256 or 128 x 128 tiles by the same wave-count
-// estimate as above, over the tiles of every product.
+// Transposed factors and batches of products: the general (any layout)
+// family.  Small outputs with a long K go to its split-K kernel; otherwise
+// 256 x 256 or 128 x 128 tiles by the same wave-count estimate as above,
+// over the tiles of every product.
 int select_general(const Problem &p)
 {
+    // fp32 with fewer 128 x 128 tiles over all products than CUs (weight
+    // gradients: a small output summed over a long K): the split-K kernel,
+    // whose 32 x 32 tiles and four-way K split occupy every CU (GPT QKV
+    // weight gradient 384 x 1152 x 16384: 49 vs 9.8 TFLOP/s).  Its bf16
+    // twin is kept for the test hook only: with a transposed factor its
+    // lanes need eight 2-byte loads per operand per MFMA and it loses to
+    // the 128 x 128 tile (23 vs 63 TFLOP/s on the same shape).
+    if (p.dtype == kF32 && ceil_div(p.M, 128) * ceil_div(p.N, 128) * p.batch < kCUs)
+        return kernel_id("mfma_f32_batched_splitk");
     if (p.dtype == kBF16)
         return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
                    ? kernel_id("mfma_bf16_batched")

@@ -67,6 +67,8 @@ hipError_t launch_mfma_f32_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_batched128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f32_batched_splitk(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_bf16_batched_splitk(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_f32(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s);
 

@@ -525,6 +525,223 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
 
 }  // namespace bf
 
+// ---------------------------------------------------------------------------
+// Split-K for products whose output is too small to fill the chip with
+// tiles but whose K is long: the weight gradient X^T dY of a layer is a
+// d_in x d_out output summed over every token of the batch (16384 for the
+// GPT above).  One 32 x 32 tile of C per work-group; its four waves take the
+// K groups round robin, each accumulating its own partial 32 x 32 block,
+// and the four partial blocks are added in LDS in a fixed order
+// (deterministic, no atomics, no workspace).  Operands go straight from
+// global memory (L2) to registers, kU groups per step, the next step's
+// loads in flight while this step's MFMAs run.  Every load is issued at a
+// clamped, in-bounds address and values out of range are zeroed with a
+// bitwise mask, so no branch sits between the loads.
+//
+// Lane (h, c) supplies row c of the tile's A block and column c of its B
+// block.  Along a stored row of K (A as written, B transposed) a lane's
+// values are one 16-byte load when the rows allow it; across stored rows
+// (A transposed, B as written) they are 4-byte (fp32) or 2-byte (bf16)
+// loads that are coalesced over the 32 lanes of a half-wave.
+
+namespace sk {
+
+constexpr int kPad = 33;   // LDS row stride of a partial block (floats)
+
+__device__ __forceinline__ float masked(float x, uint32_t keep)
+{
+    return __uint_as_float(__float_as_uint(x) & keep);
+}
+
+__device__ __forceinline__ int64_t clampk(int64_t k, int64_t K) { return k < K ? k : K - 1; }
+
+// The four partial blocks of a work-group's waves, added in wave order, to C.
+__device__ __forceinline__ void reduce_store(float *red, const f32x16 &acc, int wave, int lane,
+                                             float *__restrict__ C, int64_t ldc, int64_t M,
+                                             int64_t N, int64_t m0, int64_t n0)
+{
+    const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        red[(wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * kPad + c] = acc[r];
+    __syncthreads();
+    for (int e = threadIdx.x; e < 32 * 32; e += kThreads) {
+        const int rr = e >> 5, cc = e & 31;
+        float v = red[rr * kPad + cc];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) v += red[(w * 32 + rr) * kPad + cc];
+        if (m0 + rr < M && n0 + cc < N) store_c_stream(C + (m0 + rr) * ldc + n0 + cc, v);
+    }
+}
+
+// fp32 (v_mfma_f32_32x32x2_f32): group g is k = 8g .. 8g+7, lane half h
+// carries k = 8g + 4h + j for MFMA j.
+template <bool TA, bool TB, bool kVecA, bool kVecB>
+__global__ __launch_bounds__(kThreads) void f32_kernel(
+    int64_t M, int64_t N, int64_t K, const float *__restrict__ A, int64_t lda, int64_t sa,
+    const float *__restrict__ B, int64_t ldb, int64_t sb, float *__restrict__ C, int64_t ldc,
+    int64_t sc, int64_t batch, int64_t tiles_m, int64_t tiles_n)
+{
+    constexpr int kU = 8;
+    __shared__ float red[4 * 32 * kPad];
+    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch);
+    A += t.b * sa;
+    B += t.b * sb;
+    C += t.b * sc;
+    const int64_t m0 = t.tm * 32, n0 = t.tn * 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, c = lane & 31;
+    const bool row_ok = m0 + c < M, col_ok = n0 + c < N;
+    const int64_t row = row_ok ? m0 + c : 0, col = col_ok ? n0 + c : 0;
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+    const int64_t groups = (K + 7) / 8;
+    auto load = [&](int64_t g0, float (&a)[kU][4], float (&b)[kU][4]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t k = 8 * (g0 + 4 * u) + 4 * h;
+            if constexpr (!TA && kVecA) {
+                // K % 4 == 0 here, so the four k are all in range or all out
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(A + row * lda + (k < K ? k : K - 4));
+                const uint32_t keep = (row_ok && k < K) ? ~0u : 0u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[u][e] = masked(v[e], keep);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t kk = clampk(k + e, K);
+                    const float v = TA ? A[kk * lda + row] : A[row * lda + kk];
+                    a[u][e] = masked(v, (row_ok && k + e < K) ? ~0u : 0u);
+                }
+            }
+            if constexpr (TB && kVecB) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(B + col * ldb + (k < K ? k : K - 4));
+                const uint32_t keep = (col_ok && k < K) ? ~0u : 0u;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[u][j] = masked(v[j], keep);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t kk = clampk(k + j, K);
+                    const float v = TB ? B[col * ldb + kk] : B[kk * ldb + col];
+                    b[u][j] = masked(v, (col_ok && k + j < K) ? ~0u : 0u);
+                }
+            }
+        }
+    };
+    auto mfmas = [&](const float (&a)[kU][4], const float (&b)[kU][4]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[u][j], b[u][j], acc, 0, 0, 0);
+    };
+    float a0[kU][4], a1[kU][4], b0[kU][4], b1[kU][4];
+    int64_t g0 = wave;
+    if (g0 < groups) load(g0, a0, b0);
+    while (g0 < groups) {
+        const int64_t g1 = g0 + 4 * kU;
+        if (g1 < groups) load(g1, a1, b1);
+        mfmas(a0, b0);
+        if (g1 >= groups) break;
+        const int64_t g2 = g1 + 4 * kU;
+        if (g2 < groups) load(g2, a0, b0);
+        mfmas(a1, b1);
+        g0 = g2;
+    }
+    reduce_store(red, acc, wave, lane, C, ldc, M, N, m0, n0);
+}
+
+// bf16 (v_mfma_f32_32x32x16_bf16): group g is k = 16g .. 16g+15, lane half h
+// carries the eight k = 16g + 8h .. 16g + 8h + 7.
+__device__ __forceinline__ uint16_t masked16(uint16_t x, bool keep) { return keep ? x : 0; }
+
+template <bool TA, bool TB, bool kVecA, bool kVecB>
+__global__ __launch_bounds__(kThreads) void bf16_kernel(
+    int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A, int64_t lda, int64_t sa,
+    const uint16_t *__restrict__ B, int64_t ldb, int64_t sb, float *__restrict__ C, int64_t ldc,
+    int64_t sc, int64_t batch, int64_t tiles_m, int64_t tiles_n)
+{
+    constexpr int kU = 4;
+    __shared__ float red[4 * 32 * kPad];
+    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch);
+    A += t.b * sa;
+    B += t.b * sb;
+    C += t.b * sc;
+    const int64_t m0 = t.tm * 32, n0 = t.tn * 32;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, c = lane & 31;
+    const bool row_ok = m0 + c < M, col_ok = n0 + c < N;
+    const int64_t row = row_ok ? m0 + c : 0, col = col_ok ? n0 + c : 0;
+
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+    const int64_t groups = (K + 15) / 16;
+    auto load = [&](int64_t g0, u16x8 (&a)[kU], u16x8 (&b)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t k = 16 * (g0 + 4 * u) + 8 * h;
+            if constexpr (!TA && kVecA) {
+                // K % 8 == 0 here, so the eight k are all in range or all out
+                const u16x8 v = *reinterpret_cast<const u16x8 *>(A + row * lda + (k < K ? k : K - 8));
+                const bool keep = row_ok && k < K;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[u][e] = masked16(v[e], keep);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int64_t kk = clampk(k + e, K);
+                    const uint16_t v = TA ? A[kk * lda + row] : A[row * lda + kk];
+                    a[u][e] = masked16(v, row_ok && k + e < K);
+                }
+            }
+            if constexpr (TB && kVecB) {
+                const u16x8 v = *reinterpret_cast<const u16x8 *>(B + col * ldb + (k < K ? k : K - 8));
+                const bool keep = col_ok && k < K;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) b[u][e] = masked16(v[e], keep);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int64_t kk = clampk(k + e, K);
+                    const uint16_t v = TB ? B[col * ldb + kk] : B[kk * ldb + col];
+                    b[u][e] = masked16(v, col_ok && k + e < K);
+                }
+            }
+        }
+    };
+    auto mfmas = [&](const u16x8 (&a)[kU], const u16x8 (&b)[kU]) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                          __builtin_bit_cast(bf16x8, b[u]), acc,
+                                                          0, 0, 0);
+    };
+    u16x8 a0[kU], a1[kU], b0[kU], b1[kU];
+    int64_t g0 = wave;
+    if (g0 < groups) load(g0, a0, b0);
+    while (g0 < groups) {
+        const int64_t g1 = g0 + 4 * kU;
+        if (g1 < groups) load(g1, a1, b1);
+        mfmas(a0, b0);
+        if (g1 >= groups) break;
+        const int64_t g2 = g1 + 4 * kU;
+        if (g2 < groups) load(g2, a0, b0);
+        mfmas(a1, b1);
+        g0 = g2;
+    }
+    reduce_store(red, acc, wave, lane, C, ldc, M, N, m0, n0);
+}
+
+}  // namespace sk
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 template <int BM, int BN, bool TA, bool TB>
@@ -590,7 +807,61 @@ hipError_t launch_bf16(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
+template <typename T, bool TA, bool TB, bool VA, bool VB>
+void launch_sk_layout(const Problem &p, uint32_t blocks, int64_t tm, int64_t tn, hipStream_t s)
+{
+    const auto *A = static_cast<const T *>(p.A);
+    const auto *B = static_cast<const T *>(p.B);
+    if constexpr (sizeof(T) == 4)
+        hipLaunchKernelGGL((sk::f32_kernel<TA, TB, VA, VB>), dim3(blocks), dim3(kThreads), 0, s,
+                           p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc,
+                           p.batch, tm, tn);
+    else
+        hipLaunchKernelGGL((sk::bf16_kernel<TA, TB, VA, VB>), dim3(blocks), dim3(kThreads), 0, s,
+                           p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc,
+                           p.batch, tm, tn);
+}
+
+// The vector load exists only along a stored row of K (A as written, B
+// transposed); it needs 16-byte aligned rows and K a multiple of the vector.
+template <typename T>
+hipError_t launch_splitk(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + 31) / 32, tn = (p.N + 31) / 32;
+    if (tm * tn * p.batch > kMaxBlocks) return hipErrorInvalidValue;
+    const uint32_t blocks = static_cast<uint32_t>(tm * tn * p.batch);
+    constexpr int64_t v = 16 / sizeof(T);
+    const bool kv = p.K % v == 0;
+    const bool va = !p.ta && kv && aligned16(p.A) && p.lda % v == 0 && p.sa % v == 0;
+    const bool vb = p.tb && kv && aligned16(p.B) && p.ldb % v == 0 && p.sb % v == 0;
+    if (p.ta && p.tb) {
+        if (vb) launch_sk_layout<T, true, true, false, true>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, true, true, false, false>(p, blocks, tm, tn, s);
+    } else if (p.ta) {
+        launch_sk_layout<T, true, false, false, false>(p, blocks, tm, tn, s);
+    } else if (p.tb) {
+        if (va && vb) launch_sk_layout<T, false, true, true, true>(p, blocks, tm, tn, s);
+        else if (va) launch_sk_layout<T, false, true, true, false>(p, blocks, tm, tn, s);
+        else if (vb) launch_sk_layout<T, false, true, false, true>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, false, true, false, false>(p, blocks, tm, tn, s);
+    } else {
+        if (va) launch_sk_layout<T, false, false, true, false>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, false, false, false, false>(p, blocks, tm, tn, s);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_mfma_f32_batched_splitk(const Problem &p, hipStream_t s)
+{
+    return launch_splitk<float>(p, s);
+}
+
+hipError_t launch_mfma_bf16_batched_splitk(const Problem &p, hipStream_t s)
+{
+    return launch_splitk<uint16_t>(p, s);
+}
 
 hipError_t launch_mfma_f32_batched(const Problem &p, hipStream_t s)
 {

@@ -197,8 +197,8 @@ def test_dispatch_layout_cases():
 
 # ---- transposed factors and strided batches (pure host planning) ------------
 
-GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128"),
-                 g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128")}
+GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk"),
+                 g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk")}
 
 
 @pytest.mark.parametrize("dtype", [g.F32, g.BF16])
@@ -219,11 +219,16 @@ def test_plan_batched_plain_problem_is_the_plain_plan(dtype):
 
 def test_plan_batched_tile_choice():
     # many products of 128 x 128 tiles: the small tile fills the CUs; a few
-    # large products: the 256 x 256 tile
+    # large products: the 256 x 256 tile; a small output over a long K (a
+    # weight gradient): split-K
     small = g.gemm_plan_batched(g.F32, 0, 1, 256, 256, 64, 384)
     large = g.gemm_plan_batched(g.F32, 1, 0, 8192, 8192, 8192, 1)
     assert g.gemm_kernel_name(large) == "mfma_f32_batched"
-    assert g.gemm_kernel_name(small) in GENERAL_NAMES[g.F32]
+    assert g.gemm_kernel_name(small) == "mfma_f32_batched128"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 384, 1152, 16384, 1)) == \
+        "mfma_f32_batched_splitk"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 16384, 1)) == \
+        "mfma_bf16_batched128"
 
 
 @pytest.mark.parametrize("dtype", [g.F32, g.BF16])

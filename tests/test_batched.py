@@ -26,8 +26,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 GATE = oracle.GATE
 TRANS = [(False, False), (True, False), (False, True), (True, True)]
-GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128"],
-           "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128"]}
+GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk"],
+           "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk"]}
 
 
 def say(msg):
@@ -92,7 +92,7 @@ def exact_case(dtype, kernel, ta, tb, M, N, K, batch, seed):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("kernel_idx", [0, 1])
+@pytest.mark.parametrize("kernel_idx", [0, 1, 2])
 @pytest.mark.parametrize("ta,tb", TRANS)
 def test_small_integer_exact(dtype, kernel_idx, ta, tb):
     kernel = GENERAL[dtype][kernel_idx]

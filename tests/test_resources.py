@@ -30,6 +30,12 @@ OCCUPANCY_BUDGET = {
     "mfma_f32_direct_kernelILi128ELi64E": 3,
     "mfma_f32_direct_kernelILi64ELi64E": 5,
     "mfma_f32_splitk_kernel": 2,
+    "3f3214batched_kernelILi256ELi256E": 1,
+    "3f3214batched_kernelILi128ELi128E": 2,
+    "2bf14batched_kernelILi256ELi256E": 1,
+    "2bf14batched_kernelILi128ELi128E": 2,
+    "2sk10f32_kernel": 2,
+    "2sk11bf16_kernel": 2,
     "valu_f32_kernel": 3,
     "skinny_kernel": 1,
     "naive_kernel": 8,
@@ -82,7 +88,8 @@ def test_occupancy_budget(kernels):
 def test_matrix_core_accumulators_live_in_agprs(kernels):
     # the 256 x 256 tiles keep all 256 accumulators per lane in AGPRs
     big = ("mfma_f32_kernelILi256ELi256E", "mfma_f32_direct_kernelILi256ELi256E",
-           "mfma_bf16_kernel", "mfma_bf16_direct_kernelILi256ELi256E")
+           "mfma_bf16_kernel", "mfma_bf16_direct_kernelILi256ELi256E",
+           "3f3214batched_kernelILi256ELi256E", "2bf14batched_kernelILi256ELi256E")
     seen = 0
     for name, r in kernels.items():
         if any(f in name for f in big):
