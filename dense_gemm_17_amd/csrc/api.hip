@@ -32,14 +32,14 @@ const KernelInfo kKernels[] = {
     {"skinny_f32", kF32, launch_skinny_f32, supports_skinny},
     {"skinny_bf16", kBF16, launch_skinny_bf16, supports_skinny},
     {"valu_f32", kF32, launch_valu_f32, supports_any},
-    {"mfma_f32_direct", kF32, launch_mfma_f32_direct, supports_mfma_f32_direct},
-    {"mfma_f32_direct128", kF32, launch_mfma_f32_direct128, supports_mfma_f32_direct},
-    {"mfma_f32_narrow128", kF32, launch_mfma_f32_narrow128, supports_mfma_f32_narrow},
-    {"mfma_f32_direct128x64", kF32, launch_mfma_f32_direct128x64, supports_mfma_f32_direct},
+    {"mfma_f32_direct", kF32, launch_mfma_f32_direct, supports_mfma_f32_direct, true},
+    {"mfma_f32_direct128", kF32, launch_mfma_f32_direct128, supports_mfma_f32_direct, true},
+    {"mfma_f32_narrow128", kF32, launch_mfma_f32_narrow128, supports_mfma_f32_narrow, true},
+    {"mfma_f32_direct128x64", kF32, launch_mfma_f32_direct128x64, supports_mfma_f32_direct, true},
     {"mfma_bf16_direct128", kBF16, launch_mfma_bf16_direct128, supports_mfma_bf16_direct},
-    {"mfma_f32_narrow128x64", kF32, launch_mfma_f32_narrow128x64, supports_mfma_f32_narrow},
-    {"mfma_f32_direct64", kF32, launch_mfma_f32_direct64, supports_mfma_f32_direct},
-    {"mfma_f32_narrow64", kF32, launch_mfma_f32_narrow64, supports_mfma_f32_narrow},
+    {"mfma_f32_narrow128x64", kF32, launch_mfma_f32_narrow128x64, supports_mfma_f32_narrow, true},
+    {"mfma_f32_direct64", kF32, launch_mfma_f32_direct64, supports_mfma_f32_direct, true},
+    {"mfma_f32_narrow64", kF32, launch_mfma_f32_narrow64, supports_mfma_f32_narrow, true},
     {"mfma_f32_splitk", kF32, launch_mfma_f32_splitk, supports_any},
     {"mfma_f32_batched", kF32, launch_mfma_f32_batched, supports_any, true},
     {"mfma_f32_batched128", kF32, launch_mfma_f32_batched128, supports_any, true},
@@ -183,6 +183,8 @@ int64_t tiled_cost(const Problem &p, int64_t bm, int64_t bn, int64_t per_cu, int
 // family.  Small outputs with a long K go to its split-K kernel; otherwise
 // 256 x 256 or 128 x 128 tiles by the same wave-count estimate as above,
 // over the tiles of every product.
+int select_f32_lds(const Problem &p);
+
 int select_general(const Problem &p)
 {
     // fp32 with fewer 128 x 128 tiles over all products than CUs (weight
@@ -194,6 +196,12 @@ int select_general(const Problem &p)
     // the 128 x 128 tile (23 vs 63 TFLOP/s on the same shape).
     if (p.dtype == kF32 && ceil_div(p.M, 128) * ceil_div(p.N, 128) * p.batch < kCUs)
         return kernel_id("mfma_f32_batched_splitk");
+    // fp32 layouts the LDS-direct tiles take (16-byte aligned rows, K % 16
+    // == 0; untransposed factors also through the narrow-load tiles).
+    if (p.dtype == kF32) {
+        const int lds = select_f32_lds(p);
+        if (lds >= 0) return lds;
+    }
     if (p.dtype == kBF16)
         return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
                    ? kernel_id("mfma_bf16_batched")
@@ -202,6 +210,8 @@ int select_general(const Problem &p)
                ? kernel_id("mfma_f32_batched")
                : kernel_id("mfma_f32_batched128");
 }
+
+int select_f32_lds(const Problem &p);
 
 int select_kernel(const Problem &p)
 {
@@ -223,6 +233,16 @@ int select_kernel(const Problem &p)
     // 5.4 vs 7.8 us; 512 x 512 x 4096: 47.7 vs 73.7; 640 x 640 x 2048, 100
     // tiles: 42.2 vs 39.0, so the larger tiles win from there on).
     if ((p.M + 63) / 64 * ((p.N + 63) / 64) <= kCUs / 4) return kernel_id("mfma_f32_splitk");
+    const int lds = select_f32_lds(p);
+    if (lds >= 0) return lds;
+    if (tiled_cost(p, 256, 256, 1, 700) <= tiled_cost(p, 128, 128, 2, 670))
+        return kernel_id("mfma_f32");
+    return kernel_id("mfma_f32_128");
+}
+
+// The fp32 LDS-direct and narrow-load tiles for p, or -1 if neither takes it.
+int select_f32_lds(const Problem &p)
+{
     // Efficiencies (per mille of peak with every CU busy) measured at 4096^3
     // and 8192^3; 64 x 64 tiles (five per CU) only pay where the larger
     // tiles would leave CUs idle (a few hundred tiles or fewer).
@@ -247,9 +267,7 @@ int select_kernel(const Problem &p)
         if (c64 <= c6464) return kernel_id("mfma_f32_narrow128x64");
         return kernel_id("mfma_f32_narrow64");
     }
-    if (tiled_cost(p, 256, 256, 1, 700) <= tiled_cost(p, 128, 128, 2, 670))
-        return kernel_id("mfma_f32");
-    return kernel_id("mfma_f32_128");
+    return -1;
 }
 
 // Table choice, overridden by gemm_force_kernel for calls of the forced

@@ -50,23 +50,6 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int kGroup = 4;   // tile-rows per group in the tile order
 
-struct BatchTile {
-    int64_t b, tm, tn;
-};
-
-// (product, tile) of this work-group: the XCD remap runs over all
-// tiles x batch work-groups, then the linear index splits into the product
-// and the tile inside it (grouped order within the product).
-__device__ __forceinline__ BatchTile map_batch_tile(int64_t tiles_m, int64_t tiles_n,
-                                                    int64_t batch)
-{
-    const int64_t tiles = tiles_m * tiles_n;
-    const int64_t lin = xcd_remap(blockIdx.x, tiles * batch);
-    const int64_t b = lin / tiles;
-    const TileCoord t = grouped_tile(lin - b * tiles, tiles_m, tiles_n, kGroup);
-    return BatchTile{b, t.tm, t.tn};
-}
-
 template <int W> struct VecF;
 template <> struct VecF<2> { typedef f32x2 T; };
 template <> struct VecF<4> { typedef f32x4 T; };
@@ -247,7 +230,7 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A
     __shared__ __attribute__((aligned(16))) float As[2][BM * BK];
     __shared__ __attribute__((aligned(16))) float Bs[2][BK * BN];
 
-    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch);
+    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
     A += t.b * sa;
     B += t.b * sb;
     C += t.b * sc;
@@ -448,7 +431,7 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BK * BN];
 
-    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch);
+    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
     A += t.b * sa;
     B += t.b * sb;
     C += t.b * sc;
@@ -584,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
 {
     constexpr int kU = 8;
     __shared__ float red[4 * 32 * kPad];
-    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch);
+    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
     A += t.b * sa;
     B += t.b * sb;
     C += t.b * sc;
@@ -668,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void bf16_kernel(
 {
     constexpr int kU = 4;
     __shared__ float red[4 * 32 * kPad];
-    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch);
+    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
     A += t.b * sa;
     B += t.b * sb;
     C += t.b * sc;

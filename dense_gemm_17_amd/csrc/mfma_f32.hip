@@ -39,6 +39,8 @@
 // 4-byte loads for any layout) are one template: global -> LDS without registers, a four-stage
 // LDS ring, fragments read one K group ahead, one barrier per tile; they
 // are what the dispatch table runs wherever they apply.
+#include <type_traits>
+
 #include "gemm_internal.h"
 #include "tile_map.h"
 
@@ -317,8 +319,15 @@ template <> struct DVec<4> { typedef f32x4 T; };
 
 // kW: bytes per lane of one LDS-direct load (16 for the aligned kernels, 4
 // for the narrow one); one wave's load fills 64 kW bytes of LDS.
-template <int BM, int BN, int kW>
+//
+// TA / TB: A stored K x M (a transposed factor) / B stored N x K.  A factor
+// is staged in LDS in its stored orientation: rows of K (A as written, B
+// transposed) as 16-float rows read 16 bytes per lane, rows of M or N (A
+// transposed, B as written) as 16 rows read 4 bytes per lane, a vector of
+// one value per 32 x 32 block (the blocks interleaved over the columns).
+template <int BM, int BN, int kW, bool TA = false, bool TB = false>
 struct DTile {
+    static_assert(kW == 16 || (!TA && !TB), "transposed factors take the 16-byte loads");
     static constexpr int kMB = BM / 64, kNB = BN / 64;          // blocks per wave
     static constexpr int kAInst = BM * DBK * 4 / (64 * kW) / 4; // LDS-direct loads per wave per tile (A)
     static constexpr int kBInst = DBK * BN * 4 / (64 * kW) / 4; // ... (B)
@@ -326,7 +335,7 @@ struct DTile {
     static constexpr int kStageFloats = BM * DBK + DBK * BN;
     static constexpr int kBChunksPerRow = BN / 4;
     static constexpr int kQ = 4 * kMB * kNB;                    // MFMAs per 8-wide K group
-    static constexpr int kReads = kMB + 4;                      // fragment reads per group
+    static constexpr int kReads = (TA ? 4 : kMB) + (TB ? kNB : 4);   // fragment reads per group
     // The reads of the next group go out after MFMAs 0, 2, 4, .. (after
     // every MFMA when there are fewer than two per read); the loads of a
     // later tile after MFMAs kLoadQ0, kLoadQ0 + kLoadStep, ...
@@ -346,7 +355,9 @@ struct DTile {
     // With one 32-column block per wave, B is read 4 bytes per lane and the
     // two half-waves read rows 4 apart: 16-byte chunks of B rows are
     // XOR-permuted by 8 * bit 2 of the row so those rows use different banks.
-    static constexpr bool kBSwz = kNB == 1;
+    static constexpr bool kBSwz = !TB && kNB == 1;
+    // The same for a transposed A read 4 bytes per lane (one block per wave).
+    static constexpr bool kASwz = TA && kMB == 1;
     static_assert((kReads <= kQ || kSpreadLoads) &&
                       (kSpreadLoads || kLoadQ0 + kLoadStep * (kPerTile - 1) < kQ),
                   "slots");
@@ -404,15 +415,15 @@ __device__ __forceinline__ void wait_lds_vm_barrier()
 }
 
 // Everything a wave needs to address its loads and reads.
-template <int BM, int BN, int kW>
+template <int BM, int BN, int kW, bool TA = false, bool TB = false>
 struct DCtx {
-    using T = DTile<BM, BN, kW>;
+    using T = DTile<BM, BN, kW, TA, TB>;
     uint32_t a_voff[T::kAInst], b_voff[T::kBInst];   // lane offsets (bytes) of each load
     const char *abase, *bbase;                       // tile (k = 0) bases, wave-uniform
     int64_t a_kstride, b_kstride;                    // bytes per K step
     uint32_t lds0;                                   // LDS byte address of stage 0
     int wave;
-    uint32_t rdA0, rdA1, rdB;                        // lane parts of the read offsets in a stage
+    uint32_t rdA0, rdA1, rdB, rdB1;                  // lane parts of the read offsets in a stage
 };
 
 // The scalar-base loads need their base in scalar registers; where the
@@ -436,11 +447,11 @@ __device__ __forceinline__ void lds_direct_load(uint32_t voff, const void *sbase
     else lds_direct_load4(voff, sbase, m0v);
 }
 
-template <int BM, int BN, int kW>
-__device__ __forceinline__ void load_one(const DCtx<BM, BN, kW> &x, uint32_t stage_lds, int64_t kt,
-                                         int l)
+template <int BM, int BN, int kW, bool TA, bool TB>
+__device__ __forceinline__ void load_one(const DCtx<BM, BN, kW, TA, TB> &x, uint32_t stage_lds,
+                                         int64_t kt, int l)
 {
-    using T = DTile<BM, BN, kW>;
+    using T = DTile<BM, BN, kW, TA, TB>;
     if (l < T::kAInst)
         lds_direct_load<kW>(x.a_voff[l], x.abase + kt * x.a_kstride,
                             stage_lds + (x.wave * T::kAInst + l) * 64 * kW);
@@ -449,47 +460,68 @@ __device__ __forceinline__ void load_one(const DCtx<BM, BN, kW> &x, uint32_t sta
                             stage_lds + BM * DBK * 4 + (x.wave * T::kBInst + l - T::kAInst) * 64 * kW);
 }
 
-// Fragments of one 8-wide K group for a wave's MB x NB blocks: a[mb] holds
-// k = 4h .. 4h+3 of row c of block mb; b[j] holds, for k-step j, the NB
-// columns NB c .. NB c + NB - 1 (one per block nb).
-template <int BM, int BN>
+// Fragments of one 8-wide K group for a wave's MB x NB blocks.  A as
+// written: a[mb] holds k = 4h .. 4h+3 of row c of block mb; transposed: a[j]
+// holds, for k-step j, the MB rows MB c .. MB c + MB - 1 (one per block).  B
+// as written: b[j] holds, for k-step j, the NB columns NB c .. NB c + NB - 1
+// (one per block nb); transposed: b[nb] holds k = 4h .. 4h+3 of column c of
+// block nb.
+template <int BM, int BN, bool TA = false, bool TB = false>
 struct FragG {
-    using T = DTile<BM, BN, 16>;
-    using BV = typename DVec<T::kNB>::T;
-    f32x4 a[T::kMB];
-    BV b[4];
+    static constexpr int kMB = BM / 64, kNB = BN / 64;
+    using AV = typename DVec<kMB>::T;
+    using BV = typename DVec<kNB>::T;
+    std::conditional_t<TA, AV, f32x4> a[TA ? 4 : kMB];
+    std::conditional_t<TB, f32x4, BV> b[TB ? kNB : 4];
+    __device__ __forceinline__ float av(int mb, int j) const
+    {
+        if constexpr (TA) return a[j][mb];
+        else return a[mb][j];
+    }
+    __device__ __forceinline__ float bv(int j, int nb) const
+    {
+        if constexpr (TB) return b[nb][j];
+        else return b[j][nb];
+    }
 };
 
-template <int BM, int BN, int kW>
-__device__ __forceinline__ void read_one(FragG<BM, BN> &f, const float *stage,
-                                         const DCtx<BM, BN, kW> &x, int g, int idx)
+template <int BM, int BN, int kW, bool TA, bool TB>
+__device__ __forceinline__ void read_one(FragG<BM, BN, TA, TB> &f, const float *stage,
+                                         const DCtx<BM, BN, kW, TA, TB> &x, int g, int idx)
 {
-    using T = DTile<BM, BN, kW>;
-    using BV = typename DVec<T::kNB>::T;
+    using F = FragG<BM, BN, TA, TB>;
+    constexpr int nA = TA ? 4 : F::kMB;
     const char *st = reinterpret_cast<const char *>(stage);
-    if (idx < T::kMB)
-        f.a[idx] = *reinterpret_cast<const f32x4 *>(st + (g ? x.rdA1 : x.rdA0) + idx * 2048);
-    else
-        f.b[idx - T::kMB] =
-            *reinterpret_cast<const BV *>(st + x.rdB + (8 * g + (idx - T::kMB)) * (BN * 4));
+    if (idx < nA) {
+        if constexpr (TA)
+            f.a[idx] = *reinterpret_cast<const typename F::AV *>(st + x.rdA0 + (8 * g + idx) * (BM * 4));
+        else
+            f.a[idx] = *reinterpret_cast<const f32x4 *>(st + (g ? x.rdA1 : x.rdA0) + idx * 2048);
+    } else {
+        const int i = idx - nA;
+        if constexpr (TB)
+            f.b[i] = *reinterpret_cast<const f32x4 *>(st + (g ? x.rdB1 : x.rdB) + i * 2048);
+        else
+            f.b[i] = *reinterpret_cast<const typename F::BV *>(st + x.rdB + (8 * g + i) * (BN * 4));
+    }
 }
 
 // The MFMAs of group `cur`: the reads of `nxt` go out after MFMAs 0, 2, ..
 // (well ahead of their use), and (if loads) this wave's LDS-direct loads
 // of a later tile after the load slots.  sched_barrier(0) pins that order.
-template <int BM, int BN, int kW>
+template <int BM, int BN, int kW, bool TA, bool TB>
 __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
-                                               const FragG<BM, BN> &cur, FragG<BM, BN> &nxt,
-                                               const float *rstage, const DCtx<BM, BN, kW> &x,
-                                               int g_next, uint32_t lstage, int64_t kload,
-                                               bool loads)
+                                               const FragG<BM, BN, TA, TB> &cur,
+                                               FragG<BM, BN, TA, TB> &nxt, const float *rstage,
+                                               const DCtx<BM, BN, kW, TA, TB> &x, int g_next,
+                                               uint32_t lstage, int64_t kload, bool loads)
 {
-    using T = DTile<BM, BN, kW>;
+    using T = DTile<BM, BN, kW, TA, TB>;
 #pragma unroll
     for (int q = 0; q < T::kQ; ++q) {
         const int j = q / (T::kMB * T::kNB), mb = (q / T::kNB) % T::kMB, nb = q % T::kNB;
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.a[mb][j], cur.b[j][nb], acc[mb][nb],
-                                                            0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.av(mb, j), cur.bv(j, nb),
+                                                            acc[mb][nb], 0, 0, 0);
         const bool rd = T::kReadEveryOther ? (q < 2 * T::kReads && (q & 1) == 0) : q < T::kReads;
         if constexpr (T::kSpreadLoads) {
             __builtin_amdgcn_sched_barrier(0);
@@ -530,7 +562,7 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
 // already hold four consecutive columns, keeps its direct 16-byte stores
 // (the staging cost it 1.3%).  Needs C 16-byte aligned with ldc and N
 // multiples of 4.
-template <int BM, int BN, int kW>
+template <int BM, int BN, int kW, bool TA = false, bool TB = false>
 __device__ __forceinline__ void store_c_rows_f32(const f32x16 (&acc)[BM / 64][BN / 64],
                                                  float *lf, float *__restrict__ C, int64_t ldc,
                                                  int64_t M, int64_t N, int64_t m0, int64_t n0,
@@ -549,10 +581,11 @@ __device__ __forceinline__ void store_c_rows_f32(const f32x16 (&acc)[BM / 64][BN
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int col = wn * WN + NB * c + nb;
+            const int col = TB ? wn * WN + nb * 32 + c : wn * WN + NB * c + nb;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int lrow = wm * kHalf + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+                const int lrow = wm * kHalf + (TA ? MB * i + mb : mb * 32 + i);
                 const int swz = kChunks >= 16 ? (((lrow >> 2) & 1) << 3) : 0;
                 lf[lrow * BN + (((col >> 2) ^ swz) << 2) + (col & 3)] = acc[mb][nb][r];
             }
@@ -569,37 +602,53 @@ __device__ __forceinline__ void store_c_rows_f32(const f32x16 (&acc)[BM / 64][BN
     }
 }
 
-template <int BM, int BN, int kW, bool kRowsC = false>
+// A batch of products (stride_a, stride_b, stride_c elements apart; batch
+// = 1 for a single product) runs as one grid of (product, tile) work-groups.
+template <int BM, int BN, int kW, bool kRowsC = false, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DTile<BM, BN, kW>::kPerCU, DTile<BM, BN, kW>::kPerCU)))
 void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A,
                             int64_t lda, const float *__restrict__ B, int64_t ldb,
                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
-                            int cvec)
+                            int cvec, int64_t sa, int64_t sb, int64_t sc, int64_t batch)
 {
-    using T = DTile<BM, BN, kW>;
+    using T = DTile<BM, BN, kW, TA, TB>;
     constexpr int MB = T::kMB, NB = T::kNB, WM = BM / 2, WN = BN / 2;
     __shared__ __attribute__((aligned(1024))) float lds[DSTAGES * T::kStageFloats];
 
-    const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
+    A += t.b * sa;
+    B += t.b * sb;
+    C += t.b * sc;
     const int64_t m0 = t.tm * BM, n0 = t.tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, c = lane & 31;
 
-    DCtx<BM, BN, kW> x;
+    DCtx<BM, BN, kW, TA, TB> x;
     x.wave = wave;
     x.lds0 = lds_offset(lds);
-    x.abase = reinterpret_cast<const char *>(A + m0 * lda);
-    x.bbase = reinterpret_cast<const char *>(B + n0);
-    x.a_kstride = DBK * 4;
-    x.b_kstride = DBK * ldb * 4;
+    // Rows of K start at the tile's first row and step 16 floats per tile;
+    // rows of M or N start at the tile's first column and step 16 rows.
+    x.abase = reinterpret_cast<const char *>(TA ? A + m0 : A + m0 * lda);
+    x.bbase = reinterpret_cast<const char *>(TB ? B + n0 * ldb : B + n0);
+    x.a_kstride = TA ? DBK * lda * 4 : DBK * 4;
+    x.b_kstride = TB ? DBK * 4 : DBK * ldb * 4;
     // p: the kW-byte unit of the stage's A (or B) region this lane fills;
     // the element(s) it holds follow from the layout.
 #pragma unroll
     for (int i = 0; i < T::kAInst; ++i) {
         const int p = (wave * T::kAInst + i) * 64 + lane;
+        if constexpr (TA) {
+            // 16 rows of BM floats: row k, chunk slot p % (BM / 4); columns
+            // past M re-fetch the last full chunk (M % 4 == 0 here)
+            const int row = p / (BM / 4), slot = p % (BM / 4);
+            const int lc = T::kASwz ? slot ^ b_swz8(row) : slot;
+            const int64_t col = (m0 + 4 * lc < M) ? 4 * lc : M - 4 - m0;
+            x.a_voff[i] = static_cast<uint32_t>((row * lda + col) * 4);
+            continue;
+        }
         int row, kk;
         if constexpr (kW == 16) {
             row = p >> 2;
@@ -614,6 +663,14 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
 #pragma unroll
     for (int i = 0; i < T::kBInst; ++i) {
         const int p = (wave * T::kBInst + i) * 64 + lane;
+        if constexpr (TB) {
+            // BN rows of 16 floats, laid out as A's: row n, chunk slot p & 3
+            const int row = p >> 2;
+            const int kk = 4 * ((p & 3) ^ a_swz4(row));
+            const int64_t r = (n0 + row < N) ? row : N - 1 - n0;
+            x.b_voff[i] = static_cast<uint32_t>((r * ldb + kk) * 4);
+            continue;
+        }
         int64_t row, col;
         if constexpr (kW == 16) {
             row = p / T::kBChunksPerRow;
@@ -630,9 +687,24 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     }
     // Rows this lane reads are wm*WM + 32*idx + c: their swizzle is a_swz4(c).
     const int swz = a_swz4(c);
-    x.rdA0 = (wm * WM + c) * DBK * 4 + (((0 + h) ^ swz) << 4);
-    x.rdA1 = (wm * WM + c) * DBK * 4 + (((2 + h) ^ swz) << 4);
-    if constexpr (T::kBSwz) {
+    if constexpr (TA) {
+        // k rows 4h + 8g + j, columns MB c .. MB c + MB - 1 of the wave's rows
+        if constexpr (T::kASwz) {
+            const int m = wm * WM + c;
+            x.rdA0 = 4 * h * (BM * 4) + ((((m >> 2) ^ (h << 3)) << 2) + (m & 3)) * 4;
+        } else {
+            x.rdA0 = 4 * h * (BM * 4) + (wm * WM + MB * c) * 4;
+        }
+        x.rdA1 = x.rdA0;
+    } else {
+        x.rdA0 = (wm * WM + c) * DBK * 4 + (((0 + h) ^ swz) << 4);
+        x.rdA1 = (wm * WM + c) * DBK * 4 + (((2 + h) ^ swz) << 4);
+    }
+    if constexpr (TB) {
+        // rows wn*WN + 32*idx + c of the stage's B region, as for A
+        x.rdB = BM * DBK * 4 + (wn * WN + c) * DBK * 4 + (((0 + h) ^ swz) << 4);
+        x.rdB1 = BM * DBK * 4 + (wn * WN + c) * DBK * 4 + (((2 + h) ^ swz) << 4);
+    } else if constexpr (T::kBSwz) {
         // rows this lane reads are 4h + 8g + j: bit 2 is h
         const int n = wn * WN + c;
         x.rdB = BM * DBK * 4 + 4 * h * (BN * 4) + ((((n >> 2) ^ (h << 3)) << 2) + (n & 3)) * 4;
@@ -655,7 +727,7 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     };
     auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
 
-    FragG<BM, BN> f0, f1;
+    FragG<BM, BN, TA, TB> f0, f1;
     // The aligned kernels take K % 16 == 0 and K > 0 only; the narrow one
     // may have no full tile (K < 16), then only the tail below runs.
     if (kW == 16 || ktiles > 0) {
@@ -717,19 +789,28 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     }
 
     if constexpr (kRowsC) {
-        store_c_rows_f32<BM, BN, kW>(acc, lds, C, ldc, M, N, m0, n0, wm, wn, lane);
+        store_c_rows_f32<BM, BN, kW, TA, TB>(acc, lds, C, ldc, M, N, m0, n0, wm, wn, lane);
         return;
     }
-    // Epilogue: register r of block (mb, nb) in lane (h, c) is C row
-    // 8*(r/4) + 4*h + r%4 of block mb and column NB*c + nb of the wave's piece.
-    const int64_t col = n0 + wn * WN + NB * c;
+    // Epilogue: register r of block (mb, nb) in lane (h, c) is the MFMA
+    // output row i = 8*(r/4) + 4*h + r%4, which is row 32*mb + i of the
+    // wave's piece (MB*i + mb with a transposed A), and column NB*c + nb
+    // (32*nb + c with a transposed B).
+    const int64_t col = n0 + wn * WN + (TB ? c : NB * c);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm * WM + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+            const int64_t row = m0 + wm * WM + (TA ? MB * i + mb : mb * 32 + i);
             if (row >= M) continue;
             float *p = C + row * ldc + col;
+            if constexpr (TB) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    if (col + 32 * nb < N) store_c_stream(p + 32 * nb, acc[mb][nb][r]);
+                continue;
+            }
             typename DVec<NB>::T v;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) v[nb] = acc[mb][nb][r];
@@ -756,42 +837,64 @@ bool supports_mfma_f32_direct(const Problem &p)
 {
     const auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     // Lane offsets of the scalar-base loads are 32-bit byte offsets within a
-    // 256-row panel of A and a 16-row panel of B.
-    return p.K % 16 == 0 && p.N % 4 == 0 && p.lda % 4 == 0 && p.ldb % 4 == 0 && al(p.A) &&
-           al(p.B) && p.lda < (int64_t(1) << 22) && p.ldb < (int64_t(1) << 26);
+    // panel of up to 256 rows of K (A as written, B transposed) or 16 rows
+    // of M or N (A transposed, B as written).  A factor stored with rows of
+    // M or N has its last chunk re-fetched past the edge, so that dimension
+    // is a multiple of 4.
+    const int64_t krows = int64_t(1) << 22, mnrows = int64_t(1) << 26;
+    const bool a_ok = p.ta ? p.M % 4 == 0 && p.lda < mnrows : p.lda < krows;
+    const bool b_ok = p.tb ? p.ldb < krows : p.N % 4 == 0 && p.ldb < mnrows;
+    // K > 0: the prologue loads the first tiles unconditionally (K = 0 is
+    // written by the fill kernel, or by another general kernel).
+    return p.K > 0 && p.K % 16 == 0 && p.lda % 4 == 0 && p.ldb % 4 == 0 && p.sa % 4 == 0 &&
+           p.sb % 4 == 0 && al(p.A) && al(p.B) && a_ok && b_ok;
 }
 
-// The narrow variant takes any fp32 layout: 4-byte loads need only element
-// alignment, and the K tail is zero-filled.  Lane offsets are 32-bit byte
-// offsets within a 128-row panel of A and a 16-row panel of B.
+// The narrow variant takes any fp32 layout of untransposed factors: 4-byte
+// loads need only element alignment, and the K tail is zero-filled.  Lane
+// offsets are 32-bit byte offsets within a 128-row panel of A and a 16-row
+// panel of B.
 bool supports_mfma_f32_narrow(const Problem &p)
 {
-    return p.lda < (int64_t(1) << 23) && p.ldb < (int64_t(1) << 26);
+    return !p.ta && !p.tb && p.lda < (int64_t(1) << 23) && p.ldb < (int64_t(1) << 26);
 }
 
 namespace {
+
+template <int BM, int BN, int kW, bool TA, bool TB>
+hipError_t launch_direct_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
+{
+    const int cvec =
+        (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0 && p.sc % 4 == 0;
+    const auto *A = static_cast<const float *>(p.A);
+    const auto *B = static_cast<const float *>(p.B);
+    const dim3 grid(static_cast<uint32_t>(tm * tn * p.batch));
+    if constexpr (BM == 128) {
+        if (cvec && p.N % 4 == 0) {
+            hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN, kW, true, TA, TB>), grid,
+                               dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C,
+                               p.ldc, tm, tn, cvec, p.sa, p.sb, p.sc, p.batch);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN, kW, false, TA, TB>), grid, dim3(kThreads),
+                       0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm, tn, cvec, p.sa,
+                       p.sb, p.sc, p.batch);
+    return hipGetLastError();
+}
 
 template <int BM, int BN, int kW>
 hipError_t launch_direct(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
     const bool ok = kW == 16 ? supports_mfma_f32_direct(p) : supports_mfma_f32_narrow(p);
-    if (tm * tn > kMaxBlocks || !ok) return hipErrorInvalidValue;
-    const int cvec = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0;
-    const auto *A = static_cast<const float *>(p.A);
-    const auto *B = static_cast<const float *>(p.B);
-    if constexpr (BM == 128) {
-        if (cvec && p.N % 4 == 0) {
-            hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN, kW, true>),
-                               dim3(static_cast<uint32_t>(tm * tn)), dim3(kThreads), 0, s, p.M,
-                               p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm, tn, cvec);
-            return hipGetLastError();
-        }
+    if (tm * tn * p.batch > kMaxBlocks || !ok) return hipErrorInvalidValue;
+    if constexpr (kW == 16) {
+        if (p.ta && p.tb) return launch_direct_layout<BM, BN, kW, true, true>(p, s, tm, tn);
+        if (p.ta) return launch_direct_layout<BM, BN, kW, true, false>(p, s, tm, tn);
+        if (p.tb) return launch_direct_layout<BM, BN, kW, false, true>(p, s, tm, tn);
     }
-    hipLaunchKernelGGL((mfma_f32_direct_kernel<BM, BN, kW>), dim3(static_cast<uint32_t>(tm * tn)),
-                       dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm,
-                       tn, cvec);
-    return hipGetLastError();
+    return launch_direct_layout<BM, BN, kW, false, false>(p, s, tm, tn);
 }
 
 }  // namespace

@@ -49,4 +49,23 @@ __device__ __forceinline__ TileCoord map_tile(int64_t tiles_m, int64_t tiles_n, 
     return grouped_tile(xcd_remap(blockIdx.x, n), tiles_m, tiles_n, group);
 }
 
+// A batch of products in one grid: the XCD remap runs over all
+// tiles x batch work-groups, then the linear index splits into the product
+// and the tile inside it (grouped order within the product), so each XCD
+// runs a contiguous range of (product, tile) pairs.  With batch = 1 this is
+// map_tile.
+struct BatchTile {
+    int64_t b, tm, tn;
+};
+
+__device__ __forceinline__ BatchTile map_batch_tile(int64_t tiles_m, int64_t tiles_n,
+                                                    int64_t batch, int64_t group)
+{
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t lin = xcd_remap(blockIdx.x, tiles * batch);
+    const int64_t b = lin / tiles;
+    const TileCoord t = grouped_tile(lin - b * tiles, tiles_m, tiles_n, group);
+    return BatchTile{b, t.tm, t.tn};
+}
+
 }  // namespace mi355gemm

@@ -197,7 +197,11 @@ def test_dispatch_layout_cases():
 
 # ---- transposed factors and strided batches (pure host planning) ------------
 
-GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk"),
+# kernels that take transposed factors or batches
+GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk",
+                         "mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64",
+                         "mfma_f32_direct64", "mfma_f32_narrow128", "mfma_f32_narrow128x64",
+                         "mfma_f32_narrow64"),
                  g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk")}
 
 
@@ -223,8 +227,18 @@ def test_plan_batched_tile_choice():
     # weight gradient): split-K
     small = g.gemm_plan_batched(g.F32, 0, 1, 256, 256, 64, 384)
     large = g.gemm_plan_batched(g.F32, 1, 0, 8192, 8192, 8192, 1)
-    assert g.gemm_kernel_name(large) == "mfma_f32_batched"
-    assert g.gemm_kernel_name(small) == "mfma_f32_batched128"
+    assert g.gemm_kernel_name(large) == "mfma_f32_direct"
+    assert g.gemm_kernel_name(small) in ("mfma_f32_direct128", "mfma_f32_direct128x64",
+                                         "mfma_f32_direct64")
+    # layouts the LDS-direct tiles cannot take go to the general family
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 8190, 8192, 8192, 1)) == \
+        "mfma_f32_batched"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 0, 1, 8192, 8192, 8200, 1)) == \
+        "mfma_f32_batched"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 0, 0, 8192, 8192, 8200, 2)) == \
+        "mfma_f32_narrow128"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 0, 1, 8192, 8192, 8192, 1)) == \
+        "mfma_bf16_batched"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 384, 1152, 16384, 1)) == \
         "mfma_f32_batched_splitk"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 16384, 1)) == \
@@ -269,7 +283,7 @@ def test_plan_batched_rejects_invalid_arguments(dtype):
 
 
 def test_forced_plain_kernel_cannot_take_general_problem():
-    plain = g.kernel_id("mfma_f32_direct")
+    plain = g.kernel_id("mfma_f32_splitk")
     general = g.kernel_id("mfma_f32_batched128")
     try:
         assert g.gemm_force_kernel(plain) == 0

@@ -26,8 +26,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 GATE = oracle.GATE
 TRANS = [(False, False), (True, False), (False, True), (True, True)]
+# kernels that take every layout, and (fp32) the LDS-direct and narrow-load
+# tiles, which take the layouts their loads allow
 GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk"],
            "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk"]}
+LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mfma_f32_direct64",
+           "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64"]
+ALL = {"f32": GENERAL["f32"] + LDS_F32, "bf16": GENERAL["bf16"]}
 
 
 def say(msg):
@@ -62,6 +67,23 @@ def as_oracle(x):
     return workloads.as_numpy_operand(x)
 
 
+def takes(kernel, a, b, out=None):
+    """Does the library accept `kernel` for gemm(a, b, out) (a host plan)?"""
+    M, K, N = a.shape[-2], a.shape[-1], b.shape[-1]
+    batch = a.shape[0] if a.dim() == 3 else (b.shape[0] if b.dim() == 3 else 1)
+    ta, lda = g._layout(a, "a")
+    tb, ldb = g._layout(b, "b")
+    ldc, sc, cp = N, M * N, 3 << 40
+    if out is not None:
+        ldc, sc, cp = out.stride(-2), g._batch_stride(out), out.data_ptr()
+    dt = g.F32 if a.dtype == torch.float32 else g.BF16
+    with Forced(kernel):
+        got = g.gemm_plan_batched(dt, ta, tb, M, N, K, batch, a.data_ptr() or (1 << 40), lda,
+                                  g._batch_stride(a), b.data_ptr() or (2 << 40), ldb,
+                                  g._batch_stride(b), cp, ldc, sc)
+    return got == g.kernel_id(kernel)
+
+
 def run(a, b, kernel=None, out=None):
     with Forced(kernel):
         c = g.gemm(a, b, out=out)
@@ -82,24 +104,31 @@ def exact_case(dtype, kernel, ta, tb, M, N, K, batch, seed):
     A = small_int((batch, M, K), dtype, gen)
     B = small_int((batch, K, N), dtype, gen)
     As, Bs = stored(A, ta), stored(B, tb)
+    a, b = view(As.to(DEV), ta), view(Bs.to(DEV), tb)
+    if not takes(kernel, a, b):
+        return False
     say(f"[batched] exact {dtype} {kernel} ta={ta} tb={tb} M={M} N={N} K={K} batch={batch}")
-    C = run(view(As.to(DEV), ta), view(Bs.to(DEV), tb), kernel)
+    C = run(a, b, kernel)
     Cref, _ = oracle.gemm_batched(as_oracle(As), as_oracle(Bs), ta, tb)
     assert C.shape == (batch, M, N)
     assert np.array_equal(C.cpu().numpy().astype(np.float64), Cref)
-    C2 = run(view(As.to(DEV), ta), view(Bs.to(DEV), tb), kernel)
+    C2 = run(a, b, kernel)
     assert torch.equal(C, C2), "not deterministic"
+    return True
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("kernel_idx", [0, 1, 2])
+@pytest.mark.parametrize("dtype,kernel", [(d, k) for d in ("f32", "bf16") for k in ALL[d]])
 @pytest.mark.parametrize("ta,tb", TRANS)
-def test_small_integer_exact(dtype, kernel_idx, ta, tb):
-    kernel = GENERAL[dtype][kernel_idx]
-    # several tiles in each direction with ragged tails in M, N and K
-    exact_case(dtype, kernel, ta, tb, 300, 270, 100, 3, 41)
-    exact_case(dtype, kernel, ta, tb, 513, 129, 200, 2, 42)
-    exact_case(dtype, kernel, ta, tb, 7, 9, 3, 5, 43)
+def test_small_integer_exact(dtype, kernel, ta, tb):
+    # several tiles in each direction with ragged tails in M, N and K; the
+    # second group has M, N multiples of 4 and K of 16, the layouts the
+    # LDS-direct tiles take (their edges still ragged against the tiles)
+    ran = [exact_case(dtype, kernel, ta, tb, M, N, K, batch, seed)
+           for (M, N, K, batch, seed) in [(300, 270, 100, 3, 41), (513, 129, 200, 2, 42),
+                                          (7, 9, 3, 5, 43), (516, 268, 96, 3, 48),
+                                          (8, 12, 16, 5, 49), (260, 132, 272, 2, 50)]]
+    if not any(ran):
+        pytest.skip(f"{kernel} takes none of these layouts")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -108,15 +137,18 @@ def test_brute_force_tiny_shapes(dtype, ta, tb):
     # every (M, N, K) in {1..6}^3, two products each, every general kernel;
     # one batch holds all shapes' operands so each kernel launches per shape
     gen = workloads.generator(44)
-    for kernel in GENERAL[dtype]:
+    for kernel in ALL[dtype]:
         for M in range(1, 7):
             for N in range(1, 7):
                 for K in range(1, 7):
                     A = small_int((2, M, K), dtype, gen)
                     B = small_int((2, K, N), dtype, gen)
                     As, Bs = stored(A, ta), stored(B, tb)
+                    a, b = view(As.to(DEV), ta), view(Bs.to(DEV), tb)
+                    if not takes(kernel, a, b):
+                        continue
                     with Forced(kernel):
-                        C = g.gemm(view(As.to(DEV), ta), view(Bs.to(DEV), tb))
+                        C = g.gemm(a, b)
                     ref = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float32)
                     assert torch.equal(C.cpu(), ref), (kernel, M, N, K)
         torch.cuda.synchronize()
@@ -125,16 +157,19 @@ def test_brute_force_tiny_shapes(dtype, ta, tb):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("ta,tb", TRANS)
 def test_random_operands_gate(dtype, ta, tb):
-    w = workloads.Workload("batched_rand", 333, 287, 515, dtype)
+    w = workloads.Workload("batched_rand", 332, 288, 512, dtype)
     gen = workloads.generator()
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     A = workloads.draw((4, w.M, w.K), ("uniform", 1.0), gen).to(tdt)
     B = workloads.draw((4, w.K, w.N), ("uniform", 1.0), gen).to(tdt)
     As, Bs = stored(A, ta), stored(B, tb)
     Cref, D = oracle.gemm_batched(as_oracle(As), as_oracle(Bs), ta, tb)
-    for kernel in GENERAL[dtype] + [None]:
+    a, b = view(As.to(DEV), ta), view(Bs.to(DEV), tb)
+    for kernel in ALL[dtype] + [None]:
+        if kernel and not takes(kernel, a, b):
+            continue
         say(f"[batched] gate {dtype} {kernel or 'table'} ta={ta} tb={tb}")
-        C = run(view(As.to(DEV), ta), view(Bs.to(DEV), tb), kernel).cpu().numpy()
+        C = run(a, b, kernel).cpu().numpy()
         e, at, n = oracle.normalized_error(C.reshape(-1, w.N), Cref.reshape(-1, w.N),
                                            D.reshape(-1, w.N))
         say(f"[batched]   e={e:.3e} at={at} n>1e-5={n}")
@@ -166,7 +201,9 @@ def test_unaligned_padded_and_offset_layouts(dtype):
         Ad = Ad.reshape(batch, ar, ac + 3)[:, :, :ac]
         Bd = bbuf_d[1:1 + batch * (br * (bc + 1) + 3)].view(batch, -1)[:, :br * (bc + 1)]
         Bd = Bd.reshape(batch, br, bc + 1)[:, :, :bc]
-        for kernel in GENERAL[dtype]:
+        for kernel in ALL[dtype]:
+            if not takes(kernel, view(Ad, ta), view(Bd, tb)):
+                continue
             say(f"[batched] unaligned {dtype} {kernel} ta={ta} tb={tb}")
             C = run(view(Ad, ta), view(Bd, tb), kernel)
             assert torch.equal(C.cpu(), ref), (kernel, ta, tb)
@@ -175,12 +212,14 @@ def test_unaligned_padded_and_offset_layouts(dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_shared_and_stride_zero_operands(dtype):
     gen = workloads.generator(46)
-    M, N, K, batch = 200, 150, 90, 4
+    M, N, K, batch = 200, 152, 96, 4
     A = small_int((batch, M, K), dtype, gen)
     W = small_int((N, K), dtype, gen)               # a weight stored N x K, used as W^T
     Ad, Wd = A.to(DEV), W.to(DEV)
     ref = (A.to(torch.int64) @ W.to(torch.int64).t()).to(torch.float32)
-    for kernel in GENERAL[dtype] + [None]:
+    for kernel in ALL[dtype] + [None]:
+        if kernel and not takes(kernel, Ad, Wd.t()):
+            continue
         C = run(Ad, Wd.t(), kernel)                 # 2-D factor shared by the batch
         assert torch.equal(C.cpu(), ref)
         C = run(Ad, Wd.t().unsqueeze(0).expand(batch, K, N), kernel)   # batch stride 0
@@ -202,9 +241,11 @@ def test_outputs_side_by_side_and_guard_bands(dtype):
     B = small_int((batch, K, N), dtype, gen)
     ref = (A.to(torch.int64) @ B.to(torch.int64)).to(torch.float32)
     ldc = batch * N + 5
-    for kernel in GENERAL[dtype]:
+    for kernel in ALL[dtype]:
         buf = torch.full((M * ldc + 64,), float("nan"), device=DEV)
         out = buf[32:32 + M * ldc].view(M, ldc)[:, :batch * N].view(M, batch, N).transpose(0, 1)
+        if not takes(kernel, A.to(DEV), B.to(DEV), out):
+            continue
         run(A.to(DEV), B.to(DEV), kernel, out=out)
         got = out.cpu()
         assert torch.equal(got, ref)
@@ -218,10 +259,12 @@ def test_outputs_side_by_side_and_guard_bands(dtype):
 def test_degenerate_batches(dtype):
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     # K = 0: every product is the empty sum
-    for kernel in GENERAL[dtype] + [None]:
+    for kernel in ALL[dtype] + [None]:
         out = torch.full((3, 40, 30), float("nan"), device=DEV)
         a = torch.zeros((3, 0, 40), dtype=tdt, device=DEV).transpose(1, 2)
         b = torch.zeros((3, 0, 30), dtype=tdt, device=DEV)
+        if kernel and not takes(kernel, a, b, out):
+            continue
         run(a, b, kernel, out=out)
         assert torch.equal(out.cpu(), torch.zeros(3, 40, 30))
     # empty batch, M = 0, N = 0: nothing is written
