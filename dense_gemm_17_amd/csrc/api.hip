@@ -28,7 +28,7 @@ const KernelInfo kKernels[] = {
     {"mfma_f32", kF32, launch_mfma_f32, supports_any},
     {"mfma_f32_128", kF32, launch_mfma_f32_128, supports_any},
     {"mfma_bf16", kBF16, launch_mfma_bf16, supports_any},
-    {"mfma_bf16_direct", kBF16, launch_mfma_bf16_direct, supports_mfma_bf16_direct},
+    {"mfma_bf16_direct", kBF16, launch_mfma_bf16_direct, supports_mfma_bf16_direct, true},
     {"skinny_f32", kF32, launch_skinny_f32, supports_skinny},
     {"skinny_bf16", kBF16, launch_skinny_bf16, supports_skinny},
     {"valu_f32", kF32, launch_valu_f32, supports_any},
@@ -36,7 +36,7 @@ const KernelInfo kKernels[] = {
     {"mfma_f32_direct128", kF32, launch_mfma_f32_direct128, supports_mfma_f32_direct, true},
     {"mfma_f32_narrow128", kF32, launch_mfma_f32_narrow128, supports_mfma_f32_narrow, true},
     {"mfma_f32_direct128x64", kF32, launch_mfma_f32_direct128x64, supports_mfma_f32_direct, true},
-    {"mfma_bf16_direct128", kBF16, launch_mfma_bf16_direct128, supports_mfma_bf16_direct},
+    {"mfma_bf16_direct128", kBF16, launch_mfma_bf16_direct128, supports_mfma_bf16_direct, true},
     {"mfma_f32_narrow128x64", kF32, launch_mfma_f32_narrow128x64, supports_mfma_f32_narrow, true},
     {"mfma_f32_direct64", kF32, launch_mfma_f32_direct64, supports_mfma_f32_direct, true},
     {"mfma_f32_narrow64", kF32, launch_mfma_f32_narrow64, supports_mfma_f32_narrow, true},
@@ -202,6 +202,10 @@ int select_general(const Problem &p)
         const int lds = select_f32_lds(p);
         if (lds >= 0) return lds;
     }
+    if (p.dtype == kBF16 && supports_mfma_bf16_direct(p))
+        return tiled_cost(p, 256, 256, 1, 512) <= tiled_cost(p, 128, 128, 2, 410)
+                   ? kernel_id("mfma_bf16_direct")
+                   : kernel_id("mfma_bf16_direct128");
     if (p.dtype == kBF16)
         return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
                    ? kernel_id("mfma_bf16_batched")

@@ -271,7 +271,11 @@ void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restric
 constexpr int DBK = 32;
 constexpr int DSTAGES = 4;
 
-template <int TM, int TN>
+// TA / TB: A stored K x M / B stored N x K.  Each factor is staged in its
+// stored orientation: rows of K (A as written, B transposed) are read with
+// 16-byte reads, rows of M or N (A transposed, B as written) with the
+// transposing reads (two per 32-wide block and slice).
+template <int TM, int TN, bool TA = false, bool TB = false>
 struct DTile {
     static constexpr int kMB = TM / 64, kNB = TN / 64;         // blocks per wave
     static constexpr int kAInst = TM * DBK * 2 / 1024 / 4;     // LDS-direct loads per wave per tile (A)
@@ -280,7 +284,7 @@ struct DTile {
     static constexpr int kStageElems = TM * DBK + DBK * TN;    // bf16 elements per stage
     static constexpr int kBChunks = TN / 8;                    // 16-byte chunks per B row
     static constexpr int kQ = kMB * kNB;                       // MFMAs per 16-wide K slice
-    static constexpr int kReads = kMB + 2 * kNB;               // fragment reads per slice
+    static constexpr int kReads = (TA ? 2 * kMB : kMB) + (TB ? kNB : 2 * kNB);   // reads per slice
     // Work-groups per CU the LDS ring allows: 1 (256 x 256), 2 (128 x 128).
     static constexpr int kPerCU = 160 * 1024 / (DSTAGES * kStageElems * 2);
     static_assert((DSTAGES - 2) * kPerTile <= 63, "vmcnt is six bits");
@@ -307,23 +311,23 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
 }
 
 // Everything a wave needs to address its loads and reads.
-template <int TM, int TN>
+template <int TM, int TN, bool TA = false, bool TB = false>
 struct DCtx {
-    using T = DTile<TM, TN>;
+    using T = DTile<TM, TN, TA, TB>;
     uint32_t a_voff[T::kAInst], b_voff[T::kBInst];   // lane offsets (bytes) of each load
     const char *abase, *bbase;                       // tile (k = 0) bases, wave-uniform
     int64_t a_kstride, b_kstride;                    // bytes per K step
     uint32_t lds0;                                   // LDS byte address of stage 0
     int wave;
-    uint32_t rdA[2];                                 // lane read offsets: A, per K slice
-    uint32_t rdB[T::kNB];                            // lane read offsets: B, per 32-column block
+    uint32_t rdA[TA ? T::kMB : 2];                   // lane read offsets: A, per K slice (per block)
+    uint32_t rdB[TB ? 2 : T::kNB];                   // lane read offsets: B, per block (per K slice)
 };
 
-template <int TM, int TN>
-__device__ __forceinline__ void load_one(const DCtx<TM, TN> &x, uint32_t stage_lds, int64_t kt,
-                                         int l)
+template <int TM, int TN, bool TA, bool TB>
+__device__ __forceinline__ void load_one(const DCtx<TM, TN, TA, TB> &x, uint32_t stage_lds,
+                                         int64_t kt, int l)
 {
-    using T = DTile<TM, TN>;
+    using T = DTile<TM, TN, TA, TB>;
     if (l < T::kAInst)
         lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride,
                           stage_lds + (x.wave * T::kAInst + l) * 1024);
@@ -335,43 +339,70 @@ __device__ __forceinline__ void load_one(const DCtx<TM, TN> &x, uint32_t stage_l
 // Operand fragments of one 16-wide K slice for a wave's MB x NB MFMA blocks:
 // A as one 8-element register quad per 32-row block, B as two 4-element
 // halves (k 0-3 and 4-7 of the lane's eight) per 32-column block.
-template <int TM, int TN>
+template <int TM, int TN, bool TA = false, bool TB = false>
 struct Frag16 {
-    bf16x8 a[DTile<TM, TN>::kMB];
-    bf16x4 blo[DTile<TM, TN>::kNB], bhi[DTile<TM, TN>::kNB];
+    static constexpr int kMB = TM / 64, kNB = TN / 64;
+    // a (A as written) or alo / ahi (transposed); blo / bhi (B as written)
+    // or b (transposed).  The members a layout does not use are never
+    // touched and take no registers.
+    bf16x8 a[kMB];
+    bf16x4 alo[kMB], ahi[kMB];
+    bf16x4 blo[kNB], bhi[kNB];
+    bf16x8 b[kNB];
 };
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
-// Read j of slice s from the stage at `stage`: j < MB is A block j, then B
-// block (j - MB) / 2, lower / upper four k.
-template <int TM, int TN>
-__device__ __forceinline__ void read_one(Frag16<TM, TN> &f, const uint16_t *stage,
-                                         const DCtx<TM, TN> &x, int s, int j)
+__device__ __forceinline__ bf16x4 read_tr4(const char *p)
 {
-    using T = DTile<TM, TN>;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t *)((__attribute__((address_space(3))) char *)(p)));
+}
+
+// Read j of slice s from the stage at `stage`.  A as written: j < MB is A
+// block j (one 16-byte read); transposed: j < 2 MB is A block j / 2, lower /
+// upper four k (transposing reads).  Then B: as written, block (j - nA) / 2,
+// lower / upper four k; transposed, block j - nA (one 16-byte read).
+template <int TM, int TN, bool TA, bool TB>
+__device__ __forceinline__ void read_one(Frag16<TM, TN, TA, TB> &f, const uint16_t *stage,
+                                         const DCtx<TM, TN, TA, TB> &x, int s, int j)
+{
+    using T = DTile<TM, TN, TA, TB>;
+    constexpr int nA = TA ? 2 * T::kMB : T::kMB;
     const char *st = reinterpret_cast<const char *>(stage);
-    if (j < T::kMB) {
-        const u16x8 v = *reinterpret_cast<const u16x8 *>(st + x.rdA[s] + j * 2048);
-        f.a[j] = __builtin_bit_cast(bf16x8, v);
+    if (j < nA) {
+        if constexpr (TA) {
+            const int mb = j >> 1, upper = j & 1;
+            const bf16x4 v = read_tr4(st + x.rdA[mb] + s * (16 * TM * 2) + upper * (4 * TM * 2));
+            if (upper) f.ahi[mb] = v;
+            else f.alo[mb] = v;
+        } else {
+            const u16x8 v = *reinterpret_cast<const u16x8 *>(st + x.rdA[s] + j * 2048);
+            f.a[j] = __builtin_bit_cast(bf16x8, v);
+        }
+    } else if constexpr (TB) {
+        const u16x8 v = *reinterpret_cast<const u16x8 *>(st + x.rdB[s] + (j - nA) * 2048);
+        f.b[j - nA] = __builtin_bit_cast(bf16x8, v);
     } else {
-        const int nb = (j - T::kMB) >> 1, upper = (j - T::kMB) & 1;
-        const char *p = st + x.rdB[nb] + s * (16 * TN * 2) + upper * (4 * TN * 2);
-        const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4_t *)((__attribute__((address_space(3))) char *)(p)));
+        const int nb = (j - nA) >> 1, upper = (j - nA) & 1;
+        const bf16x4 v = read_tr4(st + x.rdB[nb] + s * (16 * TN * 2) + upper * (4 * TN * 2));
         if (upper) f.bhi[nb] = v;
         else f.blo[nb] = v;
     }
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void mfma_one(f32x16 (&acc)[TM / 64][TN / 64], const Frag16<TM, TN> &f,
-                                         int q)
+template <int TM, int TN, bool TA, bool TB>
+__device__ __forceinline__ void mfma_one(f32x16 (&acc)[TM / 64][TN / 64],
+                                         const Frag16<TM, TN, TA, TB> &f, int q)
 {
-    constexpr int NB = DTile<TM, TN>::kNB;
+    constexpr int NB = TN / 64;
     const int mb = q / NB, nb = q % NB;
-    const bf16x8 b = __builtin_shufflevector(f.blo[nb], f.bhi[nb], 0, 1, 2, 3, 4, 5, 6, 7);
-    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], b, acc[mb][nb], 0, 0, 0);
+    bf16x8 a, b;
+    if constexpr (TA) a = __builtin_shufflevector(f.alo[mb], f.ahi[mb], 0, 1, 2, 3, 4, 5, 6, 7);
+    else a = f.a[mb];
+    if constexpr (TB) b = f.b[nb];
+    else b = __builtin_shufflevector(f.blo[nb], f.bhi[nb], 0, 1, 2, 3, 4, 5, 6, 7);
+    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[mb][nb], 0, 0, 0);
 }
 
 // The MFMAs of one slice with the reads of the next slice and (if loads)
@@ -380,13 +411,14 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[TM / 64][TN / 64], const 
 // enough MFMAs (256 x 256), spread evenly otherwise (128 x 128: 4 MFMAs, 6
 // reads, 4 loads).  sched_barrier(0) pins that order so the matrix unit
 // keeps running while reads and loads are in flight.
-template <int TM, int TN>
+template <int TM, int TN, bool TA, bool TB>
 __device__ __forceinline__ void mfma_phase(f32x16 (&acc)[TM / 64][TN / 64],
-                                           const Frag16<TM, TN> &cur, Frag16<TM, TN> &nxt,
-                                           const uint16_t *rstage, const DCtx<TM, TN> &x,
-                                           int s_next, uint32_t lstage, int64_t kload, bool loads)
+                                           const Frag16<TM, TN, TA, TB> &cur,
+                                           Frag16<TM, TN, TA, TB> &nxt, const uint16_t *rstage,
+                                           const DCtx<TM, TN, TA, TB> &x, int s_next,
+                                           uint32_t lstage, int64_t kload, bool loads)
 {
-    using T = DTile<TM, TN>;
+    using T = DTile<TM, TN, TA, TB>;
 #pragma unroll
     for (int q = 0; q < T::kQ; ++q) {
         mfma_one(acc, cur, q);
@@ -481,35 +513,76 @@ __device__ __forceinline__ void store_c_rows(const f32x16 (&acc)[TM / 64][TN / 6
     }
 }
 
-template <int TM, int TN, bool kRowsC>
+__device__ __forceinline__ const void *uniform_ptr(const void *p)
+{
+    const uint64_t v = reinterpret_cast<uintptr_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const void *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v)
+{
+    return static_cast<int64_t>(reinterpret_cast<uintptr_t>(
+        uniform_ptr(reinterpret_cast<const void *>(static_cast<uintptr_t>(v)))));
+}
+
+// kBatch: a batch of products (stride_a, stride_b, stride_c elements apart)
+// as one grid of (product, tile) work-groups; a single product keeps the
+// plain tile map.
+template <int TM, int TN, bool kRowsC, bool TA = false, bool TB = false, bool kBatch = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DTile<TM, TN>::kPerCU, DTile<TM, TN>::kPerCU)))
 void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
                              int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
-                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n)
+                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
+                             int64_t sa, int64_t sb, int64_t sc, int64_t batch)
 {
-    using T = DTile<TM, TN>;
+    using T = DTile<TM, TN, TA, TB>;
     constexpr int MB = T::kMB, NB = T::kNB, WM = TM / 2, WN = TN / 2;
     __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * T::kStageElems];
 
-    const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
-    const int64_t m0 = t.tm * TM, n0 = t.tn * TN;
+    int64_t m0, n0;
+    if constexpr (kBatch) {
+        const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
+        A += t.b * sa;
+        B += t.b * sb;
+        C += t.b * sc;
+        m0 = t.tm * TM;
+        n0 = t.tn * TN;
+    } else {
+        const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+        m0 = t.tm * TM;
+        n0 = t.tn * TN;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, c = lane & 31;
     const int i16 = lane & 15, nhalf = (lane >> 4) & 1;
 
-    DCtx<TM, TN> x;
+    DCtx<TM, TN, TA, TB> x;
     x.wave = wave;
     x.lds0 = lds_offset(lds);
-    x.abase = reinterpret_cast<const char *>(A + m0 * lda);
-    x.bbase = reinterpret_cast<const char *>(B + n0);
-    x.a_kstride = DBK * 2;
-    x.b_kstride = DBK * ldb * 2;
+    // Rows of K start at the tile's first row and step 32 elements per
+    // tile; rows of M or N start at the tile's first column and step 32
+    // rows.  Stated wave-uniform so the per-tile bases stay scalar.
+    x.abase = static_cast<const char *>(uniform_ptr(TA ? A + m0 : A + m0 * lda));
+    x.bbase = static_cast<const char *>(uniform_ptr(TB ? B + n0 * ldb : B + n0));
+    x.a_kstride = uniform_i64(TA ? DBK * lda * 2 : DBK * 2);
+    x.b_kstride = uniform_i64(TB ? DBK * 2 : DBK * ldb * 2);
 #pragma unroll
     for (int i = 0; i < T::kAInst; ++i) {
         const int p = (wave * T::kAInst + i) * 64 + lane;   // LDS chunk this lane fills
+        if constexpr (TA) {
+            // 32 rows of TM elements, laid out as B's; columns past M
+            // re-fetch the last full chunk (M % 8 == 0 here)
+            const int row = p / (TM / 8), slot = p % (TM / 8);
+            const int cc = slot ^ b_swz(row);
+            const int64_t col = (m0 + 8 * cc < M) ? 8 * cc : M - 8 - m0;
+            x.a_voff[i] = static_cast<uint32_t>((row * lda + col) * 2);
+            continue;
+        }
         const int row = p >> 2, slot = p & 3;
         const int cc = slot ^ a_swz<4>(row);
         const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
@@ -518,6 +591,14 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 #pragma unroll
     for (int i = 0; i < T::kBInst; ++i) {
         const int p = (wave * T::kBInst + i) * 64 + lane;
+        if constexpr (TB) {
+            // TN rows of 32 elements, laid out as A's
+            const int row = p >> 2, slot = p & 3;
+            const int cc = slot ^ a_swz<4>(row);
+            const int64_t r = (n0 + row < N) ? row : N - 1 - n0;
+            x.b_voff[i] = static_cast<uint32_t>((r * ldb + 8 * cc) * 2);
+            continue;
+        }
         const int row = p / T::kBChunks, slot = p % T::kBChunks;
         const int cc = slot ^ b_swz(row);
         const int64_t col = (n0 + 8 * cc < N) ? 8 * cc : N - 8 - n0;
@@ -526,16 +607,31 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
     // A rows this lane reads are wm*WM + 32*j + c: their swizzle is a_swz<4>(c)
     // (it depends on bits 2-3 of the row only).
     const int aswz = a_swz<4>(c);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-        x.rdA[s] = (wm * WM + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
     // B rows this lane points at are 16s + 8h + i16/4 (+4): swizzle b_swz(i16/4).
     const int bswz = b_swz(i16 >> 2);
+    if constexpr (TA) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int n = wn * WN + nb * 32 + nhalf * 16 + 4 * (i16 & 3);
-        x.rdB[nb] = TM * DBK * 2 + (8 * h + (i16 >> 2)) * TN * 2 + (((n >> 3) ^ bswz) << 4) +
-                    (n & 7) * 2;
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = wm * WM + mb * 32 + nhalf * 16 + 4 * (i16 & 3);
+            x.rdA[mb] = (8 * h + (i16 >> 2)) * TM * 2 + (((m >> 3) ^ bswz) << 4) + (m & 7) * 2;
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            x.rdA[s] = (wm * WM + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+    }
+    if constexpr (TB) {
+        // rows wn*WN + 32*nb + c of the B region, as for A
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            x.rdB[s] = TM * DBK * 2 + (wn * WN + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int n = wn * WN + nb * 32 + nhalf * 16 + 4 * (i16 & 3);
+            x.rdB[nb] = TM * DBK * 2 + (8 * h + (i16 >> 2)) * TN * 2 + (((n >> 3) ^ bswz) << 4) +
+                        (n & 7) * 2;
+        }
     }
 
     f32x16 acc[MB][NB];
@@ -561,7 +657,7 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
         for (int l = 0; l < T::kPerTile; ++l) load_one(x, lstage(st), kclamp(st), l);
     wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
 
-    Frag16<TM, TN> f0, f1;
+    Frag16<TM, TN, TA, TB> f0, f1;
 #pragma unroll
     for (int j = 0; j < T::kReads; ++j) read_one(f0, stage(0), x, 0, j);
 
@@ -618,30 +714,50 @@ bool supports_mfma_bf16_direct(const Problem &p)
 {
     const auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     // Lane offsets of the scalar-base loads are 32-bit byte offsets within a
-    // 256-row panel of A and a 32-row panel of B.
-    return p.K % 32 == 0 && p.N % 8 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 && al(p.A) &&
-           al(p.B) && p.lda < (int64_t(1) << 23) && p.ldb < (int64_t(1) << 26);
+    // panel of up to 256 rows of K (A as written, B transposed) or 32 rows
+    // of M or N (A transposed, B as written).  A factor stored with rows of
+    // M or N re-fetches its last chunk past the edge, so that dimension is a
+    // multiple of 8.  K > 0: the prologue loads the first tiles
+    // unconditionally.
+    const int64_t krows = int64_t(1) << 23, mnrows = int64_t(1) << 26;
+    const bool a_ok = p.ta ? p.M % 8 == 0 && p.lda < mnrows : p.lda < krows;
+    const bool b_ok = p.tb ? p.ldb < krows : p.N % 8 == 0 && p.ldb < mnrows;
+    return p.K > 0 && p.K % 32 == 0 && p.lda % 8 == 0 && p.ldb % 8 == 0 && p.sa % 8 == 0 &&
+           p.sb % 8 == 0 && al(p.A) && al(p.B) && a_ok && b_ok;
 }
 
 namespace {
+
+template <int TM, int TN, bool TA, bool TB, bool kBatch = true>
+hipError_t launch_direct_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
+{
+    const auto *A = static_cast<const uint16_t *>(p.A);
+    const auto *B = static_cast<const uint16_t *>(p.B);
+    const dim3 grid(static_cast<uint32_t>(tm * tn * p.batch));
+    // whole 16-byte chunks of C rows: C aligned, ldc, N and stride_c multiples of 4
+    const bool rows_c = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0 &&
+                        p.N % 4 == 0 && p.sc % 4 == 0;
+    if (rows_c)
+        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, true, TA, TB, kBatch>), grid,
+                           dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc,
+                           tm, tn, p.sa, p.sb, p.sc, p.batch);
+    else
+        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, false, TA, TB, kBatch>), grid,
+                           dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc,
+                           tm, tn, p.sa, p.sb, p.sc, p.batch);
+    return hipGetLastError();
+}
 
 template <int TM, int TN>
 hipError_t launch_direct(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + TM - 1) / TM, tn = (p.N + TN - 1) / TN;
-    if (tm * tn > kMaxBlocks || !supports_mfma_bf16_direct(p)) return hipErrorInvalidValue;
-    const auto *A = static_cast<const uint16_t *>(p.A);
-    const auto *B = static_cast<const uint16_t *>(p.B);
-    const bool rows_c = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0;
-    if (rows_c)
-        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, true>),
-                           dim3(static_cast<uint32_t>(tm * tn)), dim3(kThreads), 0, s, p.M, p.N,
-                           p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm, tn);
-    else
-        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, false>),
-                           dim3(static_cast<uint32_t>(tm * tn)), dim3(kThreads), 0, s, p.M, p.N,
-                           p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm, tn);
-    return hipGetLastError();
+    if (tm * tn * p.batch > kMaxBlocks || !supports_mfma_bf16_direct(p)) return hipErrorInvalidValue;
+    if (p.ta && p.tb) return launch_direct_layout<TM, TN, true, true>(p, s, tm, tn);
+    if (p.ta) return launch_direct_layout<TM, TN, true, false>(p, s, tm, tn);
+    if (p.tb) return launch_direct_layout<TM, TN, false, true>(p, s, tm, tn);
+    if (p.batch != 1) return launch_direct_layout<TM, TN, false, false>(p, s, tm, tn);
+    return launch_direct_layout<TM, TN, false, false, false>(p, s, tm, tn);
 }
 
 }  // namespace

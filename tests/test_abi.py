@@ -202,7 +202,8 @@ GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_ba
                          "mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64",
                          "mfma_f32_direct64", "mfma_f32_narrow128", "mfma_f32_narrow128x64",
                          "mfma_f32_narrow64"),
-                 g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk")}
+                 g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk",
+                          "mfma_bf16_direct", "mfma_bf16_direct128")}
 
 
 @pytest.mark.parametrize("dtype", [g.F32, g.BF16])
@@ -238,11 +239,13 @@ def test_plan_batched_tile_choice():
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 0, 0, 8192, 8192, 8200, 2)) == \
         "mfma_f32_narrow128"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 0, 1, 8192, 8192, 8192, 1)) == \
+        "mfma_bf16_direct"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 1, 8188, 8192, 8192, 1)) == \
         "mfma_bf16_batched"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 384, 1152, 16384, 1)) == \
         "mfma_f32_batched_splitk"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 16384, 1)) == \
-        "mfma_bf16_batched128"
+        "mfma_bf16_direct128"
 
 
 @pytest.mark.parametrize("dtype", [g.F32, g.BF16])

@@ -32,7 +32,8 @@ GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_
            "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk"]}
 LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mfma_f32_direct64",
            "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64"]
-ALL = {"f32": GENERAL["f32"] + LDS_F32, "bf16": GENERAL["bf16"]}
+ALL = {"f32": GENERAL["f32"] + LDS_F32, "bf16": GENERAL["bf16"] + ["mfma_bf16_direct",
+                                                                  "mfma_bf16_direct128"]}
 
 
 def say(msg):
@@ -126,7 +127,7 @@ def test_small_integer_exact(dtype, kernel, ta, tb):
     ran = [exact_case(dtype, kernel, ta, tb, M, N, K, batch, seed)
            for (M, N, K, batch, seed) in [(300, 270, 100, 3, 41), (513, 129, 200, 2, 42),
                                           (7, 9, 3, 5, 43), (516, 268, 96, 3, 48),
-                                          (8, 12, 16, 5, 49), (260, 132, 272, 2, 50)]]
+                                          (8, 16, 32, 5, 49), (264, 136, 288, 2, 50)]]
     if not any(ran):
         pytest.skip(f"{kernel} takes none of these layouts")
 
