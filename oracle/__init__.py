@@ -32,7 +32,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
           "-pthread", "-shared", "-fPIC", "-Wall", "-Wextra"]
 
-MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP", "IGNORE_TA", "BATCH_B0")
+MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP", "IGNORE_TA", "BATCH_B0",
+           "F16_BIAS")
 
 
 def build(out: str = _LIB_PATH, mutant: Optional[str] = None) -> str:
@@ -55,7 +56,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     full = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, ctypes.c_int]
     rows = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64, ctypes.c_int]
     for name, argt in (("oracle_gemm_f32", full), ("oracle_gemm_bf16", full),
-                       ("oracle_gemm_f32_rows", rows), ("oracle_gemm_bf16_rows", rows)):
+                       ("oracle_gemm_f16", full), ("oracle_gemm_f32_rows", rows),
+                       ("oracle_gemm_bf16_rows", rows), ("oracle_gemm_f16_rows", rows)):
         fn = getattr(lib, name)
         fn.argtypes = argt
         fn.restype = ctypes.c_int
@@ -63,8 +65,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_gemm_batched.argtypes = [ci, ci, ci, _i64, _i64, _i64, _vp, _i64, _i64,
                                         _vp, _i64, _i64, _i64, _vp, _vp, _i64, ci]
     lib.oracle_gemm_batched.restype = ci
-    lib.oracle_decode_bf16.argtypes = [_vp, _vp, _i64]
-    lib.oracle_decode_bf16.restype = None
+    for name in ("oracle_decode_bf16", "oracle_decode_f16"):
+        getattr(lib, name).argtypes = [_vp, _vp, _i64]
+        getattr(lib, name).restype = None
     return lib
 
 
@@ -155,14 +158,15 @@ class Oracle:
         """(C, D) in fp64 for C_b = op(A_b) op(B_b), b over the batch.
 
         A and B are given as stored: A is M x K (K x M when ``transa``), B is
-        K x N (N x K when ``transb``); float32 or uint16 bf16 patterns.  A
+        K x N (N x K when ``transb``); float32, uint16 bf16 patterns or float16.  A
         3-D operand is a batch (any batch stride, 0 included, e.g. from
         numpy.broadcast_to); a 2-D one is reused by every product.  The result
         is (batch, M, N), or (M, N) when both operands are 2-D."""
         dtype = A.dtype
-        if dtype not in (np.float32, np.uint16) or B.dtype != dtype:
-            raise TypeError(f"operands must both be float32 or both uint16, got {A.dtype}, {B.dtype}")
-        kind = 0 if dtype == np.float32 else 1
+        if dtype not in (np.float32, np.uint16, np.float16) or B.dtype != dtype:
+            raise TypeError("operands must both be float32, both uint16 (bf16 patterns) or both "
+                            f"float16, got {A.dtype}, {B.dtype}")
+        kind = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.float16): 2}[dtype]
         two_d = A.ndim == 2 and B.ndim == 2
         A3, ba, sa, lda = self._stored(A, dtype)
         B3, bb, sb, ldb = self._stored(B, dtype)
@@ -183,12 +187,24 @@ class Oracle:
             raise RuntimeError(f"oracle_gemm_batched failed with code {rc}")
         return (C[0], D[0]) if two_d else (C, D)
 
-    def decode_bf16(self, bits: np.ndarray) -> np.ndarray:
+    def gemm_f16(self, A: np.ndarray, B: np.ndarray, rows: Optional[Sequence[int]] = None,
+                 threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """(C, D) in fp64 for fp16 operands (numpy float16 arrays; the oracle
+        decodes their bit patterns itself)."""
+        return self._call("oracle_gemm_f16", np.float16, A, B, rows, threads)
+
+    def _decode(self, fn, bits):
         bits = np.ascontiguousarray(bits, dtype=np.uint16).reshape(-1)
         out = np.empty(bits.shape, dtype=np.float64)
         if bits.size:
-            self.lib.oracle_decode_bf16(bits.ctypes.data, out.ctypes.data, bits.size)
+            fn(bits.ctypes.data, out.ctypes.data, bits.size)
         return out
+
+    def decode_bf16(self, bits: np.ndarray) -> np.ndarray:
+        return self._decode(self.lib.oracle_decode_bf16, bits)
+
+    def decode_f16(self, bits: np.ndarray) -> np.ndarray:
+        return self._decode(self.lib.oracle_decode_f16, bits)
 
 
 def load(path: str = _LIB_PATH) -> Oracle:
@@ -207,6 +223,10 @@ def gemm_f32(A, B, rows=None, threads=0):
 
 def gemm_bf16(A_bits, B_bits, rows=None, threads=0):
     return load().gemm_bf16(A_bits, B_bits, rows, threads)
+
+
+def gemm_f16(A, B, rows=None, threads=0):
+    return load().gemm_f16(A, B, rows, threads)
 
 
 def gemm_batched(A, B, transa=False, transb=False, threads=0):

@@ -43,6 +43,7 @@
  *   ORACLE_MUTANT_BF16_SWAP    - bf16 decode takes the pattern byte-swapped
  *   ORACLE_MUTANT_IGNORE_TA    - a transposed A is read as if it were not
  *   ORACLE_MUTANT_BATCH_B0     - every product of a batch reads the first B
+ *   ORACLE_MUTANT_F16_BIAS     - fp16 decode uses an exponent bias of 16
  */
 
 static double decode_bf16(uint16_t bits)
@@ -56,7 +57,29 @@ static double decode_bf16(uint16_t bits)
     return (double)f;
 }
 
-enum { KIND_F32 = 0, KIND_BF16 = 1 };
+/* IEEE binary16 pattern -> fp64: sign, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 is zero or subnormal (fraction * 2^-24), 31 is
+ * infinity or NaN.  Written from the format's definition. */
+static double decode_f16(uint16_t bits)
+{
+    int bias = 15;
+#ifdef ORACLE_MUTANT_F16_BIAS
+    bias = 16;
+#endif
+    const int sign = bits >> 15, e = (bits >> 10) & 31, f = bits & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)f, 1 - bias - 10);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), e - bias - 10);
+    return sign ? -v : v;
+}
+
+enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_F16 = 2 };
+
+static double decode_kind(int kind, uint16_t bits)
+{
+    return kind == KIND_F16 ? decode_f16(bits) : decode_bf16(bits);
+}
 
 typedef struct {
     int kind;
@@ -81,7 +104,7 @@ static double load_a(const job_t *j, int64_t i, int64_t k)
 #endif
     if (j->kind == KIND_F32)
         return (double)((const float *)j->A)[at];
-    return decode_bf16(((const uint16_t *)j->A)[at]);
+    return decode_kind(j->kind, ((const uint16_t *)j->A)[at]);
 }
 
 static double load_b(const job_t *j, int64_t k, int64_t n)
@@ -94,7 +117,7 @@ static double load_b(const job_t *j, int64_t k, int64_t n)
     int64_t at = j->tb ? n * j->ldb + k : k * j->ldb + n;
     if (j->kind == KIND_F32)
         return (double)((const float *)j->B)[at];
-    return decode_bf16(((const uint16_t *)j->B)[at]);
+    return decode_kind(j->kind, ((const uint16_t *)j->B)[at]);
 }
 
 /* One output row: acc and den start at zero, then for each k the row of B is
@@ -228,7 +251,7 @@ int oracle_gemm_batched(int kind, int ta, int tb, int64_t M, int64_t N, int64_t 
                         const void *B, int64_t ldb, int64_t sb, int64_t batch,
                         double *C, double *D, int64_t ldo, int nthreads)
 {
-    if (kind != KIND_F32 && kind != KIND_BF16) return 1;
+    if (kind != KIND_F32 && kind != KIND_BF16 && kind != KIND_F16) return 1;
     if (batch < 0 || sa < 0 || sb < 0 || M < 0 || N < 0) return 1;
     const int64_t es = kind == KIND_F32 ? 4 : 2;
     for (int64_t b = 0; b < batch; ++b) {
@@ -246,8 +269,33 @@ int oracle_gemm_batched(int kind, int ta, int tb, int64_t M, int64_t N, int64_t 
     return 0;
 }
 
+/* fp16 operands (raw IEEE binary16 patterns): the full product and
+ * selected rows, as for bf16 above. */
+int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
+                    const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                    double *C, double *D, int64_t ldo, int nthreads)
+{
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0};
+    return run(j, nthreads);
+}
+
+int oracle_gemm_f16_rows(int64_t M, int64_t N, int64_t K,
+                         const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
+                         const int64_t *rows, int64_t nrows,
+                         double *C, double *D, int64_t ldo, int nthreads)
+{
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0};
+    return run(j, nthreads);
+}
+
 /* bf16 pattern -> fp64, exposed so tests can pin the decoder on its own. */
 void oracle_decode_bf16(const uint16_t *in, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = decode_bf16(in[i]);
+}
+
+/* fp16 pattern -> fp64, exposed for the same reason. */
+void oracle_decode_f16(const uint16_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_f16(in[i]);
 }

@@ -233,9 +233,48 @@ def pin_batched(o):
         assert np.array_equal(Cz[b], (A[2].astype(np.int64) @ B[b].astype(np.int64)).astype(np.float64))
 
 
+def pin_f16_decoder(o):
+    # every binary16 pattern against numpy's own float16 -> float64 conversion
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = o.decode_f16(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+    # patterns worked by hand: 1, -2, 1 + 2^-10, the smallest subnormal, 65504
+    assert list(o.decode_f16(np.array([0x3C00, 0xC000, 0x3C01, 0x0001, 0x7BFF], np.uint16))) == \
+        [1.0, -2.0, 1.0 + 2.0 ** -10, 2.0 ** -24, 65504.0]
+
+
+def pin_small_int_f16(o):
+    g = workloads.generator(18)
+    for (M, N, K) in [(17, 40, 96), (5, 128, 333)]:
+        A = workloads.small_int((M, K), -8, 8, g, torch.float16).numpy()
+        B = workloads.small_int((K, N), -8, 8, g, torch.float16).numpy()
+        C, D = o.gemm_f16(A, B)
+        Ai, Bi = A.astype(np.int64), B.astype(np.int64)
+        assert np.array_equal(C, (Ai @ Bi).astype(np.float64))
+        assert np.array_equal(D, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+        Cb, _ = o.gemm_batched(np.ascontiguousarray(A.T), B, True, False)
+        assert np.array_equal(Cb, C)
+
+
+def pin_f16_matches_decoded_f32(o):
+    # fp16 -> fp32 conversion is exact, so the fp16 product must equal the
+    # fp32 product of the converted operands bit for bit
+    r = rng(19)
+    A = (r.standard_normal((23, 70)) * 3).astype(np.float16)
+    B = (r.standard_normal((70, 31)) * 1e-3).astype(np.float16)   # subnormals included
+    C, D = o.gemm_f16(A, B)
+    C2, D2 = o.gemm_f32(A.astype(np.float32), B.astype(np.float32))
+    assert np.array_equal(C, C2) and np.array_equal(D, D2)
+
+
 PINS = [pin_golden, pin_identity, pin_permutation, pin_ones, pin_small_int_f32,
         pin_small_int_bf16, pin_bf16_matches_decoded_f32, pin_numpy_blas,
         pin_transposed_small_int, pin_transposed_permutation, pin_batched,
+        pin_f16_decoder, pin_small_int_f16, pin_f16_matches_decoded_f32,
         lambda o: pin_brute_force(o, [(2, 3, 4), (3, 1, 5), (4, 4, 2)])]
 
 
