@@ -54,7 +54,7 @@ import torch  # noqa: E402
 
 import workloads  # noqa: E402
 
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}     # MI355X dense, per dtype
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}     # MI355X dense, per dtype
 HBM_PEAK_GBS = 8000.0
 METRIC = "GFLOP/s (2MNK/t) fp32 & bf16 GEMM at 8192³; % of MI355X dtype peak"
 STEP_WORKLOADS = ("f32_8192", "bf16_8192")
@@ -66,7 +66,7 @@ KERNEL_SOURCES = {
     "mfma_f32_128": ("mfma_f32_kernel<128, 128, true>", ["mfma_f32.hip"]),
     "mfma_f32_direct": ("mfma_f32_direct_kernel<256, 256, 16, false, false, false, false>",
                         ["mfma_f32.hip"]),
-    "mfma_bf16_direct": ("mfma_bf16_direct_kernel<256, 256, true, false, false, false>",
+    "mfma_bf16_direct": ("mfma_bf16_direct_kernel<256, 256, true, false, false, false, false>",
                          ["mfma_bf16.hip"]),
     "mfma_bf16": ("mfma_bf16_kernel<true>", ["mfma_bf16.hip"]),
 }
@@ -294,7 +294,7 @@ def main():
         step()
     torch.cuda.synchronize()
     kernel_of = {w.name: g.gemm_kernel_name(g.gemm_plan(
-        g.F32 if w.dtype == "f32" else g.BF16, w.M, w.N, w.K,
+        CODE[w.dtype], w.M, w.N, w.K,
         Ad.data_ptr(), Ad.stride(0), Bd.data_ptr(), Bd.stride(0), Cd.data_ptr(), Cd.stride(0)))
         for (w, Ad, Bd, Cd) in ops}
 
@@ -333,7 +333,7 @@ def main():
         A, B = host[w.name]
         rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, args.check_rows),
                                                      replace=False).tolist()))
-        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        fn = getattr(oracle, "gemm_" + w.dtype)
         Cref, D = fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B), rows=rows,
                      threads=cpu_threads())
         e, _, _ = oracle.normalized_error(Cd[rows].cpu().numpy(), Cref, D)
@@ -366,7 +366,7 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "+".join(sorted({"f32" if w.dtype == "f32" else "bf16" for w in ws})),
+        "dtype": "+".join(sorted({w.dtype for w in ws})),
         "data": "synthetic (seed 1234; fp32 uniform[-1,1], bf16 from N(0,1))",
         "config": {"workload": "+".join(names),
                    "shapes": {w.name: [w.M, w.N, w.K] for w in ws}},
@@ -399,6 +399,7 @@ def main():
 
 
 LLC_BYTES = 256 * 1024 * 1024   # MI355X last-level (Infinity) cache
+CODE = {"f32": 0, "bf16": 1, "f16": 2}   # element type codes of the library
 
 
 def other_configs(dev, skip, check_rows):
@@ -419,7 +420,7 @@ def other_configs(dev, skip, check_rows):
         copies = 1 if per_copy * 2 > LLC_BYTES else max(2, -(-2 * LLC_BYTES // per_copy))
         ops = [(A.to(dev), B.to(dev), torch.empty((w.M, w.N), dtype=torch.float32, device=dev))
                for _ in range(copies)]
-        code = g.F32 if w.dtype == "f32" else g.BF16
+        code = CODE[w.dtype]
         a0, b0, c0 = ops[0]
         kernel = g.gemm_kernel_name(g.gemm_plan(code, w.M, w.N, w.K, a0.data_ptr(), a0.stride(0),
                                                 b0.data_ptr(), b0.stride(0), c0.data_ptr(),
@@ -434,7 +435,7 @@ def other_configs(dev, skip, check_rows):
         ms, graph_ms, clocks = time_calls(dev, call, copies)
         rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, check_rows),
                                                      replace=False).tolist()))
-        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        fn = getattr(oracle, "gemm_" + w.dtype)
         Cref, D = fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B), rows=rows,
                      threads=cpu_threads())
         err, _, _ = oracle.normalized_error(c0[rows].cpu().numpy(), Cref, D)
@@ -570,7 +571,7 @@ def cpu_baseline(ws, host, seconds):
     t0 = time.perf_counter()
     for w in ws:
         A, B = host[w.name]
-        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        fn = getattr(oracle, "gemm_" + w.dtype)
         fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B),
            rows=list(range(min(probe_rows, w.M))), threads=th)
     t_probe = time.perf_counter() - t0
@@ -580,7 +581,7 @@ def cpu_baseline(ws, host, seconds):
     for w in ws:
         A, B = host[w.name]
         r = min(rows, w.M)
-        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        fn = getattr(oracle, "gemm_" + w.dtype)
         fn(workloads.as_numpy_operand(A), workloads.as_numpy_operand(B),
            rows=list(range(r)), threads=th)
         flops += 2 * r * w.N * w.K

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmi355gemm.so")
 
 F32 = 0
 BF16 = 1
+F16 = 2
 HIP_SUCCESS = 0
 HIP_ERROR_INVALID_VALUE = 1
 
@@ -34,11 +35,11 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     sig = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp]
-    for name in ("gemm_f32", "gemm_bf16_f32acc"):
+    for name in ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc"):
         getattr(lib, name).argtypes = sig
         getattr(lib, name).restype = ci
     bsig = [ci, ci, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, vp]
-    for name in ("gemm_f32_batched", "gemm_bf16_f32acc_batched"):
+    for name in ("gemm_f32_batched", "gemm_bf16_f32acc_batched", "gemm_f16_f32acc_batched"):
         getattr(lib, name).argtypes = bsig
         getattr(lib, name).restype = ci
     sz = ctypes.c_size_t
@@ -66,8 +67,8 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 # Every symbol include/mi355gemm.h declares.
-EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f32_batched", "gemm_bf16_f32acc_batched",
-           "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
+EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched",
+           "gemm_bf16_f32acc_batched", "gemm_f16_f32acc_batched", "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
            "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info")
 
 
@@ -79,6 +80,16 @@ def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 
 def gemm_bf16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
     return lib.gemm_bf16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
+    return lib.gemm_f16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, stride_b, C,
+                            ldc, stride_c, batch, stream) -> int:
+    return lib.gemm_f16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb,
+                                       stride_b, C, ldc, stride_c, batch, stream)
 
 
 def gemm_f32_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc,
@@ -188,13 +199,19 @@ def _layout(t: torch.Tensor, name: str):
                      f"(got strides {tuple(t.stride())} for shape {tuple(t.shape)})")
 
 
+# entry points (plain, batched) per operand type
+_FN = {torch.float32: ("gemm_f32", "gemm_f32_batched"),
+       torch.bfloat16: ("gemm_bf16_f32acc", "gemm_bf16_f32acc_batched"),
+       torch.float16: ("gemm_f16_f32acc", "gemm_f16_f32acc_batched")}
+
+
 def _batch_stride(t: torch.Tensor) -> int:
     return t.stride(0) if t.dim() == 3 and t.shape[0] > 1 else 0
 
 
 def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """out = a @ b on the GPU (fp32·fp32 or bf16·bf16 -> fp32).
+    """out = a @ b on the GPU (fp32·fp32, bf16·bf16 or fp16·fp16 -> fp32).
 
     a is (M, K) or (batch, M, K), b is (K, N) or (batch, K, N); a 2-D operand
     is shared by every product of a batch, and a 3-D one may have any batch
@@ -205,8 +222,9 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
     on `stream` (default: the current stream of a's device)."""
     if a.dim() not in (2, 3) or b.dim() not in (2, 3):
         raise ValueError("gemm takes 2-D or 3-D tensors")
-    if a.dtype != b.dtype or a.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError(f"operands must both be float32 or both bfloat16, got {a.dtype}, {b.dtype}")
+    if a.dtype != b.dtype or a.dtype not in _FN:
+        raise TypeError("operands must both be float32, both bfloat16 or both float16, "
+                        f"got {a.dtype}, {b.dtype}")
     if a.device.type != "cuda" or b.device != a.device:
         raise ValueError("operands must be on the same GPU")
     M, K = a.shape[-2], a.shape[-1]
@@ -226,20 +244,20 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
           or (N > 1 and out.stride(-1) != 1)):
         raise ValueError(f"out must be a float32 {shape} tensor with unit column stride on a's GPU")
     ldc = out.stride(-2) if M > 1 else max(N, 1)
-    f32 = a.dtype == torch.float32
+    plain_name, batched_name = _FN[a.dtype]
     dev = a.get_device()
     # The raw handle of the current stream, without building a Stream object
     # (a few microseconds per call, which is the whole kernel time of the
     # smallest products).
     raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
     if not batched and not ta and not tb:
-        fn, what = (lib.gemm_f32, "gemm_f32") if f32 else (lib.gemm_bf16_f32acc, "gemm_bf16_f32acc")
+        what = plain_name
         args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, raw)
     else:
-        fn, what = ((lib.gemm_f32_batched, "gemm_f32_batched") if f32 else
-                    (lib.gemm_bf16_f32acc_batched, "gemm_bf16_f32acc_batched"))
+        what = batched_name
         args = (int(ta), int(tb), M, N, K, a.data_ptr(), lda, _batch_stride(a), b.data_ptr(),
                 ldb, _batch_stride(b), out.data_ptr(), ldc, _batch_stride(out), batch, raw)
+    fn = getattr(lib, what)
     # The library launches on the calling thread's current HIP device.
     if dev != torch.cuda.current_device():
         with torch.cuda.device(dev):

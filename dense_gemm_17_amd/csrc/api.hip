@@ -18,7 +18,7 @@ namespace mi355gemm {
 namespace {
 
 bool supports_any(const Problem &) { return true; }
-bool supports_skinny(const Problem &p) { return p.M <= kSkinnyMaxM; }
+bool supports_skinny(const Problem &p) { return p.M <= kSkinnyMaxM && !is_general(p); }
 
 // Kernel registry.  Ids are positions in this table and are part of the test
 // hooks' contract (gemm_kernel_name / gemm_force_kernel).
@@ -47,6 +47,13 @@ const KernelInfo kKernels[] = {
     {"mfma_bf16_batched128", kBF16, launch_mfma_bf16_batched128, supports_any, true},
     {"mfma_f32_batched_splitk", kF32, launch_mfma_f32_batched_splitk, supports_any, true},
     {"mfma_bf16_batched_splitk", kBF16, launch_mfma_bf16_batched_splitk, supports_any, true},
+    {"naive_f16", kF16, launch_naive_f16, supports_any},
+    {"skinny_f16", kF16, launch_skinny_f16, supports_skinny},
+    {"mfma_f16_direct", kF16, launch_mfma_f16_direct, supports_mfma_bf16_direct, true},
+    {"mfma_f16_direct128", kF16, launch_mfma_f16_direct128, supports_mfma_bf16_direct, true},
+    {"mfma_f16_batched", kF16, launch_mfma_f16_batched, supports_any, true},
+    {"mfma_f16_batched128", kF16, launch_mfma_f16_batched128, supports_any, true},
+    {"mfma_f16_batched_splitk", kF16, launch_mfma_f16_batched_splitk, supports_any, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -210,6 +217,14 @@ int select_general(const Problem &p)
         return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
                    ? kernel_id("mfma_bf16_batched")
                    : kernel_id("mfma_bf16_batched128");
+    if (p.dtype == kF16 && supports_mfma_bf16_direct(p))
+        return tiled_cost(p, 256, 256, 1, 512) <= tiled_cost(p, 128, 128, 2, 410)
+                   ? kernel_id("mfma_f16_direct")
+                   : kernel_id("mfma_f16_direct128");
+    if (p.dtype == kF16)
+        return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
+                   ? kernel_id("mfma_f16_batched")
+                   : kernel_id("mfma_f16_batched128");
     return tiled_cost(p, 256, 256, 1, F32_GENERAL_256) <= tiled_cost(p, 128, 128, 2, F32_GENERAL_128)
                ? kernel_id("mfma_f32_batched")
                : kernel_id("mfma_f32_batched128");
@@ -221,7 +236,11 @@ int select_kernel(const Problem &p)
 {
     if (is_general(p)) return select_general(p);
     if (p.M <= kSkinnyMaxM)
-        return kernel_id(p.dtype == kF32 ? "skinny_f32" : "skinny_bf16");
+        return kernel_id(p.dtype == kF32 ? "skinny_f32" : p.dtype == kBF16 ? "skinny_bf16"
+                                                                            : "skinny_f16");
+    // fp16 takes the bf16 family's tiles with the fp16 instruction; layouts
+    // the LDS-direct tiles cannot take go to the general family.
+    if (p.dtype == kF16) return select_general(p);
     if (p.dtype == kBF16) {
         if (!supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16");
         // 128 x 128 runs at 0.8 of the 256 x 256 tile's per-tile efficiency
@@ -327,6 +346,23 @@ int gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t
     return run(p, stream);
 }
 
+int gemm_f16_f32acc(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                    const uint16_t *B, int64_t ldb, float *C, int64_t ldc, hipStream_t stream)
+{
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kF16};
+    return run(p, stream);
+}
+
+int gemm_f16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                            const uint16_t *A, int64_t lda, int64_t stride_a, const uint16_t *B,
+                            int64_t ldb, int64_t stride_b, float *C, int64_t ldc,
+                            int64_t stride_c, int64_t batch, hipStream_t stream)
+{
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kF16, transa, transb, batch,
+                    stride_a, stride_b, stride_c};
+    return run(p, stream);
+}
+
 int gemm_f32_batched(int transa, int transb, int64_t M, int64_t N, int64_t K, const float *A,
                      int64_t lda, int64_t stride_a, const float *B, int64_t ldb, int64_t stride_b,
                      float *C, int64_t ldc, int64_t stride_c, int64_t batch, hipStream_t stream)
@@ -361,7 +397,7 @@ int gemm_kernel_dtype(int id)
 namespace {
 int plan(const Problem &p)
 {
-    if (p.dtype != kF32 && p.dtype != kBF16) return -1;
+    if (p.dtype != kF32 && p.dtype != kBF16 && p.dtype != kF16) return -1;
     switch (validate(p)) {
     case kInvalid: return -1;
     case kNothing: return -2;

@@ -7,7 +7,13 @@
 
 namespace mi355gemm {
 
-enum Dtype : int { kF32 = 0, kBF16 = 1 };
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+// Storage type of an IEEE binary16 operand in the kernels templated on the
+// element type (bf16 operands are plain uint16_t patterns there).
+struct F16Bits {
+    uint16_t v;
+};
 
 // Arguments of one product after validation.  Pointers are device pointers;
 // A and B are `const void*` so one signature serves both element types.
@@ -69,6 +75,13 @@ hipError_t launch_mfma_bf16_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_batched_splitk(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_batched_splitk(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f16_direct(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f16_direct128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f16_batched(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f16_batched128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f16_batched_splitk(const Problem &p, hipStream_t s);
+hipError_t launch_skinny_f16(const Problem &p, hipStream_t s);
+hipError_t launch_naive_f16(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_f32(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s);
 

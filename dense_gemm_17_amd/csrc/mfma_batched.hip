@@ -46,6 +46,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// One 32 x 32 x 16 MFMA on 16-bit patterns: bf16, or IEEE fp16 when kF16
+// (the kernels stage, read and lay out the same bits either way).
+template <bool kF16>
+__device__ __forceinline__ f32x16 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+{
+    if constexpr (kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 constexpr int kThreads = 256;
 constexpr int kGroup = 4;   // tile-rows per group in the tile order
@@ -419,7 +432,7 @@ __device__ __forceinline__ bf16x8 fragment(const uint16_t *Xs, int base, int s, 
     }
 }
 
-template <int BM, int BN, bool TA, bool TB, bool kVec>
+template <int BM, int BN, bool TA, bool TB, bool kVec, bool kF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, BM == 256 ? 1 : 2)))
 void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A, int64_t lda,
                     int64_t sa, const uint16_t *__restrict__ B, int64_t ldb, int64_t sb,
@@ -478,8 +491,7 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb],
-                                                                               acc[mb][nb], 0, 0, 0);
+                        acc[mb][nb] = mfma16<kF16>(a[mb], b[nb], acc[mb][nb]);
             }
             if (more) {
                 store_operand<BM, S::kAChunks, !TA>(va, As[cur ^ 1]);
@@ -643,7 +655,7 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
 // carries the eight k = 16g + 8h .. 16g + 8h + 7.
 __device__ __forceinline__ uint16_t masked16(uint16_t x, bool keep) { return keep ? x : 0; }
 
-template <bool TA, bool TB, bool kVecA, bool kVecB>
+template <bool TA, bool TB, bool kVecA, bool kVecB, bool kF16>
 __global__ __launch_bounds__(kThreads) void bf16_kernel(
     int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A, int64_t lda, int64_t sa,
     const uint16_t *__restrict__ B, int64_t ldb, int64_t sb, float *__restrict__ C, int64_t ldc,
@@ -703,9 +715,8 @@ __global__ __launch_bounds__(kThreads) void bf16_kernel(
     auto mfmas = [&](const u16x8 (&a)[kU], const u16x8 (&b)[kU]) {
 #pragma unroll
         for (int u = 0; u < kU; ++u)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[u]),
-                                                          __builtin_bit_cast(bf16x8, b[u]), acc,
-                                                          0, 0, 0);
+            acc = mfma16<kF16>(__builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]),
+                               acc);
     };
     u16x8 a0[kU], a1[kU], b0[kU], b1[kU];
     int64_t g0 = wave;
@@ -759,23 +770,23 @@ hipError_t launch_f32(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int BM, int BN, bool TA, bool TB>
+template <int BM, int BN, bool TA, bool TB, bool kF16>
 void launch_bf16_layout(const Problem &p, bool vec, uint32_t blocks, int64_t tm, int64_t tn,
                         hipStream_t s)
 {
     const auto *A = static_cast<const uint16_t *>(p.A);
     const auto *B = static_cast<const uint16_t *>(p.B);
     if (vec)
-        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, true>), dim3(blocks),
+        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, true, kF16>), dim3(blocks),
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb,
                            p.C, p.ldc, p.sc, p.batch, tm, tn);
     else
-        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, false>), dim3(blocks),
+        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, false, kF16>), dim3(blocks),
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb,
                            p.C, p.ldc, p.sc, p.batch, tm, tn);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, bool kF16 = false>
 hipError_t launch_bf16(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
@@ -783,14 +794,14 @@ hipError_t launch_bf16(const Problem &p, hipStream_t s)
     const uint32_t blocks = static_cast<uint32_t>(tm * tn * p.batch);
     const bool vec = aligned16(p.A) && aligned16(p.B) && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
                      p.sa % 8 == 0 && p.sb % 8 == 0;
-    if (p.ta && p.tb) launch_bf16_layout<BM, BN, true, true>(p, vec, blocks, tm, tn, s);
-    else if (p.ta) launch_bf16_layout<BM, BN, true, false>(p, vec, blocks, tm, tn, s);
-    else if (p.tb) launch_bf16_layout<BM, BN, false, true>(p, vec, blocks, tm, tn, s);
-    else launch_bf16_layout<BM, BN, false, false>(p, vec, blocks, tm, tn, s);
+    if (p.ta && p.tb) launch_bf16_layout<BM, BN, true, true, kF16>(p, vec, blocks, tm, tn, s);
+    else if (p.ta) launch_bf16_layout<BM, BN, true, false, kF16>(p, vec, blocks, tm, tn, s);
+    else if (p.tb) launch_bf16_layout<BM, BN, false, true, kF16>(p, vec, blocks, tm, tn, s);
+    else launch_bf16_layout<BM, BN, false, false, kF16>(p, vec, blocks, tm, tn, s);
     return hipGetLastError();
 }
 
-template <typename T, bool TA, bool TB, bool VA, bool VB>
+template <typename T, bool TA, bool TB, bool VA, bool VB, bool kF16 = false>
 void launch_sk_layout(const Problem &p, uint32_t blocks, int64_t tm, int64_t tn, hipStream_t s)
 {
     const auto *A = static_cast<const T *>(p.A);
@@ -800,14 +811,14 @@ void launch_sk_layout(const Problem &p, uint32_t blocks, int64_t tm, int64_t tn,
                            p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc,
                            p.batch, tm, tn);
     else
-        hipLaunchKernelGGL((sk::bf16_kernel<TA, TB, VA, VB>), dim3(blocks), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((sk::bf16_kernel<TA, TB, VA, VB, kF16>), dim3(blocks), dim3(kThreads), 0, s,
                            p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc,
                            p.batch, tm, tn);
 }
 
 // The vector load exists only along a stored row of K (A as written, B
 // transposed); it needs 16-byte aligned rows and K a multiple of the vector.
-template <typename T>
+template <typename T, bool kF16 = false>
 hipError_t launch_splitk(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + 31) / 32, tn = (p.N + 31) / 32;
@@ -818,18 +829,18 @@ hipError_t launch_splitk(const Problem &p, hipStream_t s)
     const bool va = !p.ta && kv && aligned16(p.A) && p.lda % v == 0 && p.sa % v == 0;
     const bool vb = p.tb && kv && aligned16(p.B) && p.ldb % v == 0 && p.sb % v == 0;
     if (p.ta && p.tb) {
-        if (vb) launch_sk_layout<T, true, true, false, true>(p, blocks, tm, tn, s);
-        else launch_sk_layout<T, true, true, false, false>(p, blocks, tm, tn, s);
+        if (vb) launch_sk_layout<T, true, true, false, true, kF16>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, true, true, false, false, kF16>(p, blocks, tm, tn, s);
     } else if (p.ta) {
-        launch_sk_layout<T, true, false, false, false>(p, blocks, tm, tn, s);
+        launch_sk_layout<T, true, false, false, false, kF16>(p, blocks, tm, tn, s);
     } else if (p.tb) {
-        if (va && vb) launch_sk_layout<T, false, true, true, true>(p, blocks, tm, tn, s);
-        else if (va) launch_sk_layout<T, false, true, true, false>(p, blocks, tm, tn, s);
-        else if (vb) launch_sk_layout<T, false, true, false, true>(p, blocks, tm, tn, s);
-        else launch_sk_layout<T, false, true, false, false>(p, blocks, tm, tn, s);
+        if (va && vb) launch_sk_layout<T, false, true, true, true, kF16>(p, blocks, tm, tn, s);
+        else if (va) launch_sk_layout<T, false, true, true, false, kF16>(p, blocks, tm, tn, s);
+        else if (vb) launch_sk_layout<T, false, true, false, true, kF16>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, false, true, false, false, kF16>(p, blocks, tm, tn, s);
     } else {
-        if (va) launch_sk_layout<T, false, false, true, false>(p, blocks, tm, tn, s);
-        else launch_sk_layout<T, false, false, false, false>(p, blocks, tm, tn, s);
+        if (va) launch_sk_layout<T, false, false, true, false, kF16>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, false, false, false, false, kF16>(p, blocks, tm, tn, s);
     }
     return hipGetLastError();
 }
@@ -844,6 +855,21 @@ hipError_t launch_mfma_f32_batched_splitk(const Problem &p, hipStream_t s)
 hipError_t launch_mfma_bf16_batched_splitk(const Problem &p, hipStream_t s)
 {
     return launch_splitk<uint16_t>(p, s);
+}
+
+hipError_t launch_mfma_f16_batched_splitk(const Problem &p, hipStream_t s)
+{
+    return launch_splitk<uint16_t, true>(p, s);
+}
+
+hipError_t launch_mfma_f16_batched(const Problem &p, hipStream_t s)
+{
+    return launch_bf16<256, 256, true>(p, s);
+}
+
+hipError_t launch_mfma_f16_batched128(const Problem &p, hipStream_t s)
+{
+    return launch_bf16<128, 128, true>(p, s);
 }
 
 hipError_t launch_mfma_f32_batched(const Problem &p, hipStream_t s)

@@ -311,7 +311,9 @@ __device__ __forceinline__ uint32_t lds_offset(const void *p)
 }
 
 // Everything a wave needs to address its loads and reads.
-template <int TM, int TN, bool TA = false, bool TB = false>
+// kF16: the 16-bit patterns are IEEE binary16 (v_mfma_f32_32x32x16_f16)
+// rather than bf16; staging, reads and layouts are the same bits either way.
+template <int TM, int TN, bool TA = false, bool TB = false, bool kF16 = false>
 struct DCtx {
     using T = DTile<TM, TN, TA, TB>;
     uint32_t a_voff[T::kAInst], b_voff[T::kBInst];   // lane offsets (bytes) of each load
@@ -323,8 +325,8 @@ struct DCtx {
     uint32_t rdB[TB ? 2 : T::kNB];                   // lane read offsets: B, per block (per K slice)
 };
 
-template <int TM, int TN, bool TA, bool TB>
-__device__ __forceinline__ void load_one(const DCtx<TM, TN, TA, TB> &x, uint32_t stage_lds,
+template <int TM, int TN, bool TA, bool TB, bool kF16>
+__device__ __forceinline__ void load_one(const DCtx<TM, TN, TA, TB, kF16> &x, uint32_t stage_lds,
                                          int64_t kt, int l)
 {
     using T = DTile<TM, TN, TA, TB>;
@@ -363,9 +365,9 @@ __device__ __forceinline__ bf16x4 read_tr4(const char *p)
 // block j (one 16-byte read); transposed: j < 2 MB is A block j / 2, lower /
 // upper four k (transposing reads).  Then B: as written, block (j - nA) / 2,
 // lower / upper four k; transposed, block j - nA (one 16-byte read).
-template <int TM, int TN, bool TA, bool TB>
+template <int TM, int TN, bool TA, bool TB, bool kF16>
 __device__ __forceinline__ void read_one(Frag16<TM, TN, TA, TB> &f, const uint16_t *stage,
-                                         const DCtx<TM, TN, TA, TB> &x, int s, int j)
+                                         const DCtx<TM, TN, TA, TB, kF16> &x, int s, int j)
 {
     using T = DTile<TM, TN, TA, TB>;
     constexpr int nA = TA ? 2 * T::kMB : T::kMB;
@@ -391,7 +393,20 @@ __device__ __forceinline__ void read_one(Frag16<TM, TN, TA, TB> &f, const uint16
     }
 }
 
-template <int TM, int TN, bool TA, bool TB>
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// One 32 x 32 x 16 MFMA on 16-bit patterns: bf16, or fp16 when kF16.
+template <bool kF16>
+__device__ __forceinline__ f32x16 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+{
+    if constexpr (kF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool kF16, int TM, int TN, bool TA, bool TB>
 __device__ __forceinline__ void mfma_one(f32x16 (&acc)[TM / 64][TN / 64],
                                          const Frag16<TM, TN, TA, TB> &f, int q)
 {
@@ -402,7 +417,7 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[TM / 64][TN / 64],
     else a = f.a[mb];
     if constexpr (TB) b = f.b[nb];
     else b = __builtin_shufflevector(f.blo[nb], f.bhi[nb], 0, 1, 2, 3, 4, 5, 6, 7);
-    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[mb][nb], 0, 0, 0);
+    acc[mb][nb] = mfma16<kF16>(a, b, acc[mb][nb]);
 }
 
 // The MFMAs of one slice with the reads of the next slice and (if loads)
@@ -411,17 +426,17 @@ __device__ __forceinline__ void mfma_one(f32x16 (&acc)[TM / 64][TN / 64],
 // enough MFMAs (256 x 256), spread evenly otherwise (128 x 128: 4 MFMAs, 6
 // reads, 4 loads).  sched_barrier(0) pins that order so the matrix unit
 // keeps running while reads and loads are in flight.
-template <int TM, int TN, bool TA, bool TB>
+template <int TM, int TN, bool TA, bool TB, bool kF16>
 __device__ __forceinline__ void mfma_phase(f32x16 (&acc)[TM / 64][TN / 64],
                                            const Frag16<TM, TN, TA, TB> &cur,
                                            Frag16<TM, TN, TA, TB> &nxt, const uint16_t *rstage,
-                                           const DCtx<TM, TN, TA, TB> &x, int s_next,
+                                           const DCtx<TM, TN, TA, TB, kF16> &x, int s_next,
                                            uint32_t lstage, int64_t kload, bool loads)
 {
     using T = DTile<TM, TN, TA, TB>;
 #pragma unroll
     for (int q = 0; q < T::kQ; ++q) {
-        mfma_one(acc, cur, q);
+        mfma_one<kF16>(acc, cur, q);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (T::kReads <= T::kQ) {
             if (q < T::kReads) read_one(nxt, rstage, x, s_next, q);
@@ -530,7 +545,8 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v)
 // kBatch: a batch of products (stride_a, stride_b, stride_c elements apart)
 // as one grid of (product, tile) work-groups; a single product keeps the
 // plain tile map.
-template <int TM, int TN, bool kRowsC, bool TA = false, bool TB = false, bool kBatch = false>
+template <int TM, int TN, bool kRowsC, bool TA = false, bool TB = false, bool kBatch = false,
+          bool kF16 = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DTile<TM, TN>::kPerCU, DTile<TM, TN>::kPerCU)))
 void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
@@ -561,7 +577,7 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
     const int h = lane >> 5, c = lane & 31;
     const int i16 = lane & 15, nhalf = (lane >> 4) & 1;
 
-    DCtx<TM, TN, TA, TB> x;
+    DCtx<TM, TN, TA, TB, kF16> x;
     x.wave = wave;
     x.lds0 = lds_offset(lds);
     // Rows of K start at the tile's first row and step 32 elements per
@@ -728,7 +744,7 @@ bool supports_mfma_bf16_direct(const Problem &p)
 
 namespace {
 
-template <int TM, int TN, bool TA, bool TB, bool kBatch = true>
+template <int TM, int TN, bool kF16, bool TA, bool TB, bool kBatch = true>
 hipError_t launch_direct_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
 {
     const auto *A = static_cast<const uint16_t *>(p.A);
@@ -738,31 +754,33 @@ hipError_t launch_direct_layout(const Problem &p, hipStream_t s, int64_t tm, int
     const bool rows_c = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0 &&
                         p.N % 4 == 0 && p.sc % 4 == 0;
     if (rows_c)
-        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, true, TA, TB, kBatch>), grid,
+        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, true, TA, TB, kBatch, kF16>), grid,
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc,
                            tm, tn, p.sa, p.sb, p.sc, p.batch);
     else
-        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, false, TA, TB, kBatch>), grid,
+        hipLaunchKernelGGL((mfma_bf16_direct_kernel<TM, TN, false, TA, TB, kBatch, kF16>), grid,
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc,
                            tm, tn, p.sa, p.sb, p.sc, p.batch);
     return hipGetLastError();
 }
 
-template <int TM, int TN>
+template <int TM, int TN, bool kF16 = false>
 hipError_t launch_direct(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + TM - 1) / TM, tn = (p.N + TN - 1) / TN;
     if (tm * tn * p.batch > kMaxBlocks || !supports_mfma_bf16_direct(p)) return hipErrorInvalidValue;
-    if (p.ta && p.tb) return launch_direct_layout<TM, TN, true, true>(p, s, tm, tn);
-    if (p.ta) return launch_direct_layout<TM, TN, true, false>(p, s, tm, tn);
-    if (p.tb) return launch_direct_layout<TM, TN, false, true>(p, s, tm, tn);
-    if (p.batch != 1) return launch_direct_layout<TM, TN, false, false>(p, s, tm, tn);
-    return launch_direct_layout<TM, TN, false, false, false>(p, s, tm, tn);
+    if (p.ta && p.tb) return launch_direct_layout<TM, TN, kF16, true, true>(p, s, tm, tn);
+    if (p.ta) return launch_direct_layout<TM, TN, kF16, true, false>(p, s, tm, tn);
+    if (p.tb) return launch_direct_layout<TM, TN, kF16, false, true>(p, s, tm, tn);
+    if (p.batch != 1) return launch_direct_layout<TM, TN, kF16, false, false>(p, s, tm, tn);
+    return launch_direct_layout<TM, TN, kF16, false, false, false>(p, s, tm, tn);
 }
 
 }  // namespace
 
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256>(p, s); }
 hipError_t launch_mfma_bf16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128>(p, s); }
+hipError_t launch_mfma_f16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256, true>(p, s); }
+hipError_t launch_mfma_f16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, true>(p, s); }
 
 }  // namespace mi355gemm

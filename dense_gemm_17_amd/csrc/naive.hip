@@ -18,6 +18,10 @@ __device__ __forceinline__ float ld_elem(const uint16_t *p, int64_t i)
 {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
+__device__ __forceinline__ float ld_elem(const F16Bits *p, int64_t i)
+{
+    return static_cast<float>(__builtin_bit_cast(_Float16, p[i].v));
+}
 
 constexpr int kCols = 64;   // one wave spans 64 columns
 constexpr int kRows = 4;    // four waves per block, one row each
@@ -65,6 +69,7 @@ hipError_t launch_naive(const Problem &p, hipStream_t s)
 
 hipError_t launch_naive_f32(const Problem &p, hipStream_t s) { return launch_naive<float>(p, s); }
 hipError_t launch_naive_bf16(const Problem &p, hipStream_t s) { return launch_naive<uint16_t>(p, s); }
+hipError_t launch_naive_f16(const Problem &p, hipStream_t s) { return launch_naive<F16Bits>(p, s); }
 
 hipError_t launch_fill_zero(const Problem &p, hipStream_t s)
 {

@@ -47,12 +47,22 @@ template <> struct Elem<float> {
     static constexpr int kPerLoad = 4;        // columns per 16-byte load
     typedef f32x4 Raw;
     __device__ static float to_f(float x) { return x; }
+    __device__ static float raw(float x) { return x; }
     __device__ static float get(const Raw &r, int e) { return r[e]; }
 };
-template <> struct Elem<uint16_t> {
+template <> struct Elem<uint16_t> {            // bf16 patterns
     static constexpr int kPerLoad = 8;
     typedef u16x8 Raw;
     __device__ static float to_f(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+    __device__ static uint16_t raw(uint16_t x) { return x; }
+    __device__ static float get(const Raw &r, int e) { return to_f(r[e]); }
+};
+template <> struct Elem<F16Bits> {             // IEEE binary16 patterns
+    static constexpr int kPerLoad = 8;
+    typedef u16x8 Raw;
+    __device__ static float to_f(uint16_t x) { return static_cast<float>(__builtin_bit_cast(_Float16, x)); }
+    __device__ static float to_f(F16Bits x) { return to_f(x.v); }
+    __device__ static uint16_t raw(F16Bits x) { return x.v; }
     __device__ static float get(const Raw &r, int e) { return to_f(r[e]); }
 };
 
@@ -69,7 +79,7 @@ __device__ __forceinline__ typename Elem<T>::Raw load_b(const T *__restrict__ B,
     if (kVec && n + P <= N) return *reinterpret_cast<const typename Elem<T>::Raw *>(p);
 #pragma unroll
     for (int e = 0; e < P; ++e)
-        if (n + e < N) v[e] = p[e];
+        if (n + e < N) v[e] = Elem<T>::raw(p[e]);
     return v;
 }
 
@@ -325,5 +335,6 @@ static_assert(kMaxM == kSkinnyMaxM, "skinny row limit");
 
 hipError_t launch_skinny_f32(const Problem &p, hipStream_t s) { return launch_skinny<float>(p, s); }
 hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s) { return launch_skinny<uint16_t>(p, s); }
+hipError_t launch_skinny_f16(const Problem &p, hipStream_t s) { return launch_skinny<F16Bits>(p, s); }
 
 }  // namespace mi355gemm

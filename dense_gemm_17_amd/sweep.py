@@ -37,7 +37,7 @@ import dense_gemm_17_amd as g  # noqa: E402
 import workloads  # noqa: E402
 from dense_gemm_17_amd.measure import ClockSampler, toolchain  # noqa: E402
 
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}
 LLC_BYTES = 256 * 1024 * 1024
 
 
@@ -143,7 +143,7 @@ def main():
         for _ in range(copies):
             ops.append((A.to(dev), B.to(dev),
                         torch.empty((w.M, w.N), dtype=torch.float32, device=dev)))
-        code = g.F32 if w.dtype == "f32" else g.BF16
+        code = {"f32": g.F32, "bf16": g.BF16, "f16": g.F16}[w.dtype]
         Ad, Bd, Cd = ops[0]
         table = g.gemm_plan(code, w.M, w.N, w.K, Ad.data_ptr(), Ad.stride(0), Bd.data_ptr(),
                             Bd.stride(0), Cd.data_ptr(), Cd.stride(0))

@@ -74,6 +74,18 @@ int gemm_bf16_f32acc(int64_t M, int64_t N, int64_t K,
                      float *C, int64_t ldc,
                      hipStream_t stream);
 
+/* C = A·B with IEEE binary16 operands (raw patterns), fp32 accumulation and
+ * output.  The fp16 operand format is one of the next steps after the bf16
+ * path ("Bare Metal Bard", page 1, first paragraph: the matrix-instruction
+ * rung; vidyal.ai Part 6 on reduced-precision operands for those
+ * instructions).  Same layout, ownership, errors and threading as
+ * gemm_bf16_f32acc; a product of two fp16 values is exact in fp32. */
+int gemm_f16_f32acc(int64_t M, int64_t N, int64_t K,
+                    const uint16_t *A, int64_t lda,
+                    const uint16_t *B, int64_t ldb,
+                    float *C, int64_t ldc,
+                    hipStream_t stream);
+
 /* ---- transposed factors and strided batches --------------------------------
  *
  * For b = 0 .. batch-1:   C_b = op(A_b) · op(B_b)
@@ -118,6 +130,12 @@ int gemm_bf16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64
                              float *C, int64_t ldc, int64_t stride_c,
                              int64_t batch, hipStream_t stream);
 
+int gemm_f16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                            const uint16_t *A, int64_t lda, int64_t stride_a,
+                            const uint16_t *B, int64_t ldb, int64_t stride_b,
+                            float *C, int64_t ldc, int64_t stride_c,
+                            int64_t batch, hipStream_t stream);
+
 /* ---- introspection and test hooks (not needed by ordinary callers) -------
  *
  * Kernel selection follows the regime classification of the devpost write-up
@@ -128,6 +146,7 @@ int gemm_bf16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64
 /* Element type codes for gemm_plan. */
 #define MI355GEMM_F32  0
 #define MI355GEMM_BF16 1
+#define MI355GEMM_F16  2
 
 /* Number of kernels in the library; ids are 0 .. count-1. */
 int gemm_kernel_count(void);
@@ -135,7 +154,8 @@ int gemm_kernel_count(void);
 /* Static name of kernel `id` ("?" for an unknown id); never freed. */
 const char *gemm_kernel_name(int id);
 
-/* Element type (MI355GEMM_F32 / MI355GEMM_BF16) kernel `id` computes, or -1. */
+/* Element type (MI355GEMM_F32 / MI355GEMM_BF16 / MI355GEMM_F16) kernel `id`
+ * computes, or -1. */
 int gemm_kernel_dtype(int id);
 
 /* The kernel id the dispatch table picks for these arguments, without

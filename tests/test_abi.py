@@ -44,13 +44,13 @@ def test_kernel_registry():
     names = g.kernel_names()
     assert len(set(names)) == n
     for i in range(n):
-        assert g.gemm_kernel_dtype(i) in (g.F32, g.BF16)
+        assert g.gemm_kernel_dtype(i) in (g.F32, g.BF16, g.F16)
     assert g.gemm_kernel_name(-1) == "?" and g.gemm_kernel_name(n) == "?"
     assert g.gemm_kernel_dtype(n) == -1
-    assert {g.gemm_kernel_dtype(i) for i in range(n)} == {g.F32, g.BF16}
+    assert {g.gemm_kernel_dtype(i) for i in range(n)} == {g.F32, g.BF16, g.F16}
 
 
-@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16, g.F16])
 def test_plan_rejects_invalid_arguments(dtype):
     ok = dict(A=PA, B=PB, C=PC)
     assert g.gemm_plan(dtype, 64, 64, 64, **ok) >= 0
@@ -76,7 +76,7 @@ def test_plan_rejects_invalid_arguments(dtype):
     assert g.gemm_plan(7, 64, 64, 64, **ok) == -1
 
 
-@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16, g.F16])
 def test_plan_degenerate_sizes(dtype):
     assert g.gemm_plan(dtype, 0, 64, 64, A=0, B=0, C=0) == -2
     assert g.gemm_plan(dtype, 64, 0, 64, A=0, B=0, C=0) == -2
@@ -203,10 +203,12 @@ GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_ba
                          "mfma_f32_direct64", "mfma_f32_narrow128", "mfma_f32_narrow128x64",
                          "mfma_f32_narrow64"),
                  g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk",
-                          "mfma_bf16_direct", "mfma_bf16_direct128")}
+                          "mfma_bf16_direct", "mfma_bf16_direct128"),
+                 g.F16: ("mfma_f16_batched", "mfma_f16_batched128", "mfma_f16_batched_splitk",
+                         "mfma_f16_direct", "mfma_f16_direct128")}
 
 
-@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16, g.F16])
 @pytest.mark.parametrize("ta,tb,batch", [(1, 0, 1), (0, 1, 1), (1, 1, 1), (0, 0, 4), (1, 1, 7)])
 def test_plan_batched_takes_general_family(dtype, ta, tb, batch):
     kid = g.gemm_plan_batched(dtype, ta, tb, 1000, 900, 300, batch)
@@ -216,7 +218,7 @@ def test_plan_batched_takes_general_family(dtype, ta, tb, batch):
     assert g.gemm_kernel_name(kid0) in GENERAL_NAMES[dtype]
 
 
-@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16, g.F16])
 def test_plan_batched_plain_problem_is_the_plain_plan(dtype):
     for (M, N, K) in [(8192, 8192, 8192), (1, 8960, 1536), (300, 200, 100), (64, 64, 0)]:
         assert g.gemm_plan_batched(dtype, 0, 0, M, N, K, 1) == g.gemm_plan(dtype, M, N, K)
@@ -248,7 +250,7 @@ def test_plan_batched_tile_choice():
         "mfma_bf16_direct128"
 
 
-@pytest.mark.parametrize("dtype", [g.F32, g.BF16])
+@pytest.mark.parametrize("dtype", [g.F32, g.BF16, g.F16])
 def test_plan_batched_rejects_invalid_arguments(dtype):
     P = dict(A=PA, B=PB, C=PC)
     assert g.gemm_plan_batched(dtype, 1, 1, 64, 48, 32, 3, **P) >= 0
@@ -297,3 +299,13 @@ def test_forced_plain_kernel_cannot_take_general_problem():
         assert g.gemm_plan(g.F32, 512, 512, 512, PA, 512, PB, 512, PC, 512) == general
     finally:
         g.gemm_force_kernel(-1)
+
+
+def test_plan_f16_follows_the_16_bit_family():
+    name = lambda *a, **k: g.gemm_kernel_name(g.gemm_plan(g.F16, *a, **k))  # noqa: E731
+    assert name(8192, 8192, 8192) == "mfma_f16_direct"
+    assert name(16384, 1152, 384) == "mfma_f16_direct128"
+    assert name(1, 8960, 1536) == "skinny_f16"
+    assert name(1000, 3000, 777) in ("mfma_f16_batched", "mfma_f16_batched128")
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.F16, 1, 1, 4096, 4096, 4096, 2)) == \
+        "mfma_f16_direct"

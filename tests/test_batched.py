@@ -32,8 +32,12 @@ GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_
            "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk"]}
 LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mfma_f32_direct64",
            "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64"]
-ALL = {"f32": GENERAL["f32"] + LDS_F32, "bf16": GENERAL["bf16"] + ["mfma_bf16_direct",
-                                                                  "mfma_bf16_direct128"]}
+GENERAL["f16"] = ["mfma_f16_batched", "mfma_f16_batched128", "mfma_f16_batched_splitk"]
+ALL = {"f32": GENERAL["f32"] + LDS_F32,
+       "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128"],
+       "f16": GENERAL["f16"] + ["mfma_f16_direct", "mfma_f16_direct128"]}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+DTYPES = ["f32", "bf16", "f16"]
 
 
 def say(msg):
@@ -96,8 +100,7 @@ def run(a, b, kernel=None, out=None):
 
 def small_int(shape, dtype, gen):
     lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
-    return workloads.small_int(shape, lo, hi, gen, tdt)
+    return workloads.small_int(shape, lo, hi, gen, TDT[dtype])
 
 
 def exact_case(dtype, kernel, ta, tb, M, N, K, batch, seed):
@@ -118,7 +121,7 @@ def exact_case(dtype, kernel, ta, tb, M, N, K, batch, seed):
     return True
 
 
-@pytest.mark.parametrize("dtype,kernel", [(d, k) for d in ("f32", "bf16") for k in ALL[d]])
+@pytest.mark.parametrize("dtype,kernel", [(d, k) for d in DTYPES for k in ALL[d]])
 @pytest.mark.parametrize("ta,tb", TRANS)
 def test_small_integer_exact(dtype, kernel, ta, tb):
     # several tiles in each direction with ragged tails in M, N and K; the
@@ -132,7 +135,7 @@ def test_small_integer_exact(dtype, kernel, ta, tb):
         pytest.skip(f"{kernel} takes none of these layouts")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ta,tb", TRANS)
 def test_brute_force_tiny_shapes(dtype, ta, tb):
     # every (M, N, K) in {1..6}^3, two products each, every general kernel;
@@ -155,12 +158,12 @@ def test_brute_force_tiny_shapes(dtype, ta, tb):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("ta,tb", TRANS)
 def test_random_operands_gate(dtype, ta, tb):
     w = workloads.Workload("batched_rand", 332, 288, 512, dtype)
     gen = workloads.generator()
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     A = workloads.draw((4, w.M, w.K), ("uniform", 1.0), gen).to(tdt)
     B = workloads.draw((4, w.K, w.N), ("uniform", 1.0), gen).to(tdt)
     As, Bs = stored(A, ta), stored(B, tb)
@@ -177,7 +180,7 @@ def test_random_operands_gate(dtype, ta, tb):
         assert e <= GATE, (kernel, e, at)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_unaligned_padded_and_offset_layouts(dtype):
     # odd leading dimensions and batch strides, operands starting one element
     # into their buffers: the element-load path of every general kernel
@@ -210,7 +213,7 @@ def test_unaligned_padded_and_offset_layouts(dtype):
             assert torch.equal(C.cpu(), ref), (kernel, ta, tb)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_shared_and_stride_zero_operands(dtype):
     gen = workloads.generator(46)
     M, N, K, batch = 200, 152, 96, 4
@@ -232,7 +235,7 @@ def test_shared_and_stride_zero_operands(dtype):
     assert torch.equal(C.cpu(), ref2)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_outputs_side_by_side_and_guard_bands(dtype):
     # C viewed as (M, batch, N) inside rows padded by 5: products sit side by
     # side in each row; padding and everything outside stays NaN
@@ -256,9 +259,9 @@ def test_outputs_side_by_side_and_guard_bands(dtype):
         assert torch.isnan(rest[32:32 + M * ldc].view(M, ldc)[:, batch * N:]).all()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_degenerate_batches(dtype):
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     # K = 0: every product is the empty sum
     for kernel in ALL[dtype] + [None]:
         out = torch.full((3, 40, 30), float("nan"), device=DEV)

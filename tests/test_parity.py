@@ -37,8 +37,15 @@ def say(msg):
     sys.stdout.flush()
 
 
+CODE = {"f32": g.F32, "bf16": g.BF16, "f16": g.F16}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+CODE_OF_TORCH = {torch.float32: g.F32, torch.bfloat16: g.BF16, torch.float16: g.F16}
+ORACLE_FN = {"f32": oracle.gemm_f32, "bf16": oracle.gemm_bf16, "f16": oracle.gemm_f16}
+DTYPES = ["f32", "bf16", "f16"]
+
+
 def kernels_for(dtype):
-    code = g.F32 if dtype == "f32" else g.BF16
+    code = CODE[dtype]
     return [n for n in g.kernel_names() if g.gemm_kernel_dtype(g.kernel_id(n)) == code]
 
 
@@ -54,7 +61,7 @@ def takes(name, A, B):
     host tensors of the call's shape, strides and alignment)?"""
     M, K = A.shape
     N = B.shape[1]
-    dt = g.F32 if A.dtype == torch.float32 else g.BF16
+    dt = CODE_OF_TORCH[A.dtype]
     kid = g.kernel_id(name)
     with Forced(name):
         got = g.gemm_plan(dt, M, N, K, A.data_ptr() or (1 << 40), _ld(A),
@@ -100,7 +107,7 @@ def reference(w: Workload):
     if w.name not in _cache:
         A, B = workloads.make_inputs(w)
         An, Bn = workloads.as_numpy_operand(A), workloads.as_numpy_operand(B)
-        fn = oracle.gemm_f32 if w.dtype == "f32" else oracle.gemm_bf16
+        fn = ORACLE_FN[w.dtype]
         if w.M * w.N * w.K <= FULL_ORACLE_LIMIT:
             rows = None
             C, D = fn(An, Bn)
@@ -135,7 +142,7 @@ def check(w: Workload, kernel):
 SMALL_WORKLOADS = ["f32_256", "gpt_qkv", "gpt_mlp_up", "gpt_mlp_down", "skinny_1x8960x1536",
                    "skinny_7x4096x4096", "ragged_1000x3000x777", "ragged_4097x4095x1023",
                    "bf16_gpt_qkv", "bf16_gpt_mlp_down"]
-LARGE_WORKLOADS = ["f32_4096", "f32_8192", "bf16_8192"]
+LARGE_WORKLOADS = ["f32_4096", "f32_8192", "bf16_8192", "f16_8192"]
 
 
 def kernel_workload_cases():
@@ -165,11 +172,11 @@ EXACT_SHAPES = [(1, 1, 1), (3, 5, 7), (64, 64, 64), (65, 63, 67), (256, 256, 512
                 (520, 776, 2048), (16, 4096, 1024)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_small_integer_exact(dtype):
     """Integer operands: every kernel must be exact (bitwise equal to int64)."""
     gen = workloads.generator(77)
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
     for (M, N, K) in EXACT_SHAPES:
         A = workloads.small_int((M, K), lo, hi, gen, tdt)
@@ -185,9 +192,9 @@ def test_small_integer_exact(dtype):
             assert bad.size == 0, f"{k} {M}x{N}x{K}: {len(bad)} wrong, first {bad[:3].tolist()}"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_identity_and_permutation_exact(dtype):
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     gen = workloads.generator(78)
     for (K, N) in [(300, 260), (320, 264)]:
         B = workloads.draw((K, N), ("uniform", 1.0), gen).to(tdt)
@@ -213,9 +220,9 @@ SKINNY_M = [1, 2, 3, 5, 8, 9, 16]
 SKINNY_NK = [(1000, 37), (4100, 260), (8192, 44), (8200, 61), (16400, 36)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_skinny_configurations_exact(dtype):
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
     gen = workloads.generator(81)
     for (N, K) in SKINNY_NK:
@@ -228,7 +235,7 @@ def test_skinny_configurations_exact(dtype):
             exact_un = (A.to(torch.int64) @ B[:, 1:N + 1].to(torch.int64)).to(torch.float64).numpy()
             Ad = A.to(DEV)
             for Bd, ref, tag in ((Bd_al, exact, "aligned"), (Bd_un, exact_un, "unaligned")):
-                k = "skinny_f32" if dtype == "f32" else "skinny_bf16"
+                k = f"skinny_{dtype}"
                 assert takes(k, Ad, Bd)
                 say(f"[skinny] {dtype} {M}x{N}x{K} {tag}")
                 C = run(Ad, Bd, k).cpu().numpy().astype(np.float64)
@@ -236,11 +243,11 @@ def test_skinny_configurations_exact(dtype):
                 assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_ones_exact(dtype):
     """A = B = ones gives K everywhere; A = ones with integer B gives every
     row equal to B's column sums (exact: integer partial sums below 2^24)."""
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     gen = workloads.generator(82)
     for (M, N, K) in [(300, 260, 200), (33, 17, 4100), (1, 8960, 96), (257, 264, 1024)]:
         ones_a = torch.ones((M, K), dtype=tdt)
@@ -257,11 +264,11 @@ def test_ones_exact(dtype):
             assert np.all(C == colsum[None, :]), (k, M, N, K)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_brute_force_tiny_shapes(dtype):
     """Every (M, N, K) in {1..8}^3, every kernel that takes it, integer
     operands: bitwise equal to the int64 product."""
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
     gen = workloads.generator(83)
     A8 = workloads.small_int((8, 8), lo, hi, gen, tdt)
@@ -287,11 +294,11 @@ GUARD_CASES = [  # (M, N, K, extra A columns, extra B columns)
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_guard_bands_and_poisoned_padding(dtype):
     """Padding of A/B rows holds NaN and must not leak; C padding and the rows
     past M must keep their sentinel."""
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     gen = workloads.generator(79)
     for (M, N, K, pa, pb) in GUARD_CASES:
         A = workloads.small_int((M, K), -4, 4, gen, tdt)
@@ -313,9 +320,9 @@ def test_guard_bands_and_poisoned_padding(dtype):
             assert torch.all(Ch[:M, N:] == -777.0) and torch.all(Ch[M:, :] == -777.0)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_degenerate_shapes(dtype):
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     C = torch.full((5, 7), 3.0, device=DEV)
     g.gemm(torch.empty((5, 0), dtype=tdt, device=DEV), torch.empty((0, 7), dtype=tdt, device=DEV),
            out=C)
@@ -349,18 +356,19 @@ def test_non_default_stream():
 
 
 
-@pytest.mark.parametrize("dtype,M,N,K", [("f32", 32768, 256, 32768), ("bf16", 40960, 512, 32768)])
+@pytest.mark.parametrize("dtype,M,N,K", [("f32", 32768, 256, 32768), ("bf16", 40960, 512, 32768),
+                                         ("f16", 40960, 512, 32768)])
 def test_large_operands_64bit_offsets(dtype, M, N, K):
     """A spans more than 2^31 bytes (4 GiB fp32, 2.5 GiB bf16), so row
     offsets need 64-bit arithmetic.  Every kernel that takes the shape, and
     the table's choice, is checked on sampled rows (first, last, tile
     boundaries, random) against the oracle."""
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = TDT[dtype]
     gen = workloads.generator(80)
     A = workloads.draw((M, K), ("uniform", 1.0), gen).to(tdt)
     B = workloads.draw((K, N), ("uniform", 1.0), gen).to(tdt)
     rows = sample_rows(M, seed=3)
-    fn = oracle.gemm_f32 if dtype == "f32" else oracle.gemm_bf16
+    fn = ORACLE_FN[dtype]
     Cref, D = fn(workloads.as_numpy_operand(A[rows]), workloads.as_numpy_operand(B))
     Ad, Bd = A.to(DEV), B.to(DEV)
     del A

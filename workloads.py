@@ -35,7 +35,7 @@ class Workload:
     M: int
     N: int
     K: int
-    dtype: str                    # "f32" or "bf16" (inputs); output is always fp32
+    dtype: str                    # "f32", "bf16" or "f16" (inputs); output is always fp32
     dist_a: Tuple[str, float] = ("uniform", 1.0)
     dist_b: Tuple[str, float] = ("uniform", 1.0)
     note: str = ""
@@ -77,6 +77,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
              note="GPT QKV projection, bf16 operands"),
     Workload("bf16_gpt_mlp_down", 16384, 384, 1536, "bf16", _ACT, _WGT,
              note="GPT MLP down, bf16 operands"),
+    # fp16 operands (the same draws rounded to binary16) at the headline size
+    Workload("f16_8192", 8192, 8192, 8192, "f16", ("normal", 1.0), ("normal", 1.0),
+             note="fp16 in / fp32 accumulate at the headline size"),
 ]}
 
 # Groups of the workload list as the parity tests and the benchmark use them.
@@ -85,6 +88,11 @@ PARITY_WORKLOADS: List[str] = [
     "skinny_1x8960x1536", "skinny_7x4096x4096", "ragged_1000x3000x777",
     "ragged_4097x4095x1023", "f32_8192",
 ]
+
+
+# Operand types: fp32, and bf16 or fp16 rounded from the fp32 draw (round to
+# nearest even); the output is fp32 for all three.
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def generator(seed: int = SEED) -> torch.Generator:
@@ -107,9 +115,7 @@ def make_inputs(w: Workload, seed: int = SEED) -> Tuple[torch.Tensor, torch.Tens
     g = generator(seed)
     A = draw((w.M, w.K), w.dist_a, g)
     B = draw((w.K, w.N), w.dist_b, g)
-    if w.dtype == "bf16":
-        A, B = A.to(torch.bfloat16), B.to(torch.bfloat16)
-    return A, B
+    return A.to(TORCH_DTYPE[w.dtype]), B.to(TORCH_DTYPE[w.dtype])
 
 
 def small_int(shape, lo: int, hi: int, g: torch.Generator, dtype=torch.float32) -> torch.Tensor:
@@ -192,9 +198,7 @@ def make_general_inputs(w: GeneralWorkload, seed: int = SEED) -> Tuple[torch.Ten
     lead = (w.batch,) if w.batch > 1 else ()
     A = draw(lead + ((w.K, w.M) if w.ta else (w.M, w.K)), w.dist_a, g)
     B = draw(lead + ((w.N, w.K) if w.tb else (w.K, w.N)), w.dist_b, g)
-    if w.dtype == "bf16":
-        A, B = A.to(torch.bfloat16), B.to(torch.bfloat16)
-    return A, B
+    return A.to(TORCH_DTYPE[w.dtype]), B.to(TORCH_DTYPE[w.dtype])
 
 
 def general_views(w: GeneralWorkload, A: torch.Tensor, B: torch.Tensor):
