@@ -141,6 +141,7 @@ DISPATCH_GOLDEN = {
     "ragged_4097x4095x1023": "mfma_f32_narrow128x64",
     "bf16_gpt_qkv": "mfma_bf16_direct128",
     "bf16_gpt_mlp_down": "mfma_bf16_direct128",
+    "f16_8192": "mfma_f16_direct",
 }
 
 
@@ -148,7 +149,7 @@ DISPATCH_GOLDEN = {
 def test_dispatch_golden(name):
     import workloads
     w = workloads.WORKLOADS[name]
-    dt = g.F32 if w.dtype == "f32" else g.BF16
+    dt = {"f32": g.F32, "bf16": g.BF16, "f16": g.F16}[w.dtype]
     assert g.gemm_kernel_name(g.gemm_plan(dt, w.M, w.N, w.K, A=PA, B=PB, C=PC)) == DISPATCH_GOLDEN[name]
 
 

@@ -81,7 +81,7 @@ def takes(kernel, a, b, out=None):
     ldc, sc, cp = N, M * N, 3 << 40
     if out is not None:
         ldc, sc, cp = out.stride(-2), g._batch_stride(out), out.data_ptr()
-    dt = g.F32 if a.dtype == torch.float32 else g.BF16
+    dt = {torch.float32: g.F32, torch.bfloat16: g.BF16, torch.float16: g.F16}[a.dtype]
     with Forced(kernel):
         got = g.gemm_plan_batched(dt, ta, tb, M, N, K, batch, a.data_ptr() or (1 << 40), lda,
                                   g._batch_stride(a), b.data_ptr() or (2 << 40), ldb,
