@@ -550,7 +550,8 @@ __device__ __forceinline__ float masked(float x, uint32_t keep)
 
 __device__ __forceinline__ int64_t clampk(int64_t k, int64_t K) { return k < K ? k : K - 1; }
 
-// The four partial blocks of a work-group's waves, added in wave order, to C.
+// The kW partial blocks of a work-group's waves, added in wave order, to C.
+template <int kW = 4>
 __device__ __forceinline__ void reduce_store(float *red, const f32x16 &acc, int wave, int lane,
                                              float *__restrict__ C, int64_t ldc, int64_t M,
                                              int64_t N, int64_t m0, int64_t n0)
@@ -560,25 +561,31 @@ __device__ __forceinline__ void reduce_store(float *red, const f32x16 &acc, int 
     for (int r = 0; r < 16; ++r)
         red[(wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3)) * kPad + c] = acc[r];
     __syncthreads();
-    for (int e = threadIdx.x; e < 32 * 32; e += kThreads) {
+    for (int e = threadIdx.x; e < 32 * 32; e += 64 * kW) {
         const int rr = e >> 5, cc = e & 31;
         float v = red[rr * kPad + cc];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) v += red[(w * 32 + rr) * kPad + cc];
+        for (int w = 1; w < kW; ++w) v += red[(w * 32 + rr) * kPad + cc];
         if (m0 + rr < M && n0 + cc < N) store_c_stream(C + (m0 + rr) * ldc + n0 + cc, v);
     }
 }
 
+// Waves per work-group of the fp32 split-K kernel and K groups each loads
+// per step.  Measured on the GPT QKV weight gradient (384 x 1152 x 16384,
+// A transposed): 4 waves x 8 groups 49.4 TFLOP/s (two waves per SIMD);
+// 8 waves x 4 groups 20.0, although it runs four waves per SIMD.
+constexpr int kSkWaves = 4, kSkU = 8;
+
 // fp32 (v_mfma_f32_32x32x2_f32): group g is k = 8g .. 8g+7, lane half h
 // carries k = 8g + 4h + j for MFMA j.
 template <bool TA, bool TB, bool kVecA, bool kVecB>
-__global__ __launch_bounds__(kThreads) void f32_kernel(
+__global__ __launch_bounds__(64 * kSkWaves) void f32_kernel(
     int64_t M, int64_t N, int64_t K, const float *__restrict__ A, int64_t lda, int64_t sa,
     const float *__restrict__ B, int64_t ldb, int64_t sb, float *__restrict__ C, int64_t ldc,
     int64_t sc, int64_t batch, int64_t tiles_m, int64_t tiles_n)
 {
-    constexpr int kU = 8;
-    __shared__ float red[4 * 32 * kPad];
+    constexpr int kU = kSkU, kW = kSkWaves;
+    __shared__ float red[kW * 32 * kPad];
     const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
     A += t.b * sa;
     B += t.b * sb;
@@ -598,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
     auto load = [&](int64_t g0, float (&a)[kU][4], float (&b)[kU][4]) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t k = 8 * (g0 + 4 * u) + 4 * h;
+            const int64_t k = 8 * (g0 + kW * u) + 4 * h;
             if constexpr (!TA && kVecA) {
                 // K % 4 == 0 here, so the four k are all in range or all out
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(A + row * lda + (k < K ? k : K - 4));
@@ -639,16 +646,16 @@ __global__ __launch_bounds__(kThreads) void f32_kernel(
     int64_t g0 = wave;
     if (g0 < groups) load(g0, a0, b0);
     while (g0 < groups) {
-        const int64_t g1 = g0 + 4 * kU;
+        const int64_t g1 = g0 + kW * kU;
         if (g1 < groups) load(g1, a1, b1);
         mfmas(a0, b0);
         if (g1 >= groups) break;
-        const int64_t g2 = g1 + 4 * kU;
+        const int64_t g2 = g1 + kW * kU;
         if (g2 < groups) load(g2, a0, b0);
         mfmas(a1, b1);
         g0 = g2;
     }
-    reduce_store(red, acc, wave, lane, C, ldc, M, N, m0, n0);
+    reduce_store<kW>(red, acc, wave, lane, C, ldc, M, N, m0, n0);
 }
 
 // bf16 (v_mfma_f32_32x32x16_bf16): group g is k = 16g .. 16g+15, lane half h
@@ -807,7 +814,7 @@ void launch_sk_layout(const Problem &p, uint32_t blocks, int64_t tm, int64_t tn,
     const auto *A = static_cast<const T *>(p.A);
     const auto *B = static_cast<const T *>(p.B);
     if constexpr (sizeof(T) == 4)
-        hipLaunchKernelGGL((sk::f32_kernel<TA, TB, VA, VB>), dim3(blocks), dim3(kThreads), 0, s,
+        hipLaunchKernelGGL((sk::f32_kernel<TA, TB, VA, VB>), dim3(blocks), dim3(64 * sk::kSkWaves), 0, s,
                            p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc,
                            p.batch, tm, tn);
     else
