@@ -203,6 +203,8 @@ def _layout(t: torch.Tensor, name: str):
 _FN = {torch.float32: ("gemm_f32", "gemm_f32_batched"),
        torch.bfloat16: ("gemm_bf16_f32acc", "gemm_bf16_f32acc_batched"),
        torch.float16: ("gemm_f16_f32acc", "gemm_f16_f32acc_batched")}
+_PLAIN = {dt: getattr(lib, names[0]) for dt, names in _FN.items()}
+_BATCHED = {dt: getattr(lib, names[1]) for dt, names in _FN.items()}
 
 
 def _batch_stride(t: torch.Tensor) -> int:
@@ -220,13 +222,60 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
     such as ``w.t()`` is read in place as a transposed factor.  The result is
     (M, N) for two 2-D operands, else (batch, M, N).  The call is asynchronous
     on `stream` (default: the current stream of a's device)."""
-    if a.dim() not in (2, 3) or b.dim() not in (2, 3):
-        raise ValueError("gemm takes 2-D or 3-D tensors")
+    if (a.dim() == 2 and b.dim() == 2 and (a.shape[1] <= 1 or a.stride(1) == 1)
+            and (b.shape[1] <= 1 or b.stride(1) == 1)):
+        return _gemm_plain(a, b, out, stream)
+    return _gemm_general(a, b, out, stream)
+
+
+def _check_operands(a, b):
     if a.dtype != b.dtype or a.dtype not in _FN:
         raise TypeError("operands must both be float32, both bfloat16 or both float16, "
                         f"got {a.dtype}, {b.dtype}")
     if a.device.type != "cuda" or b.device != a.device:
         raise ValueError("operands must be on the same GPU")
+
+
+def _launch(fn, what, dev, args):
+    # The library launches on the calling thread's current HIP device.
+    if dev != torch.cuda.current_device():
+        with torch.cuda.device(dev):
+            rc = fn(*args)
+    else:
+        rc = fn(*args)
+    if rc != HIP_SUCCESS:
+        raise GemmError(rc, what)
+
+
+def _gemm_plain(a, b, out, stream):
+    """Two 2-D operands with unit column stride: the plain entry points (the
+    short path: the smallest products take about as long as this call)."""
+    _check_operands(a, b)
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif (out.dtype != torch.float32 or out.shape != (M, N) or out.device != a.device
+          or (N > 1 and out.stride(1) != 1)):
+        raise ValueError("out must be a float32 (M, N) tensor with unit column stride on a's GPU")
+    dev = a.get_device()
+    # The raw handle of the current stream, without building a Stream object
+    # (a few microseconds per call, which is the whole kernel time of the
+    # smallest products).
+    raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
+    name = _FN[a.dtype][0]
+    _launch(_PLAIN[a.dtype], name, dev,
+            (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), raw))
+    return out
+
+
+def _gemm_general(a, b, out, stream):
+    """Transposed views and batches: the *_batched entry points."""
+    if a.dim() not in (2, 3) or b.dim() not in (2, 3):
+        raise ValueError("gemm takes 2-D or 3-D tensors")
+    _check_operands(a, b)
     M, K = a.shape[-2], a.shape[-1]
     K2, N = b.shape[-2], b.shape[-1]
     if K != K2:
@@ -244,26 +293,14 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
           or (N > 1 and out.stride(-1) != 1)):
         raise ValueError(f"out must be a float32 {shape} tensor with unit column stride on a's GPU")
     ldc = out.stride(-2) if M > 1 else max(N, 1)
-    plain_name, batched_name = _FN[a.dtype]
     dev = a.get_device()
-    # The raw handle of the current stream, without building a Stream object
-    # (a few microseconds per call, which is the whole kernel time of the
-    # smallest products).
     raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
     if not batched and not ta and not tb:
-        what = plain_name
+        name, fn = _FN[a.dtype][0], _PLAIN[a.dtype]
         args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, raw)
     else:
-        what = batched_name
+        name, fn = _FN[a.dtype][1], _BATCHED[a.dtype]
         args = (int(ta), int(tb), M, N, K, a.data_ptr(), lda, _batch_stride(a), b.data_ptr(),
                 ldb, _batch_stride(b), out.data_ptr(), ldc, _batch_stride(out), batch, raw)
-    fn = getattr(lib, what)
-    # The library launches on the calling thread's current HIP device.
-    if dev != torch.cuda.current_device():
-        with torch.cuda.device(dev):
-            rc = fn(*args)
-    else:
-        rc = fn(*args)
-    if rc != HIP_SUCCESS:
-        raise GemmError(rc, what)
+    _launch(fn, name, dev, args)
     return out

@@ -1,6 +1,9 @@
 #!/usr/bin/env python3
 """Time every kernel of libmi355gemm on every workload it takes.
 
+The workloads are the plain products of the benchmark set and the
+transposed-factor and batched ones (GPT backward pass, attention).
+
 For each (workload, kernel) pair the kernel is forced through the library's
 test hook and timed with HIP events around back-to-back calls on one stream
 (median of several windows).  Bandwidth-bound shapes rotate through copies of
@@ -39,6 +42,36 @@ from dense_gemm_17_amd.measure import ClockSampler, toolchain  # noqa: E402
 
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}
 LLC_BYTES = 256 * 1024 * 1024
+CODE = {"f32": g.F32, "bf16": g.BF16, "f16": g.F16}
+ALL_WORKLOADS = {**workloads.WORKLOADS, **workloads.GENERAL_WORKLOADS}
+
+
+def operands(w, dev):
+    """(a, b, c) on the device for workload w: plain products as (M, K),
+    (K, N); transposed or batched ones as the views a caller passes."""
+    if w.name in workloads.GENERAL_WORKLOADS:
+        As, Bs = workloads.make_general_inputs(w)
+        a, b = workloads.general_views(w, As.to(dev), Bs.to(dev))
+        shape = (w.batch, w.M, w.N) if w.batch > 1 else (w.M, w.N)
+    else:
+        A, B = workloads.make_inputs(w)
+        a, b, shape = A.to(dev), B.to(dev), (w.M, w.N)
+    return a, b, torch.empty(shape, dtype=torch.float32, device=dev)
+
+
+def plan(w, a, b, c):
+    """The kernel id the library picks (or the forced one accepts) for
+    gemm(a, b, out=c), as a pure host call."""
+    code = CODE[w.dtype]
+    if w.name not in workloads.GENERAL_WORKLOADS:
+        return g.gemm_plan(code, w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(),
+                           b.stride(0), c.data_ptr(), c.stride(0))
+    ta, lda = g._layout(a, "a")
+    tb, ldb = g._layout(b, "b")
+    return g.gemm_plan_batched(code, ta, tb, w.M, w.N, w.K, w.batch, A=a.data_ptr(), lda=lda,
+                               stride_a=g._batch_stride(a), B=b.data_ptr(), ldb=ldb,
+                               stride_b=g._batch_stride(b), C=c.data_ptr(), ldc=c.stride(-2),
+                               stride_c=g._batch_stride(c))
 
 
 def time_calls(fn, windows: int, target_ms: float = 60.0, max_reps: int = 2000) -> float:
@@ -94,7 +127,7 @@ def repeat_in_processes(args):
     for (wl, k), ds in keyed.items():
         ms = [d["ms"] for d in ds]
         med = statistics.median(ms)
-        w = workloads.WORKLOADS[wl]
+        w = ALL_WORKLOADS[wl]
         tflops = w.flops / (med * 1e-3) / 1e12
         sclk = [d["sclk_mhz"]["median"] for d in ds if d.get("sclk_mhz")]
         print(json.dumps({
@@ -109,7 +142,7 @@ def repeat_in_processes(args):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--workloads", default=",".join(workloads.WORKLOADS))
+    ap.add_argument("--workloads", default=",".join(ALL_WORKLOADS))
     ap.add_argument("--windows", type=int, default=5)
     ap.add_argument("--processes", type=int, default=1)
     ap.add_argument("--table-only", action="store_true",
@@ -135,18 +168,12 @@ def main():
                           "toolchain": toolchain(g.gemm_build_info())}), flush=True)
 
     for name in args.workloads.split(","):
-        w = workloads.WORKLOADS[name]
-        A, B = workloads.make_inputs(w)
+        w = ALL_WORKLOADS[name]
         per_copy = w.algorithmic_bytes
         copies = 1 if per_copy * 2 > LLC_BYTES else max(2, -(-2 * LLC_BYTES // per_copy))
-        ops = []
-        for _ in range(copies):
-            ops.append((A.to(dev), B.to(dev),
-                        torch.empty((w.M, w.N), dtype=torch.float32, device=dev)))
-        code = {"f32": g.F32, "bf16": g.BF16, "f16": g.F16}[w.dtype]
-        Ad, Bd, Cd = ops[0]
-        table = g.gemm_plan(code, w.M, w.N, w.K, Ad.data_ptr(), Ad.stride(0), Bd.data_ptr(),
-                            Bd.stride(0), Cd.data_ptr(), Cd.stride(0))
+        ops = [operands(w, dev) for _ in range(copies)]
+        code = CODE[w.dtype]
+        table = plan(w, *ops[0])
         for kid in range(g.gemm_kernel_count()):
             if g.gemm_kernel_dtype(kid) != code:
                 continue
@@ -158,8 +185,7 @@ def main():
                 continue
             g.gemm_force_kernel(kid)
             try:
-                if g.gemm_plan(code, w.M, w.N, w.K, Ad.data_ptr(), Ad.stride(0), Bd.data_ptr(),
-                               Bd.stride(0), Cd.data_ptr(), Cd.stride(0)) != kid:
+                if plan(w, *ops[0]) != kid:
                     continue
                 state = {"i": 0}
 
