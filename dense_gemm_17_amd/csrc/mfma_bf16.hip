@@ -262,11 +262,14 @@ void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restric
 // last tile into a stage nobody reads again instead of being branched
 // around.
 //
-// Shapes: K a multiple of 32, N a multiple of 8, 16-byte aligned A and B
-// with lda and ldb multiples of 8, lane offsets within 32 bits (256 * lda
-// and 32 * ldb below 2^31 elements).  Rows of A past M and columns of B past
-// N are fetched from the last valid row / chunk (their products land only
-// in rows and columns of C that are not stored).
+// Shapes: K a multiple of 32 (and K > 0), 16-byte aligned A and B with lda
+// and ldb multiples of 8, lane offsets within 32 bits: a factor stored with
+// rows of K (A as written, B transposed) within 256 stored rows, one stored
+// with rows of M or N (A transposed, B as written) within 32 stored rows,
+// and that dimension a multiple of 8.  Rows of A past M and columns of B
+// past N are fetched from the last valid row / chunk (their products land
+// only in rows and columns of C that are not stored).  The same kernels run
+// fp16 operands with the fp16 instruction, and strided batches as one grid.
 
 constexpr int DBK = 32;
 constexpr int DSTAGES = 4;

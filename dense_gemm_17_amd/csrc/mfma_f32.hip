@@ -35,10 +35,11 @@
 // Those are the register-staged kernels (mfma_f32, mfma_f32_128).  The
 // LDS-direct kernels further down (mfma_f32_direct with 256 x 256 tiles,
 // mfma_f32_direct128 with 128 x 128, mfma_f32_direct128x64 with 128 x 64,
-// and mfma_f32_narrow128 / mfma_f32_narrow128x64, the 128-row ones with
-// 4-byte loads for any layout) are one template: global -> LDS without registers, a four-stage
-// LDS ring, fragments read one K group ahead, one barrier per tile; they
-// are what the dispatch table runs wherever they apply.
+// mfma_f32_direct64 with 64 x 64, and the narrow ones with 4-byte loads for
+// any layout) are one template: global -> LDS without registers, a
+// four-stage LDS ring, fragments read one K group ahead, one barrier per
+// tile; they also take a factor stored transposed and strided batches, and
+// they are what the dispatch table runs wherever they apply.
 #include <type_traits>
 
 #include "gemm_internal.h"
@@ -302,11 +303,16 @@ hipError_t launch_tiles(const Problem &p, hipStream_t s)
 // re-fetch the last tile into a stage nobody reads again instead of being
 // branched around.
 //
-// Shapes: K a multiple of 16, N a multiple of 4, 16-byte aligned A and B
-// with lda and ldb multiples of 4, and lane offsets within 32 bits
-// (256 * lda and 16 * ldb below 2^30 elements).  Rows of A past M and
-// columns of B past N are fetched from the last valid row / chunk (their
-// products land only in rows and columns of C that are not stored).
+// Shapes: K a multiple of 16 (and K > 0), 16-byte aligned A and B with lda
+// and ldb multiples of 4, and lane offsets within 32 bits.  A factor stored
+// with rows of K (A as written, B transposed) has its lane offsets within a
+// panel of up to 256 stored rows; one stored with rows of M or N (A
+// transposed, B as written) within 16 stored rows, and that dimension a
+// multiple of 4.  Rows of A past M and columns of B past N are fetched from
+// the last valid row / chunk (their products land only in rows and columns
+// of C that are not stored).  With batch > 1 the grid covers the tiles of
+// every product (the 4- and 16-byte narrow and direct tiles alike; the
+// narrow ones take untransposed factors only).
 
 constexpr int DBK = 16;           // K step of the direct variants
 constexpr int DSTAGES = 4;
