@@ -426,18 +426,29 @@ def test_concurrent_host_threads_and_streams():
 def test_graph_capture_replays_match_eager():
     """Calls captured into a HIP graph (no memset nodes: K = 0 is a fill
     kernel) replay with the eager result, replay after replay, with eager
-    work and synchronisation between replays."""
+    work and synchronisation between replays; plain, transposed and batched
+    calls in all three operand types."""
     gen = workloads.generator(85)
-    specs = [(1024, 1024, 512, torch.float32), (512, 768, 256, torch.bfloat16),
-             (3, 4096, 1024, torch.float32), (300, 260, 0, torch.float32),
-             (1000, 3000, 777, torch.float32)]
+    # (M, N, K, dtype, batch, A stored transposed, B stored transposed)
+    specs = [(1024, 1024, 512, torch.float32, 1, False, False),
+             (512, 768, 256, torch.bfloat16, 1, False, False),
+             (3, 4096, 1024, torch.float32, 1, False, False),
+             (300, 260, 0, torch.float32, 1, False, False),
+             (1000, 3000, 777, torch.float32, 1, False, False),
+             (256, 256, 64, torch.float32, 12, False, True),       # batched, B^T
+             (384, 1152, 4096, torch.float32, 1, True, False),     # A^T, split-K
+             (512, 264, 96, torch.float16, 3, True, True),
+             (300, 270, 100, torch.bfloat16, 2, True, False)]      # general family
     ins, eager, outs = [], [], []
-    for (M, N, K, dt) in specs:
-        A = workloads.draw((M, K), ("uniform", 1.0), gen).to(dt).to(DEV)
-        B = workloads.draw((K, N), ("uniform", 1.0), gen).to(dt).to(DEV)
+    for (M, N, K, dt, nb, ta, tb) in specs:
+        lead = (nb,) if nb > 1 else ()
+        A = workloads.draw(lead + ((K, M) if ta else (M, K)), ("uniform", 1.0), gen).to(dt).to(DEV)
+        B = workloads.draw(lead + ((N, K) if tb else (K, N)), ("uniform", 1.0), gen).to(dt).to(DEV)
+        A = A.transpose(-1, -2) if ta else A
+        B = B.transpose(-1, -2) if tb else B
         ins.append((A, B))
         eager.append(run(A, B).clone())
-        outs.append(torch.full((M, N), 7.0, device=DEV))
+        outs.append(torch.full(lead + (M, N), 7.0, device=DEV))
     graph = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
