@@ -346,10 +346,11 @@ def main():
     if args.copy_calibration:
         copy = copy_calibration(dev)
 
-    others = general = None
+    others = general = sequence = None
     if not args.no_configs:
         others = other_configs(dev, set(names), args.check_rows)
         general = general_configs(dev, args.check_rows)
+        sequence = sequence_config(dev)
 
     ceiling = None
     if not args.no_ceiling:
@@ -389,6 +390,9 @@ def main():
         # the same for products with a transposed factor or a batch (the GPT
         # backward pass and attention shapes)
         "general_configs": general,
+        # a launch-bound sequence (one GPT forward pass over 256 tokens):
+        # back-to-back calls against the same calls replayed from a HIP graph
+        "sequence": sequence,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels
         "env": dict(clocks.summary(), toolchain=toolchain(g.gemm_build_info())),
@@ -503,6 +507,68 @@ def time_calls(dev, call, copies):
     return ms, graph_ms, clocks
 
 
+def sequence_config(dev, windows: int = 5, reps: int = 20):
+    """The 37 products of one GPT forward pass over 256 tokens (fp32),
+    timed as back-to-back calls through the binding and as the same calls
+    captured once into a HIP graph and replayed; the graph's outputs are
+    checked bit for bit against the eager ones."""
+    import dense_gemm_17_amd as g
+    seq = workloads.gpt_forward_sequence()
+    gen = workloads.generator()
+    calls = []
+    for (name, nb, M, N, K, ta, tb) in seq:
+        lead = (nb,) if nb > 1 else ()
+        A = workloads.draw(lead + ((K, M) if ta else (M, K)), ("normal", 1.0), gen).to(dev)
+        B = workloads.draw(lead + ((N, K) if tb else (K, N)), ("normal", 1.0), gen).to(dev)
+        C = torch.empty(lead + (M, N), dtype=torch.float32, device=dev)
+        calls.append((A.transpose(-1, -2) if ta else A, B.transpose(-1, -2) if tb else B, C))
+    flops = sum(2 * nb * M * N * K for (_, nb, M, N, K, _, _) in seq)
+
+    def run_all():
+        for a, b, c in calls:
+            g.gemm(a, b, out=c)
+
+    st = torch.cuda.Stream(dev)
+    st.wait_stream(torch.cuda.current_stream(dev))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        ts = []
+        for _ in range(windows):
+            e0.record(st)
+            for _ in range(reps):
+                fn()
+            e1.record(st)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
+        return float(np.median(ts))
+
+    with torch.cuda.stream(st):
+        for _ in range(3):
+            run_all()
+        torch.cuda.synchronize()
+        eager_ms = timed(run_all)
+        eager_out = [c.clone() for (_, _, c) in calls]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            run_all()
+        for (_, _, c) in calls:
+            c.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(c, e) for (_, _, c), e in zip(calls, eager_out))
+        graph_ms = timed(graph.replay)
+        del graph
+    kernels = sorted({g.gemm_kernel_name(g.gemm_last_kernel())})
+    return {"calls": len(seq), "gflop": round(flops / 1e9, 3),
+            "eager_us": round(eager_ms * 1e3, 1), "graph_us": round(graph_ms * 1e3, 1),
+            "eager_tflops": round(flops / (eager_ms * 1e-3) / 1e12, 2),
+            "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 2),
+            "eager_us_per_call": round(eager_ms * 1e3 / len(seq), 2),
+            "graph_us_per_call": round(graph_ms * 1e3 / len(seq), 2),
+            "graph_equals_eager": same, "last_kernel": kernels[0]}
+
+
 def general_configs(dev, check_rows):
     """Transposed-factor and batched products (the GPT backward pass and
     attention shapes): the table's kernel timed like the configurations
@@ -547,6 +613,38 @@ def general_configs(dev, check_rows):
         gbs = per_copy / (ms * 1e-3) / 1e9
         ridge = PEAK_TFLOPS[w.dtype] * 1e3 / HBM_PEAK_GBS
         hbm = w.flops / per_copy < ridge
+        ws_rec = None
+        ws_bytes = g.gemm_workspace_size(CODE[w.dtype], w.ta, w.tb, w.M, w.N, w.K, w.batch)
+        if ws_bytes:
+            # the same call with a workspace: K split over work-groups
+            wsbuf = torch.empty((ws_bytes // 4,), dtype=torch.float32, device=dev)
+            state["i"] = 0
+
+            def call_ws():
+                a, b, c = ops[state["i"] % copies]
+                state["i"] += 1
+                g.gemm(a, b, out=c, workspace=wsbuf)
+
+            ms_ws, _, _ = time_calls(dev, call_ws, copies)
+            c0w = ops[0][2].reshape(w.batch, w.M, w.N)
+            e_ws = 0.0
+            for bi in sorted({0, w.batch - 1}):
+                rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, check_rows),
+                                                             replace=False).tolist()))
+                A_b = As[bi] if As.dim() == 3 else As
+                B_b = Bs[bi] if Bs.dim() == 3 else Bs
+                A_rows = (A_b.t()[rows] if w.ta else A_b[rows]).contiguous()
+                Cref, D = oracle.gemm_batched(workloads.as_numpy_operand(A_rows),
+                                              workloads.as_numpy_operand(B_b), False, w.tb,
+                                              threads=cpu_threads())
+                e, _, _ = oracle.normalized_error(c0w[bi][rows].cpu().numpy(), Cref, D)
+                e_ws = max(e_ws, e)
+            tf_ws = w.flops / (ms_ws * 1e-3) / 1e12
+            ws_rec = {"workspace_bytes": ws_bytes, "us_per_call": round(ms_ws * 1e3, 2),
+                      "tflops": round(tf_ws, 2), "frac": round(tf_ws / PEAK_TFLOPS[w.dtype], 4),
+                      "partials_kernel": g.gemm_kernel_name(g.gemm_last_kernel()),
+                      "max_norm_err_sampled": float(f"{e_ws:.3e}")}
+            del wsbuf
         out[name] = {
             "batch": w.batch, "M": w.M, "N": w.N, "K": w.K, "transa": w.ta, "transb": w.tb,
             "dtype": w.dtype, "kernel": kernel,
@@ -556,6 +654,7 @@ def general_configs(dev, check_rows):
             "us_per_call_graph": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
             "operand_copies": copies, "max_norm_err_sampled": float(f"{err:.3e}"),
             "sclk_mhz": (clocks.summary()["sclk_mhz"] or {}).get("median"),
+            "with_workspace": ws_rec,
         }
         del ops
         torch.cuda.empty_cache()

@@ -43,6 +43,13 @@ def _load() -> ctypes.CDLL:
         getattr(lib, name).argtypes = bsig
         getattr(lib, name).restype = ci
     sz = ctypes.c_size_t
+    wsig = bsig[:-1] + [vp, sz, vp]
+    for name in ("gemm_f32_batched_ws", "gemm_bf16_f32acc_batched_ws",
+                 "gemm_f16_f32acc_batched_ws"):
+        getattr(lib, name).argtypes = wsig
+        getattr(lib, name).restype = ci
+    lib.gemm_workspace_size.argtypes = [ci, ci, ci, i64, i64, i64, i64]
+    lib.gemm_workspace_size.restype = sz
     lib.gemm_plan_batched.argtypes = [ci, ci, ci, i64, i64, i64, sz, i64, i64, sz, i64, i64,
                                       sz, i64, i64, i64]
     lib.gemm_plan_batched.restype = ci
@@ -68,7 +75,9 @@ lib = _load()
 
 # Every symbol include/mi355gemm.h declares.
 EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched",
-           "gemm_bf16_f32acc_batched", "gemm_f16_f32acc_batched", "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
+           "gemm_bf16_f32acc_batched", "gemm_f16_f32acc_batched", "gemm_f32_batched_ws",
+           "gemm_bf16_f32acc_batched_ws", "gemm_f16_f32acc_batched_ws", "gemm_workspace_size",
+           "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
            "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info")
 
 
@@ -102,6 +111,10 @@ def gemm_bf16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, 
                              ldc, stride_c, batch, stream) -> int:
     return lib.gemm_bf16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb,
                                         stride_b, C, ldc, stride_c, batch, stream)
+
+
+def gemm_workspace_size(dtype, transa, transb, M, N, K, batch=1) -> int:
+    return lib.gemm_workspace_size(dtype, int(transa), int(transb), M, N, K, batch)
 
 
 def gemm_kernel_count() -> int:
@@ -204,6 +217,7 @@ _FN = {torch.float32: ("gemm_f32", "gemm_f32_batched"),
        torch.bfloat16: ("gemm_bf16_f32acc", "gemm_bf16_f32acc_batched"),
        torch.float16: ("gemm_f16_f32acc", "gemm_f16_f32acc_batched")}
 _PLAIN = {dt: getattr(lib, names[0]) for dt, names in _FN.items()}
+_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 _BATCHED = {dt: getattr(lib, names[1]) for dt, names in _FN.items()}
 
 
@@ -212,7 +226,8 @@ def _batch_stride(t: torch.Tensor) -> int:
 
 
 def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
-         stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+         stream: Optional[torch.cuda.Stream] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out = a @ b on the GPU (fp32·fp32, bf16·bf16 or fp16·fp16 -> fp32).
 
     a is (M, K) or (batch, M, K), b is (K, N) or (batch, K, N); a 2-D operand
@@ -221,11 +236,24 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
     along its rows or its columns: rows may be padded, and a transposed view
     such as ``w.t()`` is read in place as a transposed factor.  The result is
     (M, N) for two 2-D operands, else (batch, M, N).  The call is asynchronous
-    on `stream` (default: the current stream of a's device)."""
-    if (a.dim() == 2 and b.dim() == 2 and (a.shape[1] <= 1 or a.stride(1) == 1)
-            and (b.shape[1] <= 1 or b.stride(1) == 1)):
+    on `stream` (default: the current stream of a's device).  `workspace`
+    (a device tensor of at least ``workspace_size(a, b)`` bytes) lets a
+    single product with a small output split its K range over work-groups
+    (the *_ws entry points); the caller keeps it alive until the stream has
+    passed the call."""
+    if workspace is None and (a.dim() == 2 and b.dim() == 2 and (a.shape[1] <= 1 or a.stride(1) == 1)
+                              and (b.shape[1] <= 1 or b.stride(1) == 1)):
         return _gemm_plain(a, b, out, stream)
-    return _gemm_general(a, b, out, stream)
+    return _gemm_general(a, b, out, stream, workspace)
+
+
+def workspace_size(a: torch.Tensor, b: torch.Tensor) -> int:
+    """Bytes of workspace gemm(a, b, workspace=...) can use (0: none)."""
+    if a.dim() != 2 or b.dim() != 2:
+        return 0
+    ta, _ = _layout(a, "a")
+    tb, _ = _layout(b, "b")
+    return gemm_workspace_size(_CODE[a.dtype], ta, tb, a.shape[0], b.shape[1], a.shape[1], 1)
 
 
 def _check_operands(a, b):
@@ -271,8 +299,9 @@ def _gemm_plain(a, b, out, stream):
     return out
 
 
-def _gemm_general(a, b, out, stream):
-    """Transposed views and batches: the *_batched entry points."""
+def _gemm_general(a, b, out, stream, workspace=None):
+    """Transposed views and batches: the *_batched entry points (*_ws with a
+    workspace)."""
     if a.dim() not in (2, 3) or b.dim() not in (2, 3):
         raise ValueError("gemm takes 2-D or 3-D tensors")
     _check_operands(a, b)
@@ -295,7 +324,15 @@ def _gemm_general(a, b, out, stream):
     ldc = out.stride(-2) if M > 1 else max(N, 1)
     dev = a.get_device()
     raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
-    if not batched and not ta and not tb:
+    if workspace is not None:
+        if workspace.device != a.device:
+            raise ValueError("workspace must be on the operands' GPU")
+        name = _FN[a.dtype][1] + "_ws"
+        fn = getattr(lib, name)
+        args = (int(ta), int(tb), M, N, K, a.data_ptr(), lda, _batch_stride(a), b.data_ptr(),
+                ldb, _batch_stride(b), out.data_ptr(), ldc, _batch_stride(out), batch,
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(), raw)
+    elif not batched and not ta and not tb:
         name, fn = _FN[a.dtype][0], _PLAIN[a.dtype]
         args = (M, N, K, a.data_ptr(), lda, b.data_ptr(), ldb, out.data_ptr(), ldc, raw)
     else:

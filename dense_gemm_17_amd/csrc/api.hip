@@ -325,6 +325,63 @@ int run(const Problem &p, hipStream_t stream)
     return err;
 }
 
+// ---- K split over work-groups, through a caller's workspace ------------------
+// A single product whose output has fewer 128 x 128 tiles than CUs (weight
+// gradients: a d_in x d_out output summed over every token) leaves most CUs
+// idle however its tiles are cut.  With a workspace the K range is split in
+// S equal chunks: the S partial products run as one strided batch (the
+// tiled kernels then fill the CUs) into S packed M x N fp32 buffers, and a
+// second kernel adds them in the order 0, 1, .., S-1 (deterministic).
+// S is the smallest power of two giving at least kCUs tiles of 128 x 128,
+// with chunks a multiple of 32 and at least 256 long; 1 means no split.
+int64_t split_count(const Problem &p)
+{
+    if (p.batch != 1 || p.M <= kSkinnyMaxM) return 1;
+    const int64_t tiles = ceil_div(p.M, 128) * ceil_div(p.N, 128);
+    if (tiles >= kCUs) return 1;
+    int64_t S = 1;
+    while (tiles * S < kCUs && S < 64) S *= 2;
+    while (S > 1 && (p.K % (S * 32) != 0 || p.K / S < 256)) S /= 2;
+    return S;
+}
+
+int64_t workspace_needed(const Problem &p)
+{
+    const int64_t S = split_count(p);
+    return S > 1 ? S * p.M * p.N * 4 : 0;
+}
+
+int run_ws(const Problem &p, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    const Verdict v = validate(p);
+    if (v != kCompute) return run(p, stream);
+    const int64_t S = split_count(p);
+    const int64_t need = S > 1 ? S * p.M * p.N * 4 : 0;
+    if (S <= 1 || !ws || static_cast<int64_t>(ws_bytes) < need) return run(p, stream);
+    const uintptr_t w = reinterpret_cast<uintptr_t>(ws);
+    if (w % 16 != 0) return hipErrorInvalidValue;
+    const int64_t es = p.dtype == kF32 ? 4 : 2;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p.A), b = reinterpret_cast<uintptr_t>(p.B);
+    const uintptr_t c = reinterpret_cast<uintptr_t>(p.C);
+    const int64_t abytes = extent_bytes(p.ta ? p.K : p.M, p.ta ? p.M : p.K, p.lda, es);
+    const int64_t bbytes = extent_bytes(p.tb ? p.N : p.K, p.tb ? p.K : p.N, p.ldb, es);
+    const int64_t cbytes = extent_bytes(p.M, p.N, p.ldc, 4);
+    if (overlaps(w, need, a, abytes) || overlaps(w, need, b, bbytes) ||
+        overlaps(w, need, c, cbytes))
+        return hipErrorInvalidValue;
+    Problem q = p;
+    q.K = p.K / S;
+    q.C = static_cast<float *>(ws);
+    q.ldc = p.N;
+    q.batch = S;
+    q.sc = p.M * p.N;
+    q.sa = p.ta ? q.K * p.lda : q.K;   // the next chunk of K: rows (A stored K x M) or columns
+    q.sb = p.tb ? q.K : q.K * p.ldb;
+    const int rc = run(q, stream);
+    if (rc != hipSuccess) return rc;
+    return launch_sum_partials(q.C, S, p.M, p.N, p.C, p.ldc, stream);
+}
+
 }  // namespace
 }  // namespace mi355gemm
 
@@ -380,6 +437,48 @@ int gemm_bf16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64
     const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kBF16, transa, transb, batch,
                     stride_a, stride_b, stride_c};
     return run(p, stream);
+}
+
+int gemm_f32_batched_ws(int transa, int transb, int64_t M, int64_t N, int64_t K, const float *A,
+                        int64_t lda, int64_t stride_a, const float *B, int64_t ldb,
+                        int64_t stride_b, float *C, int64_t ldc, int64_t stride_c, int64_t batch,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kF32, transa, transb, batch,
+                    stride_a, stride_b, stride_c};
+    return run_ws(p, workspace, workspace_bytes, stream);
+}
+
+int gemm_bf16_f32acc_batched_ws(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                                const uint16_t *A, int64_t lda, int64_t stride_a,
+                                const uint16_t *B, int64_t ldb, int64_t stride_b, float *C,
+                                int64_t ldc, int64_t stride_c, int64_t batch, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream)
+{
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kBF16, transa, transb, batch,
+                    stride_a, stride_b, stride_c};
+    return run_ws(p, workspace, workspace_bytes, stream);
+}
+
+int gemm_f16_f32acc_batched_ws(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda, int64_t stride_a,
+                               const uint16_t *B, int64_t ldb, int64_t stride_b, float *C,
+                               int64_t ldc, int64_t stride_c, int64_t batch, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream)
+{
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, kF16, transa, transb, batch,
+                    stride_a, stride_b, stride_c};
+    return run_ws(p, workspace, workspace_bytes, stream);
+}
+
+size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                           int64_t batch)
+{
+    if (dtype != kF32 && dtype != kBF16 && dtype != kF16) return 0;
+    if (M < 0 || N < 0 || K <= 0 || batch != 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return 0;
+    Problem p{M, N, K, nullptr, 0, nullptr, 0, nullptr, 0, dtype, transa, transb, batch};
+    return static_cast<size_t>(workspace_needed(p));
 }
 
 int gemm_kernel_count(void) { return kNumKernels; }

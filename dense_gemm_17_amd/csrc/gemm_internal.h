@@ -82,6 +82,8 @@ hipError_t launch_mfma_f16_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f16_batched_splitk(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_f16(const Problem &p, hipStream_t s);
 hipError_t launch_naive_f16(const Problem &p, hipStream_t s);
+hipError_t launch_sum_partials(const float *W, int64_t S, int64_t M, int64_t N, float *C,
+                               int64_t ldc, hipStream_t s);
 hipError_t launch_skinny_f32(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_bf16(const Problem &p, hipStream_t s);
 

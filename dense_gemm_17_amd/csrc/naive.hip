@@ -71,6 +71,37 @@ hipError_t launch_naive_f32(const Problem &p, hipStream_t s) { return launch_nai
 hipError_t launch_naive_bf16(const Problem &p, hipStream_t s) { return launch_naive<uint16_t>(p, s); }
 hipError_t launch_naive_f16(const Problem &p, hipStream_t s) { return launch_naive<F16Bits>(p, s); }
 
+// C = sum over s < S of the S partial products W_s (M x N, packed, M*N
+// apart), added in the order s = 0, 1, ... (deterministic): the second pass
+// of a product whose K range was split over work-groups.  One thread per
+// element of C; consecutive threads take consecutive columns, so every
+// read of a partial and every store is coalesced.
+namespace {
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(const float *__restrict__ W, int64_t S,
+                                                           int64_t M, int64_t N,
+                                                           float *__restrict__ C, int64_t ldc)
+{
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= M * N) return;
+    const int64_t i = e / N, j = e - i * N;
+    float v = W[e];
+    for (int64_t s = 1; s < S; ++s) v += W[s * M * N + e];
+    store_c_stream(C + i * ldc + j, v);
+}
+
+}  // namespace
+
+hipError_t launch_sum_partials(const float *W, int64_t S, int64_t M, int64_t N, float *C,
+                               int64_t ldc, hipStream_t s)
+{
+    const int64_t blocks = (M * N + 255) / 256;
+    if (blocks > kMaxBlocks) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sum_partials_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s,
+                       W, S, M, N, C, ldc);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(const Problem &p, hipStream_t s)
 {
     const int64_t cb = (p.N + kCols - 1) / kCols;

@@ -136,6 +136,44 @@ int gemm_f16_f32acc_batched(int transa, int transb, int64_t M, int64_t N, int64_
                             float *C, int64_t ldc, int64_t stride_c,
                             int64_t batch, hipStream_t stream);
 
+/* ---- the same with a caller-provided workspace -----------------------------
+ *
+ * Exactly gemm_*_batched (same arguments, layout, results up to the
+ * summation order, errors), plus a workspace: device memory owned by the
+ * caller, at least gemm_workspace_size() bytes, 16-byte aligned, not
+ * overlapping A, B or C.  A single product (batch == 1) whose output has
+ * fewer 128 x 128 tiles than the GPU has CUs -- a weight gradient, a small
+ * d_in x d_out output summed over every token of a training step ("Bare
+ * Metal Bard", page 1, second paragraph) -- then splits its K range over
+ * work-groups: the partial products go to the workspace and are added in a
+ * fixed order (deterministic).  With a smaller or null workspace, or any
+ * other shape, the call is exactly the one without a workspace and does not
+ * touch it.  The workspace's contents on return are unspecified; calls that
+ * share one workspace must be ordered on one stream (concurrent use races).
+ * The library still allocates nothing. */
+int gemm_f32_batched_ws(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                        const float *A, int64_t lda, int64_t stride_a,
+                        const float *B, int64_t ldb, int64_t stride_b,
+                        float *C, int64_t ldc, int64_t stride_c, int64_t batch,
+                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+int gemm_bf16_f32acc_batched_ws(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                                const uint16_t *A, int64_t lda, int64_t stride_a,
+                                const uint16_t *B, int64_t ldb, int64_t stride_b,
+                                float *C, int64_t ldc, int64_t stride_c, int64_t batch,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+int gemm_f16_f32acc_batched_ws(int transa, int transb, int64_t M, int64_t N, int64_t K,
+                               const uint16_t *A, int64_t lda, int64_t stride_a,
+                               const uint16_t *B, int64_t ldb, int64_t stride_b,
+                               float *C, int64_t ldc, int64_t stride_c, int64_t batch,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes the *_ws calls use for these sizes and element type (0:
+ * they use none); a pure host function, no HIP call. */
+size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                           int64_t batch);
+
 /* ---- introspection and test hooks (not needed by ordinary callers) -------
  *
  * Kernel selection follows the regime classification of the devpost write-up

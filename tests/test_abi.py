@@ -310,3 +310,20 @@ def test_plan_f16_follows_the_16_bit_family():
     assert name(1000, 3000, 777) in ("mfma_f16_batched", "mfma_f16_batched128")
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.F16, 1, 1, 4096, 4096, 4096, 2)) == \
         "mfma_f16_direct"
+
+
+def test_workspace_size():
+    F32, BF16 = g.F32, g.BF16
+    # a weight gradient (small output, long K): S = 16 chunks of 1024
+    assert g.gemm_workspace_size(F32, 1, 0, 384, 1152, 16384) == 16 * 384 * 1152 * 4
+    assert g.gemm_workspace_size(BF16, 1, 0, 384, 1152, 16384) == 16 * 384 * 1152 * 4
+    # chunks of at least 256: K = 1536 splits in 4
+    assert g.gemm_workspace_size(F32, 0, 0, 256, 384, 1536) == 4 * 256 * 384 * 4
+    # outputs that fill the CUs, batches, skinny and short K: none
+    assert g.gemm_workspace_size(F32, 0, 0, 8192, 8192, 8192) == 0
+    assert g.gemm_workspace_size(F32, 1, 0, 384, 1152, 16384, 2) == 0
+    assert g.gemm_workspace_size(F32, 0, 0, 8, 4096, 4096) == 0
+    assert g.gemm_workspace_size(F32, 0, 0, 384, 1152, 256) == 0
+    assert g.gemm_workspace_size(F32, 0, 0, 384, 1152, 1000) == 0     # no even chunking
+    assert g.gemm_workspace_size(7, 0, 0, 384, 1152, 16384) == 0
+    assert g.gemm_workspace_size(F32, 0, 0, -1, 1152, 16384) == 0

@@ -339,3 +339,83 @@ def test_benchmark_shapes_sampled(name):
         e, at, n = oracle.normalized_error(Ch[bi][rows], Cref, D)
         say(f"[batched]   product {bi}: e={e:.3e} at={at}")
         assert e <= GATE
+
+
+# ---- K split over work-groups through a caller's workspace -------------------
+
+WS_SHAPES = [(384, 1152, 4096, True, False), (128, 200, 2048, True, True),
+             (256, 384, 1536, False, False), (200, 72, 8192, False, True)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N,K,ta,tb", WS_SHAPES)
+def test_workspace_split_exact(dtype, M, N, K, ta, tb):
+    gen = workloads.generator(61)
+    A = small_int((M, K), dtype, gen)
+    B = small_int((K, N), dtype, gen)
+    As, Bs = stored(A, ta), stored(B, tb)
+    a, b = view(As.to(DEV), ta), view(Bs.to(DEV), tb)
+    need = g.workspace_size(a, b)
+    assert need > 0, "these shapes split their K range"
+    ws = torch.full((need // 4 + 64,), float("nan"), device=DEV)
+    say(f"[ws] {dtype} {M}x{N}x{K} ta={ta} tb={tb} workspace={need}")
+    C = g.gemm(a, b, workspace=ws)
+    C2 = g.gemm(a, b, workspace=ws)
+    torch.cuda.synchronize()
+    Cref, _ = oracle.gemm_batched(as_oracle(As), as_oracle(Bs), ta, tb)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), Cref)
+    assert torch.equal(C, C2), "not deterministic"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_workspace_gate_random(dtype):
+    gen = workloads.generator(62)
+    M, N, K = 384, 1152, 8192
+    tdt = TDT[dtype]
+    X = workloads.draw((K, M), ("normal", 1.0), gen).to(tdt)     # activations, stored K x M
+    dY = workloads.draw((K, N), ("normal", 1.0), gen).to(tdt)
+    a, b = X.to(DEV).t(), dY.to(DEV)
+    ws = torch.empty((g.workspace_size(a, b) // 4,), device=DEV)
+    C = g.gemm(a, b, workspace=ws).cpu().numpy()
+    plain = g.gemm(a, b).cpu().numpy()
+    rows = [0, 1, 63, 64, 127, 128, 200, 383]
+    A_rows = X.t()[rows].contiguous()
+    Cref, D = oracle.gemm_batched(as_oracle(A_rows), as_oracle(dY), False, False)
+    for got in (C, plain):
+        e, at, n = oracle.normalized_error(got[rows], Cref, D)
+        say(f"[ws] {dtype} random e={e:.3e} at={at}")
+        assert e <= GATE
+
+
+def test_workspace_too_small_or_absent_is_the_plain_call():
+    gen = workloads.generator(63)
+    A = small_int((4096, 384), "f32", gen)
+    B = small_int((4096, 1152), "f32", gen)
+    a, b = A.to(DEV).t(), B.to(DEV)
+    need = g.workspace_size(a, b)
+    small = torch.full((need // 4 - 1,), 5.0, device=DEV)
+    C = g.gemm(a, b, workspace=small)
+    torch.cuda.synchronize()
+    assert torch.equal(small, torch.full_like(small, 5.0)), "a short workspace must not be touched"
+    ref = (A.to(torch.int64).t() @ B.to(torch.int64)).to(torch.float32)
+    assert torch.equal(C.cpu(), ref)
+    # shapes that fill the CUs use no workspace
+    assert g.workspace_size(torch.empty((4096, 4096), device=DEV),
+                            torch.empty((4096, 4096), device=DEV)) == 0
+
+
+def test_workspace_refused_when_misaligned_or_overlapping():
+    a = torch.zeros((4096, 384), device=DEV).t()
+    b = torch.zeros((4096, 1152), device=DEV)
+    need = g.workspace_size(a, b)
+    buf = torch.zeros((need // 4 + 16,), device=DEV)
+    with pytest.raises(g.GemmError):
+        g.gemm(a, b, workspace=buf[1:])                     # 4-byte offset
+    big = torch.zeros((need // 4 + 384 * 1152,), device=DEV)
+    out = big[:384 * 1152].view(384, 1152)
+    with pytest.raises(g.GemmError):
+        g.gemm(a, b, out=out, workspace=big)                # workspace overlapping C
+    # C past the bytes the split uses: allowed
+    out2 = big[need // 4:].view(384, 1152)
+    g.gemm(a, b, out=out2, workspace=big)
+    torch.cuda.synchronize()
