@@ -344,7 +344,8 @@ def test_benchmark_shapes_sampled(name):
 # ---- K split over work-groups through a caller's workspace -------------------
 
 WS_SHAPES = [(384, 1152, 4096, True, False), (128, 200, 2048, True, True),
-             (256, 384, 1536, False, False), (200, 72, 8192, False, True)]
+             (256, 384, 1536, False, False), (200, 72, 8192, False, True),
+             (128, 198, 2048, True, False)]     # N % 4 != 0: element-wise partial sums
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
