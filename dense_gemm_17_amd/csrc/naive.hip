@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256) void sum_partials_kernel(const float *__restri
     if (e >= M * N) return;
     const int64_t i = e / N, j = e - i * N;
     float v = W[e];
+#pragma unroll 8
     for (int64_t s = 1; s < S; ++s) v += W[s * M * N + e];
     store_c_stream(C + i * ldc + j, v);
 }
@@ -103,6 +104,9 @@ __global__ __launch_bounds__(256) void sum_partials4_kernel(const float *__restr
     if (e >= M * N) return;
     const int64_t i = e / N, j = e - i * N;
     f32x4 v = *reinterpret_cast<const f32x4 *>(W + e);
+    // unrolled so that several partials are in flight; the additions keep
+    // the order s = 1, 2, ...
+#pragma unroll 8
     for (int64_t s = 1; s < S; ++s) v += *reinterpret_cast<const f32x4 *>(W + s * M * N + e);
     store_c_stream(reinterpret_cast<f32x4 *>(C + i * ldc + j), v);
 }
