@@ -33,7 +33,7 @@ CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
           "-pthread", "-shared", "-fPIC", "-Wall", "-Wextra"]
 
 MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP", "IGNORE_TA", "BATCH_B0",
-           "F16_BIAS")
+           "F16_BIAS", "E4M3_NAN")
 
 
 def build(out: str = _LIB_PATH, mutant: Optional[str] = None) -> str:
@@ -68,6 +68,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     for name in ("oracle_decode_bf16", "oracle_decode_f16"):
         getattr(lib, name).argtypes = [_vp, _vp, _i64]
         getattr(lib, name).restype = None
+    lib.oracle_gemm_fp8_batched.argtypes = [ci, ci, ci, ci, _i64, _i64, _i64, _vp, _i64, _i64,
+                                            _vp, _i64, _i64, _i64, _vp, _vp, _i64, ci]
+    lib.oracle_gemm_fp8_batched.restype = ci
+    lib.oracle_decode_fp8.argtypes = [ci, _vp, _vp, _i64]
+    lib.oracle_decode_fp8.restype = None
     return lib
 
 
@@ -200,6 +205,38 @@ class Oracle:
             fn(bits.ctypes.data, out.ctypes.data, bits.size)
         return out
 
+    def gemm_fp8_batched(self, A: np.ndarray, B: np.ndarray, fmt_a: int = 0, fmt_b: int = 0,
+                         transa: bool = False, transb: bool = False,
+                         threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """(C, D) in fp64 for 8-bit operands given as uint8 patterns (format
+        0: e4m3, 1: e5m2), laid out as for gemm_batched."""
+        two_d = A.ndim == 2 and B.ndim == 2
+        A3, ba, sa, lda = self._stored(A, np.uint8)
+        B3, bb, sb, ldb = self._stored(B, np.uint8)
+        if A.ndim == 3 and B.ndim == 3 and ba != bb:
+            raise ValueError(f"batch sizes differ: {ba} and {bb}")
+        batch = ba if A.ndim == 3 else bb
+        M, K = (A3.shape[2], A3.shape[1]) if transa else (A3.shape[1], A3.shape[2])
+        K2, N = (B3.shape[2], B3.shape[1]) if transb else (B3.shape[1], B3.shape[2])
+        if K != K2:
+            raise ValueError(f"inner dimensions differ: {K} and {K2}")
+        C = np.zeros((batch, M, N), dtype=np.float64)
+        D = np.zeros((batch, M, N), dtype=np.float64)
+        ptr = lambda a: a.ctypes.data if a.size else None  # noqa: E731
+        rc = self.lib.oracle_gemm_fp8_batched(fmt_a, fmt_b, int(transa), int(transb), M, N, K,
+                                              ptr(A3), lda, sa, ptr(B3), ldb, sb, batch,
+                                              ptr(C), ptr(D), max(N, 1), threads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_fp8_batched failed with code {rc}")
+        return (C[0], D[0]) if two_d else (C, D)
+
+    def decode_fp8(self, fmt: int, bits: np.ndarray) -> np.ndarray:
+        bits = np.ascontiguousarray(bits, dtype=np.uint8).reshape(-1)
+        out = np.empty(bits.shape, dtype=np.float64)
+        if bits.size:
+            self.lib.oracle_decode_fp8(fmt, bits.ctypes.data, out.ctypes.data, bits.size)
+        return out
+
     def decode_bf16(self, bits: np.ndarray) -> np.ndarray:
         return self._decode(self.lib.oracle_decode_bf16, bits)
 
@@ -227,6 +264,10 @@ def gemm_bf16(A_bits, B_bits, rows=None, threads=0):
 
 def gemm_f16(A, B, rows=None, threads=0):
     return load().gemm_f16(A, B, rows, threads)
+
+
+def gemm_fp8_batched(A, B, fmt_a=0, fmt_b=0, transa=False, transb=False, threads=0):
+    return load().gemm_fp8_batched(A, B, fmt_a, fmt_b, transa, transb, threads)
 
 
 def gemm_batched(A, B, transa=False, transb=False, threads=0):

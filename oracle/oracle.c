@@ -44,6 +44,7 @@
  *   ORACLE_MUTANT_IGNORE_TA    - a transposed A is read as if it were not
  *   ORACLE_MUTANT_BATCH_B0     - every product of a batch reads the first B
  *   ORACLE_MUTANT_F16_BIAS     - fp16 decode uses an exponent bias of 16
+ *   ORACLE_MUTANT_E4M3_NAN     - e4m3 decode treats exponent 15 as infinity/NaN
  */
 
 static double decode_bf16(uint16_t bits)
@@ -74,7 +75,41 @@ static double decode_f16(uint16_t bits)
     return sign ? -v : v;
 }
 
-enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_F16 = 2 };
+/* 8-bit floating point patterns (the OCP 8-bit formats), decoded from their
+ * definitions.  e4m3: sign, 4-bit exponent (bias 7), 3-bit fraction; no
+ * infinities, the only NaN patterns are S.1111.111 (so exponent 15 carries
+ * ordinary values up to 448).  e5m2: sign, 5-bit exponent (bias 15), 2-bit
+ * fraction, IEEE-style infinities and NaNs at exponent 31.  Exponent 0 is
+ * zero or subnormal in both. */
+static double decode_e4m3(uint8_t bits)
+{
+    const int sign = bits >> 7, e = (bits >> 3) & 15, f = bits & 7;
+    double v;
+#ifdef ORACLE_MUTANT_E4M3_NAN
+    if (e == 15) return f ? NAN : (sign ? -INFINITY : INFINITY);
+#endif
+    if (e == 15 && f == 7) return NAN;
+    if (e == 0) v = ldexp((double)f, 1 - 7 - 3);
+    else v = ldexp((double)(8 + f), e - 7 - 3);
+    return sign ? -v : v;
+}
+
+static double decode_e5m2(uint8_t bits)
+{
+    const int sign = bits >> 7, e = (bits >> 2) & 31, f = bits & 3;
+    double v;
+    if (e == 0) v = ldexp((double)f, 1 - 15 - 2);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(4 + f), e - 15 - 2);
+    return sign ? -v : v;
+}
+
+enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_F16 = 2, KIND_E4M3 = 3, KIND_E5M2 = 4 };
+
+static double decode_byte(int kind, uint8_t bits)
+{
+    return kind == KIND_E4M3 ? decode_e4m3(bits) : decode_e5m2(bits);
+}
 
 static double decode_kind(int kind, uint16_t bits)
 {
@@ -91,6 +126,7 @@ typedef struct {
     int64_t nrows;
     int64_t r0, r1;        /* this worker's block of output rows */
     int ta, tb;            /* operand stored transposed: A as K x M, B as N x K */
+    int kind_b;            /* B's element type when it differs from A's (8-bit formats) */
 } job_t;
 
 /* Element (i, k) of the M x K left factor.  Stored as written (row i at
@@ -104,6 +140,8 @@ static double load_a(const job_t *j, int64_t i, int64_t k)
 #endif
     if (j->kind == KIND_F32)
         return (double)((const float *)j->A)[at];
+    if (j->kind >= KIND_E4M3)
+        return decode_byte(j->kind, ((const uint8_t *)j->A)[at]);
     return decode_kind(j->kind, ((const uint16_t *)j->A)[at]);
 }
 
@@ -117,6 +155,8 @@ static double load_b(const job_t *j, int64_t k, int64_t n)
     int64_t at = j->tb ? n * j->ldb + k : k * j->ldb + n;
     if (j->kind == KIND_F32)
         return (double)((const float *)j->B)[at];
+    if (j->kind >= KIND_E4M3)
+        return decode_byte(j->kind_b, ((const uint8_t *)j->B)[at]);
     return decode_kind(j->kind, ((const uint16_t *)j->B)[at]);
 }
 
@@ -202,7 +242,7 @@ int oracle_gemm_f32(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda, const float *B, int64_t ldb,
                     double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -210,7 +250,7 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                      double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -221,7 +261,7 @@ int oracle_gemm_f32_rows(int64_t M, int64_t N, int64_t K,
                          const int64_t *rows, int64_t nrows,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -230,7 +270,7 @@ int oracle_gemm_bf16_rows(int64_t M, int64_t N, int64_t K,
                           const int64_t *rows, int64_t nrows,
                           double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -262,7 +302,7 @@ int oracle_gemm_batched(int kind, int ta, int tb, int64_t M, int64_t N, int64_t 
         job_t j = {kind, M, N, K,
                    (const char *)A + b * sa * es, lda,
                    (const char *)B + bb * sb * es, ldb,
-                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0};
+                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0, 0};
         int rc = run(j, nthreads);
         if (rc != 0) return rc;
     }
@@ -275,7 +315,7 @@ int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                     double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0};
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -284,7 +324,7 @@ int oracle_gemm_f16_rows(int64_t M, int64_t N, int64_t K,
                          const int64_t *rows, int64_t nrows,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0};
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
     return run(j, nthreads);
 }
 
@@ -292,6 +332,32 @@ int oracle_gemm_f16_rows(int64_t M, int64_t N, int64_t K,
 void oracle_decode_bf16(const uint16_t *in, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = decode_bf16(in[i]);
+}
+
+/* 8-bit operands: A in format fmt_a, B in fmt_b (0: e4m3, 1: e5m2), either
+ * stored transposed, a strided batch as in oracle_gemm_batched (strides and
+ * leading dimensions in bytes = elements). */
+int oracle_gemm_fp8_batched(int fmt_a, int fmt_b, int ta, int tb, int64_t M, int64_t N,
+                            int64_t K, const uint8_t *A, int64_t lda, int64_t sa,
+                            const uint8_t *B, int64_t ldb, int64_t sb, int64_t batch,
+                            double *C, double *D, int64_t ldo, int nthreads)
+{
+    if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return 1;
+    if (batch < 0 || sa < 0 || sb < 0 || M < 0 || N < 0) return 1;
+    for (int64_t b = 0; b < batch; ++b) {
+        job_t j = {KIND_E4M3 + fmt_a, M, N, K, A + b * sa, lda, B + b * sb, ldb,
+                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0,
+                   KIND_E4M3 + fmt_b};
+        int rc = run(j, nthreads);
+        if (rc != 0) return rc;
+    }
+    return 0;
+}
+
+/* 8-bit pattern -> fp64 (fmt 0: e4m3, 1: e5m2), exposed to pin the decoders. */
+void oracle_decode_fp8(int fmt, const uint8_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_byte(KIND_E4M3 + fmt, in[i]);
 }
 
 /* fp16 pattern -> fp64, exposed for the same reason. */

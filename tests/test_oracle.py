@@ -271,10 +271,56 @@ def pin_f16_matches_decoded_f32(o):
     assert np.array_equal(C, C2) and np.array_equal(D, D2)
 
 
+FP8_TORCH = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}
+
+
+def fp8_bits(t):
+    return t.contiguous().view(torch.uint8).numpy()
+
+
+def pin_fp8_decoders(o):
+    # all 256 patterns of each 8-bit format against torch's own conversion
+    bits = np.arange(256, dtype=np.uint8)
+    for fmt, tdt in FP8_TORCH.items():
+        mine = o.decode_fp8(fmt, bits)
+        ref = torch.from_numpy(bits.copy()).view(tdt).to(torch.float64).numpy()
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(mine), nan)
+        assert np.array_equal(mine[~nan], ref[~nan])
+        assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+    # hand-worked: e4m3 1.0 = 0x38, 448 = 0x7E, smallest subnormal 2^-9 = 0x01;
+    # e5m2 1.0 = 0x3C, 57344 = 0x7B, infinity = 0x7C
+    assert list(o.decode_fp8(0, np.array([0x38, 0x7E, 0x01, 0xB8], np.uint8))) == \
+        [1.0, 448.0, 2.0 ** -9, -1.0]
+    assert list(o.decode_fp8(1, np.array([0x3C, 0x7B, 0x7C], np.uint8))) == \
+        [1.0, 57344.0, math.inf]
+
+
+def pin_fp8_products(o):
+    # small integers are exact in both formats: the product of the logical
+    # matrices exactly, for mixed formats and the transposed-B layout
+    g = workloads.generator(21)
+    for fa, fb in ((0, 0), (1, 1), (0, 1)):
+        A = workloads.small_int((19, 64), -8, 8, g).to(FP8_TORCH[fa])
+        B = workloads.small_int((64, 23), -8, 8, g).to(FP8_TORCH[fb])
+        C, D = o.gemm_fp8_batched(fp8_bits(A), fp8_bits(B.t()), fa, fb, False, True)
+        Ai, Bi = A.to(torch.int64).numpy(), B.to(torch.int64).numpy()
+        assert np.array_equal(C, (Ai @ Bi).astype(np.float64))
+        assert np.array_equal(D, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+    # random operands: bit-equal to the fp32 product of the converted operands
+    r = torch.Generator().manual_seed(22)
+    A = (torch.randn((17, 96), generator=r) * 4).to(torch.float8_e4m3fn)
+    B = (torch.randn((96, 13), generator=r) * 1e-2).to(torch.float8_e5m2)
+    C, D = o.gemm_fp8_batched(fp8_bits(A), fp8_bits(B), 0, 1)
+    C2, D2 = o.gemm_f32(A.float().numpy(), B.float().numpy())
+    assert np.array_equal(C, C2) and np.array_equal(D, D2)
+
+
 PINS = [pin_golden, pin_identity, pin_permutation, pin_ones, pin_small_int_f32,
         pin_small_int_bf16, pin_bf16_matches_decoded_f32, pin_numpy_blas,
         pin_transposed_small_int, pin_transposed_permutation, pin_batched,
         pin_f16_decoder, pin_small_int_f16, pin_f16_matches_decoded_f32,
+        pin_fp8_decoders, pin_fp8_products,
         lambda o: pin_brute_force(o, [(2, 3, 4), (3, 1, 5), (4, 4, 2)])]
 
 

@@ -204,3 +204,26 @@ def make_general_inputs(w: GeneralWorkload, seed: int = SEED) -> Tuple[torch.Ten
 def general_views(w: GeneralWorkload, A: torch.Tensor, B: torch.Tensor):
     """The logical factors op(A), op(B) as views of the stored tensors."""
     return (A.transpose(-1, -2) if w.ta else A), (B.transpose(-1, -2) if w.tb else B)
+
+
+# ---- a launch-bound sequence ------------------------------------------------
+# The matrix products of one forward pass of the same GPT over a single
+# sequence of 256 tokens (6 layers; per layer the QKV projection, the
+# per-head scores Q K^T and probabilities x values over 6 heads of width 64,
+# the attention output projection, MLP up and MLP down; then the output
+# layer onto the 65-character vocabulary): 37 calls of at most 0.3 GFLOP
+# each, the regime where the launches, not the kernels, set the time.
+# Entries: (name, batch, M, N, K, A stored transposed, B stored transposed).
+def gpt_forward_sequence(tokens: int = 256, layers: int = 6, d_model: int = 384,
+                         heads: int = 6, vocab: int = 65):
+    dh = d_model // heads
+    seq = []
+    for l in range(layers):
+        seq += [(f"l{l}_qkv", 1, tokens, 3 * d_model, d_model, False, False),
+                (f"l{l}_scores", heads, tokens, tokens, dh, False, True),
+                (f"l{l}_pv", heads, tokens, dh, tokens, False, False),
+                (f"l{l}_proj", 1, tokens, d_model, d_model, False, False),
+                (f"l{l}_mlp_up", 1, tokens, 4 * d_model, d_model, False, False),
+                (f"l{l}_mlp_down", 1, tokens, d_model, 4 * d_model, False, False)]
+    seq.append(("lm_head", 1, tokens, vocab, d_model, False, False))
+    return seq
