@@ -54,7 +54,8 @@ import torch  # noqa: E402
 
 import workloads  # noqa: E402
 
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}     # MI355X dense, per dtype
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6,     # MI355X dense, per dtype
+               "fp8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 METRIC = "GFLOP/s (2MNK/t) fp32 & bf16 GEMM at 8192³; % of MI355X dtype peak"
 STEP_WORKLOADS = ("f32_8192", "bf16_8192")
@@ -351,6 +352,7 @@ def main():
         others = other_configs(dev, set(names), args.check_rows)
         general = general_configs(dev, args.check_rows)
         sequence = sequence_config(dev)
+        fp8 = fp8_configs(dev, args.check_rows)
 
     ceiling = None
     if not args.no_ceiling:
@@ -393,6 +395,7 @@ def main():
         # a launch-bound sequence (one GPT forward pass over 256 tokens):
         # back-to-back calls against the same calls replayed from a HIP graph
         "sequence": sequence,
+        "fp8": fp8,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels
         "env": dict(clocks.summary(), toolchain=toolchain(g.gemm_build_info())),
@@ -655,6 +658,52 @@ def general_configs(dev, check_rows):
             "operand_copies": copies, "max_norm_err_sampled": float(f"{err:.3e}"),
             "sclk_mhz": (clocks.summary()["sclk_mhz"] or {}).get("median"),
             "with_workspace": ws_rec,
+        }
+        del ops
+        torch.cuda.empty_cache()
+    return out
+
+
+def fp8_configs(dev, check_rows):
+    """8-bit float products (e4m3 / e5m2, B given transposed): the table's
+    kernel timed like the configurations above, sampled rows checked against
+    the oracle."""
+    import dense_gemm_17_amd as g
+    import oracle
+    out = {}
+    rng = np.random.default_rng(4)
+    for name, w in workloads.FP8_WORKLOADS.items():
+        A, Bt = workloads.make_fp8_inputs(w)
+        per_copy = w.algorithmic_bytes
+        copies = 1 if per_copy * 2 > LLC_BYTES else max(2, -(-2 * LLC_BYTES // per_copy))
+        ops = [(A.to(dev), Bt.to(dev).t(), torch.empty((w.M, w.N), dtype=torch.float32,
+                                                       device=dev)) for _ in range(copies)]
+        state = {"i": 0}
+
+        def call():
+            a, b, c = ops[state["i"] % copies]
+            state["i"] += 1
+            g.gemm(a, b, out=c)
+
+        ms, graph_ms, clocks = time_calls(dev, call, copies)
+        kernel = g.gemm_kernel_name(g.gemm_last_kernel())
+        rows = sorted(set([0, w.M - 1] + rng.choice(w.M, size=min(w.M, check_rows),
+                                                     replace=False).tolist()))
+        Cref, D = oracle.gemm_fp8_batched(workloads.fp8_bits(A[rows]), workloads.fp8_bits(Bt),
+                                          w.fa, w.fb, False, True, threads=cpu_threads())
+        err, _, _ = oracle.normalized_error(ops[0][2][rows].cpu().numpy(), Cref, D)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        gbs = per_copy / (ms * 1e-3) / 1e9
+        hbm = w.flops / per_copy < PEAK_TFLOPS["fp8"] * 1e3 / HBM_PEAK_GBS
+        out[name] = {
+            "M": w.M, "N": w.N, "K": w.K, "formats": ["e4m3", "e5m2"][w.fa] + "x" +
+            ["e4m3", "e5m2"][w.fb], "kernel": kernel,
+            "us_per_call": round(ms * 1e3, 2), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+            "bound": "hbm" if hbm else "mfma",
+            "frac": round(gbs / HBM_PEAK_GBS if hbm else tflops / PEAK_TFLOPS["fp8"], 4),
+            "us_per_call_graph": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+            "operand_copies": copies, "max_norm_err_sampled": float(f"{err:.3e}"),
+            "sclk_mhz": (clocks.summary()["sclk_mhz"] or {}).get("median"),
         }
         del ops
         torch.cuda.empty_cache()

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmi355gemm.so")
 F32 = 0
 BF16 = 1
 F16 = 2
+FP8 = 3
 HIP_SUCCESS = 0
 HIP_ERROR_INVALID_VALUE = 1
 
@@ -48,6 +49,11 @@ def _load() -> ctypes.CDLL:
                  "gemm_f16_f32acc_batched_ws"):
         getattr(lib, name).argtypes = wsig
         getattr(lib, name).restype = ci
+    lib.gemm_fp8_f32acc.argtypes = [ci, ci] + sig
+    lib.gemm_fp8_f32acc.restype = ci
+    lib.gemm_fp8_f32acc_batched.argtypes = [ci, ci, i64, i64, i64, vp, i64, i64, vp, i64, i64,
+                                            vp, i64, i64, i64, vp]
+    lib.gemm_fp8_f32acc_batched.restype = ci
     lib.gemm_workspace_size.argtypes = [ci, ci, ci, i64, i64, i64, i64]
     lib.gemm_workspace_size.restype = sz
     lib.gemm_plan_batched.argtypes = [ci, ci, ci, i64, i64, i64, sz, i64, i64, sz, i64, i64,
@@ -76,7 +82,8 @@ lib = _load()
 # Every symbol include/mi355gemm.h declares.
 EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched",
            "gemm_bf16_f32acc_batched", "gemm_f16_f32acc_batched", "gemm_f32_batched_ws",
-           "gemm_bf16_f32acc_batched_ws", "gemm_f16_f32acc_batched_ws", "gemm_workspace_size",
+           "gemm_bf16_f32acc_batched_ws", "gemm_f16_f32acc_batched_ws", "gemm_fp8_f32acc",
+           "gemm_fp8_f32acc_batched", "gemm_workspace_size",
            "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
            "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info")
 
@@ -93,6 +100,16 @@ def gemm_bf16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
 
 def gemm_f16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream) -> int:
     return lib.gemm_f16_f32acc(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_fp8_f32acc(fmt_a, fmt_b, M, N, K, A, lda, Bt, ldb, C, ldc, stream) -> int:
+    return lib.gemm_fp8_f32acc(fmt_a, fmt_b, M, N, K, A, lda, Bt, ldb, C, ldc, stream)
+
+
+def gemm_fp8_f32acc_batched(fmt_a, fmt_b, M, N, K, A, lda, stride_a, Bt, ldb, stride_b, C, ldc,
+                            stride_c, batch, stream) -> int:
+    return lib.gemm_fp8_f32acc_batched(fmt_a, fmt_b, M, N, K, A, lda, stride_a, Bt, ldb,
+                                       stride_b, C, ldc, stride_c, batch, stream)
 
 
 def gemm_f16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, stride_b, C,
@@ -219,6 +236,8 @@ _FN = {torch.float32: ("gemm_f32", "gemm_f32_batched"),
 _PLAIN = {dt: getattr(lib, names[0]) for dt, names in _FN.items()}
 _CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 _BATCHED = {dt: getattr(lib, names[1]) for dt, names in _FN.items()}
+# 8-bit float operand formats of gemm_fp8_f32acc*
+FP8_FORMAT = {torch.float8_e4m3fn: 0, torch.float8_e5m2: 1}
 
 
 def _batch_stride(t: torch.Tensor) -> int:
@@ -228,7 +247,8 @@ def _batch_stride(t: torch.Tensor) -> int:
 def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
          stream: Optional[torch.cuda.Stream] = None,
          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """out = a @ b on the GPU (fp32·fp32, bf16·bf16 or fp16·fp16 -> fp32).
+    """out = a @ b on the GPU (fp32·fp32, bf16·bf16 or fp16·fp16 -> fp32, or
+    8-bit floats: e4m3 / e5m2 in any pairing -> fp32).
 
     a is (M, K) or (batch, M, K), b is (K, N) or (batch, K, N); a 2-D operand
     is shared by every product of a batch, and a 3-D one may have any batch
@@ -240,7 +260,11 @@ def gemm(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
     (a device tensor of at least ``workspace_size(a, b)`` bytes) lets a
     single product with a small output split its K range over work-groups
     (the *_ws entry points); the caller keeps it alive until the stream has
-    passed the call."""
+    passed the call.  8-bit operands take one layout: a row-major, b the
+    transposed view of a row-major (N, K) tensor (``w.t()``), K and the row
+    pitches multiples of 16 bytes; they have no workspace variant."""
+    if a.dtype in FP8_FORMAT or b.dtype in FP8_FORMAT:
+        return _gemm_fp8(a, b, out, stream)
     if workspace is None and (a.dim() == 2 and b.dim() == 2 and (a.shape[1] <= 1 or a.stride(1) == 1)
                               and (b.shape[1] <= 1 or b.stride(1) == 1)):
         return _gemm_plain(a, b, out, stream)
@@ -296,6 +320,50 @@ def _gemm_plain(a, b, out, stream):
     name = _FN[a.dtype][0]
     _launch(_PLAIN[a.dtype], name, dev,
             (M, N, K, a.data_ptr(), _ld(a), b.data_ptr(), _ld(b), out.data_ptr(), _ld(out), raw))
+    return out
+
+
+def _gemm_fp8(a, b, out, stream):
+    """8-bit float operands: gemm_fp8_f32acc_batched (A as written, B
+    transposed)."""
+    if a.dtype not in FP8_FORMAT or b.dtype not in FP8_FORMAT:
+        raise TypeError(f"8-bit operands must both be float8_e4m3fn or float8_e5m2, got "
+                        f"{a.dtype}, {b.dtype}")
+    if a.device.type != "cuda" or b.device != a.device:
+        raise ValueError("operands must be on the same GPU")
+    if a.dim() not in (2, 3) or b.dim() not in (2, 3):
+        raise ValueError("gemm takes 2-D or 3-D tensors")
+    M, K = a.shape[-2], a.shape[-1]
+    K2, N = b.shape[-2], b.shape[-1]
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+    if a.dim() == 3 and b.dim() == 3 and a.shape[0] != b.shape[0]:
+        raise ValueError(f"batch sizes differ: {a.shape[0]} and {b.shape[0]}")
+    # a: unit stride along K, rows lda bytes apart; b: the view of Bt (N x K)
+    # with unit stride along K, rows of Bt ldb bytes apart.  A single row (or
+    # K = 0) has no pitch of its own: a packed one is passed.
+    if K > 1 and (a.stride(-1) != 1 or b.stride(-2) != 1):
+        raise ValueError("8-bit operands: a must be row-major (M, K) and b the transposed view "
+                         "of a row-major (N, K) tensor, e.g. w.t()")
+    lda = a.stride(-2) if M > 1 else max(K, 16)
+    ldb = b.stride(-1) if N > 1 else max(K, 16)
+    if K == 0:
+        lda = ldb = 16
+    batched = a.dim() == 3 or b.dim() == 3
+    batch = a.shape[0] if a.dim() == 3 else (b.shape[0] if b.dim() == 3 else 1)
+    shape = (batch, M, N) if batched else (M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=a.device)
+    elif (out.dtype != torch.float32 or tuple(out.shape) != shape or out.device != a.device
+          or (N > 1 and out.stride(-1) != 1)):
+        raise ValueError(f"out must be a float32 {shape} tensor with unit column stride on a's GPU")
+    ldc = out.stride(-2) if M > 1 else max(N, 1)
+    dev = a.get_device()
+    raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
+    _launch(lib.gemm_fp8_f32acc_batched, "gemm_fp8_f32acc_batched", dev,
+            (FP8_FORMAT[a.dtype], FP8_FORMAT[b.dtype], M, N, K, a.data_ptr(), lda,
+             _batch_stride(a), b.data_ptr(), ldb, _batch_stride(b), out.data_ptr(), ldc,
+             _batch_stride(out), batch, raw))
     return out
 
 

@@ -54,6 +54,9 @@ const KernelInfo kKernels[] = {
     {"mfma_f16_batched", kF16, launch_mfma_f16_batched, supports_any, true},
     {"mfma_f16_batched128", kF16, launch_mfma_f16_batched128, supports_any, true},
     {"mfma_f16_batched_splitk", kF16, launch_mfma_f16_batched_splitk, supports_any, true},
+    {"mfma_fp8_direct128", kFp8, launch_mfma_fp8_direct128, supports_mfma_fp8_direct, true},
+    {"mfma_fp8_batched", kFp8, launch_mfma_fp8_batched, supports_fp8, true},
+    {"mfma_fp8_batched128", kFp8, launch_mfma_fp8_batched128, supports_fp8, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -119,9 +122,12 @@ Verdict validate(const Problem &p)
     if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0) return kInvalid;
     if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim || p.batch > kMaxDim) return kInvalid;
     if ((p.ta != 0 && p.ta != 1) || (p.tb != 0 && p.tb != 1)) return kInvalid;
+    if (p.dtype < kF32 || p.dtype > kFp8) return kInvalid;
+    // 8-bit floats: A as written, B transposed, formats e4m3 (0) / e5m2 (1)
+    if (p.dtype == kFp8 && (p.ta != 0 || p.tb != 1 || (p.fa & ~1) || (p.fb & ~1))) return kInvalid;
     if (p.sa < 0 || p.sb < 0 || p.sc < 0) return kInvalid;
     if (p.M == 0 || p.N == 0 || p.batch == 0) return kNothing;
-    const int64_t es = p.dtype == kF32 ? 4 : 2;
+    const int64_t es = p.dtype == kF32 ? 4 : p.dtype == kFp8 ? 1 : 2;
     const uintptr_t c = reinterpret_cast<uintptr_t>(p.C);
     if (!p.C || p.ldc < p.N || (c % 4) != 0) return kInvalid;
     if (!outputs_disjoint(p)) return kInvalid;
@@ -173,6 +179,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // large sizes, used by select_general.
 constexpr int64_t F32_GENERAL_256 = 700, F32_GENERAL_128 = 670;
 constexpr int64_t BF16_GENERAL_256 = 340, BF16_GENERAL_128 = 300;
+// 8-bit floats at 8192^3 (all three within 2%: the LDS-direct 128 x 128
+// tile 0.353, register-staged 256 x 256 0.345, 128 x 128 0.352); the GPT
+// projections (fewer, smaller tiles) favour the 128 x 128 tiles by 1.1-3x.
+constexpr int64_t FP8_BATCHED_256 = 345, FP8_BATCHED_128 = 352, FP8_DIRECT_128 = 353;
 
 // Relative time of a tiled launch: waves x per-work-group work / efficiency,
 // in units of one CU doing a 128 x 128 tile alone at full rate.
@@ -217,6 +227,16 @@ int select_general(const Problem &p)
         return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
                    ? kernel_id("mfma_bf16_batched")
                    : kernel_id("mfma_bf16_batched128");
+    // 8-bit floats: the LDS-direct tiles when K is whole 64-byte tiles,
+    // else the register-staged ones (K a multiple of 16 bytes).
+    if (p.dtype == kFp8 && supports_mfma_fp8_direct(p))
+        return tiled_cost(p, 256, 256, 1, FP8_BATCHED_256) < tiled_cost(p, 128, 128, 2, FP8_DIRECT_128)
+                   ? kernel_id("mfma_fp8_batched")
+                   : kernel_id("mfma_fp8_direct128");
+    if (p.dtype == kFp8)
+        return tiled_cost(p, 256, 256, 1, FP8_BATCHED_256) <= tiled_cost(p, 128, 128, 2, FP8_BATCHED_128)
+                   ? kernel_id("mfma_fp8_batched")
+                   : kernel_id("mfma_fp8_batched128");
     if (p.dtype == kF16 && supports_mfma_bf16_direct(p))
         return tiled_cost(p, 256, 256, 1, 512) <= tiled_cost(p, 128, 128, 2, 410)
                    ? kernel_id("mfma_f16_direct")
@@ -234,7 +254,7 @@ int select_f32_lds(const Problem &p);
 
 int select_kernel(const Problem &p)
 {
-    if (is_general(p)) return select_general(p);
+    if (is_general(p) || p.dtype == kFp8) return select_general(p);
     if (p.M <= kSkinnyMaxM)
         return kernel_id(p.dtype == kF32 ? "skinny_f32" : p.dtype == kBF16 ? "skinny_bf16"
                                                                             : "skinny_f16");
@@ -304,7 +324,8 @@ int choose(const Problem &p)
 
 bool can_take(int id, const Problem &p)
 {
-    return id >= 0 && kKernels[id].supports(p) && (kKernels[id].general || !is_general(p));
+    return id >= 0 && kKernels[id].dtype == p.dtype && kKernels[id].supports(p) &&
+           (kKernels[id].general || !is_general(p));
 }
 
 int run(const Problem &p, hipStream_t stream)
@@ -471,6 +492,27 @@ int gemm_f16_f32acc_batched_ws(int transa, int transb, int64_t M, int64_t N, int
     return run_ws(p, workspace, workspace_bytes, stream);
 }
 
+int gemm_fp8_f32acc(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                    int64_t lda, const uint8_t *Bt, int64_t ldb, float *C, int64_t ldc,
+                    hipStream_t stream)
+{
+    Problem p{M, N, K, A, lda, Bt, ldb, C, ldc, kFp8, 0, 1};
+    p.fa = fmt_a;
+    p.fb = fmt_b;
+    return run(p, stream);
+}
+
+int gemm_fp8_f32acc_batched(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                            const uint8_t *A, int64_t lda, int64_t stride_a, const uint8_t *Bt,
+                            int64_t ldb, int64_t stride_b, float *C, int64_t ldc,
+                            int64_t stride_c, int64_t batch, hipStream_t stream)
+{
+    Problem p{M, N, K, A, lda, Bt, ldb, C, ldc, kFp8, 0, 1, batch, stride_a, stride_b, stride_c};
+    p.fa = fmt_a;
+    p.fb = fmt_b;
+    return run(p, stream);
+}
+
 size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
                            int64_t batch)
 {
@@ -496,7 +538,7 @@ int gemm_kernel_dtype(int id)
 namespace {
 int plan(const Problem &p)
 {
-    if (p.dtype != kF32 && p.dtype != kBF16 && p.dtype != kF16) return -1;
+    if (p.dtype != kF32 && p.dtype != kBF16 && p.dtype != kF16 && p.dtype != kFp8) return -1;
     switch (validate(p)) {
     case kInvalid: return -1;
     case kNothing: return -2;

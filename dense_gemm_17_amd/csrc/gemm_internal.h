@@ -7,7 +7,7 @@
 
 namespace mi355gemm {
 
-enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2 };
+enum Dtype : int { kF32 = 0, kBF16 = 1, kF16 = 2, kFp8 = 3 };
 
 // Storage type of an IEEE binary16 operand in the kernels templated on the
 // element type (bf16 operands are plain uint16_t patterns there).
@@ -21,7 +21,9 @@ struct F16Bits {
 // ta / tb mark a factor stored transposed (A as K x M, B as N x K) and
 // sa, sb, sc are the element distances between consecutive products.  A
 // plain product has ta = tb = 0 and batch = 1; only the kernels registered
-// as general read these fields.
+// as general read these fields.  8-bit float operands (dtype kFp8) come as
+// A as written and B transposed only (ta = 0, tb = 1), with fa and fb the
+// formats of A and B (0 e4m3, 1 e5m2); their sizes and strides are bytes.
 struct Problem {
     int64_t M, N, K;
     const void *A; int64_t lda;
@@ -30,6 +32,7 @@ struct Problem {
     int dtype;
     int ta = 0, tb = 0;
     int64_t batch = 1, sa = 0, sb = 0, sc = 0;
+    int fa = 0, fb = 0;
 };
 
 // True when only a general (transposed / batched) kernel can take p.
@@ -81,6 +84,21 @@ hipError_t launch_mfma_f16_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f16_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f16_batched_splitk(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_f16(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_fp8_batched(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_fp8_batched128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s);
+bool supports_mfma_fp8_direct(const Problem &p);
+
+// Layout every 8-bit kernel needs: A as written and B transposed, K, lda,
+// ldb, stride_a and stride_b multiples of 16 (bytes), A and B 16-byte
+// aligned, formats 0 or 1.
+inline bool supports_fp8(const Problem &p)
+{
+    const auto al = [](const void *q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    return p.dtype == kFp8 && p.ta == 0 && p.tb == 1 && (p.fa == 0 || p.fa == 1) &&
+           (p.fb == 0 || p.fb == 1) && p.K % 16 == 0 && p.lda % 16 == 0 && p.ldb % 16 == 0 &&
+           p.sa % 16 == 0 && p.sb % 16 == 0 && al(p.A) && al(p.B);
+}
 hipError_t launch_naive_f16(const Problem &p, hipStream_t s);
 hipError_t launch_sum_partials(const float *W, int64_t S, int64_t M, int64_t N, float *C,
                                int64_t ldc, hipStream_t s);

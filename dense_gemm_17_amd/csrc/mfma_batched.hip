@@ -60,6 +60,32 @@ __device__ __forceinline__ f32x16 mfma16(const bf16x8 &a, const bf16x8 &b, const
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef unsigned short u16x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Operand kinds of the 16-bit-staged kernels: 0 bf16, 1 fp16, and the OCP
+// 8-bit floats staged two to a 16-bit slot, kFp8Op + 2 * fa + fb with
+// fa, fb the formats of A and B (0 e4m3, 1 e5m2).
+constexpr int kFp8Op = 2;
+
+// One 32 x 32 x 64 MFMA on 8-bit floats with unit block scales (the E8M0
+// scale 127 is 2^0).  Each operand is the lane's 32 bytes of K: the two
+// 16-byte halves given.  A and B take the same bytes of K from their halves,
+// so every k meets its partner whichever k the hardware assigns to them.
+template <int kOp>
+__device__ __forceinline__ f32x16 mfma8(const bf16x8 &a0, const bf16x8 &a1, const bf16x8 &b0,
+                                        const bf16x8 &b1, const f32x16 &c)
+{
+    constexpr int fa = (kOp - kFp8Op) >> 1, fb = (kOp - kFp8Op) & 1;
+    const i32x8 a = __builtin_bit_cast(
+        i32x8, __builtin_shufflevector(__builtin_bit_cast(u16x8, a0), __builtin_bit_cast(u16x8, a1),
+                                       0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+    const i32x8 b = __builtin_bit_cast(
+        i32x8, __builtin_shufflevector(__builtin_bit_cast(u16x8, b0), __builtin_bit_cast(u16x8, b1),
+                                       0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fa, fb, 0, 127, 0, 127);
+}
+
 constexpr int kThreads = 256;
 constexpr int kGroup = 4;   // tile-rows per group in the tile order
 
@@ -432,7 +458,11 @@ __device__ __forceinline__ bf16x8 fragment(const uint16_t *Xs, int base, int s, 
     }
 }
 
-template <int BM, int BN, bool TA, bool TB, bool kVec, bool kF16>
+// kOp: bf16 (0), fp16 (1) or 8-bit floats (kFp8Op and up; A as written and
+// B transposed only, every dimension and leading dimension in 16-bit slots,
+// i.e. halved).  An 8-bit K tile is 128 bytes: two 64-byte MFMA steps, each
+// made of the lane's 16-byte reads of slices 2t and 2t + 1.
+template <int BM, int BN, bool TA, bool TB, bool kVec, int kOp>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, BM == 256 ? 1 : 2)))
 void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A, int64_t lda,
                     int64_t sa, const uint16_t *__restrict__ B, int64_t ldb, int64_t sb,
@@ -441,6 +471,7 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
 {
     using S = Shape<BM, BN>;
     constexpr int MB = S::kMB, NB = S::kNB;
+    static_assert(kOp < kFp8Op || (!TA && TB), "8-bit operands: A as written, B transposed");
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * BK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BK * BN];
 
@@ -478,20 +509,42 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
                 load_operand<BM, S::kAChunks, !TA, kVec>(va, A, lda, m0, M, k0, K, a_full && kfull);
                 load_operand<BN, S::kBChunks, TB, kVec>(vb, B, ldb, n0, N, k0, K, b_full && kfull);
             }
+            if constexpr (kOp >= kFp8Op) {
 #pragma unroll
-            for (int s = 0; s < BK / 16; ++s) {
-                bf16x8 a[MB], b[NB];
+                for (int t = 0; t < BK / 32; ++t) {
+                    bf16x8 a0[MB], a1[MB], b0[NB], b1[NB];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    a[mb] = fragment<BM, !TA>(As[cur], wm * S::kWM + mb * 32, s, lane);
+                    for (int mb = 0; mb < MB; ++mb) {
+                        a0[mb] = fragment<BM, true>(As[cur], wm * S::kWM + mb * 32, 2 * t, lane);
+                        a1[mb] = fragment<BM, true>(As[cur], wm * S::kWM + mb * 32, 2 * t + 1, lane);
+                    }
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    b[nb] = fragment<BN, TB>(Bs[cur], wn * S::kWN + nb * 32, s, lane);
+                    for (int nb = 0; nb < NB; ++nb) {
+                        b0[nb] = fragment<BN, true>(Bs[cur], wn * S::kWN + nb * 32, 2 * t, lane);
+                        b1[nb] = fragment<BN, true>(Bs[cur], wn * S::kWN + nb * 32, 2 * t + 1, lane);
+                    }
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[mb][nb] = mfma8<kOp>(a0[mb], a1[mb], b0[nb], b1[nb], acc[mb][nb]);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < BK / 16; ++s) {
+                    bf16x8 a[MB], b[NB];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        a[mb] = fragment<BM, !TA>(As[cur], wm * S::kWM + mb * 32, s, lane);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb)
-                        acc[mb][nb] = mfma16<kF16>(a[mb], b[nb], acc[mb][nb]);
+                        b[nb] = fragment<BN, TB>(Bs[cur], wn * S::kWN + nb * 32, s, lane);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[mb][nb] = mfma16<kOp == 1>(a[mb], b[nb], acc[mb][nb]);
+                }
             }
             if (more) {
                 store_operand<BM, S::kAChunks, !TA>(va, As[cur ^ 1]);
@@ -777,18 +830,18 @@ hipError_t launch_f32(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int BM, int BN, bool TA, bool TB, bool kF16>
+template <int BM, int BN, bool TA, bool TB, int kOp>
 void launch_bf16_layout(const Problem &p, bool vec, uint32_t blocks, int64_t tm, int64_t tn,
                         hipStream_t s)
 {
     const auto *A = static_cast<const uint16_t *>(p.A);
     const auto *B = static_cast<const uint16_t *>(p.B);
     if (vec)
-        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, true, kF16>), dim3(blocks),
+        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, true, kOp>), dim3(blocks),
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb,
                            p.C, p.ldc, p.sc, p.batch, tm, tn);
     else
-        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, false, kF16>), dim3(blocks),
+        hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, false, kOp>), dim3(blocks),
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb,
                            p.C, p.ldc, p.sc, p.batch, tm, tn);
 }
@@ -801,10 +854,35 @@ hipError_t launch_bf16(const Problem &p, hipStream_t s)
     const uint32_t blocks = static_cast<uint32_t>(tm * tn * p.batch);
     const bool vec = aligned16(p.A) && aligned16(p.B) && p.lda % 8 == 0 && p.ldb % 8 == 0 &&
                      p.sa % 8 == 0 && p.sb % 8 == 0;
-    if (p.ta && p.tb) launch_bf16_layout<BM, BN, true, true, kF16>(p, vec, blocks, tm, tn, s);
-    else if (p.ta) launch_bf16_layout<BM, BN, true, false, kF16>(p, vec, blocks, tm, tn, s);
-    else if (p.tb) launch_bf16_layout<BM, BN, false, true, kF16>(p, vec, blocks, tm, tn, s);
-    else launch_bf16_layout<BM, BN, false, false, kF16>(p, vec, blocks, tm, tn, s);
+    constexpr int op = kF16 ? 1 : 0;
+    if (p.ta && p.tb) launch_bf16_layout<BM, BN, true, true, op>(p, vec, blocks, tm, tn, s);
+    else if (p.ta) launch_bf16_layout<BM, BN, true, false, op>(p, vec, blocks, tm, tn, s);
+    else if (p.tb) launch_bf16_layout<BM, BN, false, true, op>(p, vec, blocks, tm, tn, s);
+    else launch_bf16_layout<BM, BN, false, false, op>(p, vec, blocks, tm, tn, s);
+    return hipGetLastError();
+}
+
+// 8-bit operands (A as written, B transposed; K, lda, ldb, stride_a and
+// stride_b multiples of 16 bytes and A, B 16-byte aligned, as validated):
+// the 16-bit kernel on the same bytes seen as 16-bit slots.
+template <int BM, int BN>
+hipError_t launch_fp8(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
+    if (tm * tn * p.batch > kMaxBlocks || !supports_fp8(p)) return hipErrorInvalidValue;
+    const uint32_t blocks = static_cast<uint32_t>(tm * tn * p.batch);
+    Problem q = p;
+    q.K = p.K / 2;
+    q.lda = p.lda / 2;
+    q.ldb = p.ldb / 2;
+    q.sa = p.sa / 2;
+    q.sb = p.sb / 2;
+    switch (2 * p.fa + p.fb) {
+    case 0: launch_bf16_layout<BM, BN, false, true, kFp8Op + 0>(q, true, blocks, tm, tn, s); break;
+    case 1: launch_bf16_layout<BM, BN, false, true, kFp8Op + 1>(q, true, blocks, tm, tn, s); break;
+    case 2: launch_bf16_layout<BM, BN, false, true, kFp8Op + 2>(q, true, blocks, tm, tn, s); break;
+    default: launch_bf16_layout<BM, BN, false, true, kFp8Op + 3>(q, true, blocks, tm, tn, s); break;
+    }
     return hipGetLastError();
 }
 
@@ -897,6 +975,16 @@ hipError_t launch_mfma_bf16_batched(const Problem &p, hipStream_t s)
 hipError_t launch_mfma_bf16_batched128(const Problem &p, hipStream_t s)
 {
     return launch_bf16<128, 128>(p, s);
+}
+
+hipError_t launch_mfma_fp8_batched(const Problem &p, hipStream_t s)
+{
+    return launch_fp8<256, 256>(p, s);
+}
+
+hipError_t launch_mfma_fp8_batched128(const Problem &p, hipStream_t s)
+{
+    return launch_fp8<128, 128>(p, s);
 }
 
 }  // namespace mi355gemm

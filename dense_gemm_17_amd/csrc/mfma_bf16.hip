@@ -702,6 +702,208 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
         store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
 }
 
+// ---- 8-bit floats on the same staging ---------------------------------------
+// The OCP e4m3 / e5m2 operands of v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+// block scales), A as written and B transposed: both factors then have
+// rows along K, and two 8-bit values sit in each 16-bit slot of the bf16
+// kernel's staging, so a K tile of DBK slots is 64 bytes of K, exactly one
+// MFMA deep.  A lane's 32 bytes per operand are its 16-byte reads of both
+// slices of the tile (the same bytes of K for A and B in every lane, which
+// is all the dot products need).  Per MFMA the matrix unit is busy twice as long as
+// for bf16 while the bytes staged per MFMA are the same, so one tile's
+// MFMAs cover the loads of a tile and the reads of the next: one phase per
+// tile, with the next tile's reads and the loads of the tile four ahead
+// slotted between the MFMAs.  128 x 128 tiles, two work-groups per CU: at
+// 256 x 256 the two fragment sets (128 registers) beside 256 accumulators
+// made the compiler spill (about 600 registers to scratch), so that size is
+// not built.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// A wave's 8-bit operands for one tile: per 32-row (A) or 32-column (B)
+// block the lane's 32 bytes, filled a 16-byte half (one slice) at a time
+// straight into the register tuple the MFMA takes.
+template <int TM, int TN>
+struct Frag8 {
+    i32x8 a[TM / 64], b[TN / 64];
+};
+
+template <int kHalf>
+__device__ __forceinline__ void set_half(i32x8 &v, const u16x8 &x)
+{
+    const i32x4 w = __builtin_bit_cast(i32x4, x);
+    const i32x8 ww = __builtin_shufflevector(w, w, 0, 1, 2, 3, 0, 1, 2, 3);
+    if constexpr (kHalf == 0) v = __builtin_shufflevector(v, ww, 8, 9, 10, 11, 4, 5, 6, 7);
+    else v = __builtin_shufflevector(v, ww, 0, 1, 2, 3, 12, 13, 14, 15);
+}
+
+// Read r of a tile: r < 2 kMB: A block r / 2, slice r % 2; then B likewise.
+template <int TM, int TN>
+__device__ __forceinline__ void read8(Frag8<TM, TN> &f, const uint16_t *stage,
+                                      const DCtx<TM, TN, false, true> &x, int r)
+{
+    constexpr int nA = 2 * (TM / 64);
+    const char *st = reinterpret_cast<const char *>(stage);
+    const bool isA = r < nA;
+    const int j = (isA ? r : r - nA) >> 1, s = r & 1;
+    const u16x8 v = *reinterpret_cast<const u16x8 *>(st + (isA ? x.rdA[s] : x.rdB[s]) + j * 2048);
+    if (isA) {
+        if (s) set_half<1>(f.a[j], v);
+        else set_half<0>(f.a[j], v);
+    } else {
+        if (s) set_half<1>(f.b[j], v);
+        else set_half<0>(f.b[j], v);
+    }
+}
+
+// fp8 operation codes: 2 * fa + fb, fa and fb the formats (0 e4m3, 1 e5m2).
+template <int kFmt>
+__device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmt >> 1, kFmt & 1, 0, 127,
+                                                           0, 127);
+}
+
+// MFMAs of one tile (fragments cur) with the reads of the next tile into
+// nxt and this wave's loads of tile `kload` into stage `lstage` slotted in,
+// spread evenly (256 x 256: one read after each MFMA, a load after every
+// other).
+template <int kFmt, int TM, int TN>
+__device__ __forceinline__ void mfma_phase8(f32x16 (&acc)[TM / 64][TN / 64],
+                                            const Frag8<TM, TN> &cur, Frag8<TM, TN> &nxt,
+                                            const uint16_t *rstage,
+                                            const DCtx<TM, TN, false, true> &x, uint32_t lstage,
+                                            int64_t kload)
+{
+    using T = DTile<TM, TN, false, true>;
+    constexpr int NB = T::kNB, R = 2 * T::kReads, Q = T::kQ;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int mb = q / NB, nb = q % NB;
+        acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], acc[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r * Q / R == q) read8(nxt, rstage, x, r);
+#pragma unroll
+        for (int l = 0; l < T::kPerTile; ++l)
+            if (l * Q / T::kPerTile == q) load_one(x, lstage, kload, l);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// M, N, K, lda, ldb, stride_a and stride_b in 16-bit slots (bytes / 2).
+template <int TM, int TN, bool kRowsC, bool kBatch, int kFmt>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(DTile<TM, TN>::kPerCU, DTile<TM, TN>::kPerCU)))
+void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
+                            int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
+                            float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
+                            int64_t sa, int64_t sb, int64_t sc, int64_t batch)
+{
+    using T = DTile<TM, TN, false, true>;
+    constexpr int MB = T::kMB, NB = T::kNB, WM = TM / 2, WN = TN / 2, P = T::kPerTile;
+    static_assert((DSTAGES - 1) * P <= 63, "vmcnt is six bits");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * T::kStageElems];
+
+    int64_t m0, n0;
+    if constexpr (kBatch) {
+        const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
+        A += t.b * sa;
+        B += t.b * sb;
+        C += t.b * sc;
+        m0 = t.tm * TM;
+        n0 = t.tn * TN;
+    } else {
+        const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+        m0 = t.tm * TM;
+        n0 = t.tn * TN;
+    }
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, c = lane & 31;
+
+    // Both factors as the bf16 kernel's A: rows of K, DBK slots per tile,
+    // rows past M or N re-fetch the last row.
+    DCtx<TM, TN, false, true> x;
+    x.wave = wave;
+    x.lds0 = lds_offset(lds);
+    x.abase = static_cast<const char *>(uniform_ptr(A + m0 * lda));
+    x.bbase = static_cast<const char *>(uniform_ptr(B + n0 * ldb));
+    x.a_kstride = DBK * 2;
+    x.b_kstride = DBK * 2;
+#pragma unroll
+    for (int i = 0; i < T::kAInst; ++i) {
+        const int p = (wave * T::kAInst + i) * 64 + lane;
+        const int row = p >> 2, cc = (p & 3) ^ a_swz<4>(p >> 2);
+        const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
+        x.a_voff[i] = static_cast<uint32_t>((r * lda + 8 * cc) * 2);
+    }
+#pragma unroll
+    for (int i = 0; i < T::kBInst; ++i) {
+        const int p = (wave * T::kBInst + i) * 64 + lane;
+        const int row = p >> 2, cc = (p & 3) ^ a_swz<4>(p >> 2);
+        const int64_t r = (n0 + row < N) ? row : N - 1 - n0;
+        x.b_voff[i] = static_cast<uint32_t>((r * ldb + 8 * cc) * 2);
+    }
+    const int aswz = a_swz<4>(c);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        x.rdA[s] = (wm * WM + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+        x.rdB[s] = TM * DBK * 2 + (wn * WN + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+    }
+
+    f32x16 acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int64_t ktiles = K / DBK;
+    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * T::kStageElems; };
+    auto lstage = [&](int64_t kt) {
+        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * T::kStageElems * 2;
+    };
+    auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
+
+    // Prologue: tiles 0..3 in flight (re-fetching the last tile past the
+    // end); read tile 0 once it has landed; then wait for tile 1 (and every
+    // wave's reads of tile 0, whose stage the first phase refills).
+#pragma unroll
+    for (int st = 0; st < DSTAGES; ++st)
+#pragma unroll
+        for (int l = 0; l < P; ++l) load_one(x, lstage(st), kclamp(st), l);
+    wait_lds_vm_barrier<(DSTAGES - 1) * P>();
+    Frag8<TM, TN> f, g;
+#pragma unroll
+    for (int r = 0; r < 2 * T::kReads; ++r) read8(f, stage(0), x, r);
+    wait_lds_vm_barrier<(DSTAGES - 2) * P>();
+
+    // Tile kt: MFMAs on its fragments (in registers) with the reads of tile
+    // kt + 1 and the loads of tile kt + 4 into tile kt's stage (read in the
+    // previous phase, which every wave finished before the last barrier) |
+    // wait until tile kt + 2 has landed everywhere and this wave's reads are
+    // done, barrier.  Two tiles per trip so the fragment sets alternate
+    // without copies; reads past the last tile hit landed re-fetches.
+    for (int64_t kt = 0; kt < ktiles; kt += 2) {
+        mfma_phase8<kFmt>(acc, f, g, stage(kt + 1), x, lstage(kt), kclamp(kt + DSTAGES));
+        wait_lds_vm_barrier<(DSTAGES - 2) * P>();
+        if (kt + 1 == ktiles) break;
+        mfma_phase8<kFmt>(acc, g, f, stage(kt + 2), x, lstage(kt + 1), kclamp(kt + 1 + DSTAGES));
+        wait_lds_vm_barrier<(DSTAGES - 2) * P>();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    if constexpr (kRowsC)
+        store_c_rows<TM, TN>(acc, reinterpret_cast<float *>(lds), C, ldc, M, N, m0, n0, wm, wn,
+                             lane);
+    else
+        store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
@@ -784,6 +986,57 @@ hipError_t launch_direct(const Problem &p, hipStream_t s)
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256>(p, s); }
 hipError_t launch_mfma_bf16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128>(p, s); }
 hipError_t launch_mfma_f16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256, true>(p, s); }
+
+// 8-bit operands: K a multiple of 64 bytes (one tile), the general 8-bit
+// layout conditions, and lane offsets within 32 bits over the 256 rows of
+// a panel.
+bool supports_mfma_fp8_direct(const Problem &p)
+{
+    const int64_t krows = int64_t(1) << 24;   // bytes per row
+    return supports_fp8(p) && p.K > 0 && p.K % 64 == 0 && p.lda < krows && p.ldb < krows;
+}
+
+namespace {
+
+template <int TM, int TN, bool kRowsC, bool kBatch>
+void launch_fp8_fmt(const Problem &p, const dim3 &grid, int64_t tm, int64_t tn, hipStream_t s)
+{
+    const auto *A = static_cast<const uint16_t *>(p.A);
+    const auto *B = static_cast<const uint16_t *>(p.B);
+#define MI355_FP8_LAUNCH(F)                                                                        \
+    hipLaunchKernelGGL((mfma_fp8_direct_kernel<TM, TN, kRowsC, kBatch, F>), grid, dim3(kThreads), \
+                       0, s, p.M, p.N, p.K / 2, A, p.lda / 2, B, p.ldb / 2, p.C, p.ldc, tm, tn,   \
+                       p.sa / 2, p.sb / 2, p.sc, p.batch)
+    switch (2 * p.fa + p.fb) {
+    case 0: MI355_FP8_LAUNCH(0); break;
+    case 1: MI355_FP8_LAUNCH(1); break;
+    case 2: MI355_FP8_LAUNCH(2); break;
+    default: MI355_FP8_LAUNCH(3); break;
+    }
+#undef MI355_FP8_LAUNCH
+}
+
+template <int TM, int TN>
+hipError_t launch_fp8_direct(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + TM - 1) / TM, tn = (p.N + TN - 1) / TN;
+    if (tm * tn * p.batch > kMaxBlocks || !supports_mfma_fp8_direct(p)) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<uint32_t>(tm * tn * p.batch));
+    const bool rows_c = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0 &&
+                        p.N % 4 == 0 && p.sc % 4 == 0;
+    if (p.batch != 1) {
+        if (rows_c) launch_fp8_fmt<TM, TN, true, true>(p, grid, tm, tn, s);
+        else launch_fp8_fmt<TM, TN, false, true>(p, grid, tm, tn, s);
+    } else {
+        if (rows_c) launch_fp8_fmt<TM, TN, true, false>(p, grid, tm, tn, s);
+        else launch_fp8_fmt<TM, TN, false, false>(p, grid, tm, tn, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s) { return launch_fp8_direct<128, 128>(p, s); }
 hipError_t launch_mfma_f16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, true>(p, s); }
 
 }  // namespace mi355gemm

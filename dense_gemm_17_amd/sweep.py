@@ -40,15 +40,18 @@ import dense_gemm_17_amd as g  # noqa: E402
 import workloads  # noqa: E402
 from dense_gemm_17_amd.measure import ClockSampler, toolchain  # noqa: E402
 
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6, "fp8": 5033.2}
 LLC_BYTES = 256 * 1024 * 1024
-CODE = {"f32": g.F32, "bf16": g.BF16, "f16": g.F16}
-ALL_WORKLOADS = {**workloads.WORKLOADS, **workloads.GENERAL_WORKLOADS}
+CODE = {"f32": g.F32, "bf16": g.BF16, "f16": g.F16, "fp8": g.FP8}
+ALL_WORKLOADS = {**workloads.WORKLOADS, **workloads.GENERAL_WORKLOADS, **workloads.FP8_WORKLOADS}
 
 
 def operands(w, dev):
     """(a, b, c) on the device for workload w: plain products as (M, K),
     (K, N); transposed or batched ones as the views a caller passes."""
+    if w.name in workloads.FP8_WORKLOADS:
+        A, Bt = workloads.make_fp8_inputs(w)
+        return A.to(dev), Bt.to(dev).t(), torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
     if w.name in workloads.GENERAL_WORKLOADS:
         As, Bs = workloads.make_general_inputs(w)
         a, b = workloads.general_views(w, As.to(dev), Bs.to(dev))
@@ -63,6 +66,11 @@ def plan(w, a, b, c):
     """The kernel id the library picks (or the forced one accepts) for
     gemm(a, b, out=c), as a pure host call."""
     code = CODE[w.dtype]
+    if w.name in workloads.FP8_WORKLOADS:
+        return g.gemm_plan_batched(code, 0, 1, w.M, w.N, w.K, 1, A=a.data_ptr(),
+                                   lda=a.stride(-2), stride_a=0, B=b.data_ptr(),
+                                   ldb=b.stride(-1), stride_b=0, C=c.data_ptr(),
+                                   ldc=c.stride(-2), stride_c=0)
     if w.name not in workloads.GENERAL_WORKLOADS:
         return g.gemm_plan(code, w.M, w.N, w.K, a.data_ptr(), a.stride(0), b.data_ptr(),
                            b.stride(0), c.data_ptr(), c.stride(0))

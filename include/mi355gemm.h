@@ -169,6 +169,44 @@ int gemm_f16_f32acc_batched_ws(int transa, int transb, int64_t M, int64_t N, int
                                float *C, int64_t ldc, int64_t stride_c, int64_t batch,
                                void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- 8-bit float operands --------------------------------------------------
+ *
+ * C = A·B (and the strided batch C_b = A_b·B_b) with 8-bit floating-point
+ * operands, exact products, fp32 accumulation and fp32 output.  The FP8
+ * matmul is the last operand-precision step the pages take (vidyal.ai tag
+ * page, Part 6: FP8 on the matrix instructions, and Part 11: FP8 matmuls
+ * and their scales).  The formats are the OCP 8-bit floats the gfx950
+ * matrix cores take, chosen per operand by fmt_a / fmt_b:
+ *   0  e4m3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; no infinities,
+ *      NaN only for the all-ones magnitude 0x7F / 0xFF; largest 448;
+ *   1  e5m2: 1 sign, 5 exponent (bias 15), 2 mantissa bits; IEEE-style
+ *      infinities and NaNs; largest 57344.
+ * Every block scale is 1 (no scaling is applied; a caller folds its scales
+ * into the operands or the output).
+ *
+ * Layout (bytes; each row contiguous): A_b is M x K at
+ * A[b*stride_a + i*lda + k], lda >= K; B is given transposed: Bt_b is N x K,
+ * element (k, j) of B_b at Bt[b*stride_b + j*ldb + k], ldb >= K (both
+ * factors run along K, the layout of a weight stored output-major).  C_b is
+ * fp32 M x N at C[b*stride_c + i*ldc + j] (elements), overwritten.  K, lda,
+ * ldb, stride_a and stride_b must be multiples of 16 and A, Bt 16-byte
+ * aligned; C 4-byte aligned.  Anything else, a format other than 0 or 1, or
+ * outputs that overlap each other or the operands returns
+ * hipErrorInvalidValue without launching.  M, N or batch == 0 is a no-op;
+ * K == 0 writes C = 0.  Ownership, stream ordering, determinism and
+ * threading are as for gemm_bf16_f32acc.  No workspace variant. */
+int gemm_fp8_f32acc(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                    const uint8_t *A, int64_t lda,
+                    const uint8_t *Bt, int64_t ldb,
+                    float *C, int64_t ldc,
+                    hipStream_t stream);
+
+int gemm_fp8_f32acc_batched(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                            const uint8_t *A, int64_t lda, int64_t stride_a,
+                            const uint8_t *Bt, int64_t ldb, int64_t stride_b,
+                            float *C, int64_t ldc, int64_t stride_c,
+                            int64_t batch, hipStream_t stream);
+
 /* Workspace bytes the *_ws calls use for these sizes and element type (0:
  * they use none); a pure host function, no HIP call. */
 size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
@@ -185,6 +223,7 @@ size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t
 #define MI355GEMM_F32  0
 #define MI355GEMM_BF16 1
 #define MI355GEMM_F16  2
+#define MI355GEMM_FP8  3   /* 8-bit floats; gemm_plan_batched needs transa 0, transb 1 */
 
 /* Number of kernels in the library; ids are 0 .. count-1. */
 int gemm_kernel_count(void);

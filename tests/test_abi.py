@@ -44,10 +44,10 @@ def test_kernel_registry():
     names = g.kernel_names()
     assert len(set(names)) == n
     for i in range(n):
-        assert g.gemm_kernel_dtype(i) in (g.F32, g.BF16, g.F16)
+        assert g.gemm_kernel_dtype(i) in (g.F32, g.BF16, g.F16, g.FP8)
     assert g.gemm_kernel_name(-1) == "?" and g.gemm_kernel_name(n) == "?"
     assert g.gemm_kernel_dtype(n) == -1
-    assert {g.gemm_kernel_dtype(i) for i in range(n)} == {g.F32, g.BF16, g.F16}
+    assert {g.gemm_kernel_dtype(i) for i in range(n)} == {g.F32, g.BF16, g.F16, g.FP8}
 
 
 @pytest.mark.parametrize("dtype", [g.F32, g.BF16, g.F16])
@@ -327,3 +327,62 @@ def test_workspace_size():
     assert g.gemm_workspace_size(F32, 0, 0, 384, 1152, 1000) == 0     # no even chunking
     assert g.gemm_workspace_size(7, 0, 0, 384, 1152, 16384) == 0
     assert g.gemm_workspace_size(F32, 0, 0, -1, 1152, 16384) == 0
+
+
+# ---- 8-bit float operands (pure host planning) --------------------------------
+
+FP8_NAMES = ("mfma_fp8_direct128", "mfma_fp8_batched", "mfma_fp8_batched128")
+
+
+def test_plan_fp8_layouts_and_kernels():
+    P = dict(A=PA, B=PB, C=PC)
+    # the one layout: A as written, B transposed
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 8192, 8192, 8192, 1, **P)) in \
+        FP8_NAMES
+    for ta, tb in ((0, 0), (1, 0), (1, 1)):
+        assert g.gemm_plan_batched(g.FP8, ta, tb, 256, 256, 256, 1, **P) == -1
+    assert g.gemm_plan(g.FP8, 256, 256, 256, PA, 256, PB, 256, PC, 256) == -1
+    # K a multiple of 64: the LDS-direct tile takes it; a multiple of 16
+    # only: the register-staged tiles; anything else is rejected
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 300, 260, 192, 1, **P)) == \
+        "mfma_fp8_direct128"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 300, 260, 208, 1, **P)) in \
+        ("mfma_fp8_batched", "mfma_fp8_batched128")
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 300, 260, 200, 1, **P) == -1
+    # leading dimensions and strides in bytes, multiples of 16; 16-byte bases
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, lda=72, **P) == -1
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, ldb=80, **P) >= 0
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 2, stride_a=64 * 64 + 8, **P) == -1
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, A=PA + 8, B=PB, C=PC) == -1
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, A=PA, B=PB + 4, C=PC) == -1
+    # C's range reaching into A's (one byte per operand element)
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, A=PC + 64 * 64 * 4 - 16, B=PB,
+                               C=PC) == -1
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, A=PC + 64 * 64 * 4, B=PB,
+                               C=PC) >= 0
+    # K = 0 is computed (zeros) by a general kernel; empty problems do nothing
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 0, 1, **P)) in FP8_NAMES
+    assert g.gemm_plan_batched(g.FP8, 0, 1, 0, 64, 64, 1, **P) == -2
+    # no workspace variant
+    assert g.gemm_workspace_size(g.FP8, 0, 1, 384, 1152, 16384, 1) == 0
+
+
+def test_fp8_entry_points_reject_before_any_hip_call():
+    # invalid formats and layouts come back without touching the runtime
+    for fa, fb in ((2, 0), (0, -1)):
+        assert g.gemm_fp8_f32acc(fa, fb, 64, 64, 64, PA, 64, PB, 64, PC, 64, None) == INVALID
+    assert g.gemm_fp8_f32acc(0, 0, 64, 64, 24, PA, 64, PB, 64, PC, 64, None) == INVALID
+    assert g.gemm_fp8_f32acc_batched(0, 1, 64, 64, 64, PA, 64, 4104, PB, 64, 4096, PC, 64,
+                                     4096, 2, None) == INVALID
+    assert g.gemm_fp8_f32acc(0, 0, 0, 64, 64, PA, 64, PB, 64, PC, 64, None) == 0
+
+
+def test_forced_fp8_kernel_only_for_fp8_calls():
+    kid = g.kernel_id("mfma_fp8_batched")
+    try:
+        assert g.gemm_force_kernel(kid) == 0
+        # other element types keep the table's choice
+        assert g.gemm_kernel_dtype(g.gemm_plan(g.F32, 512, 512, 512)) == g.F32
+        assert g.gemm_plan_batched(g.FP8, 0, 1, 512, 512, 512, 1) == kid
+    finally:
+        g.gemm_force_kernel(-1)

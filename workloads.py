@@ -227,3 +227,59 @@ def gpt_forward_sequence(tokens: int = 256, layers: int = 6, d_model: int = 384,
                 (f"l{l}_mlp_down", 1, tokens, d_model, 4 * d_model, False, False)]
     seq.append(("lm_head", 1, tokens, vocab, d_model, False, False))
     return seq
+
+
+# ---- 8-bit float operands ------------------------------------------------------
+# Products with OCP 8-bit float operands (e4m3 / e5m2), the weight stored
+# output-major (N x K), as FP8 inference keeps it.  The fp32 draws are
+# rounded to the format (round to nearest even, saturating to the largest
+# finite value where torch's conversion does): N(0, 1) activations and
+# weights, well inside both formats' range.
+FP8_TORCH = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}
+
+
+@dataclass(frozen=True)
+class Fp8Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    fa: int                       # format of A: 0 e4m3, 1 e5m2
+    fb: int                       # format of B
+    batch: int = 1
+    note: str = ""
+    dtype: str = "fp8"
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Each operand read once (1 byte per element), C written once (fp32)."""
+        return self.batch * (self.M * self.K + self.N * self.K + 4 * self.M * self.N)
+
+
+FP8_WORKLOADS: Dict[str, Fp8Workload] = {w.name: w for w in [
+    Fp8Workload("fp8_e4m3_8192", 8192, 8192, 8192, 0, 0,
+                note="e4m3 x e4m3 at the headline size"),
+    Fp8Workload("fp8_e5m2_e4m3_8192", 8192, 8192, 8192, 1, 0,
+                note="e5m2 x e4m3 (gradient x weight pairing) at the headline size"),
+    Fp8Workload("fp8_gpt_qkv", 16384, 1152, 384, 0, 0, note="GPT QKV projection, e4m3"),
+    Fp8Workload("fp8_gpt_mlp_down", 16384, 384, 1536, 0, 0, note="GPT MLP down, e4m3"),
+]}
+
+
+def make_fp8_inputs(w: Fp8Workload, seed: int = SEED) -> Tuple[torch.Tensor, torch.Tensor]:
+    """CPU tensors (A, Bt): A (batch, M, K) or (M, K) and Bt (N, K), the
+    transposed right factor, as 8-bit floats rounded from N(0, 1) draws."""
+    g = generator(seed)
+    shape_a = (w.batch, w.M, w.K) if w.batch > 1 else (w.M, w.K)
+    A = draw(shape_a, ("normal", 1.0), g).to(FP8_TORCH[w.fa])
+    Bt = draw((w.N, w.K), ("normal", 1.0), g).to(FP8_TORCH[w.fb])
+    return A, Bt
+
+
+def fp8_bits(t: torch.Tensor):
+    """Raw 8-bit patterns of a CPU 8-bit float tensor as a numpy uint8 array."""
+    return t.contiguous().view(torch.uint8).numpy()
