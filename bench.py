@@ -103,7 +103,7 @@ def parse():
 
 PROBE_LIB = os.path.join(ROOT, "dense_gemm_17_amd", "libmi355probe.so")
 # flops per MFMA of the probe's instructions: 32x32x16 bf16, 32x32x2 fp32
-PROBE_FLOPS = {"bf16": 2 * 32 * 32 * 16, "f32": 2 * 32 * 32 * 2}
+PROBE_FLOPS = {"bf16": 2 * 32 * 32 * 16, "f32": 2 * 32 * 32 * 2, "fp8": 2 * 32 * 32 * 64}
 
 
 def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
@@ -124,7 +124,7 @@ def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
         # ~5-10 ms per launch.  The vector-ALU loop runs four waves per SIMD
         # (4096 work-groups) to cover the FMA latency.
         code, blocks, iters = {"f32": (0, 1024, 2000), "bf16": (1, 1024, 8000),
-                               "f32_valu": (2, 4096, 20000)}[dt]
+                               "f32_valu": (2, 4096, 20000), "fp8": (3, 1024, 4000)}[dt]
         for zero in ([0, 1] if zero_too else [0]):
             def launch():
                 rc = lib.probe_mfma_loop(code, blocks, iters, zero,
@@ -149,7 +149,8 @@ def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
                 blocks * 256 * iters * 16 * 2
             tf = flops / (ms * 1e-3) / 1e12
             res[f"{dt}_{'zero' if zero else 'random'}"] = {
-                "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_TFLOPS["bf16" if dt == "bf16" else "f32"], 4),
+                "tflops": round(tf, 1),
+                "frac_peak": round(tf / PEAK_TFLOPS[dt if dt in ("bf16", "fp8") else "f32"], 4),
                 **clocks.summary()}
     return res
 
@@ -264,7 +265,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.ceiling_only:
-        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, dtypes=("bf16", "f32", "f32_valu"),
+        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, dtypes=("bf16", "f32", "f32_valu", "fp8"),
                                                         zero_too=True),
                           "toolchain": toolchain(g.gemm_build_info())}), flush=True)
         return

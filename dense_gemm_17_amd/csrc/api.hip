@@ -57,6 +57,7 @@ const KernelInfo kKernels[] = {
     {"mfma_fp8_direct128", kFp8, launch_mfma_fp8_direct128, supports_mfma_fp8_direct, true},
     {"mfma_fp8_batched", kFp8, launch_mfma_fp8_batched, supports_fp8, true},
     {"mfma_fp8_batched128", kFp8, launch_mfma_fp8_batched128, supports_fp8, true},
+    {"mfma_fp8_direct256x128", kFp8, launch_mfma_fp8_direct256x128, supports_mfma_fp8_direct, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -179,10 +180,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // large sizes, used by select_general.
 constexpr int64_t F32_GENERAL_256 = 700, F32_GENERAL_128 = 670;
 constexpr int64_t BF16_GENERAL_256 = 340, BF16_GENERAL_128 = 300;
-// 8-bit floats at 8192^3 (all three within 2%: the LDS-direct 128 x 128
-// tile 0.353, register-staged 256 x 256 0.345, 128 x 128 0.352); the GPT
-// projections (fewer, smaller tiles) favour the 128 x 128 tiles by 1.1-3x.
-constexpr int64_t FP8_BATCHED_256 = 345, FP8_BATCHED_128 = 352, FP8_DIRECT_128 = 353;
+// 8-bit floats at 8192^3: LDS-direct 256 x 128 0.378 (at the board's power
+// limit), 128 x 128 0.341-0.353, register-staged 256 x 256 0.345, 128 x 128
+// 0.337-0.352.  With a short K (the GPT QKV projection, K = 384: six K
+// tiles) the two 128 x 128 work-groups per CU hide each other's prologue
+// and epilogue and win (665 vs 483 TFLOP/s); from K = 1536 (MLP down) the
+// 256 x 128 tile does (889 vs 815).
+constexpr int64_t FP8_BATCHED_256 = 345, FP8_BATCHED_128 = 345, FP8_DIRECT_128 = 345,
+                  FP8_DIRECT_256x128 = 378;
 
 // Relative time of a tiled launch: waves x per-work-group work / efficiency,
 // in units of one CU doing a 128 x 128 tile alone at full rate.
@@ -230,8 +235,9 @@ int select_general(const Problem &p)
     // 8-bit floats: the LDS-direct tiles when K is whole 64-byte tiles,
     // else the register-staged ones (K a multiple of 16 bytes).
     if (p.dtype == kFp8 && supports_mfma_fp8_direct(p))
-        return tiled_cost(p, 256, 256, 1, FP8_BATCHED_256) < tiled_cost(p, 128, 128, 2, FP8_DIRECT_128)
-                   ? kernel_id("mfma_fp8_batched")
+        return p.K >= 1024 && tiled_cost(p, 256, 128, 1, FP8_DIRECT_256x128) <=
+                                  tiled_cost(p, 128, 128, 2, FP8_DIRECT_128)
+                   ? kernel_id("mfma_fp8_direct256x128")
                    : kernel_id("mfma_fp8_direct128");
     if (p.dtype == kFp8)
         return tiled_cost(p, 256, 256, 1, FP8_BATCHED_256) <= tiled_cost(p, 128, 128, 2, FP8_BATCHED_128)

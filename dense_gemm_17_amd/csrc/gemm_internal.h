@@ -87,6 +87,7 @@ hipError_t launch_skinny_f16(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_fp8_direct256x128(const Problem &p, hipStream_t s);
 bool supports_mfma_fp8_direct(const Problem &p);
 
 // Layout every 8-bit kernel needs: A as written and B transposed, K, lda,

@@ -493,7 +493,9 @@ __device__ __forceinline__ void store_c_rows(const f32x16 (&acc)[TM / 64][TN / 6
 {
     constexpr int MB = TM / 64, NB = TN / 64;
     constexpr int kRingFloats = DSTAGES * DTile<TM, TN>::kStageElems / 2;
-    constexpr int kPassRows = kRingFloats / TN < TM ? kRingFloats / TN : TM;
+    constexpr int kRingRows = kRingFloats / TN;   // whole rows the ring holds ...
+    constexpr int kPow2Rows = kRingRows >= 256 ? 256 : kRingRows >= 128 ? 128 : 64;   // ... as 2^n
+    constexpr int kPassRows = kPow2Rows < TM ? kPow2Rows : TM;
     constexpr int kPasses = TM / kPassRows;
     constexpr int kMBP = MB / kPasses;       // 32-row blocks per wave per pass
     constexpr int kHalf = kMBP * 32;         // rows per wave per pass
@@ -713,10 +715,10 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 // for bf16 while the bytes staged per MFMA are the same, so one tile's
 // MFMAs cover the loads of a tile and the reads of the next: one phase per
 // tile, with the next tile's reads and the loads of the tile four ahead
-// slotted between the MFMAs.  128 x 128 tiles, two work-groups per CU: at
-// 256 x 256 the two fragment sets (128 registers) beside 256 accumulators
-// made the compiler spill (about 600 registers to scratch), so that size is
-// not built.
+// slotted between the MFMAs.  128 x 128 tiles (two work-groups per CU) or
+// 256 x 128 (one): at 256 x 256 the two fragment sets (128 registers)
+// beside 256 accumulators made the compiler spill (about 600 registers to
+// scratch), so that size is not built.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -1037,6 +1039,7 @@ hipError_t launch_fp8_direct(const Problem &p, hipStream_t s)
 }  // namespace
 
 hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s) { return launch_fp8_direct<128, 128>(p, s); }
+hipError_t launch_mfma_fp8_direct256x128(const Problem &p, hipStream_t s) { return launch_fp8_direct<256, 128>(p, s); }
 hipError_t launch_mfma_f16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, true>(p, s); }
 
 }  // namespace mi355gemm

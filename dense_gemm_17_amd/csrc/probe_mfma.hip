@@ -48,6 +48,29 @@ __device__ __forceinline__ bf16x8 bf16_operand(uint32_t seed)
     return __builtin_bit_cast(bf16x8, v);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// 32 e4m3 values with random sign, exponent field in [4, 10] (2^-3 .. 2^3)
+// and mantissa: never the NaN pattern.
+__device__ __forceinline__ i32x8 fp8_operand(uint32_t seed)
+{
+    uint32_t x = mix(seed) | 1u;
+    i32x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int byte = 0; byte < 4; ++byte) {
+            x ^= x << 13;
+            x ^= x >> 17;
+            x ^= x << 5;
+            w |= ((x & 0x80u) | ((4u + (x >> 16) % 7u) << 3) | ((x >> 8) & 7u)) << (8 * byte);
+        }
+        v[e] = static_cast<int>(w);
+    }
+    return v;
+}
+
 __device__ __forceinline__ float f32_operand(uint32_t seed)
 {
     const uint32_t h = mix(seed);
@@ -85,6 +108,42 @@ void bf16_loop(float *out, int iters)
                                                                          0, 0, 0);
     }
     // One element of each accumulator keeps every MFMA live.
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum += acc[i][j][0];
+    out[t] = sum;
+}
+
+template <bool kZero>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fp8_loop(float *out, int iters)
+{
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    i32x8 a[2][4], b[2][4];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[s][i] = kZero ? i32x8{} : fp8_operand(t * 16u + s * 8u + i);
+            b[s][i] = kZero ? i32x8{} : fp8_operand(t * 16u + s * 8u + 4u + i);
+        }
+    for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        a[s][i], b[s][j], acc[i][j], 0, 0, 0, 127, 0, 127);
+    }
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -158,7 +217,8 @@ __global__ __launch_bounds__(256) void valu_loop(float *out, int iters)
 }  // namespace
 
 // dtype 0 = fp32 (v_mfma_f32_32x32x2_f32), 1 = bf16 (v_mfma_f32_32x32x16_bf16),
-// 2 = fp32 vector FMA (valu_loop: blocks * 256 * iters * 16 FMAs of 2 flops).
+// 2 = fp32 vector FMA (valu_loop: blocks * 256 * iters * 16 FMAs of 2 flops),
+// 3 = e4m3 (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales; 2*32*32*64 flops).
 // One launch: `blocks` work-groups of 256 threads, each wave doing `iters`
 // (even) rounds of 16 MFMAs, i.e. blocks * 4 * iters * 16 MFMAs of
 // 2*32*32*2 (fp32) or 2*32*32*16 (bf16) flops.  `out` holds blocks * 256
@@ -166,7 +226,7 @@ __global__ __launch_bounds__(256) void valu_loop(float *out, int iters)
 extern "C" int probe_mfma_loop(int dtype, int blocks, int iters, int zero, float *out,
                                hipStream_t stream)
 {
-    if (blocks <= 0 || iters <= 0 || (iters & 1) || !out || dtype < 0 || dtype > 2)
+    if (blocks <= 0 || iters <= 0 || (iters & 1) || !out || dtype < 0 || dtype > 3)
         return hipErrorInvalidValue;
     const dim3 g(blocks), b(256);
     if (dtype == 1 && zero) hipLaunchKernelGGL(bf16_loop<true>, g, b, 0, stream, out, iters);
@@ -175,5 +235,7 @@ extern "C" int probe_mfma_loop(int dtype, int blocks, int iters, int zero, float
     if (dtype == 0 && !zero) hipLaunchKernelGGL(f32_loop<false>, g, b, 0, stream, out, iters);
     if (dtype == 2 && zero) hipLaunchKernelGGL(valu_loop<true>, g, b, 0, stream, out, iters);
     if (dtype == 2 && !zero) hipLaunchKernelGGL(valu_loop<false>, g, b, 0, stream, out, iters);
+    if (dtype == 3 && zero) hipLaunchKernelGGL(fp8_loop<true>, g, b, 0, stream, out, iters);
+    if (dtype == 3 && !zero) hipLaunchKernelGGL(fp8_loop<false>, g, b, 0, stream, out, iters);
     return hipGetLastError();
 }

@@ -331,7 +331,8 @@ def test_workspace_size():
 
 # ---- 8-bit float operands (pure host planning) --------------------------------
 
-FP8_NAMES = ("mfma_fp8_direct128", "mfma_fp8_batched", "mfma_fp8_batched128")
+FP8_NAMES = ("mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_batched",
+             "mfma_fp8_batched128")
 
 
 def test_plan_fp8_layouts_and_kernels():
@@ -345,6 +346,10 @@ def test_plan_fp8_layouts_and_kernels():
     # K a multiple of 64: the LDS-direct tile takes it; a multiple of 16
     # only: the register-staged tiles; anything else is rejected
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 300, 260, 192, 1, **P)) == \
+        "mfma_fp8_direct128"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 8192, 8192, 8192, 1, **P)) == \
+        "mfma_fp8_direct256x128"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 16384, 1152, 384, 1, **P)) == \
         "mfma_fp8_direct128"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 300, 260, 208, 1, **P)) in \
         ("mfma_fp8_batched", "mfma_fp8_batched128")

@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 GATE = oracle.GATE
 FMTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
-KERNELS = ["mfma_fp8_direct128", "mfma_fp8_batched", "mfma_fp8_batched128"]
+KERNELS = ["mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_batched",
+           "mfma_fp8_batched128"]
 TORCH = workloads.FP8_TORCH
 
 

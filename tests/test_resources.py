@@ -26,6 +26,7 @@ OCCUPANCY_BUDGET = {
     "mfma_bf16_direct_kernelILi256ELi256E": 1,
     "mfma_bf16_direct_kernelILi128ELi128E": 2,
     "mfma_fp8_direct_kernelILi128ELi128E": 2,
+    "mfma_fp8_direct_kernelILi256ELi128E": 1,
     "mfma_f32_direct_kernelILi256ELi256E": 1,
     "mfma_f32_direct_kernelILi128ELi128E": 2,
     "mfma_f32_direct_kernelILi128ELi64E": 3,
