@@ -58,6 +58,7 @@ const KernelInfo kKernels[] = {
     {"mfma_fp8_batched", kFp8, launch_mfma_fp8_batched, supports_fp8, true},
     {"mfma_fp8_batched128", kFp8, launch_mfma_fp8_batched128, supports_fp8, true},
     {"mfma_fp8_direct256x128", kFp8, launch_mfma_fp8_direct256x128, supports_mfma_fp8_direct, true},
+    {"skinny_fp8", kFp8, launch_skinny_fp8, supports_skinny_fp8, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -234,6 +235,12 @@ int select_general(const Problem &p)
                    : kernel_id("mfma_bf16_batched128");
     // 8-bit floats: the LDS-direct tiles when K is whole 64-byte tiles,
     // else the register-staged ones (K a multiple of 16 bytes).
+    // 8-bit floats with at most 4 rows (one product): stream Bt once on the
+    // vector ALUs (1 x 8960 x 1536: 7.8 vs 11.1 us for the 128 x 128 tile).
+    // With more rows the widening and fp32 FMAs (about 19 vector operations
+    // per byte of Bt at 16 rows) outrun the stream and the matrix cores win
+    // (16 x 8192 x 8192: 41.9 us on the 128 x 128 tile vs 51.9).
+    if (p.dtype == kFp8 && p.M <= 4 && supports_skinny_fp8(p)) return kernel_id("skinny_fp8");
     if (p.dtype == kFp8 && supports_mfma_fp8_direct(p))
         return p.K >= 1024 && tiled_cost(p, 256, 128, 1, FP8_DIRECT_256x128) <=
                                   tiled_cost(p, 128, 128, 2, FP8_DIRECT_128)

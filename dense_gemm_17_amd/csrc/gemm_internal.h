@@ -89,6 +89,8 @@ hipError_t launch_mfma_fp8_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_direct256x128(const Problem &p, hipStream_t s);
 bool supports_mfma_fp8_direct(const Problem &p);
+hipError_t launch_skinny_fp8(const Problem &p, hipStream_t s);
+bool supports_skinny_fp8(const Problem &p);
 
 // Layout every 8-bit kernel needs: A as written and B transposed, K, lda,
 // ldb, stride_a and stride_b multiples of 16 (bytes), A and B 16-byte

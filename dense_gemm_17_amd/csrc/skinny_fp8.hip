@@ -1,0 +1,147 @@
+// Bandwidth kernel for 8-bit float products with few rows (M <= 16):
+// C (M x N) = A B with B given transposed (Bt, N x K, each row running
+// along K), the shape of a decode step through FP8 weights (vidyal.ai tag
+// page, Part 11: low-precision matmuls are bandwidth-bound at small batch).
+// Such products sit far below the ridge point, so their time is the time
+// to stream Bt once.
+//
+//   * each wave owns four rows of Bt (four columns of C); its 64 lanes
+//     take consecutive 16-byte chunks of each row, so every load
+//     instruction reads 1 KiB contiguous per row;
+//   * A (at most 16 rows) is read from the caches by every wave;
+//   * the 8-bit values are widened to fp32 with the hardware conversion
+//     (v_cvt_pk_f32_fp8 / _bf8) and multiplied and added in fp32 (exact
+//     products);
+//   * each lane's partial sums are added over the wave by an xor butterfly,
+//     which leaves the same total in every lane (a fixed order: the result
+//     is repeatable bit for bit).
+#include "gemm_internal.h"
+
+namespace mi355gemm {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRows = 4;    // rows of Bt per wave
+constexpr int kWaves = 4;   // waves per work-group
+
+// Sixteen 8-bit values (format 0 e4m3, 1 e5m2) as fp32.  A and B are
+// widened by the same code, so any order of the values within the chunk
+// pairs each k with its partner.
+template <int kFmt>
+__device__ __forceinline__ void widen16(const u32x4 &v, float (&out)[16])
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int w = static_cast<int>(v[q]);
+        f32x2 lo, hi;
+        if constexpr (kFmt == 0) {
+            lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+        } else {
+            lo = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+            hi = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+        }
+        out[4 * q] = lo[0];
+        out[4 * q + 1] = lo[1];
+        out[4 * q + 2] = hi[0];
+        out[4 * q + 3] = hi[1];
+    }
+}
+
+// kMR >= M accumulator rows; K a multiple of 16, rows 16-byte aligned.
+template <int kMR, int kFA, int kFB>
+__global__ __launch_bounds__(64 * kWaves) void skinny_fp8_kernel(
+    int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ A, int64_t lda,
+    const uint8_t *__restrict__ Bt, int64_t ldb, float *__restrict__ C, int64_t ldc)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t j0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kRows;
+    if (j0 >= N) return;   // wave-uniform
+    float acc[kMR][kRows];
+#pragma unroll
+    for (int i = 0; i < kMR; ++i)
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) acc[i][r] = 0.f;
+    const int64_t chunks = K / 16;
+#pragma unroll 2
+    for (int64_t c = lane; c < chunks; c += 64) {
+        u32x4 b[kRows];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r)
+            b[r] = (j0 + r < N) ? *reinterpret_cast<const u32x4 *>(Bt + (j0 + r) * ldb + 16 * c)
+                                : u32x4{0u, 0u, 0u, 0u};
+        float bf[kRows][16];
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) widen16<kFB>(b[r], bf[r]);
+#pragma unroll
+        for (int i = 0; i < kMR; ++i) {
+            if (i >= M) break;
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(A + i * lda + 16 * c);
+            float af[16];
+            widen16<kFA>(a, af);
+#pragma unroll
+            for (int r = 0; r < kRows; ++r)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][r] = __builtin_fmaf(af[e], bf[r][e], acc[i][r]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMR; ++i)
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            float v = acc[i][r];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            acc[i][r] = v;
+        }
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < kMR; ++i)
+#pragma unroll
+            for (int r = 0; r < kRows; ++r)
+                if (i < M && j0 + r < N) store_c_stream(C + i * ldc + j0 + r, acc[i][r]);
+    }
+}
+
+template <int kMR>
+void launch_rows(const Problem &p, dim3 grid, hipStream_t s)
+{
+    const auto *A = static_cast<const uint8_t *>(p.A);
+    const auto *B = static_cast<const uint8_t *>(p.B);
+#define MI355_SKINNY_FP8(FA, FB)                                                                \
+    hipLaunchKernelGGL((skinny_fp8_kernel<kMR, FA, FB>), grid, dim3(64 * kWaves), 0, s, p.M,  \
+                       p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc)
+    switch (2 * p.fa + p.fb) {
+    case 0: MI355_SKINNY_FP8(0, 0); break;
+    case 1: MI355_SKINNY_FP8(0, 1); break;
+    case 2: MI355_SKINNY_FP8(1, 0); break;
+    default: MI355_SKINNY_FP8(1, 1); break;
+    }
+#undef MI355_SKINNY_FP8
+}
+
+}  // namespace
+
+bool supports_skinny_fp8(const Problem &p)
+{
+    return supports_fp8(p) && p.batch == 1 && p.M <= kSkinnyMaxM;
+}
+
+hipError_t launch_skinny_fp8(const Problem &p, hipStream_t s)
+{
+    if (!supports_skinny_fp8(p)) return hipErrorInvalidValue;
+    const int64_t per_block = kWaves * kRows;
+    const int64_t blocks = (p.N + per_block - 1) / per_block;
+    if (blocks > kMaxBlocks) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<uint32_t>(blocks));
+    if (p.M <= 1) launch_rows<1>(p, grid, s);
+    else if (p.M <= 2) launch_rows<2>(p, grid, s);
+    else if (p.M <= 4) launch_rows<4>(p, grid, s);
+    else if (p.M <= 8) launch_rows<8>(p, grid, s);
+    else launch_rows<16>(p, grid, s);
+    return hipGetLastError();
+}
+
+}  // namespace mi355gemm

@@ -332,7 +332,7 @@ def test_workspace_size():
 # ---- 8-bit float operands (pure host planning) --------------------------------
 
 FP8_NAMES = ("mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_batched",
-             "mfma_fp8_batched128")
+             "mfma_fp8_batched128", "skinny_fp8")
 
 
 def test_plan_fp8_layouts_and_kernels():
@@ -365,6 +365,15 @@ def test_plan_fp8_layouts_and_kernels():
                                C=PC) == -1
     assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, A=PC + 64 * 64 * 4, B=PB,
                                C=PC) >= 0
+    # at most 4 rows of one product: the bandwidth kernel
+    for M in (1, 3, 4):
+        assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, M, 8960, 1536, 1, **P)) == \
+            "skinny_fp8"
+    for M in (5, 16, 17):
+        assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, M, 8960, 1536, 1, **P)) != \
+            "skinny_fp8"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 1, 8960, 1536, 2, **P)) != \
+        "skinny_fp8"
     # K = 0 is computed (zeros) by a general kernel; empty problems do nothing
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 0, 1, **P)) in FP8_NAMES
     assert g.gemm_plan_batched(g.FP8, 0, 1, 0, 64, 64, 1, **P) == -2

@@ -26,6 +26,8 @@ GATE = oracle.GATE
 FMTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
 KERNELS = ["mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_batched",
            "mfma_fp8_batched128"]
+SKINNY_SHAPES = [(1, 300, 1024), (2, 77, 16), (3, 130, 4096), (7, 520, 256), (16, 64, 2048),
+                 (9, 1000, 208)]
 TORCH = workloads.FP8_TORCH
 
 
@@ -210,3 +212,55 @@ def test_benchmark_shapes_sampled(name):
                                       w.fa, w.fb, False, True, threads=8)
     e, at, _ = oracle.normalized_error(C[rows].cpu().numpy(), Cref, D)
     assert e <= GATE, (e, at)
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
+def test_skinny_gate_and_exact(M, N, K):
+    """At most 16 rows: the bandwidth kernel (Bt streamed once; the table's
+    choice up to 4 rows), forced; random operands to the gate, small
+    integers exactly, all four format pairings."""
+    assert takes("skinny_fp8", M, N, K)
+    gen = workloads.generator(36)
+    for fa, fb in FMTS:
+        A, Bt = randn((M, K), fa, gen), randn((N, K), fb, gen)
+        say(f"fp8 skinny formats {fa},{fb} {M}x{N}x{K}")
+        with Forced("skinny_fp8"):
+            C = run(A, Bt)
+        assert g.gemm_kernel_name(g.gemm_last_kernel()) == "skinny_fp8"
+        Cref, D = ref(A, Bt, fa, fb)
+        e, at, _ = oracle.normalized_error(C.cpu().numpy(), Cref, D)
+        assert e <= GATE, (fa, fb, e, at)
+        Ai = workloads.small_int((M, K), -8, 8, gen).to(TORCH[fa])
+        Bi = workloads.small_int((N, K), -8, 8, gen).to(TORCH[fb])
+        with Forced("skinny_fp8"):
+            C = run(Ai, Bi)
+        Cref, _ = ref(Ai, Bi, fa, fb)
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), Cref)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("kernel", ["skinny_fp8", "mfma_fp8_direct128"])
+def test_every_finite_pattern_decodes(fmt, kernel):
+    """C = A times a one-hot Bt: row 0 of A holds every finite pattern of
+    the format once, column j of C picks pattern j, so C[0] is the
+    decoded value of each pattern (exact)."""
+    bits = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(bits.copy()).view(TORCH[fmt]).float()
+    keep = torch.isfinite(vals).numpy()
+    pats = bits[keep]
+    K = 256
+    N = len(pats)
+    A = np.zeros((1, K), dtype=np.uint8)
+    A[0, :N] = pats
+    one = torch.ones(1).to(TORCH[fmt]).view(torch.uint8).item()
+    Bt = np.zeros((N, K), dtype=np.uint8)
+    Bt[np.arange(N), np.arange(N)] = one
+    At = torch.from_numpy(A).view(TORCH[fmt])
+    Btt = torch.from_numpy(Bt).view(TORCH[fmt])
+    say(f"fp8 decode {kernel} format {fmt}")
+    with Forced(kernel):
+        C = run(At, Btt)
+    assert g.gemm_kernel_name(g.gemm_last_kernel()) == kernel
+    expect = oracle.load().decode_fp8(fmt, pats)
+    got = C[0].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, expect)      # -0 comes out as +0: it is added to +0 terms

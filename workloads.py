@@ -267,6 +267,12 @@ FP8_WORKLOADS: Dict[str, Fp8Workload] = {w.name: w for w in [
                 note="e5m2 x e4m3 (gradient x weight pairing) at the headline size"),
     Fp8Workload("fp8_gpt_qkv", 16384, 1152, 384, 0, 0, note="GPT QKV projection, e4m3"),
     Fp8Workload("fp8_gpt_mlp_down", 16384, 384, 1536, 0, 0, note="GPT MLP down, e4m3"),
+    Fp8Workload("fp8_skinny_1x8960x1536", 1, 8960, 1536, 0, 0,
+                note="one-row product through e4m3 weights (decode-like)"),
+    Fp8Workload("fp8_skinny_4x8192x8192", 4, 8192, 8192, 0, 0,
+                note="four-row product through e4m3 weights"),
+    Fp8Workload("fp8_skinny_16x8192x8192", 16, 8192, 8192, 0, 0,
+                note="sixteen-row product through e4m3 weights"),
 ]}
 
 
