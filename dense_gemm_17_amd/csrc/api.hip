@@ -242,8 +242,11 @@ int select_general(const Problem &p)
     // (16 x 8192 x 8192: 41.9 us on the 128 x 128 tile vs 51.9).
     if (p.dtype == kFp8 && p.M <= 4 && supports_skinny_fp8(p)) return kernel_id("skinny_fp8");
     if (p.dtype == kFp8 && supports_mfma_fp8_direct(p))
-        return p.K >= 1024 && tiled_cost(p, 256, 128, 1, FP8_DIRECT_256x128) <=
-                                  tiled_cost(p, 128, 128, 2, FP8_DIRECT_128)
+        // (M <= 128: one 128-row tile covers M and the 256-row tile would
+        // do at least twice the padded work; 16 x 8192 x 8192: 41.9 vs 58.6 us)
+        return p.K >= 1024 && p.M > 128 &&
+                       tiled_cost(p, 256, 128, 1, FP8_DIRECT_256x128) <=
+                           tiled_cost(p, 128, 128, 2, FP8_DIRECT_128)
                    ? kernel_id("mfma_fp8_direct256x128")
                    : kernel_id("mfma_fp8_direct128");
     if (p.dtype == kFp8)

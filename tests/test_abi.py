@@ -372,6 +372,9 @@ def test_plan_fp8_layouts_and_kernels():
     for M in (5, 16, 17):
         assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, M, 8960, 1536, 1, **P)) != \
             "skinny_fp8"
+    # rows that one 128-row tile covers: the 128 x 128 tile, whatever K
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 16, 8192, 8192, 1, **P)) == \
+        "mfma_fp8_direct128"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 1, 8960, 1536, 2, **P)) != \
         "skinny_fp8"
     # K = 0 is computed (zeros) by a general kernel; empty problems do nothing
