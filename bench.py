@@ -19,12 +19,6 @@ Prints exactly one JSON line.  Extra legs:
       scaled by what the counters read for the copy, tagged with a digest of
       the kernel's sources.  The benchmark line reports that traffic for the
       dominant kernel only while the digest still matches (else null).
-  mfma ceiling (default on, --no-ceiling skips it; --ceiling-only runs just
-      it, with zero operands for contrast): a loop of nothing but MFMAs on
-      random operands of each timed dtype, from libmi355probe.so, after the
-      clock has settled.  Reported beside the roofline as context: on this
-      board the bf16 matrix cores run at the power limit, where the clock
-      (and so the reachable throughput) depends on the operand data.
   other configurations (default on, --no-configs skips it): the table's
       kernel on every other workload of the set (the small, GPT-shaped,
       skinny and ragged products), time per call of back-to-back calls (and
@@ -92,67 +86,13 @@ def parse():
     p.add_argument("--check-rows", type=int, default=8,
                    help="rows per product checked against the oracle after timing")
     p.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--runs", type=int, default=3,
+                   help="processes the step is timed in (this one and runs-1 children, each "
+                        "started before this process touches the GPU) for the spread")
+    p.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     p.add_argument("--no-configs", action="store_true",
                    help="skip the other configurations' section (profiler runs of the step)")
-    p.add_argument("--no-ceiling", action="store_true",
-                   help="skip the matrix-core ceiling probe (profiler runs)")
-    p.add_argument("--ceiling-only", action="store_true",
-                   help="run only the ceiling probe, random and zero operands")
     return p.parse_args()
-
-
-PROBE_LIB = os.path.join(ROOT, "dense_gemm_17_amd", "libmi355probe.so")
-# flops per MFMA of the probe's instructions: 32x32x16 bf16, 32x32x2 fp32
-PROBE_FLOPS = {"bf16": 2 * 32 * 32 * 16, "f32": 2 * 32 * 32 * 2, "fp8": 2 * 32 * 32 * 64}
-
-
-def mfma_ceiling(dev, dtypes=("bf16", "f32"), zero_too=False, settle_s=2.0):
-    """Steady-state throughput of a loop of nothing but MFMAs (operands in
-    registers, no memory traffic) on 1024 work-groups of one wave per SIMD,
-    as the GEMM kernels run: the most a kernel built on the same instruction
-    can reach on this board with such operand data.  Each case first runs
-    for `settle_s` seconds so the clock has settled at the power limit."""
-    import ctypes
-    from dense_gemm_17_amd.measure import ClockSampler
-    lib = ctypes.CDLL(PROBE_LIB)
-    lib.probe_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_void_p, ctypes.c_void_p]
-    out = torch.empty(4096 * 256, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    res = {}
-    for dt in dtypes:
-        # ~5-10 ms per launch.  The vector-ALU loop runs four waves per SIMD
-        # (4096 work-groups) to cover the FMA latency.
-        code, blocks, iters = {"f32": (0, 1024, 2000), "bf16": (1, 1024, 8000),
-                               "f32_valu": (2, 4096, 20000), "fp8": (3, 1024, 4000)}[dt]
-        for zero in ([0, 1] if zero_too else [0]):
-            def launch():
-                rc = lib.probe_mfma_loop(code, blocks, iters, zero,
-                                         out.data_ptr(), stream.cuda_stream)
-                if rc != 0:
-                    raise RuntimeError(f"probe_mfma_loop failed: {rc}")
-            t_end = time.perf_counter() + settle_s
-            while time.perf_counter() < t_end:
-                for _ in range(20):
-                    launch()
-                torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 40
-            with ClockSampler() as clocks:
-                e0.record(stream)
-                for _ in range(reps):
-                    launch()
-                e1.record(stream)
-                torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            flops = blocks * 4 * iters * 16 * PROBE_FLOPS[dt] if dt != "f32_valu" else \
-                blocks * 256 * iters * 16 * 2
-            tf = flops / (ms * 1e-3) / 1e12
-            res[f"{dt}_{'zero' if zero else 'random'}"] = {
-                "tflops": round(tf, 1),
-                "frac_peak": round(tf / PEAK_TFLOPS[dt if dt in ("bf16", "fp8") else "f32"], 4),
-                **clocks.summary()}
-    return res
 
 
 def code_text(path: str) -> str:
@@ -211,7 +151,7 @@ def ingest_counters(fetch_dir: str, write_dir: str):
                                   "bytes_per_launch": round(fb + wb), "dispatches": len(f),
                                   "source_digest": source_digest(kernel)}
     with open(TRAFFIC_FILE, "w") as fh:
-        run = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-ceiling --no-configs --copy-calibration"
+        run = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs --copy-calibration"
         fh.write("# HBM bytes per launch at 8192^3, one rocprofv3 run per counter:\n")
         for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             fh.write(f"#   timeout -s KILL 90 rocprofv3 --pmc {ctr} -d {d} -o pmc "
@@ -256,6 +196,12 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    # The spread over separate processes: the children run first, before
+    # this process initialises the GPU, each timing the same step on its own.
+    children = []
+    if not args.child:
+        for _ in range(max(0, args.runs - 1)):
+            children.append(child_run(args))
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -264,11 +210,6 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    if args.ceiling_only:
-        print(json.dumps({"mfma_ceiling": mfma_ceiling(dev, dtypes=("bf16", "f32", "f32_valu", "fp8"),
-                                                        zero_too=True),
-                          "toolchain": toolchain(g.gemm_build_info())}), flush=True)
-        return
     names = [n for n in args.workloads.split(",") if n]
     ws = [workloads.WORKLOADS[n] for n in names]
 
@@ -325,6 +266,11 @@ def main():
     total_flops = sum(w.flops for w in ws)
     ms_per_step = wall * 1e3 / args.steps
     value = total_flops / (wall / args.steps) / 1e9
+    if args.child:
+        print(json.dumps({"ms_per_step": ms_per_step,
+                          "avg_ms": {n: r["avg_ms"] for n, r in per.items()}}), flush=True)
+        return
+    null_us = identity_null(dev, args.steps * len(ops))
 
     # correctness of what was timed: a few rows against the oracle
     check = {}
@@ -355,10 +301,6 @@ def main():
         sequence = sequence_config(dev)
         fp8 = fp8_configs(dev, args.check_rows)
 
-    ceiling = None
-    if not args.no_ceiling:
-        ceiling = mfma_ceiling(dev, dtypes=sorted({w.dtype for w in ws}))
-
     dom = max(per.values(), key=lambda r: r["avg_ms"])
     dom_w = next(w for w in ws if per[w.name] is dom)
     roofline = {
@@ -366,6 +308,11 @@ def main():
         "achieved": dom["tflops"], "peak": PEAK_TFLOPS[dom_w.dtype], "unit": "TFLOP/s",
         "frac": dom["frac_peak"], "traffic": traffic_for(dom["kernel"]),
     }
+    runs = [{"ms_per_step": ms_per_step, "avg_ms": {n: r["avg_ms"] for n, r in per.items()}}]
+    runs += [c for c in children if c is not None]
+    spread = {"processes": len(runs), "ms_per_step": spread_of([r["ms_per_step"] for r in runs])}
+    for n in per:
+        spread[n + "_avg_ms"] = spread_of([r["avg_ms"][n] for r in runs if n in r["avg_ms"]])
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -374,17 +321,20 @@ def main():
         "data": "synthetic (seed 1234; fp32 uniform[-1,1], bf16 from N(0,1))",
         "config": {"workload": "+".join(names),
                    "shapes": {w.name: [w.M, w.N, w.K] for w in ws}},
+        # each product's own rate: value above is the step's flops over the
+        # step's time, which blends the two dtypes
+        "headline": {n: {"gflops": round(r["tflops"] * 1e3, 1), "frac_peak": r["frac_peak"],
+                         "kernel": r["kernel"], "avg_ms": r["avg_ms"]} for n, r in per.items()},
+        # the step timed in separate processes (median, min, max)
+        "spread": spread,
+        # a do-nothing kernel timed the same way as each product (one launch
+        # between two events on the same stream)
+        "identity_null_us": null_us,
         "per_kernel": per, "max_norm_err_sampled": check,
         "roofline": roofline,
         "roofline_by_kernel": {n: {"bound": "mfma", "achieved": r["tflops"],
                                    "peak": PEAK_TFLOPS[r["dtype"]], "unit": "TFLOP/s",
-                                   "frac": r["frac_peak"],
-                                   "frac_of_measured_ceiling":
-                                       round(r["tflops"] / ceiling[f"{r['dtype']}_random"]["tflops"], 4)
-                                       if ceiling else None} for n, r in per.items()},
-        # context, not the roofline: an MFMA-only loop on random operands of
-        # the same type, timed on this board in this run
-        "mfma_ceiling": ceiling,
+                                   "frac": r["frac_peak"]} for n, r in per.items()},
         "cpu_baseline": cpu,
         # every other configuration of the set, the table's kernel, time per
         # call (short calls also from a replayed HIP graph), its roofline and
@@ -711,6 +661,63 @@ def fp8_configs(dev, check_rows):
     return out
 
 
+def spread_of(xs):
+    xs = sorted(float(x) for x in xs)
+    if not xs:
+        return None
+    return {"median": round(float(np.median(xs)), 4), "min": round(xs[0], 4),
+            "max": round(xs[-1], 4), "n": len(xs)}
+
+
+def child_run(args):
+    """Time the step in a process of its own (started as a child, never by
+    replacing this one); returns its per-step and per-product times, or None
+    if it failed."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--child", "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--workloads", args.workloads, "--no-cpu-baseline",
+           "--no-configs", "--check-rows", "1"]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    except subprocess.TimeoutExpired:
+        return None
+    if r.returncode != 0:
+        print(f"bench child run failed ({r.returncode}): {r.stderr[-400:]}", file=sys.stderr)
+        return None
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    return json.loads(lines[-1]) if lines else None
+
+
+def identity_null(dev, reps):
+    """Microseconds per launch of a kernel that does nothing, timed like
+    the products: one launch between two events on the current stream,
+    averaged over `reps` launches."""
+    import dense_gemm_17_amd as g
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(10):
+        g.gemm_null_launch(stream.cuda_stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        rc = g.gemm_null_launch(stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"gemm_null_launch failed: {rc}")
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return round(float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3, 2)
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(ws, host, seconds):
     """The oracle, as it stands, on a bounded sample: the first R rows of each
     product of the step, R sized from a short calibration run."""
@@ -736,7 +743,7 @@ def cpu_baseline(ws, host, seconds):
         flops += 2 * r * w.N * w.K
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e9, 3), "unit": "GFLOP/s", "cores": th,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {rows} rows of each product of the step "
                       f"({flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64 accumulation)"}
 

@@ -74,6 +74,8 @@ def _load() -> ctypes.CDLL:
     lib.gemm_last_kernel.restype = ci
     lib.gemm_build_info.argtypes = []
     lib.gemm_build_info.restype = ctypes.c_char_p
+    lib.gemm_null_launch.argtypes = [vp]
+    lib.gemm_null_launch.restype = ci
     return lib
 
 
@@ -85,7 +87,8 @@ EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched"
            "gemm_bf16_f32acc_batched_ws", "gemm_f16_f32acc_batched_ws", "gemm_fp8_f32acc",
            "gemm_fp8_f32acc_batched", "gemm_workspace_size",
            "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
-           "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info")
+           "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info",
+           "gemm_null_launch")
 
 
 # ---- raw entry points (pointers and sizes, same names as the C-ABI) --------
@@ -180,6 +183,10 @@ def gemm_last_kernel() -> int:
 
 def gemm_build_info() -> str:
     return lib.gemm_build_info().decode()
+
+
+def gemm_null_launch(stream) -> int:
+    return lib.gemm_null_launch(stream)
 
 
 def kernel_id(name: str) -> int:

@@ -3,9 +3,7 @@
 Every HIP source under csrc/ is compiled to an object (in parallel), then the
 objects are linked into ``dense_gemm_17_amd/libmi355gemm.so``.  The compiler's
 per-kernel resource remarks (VGPR/AGPR/SGPR counts, scratch, LDS, occupancy)
-are kept in ``_build/resources.txt`` for the resource-budget test.  Sources
-named ``probe_*.hip`` are measurement probes, not GEMM kernels: they go into
-a separate ``libmi355probe.so`` that only the benchmark loads.
+are kept in ``_build/resources.txt`` for the resource-budget test.
 
 Usage:  python dense_gemm_17_amd/build.py   (run by path: importing the package
         needs the library this script builds)
@@ -21,7 +19,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmi355gemm.so")
-PROBE_LIB = os.path.join(HERE, "libmi355probe.so")
 ROOT = os.path.dirname(HERE)
 
 ARCH = "gfx950"
@@ -38,9 +35,8 @@ HIP_FLAGS = [
 REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 
 
-def sources(probes: bool = False):
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
-                  if f.endswith(".hip") and f.startswith("probe_") == probes)
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _link(objs, out):
@@ -62,22 +58,19 @@ def _compile(src: str) -> tuple:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link the shared libraries; returns the
-    GEMM library's path."""
+    """Compile every HIP source and link the shared library; returns its
+    path."""
     os.makedirs(BUILD, exist_ok=True)
-    srcs, probes = sources(), sources(probes=True)
-    jobs = max(1, min(len(srcs) + len(probes), int(os.environ.get("MAX_JOBS", "8"))))
+    srcs = sources()
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", "8"))))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, srcs + probes))
-    gemm, probe = results[:len(srcs)], results[len(srcs):]
+        results = list(ex.map(_compile, srcs))
     with open(os.path.join(BUILD, "resources.txt"), "w") as f:
-        for _, remarks in gemm:
+        for _, remarks in results:
             f.write(remarks)
-    _link([o for o, _ in gemm], LIB)
-    if probe:
-        _link([o for o, _ in probe], PROBE_LIB)
+    _link([o for o, _ in results], LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB} from {len(probes)}")
+        print(f"built {LIB} from {len(srcs)} sources")
     return LIB
 
 

@@ -539,6 +539,8 @@ size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t
     return static_cast<size_t>(workspace_needed(p));
 }
 
+int gemm_null_launch(hipStream_t stream) { return launch_null(stream); }
+
 int gemm_kernel_count(void) { return kNumKernels; }
 
 const char *gemm_kernel_name(int id)

@@ -55,6 +55,7 @@ struct KernelInfo {
 hipError_t launch_naive_f32(const Problem &p, hipStream_t s);
 hipError_t launch_naive_bf16(const Problem &p, hipStream_t s);
 hipError_t launch_fill_zero(const Problem &p, hipStream_t s);
+hipError_t launch_null(hipStream_t s);
 hipError_t launch_valu_f32(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_128(const Problem &p, hipStream_t s);

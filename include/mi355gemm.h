@@ -263,6 +263,14 @@ int gemm_force_kernel(int id);
  * (-1 before any). */
 int gemm_last_kernel(void);
 
+/* Timing hook: enqueues one launch of a kernel that does nothing (one
+ * work-group of 64 lanes) on `stream` and returns the launch status.  It is
+ * the null measurement of the devpost write-up ("gpu kernels", "How we know
+ * the numbers are real": every timed kernel sits beside a do-nothing kernel
+ * timed the same way), so that launch and timer cost can be read off next
+ * to the products.  Touches no memory. */
+int gemm_null_launch(hipStream_t stream);
+
 /* Static description of the toolchain that compiled this library (compiler
  * version, HIP version, target), for recording beside measurements; never
  * freed.  Reading it needs no GPU and starts no process. */

@@ -12,7 +12,10 @@ with the magnitude sum D = sum_k |a_ik * b_kj| that the correctness gate
 divides by.  Every entry point here is pinned by ``tests/test_oracle.py``
 (identity, permutation, ones, exact small-integer, brute force against exact
 rational arithmetic, numpy fp64 BLAS, thread-count invariance and planted
-mutants); no function is "parity unpinned".
+mutants).  The row-sampled entries (fp32, bf16 and fp16) are pinned to the
+selected rows of the full product and, on small-integer operands, to the
+exact integer product's rows, with a planted fp16-rows mistake that the pin
+rejects; no function is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -33,7 +36,7 @@ CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
           "-pthread", "-shared", "-fPIC", "-Wall", "-Wextra"]
 
 MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP", "IGNORE_TA", "BATCH_B0",
-           "F16_BIAS", "E4M3_NAN")
+           "F16_BIAS", "E4M3_NAN", "F16_ROWS_BF16")
 
 
 def build(out: str = _LIB_PATH, mutant: Optional[str] = None) -> str:

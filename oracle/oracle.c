@@ -45,6 +45,8 @@
  *   ORACLE_MUTANT_BATCH_B0     - every product of a batch reads the first B
  *   ORACLE_MUTANT_F16_BIAS     - fp16 decode uses an exponent bias of 16
  *   ORACLE_MUTANT_E4M3_NAN     - e4m3 decode treats exponent 15 as infinity/NaN
+ *   ORACLE_MUTANT_F16_ROWS_BF16 - the fp16 row-sampled entry decodes its
+ *                                 operands as bf16 patterns
  */
 
 static double decode_bf16(uint16_t bits)
@@ -324,7 +326,11 @@ int oracle_gemm_f16_rows(int64_t M, int64_t N, int64_t K,
                          const int64_t *rows, int64_t nrows,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
+#ifdef ORACLE_MUTANT_F16_ROWS_BF16
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
+#else
     job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
+#endif
     return run(j, nthreads);
 }
 

@@ -125,8 +125,7 @@ def test_plan_is_pure():
 
 
 # The dispatch table's choice for every workload of the benchmark set, and
-# for the layout cases that change it.  Measured alternatives for each row
-# are recorded by dense_gemm_17_amd/sweep.py.
+# for the layout cases that change it.
 DISPATCH_GOLDEN = {
     "f32_256": "mfma_f32_splitk",
     "f32_4096": "mfma_f32_direct",

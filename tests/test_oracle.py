@@ -271,6 +271,33 @@ def pin_f16_matches_decoded_f32(o):
     assert np.array_equal(C, C2) and np.array_equal(D, D2)
 
 
+def pin_rows_subsets(o):
+    # the row-sampled entries (the checkers of the largest products) must
+    # give exactly the selected rows of the full product, for every element
+    # type, with rows repeated and out of order; on small-integer operands
+    # they must also equal the exact integer product's rows
+    rows = [19, 2, 2, 0, 11]
+    r = rng(31)
+    A = (r.standard_normal((20, 37)) * 2).astype(np.float16)
+    B = (r.standard_normal((37, 15)) * 1e-3).astype(np.float16)    # subnormals included
+    C, D = o.gemm_f16(A, B)
+    Cr, Dr = o.gemm_f16(A, B, rows=rows, threads=2)
+    assert np.array_equal(Cr, C[rows]) and np.array_equal(Dr, D[rows])
+    g = workloads.generator(32)
+    for dt, fn in ((torch.float16, o.gemm_f16), (torch.float32, o.gemm_f32)):
+        Ai = workloads.small_int((20, 41), -8, 8, g, dt)
+        Bi = workloads.small_int((41, 9), -8, 8, g, dt)
+        Cr, Dr = fn(Ai.numpy(), Bi.numpy(), rows=rows)
+        Ae, Be = Ai.to(torch.int64).numpy(), Bi.to(torch.int64).numpy()
+        assert np.array_equal(Cr, (Ae @ Be)[rows].astype(np.float64))
+        assert np.array_equal(Dr, (np.abs(Ae) @ np.abs(Be))[rows].astype(np.float64))
+    Ab = workloads.bf16_bits(workloads.small_int((20, 30), -8, 8, g, torch.bfloat16))
+    Bb = workloads.bf16_bits(workloads.small_int((30, 10), -8, 8, g, torch.bfloat16))
+    Cb, Db = o.gemm_bf16(Ab, Bb)
+    Cbr, Dbr = o.gemm_bf16(Ab, Bb, rows=rows)
+    assert np.array_equal(Cbr, Cb[rows]) and np.array_equal(Dbr, Db[rows])
+
+
 FP8_TORCH = {0: torch.float8_e4m3fn, 1: torch.float8_e5m2}
 
 
@@ -320,7 +347,7 @@ PINS = [pin_golden, pin_identity, pin_permutation, pin_ones, pin_small_int_f32,
         pin_small_int_bf16, pin_bf16_matches_decoded_f32, pin_numpy_blas,
         pin_transposed_small_int, pin_transposed_permutation, pin_batched,
         pin_f16_decoder, pin_small_int_f16, pin_f16_matches_decoded_f32,
-        pin_fp8_decoders, pin_fp8_products,
+        pin_fp8_decoders, pin_fp8_products, pin_rows_subsets,
         lambda o: pin_brute_force(o, [(2, 3, 4), (3, 1, 5), (4, 4, 2)])]
 
 
