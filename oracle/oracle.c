@@ -129,6 +129,7 @@ typedef struct {
     int64_t r0, r1;        /* this worker's block of output rows */
     int ta, tb;            /* operand stored transposed: A as K x M, B as N x K */
     int kind_b;            /* B's element type when it differs from A's (8-bit formats) */
+    const double *Bd;      /* B's values decoded once into a K x N fp64 array, or NULL */
 } job_t;
 
 /* Element (i, k) of the M x K left factor.  Stored as written (row i at
@@ -147,7 +148,7 @@ static double load_a(const job_t *j, int64_t i, int64_t k)
     return decode_kind(j->kind, ((const uint16_t *)j->A)[at]);
 }
 
-static double load_b(const job_t *j, int64_t k, int64_t n)
+static double load_b_stored(const job_t *j, int64_t k, int64_t n)
 {
 #ifdef ORACLE_MUTANT_TRANSPOSE_B
     int64_t t = k; k = n % j->K; n = t % j->N;
@@ -160,6 +161,16 @@ static double load_b(const job_t *j, int64_t k, int64_t n)
     if (j->kind >= KIND_E4M3)
         return decode_byte(j->kind_b, ((const uint8_t *)j->B)[at]);
     return decode_kind(j->kind, ((const uint16_t *)j->B)[at]);
+}
+
+/* Element (k, n) of B: from the decoded copy when there is one (any B that
+ * is not plain row-major fp32), else straight from storage.  The copy holds
+ * exactly the values load_b_stored returns; it only spares the inner loop a
+ * decode or a strided read per multiply. */
+static double load_b(const job_t *j, int64_t k, int64_t n)
+{
+    if (j->Bd) return j->Bd[k * j->N + n];
+    return load_b_stored(j, k, n);
 }
 
 /* One output row: acc and den start at zero, then for each k the row of B is
@@ -215,9 +226,18 @@ static int run(job_t base, int nthreads)
     if (nthreads > base.nrows) nthreads = (int)base.nrows;
     if (nthreads > 1024) nthreads = 1024;
 
+    double *bd = NULL;
+    if (base.K > 0 && (base.kind != KIND_F32 || base.tb)) {
+        bd = (double *)malloc(sizeof(double) * (size_t)base.K * (size_t)base.N);
+        if (!bd) return 2;
+        for (int64_t k = 0; k < base.K; ++k)
+            for (int64_t n = 0; n < base.N; ++n) bd[k * base.N + n] = load_b_stored(&base, k, n);
+        base.Bd = bd;
+    }
+
     job_t *jobs = (job_t *)malloc(sizeof(job_t) * (size_t)nthreads);
     pthread_t *tids = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
-    if (!jobs || !tids) { free(jobs); free(tids); return 2; }
+    if (!jobs || !tids) { free(jobs); free(tids); free(bd); return 2; }
     int64_t per = base.nrows / nthreads, extra = base.nrows % nthreads, r = 0;
     int started = 0, rc = 0;
     for (int t = 0; t < nthreads; ++t) {
@@ -234,6 +254,7 @@ static int run(job_t base, int nthreads)
     for (int t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
     free(jobs);
     free(tids);
+    free(bd);
     return rc;
 }
 
@@ -244,7 +265,7 @@ int oracle_gemm_f32(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda, const float *B, int64_t ldb,
                     double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL};
     return run(j, nthreads);
 }
 
@@ -252,7 +273,7 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                      double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL};
     return run(j, nthreads);
 }
 
@@ -263,7 +284,7 @@ int oracle_gemm_f32_rows(int64_t M, int64_t N, int64_t K,
                          const int64_t *rows, int64_t nrows,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
     return run(j, nthreads);
 }
 
@@ -272,7 +293,7 @@ int oracle_gemm_bf16_rows(int64_t M, int64_t N, int64_t K,
                           const int64_t *rows, int64_t nrows,
                           double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
     return run(j, nthreads);
 }
 
@@ -304,7 +325,7 @@ int oracle_gemm_batched(int kind, int ta, int tb, int64_t M, int64_t N, int64_t 
         job_t j = {kind, M, N, K,
                    (const char *)A + b * sa * es, lda,
                    (const char *)B + bb * sb * es, ldb,
-                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0, 0};
+                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0, 0, NULL};
         int rc = run(j, nthreads);
         if (rc != 0) return rc;
     }
@@ -317,7 +338,7 @@ int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                     double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0};
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL};
     return run(j, nthreads);
 }
 
@@ -327,9 +348,9 @@ int oracle_gemm_f16_rows(int64_t M, int64_t N, int64_t K,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
 #ifdef ORACLE_MUTANT_F16_ROWS_BF16
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
 #else
-    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0};
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
 #endif
     return run(j, nthreads);
 }
@@ -353,7 +374,7 @@ int oracle_gemm_fp8_batched(int fmt_a, int fmt_b, int ta, int tb, int64_t M, int
     for (int64_t b = 0; b < batch; ++b) {
         job_t j = {KIND_E4M3 + fmt_a, M, N, K, A + b * sa, lda, B + b * sb, ldb,
                    C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0,
-                   KIND_E4M3 + fmt_b};
+                   KIND_E4M3 + fmt_b, NULL};
         int rc = run(j, nthreads);
         if (rc != 0) return rc;
     }

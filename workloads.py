@@ -21,6 +21,7 @@ write-up ("What we built") routes through a dispatch table.
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 from typing import Dict, List, Tuple
 
@@ -289,3 +290,68 @@ def make_fp8_inputs(w: Fp8Workload, seed: int = SEED) -> Tuple[torch.Tensor, tor
 def fp8_bits(t: torch.Tensor):
     """Raw 8-bit patterns of a CPU 8-bit float tensor as a numpy uint8 array."""
     return t.contiguous().view(torch.uint8).numpy()
+
+
+# ---- fused attention forward ---------------------------------------------------
+# The GPT's attention ("Bare Metal Bard", page 1, second and third paragraphs:
+# 6 heads of width 64 over a context of 256, 64 sequences; the fused kernel
+# let the same model train at a context of 2048).  Q, K and V are read where
+# the QKV projection leaves them: one (B*S) x (3*H*D) fp32 buffer, token-major,
+# the Q block of each token's row first, then K, then V, each H heads of D;
+# the output is written token-major, (B*S) x (H*D), as the attention output
+# projection reads it.  Entries are N(0, 1): with the 1/sqrt(D) scale the
+# scores are of order one, so the softmax is neither flat nor one-hot.
+
+
+@dataclass(frozen=True)
+class AttentionWorkload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    causal: bool
+    note: str = ""
+    dtype: str = "f32"
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def pairs(self) -> int:
+        """(query, key) pairs scored per head: S^2, or S(S+1)/2 with the
+        causal mask."""
+        return self.S * (self.S + 1) // 2 if self.causal else self.S * self.S
+
+    @property
+    def flops(self) -> int:
+        """Two products per scored pair, each of D multiply-adds: 4 D flops
+        per pair (the exponentials are not counted)."""
+        return 4 * self.B * self.H * self.pairs * self.D
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O written once (fp32), plus the log-sum-exp."""
+        return 4 * self.B * self.H * self.S * (4 * self.D + 1)
+
+
+ATTENTION_WORKLOADS: Dict[str, AttentionWorkload] = {w.name: w for w in [
+    AttentionWorkload("attn_gpt_causal", 64, 6, 256, 64, True,
+                      note="the GPT's attention: 64 sequences, 6 heads of 64, context 256"),
+    AttentionWorkload("attn_gpt_full", 64, 6, 256, 64, False,
+                      note="the same without the causal mask"),
+    AttentionWorkload("attn_2048_causal", 8, 6, 2048, 64, True,
+                      note="context 2048, 8 sequences"),
+]}
+
+
+def make_attention_qkv(w: AttentionWorkload, seed: int = SEED) -> torch.Tensor:
+    """The QKV projection's output, (B*S) x (3*H*D) fp32, N(0, 1)."""
+    return draw((w.B * w.S, 3 * w.H * w.D), ("normal", 1.0), generator(seed))
+
+
+def attention_views(w: AttentionWorkload, qkv: torch.Tensor):
+    """Q, K, V as (B, H, S, D) views of the projection buffer (no copy)."""
+    t = qkv.view(w.B, w.S, 3, w.H, w.D)
+    return tuple(t[:, :, i].permute(0, 2, 1, 3) for i in range(3))
