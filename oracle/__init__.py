@@ -36,7 +36,7 @@ CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math",
           "-pthread", "-shared", "-fPIC", "-Wall", "-Wextra"]
 
 MUTANTS = ("DROP_LAST_K", "TRANSPOSE_B", "SIGNED_D", "BF16_SWAP", "IGNORE_TA", "BATCH_B0",
-           "F16_BIAS", "E4M3_NAN", "F16_ROWS_BF16")
+           "F16_BIAS", "E4M3_NAN", "F16_ROWS_BF16", "MX_BLOCK16", "E8M0_BIAS")
 
 
 def build(out: str = _LIB_PATH, mutant: Optional[str] = None) -> str:
@@ -76,6 +76,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_gemm_fp8_batched.restype = ci
     lib.oracle_decode_fp8.argtypes = [ci, _vp, _vp, _i64]
     lib.oracle_decode_fp8.restype = None
+    lib.oracle_gemm_mxfp8.argtypes = [ci, ci, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                                      _vp, _i64, _vp, _i64, _vp, _vp, _i64, ci]
+    lib.oracle_gemm_mxfp8.restype = ci
+    lib.oracle_decode_e8m0.argtypes = [_vp, _vp, _i64]
+    lib.oracle_decode_e8m0.restype = None
     return lib
 
 
@@ -233,6 +238,47 @@ class Oracle:
             raise RuntimeError(f"oracle_gemm_fp8_batched failed with code {rc}")
         return (C[0], D[0]) if two_d else (C, D)
 
+    def gemm_mxfp8(self, A: np.ndarray, SA: np.ndarray, Bt: np.ndarray, SB: np.ndarray,
+                   fmt_a: int = 0, fmt_b: int = 0, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """(C, D) in fp64 for 8-bit operands with MX block scales: A (M x K)
+        and Bt (N x K) uint8 patterns, SA (K/32 x >= M) and SB (K/32 x >= N)
+        uint8 E8M0 scales, the scale of block kb of row i of A at SA[kb, i]
+        (rows of the scale arrays may be padded)."""
+        A = np.asarray(A, dtype=np.uint8)
+        Bt = np.asarray(Bt, dtype=np.uint8)
+        M, K = A.shape
+        N, K2 = Bt.shape
+        if K != K2:
+            raise ValueError(f"inner dimensions differ: {K} and {K2}")
+        SA = np.asarray(SA, dtype=np.uint8)
+        SB = np.asarray(SB, dtype=np.uint8)
+        for S_, n in ((SA, M), (SB, N)):
+            if S_.ndim != 2 or S_.shape[1] < n or S_.shape[0] * 32 < K or \
+                    (S_.shape[1] > 1 and S_.strides[1] != 1):
+                raise ValueError("scales must be (blocks of K) x (rows) uint8, unit column stride")
+        lda = A.strides[0] if M > 1 else max(K, 1)
+        ldb = Bt.strides[0] if N > 1 else max(K, 1)
+        if (K > 1 and (A.strides[1] != 1 or Bt.strides[1] != 1)):
+            raise ValueError("operands need unit stride along K")
+        C = np.zeros((M, N), dtype=np.float64)
+        D = np.zeros((M, N), dtype=np.float64)
+        ptr = lambda a: a.ctypes.data if a.size else None  # noqa: E731
+        ld_sa = SA.strides[0] if SA.shape[0] > 1 else SA.shape[1]
+        ld_sb = SB.strides[0] if SB.shape[0] > 1 else SB.shape[1]
+        rc = self.lib.oracle_gemm_mxfp8(fmt_a, fmt_b, M, N, K, ptr(A), lda, ptr(SA), ld_sa,
+                                        ptr(Bt), ldb, ptr(SB), ld_sb, ptr(C), ptr(D), max(N, 1),
+                                        threads)
+        if rc != 0:
+            raise RuntimeError(f"oracle_gemm_mxfp8 failed with code {rc}")
+        return C, D
+
+    def decode_e8m0(self, bits: np.ndarray) -> np.ndarray:
+        bits = np.ascontiguousarray(bits, dtype=np.uint8).reshape(-1)
+        out = np.empty(bits.shape, dtype=np.float64)
+        if bits.size:
+            self.lib.oracle_decode_e8m0(bits.ctypes.data, out.ctypes.data, bits.size)
+        return out
+
     def decode_fp8(self, fmt: int, bits: np.ndarray) -> np.ndarray:
         bits = np.ascontiguousarray(bits, dtype=np.uint8).reshape(-1)
         out = np.empty(bits.shape, dtype=np.float64)
@@ -271,6 +317,10 @@ def gemm_f16(A, B, rows=None, threads=0):
 
 def gemm_fp8_batched(A, B, fmt_a=0, fmt_b=0, transa=False, transb=False, threads=0):
     return load().gemm_fp8_batched(A, B, fmt_a, fmt_b, transa, transb, threads)
+
+
+def gemm_mxfp8(A, SA, Bt, SB, fmt_a=0, fmt_b=0, threads=0):
+    return load().gemm_mxfp8(A, SA, Bt, SB, fmt_a, fmt_b, threads)
 
 
 def gemm_batched(A, B, transa=False, transb=False, threads=0):

@@ -47,6 +47,8 @@
  *   ORACLE_MUTANT_E4M3_NAN     - e4m3 decode treats exponent 15 as infinity/NaN
  *   ORACLE_MUTANT_F16_ROWS_BF16 - the fp16 row-sampled entry decodes its
  *                                 operands as bf16 patterns
+ *   ORACLE_MUTANT_MX_BLOCK16   - MX scales applied per 16 elements of K, not 32
+ *   ORACLE_MUTANT_E8M0_BIAS    - E8M0 scale exponent biased by 128, not 127
  */
 
 static double decode_bf16(uint16_t bits)
@@ -106,6 +108,28 @@ static double decode_e5m2(uint8_t bits)
     return sign ? -v : v;
 }
 
+/* OCP microscaling (MX) block scale, E8M0: an 8-bit biased exponent and
+ * nothing else, the value 2^(e - 127); the all-ones pattern is NaN.  One
+ * scale covers a block of 32 consecutive elements along K. */
+static double decode_e8m0(uint8_t e)
+{
+    int bias = 127;
+#ifdef ORACLE_MUTANT_E8M0_BIAS
+    bias = 128;
+#endif
+    if (e == 255) return NAN;
+    return ldexp(1.0, (int)e - bias);
+}
+
+static int64_t mx_block(int64_t k)
+{
+#ifdef ORACLE_MUTANT_MX_BLOCK16
+    return k / 16;
+#else
+    return k / 32;
+#endif
+}
+
 enum { KIND_F32 = 0, KIND_BF16 = 1, KIND_F16 = 2, KIND_E4M3 = 3, KIND_E5M2 = 4 };
 
 static double decode_byte(int kind, uint8_t bits)
@@ -130,6 +154,10 @@ typedef struct {
     int ta, tb;            /* operand stored transposed: A as K x M, B as N x K */
     int kind_b;            /* B's element type when it differs from A's (8-bit formats) */
     const double *Bd;      /* B's values decoded once into a K x N fp64 array, or NULL */
+    const uint8_t *sa, *sb;  /* MX block scales of A and B (E8M0), or NULL: scale of block
+                                kb of row i of A at sa[kb * ld_sa + i], of column n of B
+                                at sb[kb * ld_sb + n] */
+    int64_t ld_sa, ld_sb;
 } job_t;
 
 /* Element (i, k) of the M x K left factor.  Stored as written (row i at
@@ -143,8 +171,10 @@ static double load_a(const job_t *j, int64_t i, int64_t k)
 #endif
     if (j->kind == KIND_F32)
         return (double)((const float *)j->A)[at];
-    if (j->kind >= KIND_E4M3)
-        return decode_byte(j->kind, ((const uint8_t *)j->A)[at]);
+    if (j->kind >= KIND_E4M3) {
+        const double v = decode_byte(j->kind, ((const uint8_t *)j->A)[at]);
+        return j->sa ? v * decode_e8m0(j->sa[mx_block(k) * j->ld_sa + i]) : v;
+    }
     return decode_kind(j->kind, ((const uint16_t *)j->A)[at]);
 }
 
@@ -158,13 +188,16 @@ static double load_b_stored(const job_t *j, int64_t k, int64_t n)
     int64_t at = j->tb ? n * j->ldb + k : k * j->ldb + n;
     if (j->kind == KIND_F32)
         return (double)((const float *)j->B)[at];
-    if (j->kind >= KIND_E4M3)
-        return decode_byte(j->kind_b, ((const uint8_t *)j->B)[at]);
+    if (j->kind >= KIND_E4M3) {
+        const double v = decode_byte(j->kind_b, ((const uint8_t *)j->B)[at]);
+        return j->sb ? v * decode_e8m0(j->sb[mx_block(k) * j->ld_sb + n]) : v;
+    }
     return decode_kind(j->kind, ((const uint16_t *)j->B)[at]);
 }
 
-/* Element (k, n) of B: from the decoded copy when there is one (any B that
- * is not plain row-major fp32), else straight from storage.  The copy holds
+/* Element (k, n) of B: from the decoded copy when there is one (fp16 and
+ * 8-bit patterns, whose decode is the slow part, and any B stored
+ * transposed), else straight from storage.  The copy holds
  * exactly the values load_b_stored returns; it only spares the inner loop a
  * decode or a strided read per multiply. */
 static double load_b(const job_t *j, int64_t k, int64_t n)
@@ -227,7 +260,7 @@ static int run(job_t base, int nthreads)
     if (nthreads > 1024) nthreads = 1024;
 
     double *bd = NULL;
-    if (base.K > 0 && (base.kind != KIND_F32 || base.tb)) {
+    if (base.K > 0 && (base.kind == KIND_F16 || base.kind >= KIND_E4M3 || base.tb)) {
         bd = (double *)malloc(sizeof(double) * (size_t)base.K * (size_t)base.N);
         if (!bd) return 2;
         for (int64_t k = 0; k < base.K; ++k)
@@ -265,7 +298,7 @@ int oracle_gemm_f32(int64_t M, int64_t N, int64_t K,
                     const float *A, int64_t lda, const float *B, int64_t ldb,
                     double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL, NULL, NULL, 0, 0};
     return run(j, nthreads);
 }
 
@@ -273,7 +306,7 @@ int oracle_gemm_bf16(int64_t M, int64_t N, int64_t K,
                      const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                      double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL, NULL, NULL, 0, 0};
     return run(j, nthreads);
 }
 
@@ -284,7 +317,7 @@ int oracle_gemm_f32_rows(int64_t M, int64_t N, int64_t K,
                          const int64_t *rows, int64_t nrows,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
+    job_t j = {KIND_F32, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL, NULL, NULL, 0, 0};
     return run(j, nthreads);
 }
 
@@ -293,7 +326,7 @@ int oracle_gemm_bf16_rows(int64_t M, int64_t N, int64_t K,
                           const int64_t *rows, int64_t nrows,
                           double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL, NULL, NULL, 0, 0};
     return run(j, nthreads);
 }
 
@@ -325,7 +358,7 @@ int oracle_gemm_batched(int kind, int ta, int tb, int64_t M, int64_t N, int64_t 
         job_t j = {kind, M, N, K,
                    (const char *)A + b * sa * es, lda,
                    (const char *)B + bb * sb * es, ldb,
-                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0, 0, NULL};
+                   C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0, 0, NULL, NULL, NULL, 0, 0};
         int rc = run(j, nthreads);
         if (rc != 0) return rc;
     }
@@ -338,7 +371,7 @@ int oracle_gemm_f16(int64_t M, int64_t N, int64_t K,
                     const uint16_t *A, int64_t lda, const uint16_t *B, int64_t ldb,
                     double *C, double *D, int64_t ldo, int nthreads)
 {
-    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL};
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, NULL, M, 0, 0, 0, 0, 0, NULL, NULL, NULL, 0, 0};
     return run(j, nthreads);
 }
 
@@ -348,9 +381,9 @@ int oracle_gemm_f16_rows(int64_t M, int64_t N, int64_t K,
                          double *C, double *D, int64_t ldo, int nthreads)
 {
 #ifdef ORACLE_MUTANT_F16_ROWS_BF16
-    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
+    job_t j = {KIND_BF16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL, NULL, NULL, 0, 0};
 #else
-    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL};
+    job_t j = {KIND_F16, M, N, K, A, lda, B, ldb, C, D, ldo, rows, nrows, 0, 0, 0, 0, 0, NULL, NULL, NULL, 0, 0};
 #endif
     return run(j, nthreads);
 }
@@ -374,17 +407,45 @@ int oracle_gemm_fp8_batched(int fmt_a, int fmt_b, int ta, int tb, int64_t M, int
     for (int64_t b = 0; b < batch; ++b) {
         job_t j = {KIND_E4M3 + fmt_a, M, N, K, A + b * sa, lda, B + b * sb, ldb,
                    C + b * M * ldo, D + b * M * ldo, ldo, NULL, M, 0, 0, ta != 0, tb != 0,
-                   KIND_E4M3 + fmt_b, NULL};
+                   KIND_E4M3 + fmt_b, NULL, NULL, NULL, 0, 0};
         int rc = run(j, nthreads);
         if (rc != 0) return rc;
     }
     return 0;
 }
 
+/* 8-bit operands with MX block scales (OCP microscaling: every 32
+ * consecutive elements along K of a row of A, or of a column of B, share
+ * one E8M0 scale): A stored M x K as written, B given transposed (stored
+ * N x K, row n at Bt + n*ldb),
+ *     C[i][n] = sum_k (a_ik * 2^(SA[k/32][i] - 127)) * (b_kn * 2^(SB[k/32][n] - 127))
+ * with the scale of block kb of row i of A at SA[kb*ld_sa + i] and of
+ * column n of B at SB[kb*ld_sb + n].  Each scaled element is exact in fp64
+ * (a power of two times a value of at most 4 significant bits), so the only
+ * rounding is the fp64 sum, as for the unscaled product. */
+int oracle_gemm_mxfp8(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                      const uint8_t *A, int64_t lda, const uint8_t *SA, int64_t ld_sa,
+                      const uint8_t *Bt, int64_t ldb, const uint8_t *SB, int64_t ld_sb,
+                      double *C, double *D, int64_t ldo, int nthreads)
+{
+    if ((fmt_a != 0 && fmt_a != 1) || (fmt_b != 0 && fmt_b != 1)) return 1;
+    if (M < 0 || N < 0 || K < 0 || ld_sa < M || ld_sb < N) return 1;
+    if (K > 0 && (!SA || !SB)) return 1;
+    job_t j = {KIND_E4M3 + fmt_a, M, N, K, A, lda, Bt, ldb, C, D, ldo, NULL, M, 0, 0, 0, 1,
+               KIND_E4M3 + fmt_b, NULL, SA, SB, ld_sa, ld_sb};
+    return run(j, nthreads);
+}
+
 /* 8-bit pattern -> fp64 (fmt 0: e4m3, 1: e5m2), exposed to pin the decoders. */
 void oracle_decode_fp8(int fmt, const uint8_t *in, double *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = decode_byte(KIND_E4M3 + fmt, in[i]);
+}
+
+/* E8M0 scale pattern -> fp64, exposed for the same reason. */
+void oracle_decode_e8m0(const uint8_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = decode_e8m0(in[i]);
 }
 
 /* fp16 pattern -> fp64, exposed for the same reason. */

@@ -343,11 +343,58 @@ def pin_fp8_products(o):
     assert np.array_equal(C, C2) and np.array_equal(D, D2)
 
 
+def pin_mx_scales(o):
+    """8-bit operands with MX block scales (one E8M0 scale per 32 elements of
+    K of each row of A and each column of B)."""
+    # the scale decoder on all 256 patterns against torch's own E8M0 type
+    bits = np.arange(256, dtype=np.uint8)
+    mine = o.decode_e8m0(bits)
+    ref = torch.from_numpy(bits.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref)) and np.isnan(mine[255])
+    assert np.array_equal(mine[:255], ref[:255]) and mine[127] == 1.0 and mine[130] == 8.0
+    g = workloads.generator(40)
+    # unit scales (127) are exactly the unscaled product
+    A = workloads.small_int((9, 96), -8, 8, g).to(torch.float8_e4m3fn)
+    Bt = workloads.small_int((7, 96), -8, 8, g).to(torch.float8_e5m2)
+    ones_a = np.full((3, 9), 127, np.uint8)
+    ones_b = np.full((3, 7), 127, np.uint8)
+    C, D = o.gemm_mxfp8(fp8_bits(A), ones_a, fp8_bits(Bt), ones_b, 0, 1)
+    C0, D0 = o.gemm_fp8_batched(fp8_bits(A), fp8_bits(Bt), 0, 1, False, True)
+    assert np.array_equal(C, C0) and np.array_equal(D, D0)
+    # worked by hand: 1 x 1 x 64 of ones, A's blocks scaled 2 and 1/2, B's 1 and 8:
+    # 32 * 2 * 1 + 32 * (1/2) * 8 = 192
+    one_a = torch.ones((1, 64)).to(torch.float8_e4m3fn)
+    one_b = torch.ones((1, 64)).to(torch.float8_e4m3fn)
+    C, D = o.gemm_mxfp8(fp8_bits(one_a), np.array([[128], [126]], np.uint8), fp8_bits(one_b),
+                        np.array([[127], [130]], np.uint8))
+    assert C[0, 0] == 192.0 and D[0, 0] == 192.0
+    C, _ = o.gemm_mxfp8(fp8_bits(one_a), np.array([[255], [127]], np.uint8), fp8_bits(one_b),
+                        np.array([[127], [127]], np.uint8))
+    assert np.isnan(C[0, 0])                       # the NaN scale
+    # small integers with random scales, against exact block sums
+    for (M, N, K, fa, fb) in [(5, 6, 128, 0, 0), (3, 11, 96, 1, 0)]:
+        A = workloads.small_int((M, K), -8, 8, g).to(FP8_TORCH[fa])
+        Bt = workloads.small_int((N, K), -8, 8, g).to(FP8_TORCH[fb])
+        SA = torch.randint(118, 137, (K // 32, M + 3), generator=g).to(torch.uint8).numpy()
+        SB = torch.randint(118, 137, (K // 32, N), generator=g).to(torch.uint8).numpy()
+        C, D = o.gemm_mxfp8(fp8_bits(A), SA[:, :M], fp8_bits(Bt), SB, fa, fb)
+        Ai, Bi = A.to(torch.int64).numpy(), Bt.to(torch.int64).numpy()
+        want = np.zeros((M, N))
+        wabs = np.zeros((M, N))
+        for kb in range(K // 32):
+            blk = slice(32 * kb, 32 * kb + 32)
+            sc = np.exp2(SA[kb, :M].astype(np.float64) - 127)[:, None] * \
+                np.exp2(SB[kb].astype(np.float64) - 127)[None, :]
+            want += sc * (Ai[:, blk] @ Bi[:, blk].T)
+            wabs += sc * (np.abs(Ai[:, blk]) @ np.abs(Bi[:, blk]).T)
+        assert np.array_equal(C, want) and np.array_equal(D, wabs)
+
+
 PINS = [pin_golden, pin_identity, pin_permutation, pin_ones, pin_small_int_f32,
         pin_small_int_bf16, pin_bf16_matches_decoded_f32, pin_numpy_blas,
         pin_transposed_small_int, pin_transposed_permutation, pin_batched,
         pin_f16_decoder, pin_small_int_f16, pin_f16_matches_decoded_f32,
-        pin_fp8_decoders, pin_fp8_products, pin_rows_subsets,
+        pin_fp8_decoders, pin_fp8_products, pin_rows_subsets, pin_mx_scales,
         lambda o: pin_brute_force(o, [(2, 3, 4), (3, 1, 5), (4, 4, 2)])]
 
 
