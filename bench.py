@@ -294,12 +294,13 @@ def main():
     if args.copy_calibration:
         copy = copy_calibration(dev)
 
-    others = general = sequence = None
+    others = general = sequence = fp8 = attention = None
     if not args.no_configs:
         others = other_configs(dev, set(names), args.check_rows)
         general = general_configs(dev, args.check_rows)
         sequence = sequence_config(dev)
         fp8 = fp8_configs(dev, args.check_rows)
+        attention = attention_configs(dev)
 
     dom = max(per.values(), key=lambda r: r["avg_ms"])
     dom_w = next(w for w in ws if per[w.name] is dom)
@@ -347,6 +348,10 @@ def main():
         # back-to-back calls against the same calls replayed from a HIP graph
         "sequence": sequence,
         "fp8": fp8,
+        # the fused attention forward on the GPT's shapes, read in place from
+        # the QKV projection's output; beside it the same attention unfused
+        # (the per-head score and probability x value products above)
+        "attention": attention,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels
         "env": dict(clocks.summary(), toolchain=toolchain(g.gemm_build_info())),
@@ -716,6 +721,53 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+def attention_configs(dev):
+    """The fused attention forward on each attention workload: Q, K, V read
+    in place from a QKV projection buffer, O written token-major, timed like
+    the configurations above; the first sequence's heads checked against
+    the oracle."""
+    import dense_gemm_17_amd as g
+    from oracle import attention as att
+    out = {}
+    for name, w in workloads.ATTENTION_WORKLOADS.items():
+        qkv = workloads.make_attention_qkv(w)
+        per_copy = w.algorithmic_bytes
+        copies = 1 if per_copy * 2 > LLC_BYTES else max(2, -(-2 * LLC_BYTES // per_copy))
+        ops = []
+        for _ in range(copies):
+            qd = qkv.to(dev)
+            o = torch.empty((w.B * w.S, w.H * w.D), dtype=torch.float32, device=dev)
+            lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+            ops.append((workloads.attention_views(w, qd),
+                        o.view(w.B, w.S, w.H, w.D).permute(0, 2, 1, 3), lse))
+        state = {"i": 0}
+
+        def call():
+            (q, k, v), o, lse = ops[state["i"] % copies]
+            state["i"] += 1
+            g.attention(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse)
+
+        ms, graph_ms, clocks = time_calls(dev, call, copies)
+        Q, K, V = workloads.attention_views(w, qkv)
+        Oref, DN, _, _ = att.attention_fwd(Q[:1].numpy(), K[:1].numpy(), V[:1].numpy(),
+                                           w.causal, w.scale)
+        err, _ = att.normalized_error(ops[0][1][:1].cpu().numpy(), Oref, DN)
+        tflops = w.flops / (ms * 1e-3) / 1e12
+        out[name] = {
+            "B": w.B, "H": w.H, "S": w.S, "D": w.D, "causal": w.causal,
+            "kernel": f"attention_fwd_kernel<{w.D}>", "us_per_call": round(ms * 1e3, 2),
+            "tflops": round(tflops, 2), "bound": "mfma",
+            "frac": round(tflops / PEAK_TFLOPS["f32"], 4),
+            "gbs": round(per_copy / (ms * 1e-3) / 1e9, 1),
+            "us_per_call_graph": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+            "operand_copies": copies, "max_norm_err_first_sequence": float(f"{err:.3e}"),
+            "sclk_mhz": (clocks.summary()["sclk_mhz"] or {}).get("median"),
+        }
+        del ops
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(ws, host, seconds):

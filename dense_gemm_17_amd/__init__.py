@@ -76,6 +76,9 @@ def _load() -> ctypes.CDLL:
     lib.gemm_build_info.restype = ctypes.c_char_p
     lib.gemm_null_launch.argtypes = [vp]
     lib.gemm_null_launch.restype = ci
+    lib.attention_fwd_f32.argtypes = [i64, i64, i64, i64, ci, ctypes.c_float] + \
+        [vp, i64, i64, i64] * 4 + [vp, vp]
+    lib.attention_fwd_f32.restype = ci
     return lib
 
 
@@ -88,7 +91,7 @@ EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched"
            "gemm_fp8_f32acc_batched", "gemm_workspace_size",
            "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
            "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info",
-           "gemm_null_launch")
+           "gemm_null_launch", "attention_fwd_f32")
 
 
 # ---- raw entry points (pointers and sizes, same names as the C-ABI) --------
@@ -187,6 +190,51 @@ def gemm_build_info() -> str:
 
 def gemm_null_launch(stream) -> int:
     return lib.gemm_null_launch(stream)
+
+
+def attention_fwd_f32(B, H, S, D, causal, scale, Q, q_sb, q_sh, q_ss, K, k_sb, k_sh, k_ss,
+                      V, v_sb, v_sh, v_ss, O, o_sb, o_sh, o_ss, lse, stream) -> int:
+    return lib.attention_fwd_f32(B, H, S, D, causal, scale, Q, q_sb, q_sh, q_ss, K, k_sb, k_sh,
+                                 k_ss, V, v_sb, v_sh, v_ss, O, o_sb, o_sh, o_ss, lse, stream)
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+              scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Fused attention forward: out = softmax(scale * q k^T [causal mask]) v
+    per (sequence, head), fp32.  q, k, v and out are (B, H, S, D) float32
+    tensors on one GPU with unit stride along D (views such as slices of a
+    QKV projection buffer are read in place); scale defaults to 1/sqrt(D);
+    lse, if given, is a contiguous (B, H, S) float32 tensor that receives
+    log sum_j exp(s_ij).  Asynchronous on `stream` (default: the current
+    stream of q's device)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.float32 or t.dim() != 4 or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a 4-D float32 CUDA tensor")
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError("q, k and v must have one (B, H, S, D) shape on one GPU")
+        if t.shape[3] > 1 and t.stride(3) != 1:
+            raise ValueError(f"{name} needs unit stride along D")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    if out is None:
+        out = torch.empty((B, H, S, D), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != q.shape or out.device != q.device or \
+            (D > 1 and out.stride(3) != 1):
+        raise ValueError("out must be a float32 (B, H, S, D) tensor with unit stride along D")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (B, H, S)
+                            or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 (B, H, S) tensor on q's GPU")
+    dev = q.get_device()
+    raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
+    args = [B, H, S, D, int(bool(causal)), float(scale)]
+    for t in (q, k, v, out):
+        args += [t.data_ptr(), t.stride(0), t.stride(1), t.stride(2)]
+    args += [lse.data_ptr() if lse is not None else None, raw]
+    _launch(lib.attention_fwd_f32, "attention_fwd_f32", dev, args)
+    return out
 
 
 def kernel_id(name: str) -> int:

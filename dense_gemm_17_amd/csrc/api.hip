@@ -419,6 +419,83 @@ int run_ws(const Problem &p, void *ws, size_t ws_bytes, hipStream_t stream)
     return launch_sum_partials(q.C, S, p.M, p.N, p.C, p.ldc, stream);
 }
 
+
+// ---- fused attention: validation ---------------------------------------------
+// A (B, H, S, D) fp32 tensor with unit stride along D and non-negative
+// element strides sb, sh, ss.
+struct Tensor4 {
+    const void *p;
+    int64_t sb, sh, ss;
+};
+
+// Bytes from the base to the end of the last element, or -1 on overflow.
+int64_t tensor4_extent(const Tensor4 &t, int64_t B, int64_t H, int64_t S, int64_t D)
+{
+    const __int128 last = static_cast<__int128>(B - 1) * t.sb +
+                          static_cast<__int128>(H - 1) * t.sh +
+                          static_cast<__int128>(S - 1) * t.ss + D;
+    const __int128 bytes = last * 4;
+    if (bytes > static_cast<__int128>(INT64_MAX)) return -1;
+    return static_cast<int64_t>(bytes);
+}
+
+// Distinct (b, h, i) rows of t never share an element: with the dimensions
+// of more than one entry ordered by stride, each stride is at least the span
+// of everything inside it (the rows themselves span D).
+bool tensor4_rows_disjoint(const Tensor4 &t, int64_t B, int64_t H, int64_t S, int64_t D)
+{
+    int64_t n[3] = {B, H, S}, st[3] = {t.sb, t.sh, t.ss};
+    for (int i = 0; i < 3; ++i)
+        for (int j = i + 1; j < 3; ++j)
+            if (st[j] < st[i] || (st[j] == st[i] && n[j] < n[i])) {
+                const int64_t a = n[i], b = st[i];
+                n[i] = n[j]; st[i] = st[j]; n[j] = a; st[j] = b;
+            }
+    __int128 span = D;
+    for (int i = 0; i < 3; ++i) {
+        if (n[i] <= 1) continue;
+        if (static_cast<__int128>(st[i]) < span) return false;
+        span = static_cast<__int128>(n[i] - 1) * st[i] + span;
+    }
+    return true;
+}
+
+bool tensor4_ok(const Tensor4 &t)
+{
+    return t.p && (reinterpret_cast<uintptr_t>(t.p) & 15) == 0 && t.sb >= 0 && t.sh >= 0 &&
+           t.ss >= 0 && t.sb % 4 == 0 && t.sh % 4 == 0 && t.ss % 4 == 0;
+}
+
+int attention_validate(int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
+                       const Tensor4 &q, const Tensor4 &k, const Tensor4 &v, const Tensor4 &o,
+                       const float *lse)
+{
+    if (B < 0 || H < 0 || S < 0 || (D != 64 && D != 128) || (causal != 0 && causal != 1))
+        return kInvalid;
+    if (B > kMaxDim || H > kMaxDim || S > kMaxDim) return kInvalid;
+    if (!(scale == scale) || scale - scale != 0.f) return kInvalid;   // NaN or infinite
+    if (B == 0 || H == 0 || S == 0) return kNothing;
+    for (const Tensor4 *t : {&q, &k, &v, &o})
+        if (!tensor4_ok(*t)) return kInvalid;
+    int64_t ext[4];
+    const Tensor4 *ts[4] = {&q, &k, &v, &o};
+    for (int i = 0; i < 4; ++i)
+        if ((ext[i] = tensor4_extent(*ts[i], B, H, S, D)) < 0) return kInvalid;
+    if (!tensor4_rows_disjoint(o, B, H, S, D)) return kInvalid;
+    const uintptr_t op = reinterpret_cast<uintptr_t>(o.p);
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(op, ext[3], reinterpret_cast<uintptr_t>(ts[i]->p), ext[i])) return kInvalid;
+    if (lse) {
+        const __int128 lb = static_cast<__int128>(B) * H * S * 4;
+        if (lb > static_cast<__int128>(INT64_MAX)) return kInvalid;
+        if (reinterpret_cast<uintptr_t>(lse) & 3) return kInvalid;
+        const uintptr_t lp = reinterpret_cast<uintptr_t>(lse);
+        for (int i = 0; i < 4; ++i)
+            if (overlaps(lp, static_cast<int64_t>(lb), reinterpret_cast<uintptr_t>(ts[i]->p), ext[i]))
+                return kInvalid;
+    }
+    return kCompute;
+}
 }  // namespace
 }  // namespace mi355gemm
 
@@ -537,6 +614,26 @@ size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t
         return 0;
     Problem p{M, N, K, nullptr, 0, nullptr, 0, nullptr, 0, dtype, transa, transb, batch};
     return static_cast<size_t>(workspace_needed(p));
+}
+
+int attention_fwd_f32(int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
+                      const float *Q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                      const float *K, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                      const float *V, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                      float *O, int64_t o_sb, int64_t o_sh, int64_t o_ss, float *lse,
+                      hipStream_t stream)
+{
+    const Tensor4 q{Q, q_sb, q_sh, q_ss}, k{K, k_sb, k_sh, k_ss}, v{V, v_sb, v_sh, v_ss},
+        o{O, o_sb, o_sh, o_ss};
+    switch (attention_validate(B, H, S, D, causal, scale, q, k, v, o, lse)) {
+    case kCompute: break;
+    case kNothing: return hipSuccess;
+    default: return hipErrorInvalidValue;
+    }
+    AttnArgs a{Q, K, V, O, lse, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss,
+               o_sb, o_sh, o_ss, B, H, S, causal,
+               static_cast<float>(static_cast<double>(scale) * 1.4426950408889634), 0};
+    return launch_attention_fwd(a, D, stream);
 }
 
 int gemm_null_launch(hipStream_t stream) { return launch_null(stream); }

@@ -38,6 +38,21 @@ struct Problem {
 // True when only a general (transposed / batched) kernel can take p.
 inline bool is_general(const Problem &p) { return p.ta || p.tb || p.batch != 1; }
 
+// Arguments of the fused attention forward after validation: Q, K, V, O are
+// (B, H, S, D) with unit stride along D and element strides per sequence,
+// head and position; lse is null or B*H*S packed floats.  scale_log2 is the
+// caller's score scale times log2(e); nqb is set by the launcher.
+struct AttnArgs {
+    const float *Q, *K, *V;
+    float *O, *lse;
+    int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss, o_sb, o_sh, o_ss;
+    int64_t B, H, S;
+    int causal;
+    float scale_log2;
+    int64_t nqb;
+};
+hipError_t launch_attention_fwd(const AttnArgs &a, int64_t D, hipStream_t s);
+
 // A launcher enqueues its kernel(s) for `p` on `stream` and returns the
 // launch status.  It may assume p passed validation and its `supports` test.
 using LaunchFn = hipError_t (*)(const Problem &p, hipStream_t stream);

@@ -263,6 +263,44 @@ int gemm_force_kernel(int id);
  * (-1 before any). */
 int gemm_last_kernel(void);
 
+/* ---- fused attention forward ----------------------------------------------
+ *
+ * Scaled dot-product attention, fp32 in / fp32 out, computed the way "Bare
+ * Metal Bard" (page 1, third paragraph) describes its fused kernel: the
+ * score matrix is never written to memory; each tile of scores lives in
+ * registers and a running maximum and sum carry the softmax from one tile
+ * of keys to the next.  For every sequence b < B, head h < H and query
+ * i < S:
+ *
+ *   s_ij      = scale * sum_c Q[b,h,i,c] K[b,h,j,c]    keys j < S, and
+ *                                                       j <= i when causal
+ *   O[b,h,i,c] = sum_j exp(s_ij) V[b,h,j,c] / sum_j exp(s_ij)
+ *   lse[(b*H + h)*S + i] = log sum_j exp(s_ij)          (natural log)
+ *
+ * Layout: element (b, h, i, c) of X (Q, K, V, O) is X[b*x_sb + h*x_sh +
+ * i*x_ss + c] -- unit stride along the head dimension c < D, any
+ * non-negative element strides otherwise, so Q, K and V can be read where a
+ * QKV projection left them (one token-major (B*S) x (3*H*D) buffer:
+ * x_sb = S*3*H*D, x_sh = D, x_ss = 3*H*D, K and V at offsets H*D and 2*H*D)
+ * and O written as the next projection reads it.  D is 64 or 128; every
+ * stride is a multiple of 4 and Q, K, V, O are 16-byte aligned.  lse is
+ * either NULL or B*H*S floats, packed.  fp32 arithmetic throughout
+ * (matrix-core products, base-2 exponentials of the scaled scores).
+ *
+ * Ownership: device memory owned by the caller; the library allocates
+ * nothing, the call is asynchronous on `stream`.  Errors
+ * (hipErrorInvalidValue, nothing launched): negative sizes, D other than 64
+ * or 128, causal other than 0 or 1, a NaN or infinite scale, a null or
+ * misaligned tensor, a stride that is negative or not a multiple of 4, an O
+ * whose rows overlap each other, O or lse overlapping Q, K, V (or each
+ * other).  B, H or S zero: nothing to do, success. */
+int attention_fwd_f32(int64_t B, int64_t H, int64_t S, int64_t D, int causal, float scale,
+                      const float *Q, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                      const float *K, int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                      const float *V, int64_t v_sb, int64_t v_sh, int64_t v_ss,
+                      float *O, int64_t o_sb, int64_t o_sh, int64_t o_ss, float *lse,
+                      hipStream_t stream);
+
 /* Timing hook: enqueues one launch of a kernel that does nothing (one
  * work-group of 64 lanes) on `stream` and returns the launch status.  It is
  * the null measurement of the devpost write-up ("gpu kernels", "How we know

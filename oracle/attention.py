@@ -19,7 +19,10 @@ statistics:
 Causal masking (a key never after its query) is the reading for a GPT, a
 decoder that predicts each character from the ones before it.  Beside the
 output it returns the magnitude sum dn_ic = sum_j p_ij |v_jc|, the scale of
-the output's rounding error that the correctness gate divides by.
+the output's rounding error that the correctness gate divides by, and the
+weighted score magnitude sm_i = sum_j p_ij * |scale| * sum_c |q_ic k_jc|, the
+scale of the rounding error of the scores and so of the log-sum-exp (a
+score computed in fp32 is off by about D * 2^-24 of its magnitude sum).
 
 fp32 inputs are widened to fp64 exactly; products of two fp32 values are
 exact in fp64; numpy's fp64 matrix product serves as the inner-product step
@@ -51,8 +54,8 @@ def plant(mutant: Optional[str]) -> None:
 
 
 def _one_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float):
-    """One (sequence, head): q, k, v are S x D fp64.  Returns o, dn (S x D)
-    and lse (S)."""
+    """One (sequence, head): q, k, v are S x D fp64.  Returns o, dn (S x D),
+    lse and sm (S)."""
     S = q.shape[0]
     s = q @ k.T
     if _mutant != "NO_SCALE":
@@ -71,26 +74,41 @@ def _one_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: 
     o = p @ vv
     dn = p @ np.abs(vv)
     lse = (m + np.log(l)).reshape(-1) if axis == 1 else np.full(S, np.nan)
-    return o, dn, lse
+    sm = np.sum(p * (abs(scale) * (np.abs(q) @ np.abs(k).T)), axis=1)
+    return o, dn, lse, sm
 
 
 def attention_fwd(Q: np.ndarray, K: np.ndarray, V: np.ndarray, causal: bool,
-                  scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+                  scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
     """Q, K, V: float32 arrays of shape (B, H, S, D) (any strides).  Returns
-    (O, dn, lse) in fp64: O and dn of shape (B, H, S, D), lse (B, H, S)."""
+    (O, dn, lse, sm) in fp64: O and dn of shape (B, H, S, D), lse and sm
+    (B, H, S)."""
     if not (Q.shape == K.shape == V.shape) or Q.ndim != 4:
         raise ValueError("Q, K and V must share one (B, H, S, D) shape")
     B, H, S, D = Q.shape
     O = np.zeros((B, H, S, D))
     DN = np.zeros((B, H, S, D))
     L = np.zeros((B, H, S))
+    SM = np.zeros((B, H, S))
     sc = float(np.float32(scale))
     for b in range(B):
         for h in range(H):
-            o, dn, lse = _one_head(Q[b, h].astype(np.float64), K[b, h].astype(np.float64),
-                                   V[b, h].astype(np.float64), causal, sc)
-            O[b, h], DN[b, h], L[b, h] = o, dn, lse
-    return O, DN, L
+            o, dn, lse, sm = _one_head(Q[b, h].astype(np.float64), K[b, h].astype(np.float64),
+                                       V[b, h].astype(np.float64), causal, sc)
+            O[b, h], DN[b, h], L[b, h], SM[b, h] = o, dn, lse, sm
+    return O, DN, L, SM
+
+
+def lse_error(lse: np.ndarray, lse_ref: np.ndarray, sm: np.ndarray) -> float:
+    """max |lse - lse_ref| / max(1, sm): the log-sum-exp's error against the
+    scale of the score rounding (at least 1, the scale of the exponential's
+    and logarithm's own rounding); non-finite values fail."""
+    lse = np.asarray(lse, dtype=np.float64)
+    if lse.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(lse)):
+        return float("inf")
+    return float(np.max(np.abs(lse - lse_ref) / np.maximum(1.0, sm)))
 
 
 def normalized_error(o: np.ndarray, o_ref: np.ndarray, dn: np.ndarray):
