@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.attention_fwd_f32.argtypes = [i64, i64, i64, i64, ci, ctypes.c_float] + \
         [vp, i64, i64, i64] * 4 + [vp, vp]
     lib.attention_fwd_f32.restype = ci
+    lib.gemm_batched_noalloc.argtypes = [ci] + bsig
+    lib.gemm_batched_noalloc.restype = ci
     return lib
 
 
@@ -91,7 +93,7 @@ EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched"
            "gemm_fp8_f32acc_batched", "gemm_workspace_size",
            "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
            "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info",
-           "gemm_null_launch", "attention_fwd_f32")
+           "gemm_null_launch", "gemm_batched_noalloc", "attention_fwd_f32")
 
 
 # ---- raw entry points (pointers and sizes, same names as the C-ABI) --------
@@ -134,6 +136,12 @@ def gemm_bf16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb, 
                              ldc, stride_c, batch, stream) -> int:
     return lib.gemm_bf16_f32acc_batched(transa, transb, M, N, K, A, lda, stride_a, B, ldb,
                                         stride_b, C, ldc, stride_c, batch, stream)
+
+
+def gemm_batched_noalloc(dtype, transa, transb, M, N, K, A, lda, stride_a, B, ldb, stride_b, C,
+                         ldc, stride_c, batch, stream) -> int:
+    return lib.gemm_batched_noalloc(dtype, transa, transb, M, N, K, A, lda, stride_a, B, ldb,
+                                    stride_b, C, ldc, stride_c, batch, stream)
 
 
 def gemm_workspace_size(dtype, transa, transb, M, N, K, batch=1) -> int:

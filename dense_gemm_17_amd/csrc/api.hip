@@ -10,6 +10,7 @@
 // limits": pinned versions, no runtime autotuning).
 #include <atomic>
 #include <climits>
+#include <mutex>
 
 #include "../../include/mi355gemm.h"
 #include "gemm_internal.h"
@@ -497,6 +498,49 @@ int attention_validate(int64_t B, int64_t H, int64_t S, int64_t D, int causal, f
     return kCompute;
 }
 }  // namespace
+
+// ---- the K split without an allocation ---------------------------------------
+// Device memory for the partial products of a K split, for callers that
+// cannot allocate.  One copy per GPU, loaded with the library's code object
+// and held until the process ends.  Host code never passes this name to a
+// kernel or a copy (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = MI355GEMM_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on that device.
+hipError_t scratch_address(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return e;
+        if (sdev != dev) return hipErrorInvalidValue;   // the stream must be the current device's
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
 }  // namespace mi355gemm
 
 using namespace mi355gemm;
@@ -604,6 +648,23 @@ int gemm_fp8_f32acc_batched(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t 
     p.fa = fmt_a;
     p.fb = fmt_b;
     return run(p, stream);
+}
+
+int gemm_batched_noalloc(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda, int64_t stride_a, const void *B,
+                         int64_t ldb, int64_t stride_b, float *C, int64_t ldc, int64_t stride_c,
+                         int64_t batch, hipStream_t stream)
+{
+    if (dtype != kF32 && dtype != kBF16 && dtype != kF16) return hipErrorInvalidValue;
+    const Problem p{M, N, K, A, lda, B, ldb, C, ldc, dtype, transa, transb, batch,
+                    stride_a, stride_b, stride_c};
+    if (validate(p) != kCompute || split_count(p) <= 1) return run(p, stream);
+    if (static_cast<uint64_t>(workspace_needed(p)) > kScratchBytes)
+        return hipErrorInvalidValue;   // beyond the fixed scratch (no split needs more)
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(stream, &ws);
+    if (e != hipSuccess) return e;
+    return run_ws(p, ws, kScratchBytes, stream);
 }
 
 size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,

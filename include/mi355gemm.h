@@ -225,6 +225,36 @@ size_t gemm_workspace_size(int dtype, int transa, int transb, int64_t M, int64_t
 #define MI355GEMM_F16  2
 #define MI355GEMM_FP8  3   /* 8-bit floats; gemm_plan_batched needs transa 0, transb 1 */
 
+/* ---- the K split without an allocation -------------------------------------
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * gemm_f32_batched_ws / gemm_bf16_f32acc_batched_ws / gemm_f16_f32acc_batched_ws
+ * (dtype MI355GEMM_F32 / _BF16 / _F16 selects which; A and B are fp32 or raw
+ * 16-bit patterns; same layout, results and errors) with the workspace taken
+ * from a fixed device array inside the library instead of the caller:
+ * MI355GEMM_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, loaded with the
+ * library's code and held until the process ends.  Its device address is
+ * looked up once per device on the first call that splits K there.  No call
+ * allocates or frees memory.  Every split needs at most 511 tiles of
+ * 128 x 128 fp32 partials (< 32 MiB); a call that would need more returns
+ * hipErrorInvalidValue and launches nothing.  Calls that split nothing do
+ * not touch the array.
+ *
+ * The array is shared by every call on one GPU and keeps the last call's
+ * partial products: calls that overlap in time on one GPU (different
+ * streams, or host threads without ordering) race and give undefined
+ * results; order them on one stream.  Nothing in it needs to start at zero
+ * (each partial product is written whole before it is summed).  `stream`
+ * must belong to the current device (hipErrorInvalidValue otherwise). */
+#define MI355GEMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int gemm_batched_noalloc(int dtype, int transa, int transb, int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda, int64_t stride_a,
+                         const void *B, int64_t ldb, int64_t stride_b,
+                         float *C, int64_t ldc, int64_t stride_c,
+                         int64_t batch, hipStream_t stream);
+
 /* Number of kernels in the library; ids are 0 .. count-1. */
 int gemm_kernel_count(void);
 
