@@ -165,13 +165,36 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
         const int64_t k0 = t * BN;
         if (k0 < wend) {
             // 1. scores, transposed: s[sb] holds keys k0 + 32 sb + (8 (r/4) + 4 h + r%4)
-            //    for query c of this wave
+            //    for query c of this wave.  The 32-key halves the wave sees
+            //    (both but on its diagonal tile) run as independent MFMA
+            //    chains, interleaved.
             f32x16 s[BN / 32];
 #pragma unroll
-            for (int sb = 0; sb < BN / 32; ++sb) {
+            for (int sb = 0; sb < BN / 32; ++sb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-                if (k0 + 32 * sb < wend) {
+            const bool all_halves = k0 + BN <= wend;
+#pragma unroll
+            for (int u = 0; u < C::DH / 4; ++u) {
+                f32x4 kv[BN / 32];
+#pragma unroll
+                for (int sb = 0; sb < BN / 32; ++sb)
+                    if (sb == 0 || all_halves)
+                        kv[sb] = *reinterpret_cast<const f32x4 *>(Ks + (32 * sb + c) * C::KS +
+                                                                  h * C::DH + 4 * u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int sb = 0; sb < BN / 32; ++sb)
+                        if (sb == 0 || all_halves)
+                            s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[sb][e], qf[4 * u + e],
+                                                                          s[sb], 0, 0, 0);
+            }
+            if (!all_halves) {
+                // the diagonal tile's later halves, each only if the wave sees it
+#pragma unroll
+                for (int sb = 1; sb < BN / 32; ++sb) {
+                    if (k0 + 32 * sb >= wend) break;
                     const float *krow = Ks + (32 * sb + c) * C::KS + h * C::DH;
 #pragma unroll
                     for (int u = 0; u < C::DH / 4; ++u) {
@@ -183,18 +206,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
                     }
                 }
             }
-            // 2. mask, scale, running maximum and sum
+            // 2. mask (only where a key can be past the sequence or after a
+            //    query of this wave), scale, running maximum and sum
             float mx = neg_inf();
+            const bool masked = k0 + BN > S || (a.causal && k0 + BN - 1 > qw);
+            if (masked) {
+                const int kl = static_cast<int>(k0) + 4 * h;   // keys and queries fit in 32 bits
+                const int lim = a.causal ? (qi < S ? static_cast<int>(qi) : static_cast<int>(S) - 1)
+                                         : static_cast<int>(S) - 1;
 #pragma unroll
-            for (int sb = 0; sb < BN / 32; ++sb)
+                for (int sb = 0; sb < BN / 32; ++sb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t key = k0 + 32 * sb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool vis = key < S && (!a.causal || key <= qi);
-                    const float x = vis ? s[sb][r] * sl2 : neg_inf();
-                    s[sb][r] = x;
-                    mx = fmaxf(mx, x);
-                }
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kl + 32 * sb + 8 * (r >> 2) + (r & 3);
+                        const float x = key <= lim ? s[sb][r] * sl2 : neg_inf();
+                        s[sb][r] = x;
+                        mx = fmaxf(mx, x);
+                    }
+            } else {
+#pragma unroll
+                for (int sb = 0; sb < BN / 32; ++sb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float x = s[sb][r] * sl2;
+                        s[sb][r] = x;
+                        mx = fmaxf(mx, x);
+                    }
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
             const float m_new = fmaxf(m, mx);
             const float m_use = m_new == neg_inf() ? 0.f : m_new;
