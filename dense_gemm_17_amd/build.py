@@ -74,6 +74,47 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C-ABI layer (argument validation, extents,
+# overlap and dispatch arithmetic): only api.hip's host code is
+# instrumented; device code is built as usual.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-shared-libsan",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized_host(out: str) -> str:
+    """Link a copy of the library whose api.hip host code is built with
+    AddressSanitizer and UndefinedBehaviorSanitizer, from the objects of the
+    last build() for the other sources.  Load it with the ASan runtime
+    preloaded (``asan_runtime()``) and MI355GEMM_LIBRARY pointing at it."""
+    san_dir = os.path.join(BUILD, "san")
+    os.makedirs(san_dir, exist_ok=True)
+    api = os.path.join(CSRC, "api.hip")
+    obj = os.path.join(san_dir, "api.o")
+    r = subprocess.run([HIPCC, *HIP_FLAGS, *SAN_FLAGS, "-c", api, "-o", obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {api}:\n{r.stderr}")
+    others = [os.path.join(BUILD, os.path.basename(src)[:-4] + ".o") for src in sources()
+              if os.path.basename(src) != "api.hip"]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise FileNotFoundError(f"build() first: missing {missing}")
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, obj,
+                        *others, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
+def asan_runtime() -> str:
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
     build(verbose=True)
     sys.exit(0)
