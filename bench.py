@@ -294,13 +294,14 @@ def main():
     if args.copy_calibration:
         copy = copy_calibration(dev)
 
-    others = general = sequence = fp8 = attention = None
+    others = general = sequence = fp8 = attention = mx = None
     if not args.no_configs:
         others = other_configs(dev, set(names), args.check_rows)
         general = general_configs(dev, args.check_rows)
         sequence = sequence_config(dev)
         fp8 = fp8_configs(dev, args.check_rows)
         attention = attention_configs(dev)
+        mx = mx_configs(dev)
 
     dom = max(per.values(), key=lambda r: r["avg_ms"])
     dom_w = next(w for w in ws if per[w.name] is dom)
@@ -344,14 +345,18 @@ def main():
         # the same for products with a transposed factor or a batch (the GPT
         # backward pass and attention shapes)
         "general_configs": general,
-        # a launch-bound sequence (one GPT forward pass over 256 tokens):
-        # back-to-back calls against the same calls replayed from a HIP graph
+        # a launch-bound sequence (one GPT forward pass over 256 tokens, with
+        # the attention unfused and fused): back-to-back calls against the
+        # same calls replayed from a HIP graph, every output checked
         "sequence": sequence,
         "fp8": fp8,
         # the fused attention forward on the GPT's shapes, read in place from
         # the QKV projection's output; beside it the same attention unfused
         # (the per-head score and probability x value products above)
         "attention": attention,
+        # 8-bit products with MX block scales (one E8M0 scale per 32 elements
+        # of K of each row of A and of Bt)
+        "mx_fp8": mx,
         # GPU core clock and board power sampled over the timed steps, and
         # the toolchain that built the kernels
         "env": dict(clocks.summary(), toolchain=toolchain(g.gemm_build_info())),
@@ -467,25 +472,84 @@ def time_calls(dev, call, copies):
 
 
 def sequence_config(dev, windows: int = 5, reps: int = 20):
-    """The 37 products of one GPT forward pass over 256 tokens (fp32),
+    """One GPT forward pass over a single sequence of 256 tokens (fp32), the
+    launch-bound regime: as 37 library calls with the attention unfused
+    (per-head score and probability x value products) and as 31 with the
+    fused attention reading the QKV projection's output in place.  Each is
     timed as back-to-back calls through the binding and as the same calls
-    captured once into a HIP graph and replayed; the graph's outputs are
-    checked bit for bit against the eager ones."""
+    captured once into a HIP graph and replayed; after a replay every
+    product (and attention) output is checked against the oracle on the
+    inputs it read."""
     import dense_gemm_17_amd as g
-    seq = workloads.gpt_forward_sequence()
+    import oracle
+    from oracle import attention as att
     gen = workloads.generator()
-    calls = []
-    for (name, nb, M, N, K, ta, tb) in seq:
-        lead = (nb,) if nb > 1 else ()
-        A = workloads.draw(lead + ((K, M) if ta else (M, K)), ("normal", 1.0), gen).to(dev)
-        B = workloads.draw(lead + ((N, K) if tb else (K, N)), ("normal", 1.0), gen).to(dev)
-        C = torch.empty(lead + (M, N), dtype=torch.float32, device=dev)
-        calls.append((A.transpose(-1, -2) if ta else A, B.transpose(-1, -2) if tb else B, C))
-    flops = sum(2 * nb * M * N * K for (_, nb, M, N, K, _, _) in seq)
+    heads, dh, T = 6, 64, 256
 
-    def run_all():
-        for a, b, c in calls:
-            g.gemm(a, b, out=c)
+    def operand(shape, sigma):
+        return workloads.draw(shape, ("normal", sigma), gen).to(dev)
+
+    def build(fused):
+        ops = []     # ("gemm", a, b, c) or ("attn", qkv, o)
+        for (name, nb, M, N, K, ta, tb) in workloads.gpt_forward_sequence():
+            kind = name.split("_", 1)[1]
+            if fused and kind == "pv":
+                continue
+            if fused and kind == "scores":
+                qkv = ops[-1][3]                            # this layer's QKV output
+                o = torch.empty((T, heads * dh), dtype=torch.float32, device=dev)
+                ops.append(("attn", qkv, o))
+                continue
+            lead = (nb,) if nb > 1 else ()
+            w = 0.02 if kind in ("qkv", "proj", "mlp_up", "mlp_down", "head") else 1.0
+            A = operand(lead + ((K, M) if ta else (M, K)), 1.0)
+            B = operand(lead + ((N, K) if tb else (K, N)), w)
+            C = torch.empty(lead + (M, N), dtype=torch.float32, device=dev)
+            ops.append(("gemm", A.transpose(-1, -2) if ta else A,
+                        B.transpose(-1, -2) if tb else B, C))
+        return ops
+
+    def qkv_views(qkv):
+        t = qkv.view(1, T, 3, heads, dh)
+        return tuple(t[:, :, i].permute(0, 2, 1, 3) for i in range(3))
+
+    def run(ops):
+        for op in ops:
+            if op[0] == "gemm":
+                g.gemm(op[1], op[2], out=op[3])
+            else:
+                q, k, v = qkv_views(op[1])
+                g.attention(q, k, v, causal=True, scale=dh ** -0.5,
+                            out=op[2].view(1, T, heads, dh).permute(0, 2, 1, 3))
+
+    def flops(ops):
+        f = 0
+        for op in ops:
+            if op[0] == "gemm":
+                a, b = op[1], op[2]
+                nb = a.shape[0] if a.dim() == 3 else 1
+                f += 2 * nb * a.shape[-2] * a.shape[-1] * b.shape[-1]
+            else:
+                f += 4 * heads * (T * (T + 1) // 2) * dh
+        return f
+
+    def check(ops):
+        worst = 0.0
+        for op in ops:
+            if op[0] == "gemm":
+                a, b, c = op[1].cpu(), op[2].cpu(), op[3].cpu()
+                if a.dim() == 2:
+                    a, b, c = a[None], b[None], c[None]
+                for i in range(a.shape[0]):
+                    Cref, D = oracle.gemm_f32(np.ascontiguousarray(a[i].numpy()),
+                                              np.ascontiguousarray(b[i].numpy()))
+                    worst = max(worst, oracle.normalized_error(c[i].numpy(), Cref, D)[0])
+            else:
+                q, k, v = (x.cpu().numpy() for x in qkv_views(op[1]))
+                Oref, DN, _, _ = att.attention_fwd(q, k, v, True, dh ** -0.5)
+                o = op[2].cpu().view(1, T, heads, dh).permute(0, 2, 1, 3).numpy()
+                worst = max(worst, att.normalized_error(o, Oref, DN)[0])
+        return worst
 
     st = torch.cuda.Stream(dev)
     st.wait_stream(torch.cuda.current_stream(dev))
@@ -502,30 +566,32 @@ def sequence_config(dev, windows: int = 5, reps: int = 20):
             ts.append(e0.elapsed_time(e1) / reps)
         return float(np.median(ts))
 
-    with torch.cuda.stream(st):
-        for _ in range(3):
-            run_all()
-        torch.cuda.synchronize()
-        eager_ms = timed(run_all)
-        eager_out = [c.clone() for (_, _, c) in calls]
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=st):
-            run_all()
-        for (_, _, c) in calls:
-            c.fill_(float("nan"))
-        graph.replay()
-        torch.cuda.synchronize()
-        same = all(torch.equal(c, e) for (_, _, c), e in zip(calls, eager_out))
-        graph_ms = timed(graph.replay)
-        del graph
-    kernels = sorted({g.gemm_kernel_name(g.gemm_last_kernel())})
-    return {"calls": len(seq), "gflop": round(flops / 1e9, 3),
-            "eager_us": round(eager_ms * 1e3, 1), "graph_us": round(graph_ms * 1e3, 1),
-            "eager_tflops": round(flops / (eager_ms * 1e-3) / 1e12, 2),
-            "graph_tflops": round(flops / (graph_ms * 1e-3) / 1e12, 2),
-            "eager_us_per_call": round(eager_ms * 1e3 / len(seq), 2),
-            "graph_us_per_call": round(graph_ms * 1e3 / len(seq), 2),
-            "graph_equals_eager": same, "last_kernel": kernels[0]}
+    out = {}
+    for label, fused in (("unfused_attention", False), ("fused_attention", True)):
+        ops = build(fused)
+        with torch.cuda.stream(st):
+            for _ in range(3):
+                run(ops)
+            torch.cuda.synchronize()
+            eager_ms = timed(lambda: run(ops))
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=st):
+                run(ops)
+            for op in ops:
+                op[-1].fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            err = check(ops)
+            graph_ms = timed(graph.replay)
+            del graph
+        f = flops(ops)
+        out[label] = {"calls": len(ops), "gflop": round(f / 1e9, 3),
+                      "eager_us": round(eager_ms * 1e3, 1), "graph_us": round(graph_ms * 1e3, 1),
+                      "eager_us_per_call": round(eager_ms * 1e3 / len(ops), 2),
+                      "graph_us_per_call": round(graph_ms * 1e3 / len(ops), 2),
+                      "graph_tflops": round(f / (graph_ms * 1e-3) / 1e12, 2),
+                      "max_norm_err_every_output": float(f"{err:.3e}")}
+    return out
 
 
 def general_configs(dev, check_rows):
@@ -721,6 +787,59 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+MX_WORKLOADS = {"mx_e4m3_8192": (8192, 8192, 8192), "mx_gpt_qkv": (16384, 1152, 384),
+                "mx_skinny_4x8192x8192": (4, 8192, 8192)}
+
+
+def mx_configs(dev, check_rows=4):
+    """8-bit e4m3 products with MX block scales drawn in [2^-7, 2^7]: the
+    table's kernel timed like the configurations above, sampled rows checked
+    against the oracle."""
+    import dense_gemm_17_amd as g
+    import oracle
+    out = {}
+    rng = np.random.default_rng(5)
+    for name, (M, N, K) in MX_WORKLOADS.items():
+        gen = workloads.generator()
+        A = workloads.draw((M, K), ("normal", 1.0), gen).to(torch.float8_e4m3fn)
+        Bt = workloads.draw((N, K), ("normal", 1.0), gen).to(torch.float8_e4m3fn)
+        SA = torch.randint(120, 135, (K // 32, -(-M // 4) * 4), generator=gen).to(torch.uint8)
+        SB = torch.randint(120, 135, (K // 32, -(-N // 4) * 4), generator=gen).to(torch.uint8)
+        per_copy = M * K + N * K + 4 * M * N + (K // 32) * (M + N)
+        copies = 1 if per_copy * 2 > LLC_BYTES else max(2, -(-2 * LLC_BYTES // per_copy))
+        ops = [(A.to(dev), SA.to(dev), Bt.to(dev).t(), SB.to(dev),
+                torch.empty((M, N), dtype=torch.float32, device=dev)) for _ in range(copies)]
+        state = {"i": 0}
+
+        def call():
+            a, sa, b, sb, c = ops[state["i"] % copies]
+            state["i"] += 1
+            g.gemm_mx(a, sa, b, sb, out=c)
+
+        ms, graph_ms, clocks = time_calls(dev, call, copies)
+        kernel = g.gemm_kernel_name(g.gemm_last_kernel())
+        rows = sorted(set([0, M - 1] + rng.choice(M, size=min(M, check_rows), replace=False).tolist()))
+        Cref, D = oracle.gemm_mxfp8(workloads.fp8_bits(A[rows]), SA[:, rows].numpy(),
+                                    workloads.fp8_bits(Bt), SB.numpy(), 0, 0, threads=cpu_threads())
+        err, _, _ = oracle.normalized_error(ops[0][4][rows].cpu().numpy(), Cref, D)
+        flops = 2 * M * N * K
+        tflops = flops / (ms * 1e-3) / 1e12
+        gbs = per_copy / (ms * 1e-3) / 1e9
+        hbm = flops / per_copy < PEAK_TFLOPS["fp8"] * 1e3 / HBM_PEAK_GBS
+        out[name] = {
+            "M": M, "N": N, "K": K, "formats": "e4m3xe4m3, E8M0 scales per 32", "kernel": kernel,
+            "us_per_call": round(ms * 1e3, 2), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+            "bound": "hbm" if hbm else "mfma",
+            "frac": round(gbs / HBM_PEAK_GBS if hbm else tflops / PEAK_TFLOPS["fp8"], 4),
+            "us_per_call_graph": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+            "operand_copies": copies, "max_norm_err_sampled": float(f"{err:.3e}"),
+            "sclk_mhz": (clocks.summary()["sclk_mhz"] or {}).get("median"),
+        }
+        del ops
+        torch.cuda.empty_cache()
+    return out
 
 
 def attention_configs(dev):

@@ -14,7 +14,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmi355gemm.so")
+# MI355GEMM_LIBRARY names another build of the same library (the host
+# sanitizer build the CPU tests load); by default the in-tree one.
+LIB_PATH = os.environ.get("MI355GEMM_LIBRARY") or os.path.join(_HERE, "libmi355gemm.so")
 
 F32 = 0
 BF16 = 1
@@ -76,6 +78,11 @@ def _load() -> ctypes.CDLL:
     lib.gemm_build_info.restype = ctypes.c_char_p
     lib.gemm_null_launch.argtypes = [vp]
     lib.gemm_null_launch.restype = ci
+    lib.gemm_mxfp8_f32acc.argtypes = [ci, ci, i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                                      vp, i64, vp]
+    lib.gemm_mxfp8_f32acc.restype = ci
+    lib.gemm_plan_mxfp8.argtypes = [i64, i64, i64, sz, i64, sz, i64, sz, i64, sz, i64, sz, i64]
+    lib.gemm_plan_mxfp8.restype = ci
     lib.attention_fwd_f32.argtypes = [i64, i64, i64, i64, ci, ctypes.c_float] + \
         [vp, i64, i64, i64] * 4 + [vp, vp]
     lib.attention_fwd_f32.restype = ci
@@ -93,7 +100,8 @@ EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched"
            "gemm_fp8_f32acc_batched", "gemm_workspace_size",
            "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
            "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info",
-           "gemm_null_launch", "gemm_batched_noalloc", "attention_fwd_f32")
+           "gemm_null_launch", "gemm_batched_noalloc", "attention_fwd_f32",
+           "gemm_mxfp8_f32acc", "gemm_plan_mxfp8")
 
 
 # ---- raw entry points (pointers and sizes, same names as the C-ABI) --------
@@ -198,6 +206,58 @@ def gemm_build_info() -> str:
 
 def gemm_null_launch(stream) -> int:
     return lib.gemm_null_launch(stream)
+
+
+def gemm_mxfp8_f32acc(fmt_a, fmt_b, M, N, K, A, lda, scale_a, ld_scale_a, Bt, ldb, scale_b,
+                      ld_scale_b, C, ldc, stream) -> int:
+    return lib.gemm_mxfp8_f32acc(fmt_a, fmt_b, M, N, K, A, lda, scale_a, ld_scale_a, Bt, ldb,
+                                 scale_b, ld_scale_b, C, ldc, stream)
+
+
+def gemm_plan_mxfp8(M, N, K, A, lda, scale_a, ld_scale_a, Bt, ldb, scale_b, ld_scale_b, C,
+                    ldc) -> int:
+    return lib.gemm_plan_mxfp8(M, N, K, A, lda, scale_a, ld_scale_a, Bt, ldb, scale_b,
+                               ld_scale_b, C, ldc)
+
+
+def gemm_mx(a: torch.Tensor, scale_a: torch.Tensor, b: torch.Tensor, scale_b: torch.Tensor,
+            out: Optional[torch.Tensor] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """out = (a with its MX block scales) @ (b with its MX block scales), fp32.
+
+    a is an (M, K) 8-bit float tensor (e4m3 or e5m2) with unit stride along
+    K; b is (K, N), the transposed view of a row-major (N, K) 8-bit tensor
+    (``w.t()``).  scale_a is a uint8 (K/32, M') tensor, M' >= M, holding the
+    E8M0 scale of block kb of row i at scale_a[kb, i]; scale_b likewise
+    (K/32, N') for the rows of b's storage.  Rows of the scale tensors may be
+    padded; their pitch (the width for a single row) is a multiple of 4."""
+    if a.dtype not in FP8_FORMAT or b.dtype not in FP8_FORMAT:
+        raise TypeError("operands must be float8_e4m3fn or float8_e5m2")
+    if scale_a.dtype != torch.uint8 or scale_b.dtype != torch.uint8:
+        raise TypeError("scales must be uint8 E8M0 patterns")
+    M, K = a.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {tuple(a.shape)} @ {tuple(b.shape)}")
+    if (K > 1 and (a.stride(1) != 1 or b.stride(0) != 1)):
+        raise ValueError("a needs unit stride along K and b must be a transposed row-major tensor")
+    for t, n in ((scale_a, M), (scale_b, N)):
+        if t.dim() != 2 or t.shape[0] != K // 32 or t.shape[1] < n or \
+                (t.shape[1] > 1 and t.stride(1) != 1) or t.device != a.device:
+            raise ValueError("scales must be (K/32, >= rows) uint8 tensors with unit column stride")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    dev = a.get_device()
+    raw = stream.cuda_stream if stream is not None else _current_raw_stream(dev)
+    lda = a.stride(0) if M > 1 else max(K, 16)
+    ldb = b.stride(1) if N > 1 else max(K, 16)
+    lsa = scale_a.stride(0) if scale_a.shape[0] > 1 else scale_a.shape[1]
+    lsb = scale_b.stride(0) if scale_b.shape[0] > 1 else scale_b.shape[1]
+    _launch(lib.gemm_mxfp8_f32acc, "gemm_mxfp8_f32acc", dev,
+            (FP8_FORMAT[a.dtype], FP8_FORMAT[b.dtype], M, N, K, a.data_ptr(), lda,
+             scale_a.data_ptr(), lsa, b.data_ptr(), ldb, scale_b.data_ptr(), lsb, out.data_ptr(),
+             _ld(out), raw))
+    return out
 
 
 def attention_fwd_f32(B, H, S, D, causal, scale, Q, q_sb, q_sh, q_ss, K, k_sb, k_sh, k_ss,

@@ -56,7 +56,7 @@ const KernelInfo kKernels[] = {
     {"mfma_f16_batched128", kF16, launch_mfma_f16_batched128, supports_any, true},
     {"mfma_f16_batched_splitk", kF16, launch_mfma_f16_batched_splitk, supports_any, true},
     {"mfma_fp8_direct128", kFp8, launch_mfma_fp8_direct128, supports_mfma_fp8_direct, true},
-    {"mfma_fp8_batched", kFp8, launch_mfma_fp8_batched, supports_fp8, true},
+    {"mfma_fp8_batched", kFp8, launch_mfma_fp8_batched, supports_fp8_unscaled, true},
     {"mfma_fp8_batched128", kFp8, launch_mfma_fp8_batched128, supports_fp8, true},
     {"mfma_fp8_direct256x128", kFp8, launch_mfma_fp8_direct256x128, supports_mfma_fp8_direct, true},
     {"skinny_fp8", kFp8, launch_skinny_fp8, supports_skinny_fp8, true},
@@ -149,6 +149,19 @@ Verdict validate(const Problem &p)
     const int64_t bbytes = batch_extent(extent_bytes(b_rows, b_cols, p.ldb, es), p.batch, p.sb, es);
     if (abytes < 0 || bbytes < 0) return kInvalid;
     if (overlaps(c, cbytes, a, abytes) || overlaps(c, cbytes, b, bbytes)) return kInvalid;
+    if (p.xa || p.xb) {
+        // MX block scales: one product, K whole 32-element blocks, scale
+        // arrays of K/32 rows of ldxa (ldxb) bytes, rows a multiple of 4
+        // bytes and the arrays 4-byte aligned, not under C
+        if (p.dtype != kFp8 || p.batch != 1 || !p.xa || !p.xb || p.K % 32 != 0) return kInvalid;
+        if (p.ldxa < p.M || p.ldxb < p.N || p.ldxa % 4 != 0 || p.ldxb % 4 != 0) return kInvalid;
+        const uintptr_t xa = reinterpret_cast<uintptr_t>(p.xa), xb = reinterpret_cast<uintptr_t>(p.xb);
+        if (xa % 4 != 0 || xb % 4 != 0) return kInvalid;
+        const int64_t xab = extent_bytes(p.K / 32, p.ldxa, p.ldxa, 1);
+        const int64_t xbb = extent_bytes(p.K / 32, p.ldxb, p.ldxb, 1);
+        if (xab < 0 || xbb < 0) return kInvalid;
+        if (overlaps(c, cbytes, xa, xab) || overlaps(c, cbytes, xb, xbb)) return kInvalid;
+    }
     return kCompute;
 }
 
@@ -211,14 +224,18 @@ int select_f32_lds(const Problem &p);
 
 int select_general(const Problem &p)
 {
-    // fp32 with fewer 128 x 128 tiles over all products than CUs (weight
-    // gradients: a small output summed over a long K): the split-K kernel,
-    // whose 32 x 32 tiles and four-way K split occupy every CU (GPT QKV
-    // weight gradient 384 x 1152 x 16384: 49 vs 9.8 TFLOP/s).  Its bf16
-    // twin is kept for the test hook only: with a transposed factor its
-    // lanes need eight 2-byte loads per operand per MFMA and it loses to
-    // the 128 x 128 tile (23 vs 63 TFLOP/s on the same shape).
-    if (p.dtype == kF32 && ceil_div(p.M, 128) * ceil_div(p.N, 128) * p.batch < kCUs)
+    // fp32 with fewer 128 x 128 tiles over all products than CUs and a K of
+    // at least 256 (weight gradients: a small output summed over a long K;
+    // per-head probabilities x values): the split-K kernel, whose 32 x 32
+    // tiles and four-way K split occupy every CU (GPT QKV weight gradient
+    // 384 x 1152 x 16384: 49 vs 9.8 TFLOP/s; 6 x 256 x 64 x 256: 5.1 vs 7.6
+    // us for the 64 x 64 tile).  With a short K there is nothing to split
+    // and the 64 x 64 LDS-direct tile wins (6 heads of 256 x 256 x 64
+    // scores: 4.1 vs 7.4 us).  The bf16 twin is kept for the test hook only:
+    // with a transposed factor its lanes need eight 2-byte loads per operand
+    // per MFMA and it loses to the 128 x 128 tile (23 vs 63 TFLOP/s on the
+    // same shape).
+    if (p.dtype == kF32 && p.K >= 256 && ceil_div(p.M, 128) * ceil_div(p.N, 128) * p.batch < kCUs)
         return kernel_id("mfma_f32_batched_splitk");
     // fp32 layouts the LDS-direct tiles take (16-byte aligned rows, K % 16
     // == 0; untransposed factors also through the narrow-load tiles).
@@ -251,7 +268,8 @@ int select_general(const Problem &p)
                    ? kernel_id("mfma_fp8_direct256x128")
                    : kernel_id("mfma_fp8_direct128");
     if (p.dtype == kFp8)
-        return tiled_cost(p, 256, 256, 1, FP8_BATCHED_256) <= tiled_cost(p, 128, 128, 2, FP8_BATCHED_128)
+        return !p.xa && tiled_cost(p, 256, 256, 1, FP8_BATCHED_256) <=
+                            tiled_cost(p, 128, 128, 2, FP8_BATCHED_128)
                    ? kernel_id("mfma_fp8_batched")
                    : kernel_id("mfma_fp8_batched128");
     if (p.dtype == kF16 && supports_mfma_bf16_direct(p))
@@ -639,6 +657,26 @@ int gemm_fp8_f32acc(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const
     return run(p, stream);
 }
 
+int gemm_mxfp8_f32acc(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K, const uint8_t *A,
+                      int64_t lda, const uint8_t *scale_a, int64_t ld_scale_a, const uint8_t *Bt,
+                      int64_t ldb, const uint8_t *scale_b, int64_t ld_scale_b, float *C,
+                      int64_t ldc, hipStream_t stream)
+{
+    Problem p{M, N, K, A, lda, Bt, ldb, C, ldc, kFp8, 0, 1};
+    p.fa = fmt_a;
+    p.fb = fmt_b;
+    p.xa = scale_a;
+    p.xb = scale_b;
+    p.ldxa = ld_scale_a;
+    p.ldxb = ld_scale_b;
+    // the scale pointers are checked even where nothing is computed
+    if (!scale_a || !scale_b || ld_scale_a < 0 || ld_scale_b < 0) {
+        if (M > 0 && N > 0 && K > 0) return hipErrorInvalidValue;
+    }
+    if (K % 32 != 0) return hipErrorInvalidValue;
+    return run(p, stream);
+}
+
 int gemm_fp8_f32acc_batched(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
                             const uint8_t *A, int64_t lda, int64_t stride_a, const uint8_t *Bt,
                             int64_t ldb, int64_t stride_b, float *C, int64_t ldc,
@@ -735,6 +773,20 @@ int gemm_plan(int dtype, int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t l
     const Problem p{M, N, K, reinterpret_cast<const void *>(A), lda,
                     reinterpret_cast<const void *>(B), ldb, reinterpret_cast<float *>(C), ldc,
                     dtype};
+    return plan(p);
+}
+
+int gemm_plan_mxfp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda, uintptr_t scale_a,
+                    int64_t ld_scale_a, uintptr_t Bt, int64_t ldb, uintptr_t scale_b,
+                    int64_t ld_scale_b, uintptr_t C, int64_t ldc)
+{
+    Problem p{M, N, K, reinterpret_cast<const void *>(A), lda, reinterpret_cast<const void *>(Bt),
+              ldb, reinterpret_cast<float *>(C), ldc, kFp8, 0, 1};
+    p.xa = reinterpret_cast<const uint8_t *>(scale_a);
+    p.xb = reinterpret_cast<const uint8_t *>(scale_b);
+    p.ldxa = ld_scale_a;
+    p.ldxb = ld_scale_b;
+    if (K % 32 != 0) return -1;
     return plan(p);
 }
 

@@ -24,6 +24,9 @@ struct F16Bits {
 // as general read these fields.  8-bit float operands (dtype kFp8) come as
 // A as written and B transposed only (ta = 0, tb = 1), with fa and fb the
 // formats of A and B (0 e4m3, 1 e5m2); their sizes and strides are bytes.
+// xa / xb, when not null, are MX block scales of such a product (one E8M0
+// byte per 32 elements of K: block kb of row i of A at xa[kb * ldxa + i],
+// of row j of Bt at xb[kb * ldxb + j]); a single product only.
 struct Problem {
     int64_t M, N, K;
     const void *A; int64_t lda;
@@ -33,6 +36,8 @@ struct Problem {
     int ta = 0, tb = 0;
     int64_t batch = 1, sa = 0, sb = 0, sc = 0;
     int fa = 0, fb = 0;
+    const uint8_t *xa = nullptr, *xb = nullptr;
+    int64_t ldxa = 0, ldxb = 0;
 };
 
 // True when only a general (transposed / batched) kernel can take p.
@@ -118,6 +123,8 @@ inline bool supports_fp8(const Problem &p)
            (p.fb == 0 || p.fb == 1) && p.K % 16 == 0 && p.lda % 16 == 0 && p.ldb % 16 == 0 &&
            p.sa % 16 == 0 && p.sb % 16 == 0 && al(p.A) && al(p.B);
 }
+// The 256 x 256 register-staged 8-bit tile takes no MX scales.
+inline bool supports_fp8_unscaled(const Problem &p) { return supports_fp8(p) && !p.xa; }
 hipError_t launch_naive_f16(const Problem &p, hipStream_t s);
 hipError_t launch_sum_partials(const float *W, int64_t S, int64_t M, int64_t N, float *C,
                                int64_t ldc, hipStream_t s);

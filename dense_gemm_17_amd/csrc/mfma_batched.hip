@@ -68,13 +68,17 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // fa, fb the formats of A and B (0 e4m3, 1 e5m2).
 constexpr int kFp8Op = 2;
 
-// One 32 x 32 x 64 MFMA on 8-bit floats with unit block scales (the E8M0
-// scale 127 is 2^0).  Each operand is the lane's 32 bytes of K: the two
-// 16-byte halves given.  A and B take the same bytes of K from their halves,
-// so every k meets its partner whichever k the hardware assigns to them.
+// One 32 x 32 x 64 MFMA on 8-bit floats; sa and sb are lane (b, c)'s E8M0
+// scales of block b (of 32 elements of K) of row c of A and of B (127 is
+// 2^0).  Each operand is the lane's 32 bytes of K: the two 16-byte halves
+// given, which the instruction takes as K positions 16 h .. 16 h + 15 and
+// 32 + 16 h .. 47 + 16 h of its 64 (block 0 is the first half of both
+// half-waves, block 1 the second).  A and B take the same bytes of K from
+// their halves, so every k meets its partner.
 template <int kOp>
 __device__ __forceinline__ f32x16 mfma8(const bf16x8 &a0, const bf16x8 &a1, const bf16x8 &b0,
-                                        const bf16x8 &b1, const f32x16 &c)
+                                        const bf16x8 &b1, const f32x16 &c, int sa = 127,
+                                        int sb = 127)
 {
     constexpr int fa = (kOp - kFp8Op) >> 1, fb = (kOp - kFp8Op) & 1;
     const i32x8 a = __builtin_bit_cast(
@@ -83,7 +87,7 @@ __device__ __forceinline__ f32x16 mfma8(const bf16x8 &a0, const bf16x8 &a1, cons
     const i32x8 b = __builtin_bit_cast(
         i32x8, __builtin_shufflevector(__builtin_bit_cast(u16x8, b0), __builtin_bit_cast(u16x8, b1),
                                        0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15));
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fa, fb, 0, 127, 0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fa, fb, 0, sa, 0, sb);
 }
 
 constexpr int kThreads = 256;
@@ -461,13 +465,21 @@ __device__ __forceinline__ bf16x8 fragment(const uint16_t *Xs, int base, int s, 
 // kOp: bf16 (0), fp16 (1) or 8-bit floats (kFp8Op and up; A as written and
 // B transposed only, every dimension and leading dimension in 16-bit slots,
 // i.e. halved).  An 8-bit K tile is 128 bytes: two 64-byte MFMA steps, each
-// made of the lane's 16-byte reads of slices 2t and 2t + 1.
-template <int BM, int BN, bool TA, bool TB, bool kVec, int kOp>
+// made of the lane's 16-byte reads of slices 2t and 2t + 1 (bytes 16 h ..
+// 16 h + 15 and 32 + 16 h .. 47 + 16 h of the step, the instruction's own
+// K positions).  kMX (8-bit only, a single product): MX block scales, the
+// scale of 32-byte block kb of row i of A at xa[kb * ldxa + i] and of row j
+// of B at xb[kb * ldxb + j]; lane (h, c) passes the scale of block
+// 4 kt + 2 t + h of its row, and the next tile's scale bytes are loaded
+// with its operands (127 past the last block of K, where the operands are
+// zero-filled).
+template <int BM, int BN, bool TA, bool TB, bool kVec, int kOp, bool kMX = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, BM == 256 ? 1 : 2)))
 void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A, int64_t lda,
                     int64_t sa, const uint16_t *__restrict__ B, int64_t ldb, int64_t sb,
                     float *__restrict__ C, int64_t ldc, int64_t sc, int64_t batch,
-                    int64_t tiles_m, int64_t tiles_n)
+                    int64_t tiles_m, int64_t tiles_n, const uint8_t *__restrict__ xa = nullptr,
+                    int64_t ldxa = 0, const uint8_t *__restrict__ xb = nullptr, int64_t ldxb = 0)
 {
     using S = Shape<BM, BN>;
     constexpr int MB = S::kMB, NB = S::kNB;
@@ -493,10 +505,36 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int64_t ktiles = (K + BK - 1) / BK;
+    // MX scales of the lane's blocks for the two steps of a tile (this tile
+    // and the next, loaded with its operands)
+    int xs_a[2][MB], xs_b[2][NB], xn_a[2][MB], xn_b[2][NB];
+    const int xh = lane >> 5, xc = lane & 31;
+    auto load_scales = [&](int64_t kt, int (&ya)[2][MB], int (&yb)[2][NB]) {
+        const int64_t nblk = K / 16;   // 32-byte blocks of K (K in 16-bit slots)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int64_t kb = 4 * kt + 2 * t + xh;
+            const bool in = kb < nblk;
+            const int64_t kbc = in ? kb : 0;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int64_t r = m0 + wm * S::kWM + mb * 32 + xc;
+                const int v = xa[kbc * ldxa + (r < ldxa ? r : ldxa - 1)];
+                ya[t][mb] = in ? v : 127;
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int64_t r = n0 + wn * S::kWN + nb * 32 + xc;
+                const int v = xb[kbc * ldxb + (r < ldxb ? r : ldxb - 1)];
+                yb[t][nb] = in ? v : 127;
+            }
+        }
+    };
     if (ktiles > 0) {
         u16x8 va[S::kAChunks], vb[S::kBChunks];
         load_operand<BM, S::kAChunks, !TA, kVec>(va, A, lda, m0, M, 0, K, a_full && BK <= K);
         load_operand<BN, S::kBChunks, TB, kVec>(vb, B, ldb, n0, N, 0, K, b_full && BK <= K);
+        if constexpr (kMX) load_scales(0, xs_a, xs_b);
         store_operand<BM, S::kAChunks, !TA>(va, As[0]);
         store_operand<BN, S::kBChunks, TB>(vb, Bs[0]);
         __syncthreads();
@@ -508,8 +546,37 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
                 const bool kfull = k0 + BK <= K;
                 load_operand<BM, S::kAChunks, !TA, kVec>(va, A, lda, m0, M, k0, K, a_full && kfull);
                 load_operand<BN, S::kBChunks, TB, kVec>(vb, B, ldb, n0, N, k0, K, b_full && kfull);
+                if constexpr (kMX) load_scales(kt + 1, xn_a, xn_b);
             }
-            if constexpr (kOp >= kFp8Op) {
+            if constexpr (kMX) {
+#pragma unroll
+                for (int t = 0; t < BK / 32; ++t) {
+                    bf16x8 a0[MB], a1[MB], b0[NB], b1[NB];
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        a0[mb] = fragment<BM, true>(As[cur], wm * S::kWM + mb * 32, 2 * t, lane);
+                        a1[mb] = fragment<BM, true>(As[cur], wm * S::kWM + mb * 32, 2 * t + 1, lane);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        b0[nb] = fragment<BN, true>(Bs[cur], wn * S::kWN + nb * 32, 2 * t, lane);
+                        b1[nb] = fragment<BN, true>(Bs[cur], wn * S::kWN + nb * 32, 2 * t + 1, lane);
+                    }
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+                            acc[mb][nb] = mfma8<kOp>(a0[mb], a1[mb], b0[nb], b1[nb], acc[mb][nb],
+                                                     xs_a[t][mb], xs_b[t][nb]);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) xs_a[t][mb] = xn_a[t][mb];
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) xs_b[t][nb] = xn_b[t][nb];
+                }
+            } else if constexpr (kOp >= kFp8Op) {
 #pragma unroll
                 for (int t = 0; t < BK / 32; ++t) {
                     bf16x8 a0[MB], a1[MB], b0[NB], b1[NB];
@@ -836,6 +903,18 @@ void launch_bf16_layout(const Problem &p, bool vec, uint32_t blocks, int64_t tm,
 {
     const auto *A = static_cast<const uint16_t *>(p.A);
     const auto *B = static_cast<const uint16_t *>(p.B);
+    // MX block scales: the 128 x 128 tile only (the 256 x 256 one runs out of
+    // registers with the scale bytes); the 8-bit operands are always
+    // vector-aligned
+    if constexpr (kOp >= kFp8Op && !TA && TB && BM == 128) {
+        if (p.xa) {
+            hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, true, kOp, true>), dim3(blocks),
+                               dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb,
+                               p.sb, p.C, p.ldc, p.sc, p.batch, tm, tn, p.xa, p.ldxa, p.xb,
+                               p.ldxb);
+            return;
+        }
+    }
     if (vec)
         hipLaunchKernelGGL((bf::batched_kernel<BM, BN, TA, TB, true, kOp>), dim3(blocks),
                            dim3(kThreads), 0, s, p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb,
@@ -870,6 +949,7 @@ hipError_t launch_fp8(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + BM - 1) / BM, tn = (p.N + BN - 1) / BN;
     if (tm * tn * p.batch > kMaxBlocks || !supports_fp8(p)) return hipErrorInvalidValue;
+    if (p.xa && (BM != 128 || p.batch != 1)) return hipErrorInvalidValue;
     const uint32_t blocks = static_cast<uint32_t>(tm * tn * p.batch);
     Problem q = p;
     q.K = p.K / 2;

@@ -705,13 +705,24 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 }
 
 // ---- 8-bit floats on the same staging ---------------------------------------
-// The OCP e4m3 / e5m2 operands of v_mfma_scale_f32_32x32x64_f8f6f4 (unit
-// block scales), A as written and B transposed: both factors then have
-// rows along K, and two 8-bit values sit in each 16-bit slot of the bf16
-// kernel's staging, so a K tile of DBK slots is 64 bytes of K, exactly one
-// MFMA deep.  A lane's 32 bytes per operand are its 16-byte reads of both
-// slices of the tile (the same bytes of K for A and B in every lane, which
-// is all the dot products need).  Per MFMA the matrix unit is busy twice as long as
+// The OCP e4m3 / e5m2 operands of v_mfma_scale_f32_32x32x64_f8f6f4, A as
+// written and B transposed: both factors then have rows along K, and two
+// 8-bit values sit in each 16-bit slot of the bf16 kernel's staging, so a K
+// tile of DBK slots is 64 bytes of K, exactly one MFMA deep.  Lane (h, c)'s
+// 32 bytes per operand are bytes 16 h .. 16 h + 15 and 32 + 16 h .. 47 + 16 h
+// of the tile (two 16-byte reads), which is where the instruction takes K
+// positions from: its 32-element block 0 is the first 16 bytes of both
+// half-waves, block 1 the second 16, and the scale of block b of row
+// (column) c is the scale operand of lane (b, c) (measured: lanes holding
+// bytes 32 h .. 32 h + 31 with the scale of block h give exactly the sums
+// of that mapping).  MX block scales (vidyal.ai tag page, Part 11, names
+// them; OCP microscaling fixes the block at 32 elements and the scale
+// format at E8M0) so need no other operand layout.  Without them every
+// scale is 127 (2^0); with them (kMX) each stage also holds the tile's
+// scales -- two blocks of K for each row of A and each column of B,
+// 2 TM + 2 TN bytes, loaded by one more 4-byte LDS-direct load per wave --
+// and lane (h, c) reads the byte of block h of its row (column) beside its
+// fragments.  Per MFMA the matrix unit is busy twice as long as
 // for bf16 while the bytes staged per MFMA are the same, so one tile's
 // MFMAs cover the loads of a tile and the reads of the next: one phase per
 // tile, with the next tile's reads and the loads of the tile four ahead
@@ -728,7 +739,41 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 template <int TM, int TN>
 struct Frag8 {
     i32x8 a[TM / 64], b[TN / 64];
+    int sa[TM / 64], sb[TN / 64];   // MX scales (E8M0 in the low byte) of the lane's blocks
 };
+
+// MX scale staging of one wave: its 4-byte LDS-direct load of the tile's
+// scale bytes (scalar base, advanced by kstride bytes per tile, lane offset
+// voff, landing at byte lds_off of each stage) and the stage byte offsets
+// of the lane's scales of its A and B blocks.
+template <int TM, int TN>
+struct MXCtx {
+    const char *base;
+    int64_t kstride;
+    uint32_t voff, lds_off;
+    uint32_t rdA[TM / 64], rdB[TN / 64];
+};
+
+// One LDS-direct 4-byte load, scalar-base form: lane i's 4 bytes land at
+// LDS byte M0 + 4 i (counted like the 16-byte loads).
+__device__ __forceinline__ void lds_direct_load4(uint32_t voff, const void *sbase, uint32_t m0v)
+{
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory", "m0");
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void read_scales(Frag8<TM, TN> &f, const uint16_t *stage,
+                                            const MXCtx<TM, TN> &mx)
+{
+    const uint8_t *st = reinterpret_cast<const uint8_t *>(stage);
+#pragma unroll
+    for (int j = 0; j < TM / 64; ++j) f.sa[j] = st[mx.rdA[j]];
+#pragma unroll
+    for (int j = 0; j < TN / 64; ++j) f.sb[j] = st[mx.rdB[j]];
+}
 
 template <int kHalf>
 __device__ __forceinline__ void set_half(i32x8 &v, const u16x8 &x)
@@ -758,55 +803,85 @@ __device__ __forceinline__ void read8(Frag8<TM, TN> &f, const uint16_t *stage,
     }
 }
 
-// fp8 operation codes: 2 * fa + fb, fa and fb the formats (0 e4m3, 1 e5m2).
+// fp8 operation codes: 2 * fa + fb, fa and fb the formats (0 e4m3, 1 e5m2);
+// sa and sb the E8M0 scales of the lane's blocks (127: 2^0).
 template <int kFmt>
-__device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c)
+__device__ __forceinline__ f32x16 mfma8(const i32x8 &a, const i32x8 &b, const f32x16 &c,
+                                        int sa = 127, int sb = 127)
 {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmt >> 1, kFmt & 1, 0, 127,
-                                                           0, 127);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, kFmt >> 1, kFmt & 1, 0, sa,
+                                                           0, sb);
 }
 
 // MFMAs of one tile (fragments cur) with the reads of the next tile into
 // nxt and this wave's loads of tile `kload` into stage `lstage` slotted in,
 // spread evenly (256 x 256: one read after each MFMA, a load after every
 // other).
-template <int kFmt, int TM, int TN>
+// Load l of a tile: the A and B chunks, then (kMX) the scale load.
+template <bool kMX, int TM, int TN>
+__device__ __forceinline__ void load8_one(const DCtx<TM, TN, false, true> &x,
+                                          const MXCtx<TM, TN> &mx, uint32_t stage_lds, int64_t kt,
+                                          int l)
+{
+    if (kMX && l == DTile<TM, TN, false, true>::kPerTile)
+        lds_direct_load4(mx.voff, mx.base + kt * mx.kstride, stage_lds + mx.lds_off);
+    else
+        load_one(x, stage_lds, kt, l);
+}
+
+template <int kFmt, bool kMX, int TM, int TN>
 __device__ __forceinline__ void mfma_phase8(f32x16 (&acc)[TM / 64][TN / 64],
                                             const Frag8<TM, TN> &cur, Frag8<TM, TN> &nxt,
                                             const uint16_t *rstage,
-                                            const DCtx<TM, TN, false, true> &x, uint32_t lstage,
+                                            const DCtx<TM, TN, false, true> &x,
+                                            const MXCtx<TM, TN> &mx, uint32_t lstage,
                                             int64_t kload)
 {
     using T = DTile<TM, TN, false, true>;
-    constexpr int NB = T::kNB, R = 2 * T::kReads, Q = T::kQ;
+    constexpr int NB = T::kNB, R = 2 * T::kReads, Q = T::kQ, P = T::kPerTile + (kMX ? 1 : 0);
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int mb = q / NB, nb = q % NB;
-        acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], acc[mb][nb]);
+        if constexpr (kMX)
+            acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], acc[mb][nb], cur.sa[mb], cur.sb[nb]);
+        else
+            acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], acc[mb][nb]);
         __builtin_amdgcn_sched_barrier(0);
+        if (kMX && q == 0) read_scales(nxt, rstage, mx);
 #pragma unroll
         for (int r = 0; r < R; ++r)
             if (r * Q / R == q) read8(nxt, rstage, x, r);
 #pragma unroll
-        for (int l = 0; l < T::kPerTile; ++l)
-            if (l * Q / T::kPerTile == q) load_one(x, lstage, kload, l);
+        for (int l = 0; l < P; ++l)
+            if (l * Q / P == q) load8_one<kMX>(x, mx, lstage, kload, l);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // M, N, K, lda, ldb, stride_a and stride_b in 16-bit slots (bytes / 2).
-template <int TM, int TN, bool kRowsC, bool kBatch, int kFmt>
+// kMX: xa / xb are the MX scales (E8M0), the scale of 32-element block kb of
+// row i of A at xa[kb * ldxa + i], of row j of B (column j of the product)
+// at xb[kb * ldxb + j]; ldxa and ldxb multiples of 4, xa and xb 4-byte
+// aligned (a single product).
+template <int TM, int TN, bool kRowsC, bool kBatch, int kFmt, bool kMX = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DTile<TM, TN>::kPerCU, DTile<TM, TN>::kPerCU)))
 void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
                             int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
-                            int64_t sa, int64_t sb, int64_t sc, int64_t batch)
+                            int64_t sa, int64_t sb, int64_t sc, int64_t batch,
+                            const uint8_t *__restrict__ xa = nullptr, int64_t ldxa = 0,
+                            const uint8_t *__restrict__ xb = nullptr, int64_t ldxb = 0)
 {
     using T = DTile<TM, TN, false, true>;
-    constexpr int MB = T::kMB, NB = T::kNB, WM = TM / 2, WN = TN / 2, P = T::kPerTile;
+    constexpr int MB = T::kMB, NB = T::kNB, WM = TM / 2, WN = TN / 2;
+    constexpr int P = T::kPerTile + (kMX ? 1 : 0);
+    // a stage: the A and B tiles, then (kMX) 1 KiB for the scales, one
+    // 256-byte slot per wave's scale load
+    constexpr int SE = T::kStageElems + (kMX ? 512 : 0);
     static_assert((DSTAGES - 1) * P <= 63, "vmcnt is six bits");
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * T::kStageElems];
+    static_assert(!kMX || (2 * TM % 256 == 0 && 2 * TM + 2 * TN <= 1024), "scale slots");
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * SE];
 
     int64_t m0, n0;
     if constexpr (kBatch) {
@@ -856,6 +931,38 @@ void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__r
         x.rdB[s] = TM * DBK * 2 + (wn * WN + c) * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
     }
 
+    // Scale staging: the stage's scale bytes are [A block 2kt][A block
+    // 2kt+1][B block 2kt][B block 2kt+1] (TM, TM, TN, TN bytes); wave w loads
+    // bytes 256 w .. 256 w + 255 of it, waves past the end repeat the last
+    // load into their own (unread) slot.  A row past M (column past N) reads
+    // a byte of the row's padding, clamped to the last 4-byte word of the
+    // row, which is in bounds (its product rows are never stored).
+    MXCtx<TM, TN> mx{};
+    if constexpr (kMX) {
+        constexpr int kLoadsX = (2 * TM + 2 * TN) / 256;
+        const int src = wave < kLoadsX ? wave : kLoadsX - 1;
+        const int pos = 256 * src + 4 * lane;
+        if (256 * src < 2 * TM) {
+            const int kbo = pos / TM, row = pos % TM;
+            const int64_t r = (m0 + row <= ldxa - 4) ? m0 + row : ldxa - 4;
+            mx.base = reinterpret_cast<const char *>(uniform_ptr(xa + m0));
+            mx.voff = static_cast<uint32_t>(kbo * ldxa + (r - m0));
+            mx.kstride = 2 * ldxa;
+        } else {
+            const int q = pos - 2 * TM, kbo = q / TN, col = q % TN;
+            const int64_t r = (n0 + col <= ldxb - 4) ? n0 + col : ldxb - 4;
+            mx.base = reinterpret_cast<const char *>(uniform_ptr(xb + n0));
+            mx.voff = static_cast<uint32_t>(kbo * ldxb + (r - n0));
+            mx.kstride = 2 * ldxb;
+        }
+        mx.lds_off = T::kStageElems * 2 + 256 * wave;
+#pragma unroll
+        for (int j = 0; j < MB; ++j) mx.rdA[j] = T::kStageElems * 2 + h * TM + wm * WM + 32 * j + c;
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            mx.rdB[j] = T::kStageElems * 2 + 2 * TM + h * TN + wn * WN + 32 * j + c;
+    }
+
     f32x16 acc[MB][NB];
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -865,9 +972,9 @@ void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__r
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     const int64_t ktiles = K / DBK;
-    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * T::kStageElems; };
+    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * SE; };
     auto lstage = [&](int64_t kt) {
-        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * T::kStageElems * 2;
+        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * SE * 2;
     };
     auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
 
@@ -877,11 +984,12 @@ void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__r
 #pragma unroll
     for (int st = 0; st < DSTAGES; ++st)
 #pragma unroll
-        for (int l = 0; l < P; ++l) load_one(x, lstage(st), kclamp(st), l);
+        for (int l = 0; l < P; ++l) load8_one<kMX>(x, mx, lstage(st), kclamp(st), l);
     wait_lds_vm_barrier<(DSTAGES - 1) * P>();
     Frag8<TM, TN> f, g;
 #pragma unroll
     for (int r = 0; r < 2 * T::kReads; ++r) read8(f, stage(0), x, r);
+    if constexpr (kMX) read_scales(f, stage(0), mx);
     wait_lds_vm_barrier<(DSTAGES - 2) * P>();
 
     // Tile kt: MFMAs on its fragments (in registers) with the reads of tile
@@ -891,10 +999,11 @@ void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__r
     // done, barrier.  Two tiles per trip so the fragment sets alternate
     // without copies; reads past the last tile hit landed re-fetches.
     for (int64_t kt = 0; kt < ktiles; kt += 2) {
-        mfma_phase8<kFmt>(acc, f, g, stage(kt + 1), x, lstage(kt), kclamp(kt + DSTAGES));
+        mfma_phase8<kFmt, kMX>(acc, f, g, stage(kt + 1), x, mx, lstage(kt), kclamp(kt + DSTAGES));
         wait_lds_vm_barrier<(DSTAGES - 2) * P>();
         if (kt + 1 == ktiles) break;
-        mfma_phase8<kFmt>(acc, g, f, stage(kt + 2), x, lstage(kt + 1), kclamp(kt + 1 + DSTAGES));
+        mfma_phase8<kFmt, kMX>(acc, g, f, stage(kt + 2), x, mx, lstage(kt + 1),
+                               kclamp(kt + 1 + DSTAGES));
         wait_lds_vm_barrier<(DSTAGES - 2) * P>();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1000,15 +1109,16 @@ bool supports_mfma_fp8_direct(const Problem &p)
 
 namespace {
 
-template <int TM, int TN, bool kRowsC, bool kBatch>
+template <int TM, int TN, bool kRowsC, bool kBatch, bool kMX = false>
 void launch_fp8_fmt(const Problem &p, const dim3 &grid, int64_t tm, int64_t tn, hipStream_t s)
 {
     const auto *A = static_cast<const uint16_t *>(p.A);
     const auto *B = static_cast<const uint16_t *>(p.B);
 #define MI355_FP8_LAUNCH(F)                                                                        \
-    hipLaunchKernelGGL((mfma_fp8_direct_kernel<TM, TN, kRowsC, kBatch, F>), grid, dim3(kThreads), \
-                       0, s, p.M, p.N, p.K / 2, A, p.lda / 2, B, p.ldb / 2, p.C, p.ldc, tm, tn,   \
-                       p.sa / 2, p.sb / 2, p.sc, p.batch)
+    hipLaunchKernelGGL((mfma_fp8_direct_kernel<TM, TN, kRowsC, kBatch, F, kMX>), grid,            \
+                       dim3(kThreads), 0, s, p.M, p.N, p.K / 2, A, p.lda / 2, B, p.ldb / 2, p.C,  \
+                       p.ldc, tm, tn, p.sa / 2, p.sb / 2, p.sc, p.batch, p.xa, p.ldxa, p.xb,      \
+                       p.ldxb)
     switch (2 * p.fa + p.fb) {
     case 0: MI355_FP8_LAUNCH(0); break;
     case 1: MI355_FP8_LAUNCH(1); break;
@@ -1026,7 +1136,11 @@ hipError_t launch_fp8_direct(const Problem &p, hipStream_t s)
     const dim3 grid(static_cast<uint32_t>(tm * tn * p.batch));
     const bool rows_c = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0 &&
                         p.N % 4 == 0 && p.sc % 4 == 0;
-    if (p.batch != 1) {
+    if (p.xa) {   // MX block scales: a single product
+        if (p.batch != 1) return hipErrorInvalidValue;
+        if (rows_c) launch_fp8_fmt<TM, TN, true, false, true>(p, grid, tm, tn, s);
+        else launch_fp8_fmt<TM, TN, false, false, true>(p, grid, tm, tn, s);
+    } else if (p.batch != 1) {
         if (rows_c) launch_fp8_fmt<TM, TN, true, true>(p, grid, tm, tn, s);
         else launch_fp8_fmt<TM, TN, false, true>(p, grid, tm, tn, s);
     } else {

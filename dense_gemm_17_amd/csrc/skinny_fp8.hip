@@ -14,7 +14,13 @@
 //     products);
 //   * each lane's partial sums are added over the wave by an xor butterfly,
 //     which leaves the same total in every lane (a fixed order: the result
-//     is repeatable bit for bit).
+//     is repeatable bit for bit);
+//   * with MX block scales (kMX: one E8M0 scale per 32 elements of K of each
+//     row of A and of Bt, block kb of row i at x[kb * ld + i]) a chunk's
+//     16 products are summed on their own and added times 2^(sa + sb - 254)
+//     (v_ldexp_f32: the exact power-of-two scaling, rounded once); the four
+//     Bt rows' scales of a block are one 4-byte load, A's come from the
+//     caches; a NaN scale (255) makes the chunk's contribution NaN.
 #include "gemm_internal.h"
 
 namespace mi355gemm {
@@ -50,11 +56,14 @@ __device__ __forceinline__ void widen16(const u32x4 &v, float (&out)[16])
     }
 }
 
-// kMR >= M accumulator rows; K a multiple of 16, rows 16-byte aligned.
-template <int kMR, int kFA, int kFB>
+// kMR >= M accumulator rows; K a multiple of 16, rows 16-byte aligned
+// (with kMX: K a multiple of 32, ldxb a multiple of 4, xb 4-byte aligned).
+template <int kMR, int kFA, int kFB, bool kMX = false>
 __global__ __launch_bounds__(64 * kWaves) void skinny_fp8_kernel(
     int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ A, int64_t lda,
-    const uint8_t *__restrict__ Bt, int64_t ldb, float *__restrict__ C, int64_t ldc)
+    const uint8_t *__restrict__ Bt, int64_t ldb, float *__restrict__ C, int64_t ldc,
+    const uint8_t *__restrict__ xa = nullptr, int64_t ldxa = 0,
+    const uint8_t *__restrict__ xb = nullptr, int64_t ldxb = 0)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t j0 = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * kRows;
@@ -75,16 +84,37 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_fp8_kernel(
         float bf[kRows][16];
 #pragma unroll
         for (int r = 0; r < kRows; ++r) widen16<kFB>(b[r], bf[r]);
+        uint32_t xbw = 0;   // the four Bt rows' scales of this chunk's block
+        if constexpr (kMX) {
+            // j0 is a multiple of 4 and ldxb >= N a multiple of 4: the word is
+            // inside the block's row of scales
+            xbw = *reinterpret_cast<const uint32_t *>(xb + (c >> 1) * ldxb + j0);
+        }
 #pragma unroll
         for (int i = 0; i < kMR; ++i) {
             if (i >= M) break;
             const u32x4 a = *reinterpret_cast<const u32x4 *>(A + i * lda + 16 * c);
             float af[16];
             widen16<kFA>(a, af);
+            if constexpr (kMX) {
+                const int ea = xa[(c >> 1) * ldxa + i];
 #pragma unroll
-            for (int r = 0; r < kRows; ++r)
+                for (int r = 0; r < kRows; ++r) {
+                    float t = 0.f;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][r] = __builtin_fmaf(af[e], bf[r][e], acc[i][r]);
+                    for (int e = 0; e < 16; ++e) t = __builtin_fmaf(af[e], bf[r][e], t);
+                    const int eb = (xbw >> (8 * r)) & 255;
+                    const float v = (ea == 255 || eb == 255) ? __builtin_nanf("")
+                                                             : __builtin_ldexpf(t, ea + eb - 254);
+                    acc[i][r] += v;
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < kRows; ++r)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        acc[i][r] = __builtin_fmaf(af[e], bf[r][e], acc[i][r]);
+            }
         }
     }
 #pragma unroll
@@ -105,14 +135,14 @@ __global__ __launch_bounds__(64 * kWaves) void skinny_fp8_kernel(
     }
 }
 
-template <int kMR>
+template <int kMR, bool kMX>
 void launch_rows(const Problem &p, dim3 grid, hipStream_t s)
 {
     const auto *A = static_cast<const uint8_t *>(p.A);
     const auto *B = static_cast<const uint8_t *>(p.B);
-#define MI355_SKINNY_FP8(FA, FB)                                                                \
-    hipLaunchKernelGGL((skinny_fp8_kernel<kMR, FA, FB>), grid, dim3(64 * kWaves), 0, s, p.M,  \
-                       p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc)
+#define MI355_SKINNY_FP8(FA, FB)                                                                 \
+    hipLaunchKernelGGL((skinny_fp8_kernel<kMR, FA, FB, kMX>), grid, dim3(64 * kWaves), 0, s,   \
+                       p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, p.xa, p.ldxa, p.xb, p.ldxb)
     switch (2 * p.fa + p.fb) {
     case 0: MI355_SKINNY_FP8(0, 0); break;
     case 1: MI355_SKINNY_FP8(0, 1); break;
@@ -126,7 +156,7 @@ void launch_rows(const Problem &p, dim3 grid, hipStream_t s)
 
 bool supports_skinny_fp8(const Problem &p)
 {
-    return supports_fp8(p) && p.batch == 1 && p.M <= kSkinnyMaxM;
+    return supports_fp8(p) && p.batch == 1 && p.M <= (p.xa ? 8 : kSkinnyMaxM);
 }
 
 hipError_t launch_skinny_fp8(const Problem &p, hipStream_t s)
@@ -136,11 +166,18 @@ hipError_t launch_skinny_fp8(const Problem &p, hipStream_t s)
     const int64_t blocks = (p.N + per_block - 1) / per_block;
     if (blocks > kMaxBlocks) return hipErrorInvalidValue;
     const dim3 grid(static_cast<uint32_t>(blocks));
-    if (p.M <= 1) launch_rows<1>(p, grid, s);
-    else if (p.M <= 2) launch_rows<2>(p, grid, s);
-    else if (p.M <= 4) launch_rows<4>(p, grid, s);
-    else if (p.M <= 8) launch_rows<8>(p, grid, s);
-    else launch_rows<16>(p, grid, s);
+    if (p.xa) {   // MX scales: at most 8 rows (16 would leave one wave per SIMD)
+        if (p.M <= 1) launch_rows<1, true>(p, grid, s);
+        else if (p.M <= 2) launch_rows<2, true>(p, grid, s);
+        else if (p.M <= 4) launch_rows<4, true>(p, grid, s);
+        else launch_rows<8, true>(p, grid, s);
+    } else {
+        if (p.M <= 1) launch_rows<1, false>(p, grid, s);
+        else if (p.M <= 2) launch_rows<2, false>(p, grid, s);
+        else if (p.M <= 4) launch_rows<4, false>(p, grid, s);
+        else if (p.M <= 8) launch_rows<8, false>(p, grid, s);
+        else launch_rows<16, false>(p, grid, s);
+    }
     return hipGetLastError();
 }
 

@@ -293,6 +293,44 @@ int gemm_force_kernel(int id);
  * (-1 before any). */
 int gemm_last_kernel(void);
 
+/* ---- 8-bit floats with MX block scales ---------------------------------------
+ *
+ * The product of gemm_fp8_f32acc with OCP microscaling (MX) block scales
+ * (vidyal.ai tag page, Part 11, "how FP8, MX and NVFP4 scales work"; the
+ * block of 32 elements and the E8M0 scale format are the OCP MX
+ * definitions): every 32 consecutive elements along K of a row of A, and
+ * of a row of Bt (a column of the product), share one scale byte e, the
+ * power of two 2^(e - 127) (e = 255 is NaN):
+ *
+ *   C[i][j] = sum_k (A[i][k] 2^(SA[k/32][i] - 127)) (Bt[j][k] 2^(SB[k/32][j] - 127))
+ *
+ * with the scale of block kb of row i of A at scale_a[kb*ld_scale_a + i]
+ * and of row j of Bt at scale_b[kb*ld_scale_b + j] (scale arrays stored
+ * block-major: the scales of one block of K for all rows are contiguous,
+ * so a tile's scales are one contiguous run per block).  A, Bt, C, lda, ldb,
+ * ldc, formats and layout conditions as gemm_fp8_f32acc; K a multiple of
+ * 32; ld_scale_a >= M and ld_scale_b >= N, both multiples of 4; scale_a and
+ * scale_b 4-byte aligned, each K/32 rows of its leading dimension long, not
+ * overlapping C.  A NaN scale makes the outputs it touches NaN.  The
+ * matrix-core kernels pass each lane's scale to the instruction's scale
+ * operand (v_mfma_scale_f32_32x32x64_f8f6f4); the bandwidth kernel for at
+ * most 4 rows scales each block's partial sum by 2^(sa + sb - 254).  Errors
+ * as gemm_fp8_f32acc, plus hipErrorInvalidValue for a K that is not a
+ * multiple of 32 or bad scale arrays. */
+int gemm_mxfp8_f32acc(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,
+                      const uint8_t *A, int64_t lda,
+                      const uint8_t *scale_a, int64_t ld_scale_a,
+                      const uint8_t *Bt, int64_t ldb,
+                      const uint8_t *scale_b, int64_t ld_scale_b,
+                      float *C, int64_t ldc, hipStream_t stream);
+
+/* The table's choice for a gemm_mxfp8_f32acc call (pure host function, as
+ * gemm_plan): a kernel id, -1 for arguments the call would refuse, -2 for
+ * nothing to do. */
+int gemm_plan_mxfp8(int64_t M, int64_t N, int64_t K, uintptr_t A, int64_t lda,
+                    uintptr_t scale_a, int64_t ld_scale_a, uintptr_t Bt, int64_t ldb,
+                    uintptr_t scale_b, int64_t ld_scale_b, uintptr_t C, int64_t ldc);
+
 /* ---- fused attention forward ----------------------------------------------
  *
  * Scaled dot-product attention, fp32 in / fp32 out, computed the way "Bare

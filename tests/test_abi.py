@@ -402,3 +402,28 @@ def test_forced_fp8_kernel_only_for_fp8_calls():
         assert g.gemm_plan_batched(g.FP8, 0, 1, 512, 512, 512, 1) == kid
     finally:
         g.gemm_force_kernel(-1)
+
+
+def test_mx_table_choices():
+    # 8-bit products with MX block scales: the bandwidth kernel up to 4 rows,
+    # the LDS-direct tiles for whole 64-byte K tiles, the 128 x 128
+    # register-staged tile otherwise (the 256 x 256 one takes no scales);
+    # refused: K not whole 32-element blocks, scale pitches below the rows
+    # or not multiples of 4
+    P = 1 << 40
+
+    def plan(M, N, K, lsa=None, lsb=None):
+        lsa = -(-M // 4) * 4 if lsa is None else lsa
+        lsb = -(-N // 4) * 4 if lsb is None else lsb
+        k = g.gemm_plan_mxfp8(M, N, K, P, K, 2 * P, lsa, 3 * P, K, 4 * P, lsb, 5 * P, N)
+        return g.gemm_kernel_name(k) if k >= 0 else k
+
+    assert plan(4, 512, 1024) == "skinny_fp8"
+    assert plan(8, 77, 160) == "mfma_fp8_batched128"
+    assert plan(256, 256, 512) == "mfma_fp8_direct128"
+    assert plan(8192, 8192, 8192) == "mfma_fp8_direct256x128"
+    assert plan(512, 512, 480) == "mfma_fp8_batched128"
+    assert plan(64, 64, 48) == -1
+    assert plan(64, 64, 64, lsa=60) == -1
+    assert plan(64, 77, 64, lsb=77) == -1
+    assert plan(0, 64, 64) == -2
