@@ -86,6 +86,10 @@ def _load() -> ctypes.CDLL:
     lib.attention_fwd_f32.argtypes = [i64, i64, i64, i64, ci, ctypes.c_float] + \
         [vp, i64, i64, i64] * 4 + [vp, vp]
     lib.attention_fwd_f32.restype = ci
+    lib.attention_force_kernel.argtypes = [ci]
+    lib.attention_force_kernel.restype = ci
+    lib.attention_last_kernel.argtypes = []
+    lib.attention_last_kernel.restype = ci
     lib.gemm_batched_noalloc.argtypes = [ci] + bsig
     lib.gemm_batched_noalloc.restype = ci
     return lib
@@ -101,7 +105,8 @@ EXPORTS = ("gemm_f32", "gemm_bf16_f32acc", "gemm_f16_f32acc", "gemm_f32_batched"
            "gemm_kernel_count", "gemm_kernel_name", "gemm_kernel_dtype", "gemm_plan",
            "gemm_plan_batched", "gemm_force_kernel", "gemm_last_kernel", "gemm_build_info",
            "gemm_null_launch", "gemm_batched_noalloc", "attention_fwd_f32",
-           "gemm_mxfp8_f32acc", "gemm_plan_mxfp8")
+           "gemm_mxfp8_f32acc", "gemm_plan_mxfp8", "attention_force_kernel",
+           "attention_last_kernel")
 
 
 # ---- raw entry points (pointers and sizes, same names as the C-ABI) --------
@@ -264,6 +269,14 @@ def attention_fwd_f32(B, H, S, D, causal, scale, Q, q_sb, q_sh, q_ss, K, k_sb, k
                       V, v_sb, v_sh, v_ss, O, o_sb, o_sh, o_ss, lse, stream) -> int:
     return lib.attention_fwd_f32(B, H, S, D, causal, scale, Q, q_sb, q_sh, q_ss, K, k_sb, k_sh,
                                  k_ss, V, v_sb, v_sh, v_ss, O, o_sb, o_sh, o_ss, lse, stream)
+
+
+def attention_force_kernel(variant: int) -> int:
+    return lib.attention_force_kernel(variant)
+
+
+def attention_last_kernel() -> int:
+    return lib.attention_last_kernel()
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,

@@ -60,6 +60,7 @@ const KernelInfo kKernels[] = {
     {"mfma_fp8_batched128", kFp8, launch_mfma_fp8_batched128, supports_fp8, true},
     {"mfma_fp8_direct256x128", kFp8, launch_mfma_fp8_direct256x128, supports_mfma_fp8_direct, true},
     {"skinny_fp8", kFp8, launch_skinny_fp8, supports_skinny_fp8, true},
+    {"mfma_bf16_direct64", kBF16, launch_mfma_bf16_direct64, supports_mfma_bf16_direct, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -76,6 +77,8 @@ int kernel_id(const char *name)
 
 std::atomic<int> g_forced{-1};
 std::atomic<int> g_last{-1};
+std::atomic<int> g_attn_forced{-1};
+std::atomic<int> g_attn_last{-1};
 
 constexpr int64_t kMaxDim = INT_MAX;
 
@@ -222,6 +225,30 @@ int64_t tiled_cost(const Problem &p, int64_t bm, int64_t bn, int64_t per_cu, int
 // over the tiles of every product.
 int select_f32_lds(const Problem &p);
 
+// bf16 LDS-direct tiles by the wave-count estimate.  128 x 128 runs at 0.8
+// of the 256 x 256 tile's per-tile efficiency (fitted over twelve shapes,
+// 0.66-1.03; 0.512 of peak at 8192^3 for the large tile), so it wins only
+// where 256 tiles fill the CUs badly.  Where even 128 x 128 tiles number
+// fewer than CUs (a small output over a long K: the weight gradients of a
+// training step) each of them runs alone on its CU, and the 64 x 64 tile
+// (up to five work-groups per CU) is weighed against that: a CU's time is
+// its tile count there times the tile's work over its efficiency
+// (BF16_DIRECT_64, of peak).
+constexpr int64_t BF16_DIRECT_64 = 300;
+int select_bf16_direct(const Problem &p)
+{
+    const int64_t t128 = ceil_div(p.M, 128) * ceil_div(p.N, 128) * p.batch;
+    if (t128 < kCUs) {
+        const int64_t t64 = ceil_div(p.M, 64) * ceil_div(p.N, 64) * p.batch;
+        const int64_t c64 = ceil_div(t64, kCUs) * 64 * 64 * 1000 / BF16_DIRECT_64;
+        const int64_t c128 = 128 * 128 * 1000 / 410;
+        if (t64 <= 5 * kCUs && c64 < c128) return kernel_id("mfma_bf16_direct64");
+    }
+    return tiled_cost(p, 256, 256, 1, 512) <= tiled_cost(p, 128, 128, 2, 410)
+               ? kernel_id("mfma_bf16_direct")
+               : kernel_id("mfma_bf16_direct128");
+}
+
 int select_general(const Problem &p)
 {
     // fp32 with fewer 128 x 128 tiles over all products than CUs and a K of
@@ -243,10 +270,7 @@ int select_general(const Problem &p)
         const int lds = select_f32_lds(p);
         if (lds >= 0) return lds;
     }
-    if (p.dtype == kBF16 && supports_mfma_bf16_direct(p))
-        return tiled_cost(p, 256, 256, 1, 512) <= tiled_cost(p, 128, 128, 2, 410)
-                   ? kernel_id("mfma_bf16_direct")
-                   : kernel_id("mfma_bf16_direct128");
+    if (p.dtype == kBF16 && supports_mfma_bf16_direct(p)) return select_bf16_direct(p);
     if (p.dtype == kBF16)
         return tiled_cost(p, 256, 256, 1, BF16_GENERAL_256) <= tiled_cost(p, 128, 128, 2, BF16_GENERAL_128)
                    ? kernel_id("mfma_bf16_batched")
@@ -298,12 +322,7 @@ int select_kernel(const Problem &p)
     if (p.dtype == kF16) return select_general(p);
     if (p.dtype == kBF16) {
         if (!supports_mfma_bf16_direct(p)) return kernel_id("mfma_bf16");
-        // 128 x 128 runs at 0.8 of the 256 x 256 tile's per-tile efficiency
-        // (fitted over twelve shapes, 0.66-1.03; 0.512 of peak at 8192^3 for
-        // the large tile), so it wins only where 256 tiles fill the CUs badly.
-        if (tiled_cost(p, 256, 256, 1, 512) <= tiled_cost(p, 128, 128, 2, 410))
-            return kernel_id("mfma_bf16_direct");
-        return kernel_id("mfma_bf16_direct128");
+        return select_bf16_direct(p);
     }
     // At most kCUs / 4 tiles of 64 x 64 (a 512 x 512 output or smaller): the
     // split-K kernel, whose 32 x 32 tiles share their K range between four
@@ -732,8 +751,20 @@ int attention_fwd_f32(int64_t B, int64_t H, int64_t S, int64_t D, int causal, fl
     AttnArgs a{Q, K, V, O, lse, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, v_sb, v_sh, v_ss,
                o_sb, o_sh, o_ss, B, H, S, causal,
                static_cast<float>(static_cast<double>(scale) * 1.4426950408889634), 0};
-    return launch_attention_fwd(a, D, stream);
+    const int variant = attention_variant(B, H, S, D, g_attn_forced.load(std::memory_order_relaxed));
+    const hipError_t e = launch_attention_fwd(a, D, variant, stream);
+    if (e == hipSuccess) g_attn_last.store(variant, std::memory_order_relaxed);
+    return e;
 }
+
+int attention_force_kernel(int variant)
+{
+    if (variant < -1 || variant > 1) return hipErrorInvalidValue;
+    g_attn_forced.store(variant, std::memory_order_relaxed);
+    return hipSuccess;
+}
+
+int attention_last_kernel(void) { return g_attn_last.load(std::memory_order_relaxed); }
 
 int gemm_null_launch(hipStream_t stream) { return launch_null(stream); }
 

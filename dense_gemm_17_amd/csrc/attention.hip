@@ -289,15 +289,222 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
         a.lse[bh * S + qi] = (m + __builtin_amdgcn_logf(lt)) * 0.693147180559945309f;
 }
 
+// ---- few sequences and heads: the keys split over the waves ------------------
+// With few (sequence, head) pairs the kernel above runs on a handful of
+// CUs, each walking every key tile of its 128 queries alone (a single GPT
+// sequence: 6 heads x 2 query tiles = 12 work-groups).  Here a work-group
+// takes 32 queries and its four waves split the key tiles between them
+// (wave w takes tiles w, w + 4, ...), each with its own running maximum,
+// sum and output in registers; at the end the four partial softmaxes are
+// merged through LDS (the maximum of the maxima m, each part's sum and
+// output scaled by 2^(m_w - m), output over summed weights).  Each wave
+// reads its K and V tiles straight from memory into the MFMA operand
+// layout (a lane's 16-byte pieces of its key's row of K; 4-byte values of
+// V, 32 lanes on one row), the next tile's while the current one is
+// computed.  Head width 64.
+constexpr int kSplitQ = 32;   // queries per work-group
+constexpr int kSplitBN = 32;  // keys per tile
+
+__global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_split_kernel(AttnArgs a)
+{
+    constexpr int D = 64, DH = D / 2;
+    __shared__ float mrg_o[3][D / 32][16][64];   // waves 1..3: output registers by lane
+    __shared__ float mrg_ml[3][2][64];           // waves 1..3: maximum and sum by lane
+
+    const int64_t BH = a.B * a.H;
+    const int64_t blk = blockIdx.x;
+    const int64_t nq = (a.S + kSplitQ - 1) / kSplitQ;
+    const int64_t qb = a.causal ? nq - 1 - blk / BH : blk / BH;
+    const int64_t bh = blk % BH;
+    const int64_t bi = bh / a.H, hi = bh % a.H;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, c = lane & 31;
+    const int S = static_cast<int>(a.S);
+    const int q0 = static_cast<int>(qb) * kSplitQ;
+    const int qi = q0 + c;
+    const bool q_ok = qi < S;
+
+    const float *Qp = a.Q + bi * a.q_sb + hi * a.q_sh;
+    const float *Kp = a.K + bi * a.k_sb + hi * a.k_sh;
+    const float *Vp = a.V + bi * a.v_sb + hi * a.v_sh;
+
+    float qf[DH];
+    {
+        const float *src = Qp + static_cast<int64_t>(q_ok ? qi : 0) * a.q_ss + h * DH;
+#pragma unroll
+        for (int t = 0; t < DH / 4; ++t) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(src + 4 * t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qf[4 * t + e] = q_ok ? v[e] : 0.f;
+        }
+    }
+    const int kend = a.causal ? (S < q0 + kSplitQ ? S : q0 + kSplitQ) : S;
+    const int ntiles = (kend + kSplitBN - 1) / kSplitBN;
+    const int lim = a.causal ? (q_ok ? qi : S - 1) : S - 1;   // last key this lane sees
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] = 0.f;
+    float m = neg_inf(), l = 0.f;
+
+    // tile t's operands: K row (key t*32 + c), this half's 32 dims; V at
+    // keys t*32 + 8 (r/4) + 4 h + r%4, dims 32 d + c (zero past S)
+    f32x4 kf[DH / 4];
+    float vf[16][D / 32];
+    auto load = [&](int t) {
+        const int key = t * kSplitBN + c;
+        const bool ok = key < S;
+        const float *kr = Kp + static_cast<int64_t>(ok ? key : 0) * a.k_ss + h * DH;
+#pragma unroll
+        for (int u = 0; u < DH / 4; ++u) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(kr + 4 * u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kf[u][e] = ok ? v[e] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int vk = t * kSplitBN + 8 * (r >> 2) + 4 * h + (r & 3);
+            const bool vok = vk < S;
+            const float *vr = Vp + static_cast<int64_t>(vok ? vk : 0) * a.v_ss + c;
+#pragma unroll
+            for (int d = 0; d < D / 32; ++d) vf[r][d] = vok ? vr[32 * d] : 0.f;
+        }
+    };
+
+    const float sl2 = a.scale_log2;
+    int t = wave;
+    if (t < ntiles) load(t);
+    for (; t < ntiles; t += 4) {
+        f32x4 kc[DH / 4];
+        float vc[16][D / 32];
+#pragma unroll
+        for (int u = 0; u < DH / 4; ++u) kc[u] = kf[u];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int d = 0; d < D / 32; ++d) vc[r][d] = vf[r][d];
+        if (t + 4 < ntiles) load(t + 4);
+        f32x16 sc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+        for (int u = 0; u < DH / 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sc = __builtin_amdgcn_mfma_f32_32x32x2f32(kc[u][e], qf[4 * u + e], sc, 0, 0, 0);
+        float mx = neg_inf();
+        const int kl = t * kSplitBN + 4 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = kl + 8 * (r >> 2) + (r & 3);
+            const float x = key <= lim ? sc[r] * sl2 : neg_inf();
+            sc[r] = x;
+            mx = fmaxf(mx, x);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == neg_inf() ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(sc[r] - m_use);
+            sc[r] = pr;
+            psum += pr;
+        }
+        l = l * alpha + psum;
+        m = m_new;
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int d = 0; d < D / 32; ++d)
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vc[r][d], sc[r], o[d], 0, 0, 0);
+    }
+    l += __shfl_xor(l, 32);
+
+    // merge the four waves' partial softmaxes (every lane takes part; a wave
+    // that saw no key has m = -inf and weight 0)
+    if (wave > 0) {
+#pragma unroll
+        for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mrg_o[wave - 1][d][r][lane] = o[d][r];
+        mrg_ml[wave - 1][0][lane] = m;
+        mrg_ml[wave - 1][1][lane] = l;
+    }
+    __syncthreads();
+    if (wave != 0 || !q_ok) return;
+    float mw[3], lw[3];
+    float mt = m;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        mw[w] = mrg_ml[w][0][lane];
+        lw[w] = mrg_ml[w][1][lane];
+        mt = fmaxf(mt, mw[w]);
+    }
+    const float f0 = __builtin_amdgcn_exp2f(m - mt);
+    float fw[3];
+    float lt = l * f0;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        fw[w] = __builtin_amdgcn_exp2f(mw[w] - mt);
+        lt += lw[w] * fw[w];
+    }
+    const float inv = 1.f / lt;
+    float *Op = a.O + bi * a.o_sb + hi * a.o_sh + static_cast<int64_t>(qi) * a.o_ss;
+#pragma unroll
+    for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 4 * g + j;
+                float acc = o[d][r] * f0;
+#pragma unroll
+                for (int w = 0; w < 3; ++w) acc += mrg_o[w][d][r][lane] * fw[w];
+                v[j] = acc * inv;
+            }
+            *reinterpret_cast<f32x4 *>(Op + 32 * d + 8 * g + 4 * h) = v;
+        }
+    if (a.lse && h == 0)
+        a.lse[bh * a.S + qi] = (mt + __builtin_amdgcn_logf(lt)) * 0.693147180559945309f;
+}
+
 }  // namespace
 
-hipError_t launch_attention_fwd(const AttnArgs &args, int64_t D, hipStream_t s)
+int attention_variant(int64_t B, int64_t H, int64_t S, int64_t D, int forced)
+{
+    const int64_t blocks = (S + kBM - 1) / kBM * B * H;
+    if (D != 64) return 0;
+    if (forced == 0 || forced == 1) return forced;
+    // Fewer 128-query work-groups than CUs: split the keys over the waves of
+    // 32-query work-groups instead.
+    return blocks < kCUs ? 1 : 0;
+}
+
+hipError_t launch_attention_fwd(const AttnArgs &args, int64_t D, int variant, hipStream_t s)
 {
     AttnArgs a = args;
     a.nqb = (a.S + kBM - 1) / kBM;
     const int64_t blocks = a.nqb * a.B * a.H;
     if (blocks == 0) return hipSuccess;
     if (blocks > kMaxBlocks) return hipErrorInvalidValue;
+    if (variant == 1) {
+        if (D != 64) return hipErrorInvalidValue;
+        const int64_t split = (a.S + kSplitQ - 1) / kSplitQ * a.B * a.H;
+        if (split > kMaxBlocks) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(attention_fwd_split_kernel, dim3(static_cast<uint32_t>(split)),
+                           dim3(kAttnThreads), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 grid(static_cast<uint32_t>(blocks));
     if (D == 64)
         hipLaunchKernelGGL((attention_fwd_kernel<64, 64>), grid, dim3(kAttnThreads), 0, s, a);

@@ -56,7 +56,11 @@ struct AttnArgs {
     float scale_log2;
     int64_t nqb;
 };
-hipError_t launch_attention_fwd(const AttnArgs &a, int64_t D, hipStream_t s);
+// Attention kernels: 0 = 128 queries per work-group, key tiles through LDS;
+// 1 = 32 queries per work-group, key tiles split over its waves (head width
+// 64).  attention_variant picks one (forced >= 0 overrides where it can).
+int attention_variant(int64_t B, int64_t H, int64_t S, int64_t D, int forced);
+hipError_t launch_attention_fwd(const AttnArgs &a, int64_t D, int variant, hipStream_t s);
 
 // A launcher enqueues its kernel(s) for `p` on `stream` and returns the
 // launch status.  It may assume p passed validation and its `supports` test.
@@ -109,6 +113,7 @@ hipError_t launch_mfma_fp8_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_direct256x128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_bf16_direct64(const Problem &p, hipStream_t s);
 bool supports_mfma_fp8_direct(const Problem &p);
 hipError_t launch_skinny_fp8(const Problem &p, hipStream_t s);
 bool supports_skinny_fp8(const Problem &p);

@@ -67,6 +67,18 @@ __device__ __forceinline__ int b_swz(int row)
     return ((r >> 1) << 1) | ((r & 1) << 2) | ((r >> 1) << 3);
 }
 
+// The same for rows of kCh 16-byte chunks in the LDS-direct tiles: 16 or
+// more chunks take b_swz; rows of 8 chunks (128 bytes, a 64-wide tile) put
+// rows r and r + 1 in different halves of the 256-byte bank window already,
+// so only rows two apart collide, and XOR mask 4 for rows 2 and 3 (mod 4)
+// separates both the 16-lane pairs of chunks and the half-wave's four.
+template <int kCh>
+__device__ __forceinline__ int b_swzc(int row)
+{
+    if constexpr (kCh == 8) return ((row >> 1) & 1) << 2;
+    else return b_swz(row);
+}
+
 struct Frag {
     u16x8 a[kAChunks];
     u16x8 b[kBChunks];
@@ -599,7 +611,7 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
             // 32 rows of TM elements, laid out as B's; columns past M
             // re-fetch the last full chunk (M % 8 == 0 here)
             const int row = p / (TM / 8), slot = p % (TM / 8);
-            const int cc = slot ^ b_swz(row);
+            const int cc = slot ^ b_swzc<TM / 8>(row);
             const int64_t col = (m0 + 8 * cc < M) ? 8 * cc : M - 8 - m0;
             x.a_voff[i] = static_cast<uint32_t>((row * lda + col) * 2);
             continue;
@@ -621,20 +633,22 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
             continue;
         }
         const int row = p / T::kBChunks, slot = p % T::kBChunks;
-        const int cc = slot ^ b_swz(row);
+        const int cc = slot ^ b_swzc<TN / 8>(row);
         const int64_t col = (n0 + 8 * cc < N) ? 8 * cc : N - 8 - n0;
         x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 2);
     }
     // A rows this lane reads are wm*WM + 32*j + c: their swizzle is a_swz<4>(c)
     // (it depends on bits 2-3 of the row only).
     const int aswz = a_swz<4>(c);
-    // B rows this lane points at are 16s + 8h + i16/4 (+4): swizzle b_swz(i16/4).
-    const int bswz = b_swz(i16 >> 2);
+    // Rows of M or N this lane points at are 16s + 8h + i16/4 (+4): swizzle
+    // b_swzc(i16/4) for the row width of A (TM) or B (TN).
+    const int bswz = b_swzc<TN / 8>(i16 >> 2);
     if constexpr (TA) {
+        const int aswz_t = b_swzc<TM / 8>(i16 >> 2);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int m = wm * WM + mb * 32 + nhalf * 16 + 4 * (i16 & 3);
-            x.rdA[mb] = (8 * h + (i16 >> 2)) * TM * 2 + (((m >> 3) ^ bswz) << 4) + (m & 7) * 2;
+            x.rdA[mb] = (8 * h + (i16 >> 2)) * TM * 2 + (((m >> 3) ^ aswz_t) << 4) + (m & 7) * 2;
         }
     } else {
 #pragma unroll
@@ -1096,6 +1110,8 @@ hipError_t launch_direct(const Problem &p, hipStream_t s)
 
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256>(p, s); }
 hipError_t launch_mfma_bf16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128>(p, s); }
+hipError_t launch_mfma_bf16_direct64(const Problem &p, hipStream_t s) { return launch_direct<64, 64>(p, s); }
+
 hipError_t launch_mfma_f16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256, true>(p, s); }
 
 // 8-bit operands: K a multiple of 64 bytes (one tile), the general 8-bit

@@ -114,12 +114,7 @@ __device__ __forceinline__ f32x4 load_a4(const T *__restrict__ A, int64_t lda, i
 //              CU streams about the same share of B; consecutive shares go
 //              to one XCD, so a cache line split between two shares is read
 //              from HBM once and hit in that XCD's L2 the second time.
-//   kPairs:    strips as kStrips, but work-group ids 16 q + 8 h + x hold strip
-//              16 q + 2 x + h: the two neighbouring strips 2x and 2x + 1
-//              run on one XCD (ids differing by 8), so a cache line split
-//              between them is read from HBM once and hit in L2 the second
-//              time (narrow strips without re-reading B per row half).
-constexpr int kStrips = 1, kRowSplit = 2, kBalanced = 3, kPairs = 4;
+constexpr int kStrips = 1, kRowSplit = 2, kBalanced = 3;
 
 // First (next = 0) or one-past-last (next = 1) column of this work-group's
 // share under kBalanced: shares are consecutive on one XCD (work-group ids
@@ -151,11 +146,6 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
     const int tid = threadIdx.x;
     const int lane = tid % kL, grp = tid / kL;
     int64_t strip = blockIdx.x;
-    if constexpr (kMode == kPairs) {
-        const int64_t id = blockIdx.x;
-        strip = (id >> 4) * 16 + 2 * (id & 7) + ((id >> 3) & 1);
-        if (strip * kCols >= N) return;   // whole work-group
-    }
     if constexpr (kMode == kRowSplit) {
         const int64_t id = blockIdx.x;
         const int64_t half = (id >> 3) & 1;
@@ -239,7 +229,6 @@ hipError_t launch_cfg(const Problem &p, hipStream_t s, bool vec)
     constexpr int kCols = kL * Elem<T>::kPerLoad;
     const int64_t strips = (p.N + kCols - 1) / kCols;
     const int64_t blocks = kMode == kRowSplit ? 16 * ((strips + 7) / 8)
-                           : kMode == kPairs ? 16 * ((strips + 15) / 16)
                            : kMode == kBalanced ? kCUs : strips;
     if (blocks > kMaxBlocks) return hipErrorInvalidValue;
     const T *A = static_cast<const T *>(p.A);

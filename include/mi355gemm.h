@@ -369,6 +369,17 @@ int attention_fwd_f32(int64_t B, int64_t H, int64_t S, int64_t D, int causal, fl
                       float *O, int64_t o_sb, int64_t o_sh, int64_t o_ss, float *lse,
                       hipStream_t stream);
 
+/* Test hooks of attention_fwd_f32 (not for users): force one of its two
+ * kernels for calls that can take it -- 0: 128 queries per work-group with
+ * the key tiles staged through LDS for four waves; 1: 32 queries per
+ * work-group with the key tiles split over its four waves and the partial
+ * softmaxes merged at the end (head width 64; chosen by default where the
+ * first would launch fewer work-groups than the GPU has CUs) -- or -1 for
+ * the default choice; and the kernel the last successful call ran (-1
+ * before any).  Process-global. */
+int attention_force_kernel(int variant);
+int attention_last_kernel(void);
+
 /* Timing hook: enqueues one launch of a kernel that does nothing (one
  * work-group of 64 lanes) on `stream` and returns the launch status.  It is
  * the null measurement of the devpost write-up ("gpu kernels", "How we know

@@ -34,7 +34,7 @@ LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mf
            "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64"]
 GENERAL["f16"] = ["mfma_f16_batched", "mfma_f16_batched128", "mfma_f16_batched_splitk"]
 ALL = {"f32": GENERAL["f32"] + LDS_F32,
-       "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128"],
+       "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128", "mfma_bf16_direct64"],
        "f16": GENERAL["f16"] + ["mfma_f16_direct", "mfma_f16_direct128"]}
 TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 DTYPES = ["f32", "bf16", "f16"]
