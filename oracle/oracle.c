@@ -178,7 +178,10 @@ static double load_a(const job_t *j, int64_t i, int64_t k)
     return decode_kind(j->kind, ((const uint16_t *)j->A)[at]);
 }
 
-static double load_b_stored(const job_t *j, int64_t k, int64_t n)
+/* Forced inline: it runs once per multiply, and a call there halves the
+ * oracle's speed. */
+static inline __attribute__((always_inline))
+double load_b_stored(const job_t *j, int64_t k, int64_t n)
 {
 #ifdef ORACLE_MUTANT_TRANSPOSE_B
     int64_t t = k; k = n % j->K; n = t % j->N;
@@ -195,19 +198,11 @@ static double load_b_stored(const job_t *j, int64_t k, int64_t n)
     return decode_kind(j->kind, ((const uint16_t *)j->B)[at]);
 }
 
-/* Element (k, n) of B: from the decoded copy when there is one (fp16 and
- * 8-bit patterns, whose decode is the slow part, and any B stored
- * transposed), else straight from storage.  The copy holds
- * exactly the values load_b_stored returns; it only spares the inner loop a
- * decode or a strided read per multiply. */
-static double load_b(const job_t *j, int64_t k, int64_t n)
-{
-    if (j->Bd) return j->Bd[k * j->N + n];
-    return load_b_stored(j, k, n);
-}
-
 /* One output row: acc and den start at zero, then for each k the row of B is
- * scaled by A[i][k] and added (signed into C, absolute into D). */
+ * scaled by A[i][k] and added (signed into C, absolute into D).  Row k of B
+ * comes from the decoded copy when there is one (fp16 and 8-bit patterns,
+ * whose decode is the slow part, and any B stored transposed; the copy holds
+ * exactly the values load_b_stored returns), else straight from storage. */
 static void one_row(const job_t *j, int64_t i, double *crow, double *drow)
 {
     for (int64_t n = 0; n < j->N; ++n) { crow[n] = 0.0; drow[n] = 0.0; }
@@ -215,10 +210,11 @@ static void one_row(const job_t *j, int64_t i, double *crow, double *drow)
 #ifdef ORACLE_MUTANT_DROP_LAST_K
     if (kend > 0) kend -= 1;
 #endif
+    const double *bd = j->Bd;
     for (int64_t k = 0; k < kend; ++k) {
         double a = load_a(j, i, k);
         for (int64_t n = 0; n < j->N; ++n) {
-            double p = a * load_b(j, k, n);
+            double p = a * (bd ? bd[k * j->N + n] : load_b_stored(j, k, n));
             crow[n] += p;
 #ifdef ORACLE_MUTANT_SIGNED_D
             drow[n] += p;
