@@ -61,6 +61,7 @@ const KernelInfo kKernels[] = {
     {"mfma_fp8_direct256x128", kFp8, launch_mfma_fp8_direct256x128, supports_mfma_fp8_direct, true},
     {"skinny_fp8", kFp8, launch_skinny_fp8, supports_skinny_fp8, true},
     {"mfma_bf16_direct64", kBF16, launch_mfma_bf16_direct64, supports_mfma_bf16_direct, true},
+    {"mfma_bf16_wsplit64", kBF16, launch_mfma_bf16_wsplit, supports_mfma_bf16_wsplit, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -240,6 +241,9 @@ int select_bf16_direct(const Problem &p)
     const int64_t t128 = ceil_div(p.M, 128) * ceil_div(p.N, 128) * p.batch;
     if (t128 < kCUs) {
         const int64_t t64 = ceil_div(p.M, 64) * ceil_div(p.N, 64) * p.batch;
+        // A long K over at most one 64 x 64 tile per CU: split K over the
+        // waves of each tile (four MFMAs per slice instead of one).
+        if (p.batch == 1 && p.K >= 2048 && t64 <= kCUs) return kernel_id("mfma_bf16_wsplit64");
         const int64_t c64 = ceil_div(t64, kCUs) * 64 * 64 * 1000 / BF16_DIRECT_64;
         const int64_t c128 = 128 * 128 * 1000 / 410;
         if (t64 <= 5 * kCUs && c64 < c128) return kernel_id("mfma_bf16_direct64");

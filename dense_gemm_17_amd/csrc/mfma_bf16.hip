@@ -1029,6 +1029,228 @@ void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__r
         store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
 }
 
+// ---- small outputs over a long K: the K range split over the waves -----------
+// A weight gradient (a d_in x d_out output summed over every token of a
+// training step) has few output tiles and a long K; with one 32 x 32 block
+// per wave the 64 x 64 tile above does one MFMA per slice between its
+// reads, loads and barrier.  Here each wave of a 64 x 64 work-group
+// computes the whole tile (2 x 2 blocks, four MFMAs per slice) over every
+// fourth 32-deep K tile, through a 4-stage LDS ring of its own (8 KiB per
+// stage, filled by its own LDS-direct loads): the waves never wait for each
+// other until the end, where waves 1-3 leave their partial tiles in LDS
+// and wave 0 adds them in the order 0, 1, 2, 3 (deterministic) and writes
+// C.  Staging, swizzles and reads per factor layout as in the tiles above
+// (rows of K: 4 chunks per row, a_swz; rows of 64 M or N: 8 chunks,
+// b_swzc<8>, transposing reads).
+constexpr int WS_STAGE = 8192;                      // bytes per stage: A then B, 4 KiB each
+constexpr int WS_RING = DSTAGES * WS_STAGE;         // bytes per wave
+
+template <bool TA, bool TB>
+struct WsCtx {
+    uint32_t a_voff[4], b_voff[4];
+    const char *abase, *bbase;
+    int64_t a_kstride, b_kstride;
+    uint32_t ring;                                  // LDS byte address of this wave's ring
+    uint32_t rdA[TA ? 2 : 2], rdB[2];               // A: per block (TA) or slice; B: per block (!TB) or slice
+};
+
+template <bool TA, bool TB>
+__device__ __forceinline__ void ws_loads(const WsCtx<TA, TB> &x, int stage, int64_t kt, int l)
+{
+    const uint32_t st = x.ring + stage * WS_STAGE;
+    if (l < 4) lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride, st + l * 1024);
+    else lds_direct_load16(x.b_voff[l - 4], x.bbase + kt * x.b_kstride, st + 4096 + (l - 4) * 1024);
+}
+
+// Read j of slice s from stage `st` (a byte pointer into this wave's ring).
+// A: j < nA (one 16-byte read per block, or two transposing reads); then B.
+template <bool TA, bool TB>
+__device__ __forceinline__ void ws_read(Frag16<128, 128, TA, TB> &f, const char *st,
+                                        const WsCtx<TA, TB> &x, int s, int j)
+{
+    constexpr int nA = TA ? 4 : 2;
+    if (j < nA) {
+        if constexpr (TA) {
+            const int mb = j >> 1, upper = j & 1;
+            const bf16x4 v = read_tr4(st + x.rdA[mb] + s * (16 * 64 * 2) + upper * (4 * 64 * 2));
+            if (upper) f.ahi[mb] = v;
+            else f.alo[mb] = v;
+        } else {
+            const u16x8 v = *reinterpret_cast<const u16x8 *>(st + x.rdA[s] + j * 2048);
+            f.a[j] = __builtin_bit_cast(bf16x8, v);
+        }
+    } else if constexpr (TB) {
+        const u16x8 v = *reinterpret_cast<const u16x8 *>(st + 4096 + x.rdB[s] + (j - nA) * 2048);
+        f.b[j - nA] = __builtin_bit_cast(bf16x8, v);
+    } else {
+        const int nb = (j - nA) >> 1, upper = (j - nA) & 1;
+        const bf16x4 v = read_tr4(st + 4096 + x.rdB[nb] + s * (16 * 64 * 2) + upper * (4 * 64 * 2));
+        if (upper) f.bhi[nb] = v;
+        else f.blo[nb] = v;
+    }
+}
+
+template <bool kF16, bool TA, bool TB>
+__device__ __forceinline__ void ws_phase(f32x16 (&acc)[2][2], const Frag16<128, 128, TA, TB> &cur,
+                                         Frag16<128, 128, TA, TB> &nxt, const char *rst,
+                                         const WsCtx<TA, TB> &x, int s_next, int lstage,
+                                         int64_t kload, bool loads)
+{
+    constexpr int R = (TA ? 4 : 2) + (TB ? 2 : 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int mb = q >> 1, nb = q & 1;
+        bf16x8 a, b;
+        if constexpr (TA) a = __builtin_shufflevector(cur.alo[mb], cur.ahi[mb], 0, 1, 2, 3, 4, 5, 6, 7);
+        else a = cur.a[mb];
+        if constexpr (TB) b = cur.b[nb];
+        else b = __builtin_shufflevector(cur.blo[nb], cur.bhi[nb], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[mb][nb] = mfma16<kF16>(a, b, acc[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (r * 4 / R == q) ws_read(nxt, rst, x, s_next, r);
+        if (loads) {
+            ws_loads(x, lstage, kload, 2 * q);
+            ws_loads(x, lstage, kload, 2 * q + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool TA, bool TB, bool kF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_bf16_wsplit_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
+                             int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
+                             float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * WS_RING];
+
+    const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+    const int64_t m0 = t.tm * 64, n0 = t.tn * 64;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, c = lane & 31, i16 = lane & 15, nhalf = (lane >> 4) & 1;
+
+    WsCtx<TA, TB> x;
+    x.ring = lds_offset(lds) + wave * WS_RING;
+    x.abase = static_cast<const char *>(uniform_ptr(TA ? A + m0 : A + m0 * lda));
+    x.bbase = static_cast<const char *>(uniform_ptr(TB ? B + n0 * ldb : B + n0));
+    x.a_kstride = uniform_i64(TA ? DBK * lda * 2 : DBK * 2);
+    x.b_kstride = uniform_i64(TB ? DBK * 2 : DBK * ldb * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int p = i * 64 + lane;   // 16-byte LDS slot this lane fills (of 256 per factor)
+        if constexpr (TA) {
+            // 32 rows of K, 64 elements of M each (8 chunks); columns past M
+            // re-fetch the last full chunk (M % 8 == 0 here)
+            const int row = p >> 3, slot = p & 7;
+            const int cc = slot ^ b_swzc<8>(row);
+            const int64_t col = (m0 + 8 * cc < M) ? 8 * cc : M - 8 - m0;
+            x.a_voff[i] = static_cast<uint32_t>((row * lda + col) * 2);
+        } else {
+            const int row = p >> 2, slot = p & 3;
+            const int cc = slot ^ a_swz<4>(row);
+            const int64_t r = (m0 + row < M) ? row : M - 1 - m0;
+            x.a_voff[i] = static_cast<uint32_t>((r * lda + 8 * cc) * 2);
+        }
+        if constexpr (TB) {
+            const int row = p >> 2, slot = p & 3;
+            const int cc = slot ^ a_swz<4>(row);
+            const int64_t r = (n0 + row < N) ? row : N - 1 - n0;
+            x.b_voff[i] = static_cast<uint32_t>((r * ldb + 8 * cc) * 2);
+        } else {
+            const int row = p >> 3, slot = p & 7;
+            const int cc = slot ^ b_swzc<8>(row);
+            const int64_t col = (n0 + 8 * cc < N) ? 8 * cc : N - 8 - n0;
+            x.b_voff[i] = static_cast<uint32_t>((row * ldb + col) * 2);
+        }
+    }
+    const int aswz = a_swz<4>(c);
+    const int tswz = b_swzc<8>(i16 >> 2);
+    if constexpr (TA) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int m = mb * 32 + nhalf * 16 + 4 * (i16 & 3);
+            x.rdA[mb] = (8 * h + (i16 >> 2)) * 64 * 2 + (((m >> 3) ^ tswz) << 4) + (m & 7) * 2;
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) x.rdA[s] = c * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+    }
+    if constexpr (TB) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) x.rdB[s] = c * DBK * 2 + (((2 * s + h) ^ aswz) << 4);
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int n = nb * 32 + nhalf * 16 + 4 * (i16 & 3);
+            x.rdB[nb] = (8 * h + (i16 >> 2)) * 64 * 2 + (((n >> 3) ^ tswz) << 4) + (n & 7) * 2;
+        }
+    }
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // This wave's K tiles: wave, wave + 4, ...; past the last, the last one
+    // is re-fetched (landed, never used).
+    const int64_t ktiles = K / DBK;
+    const int64_t nj = ktiles > wave ? (ktiles - wave + 3) / 4 : 0;
+    auto ktile = [&](int64_t j) {
+        const int64_t kt = wave + 4 * j;
+        return kt < ktiles ? kt : ktiles - 1;
+    };
+    auto stage_ptr = [&](int64_t j) {
+        return reinterpret_cast<const char *>(lds) + wave * WS_RING + (j % DSTAGES) * WS_STAGE;
+    };
+    constexpr int P = 8;                 // loads per tile
+    constexpr int R = (TA ? 4 : 2) + (TB ? 2 : 4);
+    if (nj > 0) {
+#pragma unroll
+        for (int st = 0; st < DSTAGES - 1; ++st)
+#pragma unroll
+            for (int l = 0; l < P; ++l) ws_loads(x, st, ktile(st), l);
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"((DSTAGES - 2) * P) : "memory");
+        Frag16<128, 128, TA, TB> f0, f1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) ws_read(f0, stage_ptr(0), x, 0, r);
+        for (int64_t j = 0; j < nj; ++j) {
+            const int64_t jn = j + DSTAGES - 1;
+            ws_phase<kF16>(acc, f0, f1, stage_ptr(j), x, 1, static_cast<int>(jn % DSTAGES),
+                           ktile(jn), true);
+            asm volatile("s_waitcnt vmcnt(%0)" : : "n"((DSTAGES - 2) * P) : "memory");
+            ws_phase<kF16>(acc, f1, f0, stage_ptr(j + 1), x, 0, 0, 0, false);
+        }
+    }
+    // Every wave's loads landed and LDS reads done: the rings are free.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float *part = reinterpret_cast<float *>(lds);   // waves 1-3: [w - 1][block][reg][lane]
+    if (wave > 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                part[(((wave - 1) * 4 + b) * 16 + r) * 64 + lane] = acc[b >> 1][b & 1][r];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wave != 0) return;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float v = acc[b >> 1][b & 1][r];
+#pragma unroll
+            for (int w = 0; w < 3; ++w) v += part[((w * 4 + b) * 16 + r) * 64 + lane];
+            acc[b >> 1][b & 1][r] = v;
+        }
+    store_c(acc, C, ldc, M, N, m0, n0, 0, 0, lane);
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
@@ -1111,6 +1333,34 @@ hipError_t launch_direct(const Problem &p, hipStream_t s)
 hipError_t launch_mfma_bf16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256>(p, s); }
 hipError_t launch_mfma_bf16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128>(p, s); }
 hipError_t launch_mfma_bf16_direct64(const Problem &p, hipStream_t s) { return launch_direct<64, 64>(p, s); }
+
+// The K-split-over-waves 64 x 64 tile: the LDS-direct layout conditions, a
+// single product.
+bool supports_mfma_bf16_wsplit(const Problem &p)
+{
+    return p.batch == 1 && supports_mfma_bf16_direct(p);
+}
+
+namespace {
+template <bool TA, bool TB>
+void launch_wsplit_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
+{
+    hipLaunchKernelGGL((mfma_bf16_wsplit_kernel<TA, TB, false>), dim3(static_cast<uint32_t>(tm * tn)),
+                       dim3(kThreads), 0, s, p.M, p.N, p.K, static_cast<const uint16_t *>(p.A),
+                       p.lda, static_cast<const uint16_t *>(p.B), p.ldb, p.C, p.ldc, tm, tn);
+}
+}  // namespace
+
+hipError_t launch_mfma_bf16_wsplit(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + 63) / 64, tn = (p.N + 63) / 64;
+    if (tm * tn > kMaxBlocks || !supports_mfma_bf16_wsplit(p)) return hipErrorInvalidValue;
+    if (p.ta && p.tb) launch_wsplit_layout<true, true>(p, s, tm, tn);
+    else if (p.ta) launch_wsplit_layout<true, false>(p, s, tm, tn);
+    else if (p.tb) launch_wsplit_layout<false, true>(p, s, tm, tn);
+    else launch_wsplit_layout<false, false>(p, s, tm, tn);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_f16_direct(const Problem &p, hipStream_t s) { return launch_direct<256, 256, true>(p, s); }
 

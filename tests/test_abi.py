@@ -247,6 +247,8 @@ def test_plan_batched_tile_choice():
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 384, 1152, 16384, 1)) == \
         "mfma_f32_batched_splitk"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 16384, 1)) == \
+        "mfma_bf16_wsplit64"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 1024, 1)) == \
         "mfma_bf16_direct64"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 0, 0, 2048, 2048, 8192, 1)) == \
         "mfma_bf16_direct128"

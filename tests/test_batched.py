@@ -34,7 +34,8 @@ LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mf
            "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64"]
 GENERAL["f16"] = ["mfma_f16_batched", "mfma_f16_batched128", "mfma_f16_batched_splitk"]
 ALL = {"f32": GENERAL["f32"] + LDS_F32,
-       "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128", "mfma_bf16_direct64"],
+       "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128", "mfma_bf16_direct64",
+                                  "mfma_bf16_wsplit64"],
        "f16": GENERAL["f16"] + ["mfma_f16_direct", "mfma_f16_direct128"]}
 TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 DTYPES = ["f32", "bf16", "f16"]
@@ -133,6 +134,18 @@ def test_small_integer_exact(dtype, kernel, ta, tb):
                                           (8, 16, 32, 5, 49), (264, 136, 288, 2, 50)]]
     if not any(ran):
         pytest.skip(f"{kernel} takes none of these layouts")
+
+
+@pytest.mark.parametrize("ta,tb", TRANS)
+def test_wsplit64_k_split_over_waves_exact(ta, tb):
+    # the bf16 64 x 64 tile whose waves take every fourth K tile: a single
+    # product, K tile counts that leave the waves unequal shares (65 tiles)
+    # or none at all (2 tiles), ragged tile edges, the weight-gradient shape
+    kernel = "mfma_bf16_wsplit64"
+    ran = [exact_case("bf16", kernel, ta, tb, M, N, K, 1, seed)
+           for (M, N, K, seed) in [(384, 1152, 4096, 61), (200, 136, 2080, 62), (72, 64, 64, 63),
+                                   (8, 8, 32, 64), (520, 264, 2048, 65)]]
+    assert all(ran), "the kernel refused a layout it takes"
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
