@@ -243,6 +243,74 @@ def test_skinny_configurations_exact(dtype):
                 assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
 
 
+# Skinny products with 5-16 rows over long K: the row-split pairs and the
+# 16-row work-groups, strip widths from 16 to 32 columns, K with a partial
+# last block, both the LDS copy of A (aligned rows that fit) and reads of A
+# from the caches (A offset by one element).
+LONG_K_CASES = [(5, 4096, 4096), (7, 4096, 4096), (8, 1000, 1027), (9, 2050, 2048),
+                (12, 4100, 1536), (16, 1024, 1032)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_skinny_long_k_exact(dtype):
+    tdt = TDT[dtype]
+    lo, hi = (-4, 4) if dtype == "f32" else (-8, 8)
+    gen = workloads.generator(84)
+    for (M, N, K) in LONG_K_CASES:
+        A = workloads.small_int((M, K + 4), lo, hi, gen, tdt)
+        B = workloads.small_int((K, N), lo, hi, gen, tdt)
+        exact = (A[:, :K].to(torch.int64) @ B.to(torch.int64)).to(torch.float64).numpy()
+        exact_un = (A[:, 1:K + 1].to(torch.int64) @ B.to(torch.int64)).to(torch.float64).numpy()
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        for a, ref, tag in ((Ad[:, :K].contiguous(), exact, "aligned"),
+                            (Ad[:, 1:K + 1], exact_un, "A offset one element")):
+            say(f"[skinny long K] {dtype} {M}x{N}x{K} {tag}")
+            C = run(a, Bd, f"skinny_{dtype}")
+            bad = np.argwhere(C.cpu().numpy().astype(np.float64) != ref)
+            assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
+
+
+def test_skinny_streams_and_graphs():
+    # Calls on two streams with no synchronization between them, then a
+    # captured graph replayed between eager calls: every output exact, and
+    # on random operands every replay bit-identical to the eager result.
+    gen = workloads.generator(85)
+    M, N, K = 7, 4096, 4096
+    As = [workloads.small_int((M, K), -4, 4, gen).to(DEV) for _ in range(6)]
+    Bs = [workloads.small_int((K, N), -4, 4, gen).to(DEV) for _ in range(2)]
+    refs = [(a.cpu().to(torch.int64) @ b.cpu().to(torch.int64)).to(torch.float32)
+            for a in As for b in Bs]
+    streams = [torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)]
+    outs = [torch.empty((M, N), device=DEV) for _ in refs]
+    torch.cuda.synchronize()
+    for i in range(len(refs)):
+        st = streams[i % 2]
+        with torch.cuda.stream(st):
+            g.gemm(As[i // 2], Bs[i % 2], out=outs[i])
+    torch.cuda.synchronize()
+    say("[skinny] two streams")
+    for i, ref in enumerate(refs):
+        assert torch.equal(outs[i].cpu(), ref), f"call {i}"
+    Ar = workloads.draw((M, K), ("normal", 1.0), gen).to(DEV)
+    Br = workloads.draw((K, N), ("normal", 1.0), gen).to(DEV)
+    eager = g.gemm(Ar, Br)
+    Cg = torch.empty((M, N), device=DEV)
+    st = streams[0]
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            g.gemm(Ar, Br, out=Cg)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        Cg.fill_(float("nan"))
+        graph.replay()
+        again = g.gemm(Ar, Br)
+        torch.cuda.synchronize()
+        say(f"[skinny] graph replay {rep}")
+        assert torch.equal(Cg, eager) and torch.equal(again, eager)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_ones_exact(dtype):
     """A = B = ones gives K everywhere; A = ones with integer B gives every
