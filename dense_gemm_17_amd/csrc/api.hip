@@ -47,14 +47,12 @@ const KernelInfo kKernels[] = {
     {"mfma_bf16_batched", kBF16, launch_mfma_bf16_batched, supports_any, true},
     {"mfma_bf16_batched128", kBF16, launch_mfma_bf16_batched128, supports_any, true},
     {"mfma_f32_batched_splitk", kF32, launch_mfma_f32_batched_splitk, supports_any, true},
-    {"mfma_bf16_batched_splitk", kBF16, launch_mfma_bf16_batched_splitk, supports_any, true},
     {"naive_f16", kF16, launch_naive_f16, supports_any},
     {"skinny_f16", kF16, launch_skinny_f16, supports_skinny},
     {"mfma_f16_direct", kF16, launch_mfma_f16_direct, supports_mfma_bf16_direct, true},
     {"mfma_f16_direct128", kF16, launch_mfma_f16_direct128, supports_mfma_bf16_direct, true},
     {"mfma_f16_batched", kF16, launch_mfma_f16_batched, supports_any, true},
     {"mfma_f16_batched128", kF16, launch_mfma_f16_batched128, supports_any, true},
-    {"mfma_f16_batched_splitk", kF16, launch_mfma_f16_batched_splitk, supports_any, true},
     {"mfma_fp8_direct128", kFp8, launch_mfma_fp8_direct128, supports_mfma_fp8_direct, true},
     {"mfma_fp8_batched", kFp8, launch_mfma_fp8_batched, supports_fp8_unscaled, true},
     {"mfma_fp8_batched128", kFp8, launch_mfma_fp8_batched128, supports_fp8, true},
@@ -262,10 +260,11 @@ int select_general(const Problem &p)
     // 384 x 1152 x 16384: 49 vs 9.8 TFLOP/s; 6 x 256 x 64 x 256: 5.1 vs 7.6
     // us for the 64 x 64 tile).  With a short K there is nothing to split
     // and the 64 x 64 LDS-direct tile wins (6 heads of 256 x 256 x 64
-    // scores: 4.1 vs 7.4 us).  The bf16 twin is kept for the test hook only:
-    // with a transposed factor its lanes need eight 2-byte loads per operand
-    // per MFMA and it loses to the 128 x 128 tile (23 vs 63 TFLOP/s on the
-    // same shape).
+    // scores: 4.1 vs 7.4 us).  bf16 and fp16 have no such kernel: with a
+    // transposed factor a lane would need eight 2-byte loads per operand per
+    // MFMA (a version measured 23 vs 63 TFLOP/s for the 128 x 128 tile);
+    // their single products split K over the waves of 64 x 64 LDS-direct
+    // tiles instead.
     if (p.dtype == kF32 && p.K >= 256 && ceil_div(p.M, 128) * ceil_div(p.N, 128) * p.batch < kCUs)
         return kernel_id("mfma_f32_batched_splitk");
     // fp32 layouts the LDS-direct tiles take (16-byte aligned rows, K % 16

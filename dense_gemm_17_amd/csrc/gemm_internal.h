@@ -102,12 +102,10 @@ hipError_t launch_mfma_f32_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32_batched_splitk(const Problem &p, hipStream_t s);
-hipError_t launch_mfma_bf16_batched_splitk(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f16_direct(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f16_direct128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f16_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f16_batched128(const Problem &p, hipStream_t s);
-hipError_t launch_mfma_f16_batched_splitk(const Problem &p, hipStream_t s);
 hipError_t launch_skinny_f16(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_batched128(const Problem &p, hipStream_t s);

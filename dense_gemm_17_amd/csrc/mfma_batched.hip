@@ -641,7 +641,7 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
 }  // namespace bf
 
 // ---------------------------------------------------------------------------
-// Split-K for products whose output is too small to fill the chip with
+// fp32 split-K for products whose output is too small to fill the chip with
 // tiles but whose K is long: the weight gradient X^T dY of a layer is a
 // d_in x d_out output summed over every token of the batch (16384 for the
 // GPT above).  One 32 x 32 tile of C per work-group; its four waves take the
@@ -656,8 +656,8 @@ void batched_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict_
 // Lane (h, c) supplies row c of the tile's A block and column c of its B
 // block.  Along a stored row of K (A as written, B transposed) a lane's
 // values are one 16-byte load when the rows allow it; across stored rows
-// (A transposed, B as written) they are 4-byte (fp32) or 2-byte (bf16)
-// loads that are coalesced over the 32 lanes of a half-wave.
+// (A transposed, B as written) they are 4-byte loads that are coalesced
+// over the 32 lanes of a half-wave.
 
 namespace sk {
 
@@ -778,89 +778,6 @@ __global__ __launch_bounds__(64 * kSkWaves) void f32_kernel(
     reduce_store<kW>(red, acc, wave, lane, C, ldc, M, N, m0, n0);
 }
 
-// bf16 (v_mfma_f32_32x32x16_bf16): group g is k = 16g .. 16g+15, lane half h
-// carries the eight k = 16g + 8h .. 16g + 8h + 7.
-__device__ __forceinline__ uint16_t masked16(uint16_t x, bool keep) { return keep ? x : 0; }
-
-template <bool TA, bool TB, bool kVecA, bool kVecB, bool kF16>
-__global__ __launch_bounds__(kThreads) void bf16_kernel(
-    int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A, int64_t lda, int64_t sa,
-    const uint16_t *__restrict__ B, int64_t ldb, int64_t sb, float *__restrict__ C, int64_t ldc,
-    int64_t sc, int64_t batch, int64_t tiles_m, int64_t tiles_n)
-{
-    constexpr int kU = 4;
-    __shared__ float red[4 * 32 * kPad];
-    const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
-    A += t.b * sa;
-    B += t.b * sb;
-    C += t.b * sc;
-    const int64_t m0 = t.tm * 32, n0 = t.tn * 32;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = lane >> 5, c = lane & 31;
-    const bool row_ok = m0 + c < M, col_ok = n0 + c < N;
-    const int64_t row = row_ok ? m0 + c : 0, col = col_ok ? n0 + c : 0;
-
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-
-    const int64_t groups = (K + 15) / 16;
-    auto load = [&](int64_t g0, u16x8 (&a)[kU], u16x8 (&b)[kU]) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-            const int64_t k = 16 * (g0 + 4 * u) + 8 * h;
-            if constexpr (!TA && kVecA) {
-                // K % 8 == 0 here, so the eight k are all in range or all out
-                const u16x8 v = *reinterpret_cast<const u16x8 *>(A + row * lda + (k < K ? k : K - 8));
-                const bool keep = row_ok && k < K;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[u][e] = masked16(v[e], keep);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int64_t kk = clampk(k + e, K);
-                    const uint16_t v = TA ? A[kk * lda + row] : A[row * lda + kk];
-                    a[u][e] = masked16(v, row_ok && k + e < K);
-                }
-            }
-            if constexpr (TB && kVecB) {
-                const u16x8 v = *reinterpret_cast<const u16x8 *>(B + col * ldb + (k < K ? k : K - 8));
-                const bool keep = col_ok && k < K;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) b[u][e] = masked16(v[e], keep);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int64_t kk = clampk(k + e, K);
-                    const uint16_t v = TB ? B[col * ldb + kk] : B[kk * ldb + col];
-                    b[u][e] = masked16(v, col_ok && k + e < K);
-                }
-            }
-        }
-    };
-    auto mfmas = [&](const u16x8 (&a)[kU], const u16x8 (&b)[kU]) {
-#pragma unroll
-        for (int u = 0; u < kU; ++u)
-            acc = mfma16<kF16>(__builtin_bit_cast(bf16x8, a[u]), __builtin_bit_cast(bf16x8, b[u]),
-                               acc);
-    };
-    u16x8 a0[kU], a1[kU], b0[kU], b1[kU];
-    int64_t g0 = wave;
-    if (g0 < groups) load(g0, a0, b0);
-    while (g0 < groups) {
-        const int64_t g1 = g0 + 4 * kU;
-        if (g1 < groups) load(g1, a1, b1);
-        mfmas(a0, b0);
-        if (g1 >= groups) break;
-        const int64_t g2 = g1 + 4 * kU;
-        if (g2 < groups) load(g2, a0, b0);
-        mfmas(a1, b1);
-        g0 = g2;
-    }
-    reduce_store(red, acc, wave, lane, C, ldc, M, N, m0, n0);
-}
-
 }  // namespace sk
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -966,24 +883,19 @@ hipError_t launch_fp8(const Problem &p, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename T, bool TA, bool TB, bool VA, bool VB, bool kF16 = false>
+template <typename T, bool TA, bool TB, bool VA, bool VB>
 void launch_sk_layout(const Problem &p, uint32_t blocks, int64_t tm, int64_t tn, hipStream_t s)
 {
     const auto *A = static_cast<const T *>(p.A);
     const auto *B = static_cast<const T *>(p.B);
-    if constexpr (sizeof(T) == 4)
-        hipLaunchKernelGGL((sk::f32_kernel<TA, TB, VA, VB>), dim3(blocks), dim3(64 * sk::kSkWaves), 0, s,
-                           p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc,
-                           p.batch, tm, tn);
-    else
-        hipLaunchKernelGGL((sk::bf16_kernel<TA, TB, VA, VB, kF16>), dim3(blocks), dim3(kThreads), 0, s,
-                           p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc,
-                           p.batch, tm, tn);
+    hipLaunchKernelGGL((sk::f32_kernel<TA, TB, VA, VB>), dim3(blocks), dim3(64 * sk::kSkWaves), 0, s,
+                       p.M, p.N, p.K, A, p.lda, p.sa, B, p.ldb, p.sb, p.C, p.ldc, p.sc, p.batch,
+                       tm, tn);
 }
 
 // The vector load exists only along a stored row of K (A as written, B
 // transposed); it needs 16-byte aligned rows and K a multiple of the vector.
-template <typename T, bool kF16 = false>
+template <typename T>
 hipError_t launch_splitk(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + 31) / 32, tn = (p.N + 31) / 32;
@@ -994,18 +906,18 @@ hipError_t launch_splitk(const Problem &p, hipStream_t s)
     const bool va = !p.ta && kv && aligned16(p.A) && p.lda % v == 0 && p.sa % v == 0;
     const bool vb = p.tb && kv && aligned16(p.B) && p.ldb % v == 0 && p.sb % v == 0;
     if (p.ta && p.tb) {
-        if (vb) launch_sk_layout<T, true, true, false, true, kF16>(p, blocks, tm, tn, s);
-        else launch_sk_layout<T, true, true, false, false, kF16>(p, blocks, tm, tn, s);
+        if (vb) launch_sk_layout<T, true, true, false, true>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, true, true, false, false>(p, blocks, tm, tn, s);
     } else if (p.ta) {
-        launch_sk_layout<T, true, false, false, false, kF16>(p, blocks, tm, tn, s);
+        launch_sk_layout<T, true, false, false, false>(p, blocks, tm, tn, s);
     } else if (p.tb) {
-        if (va && vb) launch_sk_layout<T, false, true, true, true, kF16>(p, blocks, tm, tn, s);
-        else if (va) launch_sk_layout<T, false, true, true, false, kF16>(p, blocks, tm, tn, s);
-        else if (vb) launch_sk_layout<T, false, true, false, true, kF16>(p, blocks, tm, tn, s);
-        else launch_sk_layout<T, false, true, false, false, kF16>(p, blocks, tm, tn, s);
+        if (va && vb) launch_sk_layout<T, false, true, true, true>(p, blocks, tm, tn, s);
+        else if (va) launch_sk_layout<T, false, true, true, false>(p, blocks, tm, tn, s);
+        else if (vb) launch_sk_layout<T, false, true, false, true>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, false, true, false, false>(p, blocks, tm, tn, s);
     } else {
-        if (va) launch_sk_layout<T, false, false, true, false, kF16>(p, blocks, tm, tn, s);
-        else launch_sk_layout<T, false, false, false, false, kF16>(p, blocks, tm, tn, s);
+        if (va) launch_sk_layout<T, false, false, true, false>(p, blocks, tm, tn, s);
+        else launch_sk_layout<T, false, false, false, false>(p, blocks, tm, tn, s);
     }
     return hipGetLastError();
 }
@@ -1015,16 +927,6 @@ hipError_t launch_splitk(const Problem &p, hipStream_t s)
 hipError_t launch_mfma_f32_batched_splitk(const Problem &p, hipStream_t s)
 {
     return launch_splitk<float>(p, s);
-}
-
-hipError_t launch_mfma_bf16_batched_splitk(const Problem &p, hipStream_t s)
-{
-    return launch_splitk<uint16_t>(p, s);
-}
-
-hipError_t launch_mfma_f16_batched_splitk(const Problem &p, hipStream_t s)
-{
-    return launch_splitk<uint16_t, true>(p, s);
 }
 
 hipError_t launch_mfma_f16_batched(const Problem &p, hipStream_t s)

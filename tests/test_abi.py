@@ -202,9 +202,9 @@ GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_ba
                          "mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64",
                          "mfma_f32_direct64", "mfma_f32_narrow128", "mfma_f32_narrow128x64",
                          "mfma_f32_narrow64"),
-                 g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk",
+                 g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128",
                           "mfma_bf16_direct", "mfma_bf16_direct128"),
-                 g.F16: ("mfma_f16_batched", "mfma_f16_batched128", "mfma_f16_batched_splitk",
+                 g.F16: ("mfma_f16_batched", "mfma_f16_batched128",
                          "mfma_f16_direct", "mfma_f16_direct128")}
 
 

@@ -29,10 +29,10 @@ TRANS = [(False, False), (True, False), (False, True), (True, True)]
 # kernels that take every layout, and (fp32) the LDS-direct and narrow-load
 # tiles, which take the layouts their loads allow
 GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk"],
-           "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128", "mfma_bf16_batched_splitk"]}
+           "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128"]}
 LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mfma_f32_direct64",
            "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64"]
-GENERAL["f16"] = ["mfma_f16_batched", "mfma_f16_batched128", "mfma_f16_batched_splitk"]
+GENERAL["f16"] = ["mfma_f16_batched", "mfma_f16_batched128"]
 ALL = {"f32": GENERAL["f32"] + LDS_F32,
        "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128", "mfma_bf16_direct64",
                                   "mfma_bf16_wsplit64"],

@@ -37,7 +37,6 @@ OCCUPANCY_BUDGET = {
     "2bf14batched_kernelILi256ELi256E": 1,
     "2bf14batched_kernelILi128ELi128E": 2,
     "2sk10f32_kernel": 2,
-    "2sk11bf16_kernel": 2,
     "valu_f32_kernel": 3,
     "skinny_kernel": 1,
     "skinny_fp8_kernel": 2,
