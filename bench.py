@@ -151,10 +151,12 @@ def ingest_counters(fetch_dir: str, write_dir: str):
                                   "bytes_per_launch": round(fb + wb), "dispatches": len(f),
                                   "source_digest": source_digest(kernel)}
     with open(TRAFFIC_FILE, "w") as fh:
-        run = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs --copy-calibration"
-        fh.write("# HBM bytes per launch at 8192^3, one rocprofv3 run per counter:\n")
+        run = ("python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-configs "
+               "--copy-calibration --runs 1")
+        fh.write("# Bytes between L2 and the memory fabric per launch at 8192^3 (L2 misses:\n"
+                 "# MALL hits included), one rocprofv3 run per counter:\n")
         for ctr, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-            fh.write(f"#   timeout -s KILL 90 rocprofv3 --pmc {ctr} -d {d} -o pmc "
+            fh.write(f"#   timeout -s KILL 120 rocprofv3 --pmc {ctr} -d {d} -o pmc "
                      f"--output-format csv -- {run}\n")
         fh.write("# then: python bench.py --ingest-counters <fetch dir> <write dir>.\n")
         fh.write("# Each counter is scaled by its reading of a 256 MiB device copy.\n")
