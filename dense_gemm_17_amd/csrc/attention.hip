@@ -69,6 +69,13 @@ struct AttnCfg {
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// x where keep is all ones, +0 where it is zero (a bitwise select, so the
+// load of x stays unconditional).
+__device__ __forceinline__ float masked(float x, uint32_t keep)
+{
+    return __uint_as_float(__float_as_uint(x) & keep);
+}
+
 template <int D, int BN>
 __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs a)
 {
@@ -301,11 +308,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
 // reads its K and V tiles straight from memory into the MFMA operand
 // layout (a lane's 16-byte pieces of its key's row of K; 4-byte values of
 // V, 32 lanes on one row), the next tile's while the current one is
-// computed.  Head width 64.
+// computed (two register sets, one wave per SIMD so that both fit; a single
+// GPT sequence, causal: 11.4 -> 11.0 us).  Head width 64.
 constexpr int kSplitQ = 32;   // queries per work-group
 constexpr int kSplitBN = 32;  // keys per tile
 
-__global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_split_kernel(AttnArgs a)
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attention_fwd_split_kernel(AttnArgs a)
 {
     constexpr int D = 64, DH = D / 2;
     __shared__ float mrg_o[3][D / 32][16][64];   // waves 1..3: output registers by lane
@@ -352,41 +361,30 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_split_kernel(At
 
     // tile t's operands: K row (key t*32 + c), this half's 32 dims; V at
     // keys t*32 + 8 (r/4) + 4 h + r%4, dims 32 d + c (zero past S)
-    f32x4 kf[DH / 4];
-    float vf[16][D / 32];
-    auto load = [&](int t) {
+    auto load = [&](f32x4 (&kf)[DH / 4], float (&vf)[16][D / 32], int t) {
         const int key = t * kSplitBN + c;
         const bool ok = key < S;
+        const uint32_t kkeep = ok ? ~0u : 0u;
         const float *kr = Kp + static_cast<int64_t>(ok ? key : 0) * a.k_ss + h * DH;
 #pragma unroll
         for (int u = 0; u < DH / 4; ++u) {
             const f32x4 v = *reinterpret_cast<const f32x4 *>(kr + 4 * u);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) kf[u][e] = ok ? v[e] : 0.f;
+            for (int e = 0; e < 4; ++e) kf[u][e] = masked(v[e], kkeep);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int vk = t * kSplitBN + 8 * (r >> 2) + 4 * h + (r & 3);
             const bool vok = vk < S;
+            const uint32_t vkeep = vok ? ~0u : 0u;
             const float *vr = Vp + static_cast<int64_t>(vok ? vk : 0) * a.v_ss + c;
 #pragma unroll
-            for (int d = 0; d < D / 32; ++d) vf[r][d] = vok ? vr[32 * d] : 0.f;
+            for (int d = 0; d < D / 32; ++d) vf[r][d] = masked(vr[32 * d], vkeep);
         }
     };
 
     const float sl2 = a.scale_log2;
-    int t = wave;
-    if (t < ntiles) load(t);
-    for (; t < ntiles; t += 4) {
-        f32x4 kc[DH / 4];
-        float vc[16][D / 32];
-#pragma unroll
-        for (int u = 0; u < DH / 4; ++u) kc[u] = kf[u];
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-#pragma unroll
-            for (int d = 0; d < D / 32; ++d) vc[r][d] = vf[r][d];
-        if (t + 4 < ntiles) load(t + 4);
+    auto tile = [&](const f32x4 (&kc)[DH / 4], const float (&vc)[16][D / 32], int t) {
         f32x16 sc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -426,6 +424,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_split_kernel(At
 #pragma unroll
             for (int d = 0; d < D / 32; ++d)
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vc[r][d], sc[r], o[d], 0, 0, 0);
+    };
+
+    // Two register sets: the next tile's operands are loaded into one while
+    // the current tile is computed from the other.  Every load is issued at
+    // a clamped, in-bounds address and zeroed with a bitwise mask, and a
+    // tile index past the end is clamped rather than the load skipped: with
+    // no branch around a load the compiler can count the loads in flight and
+    // leaves the next tile's in flight through this tile's MFMAs.
+    f32x4 k0[DH / 4], k1[DH / 4];
+    float v0[16][D / 32], v1[16][D / 32];
+    auto clampt = [&](int t) { return t < ntiles ? t : ntiles - 1; };   // ntiles >= 1
+    int t = wave;
+    load(k0, v0, clampt(t));
+    for (; t < ntiles; t += 8) {
+        load(k1, v1, clampt(t + 4));
+        __builtin_amdgcn_sched_barrier(0);
+        tile(k0, v0, t);
+        if (t + 4 >= ntiles) break;
+        load(k0, v0, clampt(t + 8));
+        __builtin_amdgcn_sched_barrier(0);
+        tile(k1, v1, t + 4);
     }
     l += __shfl_xor(l, 32);
 

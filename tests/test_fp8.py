@@ -147,13 +147,43 @@ def test_padded_rows_and_guard_band(kernel):
     assert torch.all(ring == 7.0)
 
 
-def test_k_zero_and_empty():
-    A = torch.zeros((33, 0), dtype=torch.float8_e4m3fn, device=DEV)
-    Bt = torch.zeros((17, 0), dtype=torch.float8_e4m3fn, device=DEV)
-    out = torch.full((33, 17), 3.0, device=DEV)
-    g.gemm(A, Bt.t(), out=out)
+def test_skinny_padded_rows_and_guard_band():
+    # the few-row bandwidth kernel (the table's choice up to 4 rows) on rows
+    # K + pad bytes apart, writing into a window of a sentinel-filled buffer
+    M, N, K, pad = 3, 150, 320, 48
+    gen = workloads.generator(35)
+    Aw = randn((M, K + pad), 0, gen)
+    Bw = randn((N, K + pad), 0, gen)
+    big = torch.full((M + 2, N + 8), 7.0, dtype=torch.float32, device=DEV)
+    out = big[1:M + 1, 4:N + 4]
+    a, bt = Aw.to(DEV)[:, :K], Bw.to(DEV)[:, :K]
+    assert g.gemm_kernel_name(g.gemm_plan_batched(
+        g.FP8, 0, 1, M, N, K, 1, a.data_ptr(), a.stride(0), 0, bt.data_ptr(), bt.stride(0), 0,
+        out.data_ptr(), out.stride(0), 0)) == "skinny_fp8"
+    say("fp8 padded skinny_fp8")
+    g.gemm(a, bt.t(), out=out)
     torch.cuda.synchronize()
-    assert torch.all(out == 0)
+    assert g.gemm_kernel_name(g.gemm_last_kernel()) == "skinny_fp8"
+    Cref, D = oracle.gemm_fp8_batched(workloads.fp8_bits(Aw[:, :K].contiguous()),
+                                      workloads.fp8_bits(Bw[:, :K].contiguous()), 0, 0, False, True)
+    e, at, _ = oracle.normalized_error(out.cpu().numpy(), Cref, D)
+    assert e <= GATE, (e, at)
+    ring = big.clone()
+    ring[1:M + 1, 4:N + 4] = 7.0
+    assert torch.all(ring == 7.0)
+
+
+def test_k_zero_and_empty():
+    # K = 0 with few rows (the shape the bandwidth kernel takes at K > 0):
+    # C is the empty sum
+    for M in (1, 4, 33):
+        A = torch.zeros((M, 0), dtype=torch.float8_e4m3fn, device=DEV)
+        Bt = torch.zeros((17, 0), dtype=torch.float8_e4m3fn, device=DEV)
+        out = torch.full((M, 17), 3.0, device=DEV)
+        g.gemm(A, Bt.t(), out=out)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0), M
+
     empty = g.gemm(torch.zeros((0, 64), dtype=torch.float8_e4m3fn, device=DEV),
                    torch.zeros((5, 64), dtype=torch.float8_e4m3fn, device=DEV).t())
     assert empty.shape == (0, 5)
