@@ -44,6 +44,8 @@
 // Under the causal mask a work-group visits only the key tiles up to its
 // last query and a wave skips the 32-key halves past its own last query;
 // work-groups with the most keys are launched first.
+#include <type_traits>
+
 #include "gemm_internal.h"
 
 namespace mi355gemm {
@@ -128,6 +130,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
     float m = neg_inf();     // running maximum (base-2 domain), shared by the lane pair
     float l = 0.f;           // this lane's part of the running sum
 
+    // Tile t's rows of K and V: loaded raw into registers (rows past S read
+    // row 0), zeroed past S only when written to LDS, so nothing uses the
+    // loaded values before then and the loads stay in flight through the
+    // tile computed meanwhile.
     f32x4 kreg[C::kLoads], vreg[C::kLoads];
     auto gload = [&](int64_t t) {
 #pragma unroll
@@ -135,32 +141,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
             const int f = threadIdx.x + kAttnThreads * i;
             const int row = f / (D / 4), col = (f % (D / 4)) * 4;
             const int64_t key = t * BN + row;
-            const bool ok = key < S;
-            const int64_t kk = ok ? key : 0;
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(Kp + kk * a.k_ss + col);
-            const f32x4 vv = *reinterpret_cast<const f32x4 *>(Vp + kk * a.v_ss + col);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kreg[i][e] = ok ? kv[e] : 0.f;
-                vreg[i][e] = ok ? vv[e] : 0.f;
-            }
+            const int64_t kk = key < S ? key : 0;
+            kreg[i] = *reinterpret_cast<const f32x4 *>(Kp + kk * a.k_ss + col);
+            vreg[i] = *reinterpret_cast<const f32x4 *>(Vp + kk * a.v_ss + col);
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int buf, int64_t t) {
         float *Ks = lds + buf * C::kStage;
         float *Vs = Ks + BN * C::KS;
 #pragma unroll
         for (int i = 0; i < C::kLoads; ++i) {
             const int f = threadIdx.x + kAttnThreads * i;
             const int row = f / (D / 4), col = (f % (D / 4)) * 4;
-            *reinterpret_cast<f32x4 *>(Ks + row * C::KS + col) = kreg[i];
-            *reinterpret_cast<f32x4 *>(Vs + row * C::VS + col) = vreg[i];
+            const uint32_t keep = t * BN + row < S ? ~0u : 0u;
+            f32x4 kv, vv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kv[e] = masked(kreg[i][e], keep);
+                vv[e] = masked(vreg[i][e], keep);
+            }
+            *reinterpret_cast<f32x4 *>(Ks + row * C::KS + col) = kv;
+            *reinterpret_cast<f32x4 *>(Vs + row * C::VS + col) = vv;
         }
     };
 
     if (ntiles > 0) {
         gload(0);
-        lstore(0);
+        lstore(0, 0);
         if (ntiles > 1) gload(1);
     }
     __syncthreads();
@@ -170,37 +177,37 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
         const float *Ks = lds + (t & 1) * C::kStage;
         const float *Vs = Ks + BN * C::KS;
         const int64_t k0 = t * BN;
-        if (k0 < wend) {
-            // 1. scores, transposed: s[sb] holds keys k0 + 32 sb + (8 (r/4) + 4 h + r%4)
-            //    for query c of this wave.  The 32-key halves the wave sees
-            //    (both but on its diagonal tile) run as independent MFMA
-            //    chains, interleaved.
+        // One tile for this wave: kAll when the wave sees every 32-key half
+        // of it (every tile but the causal diagonal), so that the half loops
+        // carry no per-MFMA branches; else only the halves before wend.
+        auto process = [&](auto all_tag) {
+            constexpr bool kAll = decltype(all_tag)::value;
+            // 1. scores, transposed: s[sb] holds keys k0 + 32 sb + (8 (r/4) +
+            //    4 h + r%4) for query c of this wave; the halves run as
+            //    independent MFMA chains, interleaved.
             f32x16 s[BN / 32];
 #pragma unroll
             for (int sb = 0; sb < BN / 32; ++sb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-            const bool all_halves = k0 + BN <= wend;
+            if constexpr (kAll) {
 #pragma unroll
-            for (int u = 0; u < C::DH / 4; ++u) {
-                f32x4 kv[BN / 32];
+                for (int u = 0; u < C::DH / 4; ++u) {
+                    f32x4 kv[BN / 32];
 #pragma unroll
-                for (int sb = 0; sb < BN / 32; ++sb)
-                    if (sb == 0 || all_halves)
+                    for (int sb = 0; sb < BN / 32; ++sb)
                         kv[sb] = *reinterpret_cast<const f32x4 *>(Ks + (32 * sb + c) * C::KS +
                                                                   h * C::DH + 4 * u);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                    for (int e = 0; e < 4; ++e)
 #pragma unroll
-                    for (int sb = 0; sb < BN / 32; ++sb)
-                        if (sb == 0 || all_halves)
+                        for (int sb = 0; sb < BN / 32; ++sb)
                             s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[sb][e], qf[4 * u + e],
                                                                           s[sb], 0, 0, 0);
-            }
-            if (!all_halves) {
-                // the diagonal tile's later halves, each only if the wave sees it
+                }
+            } else {
 #pragma unroll
-                for (int sb = 1; sb < BN / 32; ++sb) {
+                for (int sb = 0; sb < BN / 32; ++sb) {
                     if (k0 + 32 * sb >= wend) break;
                     const float *krow = Ks + (32 * sb + c) * C::KS + h * C::DH;
 #pragma unroll
@@ -259,22 +266,26 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
             for (int d = 0; d < D / 32; ++d)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-            // 3. O^T += V^T P^T, the probabilities straight from the score registers
+            // 3. O^T += V^T P^T, the probabilities straight from the score
+            //    registers (masked-out keys carry p = 0)
 #pragma unroll
             for (int sb = 0; sb < BN / 32; ++sb) {
-                if (k0 + 32 * sb < wend) {
+                if (!kAll && k0 + 32 * sb >= wend) break;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float *vrow = Vs + (32 * sb + 8 * (r >> 2) + 4 * h + (r & 3)) * C::VS + c;
+                for (int r = 0; r < 16; ++r) {
+                    const float *vrow = Vs + (32 * sb + 8 * (r >> 2) + 4 * h + (r & 3)) * C::VS + c;
 #pragma unroll
-                        for (int d = 0; d < D / 32; ++d)
-                            o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * d], s[sb][r],
-                                                                         o[d], 0, 0, 0);
-                    }
+                    for (int d = 0; d < D / 32; ++d)
+                        o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * d], s[sb][r], o[d],
+                                                                     0, 0, 0);
                 }
             }
+        };
+        if (k0 < wend) {
+            if (k0 + BN <= wend) process(std::true_type{});
+            else process(std::false_type{});
         }
-        if (t + 1 < ntiles) lstore((t + 1) & 1);
+        if (t + 1 < ntiles) lstore((t + 1) & 1, t + 1);
         if (t + 2 < ntiles) gload(t + 2);
         __syncthreads();
     }
