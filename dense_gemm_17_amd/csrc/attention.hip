@@ -44,8 +44,6 @@
 // Under the causal mask a work-group visits only the key tiles up to its
 // last query and a wave skips the 32-key halves past its own last query;
 // work-groups with the most keys are launched first.
-#include <type_traits>
-
 #include "gemm_internal.h"
 
 namespace mi355gemm {
@@ -177,37 +175,37 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
         const float *Ks = lds + (t & 1) * C::kStage;
         const float *Vs = Ks + BN * C::KS;
         const int64_t k0 = t * BN;
-        // One tile for this wave: kAll when the wave sees every 32-key half
-        // of it (every tile but the causal diagonal), so that the half loops
-        // carry no per-MFMA branches; else only the halves before wend.
-        auto process = [&](auto all_tag) {
-            constexpr bool kAll = decltype(all_tag)::value;
-            // 1. scores, transposed: s[sb] holds keys k0 + 32 sb + (8 (r/4) +
-            //    4 h + r%4) for query c of this wave; the halves run as
-            //    independent MFMA chains, interleaved.
+        if (k0 < wend) {
+            // 1. scores, transposed: s[sb] holds keys k0 + 32 sb + (8 (r/4) + 4 h + r%4)
+            //    for query c of this wave.  The 32-key halves the wave sees
+            //    (both but on its diagonal tile) run as independent MFMA
+            //    chains, interleaved.
             f32x16 s[BN / 32];
 #pragma unroll
             for (int sb = 0; sb < BN / 32; ++sb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
-            if constexpr (kAll) {
+            const bool all_halves = k0 + BN <= wend;
 #pragma unroll
-                for (int u = 0; u < C::DH / 4; ++u) {
-                    f32x4 kv[BN / 32];
+            for (int u = 0; u < C::DH / 4; ++u) {
+                f32x4 kv[BN / 32];
 #pragma unroll
-                    for (int sb = 0; sb < BN / 32; ++sb)
+                for (int sb = 0; sb < BN / 32; ++sb)
+                    if (sb == 0 || all_halves)
                         kv[sb] = *reinterpret_cast<const f32x4 *>(Ks + (32 * sb + c) * C::KS +
                                                                   h * C::DH + 4 * u);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int sb = 0; sb < BN / 32; ++sb)
+                    for (int sb = 0; sb < BN / 32; ++sb)
+                        if (sb == 0 || all_halves)
                             s[sb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv[sb][e], qf[4 * u + e],
                                                                           s[sb], 0, 0, 0);
-                }
-            } else {
+            }
+            if (!all_halves) {
+                // the diagonal tile's later halves, each only if the wave sees it
 #pragma unroll
-                for (int sb = 0; sb < BN / 32; ++sb) {
+                for (int sb = 1; sb < BN / 32; ++sb) {
                     if (k0 + 32 * sb >= wend) break;
                     const float *krow = Ks + (32 * sb + c) * C::KS + h * C::DH;
 #pragma unroll
@@ -266,24 +264,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs
             for (int d = 0; d < D / 32; ++d)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-            // 3. O^T += V^T P^T, the probabilities straight from the score
-            //    registers (masked-out keys carry p = 0)
+            // 3. O^T += V^T P^T, the probabilities straight from the score registers
 #pragma unroll
             for (int sb = 0; sb < BN / 32; ++sb) {
-                if (!kAll && k0 + 32 * sb >= wend) break;
+                if (k0 + 32 * sb < wend) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float *vrow = Vs + (32 * sb + 8 * (r >> 2) + 4 * h + (r & 3)) * C::VS + c;
+                    for (int r = 0; r < 16; ++r) {
+                        const float *vrow = Vs + (32 * sb + 8 * (r >> 2) + 4 * h + (r & 3)) * C::VS + c;
 #pragma unroll
-                    for (int d = 0; d < D / 32; ++d)
-                        o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * d], s[sb][r], o[d],
-                                                                     0, 0, 0);
+                        for (int d = 0; d < D / 32; ++d)
+                            o[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32 * d], s[sb][r],
+                                                                         o[d], 0, 0, 0);
+                    }
                 }
             }
-        };
-        if (k0 < wend) {
-            if (k0 + BN <= wend) process(std::true_type{});
-            else process(std::false_type{});
         }
         if (t + 1 < ntiles) lstore((t + 1) & 1, t + 1);
         if (t + 2 < ntiles) gload(t + 2);
