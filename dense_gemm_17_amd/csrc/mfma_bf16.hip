@@ -254,8 +254,9 @@ void mfma_bf16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restric
 
 
 // ---------------------------------------------------------------------------
-// Direct variants (256 x 256 tile, one work-group per CU; 128 x 128 tile,
-// two per CU, for shapes whose 256-tile count leaves CUs idle): global -> LDS
+// Direct variants (128 x 128 tile, two work-groups per CU, and 64 x 64 here;
+// the 256 x 256 tile, one work-group per CU, shares this staging but runs
+// the 16 x 16 x 32 instruction, further below): global -> LDS
 // with gfx950's LDS-direct 128-bit loads (global_load_lds_dwordx4), no
 // register staging and no LDS write instructions, into a ring of four
 // 32-wide K stages so that the loads for tile t + 3 are in flight while tile
@@ -716,6 +717,312 @@ void mfma_bf16_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
                              lane);
     else
         store_c(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
+}
+
+// ---- 256 x 256 tiles on the 16 x 16 x 32 instruction ------------------------
+// The same LDS-direct ring, loads and layouts as above, but each wave's
+// 128 x 128 piece of C is 8 x 8 blocks of 16 x 16 on v_mfma_f32_16x16x32_bf16
+// (or _f16): one MFMA consumes a whole 32-deep stage.  Per flop this moves
+// half as many accumulator bytes through the register file as the 32 x 32 x
+// 16 instruction; under the board's power limit a loop of nothing but these
+// MFMAs on random bf16 operands sustains 0.72 of the nominal peak against
+// 0.69 for the 32 x 32 shape, and this tile runs 3-5% faster than the 32 x 32
+// tile at 4096^3 and 8192^3 (vidyal.ai Part 6 on feeding the matrix
+// instructions; the smaller instruction is the gfx950 variant, not the
+// pages').  Operand layout: lane (i, g) = (lane mod 16, lane / 16) supplies
+// row (A) or column (B) i of a block and k = 8g .. 8g + 7; it holds C rows
+// 4g .. 4g + 3 of column i.
+//
+// Schedule of one stage (one barrier): the 64 MFMAs in column-block-major
+// order (q = 8 nb + mb).  B fragments are re-read from the next stage in
+// place, each half right after the last MFMA that uses it; A fragments go to
+// the second of two register sets, one block every eighth MFMA; this wave's
+// loads of the tile three stages ahead follow every eighth MFMA from the
+// second.  Measured against the other placements tried (reads and loads
+// bunched at the start of the stage, every second or fourth MFMA): 2-5%
+// faster at 8192^3.  The first stage's MFMAs start from zero instead of
+// zeroed accumulators: with 256 zero-initialised registers live into the
+// loop the register allocator split them between register files and spilled.
+//
+// A 16-lane transposing read touches rows 8 apart within a half-wave (the
+// groups g and g + 1 want k = 8g .. and 8g + 8 ..), so rows of M or N get the
+// b_swz masks with bit 1 flipped when bit 3 of the row is set: both 16-byte
+// slot sets of a half-wave are then distinct.
+namespace d16 {
+
+constexpr int kTile = 256;
+constexpr int kBlocks = 8;                                  // 16-wide blocks per wave, each way
+constexpr int kInst = kTile * DBK * 2 / 1024 / 4;           // LDS-direct loads per wave per factor
+constexpr int kPerTile = 2 * kInst;
+constexpr int kStage = 2 * kTile * DBK;                     // bf16 elements per stage
+constexpr int kRegion = kTile * DBK * 2;                    // bytes of one factor per stage
+
+__device__ __forceinline__ int swz_mn(int row) { return b_swz(row) ^ (((row >> 3) & 1) << 1); }
+
+// One factor's operand fragments.  Stored along K (A as written, B
+// transposed): one 16-byte read per block into w; stored along M or N: two
+// transposing reads per block into lo / hi.  Unused members take no registers.
+struct Frag {
+    bf16x8 w[kBlocks];
+    bf16x4 lo[kBlocks], hi[kBlocks];
+};
+
+struct Ctx {
+    uint32_t a_voff[kInst], b_voff[kInst];
+    const char *abase, *bbase;
+    int64_t a_kstride, b_kstride;
+    uint32_t lds0;
+    int wave;
+    uint32_t rdA[kBlocks], rdB[kBlocks];   // lane read offsets (bytes) of each block
+};
+
+__device__ __forceinline__ void load_one(const Ctx &x, uint32_t stage_lds, int64_t kt, int l)
+{
+    if (l < kInst)
+        lds_direct_load16(x.a_voff[l], x.abase + kt * x.a_kstride, stage_lds + (x.wave * kInst + l) * 1024);
+    else
+        lds_direct_load16(x.b_voff[l - kInst], x.bbase + kt * x.b_kstride,
+                          stage_lds + kRegion + (x.wave * kInst + l - kInst) * 1024);
+}
+
+template <bool kAlongK>
+__device__ __forceinline__ void read_block(Frag &f, const char *stage, uint32_t off, int j)
+{
+    if constexpr (kAlongK) {
+        f.w[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(stage + off));
+    } else {
+        f.lo[j] = read_tr4(stage + off);
+        f.hi[j] = read_tr4(stage + off + 4 * kTile * 2);
+    }
+}
+
+template <bool kAlongK>
+__device__ __forceinline__ bf16x8 operand(const Frag &f, int j)
+{
+    if constexpr (kAlongK) return f.w[j];
+    else return __builtin_shufflevector(f.lo[j], f.hi[j], 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool kF16>
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
+{
+    if constexpr (kF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One stage: MFMAs on (cur, fb) with the next stage's reads (A into nxt, B
+// in place) and this wave's loads of tile kload slotted in.  kFirst: the
+// accumulators start at zero.
+template <bool kFirst, bool kF16, bool TA, bool TB>
+__device__ __forceinline__ void phase(f32x4 (&acc)[kBlocks][kBlocks], const Frag &cur, Frag &nxt,
+                                      Frag &fb, const uint16_t *rstage, const Ctx &x,
+                                      uint32_t lstage, int64_t kload)
+{
+    const char *st = reinterpret_cast<const char *>(rstage);
+#pragma unroll
+    for (int q = 0; q < kBlocks * kBlocks; ++q) {
+        const int nb = q / kBlocks, mb = q % kBlocks;
+        acc[mb][nb] = mfma<kF16>(operand<!TA>(cur, mb), operand<TB>(fb, nb),
+                                 kFirst ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TB) {
+            if (mb == kBlocks - 1) read_block<true>(fb, st, x.rdB[nb], nb);
+        } else {
+            if (mb == kBlocks - 1) fb.lo[nb] = read_tr4(st + x.rdB[nb]);
+            if (mb == 3 && nb > 0) fb.hi[nb - 1] = read_tr4(st + x.rdB[nb - 1] + 4 * kTile * 2);
+            if (q == kBlocks * kBlocks - 1)
+                fb.hi[kBlocks - 1] = read_tr4(st + x.rdB[kBlocks - 1] + 4 * kTile * 2);
+        }
+        if (q % 8 == 4) read_block<!TA>(nxt, st, x.rdA[q / 8], q / 8);
+        if (q % 8 == 1) load_one(x, lstage, kload, q / 8);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// C through the idle ring in two passes of 128 rows (64 per wave row): each
+// lane writes its four rows of each block (16-byte chunks XOR-permuted by
+// rows / 4 mod 4, so the four row groups of one write hit distinct banks),
+// then the work-group writes whole 16-byte row chunks.
+__device__ __forceinline__ void store_rows(const f32x4 (&acc)[kBlocks][kBlocks], float *lf,
+                                           float *__restrict__ C, int64_t ldc, int64_t M,
+                                           int64_t N, int64_t m0, int64_t n0, int wm, int wn,
+                                           int lane)
+{
+    const int i16 = lane & 15, g = lane >> 4;
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int mbl = 0; mbl < 4; ++mbl)
+#pragma unroll
+            for (int nb = 0; nb < kBlocks; ++nb) {
+                const int col = wn * 128 + nb * 16 + i16;
+                const f32x4 v = acc[pass * 4 + mbl][nb];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int lrow = wm * 64 + mbl * 16 + 4 * g + r;
+                    const int pcol = ((col >> 2) ^ (((lrow >> 2) & 3) << 2)) * 4 + (col & 3);
+                    lf[lrow * kTile + pcol] = v[r];
+                }
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 128 * (kTile / 4) / kThreads; ++i) {
+            const int q = threadIdx.x + kThreads * i;
+            const int lrow = q / (kTile / 4), chunk = q % (kTile / 4);
+            const int pchunk = chunk ^ (((lrow >> 2) & 3) << 2);
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(lf + lrow * kTile + pchunk * 4);
+            const int64_t row = m0 + (lrow / 64) * 128 + pass * 64 + lrow % 64;
+            const int64_t col = n0 + 4 * chunk;
+            if (row < M && col < N) store_c_stream(reinterpret_cast<f32x4 *>(C + row * ldc + col), v);
+        }
+    }
+}
+
+// C straight from the MFMA layout (any C alignment).
+__device__ __forceinline__ void store_direct(const f32x4 (&acc)[kBlocks][kBlocks],
+                                             float *__restrict__ C, int64_t ldc, int64_t M,
+                                             int64_t N, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane)
+{
+    const int i16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int mb = 0; mb < kBlocks; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < kBlocks; ++nb) {
+            const int64_t col = n0 + wn * 128 + nb * 16 + i16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm * 128 + mb * 16 + 4 * g + r;
+                if (row < M && col < N) store_c_stream(C + row * ldc + col, acc[mb][nb][r]);
+            }
+        }
+}
+
+}  // namespace d16
+
+template <bool kRowsC, bool TA, bool TB, bool kBatch, bool kF16>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma_bf16_d16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
+                          int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
+                          float *__restrict__ C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
+                          int64_t sa, int64_t sb, int64_t sc, int64_t batch)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[DSTAGES * d16::kStage];
+
+    int64_t m0, n0;
+    if constexpr (kBatch) {
+        const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
+        A += t.b * sa;
+        B += t.b * sb;
+        C += t.b * sc;
+        m0 = t.tm * d16::kTile;
+        n0 = t.tn * d16::kTile;
+    } else {
+        const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+        m0 = t.tm * d16::kTile;
+        n0 = t.tn * d16::kTile;
+    }
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int i16 = lane & 15, g = lane >> 4;
+
+    d16::Ctx x;
+    x.wave = wave;
+    x.lds0 = lds_offset(lds);
+    x.abase = static_cast<const char *>(uniform_ptr(TA ? A + m0 : A + m0 * lda));
+    x.bbase = static_cast<const char *>(uniform_ptr(TB ? B + n0 * ldb : B + n0));
+    x.a_kstride = uniform_i64(TA ? DBK * lda * 2 : DBK * 2);
+    x.b_kstride = uniform_i64(TB ? DBK * 2 : DBK * ldb * 2);
+    // Load lane offsets.  Along K: 256 rows of 4 chunks, chunk c of row r at
+    // slot c ^ a_swz<4>(r), rows past the edge re-read the last one.  Along
+    // M or N: 32 rows of 32 chunks at slot c ^ swz_mn(r), chunks past the
+    // edge re-read the last whole one (that dimension is a multiple of 8).
+    const auto along_k = [&](int p, int64_t base, int64_t extent, int64_t ld) {
+        const int row = p >> 2, slot = p & 3;
+        const int cc = slot ^ a_swz<4>(row);
+        const int64_t r = (base + row < extent) ? row : extent - 1 - base;
+        return static_cast<uint32_t>((r * ld + 8 * cc) * 2);
+    };
+    const auto along_mn = [&](int p, int64_t base, int64_t extent, int64_t ld) {
+        const int row = p / (d16::kTile / 8), slot = p % (d16::kTile / 8);
+        const int cc = slot ^ d16::swz_mn(row);
+        const int64_t col = (base + 8 * cc < extent) ? 8 * cc : extent - 8 - base;
+        return static_cast<uint32_t>((row * ld + col) * 2);
+    };
+#pragma unroll
+    for (int i = 0; i < d16::kInst; ++i) {
+        const int p = (wave * d16::kInst + i) * 64 + lane;
+        x.a_voff[i] = TA ? along_mn(p, m0, M, lda) : along_k(p, m0, M, lda);
+        x.b_voff[i] = TB ? along_k(p, n0, N, ldb) : along_mn(p, n0, N, ldb);
+    }
+    // Read offsets.  Along K: block j's rows base + 16 j + i16, chunk g; the
+    // swizzle (rows / 4 mod 4) depends on the lane only.  Along M or N: rows
+    // 8g + i16 / 4 (+4 for the upper half), 4 columns from base + 16 j +
+    // 4 (i16 mod 4); the swizzle touches chunk bits 1-3, so per block.
+#pragma unroll
+    for (int j = 0; j < d16::kBlocks; ++j) {
+        const int rk = (wm * 128 + 16 * j + i16) * DBK * 2 + ((g ^ ((i16 >> 2) & 3)) << 4);
+        const int row = 8 * g + (i16 >> 2);
+        const int ma = wm * 128 + 16 * j + 4 * (i16 & 3);
+        x.rdA[j] = TA ? row * d16::kTile * 2 + (((ma >> 3) ^ d16::swz_mn(row)) << 4) + (ma & 7) * 2 : rk;
+        const int rkb = d16::kRegion + (wn * 128 + 16 * j + i16) * DBK * 2 + ((g ^ ((i16 >> 2) & 3)) << 4);
+        const int nb_ = wn * 128 + 16 * j + 4 * (i16 & 3);
+        x.rdB[j] = TB ? rkb : d16::kRegion + row * d16::kTile * 2 + (((nb_ >> 3) ^ d16::swz_mn(row)) << 4) + (nb_ & 7) * 2;
+    }
+
+    const int64_t ktiles = K / DBK;
+    auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * d16::kStage; };
+    auto lstage = [&](int64_t kt) {
+        return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * d16::kStage * 2;
+    };
+    auto kclamp = [&](int64_t kt) { return kt < ktiles ? kt : ktiles - 1; };
+
+    // Prologue: tiles 0..2 in flight (past the end re-fetching the last),
+    // wait for tile 0, read all of its fragments.
+#pragma unroll
+    for (int st = 0; st < DSTAGES - 1; ++st)
+#pragma unroll
+        for (int l = 0; l < d16::kPerTile; ++l) d16::load_one(x, lstage(st), kclamp(st), l);
+    wait_lds_vm_barrier<(DSTAGES - 2) * d16::kPerTile>();
+    d16::Frag a0, a1, fb;
+    {
+        const char *st0 = reinterpret_cast<const char *>(stage(0));
+#pragma unroll
+        for (int j = 0; j < d16::kBlocks; ++j) {
+            d16::read_block<!TA>(a0, st0, x.rdA[j], j);
+            d16::read_block<TB>(fb, st0, x.rdB[j], j);
+        }
+    }
+    // Stage kt: wait until tile kt + 1 has landed everywhere and every
+    // wave's reads of tile kt are done, barrier, then the MFMAs of tile kt
+    // with the reads of tile kt + 1 and the loads of tile kt + 3 (whose
+    // stage was last read in stage kt - 2).  A sets alternate a0, a1.
+    f32x4 acc[d16::kBlocks][d16::kBlocks];   // written by stage 0's MFMAs
+    wait_lds_vm_barrier<d16::kPerTile>();
+    d16::phase<true, kF16, TA, TB>(acc, a0, a1, fb, stage(1), x, lstage(3), kclamp(3));
+    int64_t kt = 1;
+    for (; kt + 1 < ktiles; kt += 2) {
+        wait_lds_vm_barrier<d16::kPerTile>();
+        d16::phase<false, kF16, TA, TB>(acc, a1, a0, fb, stage(kt + 1), x, lstage(kt + 3), kclamp(kt + 3));
+        wait_lds_vm_barrier<d16::kPerTile>();
+        d16::phase<false, kF16, TA, TB>(acc, a0, a1, fb, stage(kt + 2), x, lstage(kt + 4), kclamp(kt + 4));
+    }
+    if (kt < ktiles) {   // an even number of tiles: the last one on a1
+        wait_lds_vm_barrier<d16::kPerTile>();
+        d16::phase<false, kF16, TA, TB>(acc, a1, a0, fb, stage(kt + 1), x, lstage(kt + 3), kclamp(kt + 3));
+    }
+    // No LDS-direct load may still be writing LDS when the work-group ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (kRowsC)
+        d16::store_rows(acc, reinterpret_cast<float *>(lds), C, ldc, M, N, m0, n0, wm, wn, lane);
+    else
+        d16::store_direct(acc, C, ldc, M, N, m0, n0, wm, wn, lane);
 }
 
 // ---- 8-bit floats on the same staging ---------------------------------------
@@ -1316,16 +1623,45 @@ hipError_t launch_direct_layout(const Problem &p, hipStream_t s, int64_t tm, int
     return hipGetLastError();
 }
 
+template <bool kF16, bool TA, bool TB, bool kBatch = true>
+hipError_t launch_d16_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
+{
+    const auto *A = static_cast<const uint16_t *>(p.A);
+    const auto *B = static_cast<const uint16_t *>(p.B);
+    const dim3 grid(static_cast<uint32_t>(tm * tn * p.batch));
+    const bool rows_c = (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && p.ldc % 4 == 0 &&
+                        p.N % 4 == 0 && p.sc % 4 == 0;
+    if (rows_c)
+        hipLaunchKernelGGL((mfma_bf16_d16_kernel<true, TA, TB, kBatch, kF16>), grid, dim3(kThreads), 0,
+                           s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm, tn, p.sa, p.sb,
+                           p.sc, p.batch);
+    else
+        hipLaunchKernelGGL((mfma_bf16_d16_kernel<false, TA, TB, kBatch, kF16>), grid, dim3(kThreads), 0,
+                           s, p.M, p.N, p.K, A, p.lda, B, p.ldb, p.C, p.ldc, tm, tn, p.sa, p.sb,
+                           p.sc, p.batch);
+    return hipGetLastError();
+}
+
+// The 256 x 256 tile runs on the 16 x 16 x 32 instruction, the smaller
+// tiles on the 32 x 32 x 16 one.
 template <int TM, int TN, bool kF16 = false>
 hipError_t launch_direct(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + TM - 1) / TM, tn = (p.N + TN - 1) / TN;
     if (tm * tn * p.batch > kMaxBlocks || !supports_mfma_bf16_direct(p)) return hipErrorInvalidValue;
-    if (p.ta && p.tb) return launch_direct_layout<TM, TN, kF16, true, true>(p, s, tm, tn);
-    if (p.ta) return launch_direct_layout<TM, TN, kF16, true, false>(p, s, tm, tn);
-    if (p.tb) return launch_direct_layout<TM, TN, kF16, false, true>(p, s, tm, tn);
-    if (p.batch != 1) return launch_direct_layout<TM, TN, kF16, false, false>(p, s, tm, tn);
-    return launch_direct_layout<TM, TN, kF16, false, false, false>(p, s, tm, tn);
+    if constexpr (TM == 256 && TN == 256) {
+        if (p.ta && p.tb) return launch_d16_layout<kF16, true, true>(p, s, tm, tn);
+        if (p.ta) return launch_d16_layout<kF16, true, false>(p, s, tm, tn);
+        if (p.tb) return launch_d16_layout<kF16, false, true>(p, s, tm, tn);
+        if (p.batch != 1) return launch_d16_layout<kF16, false, false>(p, s, tm, tn);
+        return launch_d16_layout<kF16, false, false, false>(p, s, tm, tn);
+    } else {
+        if (p.ta && p.tb) return launch_direct_layout<TM, TN, kF16, true, true>(p, s, tm, tn);
+        if (p.ta) return launch_direct_layout<TM, TN, kF16, true, false>(p, s, tm, tn);
+        if (p.tb) return launch_direct_layout<TM, TN, kF16, false, true>(p, s, tm, tn);
+        if (p.batch != 1) return launch_direct_layout<TM, TN, kF16, false, false>(p, s, tm, tn);
+        return launch_direct_layout<TM, TN, kF16, false, false, false>(p, s, tm, tn);
+    }
 }
 
 }  // namespace

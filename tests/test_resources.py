@@ -23,7 +23,7 @@ OCCUPANCY_BUDGET = {
     "mfma_f32_kernelILi256ELi256E": 1,
     "mfma_f32_kernelILi128ELi128E": 2,
     "mfma_bf16_kernel": 1,
-    "mfma_bf16_direct_kernelILi256ELi256E": 1,
+    "mfma_bf16_d16_kernel": 1,
     "mfma_bf16_direct_kernelILi128ELi128E": 2,
     "mfma_fp8_direct_kernelILi128ELi128E": 2,
     "mfma_fp8_direct_kernelILi256ELi128E": 1,
@@ -90,7 +90,7 @@ def test_occupancy_budget(kernels):
 def test_matrix_core_accumulators_live_in_agprs(kernels):
     # the 256 x 256 tiles keep all 256 accumulators per lane in AGPRs
     big = ("mfma_f32_kernelILi256ELi256E", "mfma_f32_direct_kernelILi256ELi256E",
-           "mfma_bf16_kernel", "mfma_bf16_direct_kernelILi256ELi256E",
+           "mfma_bf16_kernel", "mfma_bf16_d16_kernel",
            "3f3214batched_kernelILi256ELi256E", "2bf14batched_kernelILi256ELi256E")
     seen = 0
     for name, r in kernels.items():
