@@ -759,6 +759,12 @@ constexpr int kRegion = kTile * DBK * 2;                    // bytes of one fact
 
 __device__ __forceinline__ int swz_mn(int row) { return b_swz(row) ^ (((row >> 3) & 1) << 1); }
 
+// Rows of 4 chunks (a factor stored along K): 16 consecutive rows at one
+// logical chunk per 16 lanes.  (row >> 2) & 3, the 32 x 32 tile's mask,
+// measured 3.9 conflict cycles per read in this pattern (SQ_LDS_BANK_CONFLICT),
+// row & 3 and (row ^ row >> 2) & 3 the same; (row >> 1) & 3 measured none.
+__device__ __forceinline__ int swz_k(int row) { return (row >> 1) & 3; }
+
 // One factor's operand fragments.  Stored along K (A as written, B
 // transposed): one 16-byte read per block into w; stored along M or N: two
 // transposing reads per block into lo / hi.  Unused members take no registers.
@@ -940,12 +946,12 @@ void mfma_bf16_d16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__res
     x.a_kstride = uniform_i64(TA ? DBK * lda * 2 : DBK * 2);
     x.b_kstride = uniform_i64(TB ? DBK * 2 : DBK * ldb * 2);
     // Load lane offsets.  Along K: 256 rows of 4 chunks, chunk c of row r at
-    // slot c ^ a_swz<4>(r), rows past the edge re-read the last one.  Along
+    // slot c ^ swz_k(r), rows past the edge re-read the last one.  Along
     // M or N: 32 rows of 32 chunks at slot c ^ swz_mn(r), chunks past the
     // edge re-read the last whole one (that dimension is a multiple of 8).
     const auto along_k = [&](int p, int64_t base, int64_t extent, int64_t ld) {
         const int row = p >> 2, slot = p & 3;
-        const int cc = slot ^ a_swz<4>(row);
+        const int cc = slot ^ d16::swz_k(row);
         const int64_t r = (base + row < extent) ? row : extent - 1 - base;
         return static_cast<uint32_t>((r * ld + 8 * cc) * 2);
     };
@@ -962,16 +968,16 @@ void mfma_bf16_d16_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__res
         x.b_voff[i] = TB ? along_k(p, n0, N, ldb) : along_mn(p, n0, N, ldb);
     }
     // Read offsets.  Along K: block j's rows base + 16 j + i16, chunk g; the
-    // swizzle (rows / 4 mod 4) depends on the lane only.  Along M or N: rows
+    // swizzle (rows / 2 mod 4) depends on the lane only.  Along M or N: rows
     // 8g + i16 / 4 (+4 for the upper half), 4 columns from base + 16 j +
     // 4 (i16 mod 4); the swizzle touches chunk bits 1-3, so per block.
 #pragma unroll
     for (int j = 0; j < d16::kBlocks; ++j) {
-        const int rk = (wm * 128 + 16 * j + i16) * DBK * 2 + ((g ^ ((i16 >> 2) & 3)) << 4);
+        const int rk = (wm * 128 + 16 * j + i16) * DBK * 2 + ((g ^ d16::swz_k(i16)) << 4);
         const int row = 8 * g + (i16 >> 2);
         const int ma = wm * 128 + 16 * j + 4 * (i16 & 3);
         x.rdA[j] = TA ? row * d16::kTile * 2 + (((ma >> 3) ^ d16::swz_mn(row)) << 4) + (ma & 7) * 2 : rk;
-        const int rkb = d16::kRegion + (wn * 128 + 16 * j + i16) * DBK * 2 + ((g ^ ((i16 >> 2) & 3)) << 4);
+        const int rkb = d16::kRegion + (wn * 128 + 16 * j + i16) * DBK * 2 + ((g ^ d16::swz_k(i16)) << 4);
         const int nb_ = wn * 128 + 16 * j + 4 * (i16 & 3);
         x.rdB[j] = TB ? rkb : d16::kRegion + row * d16::kTile * 2 + (((nb_ >> 3) ^ d16::swz_mn(row)) << 4) + (nb_ & 7) * 2;
     }
