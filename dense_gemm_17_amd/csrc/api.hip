@@ -60,6 +60,7 @@ const KernelInfo kKernels[] = {
     {"skinny_fp8", kFp8, launch_skinny_fp8, supports_skinny_fp8, true},
     {"mfma_bf16_direct64", kBF16, launch_mfma_bf16_direct64, supports_mfma_bf16_direct, true},
     {"mfma_bf16_wsplit64", kBF16, launch_mfma_bf16_wsplit, supports_mfma_bf16_wsplit, true},
+    {"mfma_fp8_direct256", kFp8, launch_mfma_fp8_direct256, supports_mfma_fp8_direct, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -197,14 +198,18 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // large sizes, used by select_general.
 constexpr int64_t F32_GENERAL_256 = 700, F32_GENERAL_128 = 670;
 constexpr int64_t BF16_GENERAL_256 = 340, BF16_GENERAL_128 = 300;
-// 8-bit floats at 8192^3: LDS-direct 256 x 128 0.378 (at the board's power
-// limit), 128 x 128 0.341-0.353, register-staged 256 x 256 0.345, 128 x 128
-// 0.337-0.352.  With a short K (the GPT QKV projection, K = 384: six K
-// tiles) the two 128 x 128 work-groups per CU hide each other's prologue
-// and epilogue and win (665 vs 483 TFLOP/s); from K = 1536 (MLP down) the
-// 256 x 128 tile does (889 vs 815).
+// 8-bit floats at 8192^3: LDS-direct 256 x 256 0.511, 256 x 128 0.378-0.389
+// (at the board's power limit), 128 x 128 0.341-0.358, register-staged
+// 256 x 256 0.345, 128 x 128 0.337-0.352.  With a short K (the GPT QKV
+// projection, K = 384: six K tiles) the two 128 x 128 work-groups per CU
+// hide each other's prologue and epilogue and win (665 vs 483 TFLOP/s);
+// from K = 1536 (MLP down) the 256 x 128 tile does (889 vs 815).  The
+// larger tiles need their work-groups to fill the chip: with fewer 256-row
+// tiles than half the CUs (2048 x 2048 x 8192: 128 tiles of 256 x 128, 64 of
+// 256 x 256) two 128 x 128 work-groups per CU pull each CU's operands twice
+// as fast and win (38.8 vs 56.5 and 74.0 us).
 constexpr int64_t FP8_BATCHED_256 = 345, FP8_BATCHED_128 = 345, FP8_DIRECT_128 = 345,
-                  FP8_DIRECT_256x128 = 378;
+                  FP8_DIRECT_256x128 = 378, FP8_DIRECT_256 = 511;
 
 // Relative time of a tiled launch: waves x per-work-group work / efficiency,
 // in units of one CU doing a 128 x 128 tile alone at full rate.
@@ -286,14 +291,20 @@ int select_general(const Problem &p)
     // per byte of Bt at 16 rows) outrun the stream and the matrix cores win
     // (16 x 8192 x 8192: 41.9 us on the 128 x 128 tile vs 51.9).
     if (p.dtype == kFp8 && p.M <= 4 && supports_skinny_fp8(p)) return kernel_id("skinny_fp8");
-    if (p.dtype == kFp8 && supports_mfma_fp8_direct(p))
+    if (p.dtype == kFp8 && supports_mfma_fp8_direct(p)) {
         // (M <= 128: one 128-row tile covers M and the 256-row tile would
         // do at least twice the padded work; 16 x 8192 x 8192: 41.9 vs 58.6 us)
-        return p.K >= 1024 && p.M > 128 &&
-                       tiled_cost(p, 256, 128, 1, FP8_DIRECT_256x128) <=
-                           tiled_cost(p, 128, 128, 2, FP8_DIRECT_128)
-                   ? kernel_id("mfma_fp8_direct256x128")
-                   : kernel_id("mfma_fp8_direct128");
+        const int64_t c128 = tiled_cost(p, 128, 128, 2, FP8_DIRECT_128);
+        const bool big = p.K >= 1024 && p.M > 128;
+        const int64_t t256 = ceil_div(p.M, 256) * ceil_div(p.N, 256) * p.batch;
+        const int64_t t256x128 = ceil_div(p.M, 256) * ceil_div(p.N, 128) * p.batch;
+        const int64_t c256 = tiled_cost(p, 256, 256, 1, FP8_DIRECT_256);
+        const int64_t c256x128 = tiled_cost(p, 256, 128, 1, FP8_DIRECT_256x128);
+        if (big && t256 >= kCUs && c256 <= c256x128 && c256 <= c128)
+            return kernel_id("mfma_fp8_direct256");
+        return big && 2 * t256x128 > kCUs && c256x128 <= c128 ? kernel_id("mfma_fp8_direct256x128")
+                                                              : kernel_id("mfma_fp8_direct128");
+    }
     if (p.dtype == kFp8)
         return !p.xa && tiled_cost(p, 256, 256, 1, FP8_BATCHED_256) <=
                             tiled_cost(p, 128, 128, 2, FP8_BATCHED_128)

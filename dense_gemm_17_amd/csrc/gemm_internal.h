@@ -111,6 +111,7 @@ hipError_t launch_mfma_fp8_batched(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_batched128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_fp8_direct256x128(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_fp8_direct256(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_direct64(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_wsplit(const Problem &p, hipStream_t s);
 bool supports_mfma_bf16_wsplit(const Problem &p);

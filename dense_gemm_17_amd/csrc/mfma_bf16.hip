@@ -1156,7 +1156,7 @@ __device__ __forceinline__ void load8_one(const DCtx<TM, TN, false, true> &x,
         load_one(x, stage_lds, kt, l);
 }
 
-template <int kFmt, bool kMX, int TM, int TN>
+template <int kFmt, bool kMX, bool kFirst, int TM, int TN>
 __device__ __forceinline__ void mfma_phase8(f32x16 (&acc)[TM / 64][TN / 64],
                                             const Frag8<TM, TN> &cur, Frag8<TM, TN> &nxt,
                                             const uint16_t *rstage,
@@ -1169,10 +1169,11 @@ __device__ __forceinline__ void mfma_phase8(f32x16 (&acc)[TM / 64][TN / 64],
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int mb = q / NB, nb = q % NB;
+        const f32x16 c0 = kFirst ? f32x16{} : acc[mb][nb];
         if constexpr (kMX)
-            acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], acc[mb][nb], cur.sa[mb], cur.sb[nb]);
+            acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], c0, cur.sa[mb], cur.sb[nb]);
         else
-            acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], acc[mb][nb]);
+            acc[mb][nb] = mfma8<kFmt>(cur.a[mb], cur.b[nb], c0);
         __builtin_amdgcn_sched_barrier(0);
         if (kMX && q == 0) read_scales(nxt, rstage, mx);
 #pragma unroll
@@ -1290,13 +1291,7 @@ void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__r
             mx.rdB[j] = T::kStageElems * 2 + 2 * TM + h * TN + wn * WN + 32 * j + c;
     }
 
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    f32x16 acc[MB][NB];   // written by tile 0's MFMAs (kFirst)
 
     const int64_t ktiles = K / DBK;
     auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * SE; };
@@ -1324,13 +1319,23 @@ void mfma_fp8_direct_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__r
     // previous phase, which every wave finished before the last barrier) |
     // wait until tile kt + 2 has landed everywhere and this wave's reads are
     // done, barrier.  Two tiles per trip so the fragment sets alternate
-    // without copies; reads past the last tile hit landed re-fetches.
-    for (int64_t kt = 0; kt < ktiles; kt += 2) {
-        mfma_phase8<kFmt, kMX>(acc, f, g, stage(kt + 1), x, mx, lstage(kt), kclamp(kt + DSTAGES));
+    // without copies; reads past the last tile hit landed re-fetches.  Tile
+    // 0's MFMAs start from zero instead of zeroed accumulators (which, live
+    // into the loop, made the register allocator spill).
+    mfma_phase8<kFmt, kMX, true>(acc, f, g, stage(1), x, mx, lstage(0), kclamp(DSTAGES));
+    wait_lds_vm_barrier<(DSTAGES - 2) * P>();
+    int64_t kt = 1;
+    for (; kt + 1 < ktiles; kt += 2) {
+        mfma_phase8<kFmt, kMX, false>(acc, g, f, stage(kt + 1), x, mx, lstage(kt),
+                                      kclamp(kt + DSTAGES));
         wait_lds_vm_barrier<(DSTAGES - 2) * P>();
-        if (kt + 1 == ktiles) break;
-        mfma_phase8<kFmt, kMX>(acc, g, f, stage(kt + 2), x, mx, lstage(kt + 1),
-                               kclamp(kt + 1 + DSTAGES));
+        mfma_phase8<kFmt, kMX, false>(acc, f, g, stage(kt + 2), x, mx, lstage(kt + 1),
+                                      kclamp(kt + 1 + DSTAGES));
+        wait_lds_vm_barrier<(DSTAGES - 2) * P>();
+    }
+    if (kt < ktiles) {
+        mfma_phase8<kFmt, kMX, false>(acc, g, f, stage(kt + 1), x, mx, lstage(kt),
+                                      kclamp(kt + DSTAGES));
         wait_lds_vm_barrier<(DSTAGES - 2) * P>();
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1762,6 +1767,7 @@ hipError_t launch_fp8_direct(const Problem &p, hipStream_t s)
 
 hipError_t launch_mfma_fp8_direct128(const Problem &p, hipStream_t s) { return launch_fp8_direct<128, 128>(p, s); }
 hipError_t launch_mfma_fp8_direct256x128(const Problem &p, hipStream_t s) { return launch_fp8_direct<256, 128>(p, s); }
+hipError_t launch_mfma_fp8_direct256(const Problem &p, hipStream_t s) { return launch_fp8_direct<256, 256>(p, s); }
 hipError_t launch_mfma_f16_direct128(const Problem &p, hipStream_t s) { return launch_direct<128, 128, true>(p, s); }
 
 }  // namespace mi355gemm

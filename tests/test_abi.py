@@ -334,7 +334,7 @@ def test_workspace_size():
 
 # ---- 8-bit float operands (pure host planning) --------------------------------
 
-FP8_NAMES = ("mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_batched",
+FP8_NAMES = ("mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_direct256", "mfma_fp8_batched",
              "mfma_fp8_batched128", "skinny_fp8")
 
 
@@ -351,7 +351,12 @@ def test_plan_fp8_layouts_and_kernels():
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 300, 260, 192, 1, **P)) == \
         "mfma_fp8_direct128"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 8192, 8192, 8192, 1, **P)) == \
+        "mfma_fp8_direct256"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 16384, 384, 1536, 1, **P)) == \
         "mfma_fp8_direct256x128"
+    # fewer 256-row tiles than half the CUs: two 128 x 128 work-groups per CU
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 2048, 2048, 8192, 1, **P)) == \
+        "mfma_fp8_direct128"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 16384, 1152, 384, 1, **P)) == \
         "mfma_fp8_direct128"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 300, 260, 208, 1, **P)) in \
@@ -425,7 +430,7 @@ def test_mx_table_choices():
     assert plan(4, 512, 1024) == "skinny_fp8"
     assert plan(8, 77, 160) == "mfma_fp8_batched128"
     assert plan(256, 256, 512) == "mfma_fp8_direct128"
-    assert plan(8192, 8192, 8192) == "mfma_fp8_direct256x128"
+    assert plan(8192, 8192, 8192) == "mfma_fp8_direct256"
     assert plan(512, 512, 480) == "mfma_fp8_batched128"
     assert plan(64, 64, 48) == -1
     assert plan(64, 64, 64, lsa=60) == -1

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 GATE = oracle.GATE
 FMTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
-KERNELS = ["mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_batched",
+KERNELS = ["mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_direct256", "mfma_fp8_batched",
            "mfma_fp8_batched128"]
 SKINNY_SHAPES = [(1, 300, 1024), (2, 77, 16), (3, 130, 4096), (7, 520, 256), (16, 64, 2048),
                  (9, 1000, 208)]

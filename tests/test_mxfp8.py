@@ -28,7 +28,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 GATE = oracle.GATE
 TORCH = workloads.FP8_TORCH
-KERNELS = ["skinny_fp8", "mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_batched128"]
+KERNELS = ["skinny_fp8", "mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_direct256",
+           "mfma_fp8_batched128"]
 
 
 def say(msg):
@@ -172,7 +173,8 @@ def test_table_choice_and_headline_size_sampled():
     # 8192^3 with random scales on sampled rows
     gen = workloads.generator(55)
     for (M, N, K, want) in [(4, 512, 1024, "skinny_fp8"), (256, 256, 512, "mfma_fp8_direct128"),
-                            (2048, 2048, 2048, "mfma_fp8_direct256x128"),
+                            (2048, 2048, 2048, "mfma_fp8_direct128"),
+                            (4096, 4096, 4096, "mfma_fp8_direct256"),
                             (512, 512, 480, "mfma_fp8_batched128")]:
         A = torch.zeros((M, K), dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn)
         Bt = torch.zeros((N, K), dtype=torch.uint8, device=DEV).view(torch.float8_e4m3fn)

@@ -21,7 +21,7 @@ import workloads
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL = 1.3
-TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": workloads.FP8_TORCH[0]}
 
 # (dtype, M, N, K, A stored transposed)
 SHAPES = [
@@ -32,6 +32,10 @@ SHAPES = [
     ("f32", 1024, 1024, 4096, False), ("f32", 384, 1152, 16384, True),
     ("bf16", 16384, 1152, 384, False), ("bf16", 16384, 384, 1536, False),
     ("bf16", 2048, 2048, 8192, False), ("bf16", 384, 1152, 16384, True),
+    # 8-bit floats: B is always the transposed view of a row-major (N, K) tensor
+    ("fp8", 8192, 8192, 8192, False), ("fp8", 4096, 4096, 4096, False),
+    ("fp8", 2048, 2048, 8192, False), ("fp8", 2048, 2048, 2048, False),
+    ("fp8", 16384, 1152, 384, False), ("fp8", 16384, 384, 1536, False),
 ]
 
 
@@ -58,14 +62,17 @@ def timed_us(a, b, c, reps):
 def test_table_choice_is_near_the_fastest(dtype, M, N, K, ta):
     gen = workloads.generator(71)
     A = torch.randn((K, M) if ta else (M, K), generator=gen).to(TDT[dtype]).to(DEV)
-    B = torch.randn((K, N), generator=gen).to(TDT[dtype]).to(DEV)
+    if dtype == "fp8":
+        B = torch.randn((N, K), generator=gen).to(TDT[dtype]).to(DEV).t()
+    else:
+        B = torch.randn((K, N), generator=gen).to(TDT[dtype]).to(DEV)
     a = A.t() if ta else A
     C = torch.empty((M, N), device=DEV)
     g.gemm(a, B, out=C)
     torch.cuda.synchronize()
     table = g.gemm_kernel_name(g.gemm_last_kernel())
     reps = max(3, min(50, int(2e10 / (2 * M * N * K))))
-    code = g.F32 if dtype == "f32" else g.BF16
+    code = {"f32": g.F32, "bf16": g.BF16, "fp8": g.FP8}[dtype]
     times = {}
     for name in g.kernel_names():
         if g.gemm_kernel_dtype(g.kernel_id(name)) != code or name.startswith("naive"):
