@@ -61,6 +61,7 @@ const KernelInfo kKernels[] = {
     {"mfma_bf16_direct64", kBF16, launch_mfma_bf16_direct64, supports_mfma_bf16_direct, true},
     {"mfma_bf16_wsplit64", kBF16, launch_mfma_bf16_wsplit, supports_mfma_bf16_wsplit, true},
     {"mfma_fp8_direct256", kFp8, launch_mfma_fp8_direct256, supports_mfma_fp8_direct, true},
+    {"mfma_bf16_wsplit64x2", kBF16, launch_mfma_bf16_wsplit2, supports_mfma_bf16_wsplit2, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -245,8 +246,12 @@ int select_bf16_direct(const Problem &p)
     if (t128 < kCUs) {
         const int64_t t64 = ceil_div(p.M, 64) * ceil_div(p.N, 64) * p.batch;
         // A long K over at most one 64 x 64 tile per CU: split K over the
-        // waves of each tile (four MFMAs per slice instead of one).
-        if (p.batch == 1 && p.K >= 2048 && t64 <= kCUs) return kernel_id("mfma_bf16_wsplit64");
+        // waves of each tile (four MFMAs per slice instead of one), and with
+        // at most 3/4 of a tile per CU also over two work-groups per tile
+        // adding into C (384 x 1152 x 16384, operands cold: 70.8 -> 43.1 us;
+        // 144 tiles, 384 x 1536 x 16384: 80.4 -> 70.4 us).
+        if (p.batch == 1 && p.K >= 2048 && t64 <= kCUs)
+            return 4 * t64 <= 3 * kCUs ? kernel_id("mfma_bf16_wsplit64x2") : kernel_id("mfma_bf16_wsplit64");
         const int64_t c64 = ceil_div(t64, kCUs) * 64 * 64 * 1000 / BF16_DIRECT_64;
         const int64_t c128 = 128 * 128 * 1000 / 410;
         if (t64 <= 5 * kCUs && c64 < c128) return kernel_id("mfma_bf16_direct64");

@@ -1436,7 +1436,24 @@ __device__ __forceinline__ void ws_phase(f32x16 (&acc)[2][2], const Frag16<128, 
     }
 }
 
-template <bool TA, bool TB, bool kF16>
+// C (M x N, row stride ldc) set to -0.0, the identity of fp32 addition:
+// -0 + x is x for every x, +0 and -0 included.
+__global__ __launch_bounds__(256) void fill_neg_zero_kernel(float *__restrict__ C, int64_t ldc,
+                                                            int64_t M, int64_t N)
+{
+    const int64_t total = M * N;
+    for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * 256)
+        C[(i / N) * ldc + i % N] = -0.0f;
+}
+
+// kSplit2: two work-groups per tile, the first and the second half of the
+// K tiles, each adding its sums into C (set to -0.0 beforehand) with one
+// atomic add per element.  Two addends onto -0.0 give p0 + p1 rounded once
+// in either order (fp32 addition commutes), so the result is the same on
+// every run and equals a fixed-order two-way reduction; it needs no memory
+// beyond C.
+template <bool TA, bool TB, bool kF16, bool kSplit2 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mfma_bf16_wsplit_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__restrict__ A,
                              int64_t lda, const uint16_t *__restrict__ B, int64_t ldb,
@@ -1444,8 +1461,19 @@ void mfma_bf16_wsplit_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * WS_RING];
 
-    const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
-    const int64_t m0 = t.tm * 64, n0 = t.tn * 64;
+    int64_t m0, n0, kt0 = 0, kt1 = K / DBK;   // this work-group's K tiles [kt0, kt1)
+    if constexpr (kSplit2) {
+        const BatchTile t = map_batch_tile(tiles_m, tiles_n, 2, kGroup);
+        m0 = t.tm * 64;
+        n0 = t.tn * 64;
+        const int64_t mid = (kt1 + 1) / 2;
+        if (t.b == 0) kt1 = mid;
+        else kt0 = mid;
+    } else {
+        const TileCoord t = map_tile(tiles_m, tiles_n, kGroup);
+        m0 = t.tm * 64;
+        n0 = t.tn * 64;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, c = lane & 31, i16 = lane & 15, nhalf = (lane >> 4) & 1;
@@ -1515,13 +1543,13 @@ void mfma_bf16_wsplit_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // This wave's K tiles: wave, wave + 4, ...; past the last, the last one
-    // is re-fetched (landed, never used).
-    const int64_t ktiles = K / DBK;
+    // This wave's K tiles: kt0 + wave, kt0 + wave + 4, ... below kt1; past
+    // the last, the last one is re-fetched (landed, never used).
+    const int64_t ktiles = kt1 - kt0;
     const int64_t nj = ktiles > wave ? (ktiles - wave + 3) / 4 : 0;
     auto ktile = [&](int64_t j) {
         const int64_t kt = wave + 4 * j;
-        return kt < ktiles ? kt : ktiles - 1;
+        return kt0 + (kt < ktiles ? kt : ktiles - 1);
     };
     auto stage_ptr = [&](int64_t j) {
         return reinterpret_cast<const char *>(lds) + wave * WS_RING + (j % DSTAGES) * WS_STAGE;
@@ -1566,7 +1594,21 @@ void mfma_bf16_wsplit_kernel(int64_t M, int64_t N, int64_t K, const uint16_t *__
             for (int w = 0; w < 3; ++w) v += part[((w * 4 + b) * 16 + r) * 64 + lane];
             acc[b >> 1][b & 1][r] = v;
         }
-    store_c(acc, C, ldc, M, N, m0, n0, 0, 0, lane);
+    if constexpr (kSplit2) {
+        // register r of block b in lane (h, c): row 8 (r / 4) + 4 h + r % 4,
+        // column c of that 32 x 32 block (as store_c)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int64_t col = n0 + (b & 1) * 32 + c;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + (b >> 1) * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < M && col < N) unsafeAtomicAdd(C + row * ldc + col, acc[b >> 1][b & 1][r]);
+            }
+        }
+    } else {
+        store_c(acc, C, ldc, M, N, m0, n0, 0, 0, lane);
+    }
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -1688,6 +1730,11 @@ bool supports_mfma_bf16_wsplit(const Problem &p)
     return p.batch == 1 && supports_mfma_bf16_direct(p);
 }
 
+bool supports_mfma_bf16_wsplit2(const Problem &p)
+{
+    return supports_mfma_bf16_wsplit(p) && p.K >= 2 * DBK;
+}
+
 namespace {
 template <bool TA, bool TB>
 void launch_wsplit_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
@@ -1706,6 +1753,34 @@ hipError_t launch_mfma_bf16_wsplit(const Problem &p, hipStream_t s)
     else if (p.ta) launch_wsplit_layout<true, false>(p, s, tm, tn);
     else if (p.tb) launch_wsplit_layout<false, true>(p, s, tm, tn);
     else launch_wsplit_layout<false, false>(p, s, tm, tn);
+    return hipGetLastError();
+}
+
+namespace {
+template <bool TA, bool TB>
+void launch_wsplit2_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
+{
+    hipLaunchKernelGGL((mfma_bf16_wsplit_kernel<TA, TB, false, true>),
+                       dim3(static_cast<uint32_t>(2 * tm * tn)), dim3(kThreads), 0, s, p.M, p.N,
+                       p.K, static_cast<const uint16_t *>(p.A), p.lda,
+                       static_cast<const uint16_t *>(p.B), p.ldb, p.C, p.ldc, tm, tn);
+}
+}  // namespace
+
+// The same tiles with the K range split over two work-groups per tile (twice
+// the CUs streaming operands); C is first set to -0.0 by a fill kernel on
+// the same stream.  K of at least two 32-wide tiles.
+hipError_t launch_mfma_bf16_wsplit2(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + 63) / 64, tn = (p.N + 63) / 64;
+    if (2 * tm * tn > kMaxBlocks || !supports_mfma_bf16_wsplit2(p)) return hipErrorInvalidValue;
+    const int64_t fill_blocks = (p.M * p.N + 255) / 256 < 2048 ? (p.M * p.N + 255) / 256 : 2048;
+    hipLaunchKernelGGL(fill_neg_zero_kernel, dim3(static_cast<uint32_t>(fill_blocks)), dim3(256), 0, s,
+                       p.C, p.ldc, p.M, p.N);
+    if (p.ta && p.tb) launch_wsplit2_layout<true, true>(p, s, tm, tn);
+    else if (p.ta) launch_wsplit2_layout<true, false>(p, s, tm, tn);
+    else if (p.tb) launch_wsplit2_layout<false, true>(p, s, tm, tn);
+    else launch_wsplit2_layout<false, false>(p, s, tm, tn);
     return hipGetLastError();
 }
 

@@ -247,6 +247,8 @@ def test_plan_batched_tile_choice():
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 384, 1152, 16384, 1)) == \
         "mfma_f32_batched_splitk"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 16384, 1)) == \
+        "mfma_bf16_wsplit64x2"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 1024, 1024, 16384, 1)) == \
         "mfma_bf16_wsplit64"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 1024, 1)) == \
         "mfma_bf16_direct64"

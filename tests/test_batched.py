@@ -35,7 +35,7 @@ LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mf
 GENERAL["f16"] = ["mfma_f16_batched", "mfma_f16_batched128"]
 ALL = {"f32": GENERAL["f32"] + LDS_F32,
        "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128", "mfma_bf16_direct64",
-                                  "mfma_bf16_wsplit64"],
+                                  "mfma_bf16_wsplit64", "mfma_bf16_wsplit64x2"],
        "f16": GENERAL["f16"] + ["mfma_f16_direct", "mfma_f16_direct128"]}
 TDT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 DTYPES = ["f32", "bf16", "f16"]
@@ -136,15 +136,19 @@ def test_small_integer_exact(dtype, kernel, ta, tb):
         pytest.skip(f"{kernel} takes none of these layouts")
 
 
+@pytest.mark.parametrize("kernel", ["mfma_bf16_wsplit64", "mfma_bf16_wsplit64x2"])
 @pytest.mark.parametrize("ta,tb", TRANS)
-def test_wsplit64_k_split_over_waves_exact(ta, tb):
+def test_wsplit64_k_split_over_waves_exact(ta, tb, kernel):
     # the bf16 64 x 64 tile whose waves take every fourth K tile: a single
     # product, K tile counts that leave the waves unequal shares (65 tiles)
-    # or none at all (2 tiles), ragged tile edges, the weight-gradient shape
-    kernel = "mfma_bf16_wsplit64"
-    ran = [exact_case("bf16", kernel, ta, tb, M, N, K, 1, seed)
-           for (M, N, K, seed) in [(384, 1152, 4096, 61), (200, 136, 2080, 62), (72, 64, 64, 63),
-                                   (8, 8, 32, 64), (520, 264, 2048, 65)]]
+    # or none at all (2 tiles), ragged tile edges, the weight-gradient shape;
+    # x2: the K tiles also split over two work-groups adding into C (odd
+    # counts give the halves unequal shares, 2 tiles one each)
+    shapes = [(384, 1152, 4096, 61), (200, 136, 2080, 62), (72, 64, 64, 63), (520, 264, 2048, 65),
+              (136, 72, 96, 66)]
+    if kernel == "mfma_bf16_wsplit64":
+        shapes.append((8, 8, 32, 64))
+    ran = [exact_case("bf16", kernel, ta, tb, M, N, K, 1, seed) for (M, N, K, seed) in shapes]
     assert all(ran), "the kernel refused a layout it takes"
 
 
