@@ -62,6 +62,7 @@ const KernelInfo kKernels[] = {
     {"mfma_bf16_wsplit64", kBF16, launch_mfma_bf16_wsplit, supports_mfma_bf16_wsplit, true},
     {"mfma_fp8_direct256", kFp8, launch_mfma_fp8_direct256, supports_mfma_fp8_direct, true},
     {"mfma_bf16_wsplit64x2", kBF16, launch_mfma_bf16_wsplit2, supports_mfma_bf16_wsplit2, true},
+    {"mfma_f32_direct64x2", kF32, launch_mfma_f32_direct64x2, supports_mfma_f32_direct64x2, true},
 };
 constexpr int kNumKernels = static_cast<int>(sizeof(kKernels) / sizeof(kKernels[0]));
 
@@ -261,8 +262,26 @@ int select_bf16_direct(const Problem &p)
                : kernel_id("mfma_bf16_direct128");
 }
 
+// fp32 single products with a small output over a long K: the 64 x 64
+// LDS-direct tile with its K tiles split over two work-groups per tile
+// (mfma_f32_direct64x2).  Measured against the split-K, 64 x 64 and larger
+// tiles (operands resident): it wins with 65-192 tiles of 64 x 64 (640 x
+// 640 x 2048: 27.4 vs 41.2 us for the 64 x 64 tile; 384 x 1152 x 16384, A
+// transposed: 181 vs 308 us for the split-K kernel; 384 x 1152 x 1024: 18.5
+// vs 23.6) and, with at most 64 tiles, from K = 8192 (512 x 512 x 8192: 82.4
+// vs 94.2); with 196-256 tiles it ties or loses (1024 x 1024 x 1024: 30.1 vs
+// 24.6), and with a short K the split-K kernel keeps its lead (512 x 512 x
+// 2048: 25.1 vs 23.5).
+bool f32_k_split_pays(const Problem &p)
+{
+    if (p.dtype != kF32 || !supports_mfma_f32_direct64x2(p) || p.K < 1024) return false;
+    const int64_t t64 = ceil_div(p.M, 64) * ceil_div(p.N, 64);
+    return (4 * t64 > kCUs && 4 * t64 <= 3 * kCUs) || (4 * t64 <= kCUs && p.K >= 8192);
+}
+
 int select_general(const Problem &p)
 {
+    if (f32_k_split_pays(p)) return kernel_id("mfma_f32_direct64x2");
     // fp32 with fewer 128 x 128 tiles over all products than CUs and a K of
     // at least 256 (weight gradients: a small output summed over a long K;
     // per-head probabilities x values): the split-K kernel, whose 32 x 32
@@ -348,6 +367,7 @@ int select_kernel(const Problem &p)
     // waves, so each wave runs a quarter of the dependent MFMA chain (256^3:
     // 5.4 vs 7.8 us; 512 x 512 x 4096: 47.7 vs 73.7; 640 x 640 x 2048, 100
     // tiles: 42.2 vs 39.0, so the larger tiles win from there on).
+    if (f32_k_split_pays(p)) return kernel_id("mfma_f32_direct64x2");
     if ((p.M + 63) / 64 * ((p.N + 63) / 64) <= kCUs / 4) return kernel_id("mfma_f32_splitk");
     const int lds = select_f32_lds(p);
     if (lds >= 0) return lds;

@@ -115,6 +115,8 @@ hipError_t launch_mfma_fp8_direct256(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_direct64(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_wsplit(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_bf16_wsplit2(const Problem &p, hipStream_t s);
+hipError_t launch_mfma_f32_direct64x2(const Problem &p, hipStream_t s);
+bool supports_mfma_f32_direct64x2(const Problem &p);
 bool supports_mfma_bf16_wsplit(const Problem &p);
 bool supports_mfma_bf16_wsplit2(const Problem &p);
 bool supports_mfma_fp8_direct(const Problem &p);

@@ -523,8 +523,11 @@ __device__ __forceinline__ void read_one(FragG<BM, BN, TA, TB> &f, const float *
 // The MFMAs of group `cur`: the reads of `nxt` go out after MFMAs 0, 2, ..
 // (well ahead of their use), and (if loads) this wave's LDS-direct loads
 // of a later tile after the load slots.  sched_barrier(0) pins that order.
+// 64 x 64 tiles (one 32 x 32 block per wave): odd K steps accumulate into
+// acc_odd, so consecutive MFMAs are independent instead of one dependent
+// chain (added to acc after the K loop); other tiles leave acc_odd unused.
 template <int BM, int BN, int kW, bool TA, bool TB>
-__device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
+__device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64], f32x16 &acc_odd,
                                                const FragG<BM, BN, TA, TB> &cur,
                                                FragG<BM, BN, TA, TB> &nxt, const float *rstage,
                                                const DCtx<BM, BN, kW, TA, TB> &x, int g_next,
@@ -534,8 +537,13 @@ __device__ __forceinline__ void mfma_phase_f32(f32x16 (&acc)[BM / 64][BN / 64],
 #pragma unroll
     for (int q = 0; q < T::kQ; ++q) {
         const int j = q / (T::kMB * T::kNB), mb = (q / T::kNB) % T::kMB, nb = q % T::kNB;
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.av(mb, j), cur.bv(j, nb),
-                                                            acc[mb][nb], 0, 0, 0);
+        if constexpr (BM == 64 && BN == 64) {
+            f32x16 &a = (q & 1) ? acc_odd : acc[0][0];
+            a = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.av(0, j), cur.bv(j, 0), a, 0, 0, 0);
+        } else {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(cur.av(mb, j), cur.bv(j, nb),
+                                                                acc[mb][nb], 0, 0, 0);
+        }
         const bool rd = T::kReadEveryOther ? (q < 2 * T::kReads && (q & 1) == 0) : q < T::kReads;
         if constexpr (T::kSpreadLoads) {
             __builtin_amdgcn_sched_barrier(0);
@@ -619,8 +627,12 @@ __device__ __forceinline__ void store_c_rows_f32(const f32x16 (&acc)[BM / 64][BN
 // kBatch: a batch of products (stride_a, stride_b, stride_c elements apart)
 // runs as one grid of (product, tile) work-groups.  A single product keeps
 // the plain tile map (no division by the tile count, no pointer offsets).
+// kSplit2 (a single product, kW == 16): two work-groups per tile, the first
+// and the second half of the K tiles, each adding its sums into C (set to
+// -0.0 beforehand) with one atomic add per element: p0 + p1 rounded once in
+// either order, so the result repeats exactly from run to run.
 template <int BM, int BN, int kW, bool kRowsC = false, bool TA = false, bool TB = false,
-          bool kBatch = false>
+          bool kBatch = false, bool kSplit2 = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(DTile<BM, BN, kW>::kPerCU, DTile<BM, BN, kW>::kPerCU)))
 void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__restrict__ A,
@@ -630,10 +642,18 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
 {
     using T = DTile<BM, BN, kW, TA, TB>;
     constexpr int MB = T::kMB, NB = T::kNB, WM = BM / 2, WN = BN / 2;
+    static_assert(!kSplit2 || (kW == 16 && !kBatch && !kRowsC), "two-way K split: aligned K, one product");
     __shared__ __attribute__((aligned(1024))) float lds[DSTAGES * T::kStageFloats];
 
-    int64_t m0, n0;
-    if constexpr (kBatch) {
+    int64_t m0, n0, kt0 = 0, kt_count = K / DBK;   // this work-group's K tiles
+    if constexpr (kSplit2) {
+        const BatchTile t = map_batch_tile(tiles_m, tiles_n, 2, kGroup);
+        m0 = t.tm * BM;
+        n0 = t.tn * BN;
+        const int64_t mid = (kt_count + 1) / 2;
+        kt0 = t.b ? mid : 0;
+        kt_count = t.b ? kt_count - mid : mid;
+    } else if constexpr (kBatch) {
         const BatchTile t = map_batch_tile(tiles_m, tiles_n, batch, kGroup);
         A += t.b * sa;
         B += t.b * sb;
@@ -663,6 +683,10 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
     // scalar registers (without it the compiler computed them with vector
     // instructions and a readfirstlane per load group: 151.4 -> 148.8
     // TFLOP/s at 8192^3).
+    if constexpr (kSplit2) {   // tile kt of this work-group is tile kt0 + kt of the product
+        x.abase += kt0 * x.a_kstride;
+        x.bbase += kt0 * x.b_kstride;
+    }
     x.abase = static_cast<const char *>(uniform_ptr(x.abase));
     x.bbase = static_cast<const char *>(uniform_ptr(x.bbase));
     x.a_kstride = uniform_i64(x.a_kstride);
@@ -752,7 +776,11 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int64_t ktiles = K / DBK;
+    f32x16 acc_odd;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_odd[r] = 0.f;
+
+    const int64_t ktiles = kt_count;
     auto stage = [&](int64_t kt) { return lds + (kt % DSTAGES) * T::kStageFloats; };
     auto lstage = [&](int64_t kt) {
         return x.lds0 + static_cast<uint32_t>(kt % DSTAGES) * T::kStageFloats * 4;
@@ -782,9 +810,9 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
         // landed stage, unused).
         for (int64_t kt = 0; kt < ktiles; ++kt) {
             const int64_t nxt = kt + DSTAGES - 1;
-            mfma_phase_f32(acc, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
+            mfma_phase_f32(acc, acc_odd, f0, f1, stage(kt), x, 1, lstage(nxt), kclamp(nxt), true);
             wait_lds_vm_barrier<(DSTAGES - 2) * T::kPerTile>();
-            mfma_phase_f32(acc, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
+            mfma_phase_f32(acc, acc_odd, f1, f0, stage(kt + 1), x, 0, 0, 0, false);
         }
         // No LDS-direct load may still be writing LDS when the work-group
         // ends or stage 0 is refilled below.
@@ -815,13 +843,34 @@ void mfma_f32_direct_kernel(int64_t M, int64_t N, int64_t K, const float *__rest
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < T::kReads; ++i) read_one(f0, stage(0), x, 0, i);
-            mfma_phase_f32(acc, f0, f1, stage(0), x, 1, 0, 0, false);
-            mfma_phase_f32(acc, f1, f0, stage(0), x, 0, 0, 0, false);
+            mfma_phase_f32(acc, acc_odd, f0, f1, stage(0), x, 1, 0, 0, false);
+            mfma_phase_f32(acc, acc_odd, f1, f0, stage(0), x, 0, 0, 0, false);
         }
     }
 
+    if constexpr (BM == 64 && BN == 64) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][0][r] += acc_odd[r];
+    }
     if constexpr (kRowsC) {
         store_c_rows_f32<BM, BN, kW, TA, TB>(acc, lds, C, ldc, M, N, m0, n0, wm, wn, lane);
+        return;
+    }
+    if constexpr (kSplit2) {
+        // the epilogue's mapping below, one atomic add per element
+        const int64_t col0 = n0 + wn * WN + (TB ? c : NB * c);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r >> 2) + 4 * h + (r & 3);
+                const int64_t row = m0 + wm * WM + (TA ? MB * i + mb : mb * 32 + i);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int64_t col = col0 + (TB ? 32 * nb : nb);
+                    if (row < M && col < N) unsafeAtomicAdd(C + row * ldc + col, acc[mb][nb][r]);
+                }
+            }
         return;
     }
     // Epilogue: register r of block (mb, nb) in lane (h, c) is the MFMA
@@ -938,6 +987,51 @@ hipError_t launch_mfma_f32_narrow128(const Problem &p, hipStream_t s) { return l
 hipError_t launch_mfma_f32_direct128x64(const Problem &p, hipStream_t s) { return launch_direct<128, 64, 16>(p, s); }
 hipError_t launch_mfma_f32_narrow128x64(const Problem &p, hipStream_t s) { return launch_direct<128, 64, 4>(p, s); }
 hipError_t launch_mfma_f32_direct64(const Problem &p, hipStream_t s) { return launch_direct<64, 64, 16>(p, s); }
+
+namespace {
+
+// C (M x N, row stride ldc) set to -0.0, the identity of fp32 addition.
+__global__ __launch_bounds__(256) void f32_fill_neg_zero_kernel(float *__restrict__ C, int64_t ldc,
+                                                                int64_t M, int64_t N)
+{
+    const int64_t total = M * N;
+    for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < total;
+         i += int64_t(gridDim.x) * 256)
+        C[(i / N) * ldc + i % N] = -0.0f;
+}
+
+template <bool TA, bool TB>
+void launch_direct64x2_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
+{
+    hipLaunchKernelGGL((mfma_f32_direct_kernel<64, 64, 16, false, TA, TB, false, true>),
+                       dim3(static_cast<uint32_t>(2 * tm * tn)), dim3(kThreads), 0, s, p.M, p.N, p.K,
+                       static_cast<const float *>(p.A), p.lda, static_cast<const float *>(p.B),
+                       p.ldb, p.C, p.ldc, tm, tn, 0, p.sa, p.sb, p.sc, p.batch);
+}
+
+}  // namespace
+
+bool supports_mfma_f32_direct64x2(const Problem &p)
+{
+    return p.batch == 1 && p.K >= 2 * 16 && supports_mfma_f32_direct(p);
+}
+
+// The 64 x 64 LDS-direct tile with the K tiles split over two work-groups
+// per tile (small outputs over a long K: every CU streams operands); C is
+// first set to -0.0 by a fill kernel on the same stream.
+hipError_t launch_mfma_f32_direct64x2(const Problem &p, hipStream_t s)
+{
+    const int64_t tm = (p.M + 63) / 64, tn = (p.N + 63) / 64;
+    if (2 * tm * tn > kMaxBlocks || !supports_mfma_f32_direct64x2(p)) return hipErrorInvalidValue;
+    const int64_t fill_blocks = (p.M * p.N + 255) / 256 < 2048 ? (p.M * p.N + 255) / 256 : 2048;
+    hipLaunchKernelGGL(f32_fill_neg_zero_kernel, dim3(static_cast<uint32_t>(fill_blocks)), dim3(256),
+                       0, s, p.C, p.ldc, p.M, p.N);
+    if (p.ta && p.tb) launch_direct64x2_layout<true, true>(p, s, tm, tn);
+    else if (p.ta) launch_direct64x2_layout<true, false>(p, s, tm, tn);
+    else if (p.tb) launch_direct64x2_layout<false, true>(p, s, tm, tn);
+    else launch_direct64x2_layout<false, false>(p, s, tm, tn);
+    return hipGetLastError();
+}
 hipError_t launch_mfma_f32_narrow64(const Problem &p, hipStream_t s) { return launch_direct<64, 64, 4>(p, s); }
 
 }  // namespace mi355gemm

@@ -175,7 +175,12 @@ def test_dispatch_layout_cases():
     # at most 64 tiles of 64 x 64: the split-K kernel (any layout)
     assert name(g.F32, 512, 512, 4096, A=PA, B=PB, C=PC) == "mfma_f32_splitk"
     assert name(g.F32, 100, 300, 777, A=PA, B=PB, C=PC) == "mfma_f32_splitk"
-    assert name(g.F32, 640, 640, 2048, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
+    # 65-192 tiles of 64 x 64 over a long K (or at most 64 from K = 8192):
+    # the 64 x 64 tile with K split over two work-groups per tile
+    assert name(g.F32, 640, 640, 2048, A=PA, B=PB, C=PC) == "mfma_f32_direct64x2"
+    assert name(g.F32, 512, 512, 8192, A=PA, B=PB, C=PC) == "mfma_f32_direct64x2"
+    assert name(g.F32, 640, 640, 512, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
+    assert name(g.F32, 1024, 1024, 1024, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
     # a few hundred tiles or fewer: the 64 x 64 tiles, five per CU
     assert name(g.F32, 1000, 3000, 784, A=PA, B=PB, C=PC) == "mfma_f32_direct64"
     assert name(g.F32, 1000, 3000, 777, A=PA, B=PB, C=PC) == "mfma_f32_narrow64"
@@ -201,7 +206,7 @@ def test_dispatch_layout_cases():
 GENERAL_NAMES = {g.F32: ("mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk",
                          "mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64",
                          "mfma_f32_direct64", "mfma_f32_narrow128", "mfma_f32_narrow128x64",
-                         "mfma_f32_narrow64"),
+                         "mfma_f32_narrow64", "mfma_f32_direct64x2"),
                  g.BF16: ("mfma_bf16_batched", "mfma_bf16_batched128",
                           "mfma_bf16_direct", "mfma_bf16_direct128"),
                  g.F16: ("mfma_f16_batched", "mfma_f16_batched128",
@@ -245,6 +250,8 @@ def test_plan_batched_tile_choice():
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 1, 8188, 8192, 8192, 1)) == \
         "mfma_bf16_batched"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 384, 1152, 16384, 1)) == \
+        "mfma_f32_direct64x2"
+    assert g.gemm_kernel_name(g.gemm_plan_batched(g.F32, 1, 0, 384, 1152, 16384, 2)) == \
         "mfma_f32_batched_splitk"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.BF16, 1, 0, 384, 1152, 16384, 1)) == \
         "mfma_bf16_wsplit64x2"

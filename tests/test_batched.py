@@ -31,7 +31,7 @@ TRANS = [(False, False), (True, False), (False, True), (True, True)]
 GENERAL = {"f32": ["mfma_f32_batched", "mfma_f32_batched128", "mfma_f32_batched_splitk"],
            "bf16": ["mfma_bf16_batched", "mfma_bf16_batched128"]}
 LDS_F32 = ["mfma_f32_direct", "mfma_f32_direct128", "mfma_f32_direct128x64", "mfma_f32_direct64",
-           "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64"]
+           "mfma_f32_narrow128", "mfma_f32_narrow128x64", "mfma_f32_narrow64", "mfma_f32_direct64x2"]
 GENERAL["f16"] = ["mfma_f16_batched", "mfma_f16_batched128"]
 ALL = {"f32": GENERAL["f32"] + LDS_F32,
        "bf16": GENERAL["bf16"] + ["mfma_bf16_direct", "mfma_bf16_direct128", "mfma_bf16_direct64",
@@ -136,20 +136,22 @@ def test_small_integer_exact(dtype, kernel, ta, tb):
         pytest.skip(f"{kernel} takes none of these layouts")
 
 
-@pytest.mark.parametrize("kernel", ["mfma_bf16_wsplit64", "mfma_bf16_wsplit64x2"])
+@pytest.mark.parametrize("dtype,kernel", [("bf16", "mfma_bf16_wsplit64"), ("bf16", "mfma_bf16_wsplit64x2"),
+                                          ("f32", "mfma_f32_direct64x2")])
 @pytest.mark.parametrize("ta,tb", TRANS)
-def test_wsplit64_k_split_over_waves_exact(ta, tb, kernel):
-    # the bf16 64 x 64 tile whose waves take every fourth K tile: a single
-    # product, K tile counts that leave the waves unequal shares (65 tiles)
-    # or none at all (2 tiles), ragged tile edges, the weight-gradient shape;
-    # x2: the K tiles also split over two work-groups adding into C (odd
-    # counts give the halves unequal shares, 2 tiles one each)
+def test_k_split_kernels_exact(ta, tb, dtype, kernel):
+    # single products whose K range is split: the bf16 64 x 64 tile whose
+    # waves take every fourth K tile (K tile counts that leave the waves
+    # unequal shares or none at all); x2: the K tiles also split over two
+    # work-groups adding into C (odd tile counts give the halves unequal
+    # shares, two tiles one each); ragged tile edges, the weight-gradient
+    # shape
     shapes = [(384, 1152, 4096, 61), (200, 136, 2080, 62), (72, 64, 64, 63), (520, 264, 2048, 65),
-              (136, 72, 96, 66)]
+              (136, 72, 96, 66), (64, 128, 48, 67)]
     if kernel == "mfma_bf16_wsplit64":
         shapes.append((8, 8, 32, 64))
-    ran = [exact_case("bf16", kernel, ta, tb, M, N, K, 1, seed) for (M, N, K, seed) in shapes]
-    assert all(ran), "the kernel refused a layout it takes"
+    ran = [exact_case(dtype, kernel, ta, tb, M, N, K, 1, seed) for (M, N, K, seed) in shapes]
+    assert all(ran[:5]), "the kernel refused a layout it takes"
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -30,6 +30,8 @@ SHAPES = [
     ("f32", 16384, 384, 1536, False), ("f32", 1000, 3000, 777, False),
     ("f32", 4097, 4095, 1023, False), ("f32", 640, 640, 2048, False),
     ("f32", 1024, 1024, 4096, False), ("f32", 384, 1152, 16384, True),
+    ("f32", 512, 512, 8192, False), ("f32", 768, 768, 4096, False), ("f32", 384, 1152, 1024, True),
+    ("f32", 1024, 1024, 1024, False),
     ("bf16", 16384, 1152, 384, False), ("bf16", 16384, 384, 1536, False),
     ("bf16", 2048, 2048, 8192, False), ("bf16", 384, 1152, 16384, True),
     # 8-bit floats: B is always the transposed view of a row-major (N, K) tensor
