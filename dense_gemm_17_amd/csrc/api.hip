@@ -798,7 +798,7 @@ int attention_fwd_f32(int64_t B, int64_t H, int64_t S, int64_t D, int causal, fl
 
 int attention_force_kernel(int variant)
 {
-    if (variant < -1 || variant > 1) return hipErrorInvalidValue;
+    if (variant < -1 || variant > 2) return hipErrorInvalidValue;
     g_attn_forced.store(variant, std::memory_order_relaxed);
     return hipSuccess;
 }

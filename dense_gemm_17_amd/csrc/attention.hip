@@ -4,8 +4,10 @@
 // and sum from one tile of keys to the next).
 //
 // For one (sequence, head) the work-group takes 128 queries, 32 per wave,
-// and walks the keys in tiles of BN; each tile of K and V goes through LDS
-// once and serves all four waves.  Per tile, a wave
+// and walks the keys in tiles of BN (64, or 32 for sequences of up to 256
+// tokens, where the smaller LDS stages and register set let three
+// work-groups share a CU); each tile of K and V goes through LDS once and
+// serves all four waves.  Per tile, a wave
 //   1. computes the scores of its 32 queries against the tile's keys on the
 //      fp32 matrix cores, transposed (S^T = K Q^T): in the 32 x 32 MFMA
 //      accumulator a lane owns one column, so here a lane owns one query and
@@ -77,7 +79,7 @@ __device__ __forceinline__ float masked(float x, uint32_t keep)
 }
 
 template <int D, int BN>
-__global__ __launch_bounds__(kAttnThreads, 2) void attention_fwd_kernel(AttnArgs a)
+__global__ __launch_bounds__(kAttnThreads, (D == 64 && BN == 32) ? 3 : 2) void attention_fwd_kernel(AttnArgs a)
 {
     using C = AttnCfg<D, BN>;
     __shared__ __attribute__((aligned(16))) float lds[2 * C::kStage];
@@ -508,10 +510,15 @@ int attention_variant(int64_t B, int64_t H, int64_t S, int64_t D, int forced)
 {
     const int64_t blocks = (S + kBM - 1) / kBM * B * H;
     if (D != 64) return 0;
-    if (forced == 0 || forced == 1) return forced;
+    if (forced >= 0 && forced <= 2) return forced;
     // Fewer 128-query work-groups than CUs: split the keys over the waves of
-    // 32-query work-groups instead.
-    return blocks < kCUs ? 1 : 0;
+    // 32-query work-groups instead.  Up to 256 tokens, 32-key tiles (half the
+    // LDS and 146 instead of 202 registers: three work-groups per CU) beat
+    // 64-key tiles (GPT 64 x 6 x 256 causal 60.5 -> 53.2 us, full 68.6 ->
+    // 66.8, 128 tokens causal 41.9 -> 38.8); from 384 tokens on the longer
+    // tiles win (384 causal 53.3 vs 56.7, 2048 causal 266 vs 284).
+    if (blocks < kCUs) return 1;
+    return S <= 256 ? 2 : 0;
 }
 
 hipError_t launch_attention_fwd(const AttnArgs &args, int64_t D, int variant, hipStream_t s)
@@ -530,7 +537,9 @@ hipError_t launch_attention_fwd(const AttnArgs &args, int64_t D, int variant, hi
         return hipGetLastError();
     }
     const dim3 grid(static_cast<uint32_t>(blocks));
-    if (D == 64)
+    if (D == 64 && variant == 2)
+        hipLaunchKernelGGL((attention_fwd_kernel<64, 32>), grid, dim3(kAttnThreads), 0, s, a);
+    else if (D == 64)
         hipLaunchKernelGGL((attention_fwd_kernel<64, 64>), grid, dim3(kAttnThreads), 0, s, a);
     else if (D == 128)
         hipLaunchKernelGGL((attention_fwd_kernel<128, 32>), grid, dim3(kAttnThreads), 0, s, a);

@@ -58,7 +58,8 @@ struct AttnArgs {
 };
 // Attention kernels: 0 = 128 queries per work-group, key tiles through LDS;
 // 1 = 32 queries per work-group, key tiles split over its waves (head width
-// 64).  attention_variant picks one (forced >= 0 overrides where it can).
+// 64); 2 = kernel 0 with 32-key tiles (head width 64).  attention_variant
+// picks one (forced >= 0 overrides where it can).
 int attention_variant(int64_t B, int64_t H, int64_t S, int64_t D, int forced);
 hipError_t launch_attention_fwd(const AttnArgs &a, int64_t D, int variant, hipStream_t s);
 

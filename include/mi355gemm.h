@@ -369,14 +369,16 @@ int attention_fwd_f32(int64_t B, int64_t H, int64_t S, int64_t D, int causal, fl
                       float *O, int64_t o_sb, int64_t o_sh, int64_t o_ss, float *lse,
                       hipStream_t stream);
 
-/* Test hooks of attention_fwd_f32 (not for users): force one of its two
+/* Test hooks of attention_fwd_f32 (not for users): force one of its three
  * kernels for calls that can take it -- 0: 128 queries per work-group with
- * the key tiles staged through LDS for four waves; 1: 32 queries per
+ * 64-key tiles staged through LDS for four waves; 1: 32 queries per
  * work-group with the key tiles split over its four waves and the partial
  * softmaxes merged at the end (head width 64; chosen by default where the
- * first would launch fewer work-groups than the GPU has CUs) -- or -1 for
- * the default choice; and the kernel the last successful call ran (-1
- * before any).  Process-global. */
+ * first would launch fewer work-groups than the GPU has CUs); 2: kernel 0
+ * with 32-key tiles (head width 64; chosen by default for sequences of up
+ * to 256 tokens) -- or -1 for the default choice; and the kernel the last
+ * successful call ran (-1 before any).  Process-global; returns
+ * hipErrorInvalidValue outside -1 .. 2. */
 int attention_force_kernel(int variant);
 int attention_last_kernel(void);
 

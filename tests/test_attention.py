@@ -100,7 +100,7 @@ def test_workloads_in_place_from_qkv_buffer(name):
 
 @pytest.mark.parametrize("S", [1, 2, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 257, 385])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_ragged_lengths(S, causal, variant):
     B, H, D = 2, 3, 64
     check(rand((B, H, S, D), S), rand((B, H, S, D), S + 1000), rand((B, H, S, D), S + 2000),
@@ -119,6 +119,18 @@ def test_single_sequence_default_kernel(causal):
           name="one sequence of 2048", variant=1)
 
 
+@pytest.mark.parametrize("S,want", [(256, 2), (128, 2), (384, 0), (1024, 0)])
+def test_default_kernel_by_length(S, want):
+    # enough work-groups for the CUs: 32-key tiles up to 256 tokens, 64-key
+    # tiles beyond
+    H, D = 6, 64
+    B = -(-256 // (-(-S // 128) * H))          # 128-query work-groups >= CUs
+    assert g.attention_force_kernel(-1) == 0
+    check(rand((B, H, S, D), S + 90), rand((B, H, S, D), S + 91), rand((B, H, S, D), S + 92), True,
+          name=f"default S={S}")
+    assert g.attention_last_kernel() == want
+
+
 @pytest.mark.parametrize("S", [1, 33, 96, 128, 130, 300])
 @pytest.mark.parametrize("causal", [False, True])
 def test_head_width_128(S, causal):
@@ -127,7 +139,7 @@ def test_head_width_128(S, causal):
           causal, name=f"D=128 S={S}")
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_large_scores_and_scale(variant):
     # scores of order 1000, far past fp32's exponential range: the running
     # maximum keeps every exponential finite
@@ -140,7 +152,7 @@ def test_large_scores_and_scale(variant):
           scale=0.01, name="flat scores", variant=variant)
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_dominant_key_is_exact(variant):
     # key j* scores 2^10 above every other key: every other exponential is
     # exactly 0 in fp32, so the output is the value row of j*, bit for bit
@@ -161,7 +173,7 @@ def test_dominant_key_is_exact(variant):
     assert torch.equal(Oc[0, 0, 0], v[0, 0, 0])
 
 
-@pytest.mark.parametrize("variant", [0, 1])
+@pytest.mark.parametrize("variant", [0, 1, 2])
 def test_uniform_scores_give_the_mean(variant):
     B, H, S, D = 2, 2, 150, 64
     q = torch.zeros((B, H, S, D))
@@ -177,7 +189,7 @@ def test_key_value_permutation():
     B, H, S, D = 1, 2, 160, 64
     q, k, v = rand((B, H, S, D), 10), rand((B, H, S, D), 11), rand((B, H, S, D), 12)
     perm = torch.randperm(S, generator=workloads.generator(13))
-    for variant in (0, 1):
+    for variant in (0, 1, 2):
         O1 = check(q, k, v, False, name="perm a", variant=variant)
         O2 = check(q, k[:, :, perm], v[:, :, perm], False, name="perm b", variant=variant)
         assert torch.allclose(O1, O2, rtol=0, atol=1e-5)
