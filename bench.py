@@ -59,7 +59,7 @@ CSRC = os.path.join(ROOT, "dense_gemm_17_amd", "csrc")
 KERNEL_SOURCES = {
     "mfma_f32": ("mfma_f32_kernel<256, 256, true>", ["mfma_f32.hip"]),
     "mfma_f32_128": ("mfma_f32_kernel<128, 128, true>", ["mfma_f32.hip"]),
-    "mfma_f32_direct": ("mfma_f32_direct_kernel<256, 256, 16, false, false, false, false>",
+    "mfma_f32_direct": ("mfma_f32_direct_kernel<256, 256, 16, false, false, false, false, false>",
                         ["mfma_f32.hip"]),
     "mfma_bf16_direct": ("mfma_bf16_d16_kernel<true, false, false, false, false>",
                          ["mfma_bf16.hip"]),
