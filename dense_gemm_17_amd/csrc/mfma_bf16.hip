@@ -1,4 +1,6 @@
-// bf16-in / fp32-accumulate matrix-core family: v_mfma_f32_32x32x16_bf16.
+// bf16-in / fp32-accumulate matrix-core family: v_mfma_f32_32x32x16_bf16,
+// and v_mfma_f32_16x16x32_bf16 on the 256 x 256 LDS-direct tile (further
+// below); the 8-bit kernels share the staging.
 //
 // The matrix-instruction rung of the kernel ladder ("Bare Metal Bard", page
 // 1, first paragraph) with bf16 operands (vidyal.ai Part 6, "Tensor Cores":
@@ -6,6 +8,8 @@
 // conflicts, and what BF16 costs in accuracy).  A bf16 x bf16 product is
 // exact in fp32, so the only rounding is the fp32 accumulation.
 //
+// The register-staged kernel (mfma_bf16_kernel, any layout the others
+// refuse):
 //   * block tile 256 x 256, K step 64; 4 wave64s in a 2 x 2 grid, each
 //     owning 128 x 128 of C as 4 x 4 MFMA blocks of 32 x 32 (256 fp32
 //     accumulators per lane);
