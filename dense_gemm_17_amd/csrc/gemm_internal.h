@@ -80,6 +80,9 @@ struct KernelInfo {
 hipError_t launch_naive_f32(const Problem &p, hipStream_t s);
 hipError_t launch_naive_bf16(const Problem &p, hipStream_t s);
 hipError_t launch_fill_zero(const Problem &p, hipStream_t s);
+// C (p.M x p.N, row stride p.ldc) set to `value` (the K-split kernels that
+// add two halves into C start it at -0.0, the identity of fp32 addition).
+hipError_t launch_fill(const Problem &p, float value, hipStream_t s);
 hipError_t launch_null(hipStream_t s);
 hipError_t launch_valu_f32(const Problem &p, hipStream_t s);
 hipError_t launch_mfma_f32(const Problem &p, hipStream_t s);

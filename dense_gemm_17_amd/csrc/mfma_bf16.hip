@@ -1440,17 +1440,6 @@ __device__ __forceinline__ void ws_phase(f32x16 (&acc)[2][2], const Frag16<128, 
     }
 }
 
-// C (M x N, row stride ldc) set to -0.0, the identity of fp32 addition:
-// -0 + x is x for every x, +0 and -0 included.
-__global__ __launch_bounds__(256) void fill_neg_zero_kernel(float *__restrict__ C, int64_t ldc,
-                                                            int64_t M, int64_t N)
-{
-    const int64_t total = M * N;
-    for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < total;
-         i += int64_t(gridDim.x) * 256)
-        C[(i / N) * ldc + i % N] = -0.0f;
-}
-
 // kSplit2: two work-groups per tile, the first and the second half of the
 // K tiles, each adding its sums into C (set to -0.0 beforehand) with one
 // atomic add per element.  Two addends onto -0.0 give p0 + p1 rounded once
@@ -1778,9 +1767,9 @@ hipError_t launch_mfma_bf16_wsplit2(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + 63) / 64, tn = (p.N + 63) / 64;
     if (2 * tm * tn > kMaxBlocks || !supports_mfma_bf16_wsplit2(p)) return hipErrorInvalidValue;
-    const int64_t fill_blocks = (p.M * p.N + 255) / 256 < 2048 ? (p.M * p.N + 255) / 256 : 2048;
-    hipLaunchKernelGGL(fill_neg_zero_kernel, dim3(static_cast<uint32_t>(fill_blocks)), dim3(256), 0, s,
-                       p.C, p.ldc, p.M, p.N);
+    // -0.0 is the identity of fp32 addition: -0 + x is x for every x
+    const hipError_t e = launch_fill(p, -0.0f, s);
+    if (e != hipSuccess) return e;
     if (p.ta && p.tb) launch_wsplit2_layout<true, true>(p, s, tm, tn);
     else if (p.ta) launch_wsplit2_layout<true, false>(p, s, tm, tn);
     else if (p.tb) launch_wsplit2_layout<false, true>(p, s, tm, tn);

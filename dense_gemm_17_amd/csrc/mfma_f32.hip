@@ -990,16 +990,6 @@ hipError_t launch_mfma_f32_direct64(const Problem &p, hipStream_t s) { return la
 
 namespace {
 
-// C (M x N, row stride ldc) set to -0.0, the identity of fp32 addition.
-__global__ __launch_bounds__(256) void f32_fill_neg_zero_kernel(float *__restrict__ C, int64_t ldc,
-                                                                int64_t M, int64_t N)
-{
-    const int64_t total = M * N;
-    for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < total;
-         i += int64_t(gridDim.x) * 256)
-        C[(i / N) * ldc + i % N] = -0.0f;
-}
-
 template <bool TA, bool TB>
 void launch_direct64x2_layout(const Problem &p, hipStream_t s, int64_t tm, int64_t tn)
 {
@@ -1023,9 +1013,8 @@ hipError_t launch_mfma_f32_direct64x2(const Problem &p, hipStream_t s)
 {
     const int64_t tm = (p.M + 63) / 64, tn = (p.N + 63) / 64;
     if (2 * tm * tn > kMaxBlocks || !supports_mfma_f32_direct64x2(p)) return hipErrorInvalidValue;
-    const int64_t fill_blocks = (p.M * p.N + 255) / 256 < 2048 ? (p.M * p.N + 255) / 256 : 2048;
-    hipLaunchKernelGGL(f32_fill_neg_zero_kernel, dim3(static_cast<uint32_t>(fill_blocks)), dim3(256),
-                       0, s, p.C, p.ldc, p.M, p.N);
+    const hipError_t e = launch_fill(p, -0.0f, s);   // the identity of fp32 addition
+    if (e != hipSuccess) return e;
     if (p.ta && p.tb) launch_direct64x2_layout<true, true>(p, s, tm, tn);
     else if (p.ta) launch_direct64x2_layout<true, false>(p, s, tm, tn);
     else if (p.tb) launch_direct64x2_layout<false, true>(p, s, tm, tn);

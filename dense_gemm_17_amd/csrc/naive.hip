@@ -44,13 +44,13 @@ __global__ __launch_bounds__(256) void naive_kernel(int64_t M, int64_t N, int64_
     C[i * ldc + j] = acc;
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(int64_t M, int64_t N, float *__restrict__ C,
-                                                        int64_t ldc, int64_t col_blocks)
+__global__ __launch_bounds__(256) void fill_kernel(int64_t M, int64_t N, float *__restrict__ C,
+                                                   int64_t ldc, int64_t col_blocks, float value)
 {
     const int64_t blk = blockIdx.x;
     const int64_t j = (blk % col_blocks) * kCols + (threadIdx.x % kCols);
     const int64_t i = (blk / col_blocks) * kRows + (threadIdx.x / kCols);
-    if (i < M && j < N) C[i * ldc + j] = 0.0f;
+    if (i < M && j < N) C[i * ldc + j] = value;
 }
 
 template <typename T>
@@ -141,14 +141,16 @@ hipError_t launch_null(hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(const Problem &p, hipStream_t s)
+hipError_t launch_fill(const Problem &p, float value, hipStream_t s)
 {
     const int64_t cb = (p.N + kCols - 1) / kCols;
     const int64_t rb = (p.M + kRows - 1) / kRows;
     if (cb * rb > kMaxBlocks) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<uint32_t>(cb * rb)), dim3(256), 0, s,
-                       p.M, p.N, p.C, p.ldc, cb);
+    hipLaunchKernelGGL(fill_kernel, dim3(static_cast<uint32_t>(cb * rb)), dim3(256), 0, s, p.M, p.N,
+                       p.C, p.ldc, cb, value);
     return hipGetLastError();
 }
+
+hipError_t launch_fill_zero(const Problem &p, hipStream_t s) { return launch_fill(p, 0.0f, s); }
 
 }  // namespace mi355gemm
