@@ -492,10 +492,10 @@ def test_concurrent_host_threads_and_streams():
 
 
 def test_graph_capture_replays_match_eager():
-    """Calls captured into a HIP graph (no memset nodes: K = 0 is a fill
-    kernel) replay with the eager result, replay after replay, with eager
-    work and synchronisation between replays; plain, transposed and batched
-    calls in all three operand types."""
+    """Calls captured into a HIP graph (no memset nodes: K = 0 and the
+    two-work-group K split start C with a fill kernel) replay with the eager
+    result, replay after replay, with eager work and synchronisation between
+    replays; plain, transposed and batched calls in every operand type."""
     gen = workloads.generator(85)
     # (M, N, K, dtype, batch, A stored transposed, B stored transposed)
     specs = [(1024, 1024, 512, torch.float32, 1, False, False),
@@ -504,7 +504,9 @@ def test_graph_capture_replays_match_eager():
              (300, 260, 0, torch.float32, 1, False, False),
              (1000, 3000, 777, torch.float32, 1, False, False),
              (256, 256, 64, torch.float32, 12, False, True),       # batched, B^T
-             (384, 1152, 4096, torch.float32, 1, True, False),     # A^T, split-K
+             (384, 1152, 4096, torch.float32, 1, True, False),     # A^T, K over 2 work-groups
+             (384, 1152, 4096, torch.bfloat16, 1, True, False),    # the same in bf16
+             (2048, 2048, 1024, workloads.FP8_TORCH[0], 1, False, True),   # 8-bit 256^2 tile
              (512, 264, 96, torch.float16, 3, True, True),
              (300, 270, 100, torch.bfloat16, 2, True, False)]      # general family
     ins, eager, outs = [], [], []
