@@ -27,13 +27,17 @@
 //     row-split pairs and work-groups of 9-16 rows) and A's rows fit in 64
 //     KiB, the work-group first copies them into LDS (7 x 4096 x 4096:
 //     21.4 -> 20.2 us; 12 x 8960 x 1536: 32.1 -> 27.8);
-//   * when strips are fewer than CUs and there are more than 4 rows, each
-//     strip is split by rows between two work-groups whose ids land on the
-//     same XCD back to back, so all CUs stream B and the second read of each
-//     B line hits that XCD's L2 (1.26x at 7 x 4096 x 4096);
+//   * fp32 with 96-128 strips of 128 bytes and a long K splits each strip's
+//     K range between two work-groups (skinny_ksplit_kernel below), so every
+//     CU streams distinct bytes of B; the two halves add into C filled with
+//     -0.0 (two addends: the same bits whichever lands first);
+//   * otherwise, when strips are fewer than CUs and there are more than 4
+//     rows, each strip is split by rows between two work-groups whose ids
+//     land on the same XCD back to back, so all CUs stream B and the second
+//     read of each B line hits that XCD's L2 (1.26x at 7 x 4096 x 4096);
 //   * the partial sums of the K-groups are added in a fixed order (lane
 //     shuffles inside a wave, then LDS across waves), so the result is
-//     deterministic; no atomics, no workspace;
+//     deterministic; no workspace;
 //   * ragged N and unaligned B or A fall back to element loads with masks.
 #include "gemm_internal.h"
 #include "tile_map.h"
@@ -263,6 +267,235 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// K split over two work-groups (fp32, 1-16 rows, 96-128 strips of 128 bytes).
+//
+// With fewer strips than CUs, one work-group per strip leaves CUs idle, and
+// one CU pulls only about 25-30 GB/s from HBM however many loads it keeps in
+// flight, so the strips' CUs cannot reach the chip's bandwidth.  Here each
+// strip's K range is split in two halves, each streamed by its own
+// work-group (ids 16 q + x and 16 q + 8 + x: the same XCD), so every CU
+// streams distinct bytes of B.  The two partial strips are added into C,
+// which is first filled with -0.0: with exactly two addends the sum does
+// not depend on which arrives first (-0.0 + x = x, and x + y = y + x), so
+// the result is bitwise repeatable.
+//
+//   * a lane loads 16 bytes (4 columns) of 4 consecutive rows per step and,
+//     in the same step, the 16 bytes of A it needs for those rows; the next
+//     step's loads are issued before the current step's arithmetic, so every
+//     wave keeps a step of B in flight while it computes;
+//   * with 4 or more rows the arithmetic runs on the matrix cores:
+//     v_mfma_f32_4x4x1_16b_f32 forms sixteen independent 4 x 4 outer
+//     products per wave; lane l supplies the A value of row l % 4 and the B
+//     value of column l % 4 of block l / 4, and receives that column's four
+//     rows.  The four lanes of a block are half a K-group (same B row), so
+//     each lane's four columns (one per element of its 16-byte load) give
+//     four products, one per column offset, for each group of four rows;
+//   * one row uses plain FMAs (four per loaded element pair);
+//   * the wave and work-group sums use the fixed-order reduction of the
+//     kernels above.
+template <int kM, int kThreads, bool kAVec>
+__global__ __launch_bounds__(kThreads) void skinny_ksplit_kernel(int64_t M, int64_t N, int64_t K,
+                                                                 int64_t khalf,
+                                                                 const float *__restrict__ A, int64_t lda,
+                                                                 const float *__restrict__ B, int64_t ldb,
+                                                                 float *__restrict__ C, int64_t ldc)
+{
+    constexpr int kL = 8, P = 4, kCols = kL * P, kGroups = kThreads / kL, kWaves = kThreads / 64;
+    constexpr bool kMfma = kM >= 4;
+    constexpr int kH = kMfma ? kM / 4 : 1;      // groups of four rows (A loads per step)
+    constexpr int kStep = 4 + kH;                // 16-byte loads per step: 4 of B, kH of A
+    static_assert(kM == 1 || kM == 4 || kM == 8 || kM == 16, "compiled row counts");
+    __shared__ float red[kWaves * kM * kCols];
+
+    const int tid = threadIdx.x, lane = tid % kL, grp = tid / kL;
+    const int64_t id = blockIdx.x;
+    const int64_t part = (id >> 3) & 1;
+    const int64_t n0 = ((id >> 4) * 8 + (id & 7)) * kCols;
+    if (n0 >= N) return;                          // whole work-group
+    const int64_t k0 = part * khalf, k1 = part ? K : khalf;
+    const int64_t n = n0 + lane * P;
+    const int64_t nl = n < N ? n : N - P;         // past N: a valid column, sums dropped
+
+    // This lane's rows of A (rows past M read row 0; their sums are dropped).
+    int64_t arow[kH];
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+        const int r = kMfma ? 4 * h + (tid & 3) : 0;
+        arow[h] = (r < M ? r : 0) * lda;
+    }
+    // Byte offsets of this lane's B loads from the step's first row (32-bit:
+    // the launcher keeps 4 kGroups rows of B within 2^31 bytes).
+    uint32_t boff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) boff[r] = static_cast<uint32_t>(((4 * grp + r) * ldb + nl) * 4);
+
+    // Step j covers rows k0 + 4 (j kGroups + grp) .. + 3 of this lane.
+    auto load = [&](f32x4 *x, int64_t row0) {
+        const char *bb = reinterpret_cast<const char *>(B + row0 * ldb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = *reinterpret_cast<const f32x4 *>(bb + boff[r]);
+        const float *aa = A + row0 + 4 * grp;
+#pragma unroll
+        for (int h = 0; h < kH; ++h) {
+            if constexpr (kAVec) {
+                x[4 + h] = *reinterpret_cast<const f32x4 *>(aa + arow[h]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x[4 + h][r] = aa[arow[h] + r];
+            }
+        }
+    };
+
+    f32x4 macc[P][kH];
+    float facc[P];
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+        facc[e] = 0.f;
+#pragma unroll
+        for (int h = 0; h < kH; ++h) macc[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto compute = [&](const f32x4 *x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < P; ++e) {
+                if constexpr (kMfma) {
+#pragma unroll
+                    for (int h = 0; h < kH; ++h)
+                        macc[e][h] = __builtin_amdgcn_mfma_f32_4x4x1f32(x[4 + h][r], x[r][e], macc[e][h], 0, 0, 0);
+                } else {
+                    facc[e] = fmaf(x[4][r], x[r][e], facc[e]);
+                }
+            }
+    };
+
+    // Whole steps (every lane's four rows inside [k0, k1)), two register
+    // sets in turn so that no copy waits on a load in flight.
+    constexpr int64_t kRows = 4 * int64_t(kGroups);
+    const int64_t full = (k1 - k0) / kRows;
+    int64_t row0 = k0;
+    f32x4 xa[kStep], xb[kStep];
+    if (full > 0) {
+        load(xa, row0);
+        int64_t j = 1;
+        for (; j + 1 < full; j += 2) {
+            load(xb, row0 + kRows);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xa);
+            __builtin_amdgcn_sched_barrier(0);
+            row0 += kRows;
+            load(xa, row0 + kRows);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xb);
+            __builtin_amdgcn_sched_barrier(0);
+            row0 += kRows;
+        }
+        if (j < full) {
+            load(xb, row0 + kRows);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xa);
+            __builtin_amdgcn_sched_barrier(0);
+            row0 += kRows;
+            compute(xb);
+        } else {
+            compute(xa);
+        }
+        row0 += kRows;
+    }
+    // The rest of the half: this lane's rows past k1 (and the A values of
+    // columns of A past k1) are zero.  Every lane takes part (the matrix
+    // instruction works on the whole wave).
+    for (; row0 < k1; row0 += kRows) {
+        const int64_t k4 = row0 + 4 * grp;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            xa[r] = k4 + r < k1 ? *reinterpret_cast<const f32x4 *>(B + (k4 + r) * ldb + nl)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < kH; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xa[4 + h][r] = k4 + r < k1 ? A[arow[h] + k4 + r] : 0.f;
+        compute(xa);
+    }
+
+    // This lane's sums: rows m, columns n + e.
+    float acc[kM][P];
+#pragma unroll
+    for (int m = 0; m < kM; ++m)
+#pragma unroll
+        for (int e = 0; e < P; ++e) acc[m][e] = kMfma ? macc[e][m / 4][m % 4] : facc[e];
+#pragma unroll
+    for (int m = 0; m < kM; ++m)
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            float v = acc[m][e];
+#pragma unroll
+            for (int off = kL; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+            acc[m][e] = v;
+        }
+    const int wave = tid / 64;
+    if ((tid % 64) < kL) {
+#pragma unroll
+        for (int m = 0; m < kM; ++m)
+#pragma unroll
+            for (int e = 0; e < P; ++e) red[(wave * kM + m) * kCols + lane * P + e] = acc[m][e];
+    }
+    __syncthreads();
+    for (int o = tid; o < kM * kCols; o += kThreads) {
+        const int m = o / kCols, col = o % kCols;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += red[(w * kM + m) * kCols + col];
+        if (m < M && n0 + col < N) unsafeAtomicAdd(C + m * ldc + n0 + col, sum);
+    }
+}
+
+constexpr int kSplitThreads = 512;
+
+// Whether the K split takes this fp32 product: aligned 16-byte loads of B
+// (A's rows may be unaligned: then read one element at a time), N a
+// multiple of 4, at most 16 rows, 96-128 strips of 128 bytes
+// (192-256 work-groups) and K long enough to amortise the fill (measured
+// against the row split: 8 x 3072 x 1500 10.7 vs 17.4 us, 7 x 4096 x 4096
+// 18.1 vs 20.1, 16 x 4096 x 4096 20.4 vs 24.9, but 12 x 4096 x 1536 13.1
+// vs 12.7, so 9-16 rows need K >= 2048).
+bool ksplit_fits(const Problem &p)
+{
+    const int64_t strips = (p.N + 31) / 32;
+    const bool vec_b = (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && p.ldb % 4 == 0;
+    return vec_b && p.N % 4 == 0 && p.M <= kMaxM && p.K >= (p.M <= 8 ? 1024 : 2048) &&
+           8 * strips >= 3 * kCUs && 2 * strips <= kCUs &&
+           p.ldb <= (int64_t(1) << 31) / (4 * 4 * (kSplitThreads / 8));
+}
+
+template <int kM>
+hipError_t launch_ksplit_m(const Problem &p, hipStream_t s, dim3 grid, dim3 block, int64_t khalf, bool vec_a)
+{
+    const float *A = static_cast<const float *>(p.A), *B = static_cast<const float *>(p.B);
+    if (vec_a)
+        hipLaunchKernelGGL((skinny_ksplit_kernel<kM, kSplitThreads, true>), grid, block, 0, s, p.M, p.N, p.K,
+                           khalf, A, p.lda, B, p.ldb, p.C, p.ldc);
+    else
+        hipLaunchKernelGGL((skinny_ksplit_kernel<kM, kSplitThreads, false>), grid, block, 0, s, p.M, p.N, p.K,
+                           khalf, A, p.lda, B, p.ldb, p.C, p.ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_ksplit(const Problem &p, hipStream_t s)
+{
+    const int64_t strips = (p.N + 31) / 32;
+    const int64_t khalf = ((p.K + 1) / 2 + 3) / 4 * 4;     // a multiple of 4 below K
+    const hipError_t e = launch_fill(p, -0.0f, s);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<uint32_t>(16 * ((strips + 7) / 8))), block(kSplitThreads);
+    const bool vec_a = (reinterpret_cast<uintptr_t>(p.A) & 15) == 0 && p.lda % 4 == 0;
+    if (p.M <= 1) return launch_ksplit_m<1>(p, s, grid, block, khalf, vec_a);
+    if (p.M <= 4) return launch_ksplit_m<4>(p, s, grid, block, khalf, vec_a);
+    if (p.M <= 8) return launch_ksplit_m<8>(p, s, grid, block, khalf, vec_a);
+    return launch_ksplit_m<16>(p, s, grid, block, khalf, vec_a);
+}
+
 template <typename T, int kM, int kL, int kThreads, int kU, int kMode>
 hipError_t launch_cfg(const Problem &p, hipStream_t s, bool vec)
 {
@@ -366,6 +599,7 @@ hipError_t launch_skinny(const Problem &p, hipStream_t s)
                      (reinterpret_cast<uintptr_t>(p.A) & (4 * sizeof(T) - 1)) == 0 && p.lda % 4 == 0;
     const int64_t strips = strips_of<T>(p);
     const bool few = strips < kCUs;
+    if (P == 4 && ksplit_fits(p)) return launch_ksplit(p, s);
     if (P == 4 && p.M <= 4 && 4 * strips <= 3 * kCUs && (p.N + 8 * P - 1) / (8 * P) >= 128) {
         if (p.M <= 1) return launch_cfg<T, 1, 16, 1024, 4, kBalanced>(p, s, vec);
         if (p.M <= 2) return launch_cfg<T, 2, 16, 1024, 4, kBalanced>(p, s, vec);

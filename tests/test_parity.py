@@ -270,6 +270,45 @@ def test_skinny_long_k_exact(dtype):
             assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
 
 
+# The fp32 K split over two work-groups (1-16 rows, 96-128 strips of 128
+# bytes, K >= 1024 up to 8 rows, K >= 2048 above): every compiled row count
+# (1, 4, 8, 16 after rounding up), K with a partial last step in either
+# half, a ragged last strip, row strides of A and B wider than the product,
+# and rows of A that are not 16-byte aligned (element loads of A).
+KSPLIT_CASES = [(1, 4096, 4096), (2, 4092, 1027), (3, 3200, 1024), (4, 4096, 1030),
+                (5, 4000, 2051), (7, 4096, 4096), (8, 3072, 1500), (9, 4096, 2048),
+                (12, 4064, 2049), (16, 3100, 2050)]
+
+
+def test_skinny_k_split_exact():
+    gen = workloads.generator(86)
+    for (M, N, K) in KSPLIT_CASES:
+        # the wide A rows are a multiple of four elements, so the strided case
+        # takes the K split also where K is not
+        A = workloads.small_int((M, (K + 3) // 4 * 4 + 4), -4, 4, gen)
+        B = workloads.small_int((K, N + 4), -4, 4, gen)
+        exact = (A[:, :K].to(torch.int64) @ B[:, :N].to(torch.int64)).to(torch.float64).numpy()
+        exact_un = (A[:, 1:K + 1].to(torch.int64) @ B[:, :N].to(torch.int64)).to(torch.float64).numpy()
+        Ad, Bd = A.to(DEV), B.to(DEV)
+        for a, b, ref, tag in ((Ad[:, :K].contiguous(), Bd[:, :N].contiguous(), exact, "packed"),
+                               (Ad[:, :K], Bd[:, :N], exact, "strided"),
+                               (Ad[:, 1:K + 1], Bd[:, :N], exact_un, "A offset one element")):
+            assert takes("skinny_f32", a, b)
+            say(f"[skinny k split] {M}x{N}x{K} {tag}")
+            C = run(a, b, "skinny_f32")
+            bad = np.argwhere(C.cpu().numpy().astype(np.float64) != ref)
+            assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
+        # random operands: within the gate, and two calls bitwise equal
+        Ar = workloads.draw((M, K), ("normal", 1.0), gen)
+        Br = workloads.draw((K, N), ("normal", 1.0), gen)
+        ref, den = oracle.gemm_f32(Ar.numpy(), Br.numpy())
+        C1 = run(Ar.to(DEV), Br.to(DEV), "skinny_f32")
+        C2 = run(Ar.to(DEV), Br.to(DEV), "skinny_f32")
+        assert torch.equal(C1, C2)
+        err = oracle.normalized_error(C1.cpu().numpy(), ref, den)[0]
+        assert err <= GATE, f"{M}x{N}x{K}: {err}"
+
+
 def test_skinny_streams_and_graphs():
     # Calls on two streams with no synchronization between them, then a
     # captured graph replayed between eager calls: every output exact, and

@@ -39,6 +39,7 @@ OCCUPANCY_BUDGET = {
     "2sk10f32_kernel": 2,
     "valu_f32_kernel": 3,
     "skinny_kernel": 1,
+    "skinny_ksplit_kernel": 2,
     "skinny_fp8_kernel": 2,
     "naive_kernel": 8,
 }
