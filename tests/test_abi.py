@@ -382,16 +382,16 @@ def test_plan_fp8_layouts_and_kernels():
                                C=PC) == -1
     assert g.gemm_plan_batched(g.FP8, 0, 1, 64, 64, 64, 1, A=PC + 64 * 64 * 4, B=PB,
                                C=PC) >= 0
-    # at most 4 rows of one product: the bandwidth kernel
-    for M in (1, 3, 4):
+    # at most 16 rows of one product: the bandwidth kernel
+    for M in (1, 3, 4, 5, 16):
         assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, M, 8960, 1536, 1, **P)) == \
             "skinny_fp8"
-    for M in (5, 16, 17):
-        assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, M, 8960, 1536, 1, **P)) != \
-            "skinny_fp8"
-    # rows that one 128-row tile covers: the 128 x 128 tile, whatever K
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 16, 8192, 8192, 1, **P)) == \
-        "mfma_fp8_direct128"
+        "skinny_fp8"
+    # rows that one 128-row tile covers: the 128 x 128 tile, whatever K
+    for M in (17, 128):
+        assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, M, 8192, 8192, 1, **P)) == \
+            "mfma_fp8_direct128"
     assert g.gemm_kernel_name(g.gemm_plan_batched(g.FP8, 0, 1, 1, 8960, 1536, 2, **P)) != \
         "skinny_fp8"
     # K = 0 is computed (zeros) by a general kernel; empty problems do nothing

@@ -26,8 +26,11 @@ GATE = oracle.GATE
 FMTS = [(0, 0), (0, 1), (1, 0), (1, 1)]
 KERNELS = ["mfma_fp8_direct128", "mfma_fp8_direct256x128", "mfma_fp8_direct256", "mfma_fp8_batched",
            "mfma_fp8_batched128"]
+# K from one partial 128-byte block to 64 whole ones: every path of the
+# bandwidth kernel's loop (steps of four blocks per wave, the single blocks
+# after them, a last block that K does not fill), N not a multiple of 16.
 SKINNY_SHAPES = [(1, 300, 1024), (2, 77, 16), (3, 130, 4096), (7, 520, 256), (16, 64, 2048),
-                 (9, 1000, 208)]
+                 (9, 1000, 208), (4, 48, 6272), (5, 200, 8192), (16, 33, 6160)]
 TORCH = workloads.FP8_TORCH
 
 
@@ -148,7 +151,7 @@ def test_padded_rows_and_guard_band(kernel):
 
 
 def test_skinny_padded_rows_and_guard_band():
-    # the few-row bandwidth kernel (the table's choice up to 4 rows) on rows
+    # the few-row bandwidth kernel (the table's choice up to 16 rows) on rows
     # K + pad bytes apart, writing into a window of a sentinel-filled buffer
     M, N, K, pad = 3, 150, 320, 48
     gen = workloads.generator(35)
@@ -247,7 +250,7 @@ def test_benchmark_shapes_sampled(name):
 @pytest.mark.parametrize("M,N,K", SKINNY_SHAPES)
 def test_skinny_gate_and_exact(M, N, K):
     """At most 16 rows: the bandwidth kernel (Bt streamed once; the table's
-    choice up to 4 rows), forced; random operands to the gate, small
+    choice without block scales), forced; random operands to the gate, small
     integers exactly, all four format pairings."""
     assert takes("skinny_fp8", M, N, K)
     gen = workloads.generator(36)

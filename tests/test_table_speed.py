@@ -38,6 +38,9 @@ SHAPES = [
     ("fp8", 8192, 8192, 8192, False), ("fp8", 4096, 4096, 4096, False),
     ("fp8", 2048, 2048, 8192, False), ("fp8", 2048, 2048, 2048, False),
     ("fp8", 16384, 1152, 384, False), ("fp8", 16384, 384, 1536, False),
+    # few rows: the bandwidth kernels
+    ("f32", 7, 4096, 4096, False), ("f32", 4, 4096, 4096, False),
+    ("fp8", 16, 8192, 8192, False), ("fp8", 4, 8192, 8192, False), ("fp8", 12, 4096, 2048, False),
 ]
 
 
