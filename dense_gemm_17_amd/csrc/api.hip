@@ -309,14 +309,11 @@ int select_general(const Problem &p)
                    : kernel_id("mfma_bf16_batched128");
     // 8-bit floats: the LDS-direct tiles when K is whole 64-byte tiles,
     // else the register-staged ones (K a multiple of 16 bytes).
-    // 8-bit floats with at most 16 rows (one product, no block scales):
-    // stream Bt once with the products on the 16 x 16 x 128 matrix
-    // instruction (16 x 8192 x 8192: 18.6 vs 41.5 us for the 128 x 128
-    // tile; 4 x 8192 x 8192: 15.1 us).  With MX scales the bandwidth kernel
-    // widens to fp32 on the vector ALUs, which keeps up with the stream only
-    // to 4 rows (1 x 8960 x 1536: 7.8 vs 11.1 us for the 128 x 128 tile; at
-    // 16 rows about 19 vector operations per byte of Bt).
-    if (p.dtype == kFp8 && p.M <= (p.xa ? 4 : 16) && supports_skinny_fp8(p)) return kernel_id("skinny_fp8");
+    // 8-bit floats with at most 16 rows (one product): stream Bt once with
+    // the products on the 16 x 16 x 128 matrix instruction (16 x 8192 x
+    // 8192: 18.6 vs 41.5 us for the 128 x 128 tile, with MX scales 19.3 vs
+    // 42.8; 4 x 8192 x 8192: 15.1 us, MX 18.1).
+    if (p.dtype == kFp8 && supports_skinny_fp8(p)) return kernel_id("skinny_fp8");
     if (p.dtype == kFp8 && supports_mfma_fp8_direct(p)) {
         // (M <= 128: one 128-row tile covers M and the 256-row tile would
         // do at least twice the padded work; 16 x 8192 x 8192: 41.9 vs 58.6 us)

@@ -316,10 +316,12 @@ int gemm_last_kernel(void);
  * ldc, formats and layout conditions as gemm_fp8_f32acc; K a multiple of
  * 32; ld_scale_a >= M and ld_scale_b >= N, both multiples of 4; scale_a and
  * scale_b 4-byte aligned, each K/32 rows of its leading dimension long, not
- * overlapping C.  A NaN scale makes the outputs it touches NaN.  The
- * matrix-core kernels pass each lane's scale to the instruction's scale
- * operand (v_mfma_scale_f32_32x32x64_f8f6f4); the bandwidth kernel for at
- * most 4 rows scales each block's partial sum by 2^(sa + sb - 254).  Errors
+ * overlapping C.  A NaN scale makes the outputs it touches NaN.  Every
+ * kernel passes each lane's scale to the matrix instruction's scale
+ * operand (v_mfma_scale_f32_32x32x64_f8f6f4 in the tiles,
+ * v_mfma_scale_f32_16x16x128_f8f6f4 in the bandwidth kernel for at most 16
+ * rows), which multiplies each 32-element block's products by
+ * 2^(sa + sb - 254).  Errors
  * as gemm_fp8_f32acc, plus hipErrorInvalidValue for a K that is not a
  * multiple of 32 or bad scale arrays. */
 int gemm_mxfp8_f32acc(int fmt_a, int fmt_b, int64_t M, int64_t N, int64_t K,

@@ -423,7 +423,7 @@ def test_forced_fp8_kernel_only_for_fp8_calls():
 
 
 def test_mx_table_choices():
-    # 8-bit products with MX block scales: the bandwidth kernel up to 4 rows,
+    # 8-bit products with MX block scales: the bandwidth kernel up to 16 rows,
     # the LDS-direct tiles for whole 64-byte K tiles, the 128 x 128
     # register-staged tile otherwise (the 256 x 256 one takes no scales);
     # refused: K not whole 32-element blocks, scale pitches below the rows
@@ -437,7 +437,10 @@ def test_mx_table_choices():
         return g.gemm_kernel_name(k) if k >= 0 else k
 
     assert plan(4, 512, 1024) == "skinny_fp8"
-    assert plan(8, 77, 160) == "mfma_fp8_batched128"
+    assert plan(8, 77, 160) == "skinny_fp8"
+    assert plan(16, 8192, 8192) == "skinny_fp8"
+    assert plan(17, 8192, 8192) == "mfma_fp8_direct128"
+    assert plan(24, 77, 160) == "mfma_fp8_batched128"
     assert plan(256, 256, 512) == "mfma_fp8_direct128"
     assert plan(8192, 8192, 8192) == "mfma_fp8_direct256"
     assert plan(512, 512, 480) == "mfma_fp8_batched128"

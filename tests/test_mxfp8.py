@@ -89,7 +89,8 @@ def ref(A, SA, Bt, SB):
 
 def shape_for(kernel):
     if kernel == "skinny_fp8":
-        return [(1, 300, 1024), (3, 130, 4096), (8, 77, 160)]
+        # up to 16 rows; whole 128-byte steps and a last block K half fills
+        return [(1, 300, 1024), (3, 130, 4096), (8, 77, 160), (12, 200, 8192), (16, 33, 6176)]
     if kernel == "mfma_fp8_batched128":
         return [(300, 260, 224), (129, 70, 32)]
     return [(300, 260, 256), (520, 136, 1024)]
@@ -168,7 +169,7 @@ def test_nan_scale_poisons_its_outputs(kernel):
 
 
 def test_table_choice_and_headline_size_sampled():
-    # the table's kernels: <= 4 rows the bandwidth kernel, whole 64-byte K
+    # the table's kernels: <= 16 rows the bandwidth kernel, whole 64-byte K
     # tiles the LDS-direct tiles, else the 128 x 128 register-staged tile;
     # 8192^3 with random scales on sampled rows
     gen = workloads.generator(55)
