@@ -39,6 +39,8 @@
 //     shuffles inside a wave, then LDS across waves), so the result is
 //     deterministic; no workspace;
 //   * ragged N and unaligned B or A fall back to element loads with masks.
+#include <type_traits>
+
 #include "gemm_internal.h"
 #include "tile_map.h"
 
@@ -452,6 +454,7 @@ __global__ __launch_bounds__(kThreads) void skinny_ksplit_kernel(int64_t M, int6
 }
 
 constexpr int kSplitThreads = 512;
+constexpr int kSplitThreads16 = 512;
 
 // Whether the K split takes this fp32 product: aligned 16-byte loads of B
 // (A's rows may be unaligned: then read one element at a time), N a
@@ -494,6 +497,209 @@ hipError_t launch_ksplit(const Problem &p, hipStream_t s)
     if (p.M <= 4) return launch_ksplit_m<4>(p, s, grid, block, khalf, vec_a);
     if (p.M <= 8) return launch_ksplit_m<8>(p, s, grid, block, khalf, vec_a);
     return launch_ksplit_m<16>(p, s, grid, block, khalf, vec_a);
+}
+
+// The same K split for 16-bit operands (bf16 or fp16 bits), products on
+// v_mfma_f32_4x4x4_16b_bf16 / _f16: sixteen independent 4 x 4 blocks, each
+// summing over 4 k, lane l supplying row l % 4 of A and column l % 4 of B
+// of block l / 4 (4 consecutive k each) and receiving that column's four
+// rows.  A lane's four B rows give one 16-byte load per row (8 columns);
+// column e's four values are gathered into the lane's B operand, so a step
+// is one instruction per column and group of four rows.  kL = 8 lanes per
+// K-group: strips of 128 bytes.
+template <typename T, int kM, int kL, bool kAVec>
+__global__ __launch_bounds__(kSplitThreads16) void skinny_ksplit16_kernel(
+    int64_t M, int64_t N, int64_t K, int64_t khalf, const T *__restrict__ A, int64_t lda,
+    const T *__restrict__ B, int64_t ldb, float *__restrict__ C, int64_t ldc)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+    constexpr int kThreads = kSplitThreads16;
+    constexpr int P = 8, kCols = kL * P, kGroups = kThreads / kL, kWaves = kThreads / 64;
+    constexpr int kH = kM / 4;
+    constexpr bool kF16 = !std::is_same<T, uint16_t>::value;
+    static_assert(kM == 4 || kM == 8, "compiled row counts");
+    __shared__ float red[kWaves * kM * kCols];
+
+    const int tid = threadIdx.x, lane = tid % kL, grp = tid / kL;
+    const int64_t id = blockIdx.x;
+    const int64_t part = (id >> 3) & 1;
+    const int64_t n0 = ((id >> 4) * 8 + (id & 7)) * kCols;
+    if (n0 >= N) return;                          // whole work-group
+    const int64_t k0 = part * khalf, k1 = part ? K : khalf;
+    const int64_t n = n0 + lane * P;
+    const int64_t nl = n < N ? n : N - P;         // past N: a valid column, sums dropped
+    const uint16_t *A16 = reinterpret_cast<const uint16_t *>(A);
+    const uint16_t *B16 = reinterpret_cast<const uint16_t *>(B);
+
+    int64_t arow[kH];
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+        const int r = 4 * h + (tid & 3);
+        arow[h] = (r < M ? r : 0) * lda;
+    }
+    uint32_t boff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) boff[r] = static_cast<uint32_t>(((4 * grp + r) * ldb + nl) * 2);
+
+    struct Step {
+        u16x8 b[4];
+        u16x4 a[kH];
+    };
+    auto load = [&](Step &x, int64_t row0) {
+        const char *bb = reinterpret_cast<const char *>(B16 + row0 * ldb);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x.b[r] = *reinterpret_cast<const u16x8 *>(bb + boff[r]);
+        const uint16_t *aa = A16 + row0 + 4 * grp;
+#pragma unroll
+        for (int h = 0; h < kH; ++h) {
+            if constexpr (kAVec) {
+                x.a[h] = *reinterpret_cast<const u16x4 *>(aa + arow[h]);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) x.a[h][r] = aa[arow[h] + r];
+            }
+        }
+    };
+    f32x4 macc[P][kH];
+#pragma unroll
+    for (int e = 0; e < P; ++e)
+#pragma unroll
+        for (int h = 0; h < kH; ++h) macc[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](const Step &x) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            const u16x4 bcol = {x.b[0][e], x.b[1][e], x.b[2][e], x.b[3][e]};
+#pragma unroll
+            for (int h = 0; h < kH; ++h) {
+                if constexpr (kF16)
+                    macc[e][h] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h16x4, x.a[h]),
+                                                                    __builtin_bit_cast(h16x4, bcol),
+                                                                    macc[e][h], 0, 0, 0);
+                else
+                    macc[e][h] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4, x.a[h]),
+                                                                       __builtin_bit_cast(s16x4, bcol),
+                                                                       macc[e][h], 0, 0, 0);
+            }
+        }
+    };
+
+    constexpr int64_t kRows = 4 * int64_t(kGroups);
+    const int64_t full = (k1 - k0) / kRows;
+    int64_t row0 = k0;
+    Step xa, xb;
+    if (full > 0) {
+        load(xa, row0);
+        int64_t j = 1;
+        for (; j + 1 < full; j += 2) {
+            load(xb, row0 + kRows);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xa);
+            __builtin_amdgcn_sched_barrier(0);
+            row0 += kRows;
+            load(xa, row0 + kRows);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xb);
+            __builtin_amdgcn_sched_barrier(0);
+            row0 += kRows;
+        }
+        if (j < full) {
+            load(xb, row0 + kRows);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xa);
+            __builtin_amdgcn_sched_barrier(0);
+            row0 += kRows;
+            compute(xb);
+        } else {
+            compute(xa);
+        }
+        row0 += kRows;
+    }
+    // the rest of the half: rows past k1 and A's columns past k1 are zero;
+    // every lane takes part (the matrix instruction works on the whole wave)
+    for (; row0 < k1; row0 += kRows) {
+        const int64_t k4 = row0 + 4 * grp;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            xa.b[r] = k4 + r < k1 ? *reinterpret_cast<const u16x8 *>(B16 + (k4 + r) * ldb + nl)
+                                  : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < kH; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xa.a[h][r] = k4 + r < k1 ? A16[arow[h] + k4 + r] : uint16_t(0);
+        compute(xa);
+    }
+
+    // this lane's sums: rows m, columns n + e; then the K-groups of a wave
+    // by lane shuffles, the waves through LDS, in a fixed order
+    float acc[kM][P];
+#pragma unroll
+    for (int m = 0; m < kM; ++m)
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+            float v = macc[e][m / 4][m % 4];
+#pragma unroll
+            for (int off = kL; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+            acc[m][e] = v;
+        }
+    const int wave = tid / 64;
+    if ((tid % 64) < kL) {
+#pragma unroll
+        for (int m = 0; m < kM; ++m)
+#pragma unroll
+            for (int e = 0; e < P; ++e) red[(wave * kM + m) * kCols + lane * P + e] = acc[m][e];
+    }
+    __syncthreads();
+    for (int o = tid; o < kM * kCols; o += kThreads) {
+        const int m = o / kCols, col = o % kCols;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += red[(w * kM + m) * kCols + col];
+        if (m < M && n0 + col < N) unsafeAtomicAdd(C + m * ldc + n0 + col, sum);
+    }
+}
+
+// 16-bit K split: strips of 128 bytes (64 columns), at most 8 rows (16
+// rows' 32 accumulator blocks spill at two waves per SIMD), the 32-bit B
+// offsets as for fp32.  96-128 strips (192-256 work-groups) from K = 1024
+// (4 x 8192 x 8192: 52.8 -> 37.1 us); 48-95 strips (half the CUs or more)
+// only from K = 8192, where each work-group's half is long enough (8 x 4096
+// x 14336: 68.0 -> 48.7 us; at K = 4096 the row split stays ahead, 1 x 4096
+// x 4096 19.7 vs 20.9).  64-byte strips (two work-groups sharing each line)
+// measured slower in both cases (25.3 and 50.5 us).
+bool ksplit16_fits(const Problem &p)
+{
+    const int64_t strips = (p.N + 63) / 64;
+    const bool vec_b = (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && p.ldb % 8 == 0;
+    const bool many = 8 * strips >= 3 * kCUs, half = 16 * strips >= 3 * kCUs && p.K >= 8192;
+    return vec_b && p.N % 8 == 0 && p.M <= 8 && p.K >= 1024 && (many || half) && 2 * strips <= kCUs &&
+           p.ldb <= (int64_t(1) << 31) / (2 * 4 * (kSplitThreads16 / 8));
+}
+
+template <typename T, int kM, int kL>
+hipError_t launch_ksplit16_m(const Problem &p, hipStream_t s, dim3 grid, int64_t khalf, bool vec_a)
+{
+    const T *A = static_cast<const T *>(p.A), *B = static_cast<const T *>(p.B);
+    if (vec_a)
+        hipLaunchKernelGGL((skinny_ksplit16_kernel<T, kM, kL, true>), grid, dim3(kSplitThreads16), 0, s, p.M,
+                           p.N, p.K, khalf, A, p.lda, B, p.ldb, p.C, p.ldc);
+    else
+        hipLaunchKernelGGL((skinny_ksplit16_kernel<T, kM, kL, false>), grid, dim3(kSplitThreads16), 0, s, p.M,
+                           p.N, p.K, khalf, A, p.lda, B, p.ldb, p.C, p.ldc);
+    return hipGetLastError();
+}
+
+template <typename T, int kL>
+hipError_t launch_ksplit16(const Problem &p, hipStream_t s)
+{
+    const int64_t strips = (p.N + kL * 8 - 1) / (kL * 8);
+    const int64_t khalf = ((p.K + 1) / 2 + 3) / 4 * 4;     // a multiple of 4 below K
+    const hipError_t e = launch_fill(p, -0.0f, s);
+    if (e != hipSuccess) return e;
+    const dim3 grid(static_cast<uint32_t>(16 * ((strips + 7) / 8)));
+    const bool vec_a = (reinterpret_cast<uintptr_t>(p.A) & 7) == 0 && p.lda % 4 == 0;
+    if (p.M <= 4) return launch_ksplit16_m<T, 4, kL>(p, s, grid, khalf, vec_a);
+    return launch_ksplit16_m<T, 8, kL>(p, s, grid, khalf, vec_a);
 }
 
 template <typename T, int kM, int kL, int kThreads, int kU, int kMode>
@@ -599,7 +805,11 @@ hipError_t launch_skinny(const Problem &p, hipStream_t s)
                      (reinterpret_cast<uintptr_t>(p.A) & (4 * sizeof(T) - 1)) == 0 && p.lda % 4 == 0;
     const int64_t strips = strips_of<T>(p);
     const bool few = strips < kCUs;
-    if (P == 4 && ksplit_fits(p)) return launch_ksplit(p, s);
+    if constexpr (P == 4) {
+        if (ksplit_fits(p)) return launch_ksplit(p, s);
+    } else {
+        if (ksplit16_fits(p)) return launch_ksplit16<T, 8>(p, s);
+    }
     if (P == 4 && p.M <= 4 && 4 * strips <= 3 * kCUs && (p.N + 8 * P - 1) / (8 * P) >= 128) {
         if (p.M <= 1) return launch_cfg<T, 1, 16, 1024, 4, kBalanced>(p, s, vec);
         if (p.M <= 2) return launch_cfg<T, 2, 16, 1024, 4, kBalanced>(p, s, vec);

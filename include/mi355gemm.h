@@ -29,11 +29,11 @@
  *     max_ij |c_ij - C_ij| / sum_k |A_ik B_kj| <= 5e-4
  * against the exact product, and each kernel is deterministic (same inputs,
  * same launch -> same bits).  The kernels that split K over two work-groups
- * per output tile (small outputs over a long K, and fp32 products of at most
- * 16 rows with 96-128 column strips of 128 bytes over a long K) first set C
- * to -0.0 and then add each half into it with one atomic add per element:
- * two addends onto -0.0 give the same bits in either order; no other atomics
- * are used.
+ * per output tile (small outputs over a long K, and few-row products whose
+ * 128-byte column strips number fewer than the CUs, over a long K) first
+ * set C to -0.0 and then add each half into it with one atomic add per
+ * element: two addends onto -0.0 give the same bits in either order; no
+ * other atomics are used.
  *
  * Ownership: A, B and C are device memory owned by the caller (for example
  * PyTorch tensors on the current device).  The library never allocates,

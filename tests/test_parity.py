@@ -309,6 +309,44 @@ def test_skinny_k_split_exact():
         assert err <= GATE, f"{M}x{N}x{K}: {err}"
 
 
+# The 16-bit K split (bf16 and fp16, 1-8 rows, 96-128 strips of 128 bytes
+# from K = 1024, 48-95 strips from K = 8192): both compiled row counts (4,
+# 8), K with a partial last step in either half, a ragged last strip, row
+# strides wider than the product, rows of A not 8-byte aligned.
+KSPLIT16_CASES = [(1, 4096, 8192), (3, 4088, 8195), (2, 3200, 9000), (4, 6400, 1024),
+                  (5, 8192, 2051), (8, 6400, 1500), (7, 8192, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_skinny_k_split_16bit_exact(dtype):
+    tdt = TDT[dtype]
+    gen = workloads.generator(87)
+    for (M, N, K) in KSPLIT16_CASES:
+        A = workloads.small_int((M, (K + 3) // 4 * 4 + 4), -8, 8, gen)
+        B = workloads.small_int((K, N + 8), -8, 8, gen)
+        exact = (A[:, :K].to(torch.int64) @ B[:, :N].to(torch.int64)).to(torch.float64).numpy()
+        exact_un = (A[:, 1:K + 1].to(torch.int64) @ B[:, :N].to(torch.int64)).to(torch.float64).numpy()
+        Ad, Bd = A.to(tdt).to(DEV), B.to(tdt).to(DEV)
+        for a, b, ref, tag in ((Ad[:, :K].contiguous(), Bd[:, :N].contiguous(), exact, "packed"),
+                               (Ad[:, :K], Bd[:, :N], exact, "strided"),
+                               (Ad[:, 1:K + 1], Bd[:, :N], exact_un, "A offset one element")):
+            k = f"skinny_{dtype}"
+            assert takes(k, a, b)
+            say(f"[skinny k split] {dtype} {M}x{N}x{K} {tag}")
+            C = run(a, b, k)
+            bad = np.argwhere(C.cpu().numpy().astype(np.float64) != ref)
+            assert bad.size == 0, f"{M}x{N}x{K} {tag}: {len(bad)} wrong, first {bad[:3].tolist()}"
+        # random operands: within the gate, and two calls bitwise equal
+        Ar = workloads.draw((M, K), ("normal", 1.0), gen).to(tdt)
+        Br = workloads.draw((K, N), ("normal", 1.0), gen).to(tdt)
+        ref, den = ORACLE_FN[dtype](workloads.as_numpy_operand(Ar), workloads.as_numpy_operand(Br))
+        C1 = run(Ar.to(DEV), Br.to(DEV), f"skinny_{dtype}")
+        C2 = run(Ar.to(DEV), Br.to(DEV), f"skinny_{dtype}")
+        assert torch.equal(C1, C2)
+        err = oracle.normalized_error(C1.cpu().numpy(), ref, den)[0]
+        assert err <= GATE, f"{dtype} {M}x{N}x{K}: {err}"
+
+
 def test_skinny_streams_and_graphs():
     # Calls on two streams with no synchronization between them, then a
     # captured graph replayed between eager calls: every output exact, and
