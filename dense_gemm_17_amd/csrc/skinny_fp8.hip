@@ -28,8 +28,10 @@
 //   * the 16 x 16 sums land with lane l holding rows 4 (l / 16) .. + 3 of
 //     column l % 16; the four waves' sums are added through LDS in wave
 //     order (the same bits every run);
-//   * a last block that K does not fill is loaded with zeros past K, and
-//     the scales of its blocks past K read as 127.
+//   * the blocks left after the whole steps (and a last block that K does
+//     not fill) form one more step with zeros past K and the scales of
+//     blocks past K read as 127, so short K keeps its loads in flight
+//     together.
 #include "gemm_internal.h"
 
 namespace mi355gemm {
@@ -126,26 +128,30 @@ __global__ __launch_bounds__(256) void skinny_fp8_kernel(
         }
         t = kU * steps;
     }
-    // the rest of this wave's blocks one at a time, the last partial block
-    // (K not a multiple of 128) with zeros past K
-    for (;; ++t) {
-        const int64_t kb = wave + 4 * t;
-        if (kb * 128 >= K) break;
-        const int64_t off = kb * 128;
-        const bool in0 = off + 16 * g < K, in1 = off + 64 + 16 * g < K;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const i32x8 a = join(in0 ? *reinterpret_cast<const u32x4 *>(pa + off) : z,
-                             in1 ? *reinterpret_cast<const u32x4 *>(pa + off + 64) : z);
-        const i32x8 b = join(in0 ? *reinterpret_cast<const u32x4 *>(pb + off) : z,
-                             in1 ? *reinterpret_cast<const u32x4 *>(pb + off + 64) : z);
-        int sa = 127, sb = 127;
-        if constexpr (kMX) {
-            if (off + 32 * g < K) {
-                sa = qa[4 * kb * ldxa];
-                sb = qb[4 * kb * ldxb];
+    // The rest of this wave's blocks (fewer than kU whole ones, and the last
+    // partial block if it is this wave's) as one more step, every load
+    // issued before the first product: blocks past K and bytes past K are
+    // zeros (their scales 127), which add nothing.
+    if (wave + 4 * t < (K + 127) / 128) {   // wave-uniform
+        Step x;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const int64_t kb = wave + 4 * (t + u), off = kb * 128;
+            const bool in0 = off + 16 * g < K, in1 = off + 64 + 16 * g < K;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            x.a[u] = join(in0 ? *reinterpret_cast<const u32x4 *>(pa + off) : z,
+                          in1 ? *reinterpret_cast<const u32x4 *>(pa + off + 64) : z);
+            x.b[u] = join(in0 ? *reinterpret_cast<const u32x4 *>(pb + off) : z,
+                          in1 ? *reinterpret_cast<const u32x4 *>(pb + off + 64) : z);
+            x.sa[u] = x.sb[u] = 127;
+            if constexpr (kMX) {
+                if (off + 32 * g < K) {
+                    x.sa[u] = qa[4 * kb * ldxa];
+                    x.sb[u] = qb[4 * kb * ldxb];
+                }
             }
         }
-        acc[t & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[t & 1], kFA, kFB, 0, sa, 0, sb);
+        compute(x);
     }
 
     red[wave][lane] = acc[0] + acc[1];
