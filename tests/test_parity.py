@@ -585,7 +585,10 @@ def test_graph_capture_replays_match_eager():
              (384, 1152, 4096, torch.bfloat16, 1, True, False),    # the same in bf16
              (2048, 2048, 1024, workloads.FP8_TORCH[0], 1, False, True),   # 8-bit 256^2 tile
              (512, 264, 96, torch.float16, 3, True, True),
-             (300, 270, 100, torch.bfloat16, 2, True, False)]      # general family
+             (300, 270, 100, torch.bfloat16, 2, True, False),      # general family
+             (7, 4096, 4096, torch.float32, 1, False, False),      # few rows: K over 2 work-groups
+             (4, 8192, 2048, torch.bfloat16, 1, False, False),     # the same, 16-bit
+             (12, 4096, 2048, workloads.FP8_TORCH[0], 1, False, True)]   # 8-bit few rows
     ins, eager, outs = [], [], []
     for (M, N, K, dt, nb, ta, tb) in specs:
         lead = (nb,) if nb > 1 else ()
