@@ -101,7 +101,7 @@ bool overlaps(uintptr_t a, int64_t na, uintptr_t b, int64_t nb)
     return a < b + static_cast<uintptr_t>(nb) && b < a + static_cast<uintptr_t>(na);
 }
 
-enum Verdict { kInvalid = -1, kNothing = -2, kZeroFill = -3, kCompute = 0 };
+enum Validity { kInvalid = -1, kNothing = -2, kZeroFill = -3, kCompute = 0 };
 
 // Byte extent of `batch` matrices `stride` elements apart, each of `one`
 // bytes, or -1 if it does not fit in an int64.
@@ -125,7 +125,7 @@ bool outputs_disjoint(const Problem &p)
     return sc >= p.N && static_cast<__int128>(p.batch - 1) * sc + p.N <= ldc;
 }
 
-Verdict validate(const Problem &p)
+Validity validate(const Problem &p)
 {
     if (p.M < 0 || p.N < 0 || p.K < 0 || p.batch < 0) return kInvalid;
     if (p.M > kMaxDim || p.N > kMaxDim || p.K > kMaxDim || p.batch > kMaxDim) return kInvalid;
@@ -466,7 +466,7 @@ int64_t workspace_needed(const Problem &p)
 
 int run_ws(const Problem &p, void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    const Verdict v = validate(p);
+    const Validity v = validate(p);
     if (v != kCompute) return run(p, stream);
     const int64_t S = split_count(p);
     const int64_t need = S > 1 ? S * p.M * p.N * 4 : 0;
