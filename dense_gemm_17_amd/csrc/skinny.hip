@@ -27,7 +27,7 @@
 //     row-split pairs and work-groups of 9-16 rows) and A's rows fit in 64
 //     KiB, the work-group first copies them into LDS (7 x 4096 x 4096:
 //     21.4 -> 20.2 us; 12 x 8960 x 1536: 32.1 -> 27.8);
-//   * fp32 with 96-128 strips of 128 bytes and a long K splits each strip's
+//   * fp32 with 96-255 strips of 128 bytes and a long K splits each strip's
 //     K range between two work-groups (skinny_ksplit_kernel below), so every
 //     CU streams distinct bytes of B; the two halves add into C filled with
 //     -0.0 (two addends: the same bits whichever lands first);
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(int64_t M, int64_t N, 
 }
 
 // ---------------------------------------------------------------------------
-// K split over two work-groups (fp32, 1-16 rows, 96-128 strips of 128 bytes).
+// K split over two work-groups (fp32, 1-16 rows, 96-255 strips of 128 bytes).
 //
 // With fewer strips than CUs, one work-group per strip leaves CUs idle, and
 // one CU pulls only about 25-30 GB/s from HBM however many loads it keeps in
@@ -458,17 +458,19 @@ constexpr int kSplitThreads16 = 512;
 
 // Whether the K split takes this fp32 product: aligned 16-byte loads of B
 // (A's rows may be unaligned: then read one element at a time), N a
-// multiple of 4, at most 16 rows, 96-128 strips of 128 bytes
-// (192-256 work-groups) and K long enough to amortise the fill (measured
-// against the row split: 8 x 3072 x 1500 10.7 vs 17.4 us, 7 x 4096 x 4096
-// 18.1 vs 20.1, 16 x 4096 x 4096 20.4 vs 24.9, but 12 x 4096 x 1536 13.1
+// multiple of 4, at most 16 rows, 96-255 strips of 128 bytes (192-510
+// work-groups; with as many strips as CUs one work-group per strip wins:
+// 7 x 8192 x 4096 29.6 vs 32.0 us) and K long enough to amortise the fill
+// (measured against the row split: 8 x 3072 x 1500 10.7 vs 17.4 us, 7 x
+// 4096 x 4096 18.1 vs 20.1, 16 x 4096 x 4096 20.4 vs 24.9, 7 x 6144 x 4096
+// 29.5 vs 38.2, 7 x 5120 x 8192 52.0 vs 74.7, but 12 x 4096 x 1536 13.1
 // vs 12.7, so 9-16 rows need K >= 2048).
 bool ksplit_fits(const Problem &p)
 {
     const int64_t strips = (p.N + 31) / 32;
     const bool vec_b = (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && p.ldb % 4 == 0;
     return vec_b && p.N % 4 == 0 && p.M <= kMaxM && p.K >= (p.M <= 8 ? 1024 : 2048) &&
-           8 * strips >= 3 * kCUs && 2 * strips <= kCUs &&
+           8 * strips >= 3 * kCUs && strips < kCUs &&
            p.ldb <= (int64_t(1) << 31) / (4 * 4 * (kSplitThreads / 8));
 }
 
