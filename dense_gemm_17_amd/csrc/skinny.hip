@@ -27,7 +27,8 @@
 //     row-split pairs and work-groups of 9-16 rows) and A's rows fit in 64
 //     KiB, the work-group first copies them into LDS (7 x 4096 x 4096:
 //     21.4 -> 20.2 us; 12 x 8960 x 1536: 32.1 -> 27.8);
-//   * fp32 with 96-255 strips of 128 bytes and a long K splits each strip's
+//   * fp32 with 96-255 strips of 128 bytes (48-95 from K = 8192) and a long
+//     K splits each strip's
 //     K range between two work-groups (skinny_ksplit_kernel below), so every
 //     CU streams distinct bytes of B; the two halves add into C filled with
 //     -0.0 (two addends: the same bits whichever lands first);
@@ -460,7 +461,9 @@ constexpr int kSplitThreads16 = 512;
 // (A's rows may be unaligned: then read one element at a time), N a
 // multiple of 4, at most 16 rows, 96-255 strips of 128 bytes (192-510
 // work-groups; with as many strips as CUs one work-group per strip wins:
-// 7 x 8192 x 4096 29.6 vs 32.0 us) and K long enough to amortise the fill
+// 7 x 8192 x 4096 29.6 vs 32.0 us) or 48-95 from K = 8192 (half the CUs or
+// more: 4 x 2560 x 16384 78.1 -> 47.5 us, 12 x 3000 x 8192 59.7 -> 32.5; at
+// 7 x 2048 x 4096 no gain) and K long enough to amortise the fill
 // (measured against the row split: 8 x 3072 x 1500 10.7 vs 17.4 us, 7 x
 // 4096 x 4096 18.1 vs 20.1, 16 x 4096 x 4096 20.4 vs 24.9, 7 x 6144 x 4096
 // 29.5 vs 38.2, 7 x 5120 x 8192 52.0 vs 74.7, but 12 x 4096 x 1536 13.1
@@ -470,7 +473,7 @@ bool ksplit_fits(const Problem &p)
     const int64_t strips = (p.N + 31) / 32;
     const bool vec_b = (reinterpret_cast<uintptr_t>(p.B) & 15) == 0 && p.ldb % 4 == 0;
     return vec_b && p.N % 4 == 0 && p.M <= kMaxM && p.K >= (p.M <= 8 ? 1024 : 2048) &&
-           8 * strips >= 3 * kCUs && strips < kCUs &&
+           (8 * strips >= 3 * kCUs || (16 * strips >= 3 * kCUs && p.K >= 8192)) && strips < kCUs &&
            p.ldb <= (int64_t(1) << 31) / (4 * 4 * (kSplitThreads / 8));
 }
 

@@ -271,13 +271,14 @@ def test_skinny_long_k_exact(dtype):
 
 
 # The fp32 K split over two work-groups (1-16 rows, 96-255 strips of 128
-# bytes, K >= 1024 up to 8 rows, K >= 2048 above): every compiled row count
+# bytes or 48-95 from K = 8192, K >= 1024 up to 8 rows, K >= 2048 above): every compiled row count
 # (1, 4, 8, 16 after rounding up), K with a partial last step in either
 # half, a ragged last strip, row strides of A and B wider than the product,
 # and rows of A that are not 16-byte aligned (element loads of A).
 KSPLIT_CASES = [(1, 4096, 4096), (2, 4092, 1027), (3, 3200, 1024), (4, 4096, 1030),
                 (5, 4000, 2051), (7, 4096, 4096), (8, 3072, 1500), (9, 4096, 2048),
-                (12, 4064, 2049), (16, 3100, 2050), (7, 6144, 4096), (3, 5000, 1030)]
+                (12, 4064, 2049), (16, 3100, 2050), (7, 6144, 4096), (3, 5000, 1030),
+                (7, 2048, 8192), (12, 3000, 8195)]
 
 
 def test_skinny_k_split_exact():
