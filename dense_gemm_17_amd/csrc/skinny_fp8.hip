@@ -18,16 +18,18 @@
 // the E8M0 scale of block g of its row (OCP microscaling: one scale per 32
 // elements; 127 = 2^0 without scales; 255, NaN, gives NaN).
 //
-//   * a work-group owns 16 rows of Bt (16 columns of C); its four waves
-//     take the 128-byte K blocks round robin (wave w: blocks w, w + 4, ..);
+//   * a work-group owns 16 rows of Bt (16 columns of C); its kW waves (4,
+//     or 8 when the work-groups number at most the CUs: 1 x 4096 x 16384
+//     17.3 -> 15.9 us) take the 128-byte K blocks round robin (wave w:
+//     blocks w, w + kW, ..);
 //     rows of A past M and of Bt past N re-read the last valid row (their
 //     sums are dropped);
 //   * each wave loads kU blocks per step and issues the next step's loads
 //     before the current step's products (two register sets in turn); two
 //     accumulators alternate so that consecutive products are independent;
 //   * the 16 x 16 sums land with lane l holding rows 4 (l / 16) .. + 3 of
-//     column l % 16; the four waves' sums are added through LDS in wave
-//     order (the same bits every run);
+//     column l % 16; the waves' sums are added through LDS in wave order
+//     (the same bits every run);
 //   * the blocks left after the whole steps (and a last block that K does
 //     not fill) form one more step with zeros past K and the scales of
 //     blocks past K read as 127, so short K keeps its loads in flight
@@ -50,13 +52,13 @@ __device__ __forceinline__ i32x8 join(const u32x4 &lo, const u32x4 &hi)
 }
 
 // K a multiple of 16 (of 32 with kMX), rows 16-byte aligned.
-template <int kFA, int kFB, bool kMX>
-__global__ __launch_bounds__(256) void skinny_fp8_kernel(
+template <int kFA, int kFB, bool kMX, int kW>
+__global__ __launch_bounds__(64 * kW) void skinny_fp8_kernel(
     int64_t M, int64_t N, int64_t K, const uint8_t *__restrict__ A, int64_t lda,
     const uint8_t *__restrict__ Bt, int64_t ldb, float *__restrict__ C, int64_t ldc,
     const uint8_t *__restrict__ xa, int64_t ldxa, const uint8_t *__restrict__ xb, int64_t ldxb)
 {
-    __shared__ f32x4 red[4][64];
+    __shared__ f32x4 red[kW][64];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -70,8 +72,8 @@ __global__ __launch_bounds__(256) void skinny_fp8_kernel(
     const uint8_t *qb = kMX ? xb + g * ldxb + br : nullptr;
 
     const int64_t nfull = K / 128;               // whole blocks
-    // this wave's whole blocks: w, w + 4, ... below nfull
-    const int64_t mine = nfull > wave ? (nfull - wave + 3) / 4 : 0;
+    // this wave's whole blocks: w, w + kW, ... below nfull
+    const int64_t mine = nfull > wave ? (nfull - wave + kW - 1) / kW : 0;
     const int64_t steps = mine / kU;
 
     struct Step {
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(256) void skinny_fp8_kernel(
     auto load = [&](Step &x, int64_t t0) {
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t kb = wave + 4 * (t0 + u), off = kb * 128;
+            const int64_t kb = wave + kW * (t0 + u), off = kb * 128;
             x.a[u] = join(*reinterpret_cast<const u32x4 *>(pa + off),
                           *reinterpret_cast<const u32x4 *>(pa + off + 64));
             x.b[u] = join(*reinterpret_cast<const u32x4 *>(pb + off),
@@ -132,11 +134,11 @@ __global__ __launch_bounds__(256) void skinny_fp8_kernel(
     // partial block if it is this wave's) as one more step, every load
     // issued before the first product: blocks past K and bytes past K are
     // zeros (their scales 127), which add nothing.
-    if (wave + 4 * t < (K + 127) / 128) {   // wave-uniform
+    if (wave + kW * t < (K + 127) / 128) {   // wave-uniform
         Step x;
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
-            const int64_t kb = wave + 4 * (t + u), off = kb * 128;
+            const int64_t kb = wave + kW * (t + u), off = kb * 128;
             const bool in0 = off + 16 * g < K, in1 = off + 64 + 16 * g < K;
             const u32x4 z = {0u, 0u, 0u, 0u};
             x.a[u] = join(in0 ? *reinterpret_cast<const u32x4 *>(pa + off) : z,
@@ -156,20 +158,25 @@ __global__ __launch_bounds__(256) void skinny_fp8_kernel(
 
     red[wave][lane] = acc[0] + acc[1];
     __syncthreads();
-    // thread q: lane q % 64's element q / 64 (row 4 (l / 16) + r, column l % 16)
-    const int q = threadIdx.x, l = q & 63, r = q >> 6;
-    const float v = ((red[0][l][r] + red[1][l][r]) + red[2][l][r]) + red[3][l][r];
-    const int64_t row = 4 * (l >> 4) + r, col = j0 + (l & 15);
-    if (row < M && col < N) store_c_stream(C + row * ldc + col, v);
+    // thread q < 256: lane q % 64's element q / 64 (row 4 (l / 16) + r,
+    // column l % 16), the waves added in order
+    const int q = threadIdx.x, l = q & 63, r = (q >> 6) & 3;
+    if (q < 256) {
+        float v = red[0][l][r];
+#pragma unroll
+        for (int w = 1; w < kW; ++w) v += red[w][l][r];
+        const int64_t row = 4 * (l >> 4) + r, col = j0 + (l & 15);
+        if (row < M && col < N) store_c_stream(C + row * ldc + col, v);
+    }
 }
 
-template <bool kMX>
+template <bool kMX, int kW>
 void launch_formats(const Problem &p, dim3 grid, hipStream_t s)
 {
     const auto *A = static_cast<const uint8_t *>(p.A);
     const auto *B = static_cast<const uint8_t *>(p.B);
-#define MI355_SKINNY_FP8(FA, FB)                                                                 \
-    hipLaunchKernelGGL((skinny_fp8_kernel<FA, FB, kMX>), grid, dim3(256), 0, s, p.M, p.N, p.K, A, \
+#define MI355_SKINNY_FP8(FA, FB)                                                                     \
+    hipLaunchKernelGGL((skinny_fp8_kernel<FA, FB, kMX, kW>), grid, dim3(64 * kW), 0, s, p.M, p.N, p.K, A, \
                        p.lda, B, p.ldb, p.C, p.ldc, p.xa, p.ldxa, p.xb, p.ldxb)
     switch (2 * p.fa + p.fb) {
     case 0: MI355_SKINNY_FP8(0, 0); break;
@@ -193,8 +200,11 @@ hipError_t launch_skinny_fp8(const Problem &p, hipStream_t s)
     const int64_t wgs = (p.N + 15) / 16;
     if (wgs > kMaxBlocks) return hipErrorInvalidValue;
     const dim3 grid(static_cast<uint32_t>(wgs));
-    if (p.xa) launch_formats<true>(p, grid, s);
-    else launch_formats<false>(p, grid, s);
+    // with at most one work-group per CU, eight waves per work-group keep
+    // twice the loads in flight
+    const bool eight = wgs <= kCUs;
+    if (p.xa) eight ? launch_formats<true, 8>(p, grid, s) : launch_formats<true, 4>(p, grid, s);
+    else eight ? launch_formats<false, 8>(p, grid, s) : launch_formats<false, 4>(p, grid, s);
     return hipGetLastError();
 }
 
